@@ -1,0 +1,167 @@
+"""The CPU oracle of the Q8_0 decode GEMV -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain C, see
+``qdg_oracle.c``) with numpy arrays and shares no code with the GPU library.
+
+Functions (each mirrors one step of the method; citations in ``qdg_oracle.c``):
+
+* ``quantize(mode, x)`` -> ``(xq, xl, xs)``
+* ``block_dots(mode, wq, xq, xl)`` -> ``(dh, dl)`` exact int32 per-block dots
+* ``gemv(mode, wq, ws, x=None, xq=None, xl=None, xs=None)`` -> ``y[B][N]``
+* ``split_bounds(K, S)`` -> block boundaries of the split-K chunks
+* ``gemv_split(mode, wq, ws, xq, xl, xs, S)`` -> partials ``[S][B][N]``
+* ``combine(part)`` -> ``y``
+* ``argmax(y)`` -> first index of the maximum, per row
+* ``reference_f64(mode, ...)`` -> ``(Y, tnorm)`` binary64 anchor of the tolerance
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DEQUANT, INT8ACT, TWOPASS = 0, 1, 2
+QK = 32
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.orc_quantize.argtypes = [I, P, I64, I64, P, P, P]
+        lib.orc_block_dots.argtypes = [I, P, I64, I64, P, P, I64, P, P]
+        lib.orc_gemv.argtypes = [I, P, P, I64, I64, P, P, P, P, I64, P, I]
+        lib.orc_split_bounds.argtypes = [I64, I, P]
+        lib.orc_gemv_split.argtypes = [I, P, P, I64, I64, P, P, P, I64, I, P, I]
+        lib.orc_combine.argtypes = [P, I, I64, I64, P]
+        lib.orc_argmax.argtypes = [P, I64, I64, P]
+        lib.orc_reference_f64.argtypes = [I, P, P, I64, I64, P, P, P, P, I64, P, P, I]
+        lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
+        lib.orc_half_to_float.restype = ctypes.c_float
+        for name in ("orc_quantize", "orc_block_dots", "orc_gemv", "orc_split_bounds",
+                     "orc_gemv_split", "orc_combine", "orc_argmax", "orc_reference_f64"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def default_threads() -> int:
+    return 1
+
+
+def half_to_float(bits: int) -> float:
+    return float(_load().orc_half_to_float(int(bits)))
+
+
+def quantize(mode: int, x: np.ndarray):
+    x = _c(np.atleast_2d(x), np.float32)
+    B, K = x.shape
+    xq = np.empty((B, K), np.int8)
+    xl = np.empty((B, K), np.int8) if mode == TWOPASS else None
+    xs = np.empty((B, K // QK), np.float32)
+    _check(_load().orc_quantize(mode, _p(x), B, K, _p(xq), _p(xl), _p(xs)), "quantize")
+    return xq, xl, xs
+
+
+def block_dots(mode: int, wq: np.ndarray, xq: np.ndarray, xl: np.ndarray | None = None):
+    wq = _c(wq, np.int8)
+    xq = _c(np.atleast_2d(xq), np.int8)
+    xl = _c(None if xl is None else np.atleast_2d(xl), np.int8)
+    N, K = wq.shape
+    B = xq.shape[0]
+    dh = np.empty((B, N, K // QK), np.int32)
+    dl = np.empty((B, N, K // QK), np.int32) if mode == TWOPASS else None
+    _check(_load().orc_block_dots(mode, _p(wq), N, K, _p(xq), _p(xl), B, _p(dh), _p(dl)), "block_dots")
+    return dh, dl
+
+
+def _gemv_args(wq, ws, x, xq, xl, xs):
+    wq = _c(wq, np.int8)
+    ws = _c(ws, np.uint16)
+    N, K = wq.shape
+    x = _c(None if x is None else np.atleast_2d(x), np.float32)
+    xq = _c(None if xq is None else np.atleast_2d(xq), np.int8)
+    xl = _c(None if xl is None else np.atleast_2d(xl), np.int8)
+    xs = _c(None if xs is None else np.atleast_2d(xs), np.float32)
+    B = (x if x is not None else xq).shape[0]
+    return wq, ws, N, K, x, xq, xl, xs, B
+
+
+def gemv(mode, wq, ws, x=None, xq=None, xl=None, xs=None, nthreads: int = 1):
+    wq, ws, N, K, x, xq, xl, xs, B = _gemv_args(wq, ws, x, xq, xl, xs)
+    y = np.empty((B, N), np.float32)
+    _check(_load().orc_gemv(mode, _p(wq), _p(ws), N, K, _p(x), _p(xq), _p(xl), _p(xs), B, _p(y),
+                            int(nthreads)), "gemv")
+    return y
+
+
+def split_bounds(K: int, S: int) -> np.ndarray:
+    first = np.empty(S + 1, np.int32)
+    _check(_load().orc_split_bounds(K, S, _p(first)), "split_bounds")
+    return first
+
+
+def gemv_split(mode, wq, ws, xq, xl, xs, S: int, nthreads: int = 1):
+    wq, ws, N, K, _, xq, xl, xs, B = _gemv_args(wq, ws, None, xq, xl, xs)
+    part = np.empty((S, B, N), np.float32)
+    _check(_load().orc_gemv_split(mode, _p(wq), _p(ws), N, K, _p(xq), _p(xl), _p(xs), B, S, _p(part),
+                                  int(nthreads)), "gemv_split")
+    return part
+
+
+def combine(part: np.ndarray) -> np.ndarray:
+    part = _c(part, np.float32)
+    S, B, N = part.shape
+    y = np.empty((B, N), np.float32)
+    _check(_load().orc_combine(_p(part), S, B, N, _p(y)), "combine")
+    return y
+
+
+def argmax(y: np.ndarray) -> np.ndarray:
+    y = _c(np.atleast_2d(y), np.float32)
+    B, N = y.shape
+    idx = np.empty(B, np.int32)
+    _check(_load().orc_argmax(_p(y), B, N, _p(idx)), "argmax")
+    return idx
+
+
+def reference_f64(mode, wq, ws, x=None, xq=None, xl=None, xs=None, nthreads: int = 1):
+    wq, ws, N, K, x, xq, xl, xs, B = _gemv_args(wq, ws, x, xq, xl, xs)
+    Y = np.empty((B, N), np.float64)
+    tn = np.empty((B, N), np.float64)
+    _check(_load().orc_reference_f64(mode, _p(wq), _p(ws), N, K, _p(x), _p(xq), _p(xl), _p(xs), B,
+                                     _p(Y), _p(tn), int(nthreads)), "reference_f64")
+    return Y, tn
+
+
+def within_tolerance(y: np.ndarray, Y: np.ndarray, tnorm: np.ndarray, rel: float = 1e-5) -> np.ndarray:
+    """The f32 criterion: ``|y - Y| <= rel * max(|Y|, ||t||_2)`` elementwise."""
+    y = np.asarray(y, np.float64)
+    return np.abs(y - Y) <= rel * np.maximum(np.abs(Y), tnorm)
