@@ -1,0 +1,171 @@
+/*
+ * qdg.h -- C ABI of the MI355X (gfx950) Q8_0 decode GEMV library, libqdg.so.
+ *
+ * The library computes the memory-bound matrix-vector product of LLM decode
+ * against a Q8_0 weight matrix, as the lane kernel library page
+ * ("logicaffeine_compile/codegen_cuda/lane/kernels.rs") defines it, with the
+ * split-K and combine of the "QWEN38_EXTRA_KERNELS" page and the first-index
+ * arg-max of the "model-as-a-kernel mak_cuda/megakernel.cu" page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers are HIP device memory the caller owns.
+ *    The library allocates nothing, keeps no pointer after it returns, and keeps
+ *    no state besides the thread-local error code of qdg_last_hip_error().
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *    runs asynchronously; nothing synchronises.
+ *  - Every argument is checked before anything is enqueued.  A negative status
+ *    means nothing was enqueued, except QDG_EHIP, which reports that the HIP
+ *    runtime refused a launch (qdg_last_hip_error() holds its hipError_t).
+ *  - The same inputs give the same output bits on every call: every sum runs in
+ *    a fixed order, no result depends on workgroup scheduling, and no floating
+ *    point atomics are used.
+ *  - Layouts are row-major and dense.  K is a multiple of 32.  wq, xq, xl and x
+ *    must be 16-byte aligned; ws 2-byte; xs, y, out, partials and idx 4-byte;
+ *    the arg-max workspace 8-byte.
+ *
+ * Data (lane kernel library page: module doc, lk_w; QWEN38 page: split-K)
+ *   wq  int8     [N][K]        weight values
+ *   ws  binary16 [N][K/32]     one weight scale per 32 values (bit patterns)
+ *   x   float    [B][K]        activation (Dequant mode)
+ *   xq  int8     [B][K]        activation words (high words under TwoPass)
+ *   xl  int8     [B][K]        TwoPass low words
+ *   xs  float    [B][K/32]     activation scale per 32 values
+ *   y   float    [B][N]        output
+ *   partials float [S][B][N]   split-K partial sums, chunk-major
+ */
+#ifndef QDG_H
+#define QDG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDG_ABI_VERSION 1
+
+/* Numerics modes (lane kernel library page, mode()). */
+enum {
+    QDG_DEQUANT = 0, /* f32 activation, weight scaled in the kernel, binary64 sums  */
+    QDG_INT8ACT = 1, /* activation quantized per 32-block, int8 dots, f32 sums      */
+    QDG_TWOPASS = 2  /* high and low int8 words of the activation, f32 sums         */
+};
+
+/* Status codes.  0 is success; every failure is negative. */
+enum {
+    QDG_OK = 0,
+    QDG_EINVAL = -1,     /* NULL where a pointer is required, or an unknown mode     */
+    QDG_ESHAPE = -2,     /* K not a positive multiple of 32, N or B out of range     */
+    QDG_EALIGN = -3,     /* a pointer breaks the alignment rule above               */
+    QDG_EMODE = -4,      /* the mode does not support this B / splits combination   */
+    QDG_EWORKSPACE = -5, /* the arg-max workspace is too small                      */
+    QDG_EHIP = -6        /* the HIP runtime refused a launch                        */
+};
+
+/* Limits. */
+#define QDG_MAX_B 16        /* activation rows per call                              */
+#define QDG_MAX_SPLITS 64   /* split-K chunks                                        */
+
+typedef void *qdg_stream; /* a hipStream_t */
+
+/* QDG_ABI_VERSION of the built library. */
+int qdg_abi_version(void);
+
+/* A static, human-readable name of a status code (never NULL). */
+const char *qdg_status_str(int status);
+
+/* The hipError_t behind the calling thread's last QDG_EHIP (0 if none). */
+int qdg_last_hip_error(void);
+
+/*
+ * Quantize B activation rows of K values (lane kernel library page: module doc
+ * on the activation quantizer, lk_quant_lane, lk_two_scale, lk_two_words, kernel
+ * lk_quant).  Per 32-value block with a = max|x|:
+ *   QDG_INT8ACT: s = a > 0 ? a/127 : 1; xq = round(x/s)
+ *   QDG_TWOPASS: s = max(a, 1e-30)/127; xq = clamp(round(x/s)); r = fma(-xq, s, x)
+ *                (one rounding); xl = clamp(round(r / (s/128)))
+ * round is to nearest, ties to even; division is IEEE; clamps are to [-128, 127]
+ * (the Int8Act word never reaches them for a block whose scale is a normal
+ * float).  xs[t][g] = s.  xl must be NULL for QDG_INT8ACT.  Inputs: device
+ * x [B][K]; outputs: device xq, xl [B][K], xs [B][K/32].  B >= 1 (rows are
+ * independent), K >= 32 and a multiple of 32, B*K < 2^62.  Values outside the
+ * contract (NaN, Inf, blocks with 0 < a < 1e-30 under Int8Act) give unspecified
+ * words but never fault.
+ */
+int qdg_quantize_act(int mode, const float *x, int64_t B, int64_t K,
+                     int8_t *xq, int8_t *xl, float *xs, qdg_stream stream);
+
+/*
+ * Y[t][o] = sum_k X[t][k] * W[o][k] for a Q8_0 matrix W of N rows of K values
+ * (lane kernel library page: lk_gemv_q8, lk_q8_rows_dot, lk_q8_term, lk_q8_sum4;
+ * QWEN38 page: gk_gemv_hl_sk for splits > 1).
+ *
+ *  QDG_DEQUANT  reads x (xq, xl, xs must be NULL); every product and sum in
+ *               binary64, rounded once to binary32.  B == 1, splits == 1.
+ *  QDG_INT8ACT  reads xq, xs.  TwoPass reads xq, xl, xs.  Block g's step is
+ *  QDG_TWOPASS  p <- fma(a, b, p) with a = fl(sigma*s), b = D (Int8Act) or
+ *               a = sigma, b = fma(s, D, fl(fl(s/128)*E)) (TwoPass), D and E the
+ *               exact int32 block dots; step g goes into partial g mod 4, each
+ *               partial takes its blocks in ascending order from +0, and the
+ *               result is (P0 + P2) + (P1 + P3).  1 <= B <= QDG_MAX_B (B > 1
+ *               runs on int8 MFMA and sums every row exactly as B == 1 does).
+ *
+ * splits == 1: out is y [B][N].  splits > 1 (quantized modes): out is
+ * partials [splits][B][N]; chunk s covers the blocks the QWEN38 page's chunk
+ * rule gives (qdg_split_bounds) and sums them in the same order as a whole row;
+ * reduce with qdg_sk_combine.  1 <= splits <= QDG_MAX_SPLITS.
+ * All array arguments are device pointers; N >= 1, K >= 32 and a multiple of 32,
+ * N*K < 2^62.
+ */
+int qdg_gemv_q8(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                const float *x, const int8_t *xq, const int8_t *xl, const float *xs,
+                int64_t B, int splits, float *out, qdg_stream stream);
+
+/*
+ * y[t][o] = sum over s = 0..splits-1, ascending, starting from 0.0f, of
+ * partials[s][t][o] (QWEN38 page, gk_sk_combine): one binary32 addition per
+ * chunk, no atomics.  Device pointers; partials [splits][B][N], y [B][N].
+ */
+int qdg_sk_combine(const float *partials, int splits, int64_t B, int64_t N, float *y,
+                   qdg_stream stream);
+
+/* Bytes of device workspace qdg_argmax needs for B rows of N values. */
+size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N);
+
+/*
+ * idx[t] = the smallest i with y[t][i] equal to the row's maximum (lane kernel
+ * library page, module doc: first of equal maxima; megakernel page: amax_key,
+ * ph_argmax_part, ph_argmax_fin).  Values compare as IEEE floats (-0 equals +0);
+ * NaN is outside the contract.  Device pointers: y [B][N], idx int32 [B],
+ * workspace of at least qdg_argmax_workspace_bytes(B, N) bytes (contents on
+ * entry ignored, on return unspecified).  1 <= B, 1 <= N < 2^31.
+ */
+int qdg_argmax(const float *y, int64_t B, int64_t N, int32_t *idx,
+               void *workspace, size_t workspace_bytes, qdg_stream stream);
+
+/*
+ * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
+ * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,
+ * under QDG_TWOPASS, dl[t][o][g] with xl (dl must be NULL for QDG_INT8ACT).
+ * Device pointers; dh, dl int32 [B][N][K/32]; B in [1, QDG_MAX_B].
+ */
+int qdg_block_dots(int mode, const int8_t *wq, int64_t N, int64_t K,
+                   const int8_t *xq, const int8_t *xl, int64_t B,
+                   int32_t *dh, int32_t *dl, qdg_stream stream);
+
+/*
+ * Host only: the split-K chunk boundaries in 32-value blocks (QWEN38 page,
+ * gk_gemv_hl_sk): K runs in 512-value superblocks, per = ceil((K/512)/splits),
+ * chunk s takes superblocks [s*per, min((s+1)*per, K/512)) and the last chunk
+ * also takes the K mod 512 tail.  first_block (host, splits + 1 entries)
+ * receives the boundaries: chunk s is blocks [first_block[s], first_block[s+1]).
+ */
+int qdg_split_bounds(int64_t K, int splits, int32_t *first_block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDG_H */

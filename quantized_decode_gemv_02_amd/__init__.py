@@ -1,0 +1,227 @@
+"""Python binding of libqdg.so, the MI355X (gfx950) Q8_0 decode GEMV library.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current HIP stream.  The
+functions carry the names of the C entry points in ``include/qdg.h`` without the
+``qdg_`` prefix:
+
+* ``quantize_act(mode, x, xq, xl, xs)``
+* ``gemv_q8(mode, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits=1)``
+* ``sk_combine(partials, y)``
+* ``argmax(y, idx, workspace)`` / ``argmax_workspace_bytes(B, N)``
+* ``block_dots(mode, wq, xq, xl, dh, dl)``
+* ``split_bounds(K, splits)`` (host only)
+
+Every array is a contiguous torch tensor on the GPU (except ``split_bounds``),
+with the dtypes of the header: int8 weights/words, int16-viewed binary16 weight
+scales (``torch.float16`` tensors are accepted and reinterpreted), float32
+activations, scales and outputs.  A non-zero status raises ``QdgError``.  If
+``libqdg.so`` is missing, importing this package raises ``ImportError``: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+DEQUANT, INT8ACT, TWOPASS = 0, 1, 2
+QK = 32
+MAX_B = 16
+MAX_SPLITS = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqdg.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python quantized_decode_gemv_02_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+_SIGS = {
+    "qdg_abi_version": ([], _I),
+    "qdg_status_str": ([_I], ctypes.c_char_p),
+    "qdg_last_hip_error": ([], _I),
+    "qdg_quantize_act": ([_I, _P, _I64, _I64, _P, _P, _P, _P], _I),
+    "qdg_gemv_q8": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _I, _P, _P], _I),
+    "qdg_sk_combine": ([_P, _I, _I64, _I64, _P, _P], _I),
+    "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "qdg_argmax": ([_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P], _I),
+    "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
+    "qdg_split_bounds": ([_I64, _I, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+class QdgError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.qdg_status_str(status).decode()
+        if status == -6:
+            msg += f" (hipError_t {_lib.qdg_last_hip_error()})"
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise QdgError(fn, status)
+
+
+def abi_version() -> int:
+    return _lib.qdg_abi_version()
+
+
+def status_str(status: int) -> str:
+    return _lib.qdg_status_str(status).decode()
+
+
+def raw():
+    """The ctypes handle of libqdg.so (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in dtype:
+        raise TypeError(f"{name} must have dtype in {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i8():
+    return (_torch().int8,)
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def _scales():
+    torch = _torch()
+    return (torch.int16, torch.float16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16, torch.float16)
+
+
+def quantize_act(mode: int, x, xq, xl, xs) -> None:
+    """``x [B][K]`` float32 -> ``xq`` (and ``xl`` under TwoPass) int8 ``[B][K]``, ``xs [B][K/32]``."""
+    B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    _check("qdg_quantize_act", _lib.qdg_quantize_act(
+        mode, _ptr(x, _f32(), "x"), B, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
+        _stream()))
+
+
+def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: int = 1) -> None:
+    """``out = Y [B][N]`` (``splits == 1``) or the partials ``[splits][B][N]``."""
+    N, K = wq.shape
+    act = x if mode == DEQUANT else xq
+    B = act.shape[0] if act.dim() == 2 else 1
+    _check("qdg_gemv_q8", _lib.qdg_gemv_q8(
+        mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"),
+        _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), B, int(splits),
+        _ptr(out, _f32(), "out"), _stream()))
+
+
+def sk_combine(partials, y) -> None:
+    """``y [B][N]`` = ascending sum over the leading axis of ``partials [S][B][N]``."""
+    S = partials.shape[0]
+    N = partials.shape[-1]
+    B = partials.numel() // (S * N)
+    _check("qdg_sk_combine", _lib.qdg_sk_combine(_ptr(partials, _f32(), "partials"), S, B, N,
+                                                 _ptr(y, _f32(), "y"), _stream()))
+
+
+def argmax_workspace_bytes(B: int, N: int) -> int:
+    return int(_lib.qdg_argmax_workspace_bytes(B, N))
+
+
+def argmax(y, idx, workspace) -> None:
+    """``idx [B]`` int32 = first index of each row's maximum of ``y [B][N]``."""
+    B, N = (y.shape if y.dim() == 2 else (1, y.shape[0]))
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("qdg_argmax", _lib.qdg_argmax(_ptr(y, _f32(), "y"), B, N, _ptr(idx, (_torch().int32,), "idx"),
+                                         _ptr(workspace, None, "workspace"), nbytes, _stream()))
+
+
+def block_dots(mode: int, wq, xq, xl, dh, dl) -> None:
+    """Exact int32 per-block dots ``dh``/``dl [B][N][K/32]`` (test hook)."""
+    N, K = wq.shape
+    B = xq.shape[0] if xq.dim() == 2 else 1
+    i32 = (_torch().int32,)
+    _check("qdg_block_dots", _lib.qdg_block_dots(
+        mode, _ptr(wq, _i8(), "wq"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), B,
+        _ptr(dh, i32, "dh"), _ptr(dl, i32, "dl"), _stream()))
+
+
+def split_bounds(K: int, splits: int) -> list[int]:
+    arr = (ctypes.c_int32 * (splits + 1))()
+    _check("qdg_split_bounds", _lib.qdg_split_bounds(K, splits, ctypes.cast(arr, ctypes.c_void_p)))
+    return list(arr)
+
+
+class Bound:
+    """A C entry point with its ctypes arguments converted once (pointers, sizes,
+    stream), for loops that launch the same call many times.  Calling it checks
+    the status like the functions above."""
+
+    def __init__(self, name: str, *args):
+        self.name = name
+        self.fn = getattr(_lib, name)
+        self.args = tuple(self._conv(a) for a in args)
+
+    @staticmethod
+    def _conv(a):
+        if a is None or isinstance(a, (int, ctypes.c_void_p)):
+            return a
+        if hasattr(a, "data_ptr"):
+            return ctypes.c_void_p(a.data_ptr())
+        return a
+
+    def __call__(self) -> None:
+        _check(self.name, self.fn(*self.args))
+
+
+def bind_gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: int = 1) -> Bound:
+    N, K = wq.shape
+    act = x if mode == DEQUANT else xq
+    B = act.shape[0] if act.dim() == 2 else 1
+    for t, n in ((wq, "wq"), (ws, "ws"), (out, "out"), (x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    return Bound("qdg_gemv_q8", mode, wq, ws, N, K, x, xq, xl, xs, B, int(splits), out, _stream())
+
+
+def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:
+    B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    for t, n in ((x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    return Bound("qdg_quantize_act", mode, x, B, K, xq, xl, xs, _stream())
+
+
+def bind_sk_combine(partials, y) -> Bound:
+    S, N = partials.shape[0], partials.shape[-1]
+    B = partials.numel() // (S * N)
+    _ptr(partials, None, "partials")
+    _ptr(y, None, "y")
+    return Bound("qdg_sk_combine", partials, S, B, N, y, _stream())

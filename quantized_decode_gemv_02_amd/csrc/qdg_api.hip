@@ -1,0 +1,136 @@
+// qdg_api.hip -- the C ABI of libqdg.so (include/qdg.h): argument checks, then
+// dispatch to the gfx950 kernels.  Nothing is enqueued unless every check passes.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/qdg.h"
+#include "qdg_device.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool shape_ok(int64_t rows, int64_t K) {
+  if (rows < 1 || K < qdg::QK || K % qdg::QK) return false;
+  if (K > ((int64_t)1 << 31) || rows > ((int64_t)1 << 40)) return false;
+  return rows <= (((int64_t)1 << 62) / K);
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QDG_OK;
+  g_last_hip_error = (int)e;
+  return QDG_EHIP;
+}
+
+hipStream_t as_stream(qdg_stream s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+int qdg_abi_version(void) { return QDG_ABI_VERSION; }
+
+const char* qdg_status_str(int status) {
+  switch (status) {
+    case QDG_OK: return "ok";
+    case QDG_EINVAL: return "invalid argument (null pointer or unknown mode)";
+    case QDG_ESHAPE: return "shape out of range (K must be a positive multiple of 32)";
+    case QDG_EALIGN: return "misaligned pointer";
+    case QDG_EMODE: return "mode does not support this batch / split combination";
+    case QDG_EWORKSPACE: return "workspace too small";
+    case QDG_EHIP: return "HIP launch failed (see qdg_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int qdg_last_hip_error(void) { return g_last_hip_error; }
+
+int qdg_quantize_act(int mode, const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs,
+                     qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!x || !xq || !xs) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!shape_ok(B, K)) return QDG_ESHAPE;
+  if ((B * K / qdg::QK) * 8 / 256 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4)) return QDG_EALIGN;
+  return hip_status(qdg::launch_quantize(mode, x, B * K / qdg::QK, xq, xl, xs, as_stream(stream)));
+}
+
+int qdg_gemv_q8(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, int splits, float* out,
+                qdg_stream stream) {
+  if (mode < QDG_DEQUANT || mode > QDG_TWOPASS) return QDG_EINVAL;
+  if (!wq || !ws || !out) return QDG_EINVAL;
+  if (mode == QDG_DEQUANT && (!x || xq || xl || xs)) return QDG_EINVAL;
+  if (mode != QDG_DEQUANT && (x || !xq || !xs)) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!shape_ok(N, K)) return QDG_ESHAPE;
+  if (B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(out, 4)) return QDG_EALIGN;
+  if (x && !aligned(x, 16)) return QDG_EALIGN;
+  if (xq && !aligned(xq, 16)) return QDG_EALIGN;
+  if (xl && !aligned(xl, 16)) return QDG_EALIGN;
+  if (xs && !aligned(xs, 4)) return QDG_EALIGN;
+  if (mode == QDG_DEQUANT && (B != 1 || splits != 1)) return QDG_EMODE;
+  const hipStream_t st = as_stream(stream);
+  if (mode == QDG_DEQUANT) return hip_status(qdg::launch_gemv_dequant(wq, ws, N, K, x, out, st));
+  if (B == 1) return hip_status(qdg::launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, splits, out, st));
+  return hip_status(qdg::launch_gemv_mfma(mode, wq, ws, N, K, xq, xl, xs, B, splits, out, st));
+}
+
+int qdg_sk_combine(const float* partials, int splits, int64_t B, int64_t N, float* y, qdg_stream stream) {
+  if (!partials || !y) return QDG_EINVAL;
+  if (splits < 1 || splits > QDG_MAX_SPLITS || B < 1 || N < 1) return QDG_ESHAPE;
+  if (B > ((int64_t)1 << 40) / N) return QDG_ESHAPE;
+  if (!aligned(partials, 4) || !aligned(y, 4)) return QDG_EALIGN;
+  return hip_status(qdg::launch_combine(partials, splits, B * N, y, as_stream(stream)));
+}
+
+size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
+  if (B < 1 || N < 1) return 0;
+  return (size_t)B * (size_t)qdg::argmax_groups(N) * sizeof(unsigned long long);
+}
+
+int qdg_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, void* workspace, size_t workspace_bytes,
+               qdg_stream stream) {
+  if (!y || !idx || !workspace) return QDG_EINVAL;
+  if (B < 1 || B > 65535 || N < 1 || N >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(y, 4) || !aligned(idx, 4) || !aligned(workspace, 8)) return QDG_EALIGN;
+  if (workspace_bytes < qdg_argmax_workspace_bytes(B, N)) return QDG_EWORKSPACE;
+  return hip_status(
+      qdg::launch_argmax(y, B, N, idx, (unsigned long long*)workspace, as_stream(stream)));
+}
+
+int qdg_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                   int64_t B, int32_t* dh, int32_t* dl, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!wq || !xq || !dh) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && (!xl || !dl)) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && (xl || dl)) return QDG_EINVAL;
+  if (!shape_ok(N, K) || N > 65535 || B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
+  if (!aligned(wq, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(dh, 4) ||
+      (dl && !aligned(dl, 4)))
+    return QDG_EALIGN;
+  return hip_status(qdg::launch_block_dots(mode, wq, N, K, xq, xl, B, dh, dl, as_stream(stream)));
+}
+
+int qdg_split_bounds(int64_t K, int splits, int32_t* first_block) {
+  if (!first_block) return QDG_EINVAL;
+  if (K < qdg::QK || K % qdg::QK || K > ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  for (int s = 0; s < splits; ++s) {
+    int32_t g0, g1;
+    qdg::split_range(K, splits, s, g0, g1);
+    first_block[s] = g0;
+  }
+  first_block[splits] = (int32_t)(K / qdg::QK);
+  return QDG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// qdg_device.h -- device helpers and launcher declarations shared by the gfx950
+// kernels of libqdg.so (internal; the public interface is include/qdg.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace qdg {
+
+constexpr int QK = 32;          // values per Q8_0 block
+constexpr int SUPER = 16;       // blocks per 512-value superblock of the split-K chunk rule
+
+// The split-K chunk rule of the QWEN38 page (gk_gemv_hl_sk): 512-value
+// superblocks, per = ceil(nq/S), chunk s = superblocks [s*per, min((s+1)*per, nq)),
+// the K mod 512 tail in the last chunk.  Returned as 32-value block bounds.
+__host__ __device__ inline void split_range(int64_t K, int S, int s, int32_t& g0, int32_t& g1) {
+  const int64_t nq = K / 512, nb = K / QK, per = (nq + S - 1) / S;
+  int64_t q0 = (int64_t)s * per;
+  if (q0 > nq) q0 = nq;
+  int64_t q1 = (int64_t)(s + 1) * per;
+  if (q1 > nq) q1 = nq;
+  g0 = (int32_t)(q0 * SUPER);
+  g1 = (s == S - 1) ? (int32_t)nb : (int32_t)(q1 * SUPER);
+}
+
+// DPP lane moves (GFX9 encodings).  A lane whose source lies outside its
+// 16-lane row reads 0; callers only consume lanes whose source is inside.
+enum : int {
+  DPP_QUAD_SWAP1 = 0xB1,  // quad_perm [1,0,3,2]: lane i <- lane i^1
+  DPP_ROW_SHL2 = 0x102,   // lane i <- lane i+2 within the row
+  DPP_ROW_SHL4 = 0x104,   // lane i <- lane i+4 within the row
+  DPP_ROW_SHL8 = 0x108,   // lane i <- lane i+8 within the row
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL>((int)(b & 0xffffffffll));
+  const int hi = dpp_i32<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// Exact int32 dot of 16 int8 pairs held in one lane (four v_dot4 steps).
+__device__ __forceinline__ int dot16_i8(int4 w, int4 a) {
+  int d = __builtin_amdgcn_sdot4(w.x, a.x, 0, false);
+  d = __builtin_amdgcn_sdot4(w.y, a.y, d, false);
+  d = __builtin_amdgcn_sdot4(w.z, a.z, d, false);
+  d = __builtin_amdgcn_sdot4(w.w, a.w, d, false);
+  return d;
+}
+
+// A 32-value block's exact int32 dot, the block split over the lane pair
+// (2j, 2j+1) with 16 values each: both lanes return the block's dot.
+__device__ __forceinline__ int block_dot_pair(int4 w, int4 a) {
+  const int d = dot16_i8(w, a);
+  return d + dpp_i32<DPP_QUAD_SWAP1>(d);
+}
+
+__device__ __forceinline__ float half_bits_to_float(unsigned short h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+// One quantized step's factors (lane kernel library page, lk_q8_term):
+// Int8Act a = fl(sigma*s), b = D; TwoPass a = sigma, b = fma(s, D, fl(fl(s/128)*E)).
+template <int MODE>
+__device__ __forceinline__ void q8_term(float sigma, float s, int d, int e, float& a, float& b) {
+  if constexpr (MODE == 1) {
+    a = __fmul_rn(sigma, s);
+    b = (float)d;
+  } else {
+    const float lo = __fmul_rn(__fmul_rn(s, 0.0078125f), (float)e);
+    a = sigma;
+    b = __fmaf_rn(s, (float)d, lo);
+  }
+}
+
+}  // namespace qdg
+
+// Launchers (one translation unit each); all return the launch's hipError_t.
+namespace qdg {
+hipError_t launch_quantize(int mode, const float* x, int64_t nblocks, int8_t* xq, int8_t* xl, float* xs,
+                           hipStream_t st);
+hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                            const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* out,
+                            hipStream_t st);
+hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                               float* out, hipStream_t st);
+hipError_t launch_gemv_mfma(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                            const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, int splits,
+                            float* out, hipStream_t st);
+hipError_t launch_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq,
+                             const int8_t* xl, int64_t B, int32_t* dh, int32_t* dl, hipStream_t st);
+hipError_t launch_combine(const float* part, int splits, int64_t count, float* y, hipStream_t st);
+int argmax_groups(int64_t N);
+hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
+                         hipStream_t st);
+}  // namespace qdg

@@ -1,0 +1,194 @@
+// qdg_gemv.hip -- the batch-1 Q8_0 GEMV under the quantized numerics (Int8Act,
+// TwoPass), with split-K partials; the lane kernel library page's lk_gemv_q8 /
+// lk_q8_rows_dot / lk_q8_term / lk_q8_sum4, and the QWEN38 page's gk_gemv_hl_sk.
+//
+// What is summed, and in which order, is the page's: block g's step
+// p <- fma(a, b, p) goes into partial g mod 4, each partial takes its blocks in
+// ascending order starting from +0, and the row is (P0 + P2) + (P1 + P3).  How
+// the work maps onto gfx950 is this file's own:
+//
+//  * A wave64 takes RPW rows at once; each row gets LPR = 64/RPW lanes, a lane
+//    pair per 32-value block, so one step of a wave reads LPR*16 contiguous bytes
+//    of each of its rows (whole 128-byte lines) with one 16-byte load per lane.
+//  * A step covers BPS = LPR/2 consecutive blocks of a row.  Blocks are read in
+//    groups of 4 that start at a multiple of 4, so block j of a step belongs to
+//    partial j mod 4.  Lanes (2q, 2q+1) of a row own partial q for the whole
+//    row: they fold their own block (j = q) and, when BPS = 8, the block j = q+4
+//    that the lanes 8 to the right hold (one DPP row shift), in that order.  The
+//    chain of every partial therefore stays in one lane pair, in ascending block
+//    order, with no reduction tree at all; the pair's lanes hold equal values.
+//  * The activation window (int8 words, TwoPass low words, scales) of the
+//    workgroup's K-chunk is staged once in LDS and read with ds_read_b128.
+//  * U steps of weight loads are issued ahead of the steps being computed, so
+//    each wave keeps up to 2*U*1 KB of weights in flight.
+//  * grid = (row tiles, splits): the split s of a row covers the QWEN38 chunk
+//    [g0, g1) and writes partial[s][o]; an empty chunk writes +0.
+#include <stdlib.h>
+
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+constexpr int WG = 256;              // four waves
+constexpr int LDS_BUDGET = 56 * 1024;  // activation window bytes per workgroup
+
+template <int MODE>
+constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4; }
+
+template <int MODE, int RPW, int U>
+__global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+                                                 const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                 const float* __restrict__ xs, int64_t N, int64_t K, int S,
+                                                 int win, float* __restrict__ out) {
+  constexpr int LPR = 64 / RPW;  // lanes per row
+  constexpr int BPS = LPR / 2;   // blocks per step of a row
+  constexpr int TPP = BPS / 4;   // steps of one partial per step (1 or 2)
+  static_assert(TPP == 1 || TPP == 2, "RPW must be 4 or 8");
+  extern __shared__ __align__(16) unsigned char lds[];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
+  const int64_t nb = K / QK;
+  const int s_idx = blockIdx.y;
+  int32_t g0, g1;
+  split_range(K, S, s_idx, g0, g1);
+
+  const int64_t o = ((int64_t)blockIdx.x * (WG / 64) + wave) * RPW + r;
+  const bool row_ok = o < N;
+  const int64_t orow = row_ok ? o : N - 1;
+  const int8_t* wrow = wq + orow * K + hf * 16;
+  const uint16_t* srow = ws + orow * nb;
+
+  int8_t* lq = (int8_t*)lds;
+  int8_t* ll = lq + (int64_t)win * QK;
+  float* lsx = (float*)(lds + (int64_t)win * (MODE == 2 ? 2 : 1) * QK);
+
+  float p = 0.0f;  // this lane pair's partial (j < 4)
+  for (int wb0 = g0; wb0 < g1; wb0 += win) {
+    const int wb1 = min(wb0 + win, g1);
+    const int nwb = wb1 - wb0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nwb * 2; i += WG) {
+      ((int4*)lq)[i] = ((const int4*)(xq + (int64_t)wb0 * QK))[i];
+      if constexpr (MODE == 2) ((int4*)ll)[i] = ((const int4*)(xl + (int64_t)wb0 * QK))[i];
+    }
+    for (int i = threadIdx.x; i < nwb; i += WG) lsx[i] = xs[wb0 + i];
+    __syncthreads();
+
+    const int nsteps = (nwb + BPS - 1) / BPS;
+    const int ngroups = (nsteps + U - 1) / U;
+    int4 wcur[U];
+    unsigned short scur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = wb0 + u * BPS + j;
+      wcur[u] = b < wb1 ? *(const int4*)(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+      scur[u] = b < wb1 ? srow[b] : (unsigned short)0;
+    }
+    for (int gi = 0; gi < ngroups; ++gi) {
+      int4 wnxt[U];
+      unsigned short snxt[U];
+      const bool more = gi + 1 < ngroups;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = wb0 + ((gi + 1) * U + u) * BPS + j;
+        const bool ok = more && b < wb1;
+        wnxt[u] = ok ? *(const int4*)(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+        snxt[u] = ok ? srow[b] : (unsigned short)0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int bl = (gi * U + u) * BPS + j;  // block within the window
+        const bool ok = bl < nwb;
+        const int blc = ok ? bl : 0;
+        const int4 a = *(const int4*)(lq + blc * QK + hf * 16);
+        const int d = block_dot_pair(wcur[u], a);
+        int e = 0;
+        if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
+        float ta, tb;
+        q8_term<MODE>(half_bits_to_float(scur[u]), lsx[blc], d, e, ta, tb);
+        p = ok ? __fmaf_rn(ta, tb, p) : p;
+        if constexpr (TPP == 2) {
+          const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
+          p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        wcur[u] = wnxt[u];
+        scur[u] = snxt[u];
+      }
+    }
+  }
+  // (P0 + P2) + (P1 + P3): partial q sits in lane 2q of the row.
+  const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
+  const float y = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+  if (li == 0 && row_ok) out[(int64_t)s_idx * N + o] = y;
+}
+
+struct Tuning {
+  int rpw = 4;
+  int unroll = 4;
+};
+
+// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8}); they
+// change the lane layout and load depth only, never the arithmetic or its order.
+Tuning tuning() {
+  static Tuning t = [] {
+    Tuning v;
+    if (const char* e = getenv("QDG_RPW")) v.rpw = atoi(e) == 8 ? 8 : 4;
+    if (const char* e = getenv("QDG_UNROLL")) {
+      const int u = atoi(e);
+      v.unroll = (u == 2 || u == 8) ? u : 4;
+    }
+    return v;
+  }();
+  return t;
+}
+
+template <int MODE, int RPW, int U>
+hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                    const int8_t* xl, const float* xs, int splits, float* out, hipStream_t st) {
+  int32_t mx = 0;
+  for (int s = 0; s < splits; ++s) {
+    int32_t g0, g1;
+    split_range(K, splits, s, g0, g1);
+    mx = g1 - g0 > mx ? g1 - g0 : mx;
+  }
+  const int cap = (LDS_BUDGET / window_bytes_per_block<MODE>()) / SUPER * SUPER;
+  int win = ((mx + SUPER - 1) / SUPER) * SUPER;
+  if (win > cap) win = cap;
+  if (win < SUPER) win = SUPER;
+  const size_t lds = (size_t)win * window_bytes_per_block<MODE>();
+  const int rows_per_wg = (WG / 64) * RPW;
+  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
+  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, splits,
+                     win, out);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                       const int8_t* xl, const float* xs, int splits, float* out, hipStream_t st) {
+  const Tuning t = tuning();
+  if (t.rpw == 8) {
+    if (t.unroll == 2) return launch_t<MODE, 8, 2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+    if (t.unroll == 8) return launch_t<MODE, 8, 8>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+    return launch_t<MODE, 8, 4>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  }
+  if (t.unroll == 2) return launch_t<MODE, 4, 2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  if (t.unroll == 8) return launch_t<MODE, 4, 8>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  return launch_t<MODE, 4, 4>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                            const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* out,
+                            hipStream_t st) {
+  if (mode == 1) return launch_mode<1>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  return launch_mode<2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+}
+
+}  // namespace qdg

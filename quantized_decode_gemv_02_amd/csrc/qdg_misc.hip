@@ -1,0 +1,144 @@
+// qdg_misc.hip -- the fixed-order split-K combine, the first-index arg-max, and
+// the per-block dot test hook.
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+// QWEN38 page, gk_sk_combine: y = ((0 + P0) + P1) + ... + P(S-1), one binary32
+// addition per chunk in ascending chunk order, no atomics.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int S, int64_t count,
+                                                float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float a = 0.0f;
+  for (int s = 0; s < S; ++s) a = __fadd_rn(a, part[(int64_t)s * count + i]);
+  y[i] = a;
+}
+
+// Arg-max keys (megakernel page, amax_key): the float's bits mapped to an
+// unsigned integer that orders as the floats do, above the complement of the
+// index, so the largest key is the largest value and, among equal values, the
+// smallest index.  -0 is folded onto +0 first so that the two compare equal as
+// IEEE floats do; the maximum of keys is order-free, which makes the result
+// independent of how the values are split over lanes and workgroups.
+__device__ __forceinline__ unsigned long long amax_key(float v, unsigned idx) {
+  unsigned u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(k, m, 64);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+constexpr int AM_THREADS = 256;
+constexpr int64_t AM_PER_GROUP = 2048;  // values per workgroup of the first stage
+constexpr int AM_MAX_GROUPS = 256;
+
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long k) {
+  __shared__ unsigned long long red[AM_THREADS / 64];
+  k = wave_max_u64(k);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+  __syncthreads();
+  unsigned long long m = red[0];
+#pragma unroll
+  for (int w = 1; w < AM_THREADS / 64; ++w) m = red[w] > m ? red[w] : m;
+  return m;
+}
+
+// Stage 1: workgroup g of row t reduces its contiguous slice of y[t] to one key.
+__global__ __launch_bounds__(AM_THREADS) void k_argmax_part(const float* __restrict__ y, int64_t N, int64_t per,
+                                                           unsigned long long* __restrict__ keys) {
+  const int g = blockIdx.x, t = blockIdx.y, G = gridDim.x;
+  const float* row = y + (int64_t)t * N;
+  const int64_t i0 = (int64_t)g * per;
+  const int64_t i1 = i0 + per < N ? i0 + per : N;
+  unsigned long long best = 0ull;  // below every key of a real value
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += AM_THREADS) {
+    const unsigned long long k = amax_key(row[i], (unsigned)i);
+    best = k > best ? k : best;
+  }
+  best = block_max_u64(best);
+  if (threadIdx.x == 0) keys[(int64_t)t * G + g] = best;
+}
+
+// Stage 2: one workgroup per row reduces the row's G keys and decodes the index.
+__global__ __launch_bounds__(AM_THREADS) void k_argmax_final(const unsigned long long* __restrict__ keys, int G,
+                                                            int32_t* __restrict__ idx) {
+  const int t = blockIdx.x;
+  unsigned long long best = 0ull;
+  for (int i = threadIdx.x; i < G; i += AM_THREADS) {
+    const unsigned long long k = keys[(int64_t)t * G + i];
+    best = k > best ? k : best;
+  }
+  best = block_max_u64(best);
+  if (threadIdx.x == 0) idx[t] = (int32_t)(0xffffffffu - (unsigned)(best & 0xffffffffull));
+}
+
+// Test hook: the exact per-block int32 dots through the GEMV's own block dot.
+// One wave per (32 blocks, row o, activation row t); lane pair j takes block j.
+__global__ __launch_bounds__(64) void k_block_dots(const int8_t* __restrict__ wq, int64_t N, int64_t K,
+                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                  int32_t* __restrict__ dh, int32_t* __restrict__ dl) {
+  const int lane = threadIdx.x, j = lane >> 1, hf = lane & 1;
+  const int64_t nb = K / QK;
+  const int64_t b = (int64_t)blockIdx.x * 32 + j;
+  const int64_t o = blockIdx.y, t = blockIdx.z;
+  const bool ok = b < nb;
+  int4 w = make_int4(0, 0, 0, 0), h = w, l = w;
+  if (ok) {
+    w = *(const int4*)(wq + o * K + b * QK + hf * 16);
+    h = *(const int4*)(xq + t * K + b * QK + hf * 16);
+    if (xl) l = *(const int4*)(xl + t * K + b * QK + hf * 16);
+  }
+  const int d = block_dot_pair(w, h);
+  const int e = block_dot_pair(w, l);
+  if (ok && hf == 0) {
+    dh[(t * N + o) * nb + b] = d;
+    if (dl) dl[(t * N + o) * nb + b] = e;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* part, int splits, int64_t count, float* y, hipStream_t st) {
+  const dim3 grid((unsigned)((count + 255) / 256)), block(256);
+  hipLaunchKernelGGL(k_combine, grid, block, 0, st, part, splits, count, y);
+  return hipGetLastError();
+}
+
+int argmax_groups(int64_t N) {
+  int64_t g = (N + AM_PER_GROUP - 1) / AM_PER_GROUP;
+  if (g < 1) g = 1;
+  if (g > AM_MAX_GROUPS) g = AM_MAX_GROUPS;
+  return (int)g;
+}
+
+hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
+                         hipStream_t st) {
+  const int G = argmax_groups(N);
+  const int64_t per = (N + G - 1) / G;
+  hipLaunchKernelGGL(k_argmax_part, dim3((unsigned)G, (unsigned)B), dim3(AM_THREADS), 0, st, y, N, per, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AM_THREADS), 0, st, ws, G, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq,
+                             const int8_t* xl, int64_t B, int32_t* dh, int32_t* dl, hipStream_t st) {
+  const int64_t nb = K / QK;
+  const dim3 grid((unsigned)((nb + 31) / 32), (unsigned)N, (unsigned)B), block(64);
+  hipLaunchKernelGGL(k_block_dots, grid, block, 0, st, wq, N, K, xq, mode == 2 ? xl : nullptr, dh,
+                     mode == 2 ? dl : nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace qdg

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status before it touches
+the HIP runtime.  The host-only chunk rule matches the oracle and the hand-derived
+boundaries."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+import quantized_decode_gemv_02_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qdg.h")
+
+OK, EINVAL, ESHAPE, EALIGN, EMODE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000  # a 64 KiB-aligned fake device address: every check passes on alignment
+lib = q.raw()
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(q.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert q.abi_version() == 1
+    for s in (OK, EINVAL, ESHAPE, EALIGN, EMODE, EWORKSPACE, EHIP, 12345):
+        assert isinstance(q.status_str(s), str) and q.status_str(s)
+
+
+def test_split_bounds_match_oracle_and_golden(golden_dir):
+    for c in json.load(open(os.path.join(golden_dir, "split_bounds.json")))["cases"]:
+        assert q.split_bounds(c["K"], c["S"]) == c["first"]
+    for K in (32, 480, 512, 544, 1600, 4096, 5120, 8192, 12288, 25600, 25632):
+        for S in (1, 2, 3, 4, 5, 7, 8, 16, 64):
+            assert q.split_bounds(K, S) == list(oracle.split_bounds(K, S)), (K, S)
+
+
+def gemv(mode=1, wq=A, ws=A, N=64, K=512, x=None, xq=A, xl=None, xs=A, B=1, S=1, out=A):
+    return lib.qdg_gemv_q8(mode, P(wq), P(ws), N, K, P(x), P(xq), P(xl), P(xs), B, S, P(out), None)
+
+
+def test_gemv_validation():
+    assert gemv(mode=3) == EINVAL
+    assert gemv(mode=-1) == EINVAL
+    assert gemv(wq=None) == EINVAL
+    assert gemv(out=None) == EINVAL
+    assert gemv(mode=0, x=None, xq=None, xs=None) == EINVAL      # Dequant needs x
+    assert gemv(mode=0, x=A) == EINVAL                           # ... and no quantized words
+    assert gemv(mode=1, x=A) == EINVAL
+    assert gemv(mode=2) == EINVAL                                # TwoPass needs xl
+    assert gemv(mode=1, xl=A) == EINVAL
+    assert gemv(K=33) == ESHAPE
+    assert gemv(K=0) == ESHAPE
+    assert gemv(K=16) == ESHAPE
+    assert gemv(N=0) == ESHAPE
+    assert gemv(B=0) == ESHAPE
+    assert gemv(B=17) == ESHAPE
+    assert gemv(S=0) == ESHAPE
+    assert gemv(S=65) == ESHAPE
+    assert gemv(wq=A + 8) == EALIGN
+    assert gemv(xq=A + 4) == EALIGN
+    assert gemv(ws=A + 1) == EALIGN
+    assert gemv(xs=A + 2) == EALIGN
+    assert gemv(out=A + 2) == EALIGN
+    assert gemv(mode=2, xl=A + 8) == EALIGN
+    assert gemv(mode=0, x=A, xq=None, xs=None, B=2) == EMODE
+    assert gemv(mode=0, x=A, xq=None, xs=None, S=2) == EMODE
+
+
+def test_quantize_validation():
+    f = lib.qdg_quantize_act
+    assert f(0, P(A), 1, 512, P(A), None, P(A), None) == EINVAL    # Dequant has no quantizer
+    assert f(1, None, 1, 512, P(A), None, P(A), None) == EINVAL
+    assert f(2, P(A), 1, 512, P(A), None, P(A), None) == EINVAL    # TwoPass needs xl
+    assert f(1, P(A), 1, 512, P(A), P(A), P(A), None) == EINVAL    # Int8Act takes no xl
+    assert f(1, P(A), 1, 500, P(A), None, P(A), None) == ESHAPE
+    assert f(1, P(A), 0, 512, P(A), None, P(A), None) == ESHAPE
+    assert f(1, P(A + 4), 1, 512, P(A), None, P(A), None) == EALIGN
+    assert f(1, P(A), 1, 512, P(A), None, P(A + 1), None) == EALIGN
+
+
+def test_combine_argmax_blockdots_validation():
+    assert lib.qdg_sk_combine(None, 2, 1, 8, P(A), None) == EINVAL
+    assert lib.qdg_sk_combine(P(A), 0, 1, 8, P(A), None) == ESHAPE
+    assert lib.qdg_sk_combine(P(A), 65, 1, 8, P(A), None) == ESHAPE
+    assert lib.qdg_sk_combine(P(A + 2), 2, 1, 8, P(A), None) == EALIGN
+    need = q.argmax_workspace_bytes(1, 151936)
+    assert need >= 8 and need % 8 == 0
+    assert q.argmax_workspace_bytes(0, 10) == 0
+    assert lib.qdg_argmax(P(A), 1, 151936, P(A), P(A), need - 8, None) == EWORKSPACE
+    assert lib.qdg_argmax(P(A), 1, 0, P(A), P(A), need, None) == ESHAPE
+    assert lib.qdg_argmax(P(A), 1, 100, P(A), None, need, None) == EINVAL
+    assert lib.qdg_argmax(P(A), 1, 100, P(A), P(A + 4), need, None) == EALIGN
+    bd = lib.qdg_block_dots
+    assert bd(0, P(A), 4, 64, P(A), None, 1, P(A), None, None) == EINVAL
+    assert bd(2, P(A), 4, 64, P(A), None, 1, P(A), P(A), None) == EINVAL
+    assert bd(1, P(A), 4, 64, P(A), None, 1, P(A), P(A), None) == EINVAL
+    assert bd(1, P(A), 4, 60, P(A), None, 1, P(A), None, None) == ESHAPE
+    assert bd(1, P(A), 4, 64, P(A), None, 17, P(A), None, None) == ESHAPE
+
+
+def test_split_bounds_validation():
+    arr = (ctypes.c_int32 * 66)()
+    assert lib.qdg_split_bounds(512, 0, ctypes.cast(arr, P)) == ESHAPE
+    assert lib.qdg_split_bounds(500, 2, ctypes.cast(arr, P)) == ESHAPE
+    assert lib.qdg_split_bounds(512, 2, None) == EINVAL
+    assert lib.qdg_split_bounds(512, 64, ctypes.cast(arr, P)) == OK
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros((4, 64), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        q.gemv_q8(q.INT8ACT, w, torch.zeros((4, 2), dtype=torch.int16), torch.zeros((1, 4)),
+                  xq=torch.zeros((1, 64), dtype=torch.int8), xs=torch.zeros((1, 2)))

@@ -1,0 +1,260 @@
+"""GPU parity: every hot-path call of libqdg.so against the CPU oracle on the same
+seeded inputs.
+
+Bar: quantized words, scales, block dots, arg-max indices and the f32 outputs of
+the quantized modes (whose order the kernels share with the oracle) are compared
+bit for bit; Dequant outputs (a binary64 sum in the kernel's own order) within
+|y - Y| <= 1e-5 * max(|Y|, ||t||_2) of the oracle's binary64 reference, and
+almost always bit-equal to the oracle's own binary32 result.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_gemv_02_amd as q
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def quantize_gpu(mode, x):
+    xd = dev(x.reshape(-1, x.shape[-1]))
+    B, K = xd.shape
+    xq = torch.empty((B, K), dtype=torch.int8, device=DEV)
+    xl = torch.empty((B, K), dtype=torch.int8, device=DEV) if mode == 2 else None
+    xs = torch.empty((B, K // 32), dtype=torch.float32, device=DEV)
+    q.quantize_act(mode, xd, xq, xl, xs)
+    return xq, xl, xs
+
+
+def gemv_gpu(mode, wqd, wsd, B, N, splits=1, x=None, xq=None, xl=None, xs=None):
+    out = torch.full((splits, B, N) if splits > 1 else (B, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8(mode, wqd, wsd, out, x=x, xq=xq, xl=xl, xs=xs, splits=splits)
+    return out
+
+
+# ---------------------------------------------------------------- quantizer
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,K,kind", [(1, 512, "normal"), (1, 25600, "outliers"), (16, 5120, "normal"),
+                                      (3, 1600, "special"), (1, 32, "special")])
+def test_quantize_bit_exact(mode, B, K, kind):
+    announce(f"quantize mode={mode} B={B} K={K} {kind}")
+    rng = np.random.default_rng(100 + K + B)
+    x = rng.standard_normal((B, K)).astype(np.float32)
+    if kind == "outliers":
+        x = workloads.activation(K, 1, outliers=True, seed_out=2)[None, :]
+    if kind == "special":
+        x[:, :32] = 0.0                                   # zero block
+        if K >= 128:
+            x[:, 32:64] = np.arange(32) - 15.5            # ties after scaling
+            x[:, 32] = 127.0
+            x[:, 64:96] *= np.float32(1e-20)              # tiny but inside the contract
+            x[:, 96:128] *= np.float32(1e20)              # huge
+        x[:, 5] = -0.0
+    xq, xl, xs = quantize_gpu(mode, x)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    np.testing.assert_array_equal(host(xq), oq)
+    np.testing.assert_array_equal(host(xs), os_)
+    if mode == 2:
+        np.testing.assert_array_equal(host(xl), ol)
+
+
+# ---------------------------------------------------------------- block dots
+
+@pytest.mark.parametrize("mode,B", [(1, 1), (2, 1), (1, 3), (2, 2)])
+def test_block_dots_bit_exact(mode, B):
+    announce(f"block_dots mode={mode} B={B}")
+    rng = np.random.default_rng(7 * B + mode)
+    N, K = 45, 32 * 37
+    wq = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    xq = rng.integers(-128, 128, size=(B, K), dtype=np.int8)
+    xl = rng.integers(-128, 128, size=(B, K), dtype=np.int8) if mode == 2 else None
+    dh = torch.empty((B, N, K // 32), dtype=torch.int32, device=DEV)
+    dl = torch.empty((B, N, K // 32), dtype=torch.int32, device=DEV) if mode == 2 else None
+    q.block_dots(mode, dev(wq), dev(xq), dev(xl), dh, dl)
+    rh, rl = oracle.block_dots(mode, wq, xq, xl)
+    np.testing.assert_array_equal(host(dh), rh)
+    if mode == 2:
+        np.testing.assert_array_equal(host(dl), rl)
+
+
+# ---------------------------------------------------------------- quantized GEMV
+
+def _quant_case(N, K, B, seed, outliers=False):
+    wq, ws = workloads.weights(N, K, seed, seed + 1)
+    x = workloads.batch_activation(B, K, seed + 2, outliers, seed + 3 if outliers else None)
+    return wq, ws, x
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (7, 96), (33, 544), (129, 1600), (70, 4096), (300, 25600)])
+def test_gemv_quantized_bit_exact(mode, N, K):
+    announce(f"gemv mode={mode} N={N} K={K}")
+    wq, ws, x = _quant_case(N, K, 1, 10 * N + K)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=8)
+    xq, xl, xs = quantize_gpu(mode, x)
+    y = gemv_gpu(mode, dev(wq), dev(ws), 1, N, xq=xq, xl=xl, xs=xs)
+    np.testing.assert_array_equal(host(y), want)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K", [(100, 25600), (64, 8192), (17, 1600), (9, 256), (50, 12288)])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 8, 64])
+def test_split_partials_and_combine_bit_exact(mode, N, K, S):
+    announce(f"split mode={mode} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, 1, 3 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want_part = oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8)
+    xq, xl, xs = quantize_gpu(mode, x)
+    part = gemv_gpu(mode, dev(wq), dev(ws), 1, N, splits=S, xq=xq, xl=xl, xs=xs)
+    if S == 1:
+        part = part.reshape(1, 1, N)
+    np.testing.assert_array_equal(host(part), want_part)
+    y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    q.sk_combine(part, y)
+    np.testing.assert_array_equal(host(y), oracle.combine(want_part))
+    if S == 1:
+        np.testing.assert_array_equal(host(y), oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_))
+
+
+def test_combine_golden_and_random(golden_dir):
+    import json
+    for c in json.load(open(os.path.join(golden_dir, "combine_order.json")))["cases"]:
+        p = np.array(c["partials"], np.float32).reshape(-1, 1, 1)
+        y = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+        q.sk_combine(dev(p), y)
+        assert host(y)[0, 0] == np.float32(c["y"])
+    rng = np.random.default_rng(5)
+    p = (rng.standard_normal((7, 3, 1001)) * 10.0 ** rng.integers(-8, 8, size=(7, 3, 1001))).astype(np.float32)
+    y = torch.empty((3, 1001), dtype=torch.float32, device=DEV)
+    q.sk_combine(dev(p), y)
+    np.testing.assert_array_equal(host(y), oracle.combine(p))
+
+
+# ---------------------------------------------------------------- batched (MFMA)
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,N,K,S", [(16, 256, 5120, 1), (2, 33, 512, 1), (5, 100, 1600, 2), (16, 40, 96, 1),
+                                     (11, 64, 25600, 4), (3, 17, 32, 1)])
+def test_batched_bit_exact_and_batch_invariant(mode, B, N, K, S):
+    announce(f"batched mode={mode} B={B} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, B, 5 * B + N + K)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    xq, xl, xs = quantize_gpu(mode, x)
+    wqd, wsd = dev(wq), dev(ws)
+    out = gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs)
+    if S == 1:
+        np.testing.assert_array_equal(host(out), oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=8))
+    else:
+        np.testing.assert_array_equal(host(out), oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    # row t of the batch equals the batch-1 kernel on row t, bit for bit
+    for t in (0, B - 1):
+        y1 = gemv_gpu(mode, wqd, wsd, 1, N, splits=S, xq=xq[t:t + 1].contiguous(),
+                      xl=None if xl is None else xl[t:t + 1].contiguous(), xs=xs[t:t + 1].contiguous())
+        got = host(out)
+        np.testing.assert_array_equal(got[:, t] if S > 1 else got[t], host(y1)[:, 0] if S > 1 else host(y1)[0])
+
+
+# ---------------------------------------------------------------- Dequant
+
+@pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (37, 1600), (64, 12288), (20, 5120), (5, 25600)])
+def test_dequant_tolerance(N, K):
+    announce(f"dequant N={N} K={K}")
+    wq, ws, x = _quant_case(N, K, 1, N + 3 * K, outliers=True)
+    y = host(gemv_gpu(0, dev(wq), dev(ws), 1, N, x=dev(x)))
+    Y, tn = oracle.reference_f64(0, wq, ws, x=x)
+    assert oracle.within_tolerance(y, Y, tn).all()
+    same = (y == oracle.gemv(0, wq, ws, x=x)).mean()
+    if N >= 20:
+        assert same >= 0.95, same
+
+
+# ---------------------------------------------------------------- arg-max
+
+def argmax_gpu(y):
+    y = np.atleast_2d(y).astype(np.float32)
+    B, N = y.shape
+    idx = torch.empty(B, dtype=torch.int32, device=DEV)
+    wsp = torch.empty(q.argmax_workspace_bytes(B, N) // 8, dtype=torch.int64, device=DEV)
+    q.argmax(dev(y), idx, wsp)
+    return host(idx)
+
+
+def test_argmax_random_and_ties():
+    announce("argmax random")
+    for seed in range(60):
+        rng = np.random.default_rng(seed)
+        N = int(rng.choice([1, 2, 63, 2047, 2048, 2049, 4096, 10000, 151936]))
+        B = int(rng.integers(1, 4))
+        y = rng.standard_normal((B, N)).astype(np.float32)
+        if seed % 3 == 0:
+            y = np.round(y).astype(np.float32)  # many exact ties
+        np.testing.assert_array_equal(argmax_gpu(y), oracle.argmax(y))
+
+
+@pytest.mark.parametrize("N", [151936, 4096, 5000])
+def test_argmax_planted_ties_adversarial(N):
+    announce(f"argmax planted N={N}")
+    G = -(-N // 2048)
+    G = min(max(G, 1), 256)
+    per = -(-N // G)
+    pairs = [(0, N - 1), (per - 1, per), (per, min(2 * per - 1, N - 1)), (N - 2, N - 1), (1, 0)]
+    rng = np.random.default_rng(N)
+    for a, b in pairs:
+        y = rng.standard_normal(N).astype(np.float32)
+        y[a] = y[b] = np.float32(9.0)
+        assert argmax_gpu(y)[0] == min(a, b)
+    y = np.zeros(N, np.float32)
+    assert argmax_gpu(y)[0] == 0
+    y = np.full(N, -3.0, np.float32)
+    y[N // 2] = -0.0
+    y[N // 3] = 0.0
+    assert argmax_gpu(y)[0] == min(N // 2, N // 3)
+    y = np.full(N, -np.inf, np.float32)
+    assert argmax_gpu(y)[0] == 0
+
+
+# ---------------------------------------------------------------- determinism
+
+def test_repeat_and_fresh_buffers_bitwise():
+    announce("determinism")
+    N, K = 1000, 8192
+    wq, ws, x = _quant_case(N, K, 1, 77, outliers=True)
+    for mode in (0, 1, 2):
+        outs = []
+        for rep in range(5):
+            wqd, wsd = dev(wq), dev(ws)  # fresh allocations each time
+            if mode == 0:
+                outs.append(host(gemv_gpu(0, wqd, wsd, 1, N, x=dev(x))))
+            else:
+                xq, xl, xs = quantize_gpu(mode, x)
+                part = gemv_gpu(mode, wqd, wsd, 1, N, splits=4, xq=xq, xl=xl, xs=xs)
+                y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+                q.sk_combine(part, y)
+                outs.append(host(y))
+        for o in outs[1:]:
+            assert o.tobytes() == outs[0].tobytes()
