@@ -43,11 +43,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--splits", default="auto", help="'auto' or one S for every GEMV")
+    ap.add_argument("--splits", default="4,8",
+                    help="split-K chunks: 'auto' (timed choice), one S for both projections, or 'S_o,S_down'")
     ap.add_argument("--modes", default="1,2")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
 
 
@@ -112,13 +115,17 @@ def main() -> int:
             "part": torch.empty((S, 1, sh.N), dtype=torch.float32, device=dev) if S > 1 else None,
         }
 
-    # ---- choose S per (mode, shape): fastest GEMV + combine over a few rotated launches
+    # ---- S per (mode, shape): fixed (default 4 for the o-proj, 8 for the down-proj), or timed
     chosen = {}
+    fixed = None if args.splits == "auto" else [int(v) for v in args.splits.split(",")]
     for mode in modes:
         for si in range(len(shapes)):
-            cands = [1, 2, 4, 8] if args.splits == "auto" else [int(args.splits)]
+            if fixed is not None:
+                chosen[(mode, si)] = fixed[min(si, len(fixed) - 1)]
+                ensure_buffers(mode, si, chosen[(mode, si)])
+                continue
             best = None
-            for S in cands:
+            for S in (1, 2, 3, 4, 6, 8):
                 ensure_buffers(mode, si, S)
                 seqs = [make_calls(mode, si, S, c) for c in range(R)]
                 for c in seqs:
@@ -126,7 +133,7 @@ def main() -> int:
                         f()
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 4 * R
+                reps = 8 * R
                 e0.record()
                 for i in range(reps):
                     for f in seqs[i % R][1:]:
@@ -171,6 +178,12 @@ def main() -> int:
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     K = args.steps
     ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -185,6 +198,18 @@ def main() -> int:
     dom_ms = sum(a.elapsed_time(b) for a, b in used) / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    # HBM bytes per launch of the dominant kernel from the committed profiler counters, used
+    # only if they were taken on the current kernel sources at the same launch shape
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "gemv_q8_narrow_projections_traffic.json")
+    if os.path.exists(tpath):
+        from quantized_decode_gemv_02_amd import profiling
+        t = json.load(open(tpath))
+        dom_grid = 256 * -(-shapes[dom_key[1]].N // 16) * chosen[dom_key]
+        if (t.get("kernel_source_sha") == profiling.kernel_source_sha() and t.get("grid") == dom_grid
+                and "traffic_bytes" in t):
+            traffic = int(round(t["traffic_bytes"]))
 
     per_mode = {}
     for mode in modes:
@@ -234,7 +259,7 @@ def main() -> int:
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"k_gemv_dot4 down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
                      "alg_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_ms * 1e3, 3)},
         "cpu_baseline": cpu,

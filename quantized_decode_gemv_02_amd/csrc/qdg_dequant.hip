@@ -12,8 +12,9 @@
 //    block's term is sigma * that sum (one binary64 rounding);
 //  * terms go into partial g mod 4 in ascending block order, and the row is
 //    (P0 + P2) + (P1 + P3), then one rounding to binary32.
-// The lane layout, LDS staging of the f32 activation window and the load pipeline
-// are those of the quantized kernel (qdg_gemv.hip).
+// The lane layout, the LDS staging of the window (the f32 activation and the
+// rows' weight scales) and the load pipeline are those of the quantized kernel
+// (qdg_gemv.hip).
 #include "qdg_device.h"
 
 namespace qdg {
@@ -45,47 +46,46 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   constexpr int LPR = 64 / RPW;
   constexpr int BPS = LPR / 2;
   constexpr int TPP = BPS / 4;
+  constexpr int ROWS = (WG / 64) * RPW;
   static_assert(TPP == 1 || TPP == 2, "RPW must be 4 or 8");
   extern __shared__ __align__(16) unsigned char lds[];
-  float* lx = (float*)lds;
+  float* lx = (float*)lds;                            // [win][32]
+  uint16_t* lsg = (uint16_t*)(lx + (int64_t)win * QK);  // [ROWS][win]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
-  const int64_t o = ((int64_t)blockIdx.x * (WG / 64) + wave) * RPW + r;
+  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  const int rr = wave * RPW + r;
+  const int64_t o = o_wg + rr;
   const bool row_ok = o < N;
-  const int64_t orow = row_ok ? o : N - 1;
-  const int8_t* wrow = wq + orow * K + hf * 16;
-  const uint16_t* srow = ws + orow * nb;
+  const int8_t* wrow = wq + (row_ok ? o : N - 1) * K + hf * 16;
+  const uint16_t* my_sg = lsg + rr * win;
 
   double p = 0.0;
   for (int64_t wb0 = 0; wb0 < nb; wb0 += win) {
     const int64_t wb1 = wb0 + win < nb ? wb0 + win : nb;
     const int nwb = (int)(wb1 - wb0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nwb * 8; i += WG) ((float4*)lx)[i] = ((const float4*)(x + wb0 * QK))[i];
-    __syncthreads();
-
     const int nsteps = (nwb + BPS - 1) / BPS;
     const int ngroups = (nsteps + U - 1) / U;
     int4 wcur[U];
-    unsigned short scur[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int bl = u * BPS + j;
-      wcur[u] = bl < nwb ? *(const int4*)(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
-      scur[u] = bl < nwb ? srow[wb0 + bl] : (unsigned short)0;
+      wcur[u] = bl < nwb ? ld16_stream(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nwb * 8; i += WG) ((float4*)lx)[i] = ((const float4*)(x + wb0 * QK))[i];
+    stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
+    __syncthreads();
+
     for (int gi = 0; gi < ngroups; ++gi) {
       int4 wnxt[U];
-      unsigned short snxt[U];
       const bool more = gi + 1 < ngroups;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int bl = ((gi + 1) * U + u) * BPS + j;
-        const bool ok = more && bl < nwb;
-        wnxt[u] = ok ? *(const int4*)(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
-        snxt[u] = ok ? srow[wb0 + bl] : (unsigned short)0;
+        wnxt[u] = more && bl < nwb ? ld16_stream(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
         const double hsum = half_dot16(wcur[u], lx + blc * QK + hf * 16);
         const double other = dpp_f64<DPP_QUAD_SWAP1>(hsum);
         const double blk = __dadd_rn(hsum, other);  // the same bits in both lanes of the pair
-        const double term = __dmul_rn((double)half_bits_to_float(scur[u]), blk);
+        const double term = __dmul_rn((double)half_bits_to_float(my_sg[blc]), blk);
         p = ok ? __dadd_rn(p, term) : p;
         if constexpr (TPP == 2) {
           const double term2 = dpp_f64<DPP_ROW_SHL8>(term);
@@ -103,10 +103,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        wcur[u] = wnxt[u];
-        scur[u] = snxt[u];
-      }
+      for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
     }
   }
   const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL4>(p));
@@ -119,12 +116,12 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
 hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                float* out, hipStream_t st) {
   constexpr int RPW = 4, U = 4;
+  constexpr int rows_per_wg = (WG / 64) * RPW;
   const int64_t nb = K / QK;
-  const int cap = (LDS_BUDGET / (QK * 4)) / SUPER * SUPER;
+  const int cap = (LDS_BUDGET / (QK * 4 + 2 * rows_per_wg)) / SUPER * SUPER;
   int win = (int)(((nb + SUPER - 1) / SUPER) * SUPER);
   if (win > cap) win = cap;
-  const size_t lds = (size_t)win * QK * 4;
-  const int rows_per_wg = (WG / 64) * RPW;
+  const size_t lds = (size_t)win * (QK * 4 + 2 * rows_per_wg);
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(WG);
   hipLaunchKernelGGL((k_gemv_dequant<RPW, U>), grid, block, lds, st, wq, ws, x, N, K, win, out);
   return hipGetLastError();

@@ -49,6 +49,45 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// 16-byte loads.  The weight stream is read once per call, so it is loaded with
+// the nontemporal hint (the cache lines are not kept for reuse); activations,
+// which every workgroup re-reads, use ordinary loads.
+__device__ __forceinline__ int4 to_int4(v4i t) { return make_int4(t[0], t[1], t[2], t[3]); }
+__device__ __forceinline__ int4 ld16_stream(const int8_t* p) {
+  return to_int4(__builtin_nontemporal_load((const v4i*)p));
+}
+__device__ __forceinline__ int4 ld16(const int8_t* p) { return to_int4(*(const v4i*)p); }
+__device__ __forceinline__ unsigned short ld_u16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load((const unsigned short*)p);
+}
+
+// Copies the weight scales of `rows` consecutive rows (first row o0, rows at or
+// past N read row N-1) over blocks [b0, b0 + n) into LDS as [row][n_pitch]
+// (binary16 bits), with `nthreads` threads of index `tid`.  When a row's segment
+// starts 16-byte aligned (nb and b0 multiples of 8) the bulk moves in 16-byte
+// words and only the last n mod 8 scales of a row move one by one.
+__device__ __forceinline__ void stage_scales(uint16_t* __restrict__ dst, int pitch, const uint16_t* __restrict__ ws,
+                                             int64_t nb, int64_t N, int64_t o0, int rows, int64_t b0, int n,
+                                             int tid, int nthreads) {
+  const bool wide = (nb % 8) == 0 && (b0 % 8) == 0 && (pitch % 8) == 0;
+  const int nv = wide ? n / 8 : 0;  // 16-byte words per row
+  for (int i = tid; i < rows * nv; i += nthreads) {
+    const int r = i / nv, c = i - r * nv;
+    int64_t o = o0 + r;
+    if (o >= N) o = N - 1;
+    *(int4*)(dst + r * pitch + 8 * c) = *(const int4*)(ws + o * nb + b0 + 8 * c);
+  }
+  const int rest = n - 8 * nv;
+  for (int i = tid; i < rows * rest; i += nthreads) {
+    const int r = i / rest, c = 8 * nv + (i - r * rest);
+    int64_t o = o0 + r;
+    if (o >= N) o = N - 1;
+    dst[r * pitch + c] = ws[o * nb + b0 + c];
+  }
+}
+
 // Exact int32 dot of 16 int8 pairs held in one lane (four v_dot4 steps).
 __device__ __forceinline__ int dot16_i8(int4 w, int4 a) {
   int d = __builtin_amdgcn_sdot4(w.x, a.x, 0, false);

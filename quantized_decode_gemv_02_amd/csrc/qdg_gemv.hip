@@ -17,10 +17,14 @@
 //    that the lanes 8 to the right hold (one DPP row shift), in that order.  The
 //    chain of every partial therefore stays in one lane pair, in ascending block
 //    order, with no reduction tree at all; the pair's lanes hold equal values.
-//  * The activation window (int8 words, TwoPass low words, scales) of the
-//    workgroup's K-chunk is staged once in LDS and read with ds_read_b128.
+//  * The window of the workgroup's K-chunk -- activation words (TwoPass low
+//    words too) and scales, and the weight scales of the workgroup's rows -- is
+//    staged in LDS with 16-byte loads; a lane reads its block's activation with
+//    one ds_read_b128 and its scales with two small LDS reads.
 //  * U steps of weight loads are issued ahead of the steps being computed, so
-//    each wave keeps up to 2*U*1 KB of weights in flight.
+//    each wave keeps up to 2*U*1 KB of weights in flight; the first group is
+//    issued before the window's barrier.  Weights are read with the
+//    nontemporal hint (streamed once, never re-read).
 //  * grid = (row tiles, splits): the split s of a row covers the QWEN38 chunk
 //    [g0, g1) and writes partial[s][o]; an empty chunk writes +0.
 #include <stdlib.h>
@@ -30,11 +34,13 @@
 namespace qdg {
 namespace {
 
-constexpr int WG = 256;              // four waves
-constexpr int LDS_BUDGET = 56 * 1024;  // activation window bytes per workgroup
+constexpr int WG = 256;                // four waves
+constexpr int LDS_BUDGET = 56 * 1024;  // window bytes per workgroup
 
-template <int MODE>
-constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4; }
+// LDS bytes per block of the window: activation words (two under TwoPass), the
+// activation scale, and the binary16 weight scales of the workgroup's rows.
+template <int MODE, int RPW>
+constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * (WG / 64) * RPW; }
 
 template <int MODE, int RPW, int U>
 __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
@@ -44,6 +50,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   constexpr int LPR = 64 / RPW;  // lanes per row
   constexpr int BPS = LPR / 2;   // blocks per step of a row
   constexpr int TPP = BPS / 4;   // steps of one partial per step (1 or 2)
+  constexpr int ROWS = (WG / 64) * RPW;
   static_assert(TPP == 1 || TPP == 2, "RPW must be 4 or 8");
   extern __shared__ __align__(16) unsigned char lds[];
 
@@ -54,48 +61,48 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   int32_t g0, g1;
   split_range(K, S, s_idx, g0, g1);
 
-  const int64_t o = ((int64_t)blockIdx.x * (WG / 64) + wave) * RPW + r;
+  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  const int rr = wave * RPW + r;  // row within the workgroup
+  const int64_t o = o_wg + rr;
   const bool row_ok = o < N;
-  const int64_t orow = row_ok ? o : N - 1;
-  const int8_t* wrow = wq + orow * K + hf * 16;
-  const uint16_t* srow = ws + orow * nb;
+  const int8_t* wrow = wq + (row_ok ? o : N - 1) * K + hf * 16;
 
-  int8_t* lq = (int8_t*)lds;
-  int8_t* ll = lq + (int64_t)win * QK;
-  float* lsx = (float*)(lds + (int64_t)win * (MODE == 2 ? 2 : 1) * QK);
+  int8_t* lq = (int8_t*)lds;                                              // [win][32]
+  int8_t* ll = lq + (int64_t)win * QK;                                    // [win][32] (TwoPass)
+  float* lsx = (float*)(lds + (int64_t)win * (MODE == 2 ? 2 : 1) * QK);  // [win]
+  uint16_t* lsg = (uint16_t*)(lsx + win);                                 // [ROWS][win]
+  const uint16_t* my_sg = lsg + rr * win;
 
   float p = 0.0f;  // this lane pair's partial (j < 4)
   for (int wb0 = g0; wb0 < g1; wb0 += win) {
     const int wb1 = min(wb0 + win, g1);
     const int nwb = wb1 - wb0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < nwb * 2; i += WG) {
-      ((int4*)lq)[i] = ((const int4*)(xq + (int64_t)wb0 * QK))[i];
-      if constexpr (MODE == 2) ((int4*)ll)[i] = ((const int4*)(xl + (int64_t)wb0 * QK))[i];
-    }
-    for (int i = threadIdx.x; i < nwb; i += WG) lsx[i] = xs[wb0 + i];
-    __syncthreads();
-
     const int nsteps = (nwb + BPS - 1) / BPS;
     const int ngroups = (nsteps + U - 1) / U;
+    // the first group's weights are requested before the window is staged, so
+    // the weight stream is already in flight across the barrier
     int4 wcur[U];
-    unsigned short scur[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = wb0 + u * BPS + j;
-      wcur[u] = b < wb1 ? *(const int4*)(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
-      scur[u] = b < wb1 ? srow[b] : (unsigned short)0;
+      wcur[u] = b < wb1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nwb * 2; i += WG) {
+      ((int4*)lq)[i] = ld16(xq + (int64_t)wb0 * QK + 16 * i);
+      if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + (int64_t)wb0 * QK + 16 * i);
+    }
+    for (int i = threadIdx.x; i < nwb; i += WG) lsx[i] = xs[wb0 + i];
+    stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
+    __syncthreads();
+
     for (int gi = 0; gi < ngroups; ++gi) {
       int4 wnxt[U];
-      unsigned short snxt[U];
       const bool more = gi + 1 < ngroups;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int b = wb0 + ((gi + 1) * U + u) * BPS + j;
-        const bool ok = more && b < wb1;
-        wnxt[u] = ok ? *(const int4*)(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
-        snxt[u] = ok ? srow[b] : (unsigned short)0;
+        wnxt[u] = more && b < wb1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
         int e = 0;
         if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
         float ta, tb;
-        q8_term<MODE>(half_bits_to_float(scur[u]), lsx[blc], d, e, ta, tb);
+        q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
         p = ok ? __fmaf_rn(ta, tb, p) : p;
         if constexpr (TPP == 2) {
           const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
@@ -115,10 +122,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
         }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        wcur[u] = wnxt[u];
-        scur[u] = snxt[u];
-      }
+      for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
     }
   }
   // (P0 + P2) + (P1 + P3): partial q sits in lane 2q of the row.
@@ -156,11 +160,11 @@ hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
     split_range(K, splits, s, g0, g1);
     mx = g1 - g0 > mx ? g1 - g0 : mx;
   }
-  const int cap = (LDS_BUDGET / window_bytes_per_block<MODE>()) / SUPER * SUPER;
+  const int cap = (LDS_BUDGET / window_bytes_per_block<MODE, RPW>()) / SUPER * SUPER;
   int win = ((mx + SUPER - 1) / SUPER) * SUPER;
   if (win > cap) win = cap;
   if (win < SUPER) win = SUPER;
-  const size_t lds = (size_t)win * window_bytes_per_block<MODE>();
+  const size_t lds = (size_t)win * window_bytes_per_block<MODE, RPW>();
   const int rows_per_wg = (WG / 64) * RPW;
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
   hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, splits,
