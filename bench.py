@@ -4,9 +4,14 @@
 One step is one decode pass over the narrow projections (o-proj 5120x8192 and
 down-proj 5120x25600, batch 1): for each of the Int8Act and TwoPass numerics and
 each projection, quantize the activation, run the split-K GEMV and the ascending
-combine.  Inputs are seeded synthetic tensors resident in HBM before timing; the
-weights rotate over enough copies (>= 1 GiB between reuses of a copy) that the
-256 MB Infinity Cache cannot serve them.
+combine.  The default path makes two calls per projection, qdg_quantize_act and
+qdg_gemv_q8_sk (the split-K GEMV whose last-arriving workgroups do the
+ascending combine); --path staged makes the three calls of the pages' own
+structure (qdg_quantize_act, qdg_gemv_q8, qdg_sk_combine) instead.  Each run
+reports the other path's step time beside its own.  Inputs are seeded synthetic
+tensors resident in HBM before timing; the weights rotate over enough copies
+(>= 1 GiB between reuses of a copy) that the 256 MB Infinity Cache cannot serve
+them.
 
 Prints ONE JSON line:
   value      = algorithmic GEMV bytes of a step / step time (GB/s); algorithmic
@@ -49,6 +54,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
+    ap.add_argument("--path", choices=("fused", "staged"), default="fused")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
@@ -89,12 +95,15 @@ def main() -> int:
     setup_s = time.time() - t0
 
     # ---- per (mode, shape) buffers and pre-bound launches
-    def make_calls(mode, si, S, copy_idx):
+    def make_calls(mode, si, S, copy_idx, path="staged"):
         sh = shapes[si]
         N, K = sh.N, sh.K
         bufs = buffers[(mode, si, S)]
         w, s = copies[copy_idx][si]
         calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
+        if path == "fused":
+            calls.append(q.bind_gemv_q8_sk(mode, w, s, bufs["y"], bufs["xq"], bufs["xl"], bufs["xs"], S, bufs["fws"]))
+            return calls
         out = bufs["y"] if S == 1 else bufs["part"]
         calls.append(q.bind_gemv_q8(mode, w, s, out, xq=bufs["xq"], xl=bufs["xl"], xs=bufs["xs"], splits=S))
         if S > 1:
@@ -113,6 +122,7 @@ def main() -> int:
             "xs": torch.empty((1, sh.K // 32), dtype=torch.float32, device=dev),
             "y": torch.empty((1, sh.N), dtype=torch.float32, device=dev),
             "part": torch.empty((S, 1, sh.N), dtype=torch.float32, device=dev) if S > 1 else None,
+            "fws": q.sk_workspace(sh.N, S),
         }
 
     # ---- S per (mode, shape): fixed (default 4 for the o-proj, 8 for the down-proj), or timed
@@ -146,23 +156,26 @@ def main() -> int:
             chosen[(mode, si)] = best[0]
 
     # ---- the step: every (mode, shape) once, each mode on its own weight copy
-    steps_calls = []
     dom_key = (2 if 2 in modes else modes[-1], len(shapes) - 1)
-    for copy_pair in range(R):
-        seq = []
-        for mi, mode in enumerate(modes):
-            cidx = (copy_pair * len(modes) + mi) % R
-            for si in range(len(shapes)):
-                S = chosen[(mode, si)]
-                calls = make_calls(mode, si, S, cidx)
-                seq.append(((mode, si), calls))
-        steps_calls.append(seq)
+
+    def build_steps(path):
+        steps = []
+        for copy_pair in range(R):
+            seq = []
+            for mi, mode in enumerate(modes):
+                cidx = (copy_pair * len(modes) + mi) % R
+                for si in range(len(shapes)):
+                    seq.append(((mode, si), make_calls(mode, si, chosen[(mode, si)], cidx, path)))
+            steps.append(seq)
+        return steps
+
+    steps_calls = build_steps(args.path)
 
     step_bytes = sum(alg_bytes(m, shapes[si].N, shapes[si].K) for m in modes for si in range(len(shapes)))
     dom_bytes = alg_bytes(dom_key[0], shapes[dom_key[1]].N, shapes[dom_key[1]].K)
 
-    def run_step(i, events=None):
-        for key, calls in steps_calls[i % R]:
+    def run_step(i, events=None, steps=None):
+        for key, calls in (steps or steps_calls)[i % R]:
             if events is not None and key == dom_key:
                 calls[0]()
                 ev0, ev1 = events.pop()
@@ -196,6 +209,18 @@ def main() -> int:
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / K
     dom_ms = sum(a.elapsed_time(b) for a, b in used) / K
+
+    # the other path's step time, for reference (same steps, same rotation)
+    other = "staged" if args.path == "fused" else "fused"
+    other_steps = build_steps(other)
+    for i in range(args.warmup):
+        run_step(i, steps=other_steps)
+    torch.cuda.synchronize()
+    t_o = time.perf_counter()
+    for i in range(K):
+        run_step(i, steps=other_steps)
+    torch.cuda.synchronize()
+    other_ms = (time.perf_counter() - t_o) * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
@@ -207,8 +232,9 @@ def main() -> int:
         from quantized_decode_gemv_02_amd import profiling
         t = json.load(open(tpath))
         dom_grid = 256 * -(-shapes[dom_key[1]].N // 16) * chosen[dom_key]
+        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {'true' if args.path == 'fused' else 'false'}>"
         if (t.get("kernel_source_sha") == profiling.kernel_source_sha() and t.get("grid") == dom_grid
-                and "traffic_bytes" in t):
+                and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
 
     per_mode = {}
@@ -255,12 +281,13 @@ def main() -> int:
         "data": "synthetic (seeded; int8 weights uniform [-127,127], fp16 scales U[1e-3,1e-2), N(0,1) activations with 1% x20 outliers)",
         "config": {"workload": "narrow projections with split-K: o-proj K=8192 N=5120 and down-proj K=25600 N=5120, "
                                "batch 1, Int8Act + TwoPass, quantize + GEMV + ascending combine",
+                   "path": args.path, f"{other}_ms_per_step": round(other_ms, 5),
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"k_gemv_dot4 down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
+                     "kernel": f"k_gemv_dot4 ({args.path}) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
                      "alg_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

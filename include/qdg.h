@@ -60,7 +60,7 @@ enum {
     QDG_ESHAPE = -2,     /* K not a positive multiple of 32, N or B out of range     */
     QDG_EALIGN = -3,     /* a pointer breaks the alignment rule above               */
     QDG_EMODE = -4,      /* the mode does not support this B / splits combination   */
-    QDG_EWORKSPACE = -5, /* the arg-max workspace is too small                      */
+    QDG_EWORKSPACE = -5, /* a workspace is smaller than its *_workspace_bytes() size  */
     QDG_EHIP = -6        /* the HIP runtime refused a launch                        */
 };
 
@@ -130,6 +130,27 @@ int qdg_gemv_q8(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64
  */
 int qdg_sk_combine(const float *partials, int splits, int64_t B, int64_t N, float *y,
                    qdg_stream stream);
+
+/* Bytes of device workspace qdg_gemv_q8_sk needs (0 for an unsupported shape). */
+size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
+
+/*
+ * The split-K GEMV and its combine in one launch (QDG_INT8ACT, QDG_TWOPASS;
+ * B == 1): the chunks of the QWEN38 page's chunk rule run as in qdg_gemv_q8,
+ * and the last workgroup of each 16-row tile to finish (an atomic ticket per
+ * tile; the lane kernel library page's last-arriving-block pattern, in place of
+ * the QWEN38 page's separate combine kernel) sums the tile's partials in
+ * ascending chunk order from 0.  y [1][N] is bit-identical to qdg_gemv_q8(splits)
+ * + qdg_sk_combine: which chunk finishes last changes nothing.  Inputs as
+ * qdg_gemv_q8 (xq, xl, xs from qdg_quantize_act); workspace: device memory of at
+ * least qdg_gemv_sk_workspace_bytes(1, N, splits) bytes, 256-byte aligned and
+ * zero-filled before its first use; every call that completes leaves its tickets
+ * zero again, so it needs no clearing between calls.  Calls that share a
+ * workspace must not overlap in time (one stream, or events between them).
+ */
+int qdg_gemv_q8_sk(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                   const int8_t *xq, const int8_t *xl, const float *xs, int64_t B, int splits,
+                   float *y, void *workspace, size_t workspace_bytes, qdg_stream stream);
 
 /* Bytes of device workspace qdg_argmax needs for B rows of N values. */
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N);

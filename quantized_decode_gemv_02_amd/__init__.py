@@ -8,6 +8,7 @@ functions carry the names of the C entry points in ``include/qdg.h`` without the
 * ``quantize_act(mode, x, xq, xl, xs)``
 * ``gemv_q8(mode, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits=1)``
 * ``sk_combine(partials, y)``
+* ``gemv_q8_sk(mode, wq, ws, y, xq, xl, xs, splits, workspace)`` / ``gemv_sk_workspace_bytes(B, N, S)``
 * ``argmax(y, idx, workspace)`` / ``argmax_workspace_bytes(B, N)``
 * ``block_dots(mode, wq, xq, xl, dh, dl)``
 * ``split_bounds(K, splits)`` (host only)
@@ -49,6 +50,8 @@ _SIGS = {
     "qdg_quantize_act": ([_I, _P, _I64, _I64, _P, _P, _P, _P], _I),
     "qdg_gemv_q8": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _I, _P, _P], _I),
     "qdg_sk_combine": ([_P, _I, _I64, _I64, _P, _P], _I),
+    "qdg_gemv_sk_workspace_bytes": ([_I64, _I64, _I], ctypes.c_size_t),
+    "qdg_gemv_q8_sk": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "qdg_argmax": ([_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
@@ -144,6 +147,28 @@ def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: i
         _ptr(out, _f32(), "out"), _stream()))
 
 
+def gemv_sk_workspace_bytes(B: int, N: int, splits: int) -> int:
+    return int(_lib.qdg_gemv_sk_workspace_bytes(B, N, splits))
+
+
+def sk_workspace(N: int, splits: int):
+    """A zero-filled device workspace for ``gemv_q8_sk`` (int64 words; torch allocations are 256-byte aligned)."""
+    torch = _torch()
+    nbytes = max(gemv_sk_workspace_bytes(1, N, splits), 8)
+    return torch.zeros((nbytes + 7) // 8, dtype=torch.int64, device="cuda")
+
+
+def gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> None:
+    """Split-K GEMV whose last-arriving workgroups do the ascending combine: ``y [1][N]``."""
+    N, K = wq.shape
+    B = xq.shape[0] if xq.dim() == 2 else 1
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("qdg_gemv_q8_sk", _lib.qdg_gemv_q8_sk(
+        mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"),
+        _ptr(xs, _f32(), "xs"), B, int(splits), _ptr(y, _f32(), "y"), _ptr(workspace, None, "workspace"), nbytes,
+        _stream()))
+
+
 def sk_combine(partials, y) -> None:
     """``y [B][N]`` = ascending sum over the leading axis of ``partials [S][B][N]``."""
     S = partials.shape[0]
@@ -210,6 +235,15 @@ def bind_gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, spli
     for t, n in ((wq, "wq"), (ws, "ws"), (out, "out"), (x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_gemv_q8", mode, wq, ws, N, K, x, xq, xl, xs, B, int(splits), out, _stream())
+
+
+def bind_gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> Bound:
+    N, K = wq.shape
+    B = xq.shape[0] if xq.dim() == 2 else 1
+    for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (xq, "xq"), (xl, "xl"), (xs, "xs"), (workspace, "workspace")):
+        _ptr(t, None, n)
+    nbytes = workspace.numel() * workspace.element_size()
+    return Bound("qdg_gemv_q8_sk", mode, wq, ws, N, K, xq, xl, xs, B, int(splits), y, workspace, nbytes, _stream())
 
 
 def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:

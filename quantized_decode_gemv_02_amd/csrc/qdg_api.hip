@@ -92,6 +92,31 @@ int qdg_sk_combine(const float* partials, int splits, int64_t B, int64_t N, floa
   return hip_status(qdg::launch_combine(partials, splits, B * N, y, as_stream(stream)));
 }
 
+size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits) {
+  if (B != 1 || N < 1 || N > ((int64_t)1 << 40) || splits < 1 || splits > QDG_MAX_SPLITS) return 0;
+  return qdg::sk_workspace_bytes(N, splits);
+}
+
+int qdg_gemv_q8_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                   const int8_t* xl, const float* xs, int64_t B, int splits, float* y, void* workspace,
+                   size_t workspace_bytes, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return mode == QDG_DEQUANT ? QDG_EMODE : QDG_EINVAL;
+  if (!wq || !ws || !xq || !xs || !y || !workspace) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!shape_ok(N, K)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
+  if (B != 1) return QDG_EMODE;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) ||
+      !aligned(y, 4))
+    return QDG_EALIGN;
+  if (!aligned(workspace, 256)) return QDG_EALIGN;
+  if (workspace_bytes < qdg::sk_workspace_bytes(N, splits)) return QDG_EWORKSPACE;
+  return hip_status(qdg::launch_gemv_sk(mode, wq, ws, N, K, xq, xl, xs, splits, y, workspace, as_stream(stream)));
+}
+
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
   if (B < 1 || N < 1) return 0;
   return (size_t)B * (size_t)qdg::argmax_groups(N) * sizeof(unsigned long long);

@@ -122,6 +122,49 @@ __device__ __forceinline__ void q8_term(float sigma, float s, int d, int e, floa
   }
 }
 
+// The activation quantizer of one 32-value block, for the four values v of one
+// lane of the block's 8-lane group (lane kernel library page: lk_quant_lane,
+// lk_two_scale, lk_two_words).  All 64 lanes must call it (the block maximum is
+// a butterfly over the 8 lanes; max is exact and order-free).  Returns the four
+// words packed first-lowest in *h (and *l under TwoPass) and the block scale.
+__device__ __forceinline__ int pack4_i8(int a, int b, int c, int d) {
+  return (int)((unsigned)(a & 255) | ((unsigned)(b & 255) << 8) | ((unsigned)(c & 255) << 16) |
+               ((unsigned)(d & 255) << 24));
+}
+// round to nearest, ties to even, then saturate to int8 (a no-op inside the contract)
+__device__ __forceinline__ int rn_clamp8(float v) {
+  const float r = __builtin_rintf(v);
+  return (int)__builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+}
+template <int MODE>
+__device__ __forceinline__ float quant_lane4(float4 v, int* h, int* l) {
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  a = fmaxf(a, __shfl_xor(a, 2, 64));
+  a = fmaxf(a, __shfl_xor(a, 4, 64));
+  const float vv[4] = {v.x, v.y, v.z, v.w};
+  int hh[4], ll[4];
+  float s;
+  if constexpr (MODE == 1) {
+    s = a > 0.0f ? a / 127.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hh[i] = rn_clamp8(vv[i] / s);
+    *l = 0;
+  } else {
+    s = (a > 1e-30f ? a : 1e-30f) / 127.0f;
+    const float lsc = __fmul_rn(s, 0.0078125f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hh[i] = rn_clamp8(vv[i] / s);
+      const float r = __fmaf_rn(-(float)hh[i], s, vv[i]);
+      ll[i] = rn_clamp8(r / lsc);
+    }
+    *l = pack4_i8(ll[0], ll[1], ll[2], ll[3]);
+  }
+  *h = pack4_i8(hh[0], hh[1], hh[2], hh[3]);
+  return s;
+}
+
 }  // namespace qdg
 
 // Launchers (one translation unit each); all return the launch's hipError_t.
@@ -139,6 +182,9 @@ hipError_t launch_gemv_mfma(int mode, const int8_t* wq, const uint16_t* ws, int6
 hipError_t launch_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq,
                              const int8_t* xl, int64_t B, int32_t* dh, int32_t* dl, hipStream_t st);
 hipError_t launch_combine(const float* part, int splits, int64_t count, float* y, hipStream_t st);
+size_t sk_workspace_bytes(int64_t N, int splits);
+hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                          const int8_t* xl, const float* xs, int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
 hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
                          hipStream_t st);

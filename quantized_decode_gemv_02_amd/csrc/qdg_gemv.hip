@@ -42,11 +42,17 @@ constexpr int LDS_BUDGET = 56 * 1024;  // window bytes per workgroup
 template <int MODE, int RPW>
 constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * (WG / 64) * RPW; }
 
-template <int MODE, int RPW, int U>
+// FUSED = false: out receives y (S == 1) or the partials [S][N].
+// FUSED = true: with S > 1 the workgroup writes its partials to out, and the
+//   last workgroup of a row tile to finish (an atomic ticket per tile) sums the
+//   tile's S partials in ascending order into y and resets the ticket -- which
+//   chunk finishes last changes nothing in the result.
+template <int MODE, int RPW, int U, bool FUSED>
 __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
-                                                 const float* __restrict__ xs, int64_t N, int64_t K, int S,
-                                                 int win, float* __restrict__ out) {
+                                                 const float* __restrict__ xs, int64_t N, int64_t K, int S, int win,
+                                                 float* __restrict__ out,
+                                                 unsigned* __restrict__ tickets, float* __restrict__ y) {
   constexpr int LPR = 64 / RPW;  // lanes per row
   constexpr int BPS = LPR / 2;   // blocks per step of a row
   constexpr int TPP = BPS / 4;   // steps of one partial per step (1 or 2)
@@ -127,8 +133,39 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   }
   // (P0 + P2) + (P1 + P3): partial q sits in lane 2q of the row.
   const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
-  const float y = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
-  if (li == 0 && row_ok) out[(int64_t)s_idx * N + o] = y;
+  const float yv = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+  if constexpr (!FUSED) {
+    if (li == 0 && row_ok) out[(int64_t)s_idx * N + o] = yv;
+  } else {
+    if (S == 1) {
+      if (li == 0 && row_ok) y[o] = yv;
+      return;
+    }
+    // Publish the partials without an L2-wide release: the partial stores and the
+    // last arriver's loads are agent-scope atomic accesses (coherent across the
+    // XCDs' L2s by themselves), each writer waits until its store has completed
+    // (s_waitcnt vmcnt(0)) before the workgroup barrier, and only then does one
+    // thread take the ticket (an agent-scope RMW).  The last arriver's loads are
+    // issued after it has seen the ticket, so they return every chunk's partial.
+    if (li == 0 && row_ok)
+      __hip_atomic_store(out + (int64_t)s_idx * N + o, yv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
+    __syncthreads();
+    __shared__ int last_arrival;
+    if (threadIdx.x == 0)
+      last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)(S - 1);
+    __syncthreads();
+    if (!last_arrival) return;
+    if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
+      const int64_t oo = o_wg + threadIdx.x;
+      float a = 0.0f;
+      for (int s = 0; s < S; ++s)
+        a = __fadd_rn(a, __hip_atomic_load(out + (int64_t)s * N + oo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      y[oo] = a;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 struct Tuning {
@@ -151,39 +188,45 @@ Tuning tuning() {
   return t;
 }
 
-template <int MODE, int RPW, int U>
-hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
-                    const int8_t* xl, const float* xs, int splits, float* out, hipStream_t st) {
+int window_blocks(int64_t K, int splits, int bytes_per_block) {
   int32_t mx = 0;
   for (int s = 0; s < splits; ++s) {
     int32_t g0, g1;
     split_range(K, splits, s, g0, g1);
     mx = g1 - g0 > mx ? g1 - g0 : mx;
   }
-  const int cap = (LDS_BUDGET / window_bytes_per_block<MODE, RPW>()) / SUPER * SUPER;
+  const int cap = (LDS_BUDGET / bytes_per_block) / SUPER * SUPER;
   int win = ((mx + SUPER - 1) / SUPER) * SUPER;
   if (win > cap) win = cap;
   if (win < SUPER) win = SUPER;
-  const size_t lds = (size_t)win * window_bytes_per_block<MODE, RPW>();
+  return win;
+}
+
+template <int MODE, int RPW, int U, bool FUSED>
+hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                    const float* xs, int splits, float* out, unsigned* tickets, float* y, hipStream_t st) {
+  constexpr int bpb = window_bytes_per_block<MODE, RPW>();
+  const int win = window_blocks(K, splits, bpb);
   const int rows_per_wg = (WG / 64) * RPW;
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
-  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, splits,
-                     win, out);
+  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U, FUSED>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs, N,
+                     K, splits, win, out, tickets, y);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool FUSED>
 hipError_t launch_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
-                       const int8_t* xl, const float* xs, int splits, float* out, hipStream_t st) {
+                       const int8_t* xl, const float* xs, int splits, float* out, unsigned* tickets, float* y,
+                       hipStream_t st) {
   const Tuning t = tuning();
   if (t.rpw == 8) {
-    if (t.unroll == 2) return launch_t<MODE, 8, 2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
-    if (t.unroll == 8) return launch_t<MODE, 8, 8>(wq, ws, N, K, xq, xl, xs, splits, out, st);
-    return launch_t<MODE, 8, 4>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+    if (t.unroll == 2) return launch_t<MODE, 8, 2, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+    if (t.unroll == 8) return launch_t<MODE, 8, 8, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+    return launch_t<MODE, 8, 4, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
   }
-  if (t.unroll == 2) return launch_t<MODE, 4, 2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
-  if (t.unroll == 8) return launch_t<MODE, 4, 8>(wq, ws, N, K, xq, xl, xs, splits, out, st);
-  return launch_t<MODE, 4, 4>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  if (t.unroll == 2) return launch_t<MODE, 4, 2, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+  if (t.unroll == 8) return launch_t<MODE, 4, 8, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+  return launch_t<MODE, 4, 4, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
 }
 
 }  // namespace
@@ -191,8 +234,27 @@ hipError_t launch_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t 
 hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                             const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* out,
                             hipStream_t st) {
-  if (mode == 1) return launch_mode<1>(wq, ws, N, K, xq, xl, xs, splits, out, st);
-  return launch_mode<2>(wq, ws, N, K, xq, xl, xs, splits, out, st);
+  if (mode == 1) return launch_mode<1, false>(wq, ws, N, K, xq, xl, xs, splits, out, nullptr, nullptr, st);
+  return launch_mode<2, false>(wq, ws, N, K, xq, xl, xs, splits, out, nullptr, nullptr, st);
+}
+
+// Workspace of the in-kernel combine, each part 256-byte aligned: one ticket per
+// row tile (room for 16-row tiles), then the split partials [S][N].
+constexpr int64_t TILE_ROWS = 16;
+int64_t pad256(int64_t b) { return (b + 255) / 256 * 256; }
+int64_t sk_partials_offset(int64_t N) { return pad256(((N + TILE_ROWS - 1) / TILE_ROWS) * 4); }
+
+size_t sk_workspace_bytes(int64_t N, int splits) {
+  return (size_t)(sk_partials_offset(N) + pad256((int64_t)splits * N * 4));
+}
+
+hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                          const int8_t* xl, const float* xs, int splits, float* y, void* workspace, hipStream_t st) {
+  if (splits == 1) return launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, 1, y, st);
+  unsigned* tickets = (unsigned*)workspace;
+  float* part = (float*)((char*)workspace + sk_partials_offset(N));
+  if (mode == 1) return launch_mode<1, true>(wq, ws, N, K, xq, xl, xs, splits, part, tickets, y, st);
+  return launch_mode<2, true>(wq, ws, N, K, xq, xl, xs, splits, part, tickets, y, st);
 }
 
 }  // namespace qdg

@@ -15,24 +15,6 @@
 namespace qdg {
 namespace {
 
-__device__ __forceinline__ float lanes8_max(float a) {
-  a = fmaxf(a, __shfl_xor(a, 1, 64));
-  a = fmaxf(a, __shfl_xor(a, 2, 64));
-  a = fmaxf(a, __shfl_xor(a, 4, 64));
-  return a;
-}
-
-// rn() of the page with a saturating clamp to int8 (no-op inside the contract).
-__device__ __forceinline__ int rn_clamp8(float v) {
-  const float r = __builtin_rintf(v);
-  return (int)__builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
-}
-
-__device__ __forceinline__ int pack4(int a, int b, int c, int d) {
-  return (int)((unsigned)(a & 255) | ((unsigned)(b & 255) << 8) | ((unsigned)(c & 255) << 16) |
-               ((unsigned)(d & 255) << 24));
-}
-
 template <int MODE>
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int8_t* __restrict__ xq,
                                                   int8_t* __restrict__ xl, float* __restrict__ xs,
@@ -43,28 +25,11 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, i
   const bool on = blk < nblocks;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (on) v = *(const float4*)(x + blk * QK + sub * 4);
-  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = lanes8_max(a);
+  int h, l;
+  const float s = quant_lane4<MODE>(v, &h, &l);
   if (!on) return;
-  const float vv[4] = {v.x, v.y, v.z, v.w};
-  int h[4], l[4];
-  float s;
-  if constexpr (MODE == 1) {
-    s = a > 0.0f ? a / 127.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = rn_clamp8(vv[i] / s);
-  } else {
-    s = (a > 1e-30f ? a : 1e-30f) / 127.0f;
-    const float lsc = __fmul_rn(s, 0.0078125f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = rn_clamp8(vv[i] / s);
-      const float r = __fmaf_rn(-(float)h[i], s, vv[i]);
-      l[i] = rn_clamp8(r / lsc);
-    }
-    *(int*)(xl + blk * QK + sub * 4) = pack4(l[0], l[1], l[2], l[3]);
-  }
-  *(int*)(xq + blk * QK + sub * 4) = pack4(h[0], h[1], h[2], h[3]);
+  *(int*)(xq + blk * QK + sub * 4) = h;
+  if constexpr (MODE == 2) *(int*)(xl + blk * QK + sub * 4) = l;
   if (sub == 0) xs[blk] = s;
 }
 

@@ -258,3 +258,24 @@ def test_repeat_and_fresh_buffers_bitwise():
                 outs.append(host(y))
         for o in outs[1:]:
             assert o.tobytes() == outs[0].tobytes()
+
+
+# ---------------------------------------------------------------- split-K with in-kernel combine
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 8), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
+                                   (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4)])
+def test_in_kernel_combine_bit_exact(mode, N, K, S):
+    announce(f"gemv_q8_sk mode={mode} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, 1, 11 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    wqd, wsd = dev(wq), dev(ws)
+    xq, xl, xs = quantize_gpu(mode, x)
+    wsp = q.sk_workspace(N, S)
+    for rep in range(3):  # the tickets must come back to zero after every call
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_sk(mode, wqd, wsd, y, xq, xl, xs, S, wsp)
+        np.testing.assert_array_equal(host(y), want)
+    tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
+    assert not tickets.any()
