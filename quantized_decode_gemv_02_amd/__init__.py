@@ -37,6 +37,13 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
                       "or `python quantized_decode_gemv_02_amd/build.py`")
 
+# The library and PyTorch must share one HIP runtime: PyTorch's libamdhip64.so
+# has the soname libamdhip64.so.7 that libqdg.so needs, so loading torch first
+# makes the dynamic linker bind libqdg.so to that copy.  Loaded the other way
+# round, torch brings a second runtime into the process and the library's own
+# runtime then finds no device (hipErrorNoDevice at the first launch).
+import torch  # noqa: E402,F401  (load order only)
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

@@ -66,12 +66,12 @@ __device__ __forceinline__ unsigned short ld_u16_stream(const uint16_t* p) {
 // Copies the weight scales of `rows` consecutive rows (first row o0, rows at or
 // past N read row N-1) over blocks [b0, b0 + n) into LDS as [row][n_pitch]
 // (binary16 bits), with `nthreads` threads of index `tid`.  When a row's segment
-// starts 16-byte aligned (nb and b0 multiples of 8) the bulk moves in 16-byte
-// words and only the last n mod 8 scales of a row move one by one.
+// starts 16-byte aligned (ws 16-byte aligned, nb and b0 multiples of 8) the bulk
+// moves in 16-byte words and only the last n mod 8 scales of a row move one by one.
 __device__ __forceinline__ void stage_scales(uint16_t* __restrict__ dst, int pitch, const uint16_t* __restrict__ ws,
                                              int64_t nb, int64_t N, int64_t o0, int rows, int64_t b0, int n,
                                              int tid, int nthreads) {
-  const bool wide = (nb % 8) == 0 && (b0 % 8) == 0 && (pitch % 8) == 0;
+  const bool wide = (nb % 8) == 0 && (b0 % 8) == 0 && (pitch % 8) == 0 && ((uintptr_t)ws & 15) == 0;
   const int nv = wide ? n / 8 : 0;  // 16-byte words per row
   for (int i = tid; i < rows * nv; i += nthreads) {
     const int r = i / nv, c = i - r * nv;

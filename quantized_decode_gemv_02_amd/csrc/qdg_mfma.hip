@@ -8,43 +8,61 @@
 // block dots come from differs: here one v_mfma_i32_16x16x32_i8 gives the 16x16
 // dots of 16 activation rows t by 16 weight rows o over one 32-value block.
 //
-//  * A wave owns one tile of 16 weight rows.  Lane (col = l%16, grp = l/16)
-//    loads 16 bytes at offset 16*grp of a 64-byte span (two blocks) of weight
-//    row o0+col (B operand) and of activation row t = col (A operand); two
-//    v_permlane32_swap per fragment regroup the bytes so that each block is one
-//    16x16x32 MFMA (split_span).  A "quad" of 4 blocks (128 bytes a row, blocks
-//    g = 4m..4m+3) takes two spans and four MFMAs, block 4m+k landing in
-//    partial k -- compile-time register indices.
-//  * The MFMA result gives lane (col, grp) the dots of t = 4*grp + i (i < 4)
-//    with o = o0 + col; that lane keeps the 4 partials of those 4 (t, o) pairs,
-//    so every chain lives in one lane, in ascending block order.
-//  * The window of the chunk is staged in LDS once per workgroup of 4 waves (64
-//    weight rows): the 16 activation rows' words (read as the MFMA A operand with
-//    ds_read_b128; rows padded so the 16 rows fall on distinct banks), their
-//    scales as [t][block] (four ds_read_b128 give a lane its 4 rows' scales of a
-//    quad), and the weight scales of the 64 rows (one ds_read_b64 per quad).
-//  * Weight loads run a group of QD quads ahead of the MFMAs (the next group is
-//    requested before the current group is computed; the first group before the
-//    window's barrier); the weight stream uses the nontemporal hint.
+//  * A workgroup of 8 waves owns 32 weight rows (two tiles of 16) and walks its
+//    chunk of K in steps of 8 blocks (256 bytes a row).  Wave v = 4*tau + r works
+//    on tile tau and owns partial r: blocks r and r + 4 of every step (steps start
+//    at multiples of 8 blocks from the chunk start, itself a multiple of 16, so
+//    block k of a step is partial k mod 4).  Each of its chains runs in one lane,
+//    in ascending block order, and the four partials meet once, at the end, in
+//    the fixed order (P0 + P2) + (P1 + P3).
+//  * Loads: wave v reads rows 4*v .. 4*v + 3 of the step, 256 contiguous bytes a
+//    row (lane (r = l/16, c = l%16) takes 16 bytes at 16*c of row 4*v + r): whole
+//    128-byte lines, the layout that streams HBM best.  The words go to a shared
+//    LDS tile of 32 rows x 256 bytes, where the MFMA reads them transposed (lane
+//    col = l%16 is a weight row, l/16 picks 8 of the block's 32 bytes).  The
+//    16-byte chunks of row r sit at chunk index c ^ (r mod 16), so the writes
+//    and the reads spread over all banks.
+//  * The A operand is activation row t = col, the same 8 bytes of the block; the
+//    MFMA result gives lane (col, grp = l/16) the dots of t = 4*grp + i (i < 4)
+//    with weight row col of its tile.
+//  * Shared step data -- the 32 rows' weight words, the 16 activation rows' words,
+//    their scales and the 32 rows' weight scales -- lives in LDS in two slots:
+//    step s's data is loaded into registers ahead of step s (weights P - 1 steps
+//    ahead in a ring, the rest 2 steps ahead), written to slot s mod 2 at the
+//    start of step s, and one workgroup barrier a step makes it visible.
+//  * The loop is a uniform software pipeline: every step issues the same loads,
+//    all unconditional (addresses past the chunk are clamped to its last block,
+//    whose extra data is never summed), and the loop starts at the virtual step
+//    -P, so the compiler's wait counts keep the look-ahead in flight.
 //  * Weight rows past N read row N-1 and store nothing; activation rows t >= B
-//    are zero and store nothing.
+//    read row B-1 and store nothing (an MFMA row never mixes into another).
+#include <stdlib.h>
+
 #include "qdg_device.h"
 
 namespace qdg {
 namespace {
 
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;                  // 2 row tiles x 4 partials
 constexpr int WG = 64 * WAVES;
-constexpr int LDS_BUDGET = 78 * 1024;  // two workgroups of 4 waves per CU
+constexpr int ROWS = 32;                  // weight rows a workgroup
+constexpr int STEP = 8;                   // blocks per step: 256 bytes of a weight row
+constexpr int WTILE = ROWS * STEP * QK;   // one slot of the shared weight tile
+constexpr int APITCH = STEP * QK + 16;    // bytes per staged activation row (padded: rows on distinct banks)
 
-// LDS bytes per block of the window: the 16 activation rows' words (both words
-// under TwoPass; rows padded by 16 bytes so that the 16 rows of a ds_read_b128
-// fall on distinct banks), their scales, and the weight scales of the rows.
+// One LDS slot of staged step data besides the weights: activation words (both
+// under TwoPass), activation scales [16][8], weight scales [32][8].
 template <int MODE>
-constexpr int lds_per_block() { return (MODE == 2 ? 2 : 1) * 16 * QK + 16 * 4 + WAVES * 16 * 2; }
-constexpr int ROW_PAD = 16;
+struct Slot {
+  static constexpr int A = 0;
+  static constexpr int L = A + 16 * APITCH;
+  static constexpr int SX = L + (MODE == 2 ? 16 * APITCH : 0);
+  static constexpr int SG = SX + 16 * STEP * 4;
+  static constexpr int BYTES = SG + ROWS * STEP * 2;
+};
+template <int MODE>
+constexpr int lds_bytes() { return 2 * WTILE + 2 * Slot<MODE>::BYTES; }
+static_assert(2 * WTILE >= WAVES * 64 * 4 * 4, "the final reduction reuses the weight tile");
 
 // One 32-value block's 16x16 dots: A and B hold 8 bytes a lane, k-group l/16.
 __device__ __forceinline__ v4i mfma16x16x32(long a, long b) {
@@ -52,191 +70,452 @@ __device__ __forceinline__ v4i mfma16x16x32(long a, long b) {
   return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, z, 0, 0, 0);
 }
 
-// A 16-byte fragment loaded at offset 16*g of a 64-byte span (two blocks) holds,
-// in lane groups g = 0..3, bytes [0,16) and [16,32) of the first block and
-// [0,16), [16,32) of the second.  Swapping registers 2-3 of the lower 32 lanes
-// with registers 0-1 of the upper 32 lanes (v_permlane32_swap) leaves registers
-// 0-1 of the four groups holding the first block's bytes [0,8), [16,24), [8,16),
-// [24,32) and registers 2-3 the second block's in the same arrangement: one
-// 16x16x32 MFMA per block, no masking.  Both operands take the same swap, so the
-// bytes they multiply pairwise are the same k.
-struct Halves {
-  long first, second;
+// Byte offset of 16-byte chunk c of row r in a weight tile slot.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * (STEP * QK) + (((c ^ r) & 15) << 4); }
+
+// The shared data of one step besides the weights, in registers between its
+// loads and its LDS store.  Thread tid (of 512) moves: activation word c = tid%16
+// of row t = (tid%256)/16 -- high words for tid < 256, low words (TwoPass) for the
+// rest; activation scale k = tid%8 of row (tid%128)/8; weight scales of row
+// tid%32 -- all 8 in one 16-byte word when WIDE, else scale (tid%256)/32 of it.
+// Threads whose share repeats another's load it too and store nothing, so every
+// thread issues the same loads.
+template <int MODE, bool WIDE>
+struct StepStage {
+  v4i h;
+  float sx;
+  v4i sw;            // WIDE
+  unsigned short sh;  // not WIDE
+
+  __device__ __forceinline__ void load(const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                       const float* __restrict__ xs, const uint16_t* __restrict__ ws,
+                                       int64_t N, int64_t K, int B, int64_t o_wg, int blk0, int g1) {
+    const int tid = threadIdx.x;
+    const int64_t nb = K / QK;
+    const int t = min((tid & 255) >> 4, B - 1), c = tid & 15;
+    const int ba = min(blk0 + (c >> 1), g1 - 1);  // block of activation word c
+    const int8_t* src = (MODE == 2 && tid >= 256) ? xl : xq;
+    h = *(const v4i*)(src + (int64_t)t * K + (int64_t)ba * QK + 16 * (c & 1));
+    const int ts = min((tid & 127) >> 3, B - 1), ks = tid & 7;
+    sx = xs[(int64_t)ts * nb + min(blk0 + ks, g1 - 1)];
+    int64_t o = o_wg + (tid & 31);
+    if (o >= N) o = N - 1;
+    if constexpr (WIDE) {
+      // steps are whole when WIDE (K/32 and chunk ends are multiples of 8); the
+      // clamp only keeps the look-ahead past the chunk in bounds
+      sw = *(const v4i*)(ws + o * nb + min(blk0, g1 - STEP));
+    } else {
+      sh = ws[o * nb + min(blk0 + ((tid & 255) >> 5), g1 - 1)];
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char* slot) const {
+    const int tid = threadIdx.x;
+    const int t = (tid & 255) >> 4, c = tid & 15;
+    if (tid < 256) *(v4i*)(slot + Slot<MODE>::A + t * APITCH + 16 * c) = h;
+    if (MODE == 2 && tid >= 256) *(v4i*)(slot + Slot<MODE>::L + t * APITCH + 16 * c) = h;
+    if (tid < 128) ((float*)(slot + Slot<MODE>::SX))[tid] = sx;  // [t][k] = tid
+    uint16_t* sg = (uint16_t*)(slot + Slot<MODE>::SG);             // [row][8]
+    if constexpr (WIDE) {
+      if (tid < 32) *(v4i*)(sg + tid * STEP) = sw;
+    } else {
+      if (tid < 256) sg[(tid & 31) * STEP + (tid >> 5)] = sh;
+    }
+  }
 };
-__device__ __forceinline__ Halves split_span(v4i v) {
-  const auto p02 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
-  const auto p13 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
-  Halves h;
-  h.first = (long)(((unsigned long)(unsigned)p13[0] << 32) | (unsigned)p02[0]);
-  h.second = (long)(((unsigned long)(unsigned)p13[1] << 32) | (unsigned)p02[1]);
-  return h;
-}
 
-__device__ __forceinline__ v4i ld16v_stream(const int8_t* p) { return __builtin_nontemporal_load((const v4i*)p); }
-
-template <int MODE, int QD>
+template <int MODE, int P, bool WIDE>
 __global__ __launch_bounds__(WG) void k_gemv_mfma(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
                                                  const float* __restrict__ xs, int64_t N, int64_t K, int B, int S,
-                                                 int win, float* __restrict__ out) {
+                                                 float* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int apitch = win * QK + ROW_PAD;                       // bytes per activation row in LDS
-  int8_t* la = (int8_t*)lds;                                   // [16][apitch] high words
-  int8_t* ll = la + 16 * apitch;                               // [16][apitch] low words (TwoPass)
-  float* sx = (float*)(lds + (MODE == 2 ? 2 : 1) * 16 * apitch);  // [16][win] activation scales
-  uint16_t* sgl = (uint16_t*)(sx + 16 * win);                  // [WAVES*16][win] weight scales
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tau = wave >> 2, res = wave & 3;  // row tile, owned partial
+  unsigned char* wtile = lds;                 // [2 slots][32 rows][256 bytes]
+  unsigned char* slots = lds + 2 * WTILE;     // [2 slots] of Slot<MODE>
   const int col = lane & 15, grp = lane >> 4;
-  const int64_t nb = K / QK;
   const int s_idx = blockIdx.y;
   int32_t g0, g1;
   split_range(K, S, s_idx, g0, g1);
+  const int nsteps = (g1 - g0 + STEP - 1) / STEP;
 
-  const int64_t o_wg = (int64_t)blockIdx.x * WAVES * 16;
-  const int64_t o0 = o_wg + wave * 16;
-  int64_t o = o0 + col;
-  if (o >= N) o = N - 1;
-  const int8_t* wrow = wq + o * K + grp * 16;
-  const uint16_t* my_sg = sgl + (wave * 16 + col) * win;
-  const int8_t* my_a = la + col * apitch + grp * 16;  // A operand: activation row t = col
-  const int8_t* my_l = ll + col * apitch + grp * 16;
-  const bool lo_half = grp < 2;  // lane groups 0-1 load the first block of a span
-  const v4i z4 = {0, 0, 0, 0};
+  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  // load side: lane (r = grp, c = col) reads row 4*wave + r, 16-byte chunk c of
+  // the step (half (c & 1) of block c >> 1)
+  const int lrow = 4 * wave + grp;
+  int64_t lo = o_wg + lrow;
+  if (lo >= N) lo = N - 1;
+  const int8_t* wrow = wq + lo * K + 16 * (col & 1);
+  const int cblk = col >> 1;
+  const int w_st = tile_off(lrow, col);  // where this lane's word goes in a tile slot
+  // read side: rows 16*tau + col of the tile, blocks res and res + 4
+  int w_rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) w_rd[h] = tile_off(16 * tau + col, 2 * (res + 4 * h) + (grp >> 1)) + 8 * (grp & 1);
+  const int a_off = Slot<MODE>::A + col * APITCH + 8 * grp;  // A operand: activation row t = col
+  const int l_off = Slot<MODE>::L + col * APITCH + 8 * grp;
+  const int sx_off = Slot<MODE>::SX + grp * 4 * STEP * 4;    // rows 4*grp .. 4*grp + 3
+  const int sg_off = Slot<MODE>::SG + (16 * tau + col) * STEP * 2;
 
-  float p[4][4];  // [i][partial]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) p[i][q] = 0.0f;
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // partial `res` of (t = 4*grp + i, o = o_wg + 16*tau + col)
 
-  // Weight loads of QD quads (blocks bq .. bq + 4*QD - 1, none at or past `end`).
-  auto issue = [&](int bq, int end, v4i (&w)[QD][2]) {
+  StepStage<MODE, WIDE> st[2];
+  v4i wr[P];
+  // The loop starts at the virtual step -P: steps below 0 only issue loads (of
+  // step 0 where they would look before it), so every iteration -- the first
+  // ones included -- issues the same loads in the same order.  The start value
+  // passes through an empty asm statement so that the compiler cannot peel the
+  // first iterations into a prologue with a different load order.
+  int first = -P;
+  asm volatile("" : "+s"(first));
+  // an empty chunk (K < 512 with several chunks) loads nothing: its partials stay +0
+  if (g1 <= g0) first = nsteps;
+  for (int s0 = first; s0 < nsteps; s0 += P) {
 #pragma unroll
-    for (int qd = 0; qd < QD; ++qd) {
-      const int b = bq + 4 * qd;
-      const bool v0 = b < end, v1 = b + 1 < end, v2 = b + 2 < end, v3 = b + 3 < end;
-      w[qd][0] = v0 && (lo_half || v1) ? ld16v_stream(wrow + (int64_t)b * QK) : z4;
-      w[qd][1] = v2 && (lo_half || v3) ? ld16v_stream(wrow + (int64_t)b * QK + 64) : z4;
-    }
-  };
-  v4i wv[QD][2];
-  issue(g0, min(g0 + win, g1), wv);  // the first group's weights fly across the first barrier
-  for (int wb0 = g0; wb0 < g1; wb0 += win) {
-    const int wb1 = min(wb0 + win, g1);
-    const int nwb = wb1 - wb0;
-    __syncthreads();
-    // activation words of the window: 16 rows x nwb blocks, 16 bytes a thread-step (rows t >= B are zero)
-    for (int i = threadIdx.x; i < 16 * nwb * 2; i += WG) {
-      const int t = i / (nwb * 2), c = i - t * nwb * 2;
-      int4 h = make_int4(0, 0, 0, 0), l = h;
-      if (t < B) {
-        h = *(const int4*)(xq + (int64_t)t * K + (int64_t)wb0 * QK + 16 * c);
-        if constexpr (MODE == 2) l = *(const int4*)(xl + (int64_t)t * K + (int64_t)wb0 * QK + 16 * c);
+    for (int u = 0; u < P; ++u) {
+      const int s = s0 + u;
+      // uniform over the workgroup; leaves both loops, so no path runs from a
+      // partial group back to the loop head (the wait counts stay exact)
+      if (s >= nsteps) goto done;
+      unsigned char* slot = slots + (u & 1) * Slot<MODE>::BYTES;  // P is even: slot s mod 2
+      unsigned char* tile = wtile + (u & 1) * WTILE;
+      if (s >= 0) {  // step s's data: weights loaded during step s - P + 1, the rest during s - 2
+        st[u & 1].store(slot);
+        *(v4i*)(tile + w_st) = wr[u];
       }
-      *(int4*)(la + t * apitch + 16 * c) = h;
-      if constexpr (MODE == 2) *(int4*)(ll + t * apitch + 16 * c) = l;
-    }
-    for (int i = threadIdx.x; i < 16 * nwb; i += WG) {
-      const int t = i / nwb, bl = i - t * nwb;
-      sx[t * win + bl] = t < B ? xs[(int64_t)t * nb + wb0 + bl] : 0.0f;
-    }
-    stage_scales(sgl, win, ws, nb, N, o_wg, WAVES * 16, wb0, nwb, threadIdx.x, WG);
-    __syncthreads();
-
-    // Groups of QD quads (win and the chunk start are multiples of 16 = 4*QD
-    // blocks, so groups never straddle a window); the next group's weights --
-    // across a window boundary too -- are requested before the current group's
-    // MFMAs.  b - g0 is a multiple of 4, so block b + k is partial k.
-    for (int bq = wb0; bq < wb1; bq += 4 * QD) {
-      v4i wn[QD][2];
-      if (bq + 4 * QD < wb1)
-        issue(bq + 4 * QD, wb1, wn);
-      else if (wb1 < g1)
-        issue(wb1, min(wb1 + win, g1), wn);  // the next window's first group
+      st[u & 1].load(xq, xl, xs, ws, N, K, B, o_wg, g0 + max(s + 2, 0) * STEP, g1);
+      {
+        const int blk = min(g0 + max(s + P - 1, 0) * STEP + cblk, g1 - 1);
+        wr[(u + P - 1) % P] = __builtin_nontemporal_load((const v4i*)(wrow + (int64_t)blk * QK));
+      }
+      __syncthreads();
+      if (s >= 0) {  // uniform; steps below 0 only load
+        const int b = g0 + s * STEP;
+        const v4i sg8 = *(const v4i*)(slot + sg_off);  // the row's 8 weight scales of the step
 #pragma unroll
-      for (int qd = 0; qd < QD; ++qd) {
-        const int b = bq + 4 * qd;
-        if (b >= wb1) break;  // uniform over the wave
-        const int bl = b - wb0;
-        const bool vk[4] = {true, b + 1 < wb1, b + 2 < wb1, b + 3 < wb1};
-        const Halves a0 = split_span(*(const v4i*)(my_a + bl * QK));
-        const Halves a1 = split_span(*(const v4i*)(my_a + bl * QK + 64));
-        const Halves w0 = split_span(wv[qd][0]), w1 = split_span(wv[qd][1]);
-        v4i D[4], E[4];
-        D[0] = mfma16x16x32(a0.first, w0.first);
-        D[1] = mfma16x16x32(a0.second, w0.second);
-        D[2] = mfma16x16x32(a1.first, w1.first);
-        D[3] = mfma16x16x32(a1.second, w1.second);
-        if constexpr (MODE == 2) {
-          const Halves l0 = split_span(*(const v4i*)(my_l + bl * QK));
-          const Halves l1 = split_span(*(const v4i*)(my_l + bl * QK + 64));
-          E[0] = mfma16x16x32(l0.first, w0.first);
-          E[1] = mfma16x16x32(l0.second, w0.second);
-          E[2] = mfma16x16x32(l1.first, w1.first);
-          E[3] = mfma16x16x32(l1.second, w1.second);
-        }
-        const v2u sg2 = *(const v2u*)(my_sg + bl);  // the row's 4 weight scales of the quad
-        const unsigned short sg[4] = {(unsigned short)(sg2[0] & 0xffffu), (unsigned short)(sg2[0] >> 16),
-                                      (unsigned short)(sg2[1] & 0xffffu), (unsigned short)(sg2[1] >> 16)};
-        float sv[4][4];  // [i][k]: scale of activation row 4*grp + i at block b + k
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 s4 = *(const float4*)(sx + (grp * 4 + i) * win + bl);
-          sv[i][0] = s4.x; sv[i][1] = s4.y; sv[i][2] = s4.z; sv[i][3] = s4.w;
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (!vk[k]) continue;  // uniform over the wave
-          const float sgm = half_bits_to_float(sg[k]);
+        for (int h = 0; h < 2; ++h) {
+          const int k = res + 4 * h;
+          if (b + k >= g1) break;  // uniform over the wave
+          const long wk = *(const long*)(tile + w_rd[h]);
+          const v4i D = mfma16x16x32(*(const long*)(slot + a_off + k * QK), wk);
+          v4i E = {0, 0, 0, 0};
+          if constexpr (MODE == 2) E = mfma16x16x32(*(const long*)(slot + l_off + k * QK), wk);
+          const unsigned sgw = (unsigned)sg8[k >> 1];
+          const float sgm = half_bits_to_float((unsigned short)((k & 1) ? (sgw >> 16) : (sgw & 0xffffu)));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            const float sig = *(const float*)(slot + sx_off + (i * STEP + k) * 4);
             float ta, tb;
-            q8_term<MODE>(sgm, sv[i][k], D[k][i], MODE == 2 ? E[k][i] : 0, ta, tb);
-            p[i][k] = __fmaf_rn(ta, tb, p[i][k]);
+            q8_term<MODE>(sgm, sig, D[i], E[i], ta, tb);
+            p[i] = __fmaf_rn(ta, tb, p[i]);
           }
         }
       }
+    }
+  }
+done:
+  // the four partials of each output meet in a fixed order: (P0 + P2) + (P1 + P3)
+  __syncthreads();  // every wave is done with the tile, which now holds the partials
+  float* red = (float*)lds;  // [wave][i][lane]
 #pragma unroll
-      for (int qd = 0; qd < QD; ++qd) {
-        wv[qd][0] = wn[qd][0];
-        wv[qd][1] = wn[qd][1];
+  for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = p[i];
+  __syncthreads();
+  if (res == 0) {
+    const int64_t oo = o_wg + 16 * tau + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = grp * 4 + i;
+      const float q0 = red[((4 * tau + 0) * 4 + i) * 64 + lane], q1 = red[((4 * tau + 1) * 4 + i) * 64 + lane];
+      const float q2 = red[((4 * tau + 2) * 4 + i) * 64 + lane], q3 = red[((4 * tau + 3) * 4 + i) * 64 + lane];
+      const float y = __fadd_rn(__fadd_rn(q0, q2), __fadd_rn(q1, q3));
+      if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+    }
+  }
+}
+
+template <int MODE, int P, bool WIDE>
+hipError_t launch_mg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
+  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)splits), block(WG);
+  hipLaunchKernelGGL((k_gemv_mfma<MODE, P, WIDE>), grid, block, lds_bytes<MODE>(), st, wq, ws, xq, xl, xs, N, K,
+                     (int)B, splits, out);
+  return hipGetLastError();
+}
+
+template <int MODE, int P>
+hipError_t launch_mp(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
+  // 16-byte weight-scale words need ws 16-byte aligned and K/32 a multiple of 8
+  if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0)
+    return launch_mg<MODE, P, true>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+  return launch_mg<MODE, P, false>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+}
+
+// ---------------------------------------------------------------------------
+// The fast path for K a multiple of 256 and ws 16-byte aligned.  Same sums and
+// operand layouts as k_gemv_mfma, but a workgroup of 8 waves owns 32*TPW weight
+// rows (2*TPW tiles of 16), wave v = 4*g + r working on tiles g, g + 2, ...
+// (TPW of them, one A operand read serving all) for partial r, and every byte of
+// a step -- weights, activation words, scales -- moves from global memory
+// straight into LDS (global_load_lds) into a ring of P slots, P - 1 steps
+// ahead.  More rows a workgroup means fewer re-reads of the activations, which
+// every workgroup needs in full.  No data passes through registers, so nothing
+// the compiler schedules can make a wave wait on loads that are still ahead of
+// it; instead every wave issues exactly dma_loads() loads a step and waits,
+// before each step's barrier, until only the later steps' loads are outstanding
+// (s_waitcnt vmcnt).  The barrier then makes the whole workgroup's copies of the
+// step visible, and the slot it refills for step s + P - 1 was last read in step
+// s - 1, which every wave has finished.
+//
+// Slot layout: W [32*TPW rows][256] and A (L) [16 rows][256] with the 16-byte
+// chunk c of row r at chunk index c ^ (r mod 16) -- a wave's load writes 1 KiB in
+// lane order, so lane (r4 = l/16, j = l%16) fetches global chunk j ^ row to land
+// it in place; SX [16][8] activation scales; SG [32*TPW][8] weight scales; JUNK
+// for loads that only keep the count uniform.
+template <int MODE, int TPW>
+struct DSlot {
+  static constexpr int DROWS = 32 * TPW;
+  static constexpr int W = 0;
+  static constexpr int A = W + DROWS * 256;
+  static constexpr int L = A + 16 * 256;
+  static constexpr int SX = L + (MODE == 2 ? 16 * 256 : 0);
+  static constexpr int SG = SX + 16 * STEP * 4;
+  static constexpr int SG_BYTES = (DROWS * 16 + 1023) / 1024 * 1024;  // whole 1 KiB loads
+  static constexpr int JUNK = SG + SG_BYTES;
+  static constexpr int BYTES = JUNK + 64 * 4;
+  // loads a wave a step: TPW of weights, then one (Int8Act) or two (TwoPass) more
+  static constexpr int DMA_LOADS = TPW + (MODE == 2 ? 2 : 1);
+};
+template <int MODE, int TPW, int P>
+constexpr int dma_lds_bytes() { return P * DSlot<MODE, TPW>::BYTES; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// global_load_lds of 16 or 4 bytes a lane; AUX 2 sets the nontemporal hint
+template <int BYTES_, int AUX>
+__device__ __forceinline__ void dma(const void* g, unsigned char* l) {
+  static_assert((BYTES_ == 16 || BYTES_ == 4) && (AUX == 0 || AUX == 2), "supported forms");
+  if constexpr (BYTES_ == 16 && AUX == 2)
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 2);
+  else if constexpr (BYTES_ == 16)
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 4, 0, 0);
+}
+
+// Waits until at most N of this wave's vector-memory loads are outstanding (and
+// its LDS accesses are done), then meets the workgroup; the empty asm
+// statements keep the compiler from moving LDS accesses across.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MODE, int TPW, int P>
+__global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+                                                     const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                     const float* __restrict__ xs, int64_t N, int64_t K, int B, int S,
+                                                     float* __restrict__ out) {
+  using SL = DSlot<MODE, TPW>;
+  constexpr int DROWS = SL::DROWS;
+  static_assert(SL::BYTES >= WAVES * TPW * 4 * 64 * 4, "the final reduction reuses slot 0");
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tg = wave >> 2, res = wave & 3;  // tile group (tiles tg, tg + 2, ...), owned partial
+  const int col = lane & 15, grp = lane >> 4;
+  const int s_idx = blockIdx.y;
+  int32_t g0, g1;
+  split_range(K, S, s_idx, g0, g1);
+  const int nsteps = (g1 - g0) / STEP;  // whole steps: K/32 and chunk ends are multiples of 8 here
+  const int64_t nb = K / QK;
+  const int64_t o_wg = (int64_t)blockIdx.x * DROWS;
+
+  // ---- load side (per lane, fixed over the steps)
+  const int r4 = lane >> 4, j = lane & 15;
+  const int8_t* wsrc[TPW];  // load m of this wave: rows 4*(8*m + wave) + r4 of the tile
+  int wcb[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int row = 4 * (8 * m + wave) + r4;
+    const int c = (j ^ row) & 15;  // fetched so that it lands at chunk j
+    int64_t o = o_wg + row;
+    if (o >= N) o = N - 1;
+    wsrc[m] = wq + o * K + 16 * (c & 1);
+    wcb[m] = c >> 1;
+  }
+  // the aux load: activation words of rows 4*(wave%4) + r4 (low words on waves 4-7 under TwoPass)
+  const int arow = 4 * (wave & 3) + r4;
+  const int ac = (j ^ arow) & 15;
+  const int8_t* asrc = ((MODE == 2 && wave >= 4) ? xl : xq) + (int64_t)min(arow, B - 1) * K + 16 * (ac & 1);
+  const int acb = ac >> 1;
+  // activation scales: load q = wave & 1 covers [t][k] = 64*q + lane
+  const int sidx = 64 * (wave & 1) + lane;
+  const float* xsrc = xs + (int64_t)min(sidx >> 3, B - 1) * nb;
+  const int sk = sidx & 7;
+  // weight scales: load gq covers rows 64*gq + lane (mod the workgroup's rows)
+  const int gq = max(MODE == 2 ? wave - 2 : wave - 6, 0);
+  int64_t so = o_wg + ((64 * gq + lane) % DROWS);
+  if (so >= N) so = N - 1;
+  const uint16_t* gsrc = ws + so * nb;
+  constexpr int NG = SL::SG_BYTES / 1024;  // weight-scale loads a step (1 or 2)
+  // which aux loads this wave issues: 0 activation words, 1 activation scales, 2 weight scales, 3 placeholder
+  //   Int8Act: waves 0-3 words, 4-5 activation scales, 6 (and 7 when NG = 2) weight scales
+  //   TwoPass, second aux load: waves 0-1 activation scales, 2 (and 3) weight scales
+  const int kind1 = MODE == 2 ? 0 : (wave < 4 ? 0 : wave < 6 ? 1 : (wave - 6 < NG ? 2 : 3));
+  const int kind2 = wave < 2 ? 1 : (wave - 2 < NG ? 2 : 3);  // TwoPass only
+  static_assert(NG <= 2, "weight-scale loads fit the waves given to them");
+
+  auto issue_aux = [&](int kind, int blk0, unsigned char* slot) {
+    if (kind == 0) {  // uniform branches: each path issues exactly one load
+      const int blk = min(blk0 + acb, g1 - 1);
+      dma<16, 0>(asrc + (int64_t)blk * QK, slot + ((MODE == 2 && wave >= 4) ? SL::L : SL::A) + (wave & 3) * 1024);
+    } else if (kind == 1) {
+      dma<4, 0>(xsrc + min(blk0 + sk, g1 - 1), slot + SL::SX + (wave & 1) * 256);
+    } else if (kind == 2) {
+      dma<16, 0>(gsrc + min(blk0, g1 - STEP), slot + SL::SG + gq * 1024);
+    } else {
+      dma<4, 0>(xs, slot + SL::JUNK);
+    }
+  };
+  auto issue = [&](int s) {  // every load of step s, into slot s mod P
+    unsigned char* slot = lds + (s % P) * SL::BYTES;
+    const int blk0 = g0 + min(s, nsteps - 1) * STEP;  // steps past the chunk repeat its last one
+#pragma unroll
+    for (int m = 0; m < TPW; ++m)  // nontemporal: the weights are streamed once
+      dma<16, 2>(wsrc[m] + (int64_t)(blk0 + wcb[m]) * QK, slot + SL::W + (8 * m + wave) * 1024);
+    issue_aux(kind1, blk0, slot);
+    if constexpr (MODE == 2) issue_aux(kind2, blk0, slot);
+  };
+
+  // ---- read side
+  int w_rd[TPW][2], a_rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 2 * (res + 4 * h) + (grp >> 1);
+    a_rd[h] = SL::A + col * 256 + (((c ^ col) & 15) << 4) + 8 * (grp & 1);
+#pragma unroll
+    for (int m = 0; m < TPW; ++m)
+      w_rd[m][h] = SL::W + (16 * (tg + 2 * m) + col) * 256 + (((c ^ col) & 15) << 4) + 8 * (grp & 1);
+  }
+  const int sx_rd = SL::SX + grp * 4 * STEP * 4;  // rows 4*grp .. 4*grp + 3
+  int sg_rd[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) sg_rd[m] = SL::SG + (16 * (tg + 2 * m) + col) * 16;
+
+  // partial `res` of (t = 4*grp + i, o = o_wg + 16*(tg + 2*m) + col)
+  float p[TPW][4];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+  // an empty chunk (K < 512 with several chunks) loads nothing: its partials stay +0
+  if (nsteps > 0) {
+#pragma unroll
+    for (int q = 0; q < P - 1; ++q) issue(q);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    wait_and_barrier<(P - 2) * SL::DMA_LOADS>();  // step s is in LDS, slot (s-1) mod P is free
+    issue(s + P - 1);
+    const unsigned char* slot = lds + (s % P) * SL::BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = res + 4 * h;
+      const long ak = *(const long*)(slot + a_rd[h]);
+      long lk = 0;
+      if constexpr (MODE == 2) lk = *(const long*)(slot + a_rd[h] + (SL::L - SL::A));
+      float sig[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sig[i] = *(const float*)(slot + sx_rd + (i * STEP + k) * 4);
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const long wk = *(const long*)(slot + w_rd[m][h]);
+        const v4i D = mfma16x16x32(ak, wk);
+        v4i E = {0, 0, 0, 0};
+        if constexpr (MODE == 2) E = mfma16x16x32(lk, wk);
+        const float sgm = half_bits_to_float(*(const unsigned short*)(slot + sg_rd[m] + 2 * k));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float ta, tb;
+          q8_term<MODE>(sgm, sig[i], D[i], E[i], ta, tb);
+          p[m][i] = __fmaf_rn(ta, tb, p[m][i]);
+        }
       }
     }
   }
-  const int64_t oo = o0 + col;
+  // the four partials of each output meet in a fixed order: (P0 + P2) + (P1 + P3)
+  wait_and_barrier<0>();  // every load has landed and every wave is done with the slots
+  float* red = (float*)lds;  // [wave][m][i][lane]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = grp * 4 + i;
-    const float y = __fadd_rn(__fadd_rn(p[i][0], p[i][2]), __fadd_rn(p[i][1], p[i][3]));
-    if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * TPW + m) * 4 + i) * 64 + lane] = p[m][i];
+  wait_and_barrier<0>();
+  if (res == 0) {
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int64_t oo = o_wg + 16 * (tg + 2 * m) + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = grp * 4 + i;
+        float q[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q[r] = red[(((4 * tg + r) * TPW + m) * 4 + i) * 64 + lane];
+        const float y = __fadd_rn(__fadd_rn(q[0], q[2]), __fadd_rn(q[1], q[3]));
+        if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+      }
+    }
   }
+}
+
+template <int MODE, int TPW, int P>
+hipError_t launch_dma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                      const int8_t* xl, const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
+  constexpr int rows = DSlot<MODE, TPW>::DROWS;
+  const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)splits), block(WG);
+  constexpr int lds = dma_lds_bytes<MODE, TPW, P>();
+  // above 64 KiB of LDS the kernel's dynamic-LDS limit is raised (once)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, TPW, P>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, TPW, P>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B, splits,
+                     out);
+  return hipGetLastError();
+}
+
+// Fast-path shape (read once): QDG_MFMA_TPW = 1 or 2 tiles a wave (32 or 64 rows
+// a workgroup), QDG_MFMA_RING = 3 or 4 slots.
+struct DmaShape {
+  int tpw, ring;
+};
+DmaShape dma_shape() {
+  static const DmaShape d = [] {
+    DmaShape v{2, 3};
+    if (const char* e = getenv("QDG_MFMA_TPW")) v.tpw = atoi(e) == 1 ? 1 : 2;
+    if (const char* e = getenv("QDG_MFMA_RING")) v.ring = atoi(e) == 4 ? 4 : 3;
+    return v;
+  }();
+  return d;
 }
 
 template <int MODE>
 hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
                     const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
-  constexpr int QD = 4;
-  int32_t mx = 0;
-  for (int s = 0; s < splits; ++s) {
-    int32_t g0, g1;
-    split_range(K, splits, s, g0, g1);
-    mx = g1 - g0 > mx ? g1 - g0 : mx;
+  // the fast path needs whole steps (K/32 a multiple of 8) and 16-byte weight-scale words
+  if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && !getenv("QDG_MFMA_GENERAL")) {
+    const DmaShape d = dma_shape();
+    if (d.tpw == 1)
+      return d.ring == 4 ? launch_dma<MODE, 1, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st)
+                         : launch_dma<MODE, 1, 3>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+    return d.ring == 4 ? launch_dma<MODE, 2, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st)
+                       : launch_dma<MODE, 2, 3>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
   }
-  // window: a multiple of 16 blocks (chunk starts are, so quads stay aligned to partials)
-  const int cap = ((LDS_BUDGET - (MODE == 2 ? 2 : 1) * 16 * ROW_PAD) / lds_per_block<MODE>()) / SUPER * SUPER;
-  int win = ((mx + SUPER - 1) / SUPER) * SUPER;
-  if (win > cap) win = cap;
-  if (win < SUPER) win = SUPER;
-  const size_t lds = (size_t)win * lds_per_block<MODE>() + (MODE == 2 ? 2 : 1) * 16 * ROW_PAD;
-  const int rows_per_wg = WAVES * 16;
-  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
-  // windows above 64 KiB of LDS need the kernel's dynamic-LDS limit raised (once)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma<MODE, QD>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BUDGET + 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gemv_mfma<MODE, QD>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B, splits, win,
-                     out);
-  return hipGetLastError();
+  return launch_mp<MODE, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
 }
 
 }  // namespace

@@ -127,3 +127,17 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         q.gemv_q8(q.INT8ACT, w, torch.zeros((4, 2), dtype=torch.int16), torch.zeros((1, 4)),
                   xq=torch.zeros((1, 64), dtype=torch.int8), xs=torch.zeros((1, 2)))
+
+
+def test_one_hip_runtime_in_the_process():
+    """The package alone must not bring a second HIP runtime next to PyTorch's:
+    a fresh process that imports only the package maps one libamdhip64 (two
+    copies leave the library's runtime without a device at its first launch)."""
+    import subprocess
+    import sys
+    code = ("import quantized_decode_gemv_02_amd, torch, re\n"
+            "paths = set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)\n"
+            "print(len(paths), sorted(paths))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[0] == "1", r.stdout

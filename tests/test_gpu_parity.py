@@ -159,7 +159,8 @@ def test_combine_golden_and_random(golden_dir):
 
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B,N,K,S", [(16, 256, 5120, 1), (2, 33, 512, 1), (5, 100, 1600, 2), (16, 40, 96, 1),
-                                     (11, 64, 25600, 4), (3, 17, 32, 1)])
+                                     (11, 64, 25600, 4), (3, 17, 32, 1), (16, 96, 8192, 3),
+                                     (3, 40, 256, 2), (16, 64, 480, 4)])  # the last two: empty chunks
 def test_batched_bit_exact_and_batch_invariant(mode, B, N, K, S):
     announce(f"batched mode={mode} B={B} N={N} K={K} S={S}")
     wq, ws, x = _quant_case(N, K, B, 5 * B + N + K)
@@ -177,6 +178,45 @@ def test_batched_bit_exact_and_batch_invariant(mode, B, N, K, S):
                       xl=None if xl is None else xl[t:t + 1].contiguous(), xs=xs[t:t + 1].contiguous())
         got = host(out)
         np.testing.assert_array_equal(got[:, t] if S > 1 else got[t], host(y1)[:, 0] if S > 1 else host(y1)[0])
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B", [1, 16])
+def test_weight_scales_at_a_two_byte_offset(mode, B):
+    """The header asks only 2-byte alignment of ws: scales that start 2 bytes past a
+    16-byte boundary (K a multiple of 256, where 16-byte scale words would otherwise
+    be used) give the same bits."""
+    N, K = 70, 5120
+    announce(f"ws offset mode={mode} B={B} N={N} K={K}")
+    wq, ws, x = _quant_case(N, K, B, 77 + B)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=8)
+    buf = torch.empty(N * (K // 32) + 8, dtype=torch.int16, device=DEV)
+    wsd = buf[1:1 + N * (K // 32)].view(N, K // 32)
+    wsd.copy_(dev(ws))
+    assert wsd.data_ptr() % 16 == 2
+    xq, xl, xs = quantize_gpu(mode, x)
+    y = gemv_gpu(mode, dev(wq), wsd, B, N, xq=xq, xl=xl, xs=xs)
+    np.testing.assert_array_equal(host(y), want)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,N,K,S", [(16, 100, 5120, 1), (7, 64, 2048, 2), (16, 33, 256, 2)])
+def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, monkeypatch):
+    """Shapes with K a multiple of 256 take the LDS-direct batched kernel; the
+    general kernel (forced by QDG_MFMA_GENERAL) must give the same bits there."""
+    announce(f"batched general path mode={mode} B={B} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, B, 9 * B + N + K)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = (oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=8) if S == 1
+            else oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    xq, xl, xs = quantize_gpu(mode, x)
+    wqd, wsd = dev(wq), dev(ws)
+    fast = host(gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs))
+    monkeypatch.setenv("QDG_MFMA_GENERAL", "1")
+    general = host(gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs))
+    np.testing.assert_array_equal(fast, want)
+    np.testing.assert_array_equal(general, want)
 
 
 # ---------------------------------------------------------------- Dequant
