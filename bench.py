@@ -4,14 +4,14 @@
 One step is one decode pass over the narrow projections (o-proj 5120x8192 and
 down-proj 5120x25600, batch 1): for each of the Int8Act and TwoPass numerics and
 each projection, quantize the activation, run the split-K GEMV and the ascending
-combine.  The default path makes two calls per projection, qdg_quantize_act and
-qdg_gemv_q8_sk (the split-K GEMV whose last-arriving workgroups do the
-ascending combine); --path staged makes the three calls of the pages' own
-structure (qdg_quantize_act, qdg_gemv_q8, qdg_sk_combine) instead.  Each run
-reports the other path's step time beside its own.  Inputs are seeded synthetic
-tensors resident in HBM before timing; the weights rotate over enough copies
-(>= 1 GiB between reuses of a copy) that the 256 MB Infinity Cache cannot serve
-them.
+combine.  The default path makes the three calls of the pages' own structure
+(qdg_quantize_act, qdg_gemv_q8 with S chunks, qdg_sk_combine); --path fused
+makes two (qdg_quantize_act, then qdg_gemv_q8_sk, the split-K GEMV whose
+last-arriving workgroups do the ascending combine).  Each run reports the other
+path's step time beside its own, and times Dequant (one pass, no split-K) on the
+same projections.  Inputs are seeded synthetic tensors resident in HBM before
+timing; the weights rotate over enough copies (>= 1 GiB between reuses of a
+copy) that the 256 MB Infinity Cache cannot serve them.
 
 Prints ONE JSON line:
   value      = algorithmic GEMV bytes of a step / step time (GB/s); algorithmic
@@ -21,6 +21,9 @@ Prints ONE JSON line:
   roofline   = the down-proj TwoPass GEMV (the step's dominant kernel): its
                algorithmic bytes / its mean launch duration from HIP events
                around every launch in the timed region, against 8 TB/s;
+  config.modes = per mode and projection: S, the GEMV's mean launch time (HIP
+               events around every GEMV launch of a second pass of the same
+               steps) and GB/s;
   cpu_baseline = the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
@@ -48,13 +51,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--splits", default="4,8",
+    ap.add_argument("--splits", default="4,16",
                     help="split-K chunks: 'auto' (timed choice), one S for both projections, or 'S_o,S_down'")
     ap.add_argument("--modes", default="1,2")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
-    ap.add_argument("--path", choices=("fused", "staged"), default="fused")
+    ap.add_argument("--path", choices=("fused", "staged"), default="staged")
+    ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
@@ -135,7 +139,7 @@ def main() -> int:
                 ensure_buffers(mode, si, chosen[(mode, si)])
                 continue
             best = None
-            for S in (1, 2, 3, 4, 6, 8):
+            for S in (1, 2, 3, 4, 6, 8, 12, 16):
                 ensure_buffers(mode, si, S)
                 seqs = [make_calls(mode, si, S, c) for c in range(R)]
                 for c in seqs:
@@ -174,11 +178,14 @@ def main() -> int:
     step_bytes = sum(alg_bytes(m, shapes[si].N, shapes[si].K) for m in modes for si in range(len(shapes)))
     dom_bytes = alg_bytes(dom_key[0], shapes[dom_key[1]].N, shapes[dom_key[1]].K)
 
+    keys = [(mode, si) for mode in modes for si in range(len(shapes))]
+
     def run_step(i, events=None, steps=None):
+        # events: {key: list of (start, end)} -- one pair around every GEMV launch of the step
         for key, calls in (steps or steps_calls)[i % R]:
-            if events is not None and key == dom_key:
+            if events is not None and key in events:
                 calls[0]()
-                ev0, ev1 = events.pop()
+                ev0, ev1 = events[key][i]
                 ev0.record()
                 calls[1]()
                 ev1.record()
@@ -198,17 +205,27 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # timed region: K steps, HIP events around the dominant GEMV launch only (events on every
+    # launch would add their own stream work between the kernels of the step)
     K = args.steps
-    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    used = list(ev_pairs)
+    ev = {dom_key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(K)]}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        run_step(i, ev_pairs)
+        run_step(i, ev)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / K
-    dom_ms = sum(a.elapsed_time(b) for a, b in used) / K
+    dom_ms = sum(a.elapsed_time(b) for a, b in ev[dom_key]) / K
+
+    # per-GEMV launch times: a second pass of the same steps with events around every GEMV
+    ev_all = {key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(K)] for key in keys}
+    for i in range(K):
+        run_step(i, ev_all)
+    torch.cuda.synchronize()
+    gemv_ms = {key: sum(a.elapsed_time(b) for a, b in ev_all[key]) / K for key in keys}
 
     # the other path's step time, for reference (same steps, same rotation)
     other = "staged" if args.path == "fused" else "fused"
@@ -237,12 +254,40 @@ def main() -> int:
                 and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
 
+    # per mode and projection: the GEMV launch's mean duration (HIP events in the timed region)
+    names = {0: "dequant", 1: "int8act", 2: "twopass"}
     per_mode = {}
     for mode in modes:
-        name = {1: "int8act", 2: "twopass"}[mode]
-        per_mode[name] = {shapes[si].name: {"splits": chosen[(mode, si)],
-                                            "alg_bytes": alg_bytes(mode, shapes[si].N, shapes[si].K)}
-                          for si in range(len(shapes))}
+        per_mode[names[mode]] = {}
+        for si in range(len(shapes)):
+            b = alg_bytes(mode, shapes[si].N, shapes[si].K)
+            us = gemv_ms[(mode, si)] * 1e3
+            per_mode[names[mode]][shapes[si].name] = {
+                "splits": chosen[(mode, si)], "alg_bytes": b, "gemv_us": round(us, 3),
+                "gemv_GBs": round(b / us / 1e3, 1), "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
+
+    # Dequant (no split-K: binary64 sums in one pass) on the same projections, beside the step
+    if not args.no_dequant:
+        per_mode["dequant"] = {}
+        for si, sh in enumerate(shapes):
+            y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+            calls = [q.bind_gemv_q8(0, copies[c][si][0], copies[c][si][1], y0, x=acts[si]) for c in range(R)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            reps = max(K // 4, 2 * R)
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(reps)]
+            for i in range(reps):
+                pairs[i][0].record()
+                calls[i % R]()
+                pairs[i][1].record()
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in pairs) / reps * 1e3
+            b = alg_bytes(0, sh.N, sh.K)
+            per_mode["dequant"][sh.name] = {"splits": 1, "alg_bytes": b, "gemv_us": round(us, 3),
+                                            "gemv_GBs": round(b / us / 1e3, 1),
+                                            "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
 
     # ---- CPU baseline: the oracle on the same step (whole steps, repeated for a bounded time)
     cpu = None

@@ -32,21 +32,31 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def _one(path_glob: str) -> str:
-    hits = sorted(glob.glob(path_glob))
-    if not hits:
-        raise FileNotFoundError(path_glob)
+def _one(directory: str, pattern: str) -> str:
+    """The one file matching `pattern` anywhere under `directory` (rocprofv3 may nest its output)."""
+    hits = sorted(glob.glob(os.path.join(directory, "**", pattern), recursive=True))
+    if len(hits) != 1:
+        raise FileNotFoundError(f"{len(hits)} files match {pattern} under {directory}")
     return hits[0]
 
 
 def kernel_stats(trace_dir: str) -> list[dict]:
-    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "*kernel_stats.csv")))))
+    rows = list(csv.DictReader(open(_one(trace_dir, "*kernel_stats.csv"))))
     return [{"name": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
              "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]), "pct": float(r["Percentage"])} for r in rows]
 
 
+def trace_by_grid(trace_dir: str) -> dict:
+    """Mean / min / max duration (ns) and count per (kernel, total work-items) from the kernel trace."""
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(_one(trace_dir, "*kernel_trace.csv"))):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        acc[(short(r["Kernel_Name"]), grid)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: (sum(v) / len(v), min(v), max(v), len(v)) for k, v in acc.items()}
+
+
 def counters(pmc_dir: str) -> list[dict]:
-    return list(csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))))
+    return list(csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))))
 
 
 def short(name: str) -> str:
@@ -80,6 +90,12 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
     for k in ks:
         lines.append(f"| {short(k['name'])} | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | {k['min_ns'] / 1e3:.2f} | "
                      f"{k['max_ns'] / 1e3:.2f} | {k['pct']:.1f} |")
+    tg = trace_by_grid(trace_dir)
+    lines += ["", "### Per launch shape (kernel trace: End - Start per dispatch)", "",
+              "| kernel | grid (work-items) | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for key in sorted(tg):
+        a, lo, hi, n = tg[key]
+        lines.append(f"| {key[0]} | {key[1]} | {n} | {a / 1e3:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} |")
     lines += ["", "## HBM bytes per dispatch (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Scale: the 256 MiB calibration copy reads FETCH_SIZE x {ff:.4f} and WRITE_SIZE x {wf:.4f} "
               "bytes per KiB counted.", "",
@@ -91,12 +107,16 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
         lines.append(f"| {key[0]} | {key[1]} | {n} | {f_mean * ff / 1e6:.3f} | {f_min * ff / 1e6:.3f}..{f_max * ff / 1e6:.3f} "
                      f"| {w_mean * wf / 1e6:.4f} |")
     dom = {"kernel": dominant[0], "grid": dominant[1], "kernel_source_sha": kernel_source_sha()}
+    if (dominant[0], dominant[1]) in tg:
+        dom["trace_avg_us"] = tg[(dominant[0], dominant[1])][0] / 1e3
     if (dominant[0], dominant[1]) in fk:
         dom["fetch_bytes"] = fk[dominant][0] * ff
         dom["write_bytes"] = wk[dominant][0] * wf
         dom["traffic_bytes"] = dom["fetch_bytes"] + dom["write_bytes"]
         lines += ["", f"Dominant kernel {dominant[0]} (grid {dominant[1]}): {dom['traffic_bytes'] / 1e6:.3f} MB "
-                      "per launch (mean fetch + mean write)."]
+                      "per launch (mean fetch + mean write)"
+                      + (f", {dom['trace_avg_us']:.2f} us per launch in the kernel trace." if "trace_avg_us" in dom
+                         else ".")]
     open(out_md, "w").write("\n".join(lines) + "\n")
     json.dump(dom, open(out_json, "w"), indent=1)
     return dom
