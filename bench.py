@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
-    ap.add_argument("--path", choices=("fused", "staged"), default="staged")
+    ap.add_argument("--path", choices=("single", "fused", "staged"), default="staged")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
@@ -100,10 +100,13 @@ def main() -> int:
 
     # ---- per (mode, shape) buffers and pre-bound launches
     def make_calls(mode, si, S, copy_idx, path="staged"):
+        # the GEMV is always the last call but one (staged) or the last call
         sh = shapes[si]
         N, K = sh.N, sh.K
         bufs = buffers[(mode, si, S)]
         w, s = copies[copy_idx][si]
+        if path == "single":
+            return [q.bind_gemv_q8_fused(mode, w, s, bufs["y"], acts[si], S, bufs["fws"])]
         calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
         if path == "fused":
             calls.append(q.bind_gemv_q8_sk(mode, w, s, bufs["y"], bufs["xq"], bufs["xl"], bufs["xs"], S, bufs["fws"]))
@@ -184,12 +187,14 @@ def main() -> int:
         # events: {key: list of (start, end)} -- one pair around every GEMV launch of the step
         for key, calls in (steps or steps_calls)[i % R]:
             if events is not None and key in events:
-                calls[0]()
+                g = 0 if len(calls) == 1 else 1  # the GEMV's position (single: the only call)
+                for f in calls[:g]:
+                    f()
                 ev0, ev1 = events[key][i]
                 ev0.record()
-                calls[1]()
+                calls[g]()
                 ev1.record()
-                for f in calls[2:]:
+                for f in calls[g + 1:]:
                     f()
             else:
                 for f in calls:
@@ -227,17 +232,20 @@ def main() -> int:
     torch.cuda.synchronize()
     gemv_ms = {key: sum(a.elapsed_time(b) for a, b in ev_all[key]) / K for key in keys}
 
-    # the other path's step time, for reference (same steps, same rotation)
-    other = "staged" if args.path == "fused" else "fused"
-    other_steps = build_steps(other)
-    for i in range(args.warmup):
-        run_step(i, steps=other_steps)
-    torch.cuda.synchronize()
-    t_o = time.perf_counter()
-    for i in range(K):
-        run_step(i, steps=other_steps)
-    torch.cuda.synchronize()
-    other_ms = (time.perf_counter() - t_o) * 1e3 / K
+    # the other paths' step times, for reference (same steps, same rotation)
+    other_ms = {}
+    for other in ("single", "fused", "staged"):
+        if other == args.path:
+            continue
+        other_steps = build_steps(other)
+        for i in range(args.warmup):
+            run_step(i, steps=other_steps)
+        torch.cuda.synchronize()
+        t_o = time.perf_counter()
+        for i in range(K):
+            run_step(i, steps=other_steps)
+        torch.cuda.synchronize()
+        other_ms[f"{other}_ms_per_step"] = round((time.perf_counter() - t_o) * 1e3 / K, 5)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
@@ -249,7 +257,8 @@ def main() -> int:
         from quantized_decode_gemv_02_amd import profiling
         t = json.load(open(tpath))
         dom_grid = 256 * -(-shapes[dom_key[1]].N // 16) * chosen[dom_key]
-        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {'true' if args.path == 'fused' else 'false'}>"
+        flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[args.path]
+        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {flags}>"
         if (t.get("kernel_source_sha") == profiling.kernel_source_sha() and t.get("grid") == dom_grid
                 and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
@@ -326,13 +335,13 @@ def main() -> int:
         "data": "synthetic (seeded; int8 weights uniform [-127,127], fp16 scales U[1e-3,1e-2), N(0,1) activations with 1% x20 outliers)",
         "config": {"workload": "narrow projections with split-K: o-proj K=8192 N=5120 and down-proj K=25600 N=5120, "
                                "batch 1, Int8Act + TwoPass, quantize + GEMV + ascending combine",
-                   "path": args.path, f"{other}_ms_per_step": round(other_ms, 5),
+                   "path": args.path, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"k_gemv_dot4 ({args.path}) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
+                     "kernel": f"k_gemv_dot4 ({args.path} path) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
                      "alg_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

@@ -152,6 +152,24 @@ int qdg_gemv_q8_sk(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, in
                    const int8_t *xq, const int8_t *xl, const float *xs, int64_t B, int splits,
                    float *y, void *workspace, size_t workspace_bytes, qdg_stream stream);
 
+/*
+ * One decode projection in one launch (B == 1): qdg_quantize_act, qdg_gemv_q8 with
+ * `splits` chunks and qdg_sk_combine fused.  Every workgroup quantizes the
+ * activation blocks of its own chunk into LDS with the quantizer's arithmetic,
+ * runs the split-K GEMV on them, and the last workgroup of each 16-row tile to
+ * finish sums the tile's partials in ascending chunk order (as qdg_gemv_q8_sk).
+ * y [1][N] is bit-identical to the three calls.  QDG_DEQUANT takes splits == 1
+ * only (its one pass is already a single launch; workspace unused).  Inputs:
+ * device x float [1][K] (16-byte aligned); device workspace as for
+ * qdg_gemv_q8_sk (at least qdg_gemv_sk_workspace_bytes(1, N, splits) bytes,
+ * 256-byte aligned, zero-filled before its first use, left zeroed by every call
+ * that completes; NULL allowed when splits == 1).  Calls that share a workspace
+ * must not overlap in time.  The quantized words are not written out.
+ */
+int qdg_gemv_q8_fused(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                      const float *x, int splits, float *y, void *workspace,
+                      size_t workspace_bytes, qdg_stream stream);
+
 /* Bytes of device workspace qdg_argmax needs for B rows of N values. */
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N);
 

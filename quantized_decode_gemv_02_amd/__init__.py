@@ -9,6 +9,7 @@ functions carry the names of the C entry points in ``include/qdg.h`` without the
 * ``gemv_q8(mode, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits=1)``
 * ``sk_combine(partials, y)``
 * ``gemv_q8_sk(mode, wq, ws, y, xq, xl, xs, splits, workspace)`` / ``gemv_sk_workspace_bytes(B, N, S)``
+* ``gemv_q8_fused(mode, wq, ws, y, x, splits, workspace)`` (quantize + GEMV + combine, one launch)
 * ``argmax(y, idx, workspace)`` / ``argmax_workspace_bytes(B, N)``
 * ``block_dots(mode, wq, xq, xl, dh, dl)``
 * ``split_bounds(K, splits)`` (host only)
@@ -59,6 +60,7 @@ _SIGS = {
     "qdg_sk_combine": ([_P, _I, _I64, _I64, _P, _P], _I),
     "qdg_gemv_sk_workspace_bytes": ([_I64, _I64, _I], ctypes.c_size_t),
     "qdg_gemv_q8_sk": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, ctypes.c_size_t, _P], _I),
+    "qdg_gemv_q8_fused": ([_I, _P, _P, _I64, _I64, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "qdg_argmax": ([_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
@@ -176,6 +178,16 @@ def gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> None
         _stream()))
 
 
+def gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> None:
+    """One launch for a batch-1 projection: quantize ``x [1][K]`` (f32), split-K GEMV and ascending
+    combine into ``y [1][N]`` (``workspace`` from ``sk_workspace(N, splits)``; may be None when S == 1)."""
+    N, K = wq.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("qdg_gemv_q8_fused", _lib.qdg_gemv_q8_fused(
+        mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), int(splits),
+        _ptr(y, _f32(), "y"), _ptr(workspace, None, "workspace"), nbytes, _stream()))
+
+
 def sk_combine(partials, y) -> None:
     """``y [B][N]`` = ascending sum over the leading axis of ``partials [S][B][N]``."""
     S = partials.shape[0]
@@ -251,6 +263,14 @@ def bind_gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) ->
         _ptr(t, None, n)
     nbytes = workspace.numel() * workspace.element_size()
     return Bound("qdg_gemv_q8_sk", mode, wq, ws, N, K, xq, xl, xs, B, int(splits), y, workspace, nbytes, _stream())
+
+
+def bind_gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> Bound:
+    N, K = wq.shape
+    for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (x, "x"), (workspace, "workspace")):
+        _ptr(t, None, n)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return Bound("qdg_gemv_q8_fused", mode, wq, ws, N, K, x, int(splits), y, workspace, nbytes, _stream())
 
 
 def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:

@@ -117,6 +117,23 @@ int qdg_gemv_q8_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, in
   return hip_status(qdg::launch_gemv_sk(mode, wq, ws, N, K, xq, xl, xs, splits, y, workspace, as_stream(stream)));
 }
 
+int qdg_gemv_q8_fused(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                      int splits, float* y, void* workspace, size_t workspace_bytes, qdg_stream stream) {
+  if (mode < QDG_DEQUANT || mode > QDG_TWOPASS) return QDG_EINVAL;
+  if (!wq || !ws || !x || !y) return QDG_EINVAL;
+  if (!shape_ok(N, K)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (mode == QDG_DEQUANT && splits != 1) return QDG_EMODE;
+  if (splits > 1 && !workspace) return QDG_EINVAL;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(x, 16) || !aligned(y, 4)) return QDG_EALIGN;
+  if (splits > 1 && !aligned(workspace, 256)) return QDG_EALIGN;
+  if (splits > 1 && workspace_bytes < qdg::sk_workspace_bytes(N, splits)) return QDG_EWORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  if (mode == QDG_DEQUANT) return hip_status(qdg::launch_gemv_dequant(wq, ws, N, K, x, y, st));
+  return hip_status(qdg::launch_gemv_x(mode, wq, ws, N, K, x, splits, y, workspace, st));
+}
+
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
   if (B < 1 || N < 1) return 0;
   return (size_t)B * (size_t)qdg::argmax_groups(N) * sizeof(unsigned long long);

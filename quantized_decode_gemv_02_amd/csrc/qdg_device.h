@@ -185,6 +185,8 @@ hipError_t launch_combine(const float* part, int splits, int64_t count, float* y
 size_t sk_workspace_bytes(int64_t N, int splits);
 hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
                           const int8_t* xl, const float* xs, int splits, float* y, void* workspace, hipStream_t st);
+hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                         int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
 hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
                          hipStream_t st);

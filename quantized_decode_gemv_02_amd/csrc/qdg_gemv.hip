@@ -27,6 +27,11 @@
 //    nontemporal hint (streamed once, never re-read).
 //  * grid = (row tiles, splits): the split s of a row covers the QWEN38 chunk
 //    [g0, g1) and writes partial[s][o]; an empty chunk writes +0.
+//  * QX = true (one launch for a whole projection): the workgroup quantizes its
+//    own window of the f32 activation into LDS -- the activation quantizer's
+//    routine, eight lanes a block -- instead of copying words quantized by an
+//    earlier launch; every workgroup of a chunk quantizes the same blocks, so
+//    they all hold the words the quantizer kernel would write, bit for bit.
 #include <stdlib.h>
 
 #include "qdg_device.h"
@@ -47,11 +52,11 @@ constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2
 //   last workgroup of a row tile to finish (an atomic ticket per tile) sums the
 //   tile's S partials in ascending order into y and resets the ticket -- which
 //   chunk finishes last changes nothing in the result.
-template <int MODE, int RPW, int U, bool FUSED>
+template <int MODE, int RPW, int U, bool FUSED, bool QX>
 __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
-                                                 const float* __restrict__ xs, int64_t N, int64_t K, int S, int win,
-                                                 float* __restrict__ out,
+                                                 const float* __restrict__ xs, const float* __restrict__ x,
+                                                 int64_t N, int64_t K, int S, int win, float* __restrict__ out,
                                                  unsigned* __restrict__ tickets, float* __restrict__ y) {
   constexpr int LPR = 64 / RPW;  // lanes per row
   constexpr int BPS = LPR / 2;   // blocks per step of a row
@@ -94,11 +99,38 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
       wcur[u] = b < wb1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nwb * 2; i += WG) {
-      ((int4*)lq)[i] = ld16(xq + (int64_t)wb0 * QK + 16 * i);
-      if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + (int64_t)wb0 * QK + 16 * i);
+    if constexpr (QX) {
+      // quantize the window: 8 lanes a block, 4 values a lane; two rounds of
+      // loads are in flight before the first is quantized.  The trip count is
+      // uniform, so all lanes of every 8-lane group take part in its maximum.
+      for (int base = 0; base < nwb * 8; base += 2 * WG) {
+        float4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = base + h * WG + threadIdx.x;
+          v[h] = i < nwb * 8 ? *(const float4*)(x + (int64_t)(wb0 + (i >> 3)) * QK + (i & 7) * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = base + h * WG + threadIdx.x;
+          int hw, lw;
+          const float s = quant_lane4<MODE>(v[h], &hw, &lw);
+          if (i < nwb * 8) {
+            const int blk = i >> 3, sub = i & 7;
+            *(int*)(lq + blk * QK + sub * 4) = hw;
+            if constexpr (MODE == 2) *(int*)(ll + blk * QK + sub * 4) = lw;
+            if (sub == 0) lsx[blk] = s;
+          }
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < nwb * 2; i += WG) {
+        ((int4*)lq)[i] = ld16(xq + (int64_t)wb0 * QK + 16 * i);
+        if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + (int64_t)wb0 * QK + 16 * i);
+      }
+      for (int i = threadIdx.x; i < nwb; i += WG) lsx[i] = xs[wb0 + i];
     }
-    for (int i = threadIdx.x; i < nwb; i += WG) lsx[i] = xs[wb0 + i];
     stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
     __syncthreads();
 
@@ -202,31 +234,35 @@ int window_blocks(int64_t K, int splits, int bytes_per_block) {
   return win;
 }
 
-template <int MODE, int RPW, int U, bool FUSED>
+template <int MODE, int RPW, int U, bool FUSED, bool QX>
 hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
-                    const float* xs, int splits, float* out, unsigned* tickets, float* y, hipStream_t st) {
+                    const float* xs, const float* x, int splits, float* out, unsigned* tickets, float* y,
+                    hipStream_t st) {
   constexpr int bpb = window_bytes_per_block<MODE, RPW>();
   const int win = window_blocks(K, splits, bpb);
   const int rows_per_wg = (WG / 64) * RPW;
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
-  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U, FUSED>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs, N,
-                     K, splits, win, out, tickets, y);
+  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U, FUSED, QX>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs,
+                     x, N, K, splits, win, out, tickets, y);
   return hipGetLastError();
 }
 
-template <int MODE, bool FUSED>
+template <int MODE, bool FUSED, bool QX>
 hipError_t launch_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
-                       const int8_t* xl, const float* xs, int splits, float* out, unsigned* tickets, float* y,
-                       hipStream_t st) {
+                       const int8_t* xl, const float* xs, const float* x, int splits, float* out, unsigned* tickets,
+                       float* y, hipStream_t st) {
   const Tuning t = tuning();
+#define QDG_LAUNCH(R_, U_) \
+  return launch_t<MODE, R_, U_, FUSED, QX>(wq, ws, N, K, xq, xl, xs, x, splits, out, tickets, y, st)
   if (t.rpw == 8) {
-    if (t.unroll == 2) return launch_t<MODE, 8, 2, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
-    if (t.unroll == 8) return launch_t<MODE, 8, 8, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
-    return launch_t<MODE, 8, 4, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+    if (t.unroll == 2) QDG_LAUNCH(8, 2);
+    if (t.unroll == 8) QDG_LAUNCH(8, 8);
+    QDG_LAUNCH(8, 4);
   }
-  if (t.unroll == 2) return launch_t<MODE, 4, 2, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
-  if (t.unroll == 8) return launch_t<MODE, 4, 8, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
-  return launch_t<MODE, 4, 4, FUSED>(wq, ws, N, K, xq, xl, xs, splits, out, tickets, y, st);
+  if (t.unroll == 2) QDG_LAUNCH(4, 2);
+  if (t.unroll == 8) QDG_LAUNCH(4, 8);
+  QDG_LAUNCH(4, 4);
+#undef QDG_LAUNCH
 }
 
 }  // namespace
@@ -234,8 +270,9 @@ hipError_t launch_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t 
 hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                             const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* out,
                             hipStream_t st) {
-  if (mode == 1) return launch_mode<1, false>(wq, ws, N, K, xq, xl, xs, splits, out, nullptr, nullptr, st);
-  return launch_mode<2, false>(wq, ws, N, K, xq, xl, xs, splits, out, nullptr, nullptr, st);
+  if (mode == 1)
+    return launch_mode<1, false, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, out, nullptr, nullptr, st);
+  return launch_mode<2, false, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, out, nullptr, nullptr, st);
 }
 
 // Workspace of the in-kernel combine, each part 256-byte aligned: one ticket per
@@ -253,8 +290,17 @@ hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_
   if (splits == 1) return launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, 1, y, st);
   unsigned* tickets = (unsigned*)workspace;
   float* part = (float*)((char*)workspace + sk_partials_offset(N));
-  if (mode == 1) return launch_mode<1, true>(wq, ws, N, K, xq, xl, xs, splits, part, tickets, y, st);
-  return launch_mode<2, true>(wq, ws, N, K, xq, xl, xs, splits, part, tickets, y, st);
+  if (mode == 1) return launch_mode<1, true, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, part, tickets, y, st);
+  return launch_mode<2, true, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, part, tickets, y, st);
+}
+
+hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                         int splits, float* y, void* workspace, hipStream_t st) {
+  unsigned* tickets = (unsigned*)workspace;
+  float* part = splits == 1 ? y : (float*)((char*)workspace + sk_partials_offset(N));
+  if (mode == 1)
+    return launch_mode<1, true, true>(wq, ws, N, K, nullptr, nullptr, nullptr, x, splits, part, tickets, y, st);
+  return launch_mode<2, true, true>(wq, ws, N, K, nullptr, nullptr, nullptr, x, splits, part, tickets, y, st);
 }
 
 }  // namespace qdg

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -111,6 +111,27 @@ def test_combine_argmax_blockdots_validation():
     assert bd(1, P(A), 4, 64, P(A), None, 1, P(A), P(A), None) == EINVAL
     assert bd(1, P(A), 4, 60, P(A), None, 1, P(A), None, None) == ESHAPE
     assert bd(1, P(A), 4, 64, P(A), None, 17, P(A), None, None) == ESHAPE
+
+
+def test_fused_validation():
+    f = lib.qdg_gemv_q8_fused
+    need = q.gemv_sk_workspace_bytes(1, 64, 4)
+
+    def call(mode=1, wq=A, ws=A, N=64, K=512, x=A, S=4, y=A, wsp=A, nbytes=None):
+        return f(mode, P(wq), P(ws), N, K, P(x), S, P(y), P(wsp), need if nbytes is None else nbytes, None)
+
+    assert call(mode=3) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(y=None) == EINVAL
+    assert call(wsp=None) == EINVAL                  # S > 1 needs the workspace
+    assert call(K=500) == ESHAPE
+    assert call(S=0) == ESHAPE
+    assert call(S=65) == ESHAPE
+    assert call(mode=0, S=2) == EMODE                # Dequant: one pass only
+    assert call(x=A + 4) == EALIGN
+    assert call(wq=A + 8) == EALIGN
+    assert call(wsp=A + 8) == EALIGN
+    assert call(nbytes=need - 4) == EWORKSPACE
 
 
 def test_split_bounds_validation():

@@ -319,3 +319,48 @@ def test_in_kernel_combine_bit_exact(mode, N, K, S):
         np.testing.assert_array_equal(host(y), want)
     tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
     assert not tickets.any()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 16), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
+                                   (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4),
+                                   (40, 25632, 7)])
+def test_fused_single_launch_bit_exact(mode, N, K, S):
+    """qdg_gemv_q8_fused (quantize in the workgroup + split-K GEMV + in-kernel
+    combine) against the oracle's quantize -> chunk partials -> ascending combine."""
+    announce(f"gemv_q8_fused mode={mode} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, 1, 13 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    wqd, wsd, xd = dev(wq), dev(ws), dev(x.reshape(1, K))
+    wsp = q.sk_workspace(N, S)
+    for rep in range(3):  # the tickets must come back to zero after every call
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_fused(mode, wqd, wsd, y, xd, S, wsp)
+        np.testing.assert_array_equal(host(y), want)
+    tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
+    assert not tickets.any()
+
+
+def test_fused_single_launch_dequant_and_edge_inputs():
+    """Dequant through the fused entry point (S = 1), and quantizer edge blocks
+    (zero, tiny, huge, ties) reaching the in-workgroup quantizer."""
+    N, K = 37, 1600
+    announce(f"gemv_q8_fused dequant + edge inputs N={N} K={K}")
+    wq, ws, x = _quant_case(N, K, 1, 4242)
+    y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_fused(0, dev(wq), dev(ws), y, dev(x.reshape(1, K)))
+    Y, tn = oracle.reference_f64(0, wq, ws, x=x)
+    assert oracle.within_tolerance(host(y), Y, tn).all()
+    x = x.copy()
+    x[0, :32] = 0.0
+    x[0, 32:64] = 1e-20
+    x[0, 64:96] = 3e4
+    x[0, 96:128] = np.arange(32, dtype=np.float32) - 15.5
+    for mode in (1, 2):
+        oq, ol, os_ = oracle.quantize(mode, x)
+        want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, 2, nthreads=8))
+        wsp = q.sk_workspace(N, 2)
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_fused(mode, dev(wq), dev(ws), y, dev(x.reshape(1, K)), 2, wsp)
+        np.testing.assert_array_equal(host(y), want)
