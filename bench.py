@@ -8,8 +8,8 @@ combine.  The default path makes the three calls of the pages' own structure
 (qdg_quantize_act, qdg_gemv_q8 with S chunks, qdg_sk_combine); --path fused
 makes two (qdg_quantize_act, then qdg_gemv_q8_sk, the split-K GEMV whose
 last-arriving workgroups do the ascending combine).  Each run reports the other
-path's step time beside its own, and times Dequant (one pass, no split-K) on the
-same projections.  Inputs are seeded synthetic tensors resident in HBM before
+path's step time beside its own, and times Dequant (qdg_gemv_q8_fused with the
+same S) on the same projections.  Inputs are seeded synthetic tensors resident in HBM before
 timing; the weights rotate over enough copies (>= 1 GiB between reuses of a
 copy) that the 256 MB Infinity Cache cannot serve them.
 
@@ -275,12 +275,16 @@ def main() -> int:
                 "splits": chosen[(mode, si)], "alg_bytes": b, "gemv_us": round(us, 3),
                 "gemv_GBs": round(b / us / 1e3, 1), "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
 
-    # Dequant (no split-K: binary64 sums in one pass) on the same projections, beside the step
+    # Dequant on the same projections, beside the step: one launch with the same S (binary64
+    # chunk partials and an ascending binary64 combine in the last workgroup of each row tile)
     if not args.no_dequant:
         per_mode["dequant"] = {}
         for si, sh in enumerate(shapes):
             y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
-            calls = [q.bind_gemv_q8(0, copies[c][si][0], copies[c][si][1], y0, x=acts[si]) for c in range(R)]
+            S = chosen[(modes[0], si)]
+            dws = q.sk_workspace(sh.N, S)
+            calls = [q.bind_gemv_q8_fused(0, copies[c][si][0], copies[c][si][1], y0, acts[si], S, dws)
+                     for c in range(R)]
             for c in calls:
                 c()
             torch.cuda.synchronize()
@@ -294,7 +298,7 @@ def main() -> int:
             torch.cuda.synchronize()
             us = sum(a.elapsed_time(b) for a, b in pairs) / reps * 1e3
             b = alg_bytes(0, sh.N, sh.K)
-            per_mode["dequant"][sh.name] = {"splits": 1, "alg_bytes": b, "gemv_us": round(us, 3),
+            per_mode["dequant"][sh.name] = {"splits": S, "alg_bytes": b, "gemv_us": round(us, 3),
                                             "gemv_GBs": round(b / us / 1e3, 1),
                                             "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
 

@@ -131,7 +131,8 @@ int qdg_gemv_q8(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64
 int qdg_sk_combine(const float *partials, int splits, int64_t B, int64_t N, float *y,
                    qdg_stream stream);
 
-/* Bytes of device workspace qdg_gemv_q8_sk needs (0 for an unsupported shape). */
+/* Bytes of device workspace qdg_gemv_q8_sk and qdg_gemv_q8_fused need (0 for an
+ * unsupported shape): tickets, then room for S x N binary64 partials. */
 size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
 
 /*
@@ -158,8 +159,11 @@ int qdg_gemv_q8_sk(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, in
  * activation blocks of its own chunk into LDS with the quantizer's arithmetic,
  * runs the split-K GEMV on them, and the last workgroup of each 16-row tile to
  * finish sums the tile's partials in ascending chunk order (as qdg_gemv_q8_sk).
- * y [1][N] is bit-identical to the three calls.  QDG_DEQUANT takes splits == 1
- * only (its one pass is already a single launch; workspace unused).  Inputs:
+ * y [1][N] is bit-identical to the three calls.  QDG_DEQUANT (no quantizer)
+ * splits K the same way with binary64 chunk partials, which the last workgroup
+ * adds from +0 in ascending order in binary64 and rounds once to binary32: the
+ * plain definition within the Dequant tolerance, not the bits of splits == 1.
+ * Inputs:
  * device x float [1][K] (16-byte aligned); device workspace as for
  * qdg_gemv_q8_sk (at least qdg_gemv_sk_workspace_bytes(1, N, splits) bytes,
  * 256-byte aligned, zero-filled before its first use, left zeroed by every call

@@ -124,13 +124,12 @@ int qdg_gemv_q8_fused(int mode, const int8_t* wq, const uint16_t* ws, int64_t N,
   if (!shape_ok(N, K)) return QDG_ESHAPE;
   if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
   if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
-  if (mode == QDG_DEQUANT && splits != 1) return QDG_EMODE;
   if (splits > 1 && !workspace) return QDG_EINVAL;
   if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(x, 16) || !aligned(y, 4)) return QDG_EALIGN;
   if (splits > 1 && !aligned(workspace, 256)) return QDG_EALIGN;
   if (splits > 1 && workspace_bytes < qdg::sk_workspace_bytes(N, splits)) return QDG_EWORKSPACE;
   const hipStream_t st = as_stream(stream);
-  if (mode == QDG_DEQUANT) return hip_status(qdg::launch_gemv_dequant(wq, ws, N, K, x, y, st));
+  if (mode == QDG_DEQUANT) return hip_status(qdg::launch_gemv_dequant_sk(wq, ws, N, K, x, splits, y, workspace, st));
   return hip_status(qdg::launch_gemv_x(mode, wq, ws, N, K, x, splits, y, workspace, st));
 }
 

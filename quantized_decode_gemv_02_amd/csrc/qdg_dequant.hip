@@ -6,8 +6,10 @@
 // Any fixed binary64 order computes the plain definition to within a few binary64
 // roundings; this kernel's order is:
 //  * a lane holds 16 consecutive values of a block (the lane pair (2j, 2j+1)
-//    holds block j of its step) and forms sum_i w_i*x_i by binary64 fused
-//    multiply-adds from +0 in ascending i (every product w_i*x_i is exact);
+//    holds block j of its step) and forms sum_i w_i*x_i in four binary64 chains
+//    by i mod 4, each by fused multiply-adds from +0 in ascending i (every
+//    product w_i*x_i is exact), then (c0 + c1) + (c2 + c3) -- four independent
+//    chains keep the FMA pipeline busy;
 //  * the pair's two half-block sums are added (low half + high half), and the
 //    block's term is sigma * that sum (one binary64 rounding);
 //  * terms go into partial g mod 4 in ascending block order, and the row is
@@ -15,6 +17,16 @@
 // The lane layout, the LDS staging of the window (the f32 activation and the
 // rows' weight scales) and the load pipeline are those of the quantized kernel
 // (qdg_gemv.hip).
+//
+// Split-K (S > 1, the QWEN38 page's chunk rule, gk_gemv_hl_sk): chunk s of a row
+// sums its blocks in the order above into a binary64 partial; the last workgroup
+// of each row tile to finish (an atomic ticket per tile, the protocol of the
+// quantized kernel's in-kernel combine) adds the tile's S partials from +0 in
+// ascending chunk order in binary64 and rounds once to binary32.  Every sum is
+// still binary64 and there is still one rounding to binary32, so the result
+// stays within the Dequant tolerance of the plain definition.
+#include <stdlib.h>
+
 #include "qdg_device.h"
 
 namespace qdg {
@@ -23,38 +35,55 @@ namespace {
 constexpr int WG = 256;
 constexpr int LDS_BUDGET = 56 * 1024;
 
-__device__ __forceinline__ double half_dot16(int4 w, const float* __restrict__ x) {
+// sum_i w_i*x_i over one lane's 16 values: chains by i mod 4, then (c0+c1)+(c2+c3).
+// XF64: the window holds the activation already in binary64.
+template <bool XF64>
+__device__ __forceinline__ double half_dot16(int4 w, const void* __restrict__ xv) {
   const int ww[4] = {w.x, w.y, w.z, w.w};
-  double acc = 0.0;
+  double c[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float4 xv = *(const float4*)(x + 4 * q);
-    const float xx[4] = {xv.x, xv.y, xv.z, xv.w};
+    double xx[4];
+    if constexpr (XF64) {
+      const double2 a = ((const double2*)xv)[2 * q], b = ((const double2*)xv)[2 * q + 1];
+      xx[0] = a.x; xx[1] = a.y; xx[2] = b.x; xx[3] = b.y;
+    } else {
+      const float4 f = ((const float4*)xv)[q];
+      xx[0] = f.x; xx[1] = f.y; xx[2] = f.z; xx[3] = f.w;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int wi = (int)(signed char)((ww[q] >> (8 * i)) & 255);
-      acc = __fma_rn((double)wi, (double)xx[i], acc);
+      c[i] = __fma_rn((double)wi, xx[i], c[i]);
     }
   }
-  return acc;
+  return __dadd_rn(__dadd_rn(c[0], c[1]), __dadd_rn(c[2], c[3]));
 }
 
-template <int RPW, int U>
+template <int RPW, int U, bool XF64>
 __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
-                                                    const float* __restrict__ x, int64_t N, int64_t K, int win,
-                                                    float* __restrict__ out) {
+                                                    const float* __restrict__ x, int64_t N, int64_t K, int S,
+                                                    int win, float* __restrict__ out, double* __restrict__ part,
+                                                    unsigned* __restrict__ tickets) {
   constexpr int LPR = 64 / RPW;
   constexpr int BPS = LPR / 2;
   constexpr int TPP = BPS / 4;
   constexpr int ROWS = (WG / 64) * RPW;
   static_assert(TPP == 1 || TPP == 2, "RPW must be 4 or 8");
   extern __shared__ __align__(16) unsigned char lds[];
-  float* lx = (float*)lds;                            // [win][32]
-  uint16_t* lsg = (uint16_t*)(lx + (int64_t)win * QK);  // [ROWS][win]
+  // The window's activation: each half block (16 values) is one segment, padded
+  // by 16 bytes so that the 16 lanes of a row, which read 16 consecutive
+  // segments in the same instruction, fall on 16 different groups of 4 banks.
+  constexpr int XB = XF64 ? 8 : 4;  // bytes per staged activation value
+  constexpr int SEG = 16 * XB + 16;  // bytes per padded half-block segment
+  unsigned char* lx = lds;                                   // [win][2] segments
+  uint16_t* lsg = (uint16_t*)(lds + (int64_t)win * 2 * SEG);  // [ROWS][win]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
+  int32_t g0, g1;
+  split_range(K, S, blockIdx.y, g0, g1);
   const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
   const int rr = wave * RPW + r;
   const int64_t o = o_wg + rr;
@@ -63,8 +92,8 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   const uint16_t* my_sg = lsg + rr * win;
 
   double p = 0.0;
-  for (int64_t wb0 = 0; wb0 < nb; wb0 += win) {
-    const int64_t wb1 = wb0 + win < nb ? wb0 + win : nb;
+  for (int64_t wb0 = g0; wb0 < g1; wb0 += win) {
+    const int64_t wb1 = wb0 + win < g1 ? wb0 + win : g1;
     const int nwb = (int)(wb1 - wb0);
     const int nsteps = (nwb + BPS - 1) / BPS;
     const int ngroups = (nsteps + U - 1) / U;
@@ -75,7 +104,16 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
       wcur[u] = bl < nwb ? ld16_stream(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nwb * 8; i += WG) ((float4*)lx)[i] = ((const float4*)(x + wb0 * QK))[i];
+    for (int i = threadIdx.x; i < nwb * 8; i += WG) {  // i: 4 values, segment i/4, quarter i%4
+      const float4 f = ((const float4*)(x + wb0 * QK))[i];
+      unsigned char* d = lx + (i >> 2) * SEG + (i & 3) * 4 * XB;
+      if constexpr (XF64) {
+        ((double2*)d)[0] = make_double2((double)f.x, (double)f.y);
+        ((double2*)d)[1] = make_double2((double)f.z, (double)f.w);
+      } else {
+        *(float4*)d = f;
+      }
+    }
     stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
     __syncthreads();
 
@@ -92,7 +130,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
         const int bl = (gi * U + u) * BPS + j;
         const bool ok = bl < nwb;
         const int blc = ok ? bl : 0;
-        const double hsum = half_dot16(wcur[u], lx + blc * QK + hf * 16);
+        const double hsum = half_dot16<XF64>(wcur[u], lx + (2 * blc + hf) * SEG);
         const double other = dpp_f64<DPP_QUAD_SWAP1>(hsum);
         const double blk = __dadd_rn(hsum, other);  // the same bits in both lanes of the pair
         const double term = __dmul_rn((double)half_bits_to_float(my_sg[blc]), blk);
@@ -108,23 +146,80 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   }
   const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL4>(p));
   const double y = __dadd_rn(t, dpp_f64<DPP_ROW_SHL2>(t));
-  if (li == 0 && row_ok) out[o] = (float)y;
+  if (S == 1) {
+    if (li == 0 && row_ok) out[o] = (float)y;
+    return;
+  }
+  // Publish the chunk's partial and let the tile's last workgroup combine: the
+  // partial stores and the last arriver's loads are agent-scope atomic accesses,
+  // each writer waits for its store (vmcnt(0)) before the barrier, and only then
+  // does one thread take the ticket.
+  if (li == 0 && row_ok)
+    __hip_atomic_store(part + (int64_t)blockIdx.y * N + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
+  __syncthreads();
+  __shared__ int last_arrival;
+  if (threadIdx.x == 0)
+    last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned)(S - 1);
+  __syncthreads();
+  if (!last_arrival) return;
+  if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
+    const int64_t oo = o_wg + threadIdx.x;
+    double a = 0.0;
+    for (int s = 0; s < S; ++s)
+      a = __dadd_rn(a, __hip_atomic_load(part + (int64_t)s * N + oo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    out[oo] = (float)a;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool XF64>
+hipError_t launch_dq(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
+                     float* y, void* workspace, hipStream_t st) {
+  constexpr int RPW = 4, U = 4;
+  constexpr int rows_per_wg = (WG / 64) * RPW;
+  constexpr int bpb = 2 * (16 * (XF64 ? 8 : 4) + 16) + 2 * rows_per_wg;  // LDS bytes per block of the window
+  int32_t mx = 0;
+  for (int s = 0; s < splits; ++s) {
+    int32_t g0, g1;
+    split_range(K, splits, s, g0, g1);
+    mx = g1 - g0 > mx ? g1 - g0 : mx;
+  }
+  const int cap = (LDS_BUDGET / bpb) / SUPER * SUPER;
+  int win = ((mx + SUPER - 1) / SUPER) * SUPER;
+  if (win > cap) win = cap;
+  if (win < SUPER) win = SUPER;
+  const size_t lds = (size_t)win * bpb;
+  unsigned* tickets = (unsigned*)workspace;
+  double* part = splits == 1 ? nullptr : (double*)((char*)workspace + sk_partials_offset(N));
+  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
+  hipLaunchKernelGGL((k_gemv_dequant<RPW, U, XF64>), grid, block, lds, st, wq, ws, x, N, K, splits, win, y, part,
+                     tickets);
+  return hipGetLastError();
+}
+
+// Activation staged in binary32 (converted by every row's lanes) or binary64
+// (converted once per workgroup); QDG_DQ_X64 = 0 or 1, read once.
+bool dq_x64() {
+  static const bool v = [] {
+    const char* e = getenv("QDG_DQ_X64");
+    return e ? atoi(e) != 0 : true;
+  }();
+  return v;
 }
 
 }  // namespace
 
 hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                float* out, hipStream_t st) {
-  constexpr int RPW = 4, U = 4;
-  constexpr int rows_per_wg = (WG / 64) * RPW;
-  const int64_t nb = K / QK;
-  const int cap = (LDS_BUDGET / (QK * 4 + 2 * rows_per_wg)) / SUPER * SUPER;
-  int win = (int)(((nb + SUPER - 1) / SUPER) * SUPER);
-  if (win > cap) win = cap;
-  const size_t lds = (size_t)win * (QK * 4 + 2 * rows_per_wg);
-  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(WG);
-  hipLaunchKernelGGL((k_gemv_dequant<RPW, U>), grid, block, lds, st, wq, ws, x, N, K, win, out);
-  return hipGetLastError();
+  return launch_gemv_dequant_sk(wq, ws, N, K, x, 1, out, nullptr, st);
+}
+
+hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                                  int splits, float* y, void* workspace, hipStream_t st) {
+  if (dq_x64()) return launch_dq<true>(wq, ws, N, K, x, splits, y, workspace, st);
+  return launch_dq<false>(wq, ws, N, K, x, splits, y, workspace, st);
 }
 
 }  // namespace qdg

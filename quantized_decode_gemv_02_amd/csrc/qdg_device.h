@@ -176,6 +176,9 @@ hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int6
                             hipStream_t st);
 hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                float* out, hipStream_t st);
+hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                                  int splits, float* y, void* workspace, hipStream_t st);
+int64_t sk_partials_offset(int64_t N);
 hipError_t launch_gemv_mfma(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                             const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, int splits,
                             float* out, hipStream_t st);

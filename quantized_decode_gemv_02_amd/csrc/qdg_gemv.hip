@@ -276,13 +276,14 @@ hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int6
 }
 
 // Workspace of the in-kernel combine, each part 256-byte aligned: one ticket per
-// row tile (room for 16-row tiles), then the split partials [S][N].
+// row tile (room for 16-row tiles), then the split partials [S][N] -- binary32
+// for the quantized modes, binary64 for Dequant (sized for the latter).
 constexpr int64_t TILE_ROWS = 16;
 int64_t pad256(int64_t b) { return (b + 255) / 256 * 256; }
 int64_t sk_partials_offset(int64_t N) { return pad256(((N + TILE_ROWS - 1) / TILE_ROWS) * 4); }
 
 size_t sk_workspace_bytes(int64_t N, int splits) {
-  return (size_t)(sk_partials_offset(N) + pad256((int64_t)splits * N * 4));
+  return (size_t)(sk_partials_offset(N) + pad256((int64_t)splits * N * 8));
 }
 
 hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,

@@ -127,7 +127,7 @@ def test_fused_validation():
     assert call(K=500) == ESHAPE
     assert call(S=0) == ESHAPE
     assert call(S=65) == ESHAPE
-    assert call(mode=0, S=2) == EMODE                # Dequant: one pass only
+    assert call(mode=0, S=2, wsp=None) == EINVAL     # Dequant splits K too, with the workspace
     assert call(x=A + 4) == EALIGN
     assert call(wq=A + 8) == EALIGN
     assert call(wsp=A + 8) == EALIGN

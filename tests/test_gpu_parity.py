@@ -364,3 +364,23 @@ def test_fused_single_launch_dequant_and_edge_inputs():
         y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
         q.gemv_q8_fused(mode, dev(wq), dev(ws), y, dev(x.reshape(1, K)), 2, wsp)
         np.testing.assert_array_equal(host(y), want)
+
+
+@pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7)])
+def test_fused_dequant_split_k(N, K, S):
+    """Dequant split-K (binary64 chunk partials, ascending binary64 combine, one
+    rounding): within the Dequant tolerance of the binary64 reference, and almost
+    always the oracle's own binary32 result."""
+    announce(f"gemv_q8_fused dequant N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
+    Y, tn = oracle.reference_f64(0, wq, ws, x=x, nthreads=8)
+    want32 = oracle.gemv(0, wq, ws, x=x, nthreads=8)
+    wsp = q.sk_workspace(N, S)
+    for rep in range(3):
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_fused(0, dev(wq), dev(ws), y, dev(x.reshape(1, K)), S, wsp)
+        got = host(y)
+        assert oracle.within_tolerance(got, Y, tn).all()
+        assert (got == want32).mean() > 0.99
+    tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
+    assert not tickets.any()
