@@ -71,7 +71,7 @@ int qdg_gemv_q8(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64
   if (!shape_ok(N, K)) return QDG_ESHAPE;
   if (B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
   if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
-  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if ((N / 16 + 1) * splits >= ((int64_t)1 << 31)) return QDG_ESHAPE;  // a 1-D grid of tiles x chunks
   if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(out, 4)) return QDG_EALIGN;
   if (x && !aligned(x, 16)) return QDG_EALIGN;
   if (xq && !aligned(xq, 16)) return QDG_EALIGN;
@@ -106,7 +106,7 @@ int qdg_gemv_q8_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, in
   if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
   if (!shape_ok(N, K)) return QDG_ESHAPE;
   if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
-  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if ((N / 16 + 1) * splits >= ((int64_t)1 << 31)) return QDG_ESHAPE;  // a 1-D grid of tiles x chunks
   if (B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
   if (B != 1) return QDG_EMODE;
   if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) ||
@@ -123,7 +123,7 @@ int qdg_gemv_q8_fused(int mode, const int8_t* wq, const uint16_t* ws, int64_t N,
   if (!wq || !ws || !x || !y) return QDG_EINVAL;
   if (!shape_ok(N, K)) return QDG_ESHAPE;
   if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
-  if (N / 16 + 1 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if ((N / 16 + 1) * splits >= ((int64_t)1 << 31)) return QDG_ESHAPE;  // a 1-D grid of tiles x chunks
   if (splits > 1 && !workspace) return QDG_EINVAL;
   if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(x, 16) || !aligned(y, 4)) return QDG_EALIGN;
   if (splits > 1 && !aligned(workspace, 256)) return QDG_EALIGN;

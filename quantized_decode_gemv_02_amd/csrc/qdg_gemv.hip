@@ -25,7 +25,7 @@
 //    each wave keeps up to 2*U*1 KB of weights in flight; the first group is
 //    issued before the window's barrier.  Weights are read with the
 //    nontemporal hint (streamed once, never re-read).
-//  * grid = (row tiles, splits): the split s of a row covers the QWEN38 chunk
+//  * one workgroup per (row tile, split): the split s of a row covers the QWEN38 chunk
 //    [g0, g1) and writes partial[s][o]; an empty chunk writes +0.
 //  * QX = true (one launch for a whole projection): the workgroup quantizes its
 //    own window of the f32 activation into LDS -- the activation quantizer's
@@ -56,8 +56,9 @@ template <int MODE, int RPW, int U, bool FUSED, bool QX>
 __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
                                                  const float* __restrict__ xs, const float* __restrict__ x,
-                                                 int64_t N, int64_t K, int S, int win, float* __restrict__ out,
-                                                 unsigned* __restrict__ tickets, float* __restrict__ y) {
+                                                 int64_t N, int64_t K, int S, int win, int ntiles, int chunk_major,
+                                                 float* __restrict__ out, unsigned* __restrict__ tickets,
+                                                 float* __restrict__ y) {
   constexpr int LPR = 64 / RPW;  // lanes per row
   constexpr int BPS = LPR / 2;   // blocks per step of a row
   constexpr int TPP = BPS / 4;   // steps of one partial per step (1 or 2)
@@ -68,11 +69,15 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
-  const int s_idx = blockIdx.y;
+  // one workgroup per (row tile, chunk) on a 1-D grid: chunk-major order walks
+  // the S chunks of a tile consecutively (neighbouring workgroups read adjacent
+  // parts of the same rows, and each XCD sees only a few activation chunks)
+  const int tile = chunk_major ? (int)(blockIdx.x / S) : (int)(blockIdx.x % ntiles);
+  const int s_idx = chunk_major ? (int)(blockIdx.x % S) : (int)(blockIdx.x / ntiles);
   int32_t g0, g1;
   split_range(K, S, s_idx, g0, g1);
 
-  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  const int64_t o_wg = (int64_t)tile * ROWS;
   const int rr = wave * RPW + r;  // row within the workgroup
   const int64_t o = o_wg + rr;
   const bool row_ok = o < N;
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
     __syncthreads();
     __shared__ int last_arrival;
     if (threadIdx.x == 0)
-      last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_arrival = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (unsigned)(S - 1);
     __syncthreads();
     if (!last_arrival) return;
@@ -196,20 +201,23 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
         a = __fadd_rn(a, __hip_atomic_load(out + (int64_t)s * N + oo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       y[oo] = a;
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 struct Tuning {
   int rpw = 4;
   int unroll = 4;
+  int order = -1;  // -1: by S (chunk-major for S <= 4), 0: tile-major, 1: chunk-major
 };
 
-// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8}); they
-// change the lane layout and load depth only, never the arithmetic or its order.
+// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8}, QDG_ORDER
+// in {chunk, tile}); they change the lane layout, load depth and workgroup
+// order only, never the arithmetic or its order.
 Tuning tuning() {
   static Tuning t = [] {
     Tuning v;
+    if (const char* e = getenv("QDG_ORDER")) v.order = e[0] == 't' ? 0 : 1;
     if (const char* e = getenv("QDG_RPW")) v.rpw = atoi(e) == 8 ? 8 : 4;
     if (const char* e = getenv("QDG_UNROLL")) {
       const int u = atoi(e);
@@ -218,6 +226,14 @@ Tuning tuning() {
     return v;
   }();
   return t;
+}
+
+// Workgroup order.  Measured on the narrow projections: walking a tile's chunks
+// consecutively is 3-6% faster at S = 4 (5120x8192), tiles first 20% faster at
+// S = 16 (5120x25600).
+int chunk_major(int splits) {
+  const int o = tuning().order;
+  return o >= 0 ? o : (splits <= 4 ? 1 : 0);
 }
 
 int window_blocks(int64_t K, int splits, int bytes_per_block) {
@@ -241,9 +257,10 @@ hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
   constexpr int bpb = window_bytes_per_block<MODE, RPW>();
   const int win = window_blocks(K, splits, bpb);
   const int rows_per_wg = (WG / 64) * RPW;
-  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
+  const int ntiles = (int)((N + rows_per_wg - 1) / rows_per_wg);
+  const dim3 grid((unsigned)((int64_t)ntiles * splits)), block(WG);
   hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U, FUSED, QX>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs,
-                     x, N, K, splits, win, out, tickets, y);
+                     x, N, K, splits, win, ntiles, chunk_major(splits), out, tickets, y);
   return hipGetLastError();
 }
 
