@@ -36,6 +36,7 @@
 //    -P, so the compiler's wait counts keep the look-ahead in flight.
 //  * Weight rows past N read row N-1 and store nothing; activation rows t >= B
 //    read row B-1 and store nothing (an MFMA row never mixes into another).
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "qdg_device.h"
@@ -254,49 +255,59 @@ hipError_t launch_mp(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
 
 // ---------------------------------------------------------------------------
 // The fast path for K a multiple of 256 and ws 16-byte aligned.  Same sums and
-// operand layouts as k_gemv_mfma, but a workgroup of 8 waves owns 32*TPW weight
-// rows (2*TPW tiles of 16), wave v = 4*g + r working on tiles g, g + 2, ...
-// (TPW of them, one A operand read serving all) for partial r, and every byte of
-// a step -- weights, activation words, scales -- moves from global memory
-// straight into LDS (global_load_lds) into a ring of P slots, P - 1 steps
-// ahead.  More rows a workgroup means fewer re-reads of the activations, which
-// every workgroup needs in full.  No data passes through registers, so nothing
-// the compiler schedules can make a wave wait on loads that are still ahead of
-// it; instead every wave issues exactly dma_loads() loads a step and waits,
-// before each step's barrier, until only the later steps' loads are outstanding
+// operand layouts as k_gemv_mfma, but a workgroup of WV waves (4 or 8) owns
+// 16*(WV/4)*TPW weight rows: wave v = 4*g + r works on tiles g, g + WV/4, ...
+// (TPW of them, one A operand read serving all) for partial r.  Every byte of a
+// step -- weights, activation words, scales -- moves from global memory straight
+// into LDS (global_load_lds), into a ring of P slots, P - 1 steps ahead.  More
+// rows a workgroup means fewer re-reads of the activations, which every
+// workgroup needs in full.  No data passes through registers, so nothing the
+// compiler schedules can make a wave wait on loads that are still ahead of it;
+// instead every wave issues exactly DMA_LOADS loads a step and waits, before
+// each step's barrier, until only the later steps' loads are outstanding
 // (s_waitcnt vmcnt).  The barrier then makes the whole workgroup's copies of the
 // step visible, and the slot it refills for step s + P - 1 was last read in step
 // s - 1, which every wave has finished.
 //
-// Slot layout: W [32*TPW rows][256] and A (L) [16 rows][256] with the 16-byte
-// chunk c of row r at chunk index c ^ (r mod 16) -- a wave's load writes 1 KiB in
-// lane order, so lane (r4 = l/16, j = l%16) fetches global chunk j ^ row to land
-// it in place; SX [16][8] activation scales; SG [32*TPW][8] weight scales; JUNK
-// for loads that only keep the count uniform.
-template <int MODE, int TPW>
+// The shared loads of a step besides the weights are a list of jobs -- the
+// activation words (4 loads of 4 rows, and 4 more for the TwoPass low words),
+// the activation scales (2 dword loads) and the weight scales (one 16-byte load
+// per 64 rows) -- dealt round-robin to the waves; a wave with no job left that
+// step issues a one-dword placeholder load, so every wave issues the same count.
+//
+// Slot layout: W [rows][256] and A (L) [16 rows][256] with the 16-byte chunk c
+// of row r at chunk index c ^ (r mod 16) -- a wave's load writes 1 KiB in lane
+// order, so lane (r4 = l/16, j = l%16) fetches global chunk j ^ row to land it
+// in place; SX [16][8] activation scales; SG [rows][8] weight scales; JUNK for
+// the placeholders.
+template <int MODE, int WV, int TPW>
 struct DSlot {
-  static constexpr int DROWS = 32 * TPW;
+  static constexpr int TG = WV / 4;  // tile groups
+  static constexpr int DROWS = 16 * TG * TPW;
   static constexpr int W = 0;
   static constexpr int A = W + DROWS * 256;
   static constexpr int L = A + 16 * 256;
   static constexpr int SX = L + (MODE == 2 ? 16 * 256 : 0);
   static constexpr int SG = SX + 16 * STEP * 4;
-  static constexpr int SG_BYTES = (DROWS * 16 + 1023) / 1024 * 1024;  // whole 1 KiB loads
-  static constexpr int JUNK = SG + SG_BYTES;
+  static constexpr int NG = (DROWS * 16 + 1023) / 1024;  // weight-scale loads (1 KiB each)
+  static constexpr int JUNK = SG + NG * 1024;
   static constexpr int BYTES = JUNK + 64 * 4;
-  // loads a wave a step: TPW of weights, then one (Int8Act) or two (TwoPass) more
-  static constexpr int DMA_LOADS = TPW + (MODE == 2 ? 2 : 1);
+  static constexpr int JOBS = (MODE == 2 ? 8 : 4) + 2 + NG;
+  static constexpr int AUX = (JOBS + WV - 1) / WV;  // aux loads a wave a step
+  static constexpr int WLOADS = DROWS / (4 * WV);   // weight loads a wave a step
+  static constexpr int DMA_LOADS = WLOADS + AUX;
+  static_assert(DROWS % (4 * WV) == 0, "whole weight loads per wave");
 };
-template <int MODE, int TPW, int P>
-constexpr int dma_lds_bytes() { return P * DSlot<MODE, TPW>::BYTES; }
+template <int MODE, int WV, int TPW, int P>
+constexpr int dma_lds_bytes() { return P * DSlot<MODE, WV, TPW>::BYTES; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // global_load_lds of 16 or 4 bytes a lane; AUX 2 sets the nontemporal hint
-template <int BYTES_, int AUX>
+template <int BYTES_, int AUXF>
 __device__ __forceinline__ void dma(const void* g, unsigned char* l) {
-  static_assert((BYTES_ == 16 || BYTES_ == 4) && (AUX == 0 || AUX == 2), "supported forms");
-  if constexpr (BYTES_ == 16 && AUX == 2)
+  static_assert((BYTES_ == 16 || BYTES_ == 4) && (AUXF == 0 || AUXF == 2), "supported forms");
+  if constexpr (BYTES_ == 16 && AUXF == 2)
     __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 2);
   else if constexpr (BYTES_ == 16)
     __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
@@ -316,18 +327,20 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int MODE, int TPW, int P>
-__global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
-                                                     const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
-                                                     const float* __restrict__ xs, int64_t N, int64_t K, int B, int S,
-                                                     float* __restrict__ out) {
-  using SL = DSlot<MODE, TPW>;
-  constexpr int DROWS = SL::DROWS;
-  static_assert(SL::BYTES >= WAVES * TPW * 4 * 64 * 4, "the final reduction reuses slot 0");
+template <int MODE, int WV, int TPW, int P>
+__global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restrict__ wq,
+                                                          const uint16_t* __restrict__ ws,
+                                                          const int8_t* __restrict__ xq,
+                                                          const int8_t* __restrict__ xl,
+                                                          const float* __restrict__ xs, int64_t N, int64_t K, int B,
+                                                          int S, float* __restrict__ out) {
+  using SL = DSlot<MODE, WV, TPW>;
+  constexpr int DROWS = SL::DROWS, TG = SL::TG;
+  static_assert(SL::BYTES >= WV * TPW * 4 * 64 * 4, "the final reduction reuses slot 0");
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tg = wave >> 2, res = wave & 3;  // tile group (tiles tg, tg + 2, ...), owned partial
+  const int tg = wave >> 2, res = wave & 3;  // tile group (tiles tg, tg + TG, ...), owned partial
   const int col = lane & 15, grp = lane >> 4;
   const int s_idx = blockIdx.y;
   int32_t g0, g1;
@@ -338,47 +351,41 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__
 
   // ---- load side (per lane, fixed over the steps)
   const int r4 = lane >> 4, j = lane & 15;
-  const int8_t* wsrc[TPW];  // load m of this wave: rows 4*(8*m + wave) + r4 of the tile
-  int wcb[TPW];
+  const int8_t* wsrc[SL::WLOADS];  // load m of this wave: rows 4*(WV*m + wave) + r4
+  int wcb[SL::WLOADS];
 #pragma unroll
-  for (int m = 0; m < TPW; ++m) {
-    const int row = 4 * (8 * m + wave) + r4;
+  for (int m = 0; m < SL::WLOADS; ++m) {
+    const int row = 4 * (WV * m + wave) + r4;
     const int c = (j ^ row) & 15;  // fetched so that it lands at chunk j
     int64_t o = o_wg + row;
     if (o >= N) o = N - 1;
     wsrc[m] = wq + o * K + 16 * (c & 1);
     wcb[m] = c >> 1;
   }
-  // the aux load: activation words of rows 4*(wave%4) + r4 (low words on waves 4-7 under TwoPass)
-  const int arow = 4 * (wave & 3) + r4;
-  const int ac = (j ^ arow) & 15;
-  const int8_t* asrc = ((MODE == 2 && wave >= 4) ? xl : xq) + (int64_t)min(arow, B - 1) * K + 16 * (ac & 1);
-  const int acb = ac >> 1;
-  // activation scales: load q = wave & 1 covers [t][k] = 64*q + lane
-  const int sidx = 64 * (wave & 1) + lane;
-  const float* xsrc = xs + (int64_t)min(sidx >> 3, B - 1) * nb;
-  const int sk = sidx & 7;
-  // weight scales: load gq covers rows 64*gq + lane (mod the workgroup's rows)
-  const int gq = max(MODE == 2 ? wave - 2 : wave - 6, 0);
-  int64_t so = o_wg + ((64 * gq + lane) % DROWS);
-  if (so >= N) so = N - 1;
-  const uint16_t* gsrc = ws + so * nb;
-  constexpr int NG = SL::SG_BYTES / 1024;  // weight-scale loads a step (1 or 2)
-  // which aux loads this wave issues: 0 activation words, 1 activation scales, 2 weight scales, 3 placeholder
-  //   Int8Act: waves 0-3 words, 4-5 activation scales, 6 (and 7 when NG = 2) weight scales
-  //   TwoPass, second aux load: waves 0-1 activation scales, 2 (and 3) weight scales
-  const int kind1 = MODE == 2 ? 0 : (wave < 4 ? 0 : wave < 6 ? 1 : (wave - 6 < NG ? 2 : 3));
-  const int kind2 = wave < 2 ? 1 : (wave - 2 < NG ? 2 : 3);  // TwoPass only
-  static_assert(NG <= 2, "weight-scale loads fit the waves given to them");
 
-  auto issue_aux = [&](int kind, int blk0, unsigned char* slot) {
-    if (kind == 0) {  // uniform branches: each path issues exactly one load
-      const int blk = min(blk0 + acb, g1 - 1);
-      dma<16, 0>(asrc + (int64_t)blk * QK, slot + ((MODE == 2 && wave >= 4) ? SL::L : SL::A) + (wave & 3) * 1024);
-    } else if (kind == 1) {
-      dma<4, 0>(xsrc + min(blk0 + sk, g1 - 1), slot + SL::SX + (wave & 1) * 256);
-    } else if (kind == 2) {
-      dma<16, 0>(gsrc + min(blk0, g1 - STEP), slot + SL::SG + gq * 1024);
+  // one aux job (uniform over the wave): 0..3 high words of rows 4k.., 4..7 low
+  // words (TwoPass), then 2 activation-scale loads, then NG weight-scale loads
+  constexpr int NW_JOBS = MODE == 2 ? 8 : 4;
+  auto issue_job = [&](int job, int blk0, unsigned char* slot) {
+    if (job < NW_JOBS) {
+      const int q = job & 3;
+      const int arow = 4 * q + r4;
+      const int ac = (j ^ arow) & 15;
+      const int8_t* src = (MODE == 2 && job >= 4) ? xl : xq;
+      const int blk = min(blk0 + (ac >> 1), g1 - 1);
+      dma<16, 0>(src + (int64_t)min(arow, B - 1) * K + (int64_t)blk * QK + 16 * (ac & 1),
+                 slot + ((MODE == 2 && job >= 4) ? SL::L : SL::A) + q * 1024);
+    } else if (job < NW_JOBS + 2) {
+      const int sq = job - NW_JOBS;
+      const int sidx = 64 * sq + lane;  // [t][k] = sidx
+      dma<4, 0>(xs + (int64_t)min(sidx >> 3, B - 1) * nb + min(blk0 + (sidx & 7), g1 - 1),
+                slot + SL::SX + sq * 256);
+    } else if (job < SL::JOBS) {
+      const int gq = job - NW_JOBS - 2;
+      int64_t o = o_wg + ((64 * gq + lane) % DROWS);
+      if (o >= N) o = N - 1;
+      // steps are whole when this path runs; the clamp keeps the look-ahead in bounds
+      dma<16, 0>(ws + o * nb + min(blk0, g1 - STEP), slot + SL::SG + gq * 1024);
     } else {
       dma<4, 0>(xs, slot + SL::JUNK);
     }
@@ -387,10 +394,10 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__
     unsigned char* slot = lds + (s % P) * SL::BYTES;
     const int blk0 = g0 + min(s, nsteps - 1) * STEP;  // steps past the chunk repeat its last one
 #pragma unroll
-    for (int m = 0; m < TPW; ++m)  // nontemporal: the weights are streamed once
-      dma<16, 2>(wsrc[m] + (int64_t)(blk0 + wcb[m]) * QK, slot + SL::W + (8 * m + wave) * 1024);
-    issue_aux(kind1, blk0, slot);
-    if constexpr (MODE == 2) issue_aux(kind2, blk0, slot);
+    for (int m = 0; m < SL::WLOADS; ++m)  // nontemporal: the weights are streamed once
+      dma<16, 2>(wsrc[m] + (int64_t)(blk0 + wcb[m]) * QK, slot + SL::W + (WV * m + wave) * 1024);
+#pragma unroll
+    for (int a = 0; a < SL::AUX; ++a) issue_job(wave + WV * a, blk0, slot);
   };
 
   // ---- read side
@@ -401,14 +408,14 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__
     a_rd[h] = SL::A + col * 256 + (((c ^ col) & 15) << 4) + 8 * (grp & 1);
 #pragma unroll
     for (int m = 0; m < TPW; ++m)
-      w_rd[m][h] = SL::W + (16 * (tg + 2 * m) + col) * 256 + (((c ^ col) & 15) << 4) + 8 * (grp & 1);
+      w_rd[m][h] = SL::W + (16 * (tg + TG * m) + col) * 256 + (((c ^ col) & 15) << 4) + 8 * (grp & 1);
   }
   const int sx_rd = SL::SX + grp * 4 * STEP * 4;  // rows 4*grp .. 4*grp + 3
   int sg_rd[TPW];
 #pragma unroll
-  for (int m = 0; m < TPW; ++m) sg_rd[m] = SL::SG + (16 * (tg + 2 * m) + col) * 16;
+  for (int m = 0; m < TPW; ++m) sg_rd[m] = SL::SG + (16 * (tg + TG * m) + col) * 16;
 
-  // partial `res` of (t = 4*grp + i, o = o_wg + 16*(tg + 2*m) + col)
+  // partial `res` of (t = 4*grp + i, o = o_wg + 16*(tg + TG*m) + col)
   float p[TPW][4];
 #pragma unroll
   for (int m = 0; m < TPW; ++m)
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__
   if (res == 0) {
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
-      const int64_t oo = o_wg + 16 * (tg + 2 * m) + col;
+      const int64_t oo = o_wg + 16 * (tg + TG * m) + col;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = grp * 4 + i;
@@ -473,31 +480,36 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma_dma(const int8_t* __restrict__
   }
 }
 
-template <int MODE, int TPW, int P>
+template <int MODE, int WV, int TPW, int P>
 hipError_t launch_dma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
                       const int8_t* xl, const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
-  constexpr int rows = DSlot<MODE, TPW>::DROWS;
-  const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)splits), block(WG);
-  constexpr int lds = dma_lds_bytes<MODE, TPW, P>();
+  constexpr int rows = DSlot<MODE, WV, TPW>::DROWS;
+  const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)splits), block(64 * WV);
+  constexpr int lds = dma_lds_bytes<MODE, WV, TPW, P>();
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   // above 64 KiB of LDS the kernel's dynamic-LDS limit is raised (once)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, TPW, P>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, WV, TPW, P>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, TPW, P>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B, splits,
-                     out);
+  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, WV, TPW, P>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B,
+                     splits, out);
   return hipGetLastError();
 }
 
-// Fast-path shape (read once): QDG_MFMA_TPW = 1 or 2 tiles a wave (32 or 64 rows
-// a workgroup), QDG_MFMA_RING = 3 or 4 slots.
+// Fast-path shape (read once): QDG_MFMA_SHAPE = "WV,TPW,P" among the compiled
+// ones -- 4,4,2 (the default), 4,4,3, 4,2,2, 8,2,3.  On 25600x5120, B = 16:
+// 4,4,2 streams 4.30 / 3.96 TB/s (Int8Act / TwoPass), 8,2,3 4.27 / 3.73,
+// 4,4,3 4.06 / 3.80, 4,2,3 3.73 / 3.24.
 struct DmaShape {
-  int tpw, ring;
+  int wv, tpw, ring;
 };
 DmaShape dma_shape() {
   static const DmaShape d = [] {
-    DmaShape v{2, 3};
-    if (const char* e = getenv("QDG_MFMA_TPW")) v.tpw = atoi(e) == 1 ? 1 : 2;
-    if (const char* e = getenv("QDG_MFMA_RING")) v.ring = atoi(e) == 4 ? 4 : 3;
+    DmaShape v{4, 4, 2};
+    if (const char* e = getenv("QDG_MFMA_SHAPE")) {
+      DmaShape t{0, 0, 0};
+      if (sscanf(e, "%d,%d,%d", &t.wv, &t.tpw, &t.ring) == 3) v = t;
+    }
     return v;
   }();
   return d;
@@ -509,11 +521,14 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
   // the fast path needs whole steps (K/32 a multiple of 8) and 16-byte weight-scale words
   if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && !getenv("QDG_MFMA_GENERAL")) {
     const DmaShape d = dma_shape();
-    if (d.tpw == 1)
-      return d.ring == 4 ? launch_dma<MODE, 1, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st)
-                         : launch_dma<MODE, 1, 3>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
-    return d.ring == 4 ? launch_dma<MODE, 2, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st)
-                       : launch_dma<MODE, 2, 3>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+#define QDG_DMA(WV_, TPW_, P_)                   \
+  if (d.wv == WV_ && d.tpw == TPW_ && d.ring == P_) \
+    return launch_dma<MODE, WV_, TPW_, P_>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+    QDG_DMA(4, 4, 3);
+    QDG_DMA(4, 2, 2);
+    QDG_DMA(8, 2, 3);
+#undef QDG_DMA
+    return launch_dma<MODE, 4, 4, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
   }
   return launch_mp<MODE, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
 }
