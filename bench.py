@@ -14,16 +14,19 @@ timing; the weights rotate over enough copies (>= 1 GiB between reuses of a
 copy) that the 256 MB Infinity Cache cannot serve them.
 
 Prints ONE JSON line:
-  value      = algorithmic GEMV bytes of a step / step time (GB/s); algorithmic
+  value      = algorithmic GEMV bytes of a step / step time (GB/s), timed over K
+               steps with no events in the stream; algorithmic
                bytes per GEMV = N*K weight bytes + N*K/16 scale bytes + the
                activation in the mode's encoding (K + K/8 Int8Act, 2K + K/8
                TwoPass) + 4N output bytes (split-K partial traffic not counted);
   roofline   = the down-proj TwoPass GEMV (the step's dominant kernel): its
                algorithmic bytes / its mean launch duration from HIP events
-               around every launch in the timed region, against 8 TB/s;
-  config.modes = per mode and projection: S, the GEMV's mean launch time (HIP
-               events around every GEMV launch of a second pass of the same
-               steps) and GB/s;
+               around each of its launches in a second timed pass of the same K
+               steps (events around every GEMV), against 8 TB/s;
+  config.modes = per mode and projection: S, the GEMV's mean launch time (the
+               same second pass), GB/s, and its share of the read ceiling;
+  config.read_ceiling = qdg_stream_read over each projection's bytes and 1 GiB:
+               the practical ceiling of a launch that only reads;
   cpu_baseline = the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
@@ -59,6 +62,7 @@ def parse():
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--path", choices=("single", "fused", "staged"), default="staged")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
@@ -210,27 +214,26 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # timed region: K steps, HIP events around the dominant GEMV launch only (events on every
-    # launch would add their own stream work between the kernels of the step)
+    # Timed region 1 (value): K steps with no events.  HIP events between the kernels of a
+    # step add stream work of their own (about 7 us a step here), so the step is timed bare.
     K = args.steps
-    ev = {dom_key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for _ in range(K)]}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        run_step(i, ev)
+        run_step(i)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / K
-    dom_ms = sum(a.elapsed_time(b) for a, b in ev[dom_key]) / K
 
-    # per-GEMV launch times: a second pass of the same steps with events around every GEMV
+    # Timed region 2 (roofline and the per-mode table): the same K steps again, with a HIP event
+    # pair around every GEMV launch; the dominant kernel's mean launch time comes from here.
     ev_all = {key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     for _ in range(K)] for key in keys}
     for i in range(K):
         run_step(i, ev_all)
     torch.cuda.synchronize()
     gemv_ms = {key: sum(a.elapsed_time(b) for a, b in ev_all[key]) / K for key in keys}
+    dom_ms = gemv_ms[dom_key]
 
     # the other paths' step times, for reference (same steps, same rotation)
     other_ms = {}
@@ -275,6 +278,18 @@ def main() -> int:
                 "splits": chosen[(mode, si)], "alg_bytes": b, "gemv_us": round(us, 3),
                 "gemv_GBs": round(b / us / 1e3, 1), "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
 
+    def mean_launch_us(calls, reps):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            pairs[i][0].record()
+            calls[i % len(calls)]()
+            pairs[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in pairs) / reps * 1e3
+
     # Dequant on the same projections, beside the step: one launch with the same S (binary64
     # chunk partials and an ascending binary64 combine in the last workgroup of each row tile)
     if not args.no_dequant:
@@ -301,6 +316,26 @@ def main() -> int:
             per_mode["dequant"][sh.name] = {"splits": S, "alg_bytes": b, "gemv_us": round(us, 3),
                                             "gemv_GBs": round(b / us / 1e3, 1),
                                             "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
+
+    # The practical read ceiling: qdg_stream_read (contiguous 64 KiB slabs a workgroup, nothing
+    # but 16-byte nontemporal loads) over as many bytes as each GEMV launch moves, rotated over
+    # a pool larger than the Infinity Cache, and over 1 GiB.
+    ceiling = {}
+    if not args.no_ceiling:
+        pool = torch.empty(3 << 29, dtype=torch.uint8, device=dev)  # 1.5 GiB
+        sink = torch.zeros(256, dtype=torch.int32, device=dev)
+        sizes = {sh.name: alg_bytes(2, sh.N, sh.K) // 16 * 16 for sh in shapes}
+        sizes["1GiB"] = 1 << 30
+        for name, nb_ in sizes.items():
+            regions = max(1, pool.numel() // nb_)
+            calls = [q.bind_stream_read(pool[r * nb_:], nb_, sink) for r in range(regions)]
+            us = mean_launch_us(calls, max(20, 4 * regions))
+            ceiling[name] = {"bytes": nb_, "us": round(us, 3), "GBs": round(nb_ / us / 1e3, 1)}
+        del pool
+        for mname, per_shape in per_mode.items():
+            for sname, rec in per_shape.items():
+                if sname in ceiling:
+                    rec["pct_of_read_ceiling"] = round(100 * rec["gemv_GBs"] / ceiling[sname]["GBs"], 1)
 
     # ---- CPU baseline: the oracle on the same step (whole steps, repeated for a bounded time)
     cpu = None
@@ -342,6 +377,7 @@ def main() -> int:
                    "path": args.path, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
+                   "read_ceiling": ceiling,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,

@@ -199,6 +199,17 @@ int qdg_block_dots(int mode, const int8_t *wq, int64_t N, int64_t K,
                    int32_t *dh, int32_t *dl, qdg_stream stream);
 
 /*
+ * Measurement hook: reads `bytes` bytes of device memory at `buf` once, as fast
+ * as the library knows how (contiguous 64 KiB slabs per workgroup, 16-byte
+ * nontemporal loads), and does nothing else, so its time is the practical
+ * ceiling of a GEMV launch that moves the same bytes.  `sink` is a device array
+ * of 256 uint32 that is written only in the practically impossible case that
+ * the folded data hits one fixed value (it keeps the loads from being dead).
+ * bytes >= 16 and a multiple of 16; buf 16-byte aligned.
+ */
+int qdg_stream_read(const void *buf, int64_t bytes, uint32_t *sink, qdg_stream stream);
+
+/*
  * Host only: the split-K chunk boundaries in 32-value blocks (QWEN38 page,
  * gk_gemv_hl_sk): K runs in 512-value superblocks, per = ceil((K/512)/splits),
  * chunk s takes superblocks [s*per, min((s+1)*per, K/512)) and the last chunk

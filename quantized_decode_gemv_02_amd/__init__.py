@@ -65,6 +65,7 @@ _SIGS = {
     "qdg_argmax": ([_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
     "qdg_split_bounds": ([_I64, _I, _P], _I),
+    "qdg_stream_read": ([_P, _I64, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -271,6 +272,13 @@ def bind_gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None)
         _ptr(t, None, n)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return Bound("qdg_gemv_q8_fused", mode, wq, ws, N, K, x, int(splits), y, workspace, nbytes, _stream())
+
+
+def bind_stream_read(buf, nbytes: int, sink) -> Bound:
+    """The measurement hook: read ``nbytes`` of ``buf`` once (the practical read ceiling)."""
+    _ptr(buf, None, "buf")
+    _ptr(sink, None, "sink")
+    return Bound("qdg_stream_read", buf, int(nbytes), sink, _stream())
 
 
 def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:

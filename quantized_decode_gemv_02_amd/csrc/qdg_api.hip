@@ -161,6 +161,13 @@ int qdg_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_
   return hip_status(qdg::launch_block_dots(mode, wq, N, K, xq, xl, B, dh, dl, as_stream(stream)));
 }
 
+int qdg_stream_read(const void* buf, int64_t bytes, uint32_t* sink, qdg_stream stream) {
+  if (!buf || !sink) return QDG_EINVAL;
+  if (bytes < 16 || bytes % 16 || bytes / (64 * 1024) >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QDG_EALIGN;
+  return hip_status(qdg::launch_stream_read(buf, bytes, sink, as_stream(stream)));
+}
+
 int qdg_split_bounds(int64_t K, int splits, int32_t* first_block) {
   if (!first_block) return QDG_EINVAL;
   if (K < qdg::QK || K % qdg::QK || K > ((int64_t)1 << 31)) return QDG_ESHAPE;

@@ -191,6 +191,7 @@ hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_
 hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                          int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st);
 hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
                          hipStream_t st);
 }  // namespace qdg

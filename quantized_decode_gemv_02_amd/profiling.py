@@ -5,8 +5,9 @@ The byte counters are scaled by what the same counter reads for a plain device
 copy of 256 MiB (``bench.py --calibrate-copy``): the copy reads and writes exactly
 268435456 bytes, so ``factor = 262144 KiB / counter(copy)`` per counter.
 
-Usage (from the repository root, after the three rocprofv3 runs):
-    python -m quantized_decode_gemv_02_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT.md OUT.json
+Usage (from the repository root, after the rocprofv3 runs):
+    python -m quantized_decode_gemv_02_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT.md OUT.json \
+        KERNEL GRID "COMMAND" [OCC_DIR]
 """
 from __future__ import annotations
 
@@ -55,6 +56,38 @@ def trace_by_grid(trace_dir: str) -> dict:
     return {k: (sum(v) / len(v), min(v), max(v), len(v)) for k, v in acc.items()}
 
 
+# MI355X (gfx950): 256 CUs of 4 SIMDs; 512 VGPRs (arch + accumulation) a SIMD lane,
+# allocated in granules of 8; at most 8 waves a SIMD; 160 KiB of LDS a CU.
+CUS, SIMDS, VGPR_FILE, VGPR_GRANULE, WAVES_PER_SIMD, LDS_BYTES = 256, 4, 512, 8, 8, 160 * 1024
+
+
+def occupancy(vgpr: int, agpr: int, lds: int, wg_size: int, grid: int) -> dict:
+    """Resident capacity of one launch shape and how its grid fills it (theoretical)."""
+    regs = -(-(vgpr + agpr) // VGPR_GRANULE) * VGPR_GRANULE
+    per_simd = min(WAVES_PER_SIMD, VGPR_FILE // max(regs, 1))
+    wpw = -(-wg_size // 64)  # waves a workgroup
+    wg_cu = (SIMDS * per_simd) // wpw
+    if lds > 0:
+        wg_cu = min(wg_cu, LDS_BYTES // lds)
+    wgs = -(-grid // wg_size)
+    cap = wg_cu * CUS
+    rounds = wgs / cap if cap else float("inf")
+    return {"waves_per_simd": per_simd, "wg_per_cu": wg_cu, "workgroups": wgs, "capacity": cap,
+            "fill": min(1.0, wgs / cap) if cap else 0.0, "rounds": rounds,
+            "tail": rounds - int(rounds) if rounds > 1 and rounds != int(rounds) else 0.0}
+
+
+def trace_shapes(trace_dir: str) -> dict:
+    """(kernel, total work-items) -> resources of the dispatch, from the kernel trace."""
+    out = {}
+    for r in csv.DictReader(open(_one(trace_dir, "*kernel_trace.csv"))):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        out[(short(r["Kernel_Name"]), grid)] = (int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]),
+                                                int(r["LDS_Block_Size"]), wg)
+    return out
+
+
 def counters(pmc_dir: str) -> list[dict]:
     return list(csv.DictReader(open(_one(pmc_dir, "*counter_collection.csv"))))
 
@@ -78,7 +111,16 @@ def per_kernel_grid(rows: list[dict]) -> dict:
     return {k: (sum(v) / len(v), len(v), min(v), max(v)) for k, v in acc.items()}
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, dominant: tuple[str, int]):
+def per_kernel_counters(pmc_dir: str) -> dict:
+    """(kernel, grid) -> {counter: mean value per dispatch} for a multi-counter run."""
+    acc = defaultdict(lambda: defaultdict(list))
+    for r in counters(pmc_dir):
+        acc[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, dominant: tuple[str, int],
+              occ_dir: str | None = None):
     ks = kernel_stats(trace_dir)
     fr, wr = counters(fetch_dir), counters(write_dir)
     ff, wf = scale_factor(fr), scale_factor(wr)
@@ -106,6 +148,26 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
         w_mean = wk.get(key, (0.0, 0, 0.0, 0.0))[0]
         lines.append(f"| {key[0]} | {key[1]} | {n} | {f_mean * ff / 1e6:.3f} | {f_min * ff / 1e6:.3f}..{f_max * ff / 1e6:.3f} "
                      f"| {w_mean * wf / 1e6:.4f} |")
+    shapes = trace_shapes(trace_dir)
+    occ_meas = per_kernel_counters(occ_dir) if occ_dir else {}
+    lines += ["", "## Occupancy and split-K block fill", "",
+              "Theoretical residency from each dispatch's registers as the kernel trace reports them (VGPR + "
+              "AGPR, granule 8, 512 a lane), its LDS (160 KiB a CU; the trace reports the static allocation only "
+              "-- the B = 1 kernels' dynamic windows are a few KB and never the limit) and workgroup size, on 256 "
+              "CUs x 4 SIMDs with at most 8 waves a SIMD; fill = workgroups / resident capacity (capped at 1), "
+              "rounds = workgroups / capacity.  Waves launched: SQ_WAVES from a third pass (--pmc SQ_WAVES "
+              "SQ_WAVE_CYCLES GRBM_GUI_ACTIVE), which checks the grid.", "",
+              "| kernel | grid | VGPR+AGPR | LDS B | waves/SIMD | WG/CU | WGs | fill | rounds | waves launched |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(shapes):
+        if not key[0].startswith("k_gemv"):
+            continue
+        v, a, l, wg = shapes[key]
+        o = occupancy(v, a, l, wg, key[1])
+        m = occ_meas.get(key, {})
+        waves = f"{m['SQ_WAVES']:.0f}" if "SQ_WAVES" in m else "-"
+        lines.append(f"| {key[0]} | {key[1]} | {v}+{a} | {l} | {o['waves_per_simd']} | {o['wg_per_cu']} | "
+                     f"{o['workgroups']} | {o['fill']:.2f} | {o['rounds']:.2f} | {waves} |")
     dom = {"kernel": dominant[0], "grid": dominant[1], "kernel_source_sha": kernel_source_sha()}
     if (dominant[0], dominant[1]) in tg:
         dom["trace_avg_us"] = tg[(dominant[0], dominant[1])][0] / 1e3
@@ -125,4 +187,5 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
 if __name__ == "__main__":
     t, f, w, md, js, kern, grid = sys.argv[1:8]
     cmd = sys.argv[8] if len(sys.argv) > 8 else ""
-    print(summarize(t, f, w, md, js, cmd, (kern, int(grid))))
+    occ = sys.argv[9] if len(sys.argv) > 9 else None
+    print(summarize(t, f, w, md, js, cmd, (kern, int(grid)), occ))

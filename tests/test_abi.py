@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -132,6 +132,15 @@ def test_fused_validation():
     assert call(wq=A + 8) == EALIGN
     assert call(wsp=A + 8) == EALIGN
     assert call(nbytes=need - 4) == EWORKSPACE
+
+
+def test_stream_read_validation():
+    f = lib.qdg_stream_read
+    assert f(None, 1024, P(A), None) == EINVAL
+    assert f(P(A), 1024, None, None) == EINVAL
+    assert f(P(A), 8, P(A), None) == ESHAPE
+    assert f(P(A), 1000, P(A), None) == ESHAPE
+    assert f(P(A + 8), 1024, P(A), None) == EALIGN
 
 
 def test_split_bounds_validation():
