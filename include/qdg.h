@@ -188,6 +188,28 @@ size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N);
 int qdg_argmax(const float *y, int64_t B, int64_t N, int32_t *idx,
                void *workspace, size_t workspace_bytes, qdg_stream stream);
 
+/* Bytes of device workspace qdg_gemv_q8_argmax needs for N output rows (0 if N is out of range). */
+size_t qdg_gemv_argmax_workspace_bytes(int64_t N);
+
+/*
+ * The LM-head tail in two launches (B == 1, splits == 1): the GEMV of
+ * qdg_gemv_q8 writes the logits y [1][N] and, from each workgroup of 16 rows,
+ * the arg-max key of its largest logit (megakernel page: amax_key and the
+ * per-block arg-max partials of ph_argmax_part, here in the GEMV's epilogue);
+ * a final pass over the keys writes idx[0] = the smallest i with y[i] equal to
+ * the maximum (lane kernel library page, module doc: first of equal maxima;
+ * IEEE comparison, -0 equals +0, NaN outside the contract).  y is the same as
+ * qdg_gemv_q8's and idx the same as qdg_argmax's over it.  Arguments as
+ * qdg_gemv_q8 (x for QDG_DEQUANT, else xq/xs, and xl for QDG_TWOPASS), plus
+ * device idx int32 [1] and a device workspace of at least
+ * qdg_gemv_argmax_workspace_bytes(N) bytes, 8-byte aligned (contents on entry
+ * ignored).  N < 2^31.
+ */
+int qdg_gemv_q8_argmax(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                       const float *x, const int8_t *xq, const int8_t *xl, const float *xs,
+                       float *y, int32_t *idx, void *workspace, size_t workspace_bytes,
+                       qdg_stream stream);
+
 /*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
  * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,

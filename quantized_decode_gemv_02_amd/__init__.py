@@ -11,6 +11,7 @@ functions carry the names of the C entry points in ``include/qdg.h`` without the
 * ``gemv_q8_sk(mode, wq, ws, y, xq, xl, xs, splits, workspace)`` / ``gemv_sk_workspace_bytes(B, N, S)``
 * ``gemv_q8_fused(mode, wq, ws, y, x, splits, workspace)`` (quantize + GEMV + combine, one launch)
 * ``argmax(y, idx, workspace)`` / ``argmax_workspace_bytes(B, N)``
+* ``gemv_q8_argmax(mode, wq, ws, y, idx, workspace, x=, xq=, xl=, xs=)`` / ``gemv_argmax_workspace(N)``
 * ``block_dots(mode, wq, xq, xl, dh, dl)``
 * ``split_bounds(K, splits)`` (host only)
 
@@ -61,6 +62,8 @@ _SIGS = {
     "qdg_gemv_sk_workspace_bytes": ([_I64, _I64, _I], ctypes.c_size_t),
     "qdg_gemv_q8_sk": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_gemv_q8_fused": ([_I, _P, _P, _I64, _I64, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
+    "qdg_gemv_argmax_workspace_bytes": ([_I64], ctypes.c_size_t),
+    "qdg_gemv_q8_argmax": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "qdg_argmax": ([_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
@@ -198,6 +201,34 @@ def sk_combine(partials, y) -> None:
                                                  _ptr(y, _f32(), "y"), _stream()))
 
 
+def gemv_argmax_workspace_bytes(N: int) -> int:
+    return int(_lib.qdg_gemv_argmax_workspace_bytes(N))
+
+
+def gemv_argmax_workspace(N: int):
+    """A device workspace for ``gemv_q8_argmax`` (int64 words)."""
+    return _torch().empty((gemv_argmax_workspace_bytes(N) + 7) // 8, dtype=_torch().int64, device="cuda")
+
+
+def gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, xl=None, xs=None) -> None:
+    """LM-head tail: ``y [1][N]`` logits and ``idx [1]`` int32 first index of their maximum, in two launches."""
+    N, K = wq.shape
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("qdg_gemv_q8_argmax", _lib.qdg_gemv_q8_argmax(
+        mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), _ptr(xq, _i8(), "xq"),
+        _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(y, _f32(), "y"), _ptr(idx, (_torch().int32,), "idx"),
+        _ptr(workspace, None, "workspace"), nbytes, _stream()))
+
+
+def bind_gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, xl=None, xs=None) -> Bound:
+    N, K = wq.shape
+    for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (idx, "idx"), (workspace, "workspace"), (x, "x"), (xq, "xq"),
+                 (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    nbytes = workspace.numel() * workspace.element_size()
+    return Bound("qdg_gemv_q8_argmax", mode, wq, ws, N, K, x, xq, xl, xs, y, idx, workspace, nbytes, _stream())
+
+
 def argmax_workspace_bytes(B: int, N: int) -> int:
     return int(_lib.qdg_argmax_workspace_bytes(B, N))
 
@@ -286,6 +317,14 @@ def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:
     for t, n in ((x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_quantize_act", mode, x, B, K, xq, xl, xs, _stream())
+
+
+def bind_argmax(y, idx, workspace) -> Bound:
+    B, N = (y.shape if y.dim() == 2 else (1, y.shape[0]))
+    for t, n in ((y, "y"), (idx, "idx"), (workspace, "workspace")):
+        _ptr(t, None, n)
+    nbytes = workspace.numel() * workspace.element_size()
+    return Bound("qdg_argmax", y, B, N, idx, workspace, nbytes, _stream())
 
 
 def bind_sk_combine(partials, y) -> Bound:

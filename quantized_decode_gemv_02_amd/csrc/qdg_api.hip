@@ -133,6 +133,32 @@ int qdg_gemv_q8_fused(int mode, const int8_t* wq, const uint16_t* ws, int64_t N,
   return hip_status(qdg::launch_gemv_x(mode, wq, ws, N, K, x, splits, y, workspace, st));
 }
 
+size_t qdg_gemv_argmax_workspace_bytes(int64_t N) {
+  if (N < 1 || N >= ((int64_t)1 << 31)) return 0;
+  return (size_t)qdg::gemv_tiles(N) * sizeof(unsigned long long);
+}
+
+int qdg_gemv_q8_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                       const int8_t* xq, const int8_t* xl, const float* xs, float* y, int32_t* idx,
+                       void* workspace, size_t workspace_bytes, qdg_stream stream) {
+  if (mode < QDG_DEQUANT || mode > QDG_TWOPASS) return QDG_EINVAL;
+  if (!wq || !ws || !y || !idx || !workspace) return QDG_EINVAL;
+  if (mode == QDG_DEQUANT && (!x || xq || xl || xs)) return QDG_EINVAL;
+  if (mode != QDG_DEQUANT && (x || !xq || !xs)) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!shape_ok(N, K) || N >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(y, 4) || !aligned(idx, 4) || !aligned(workspace, 8))
+    return QDG_EALIGN;
+  if (x && !aligned(x, 16)) return QDG_EALIGN;
+  if (xq && !aligned(xq, 16)) return QDG_EALIGN;
+  if (xl && !aligned(xl, 16)) return QDG_EALIGN;
+  if (xs && !aligned(xs, 4)) return QDG_EALIGN;
+  if (workspace_bytes < qdg_gemv_argmax_workspace_bytes(N)) return QDG_EWORKSPACE;
+  return hip_status(qdg::launch_gemv_argmax(mode, wq, ws, N, K, x, xq, xl, xs, y, idx,
+                                            (unsigned long long*)workspace, as_stream(stream)));
+}
+
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
   if (B < 1 || N < 1) return 0;
   return (size_t)B * (size_t)qdg::argmax_groups(N) * sizeof(unsigned long long);

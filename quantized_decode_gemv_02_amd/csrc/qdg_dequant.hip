@@ -60,11 +60,14 @@ __device__ __forceinline__ double half_dot16(int4 w, const void* __restrict__ xv
   return __dadd_rn(__dadd_rn(c[0], c[1]), __dadd_rn(c[2], c[3]));
 }
 
-template <int RPW, int U, bool XF64>
+// AMAX (S == 1): the workgroup also writes the arg-max key of its rows' largest
+// output to keys[blockIdx.x] (as the quantized kernel's epilogue does).
+template <int RPW, int U, bool XF64, bool AMAX = false>
 __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                     const float* __restrict__ x, int64_t N, int64_t K, int S,
                                                     int win, float* __restrict__ out, double* __restrict__ part,
-                                                    unsigned* __restrict__ tickets) {
+                                                    unsigned* __restrict__ tickets,
+                                                    unsigned long long* __restrict__ keys = nullptr) {
   constexpr int LPR = 64 / RPW;
   constexpr int BPS = LPR / 2;
   constexpr int TPP = BPS / 4;
@@ -146,6 +149,22 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   }
   const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL4>(p));
   const double y = __dadd_rn(t, dpp_f64<DPP_ROW_SHL2>(t));
+  if constexpr (AMAX) {
+    __shared__ unsigned long long row_keys[ROWS];
+    if (li == 0) {
+      const float yf = (float)y;
+      if (row_ok) out[o] = yf;
+      row_keys[rr] = row_ok ? amax_key(yf, (unsigned)o) : 0ull;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long best = row_keys[0];
+#pragma unroll
+      for (int i = 1; i < ROWS; ++i) best = row_keys[i] > best ? row_keys[i] : best;
+      keys[blockIdx.x] = best;
+    }
+    return;
+  }
   if (S == 1) {
     if (li == 0 && row_ok) out[o] = (float)y;
     return;
@@ -174,9 +193,9 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool XF64>
+template <bool XF64, bool AMAX = false>
 hipError_t launch_dq(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
-                     float* y, void* workspace, hipStream_t st) {
+                     float* y, void* workspace, hipStream_t st, unsigned long long* keys = nullptr) {
   constexpr int RPW = 4, U = 4;
   constexpr int rows_per_wg = (WG / 64) * RPW;
   constexpr int bpb = 2 * (16 * (XF64 ? 8 : 4) + 16) + 2 * rows_per_wg;  // LDS bytes per block of the window
@@ -194,8 +213,8 @@ hipError_t launch_dq(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
   unsigned* tickets = (unsigned*)workspace;
   double* part = splits == 1 ? nullptr : (double*)((char*)workspace + sk_partials_offset(N));
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
-  hipLaunchKernelGGL((k_gemv_dequant<RPW, U, XF64>), grid, block, lds, st, wq, ws, x, N, K, splits, win, y, part,
-                     tickets);
+  hipLaunchKernelGGL((k_gemv_dequant<RPW, U, XF64, AMAX>), grid, block, lds, st, wq, ws, x, N, K, splits, win, y,
+                     part, tickets, keys);
   return hipGetLastError();
 }
 
@@ -214,6 +233,12 @@ bool dq_x64() {
 hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                float* out, hipStream_t st) {
   return launch_gemv_dequant_sk(wq, ws, N, K, x, 1, out, nullptr, st);
+}
+
+hipError_t launch_gemv_dequant_argmax(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                                      float* y, unsigned long long* keys, hipStream_t st) {
+  if (dq_x64()) return launch_dq<true, true>(wq, ws, N, K, x, 1, y, nullptr, st, keys);
+  return launch_dq<false, true>(wq, ws, N, K, x, 1, y, nullptr, st, keys);
 }
 
 hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,

@@ -108,6 +108,19 @@ __device__ __forceinline__ float half_bits_to_float(unsigned short h) {
   return __half2float(__ushort_as_half(h));
 }
 
+// Arg-max keys (megakernel page, amax_key): the float's bits mapped to an
+// unsigned integer that orders as the floats do, above the complement of the
+// index, so the largest key is the largest value and, among equal values, the
+// smallest index.  -0 is folded onto +0 first so that the two compare equal as
+// IEEE floats do; the maximum of keys is order-free, which makes the result
+// independent of how the values are split over lanes and workgroups.
+__device__ __forceinline__ unsigned long long amax_key(float v, unsigned idx) {
+  unsigned u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
 // One quantized step's factors (lane kernel library page, lk_q8_term):
 // Int8Act a = fl(sigma*s), b = D; TwoPass a = sigma, b = fma(s, D, fl(fl(s/128)*E)).
 template <int MODE>
@@ -179,6 +192,8 @@ hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, 
 hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                   int splits, float* y, void* workspace, hipStream_t st);
 int64_t sk_partials_offset(int64_t N);
+hipError_t launch_gemv_dequant_argmax(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                                      float* y, unsigned long long* keys, hipStream_t st);
 hipError_t launch_gemv_mfma(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                             const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, int splits,
                             float* out, hipStream_t st);
@@ -192,6 +207,11 @@ hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t
                          int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st);
+hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st);
+int64_t gemv_tiles(int64_t N);
+hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                              const int8_t* xq, const int8_t* xl, const float* xs, float* y, int32_t* idx,
+                              unsigned long long* keys, hipStream_t st);
 hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, unsigned long long* ws,
                          hipStream_t st);
 }  // namespace qdg

@@ -52,13 +52,17 @@ constexpr int window_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2
 //   last workgroup of a row tile to finish (an atomic ticket per tile) sums the
 //   tile's S partials in ascending order into y and resets the ticket -- which
 //   chunk finishes last changes nothing in the result.
-template <int MODE, int RPW, int U, bool FUSED, bool QX>
+// AMAX (S == 1 only): the workgroup also writes the arg-max key (amax_key) of
+// its rows' largest output to keys[tile]; a final pass over the tiles' keys gives
+// the first index of the row's maximum (the megakernel page's per-block arg-max
+// partials, in the GEMV's epilogue instead of a pass over the logits).
+template <int MODE, int RPW, int U, bool FUSED, bool QX, bool AMAX = false>
 __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                  const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
                                                  const float* __restrict__ xs, const float* __restrict__ x,
                                                  int64_t N, int64_t K, int S, int win, int ntiles, int chunk_major,
                                                  float* __restrict__ out, unsigned* __restrict__ tickets,
-                                                 float* __restrict__ y) {
+                                                 float* __restrict__ y, unsigned long long* __restrict__ keys = nullptr) {
   constexpr int LPR = 64 / RPW;  // lanes per row
   constexpr int BPS = LPR / 2;   // blocks per step of a row
   constexpr int TPP = BPS / 4;   // steps of one partial per step (1 or 2)
@@ -171,6 +175,22 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   // (P0 + P2) + (P1 + P3): partial q sits in lane 2q of the row.
   const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
   const float yv = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+  if constexpr (AMAX) {
+    // one key a row (0, below every real key, for rows past N), the workgroup's maximum to keys[tile]
+    __shared__ unsigned long long row_keys[ROWS];
+    if (li == 0) {
+      if (row_ok) out[o] = yv;
+      row_keys[rr] = row_ok ? amax_key(yv, (unsigned)o) : 0ull;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long best = row_keys[0];
+#pragma unroll
+      for (int i = 1; i < ROWS; ++i) best = row_keys[i] > best ? row_keys[i] : best;
+      keys[tile] = best;
+    }
+    return;
+  }
   if constexpr (!FUSED) {
     if (li == 0 && row_ok) out[(int64_t)s_idx * N + o] = yv;
   } else {
@@ -310,6 +330,32 @@ hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_
   float* part = (float*)((char*)workspace + sk_partials_offset(N));
   if (mode == 1) return launch_mode<1, true, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, part, tickets, y, st);
   return launch_mode<2, true, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, part, tickets, y, st);
+}
+
+int64_t gemv_tiles(int64_t N) { return (N + 15) / 16; }
+
+hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                              const int8_t* xq, const int8_t* xl, const float* xs, float* y, int32_t* idx,
+                              unsigned long long* keys, hipStream_t st) {
+  hipError_t e;
+  if (mode == 0) {
+    e = launch_gemv_dequant_argmax(wq, ws, N, K, x, y, keys, st);
+  } else {
+    // the default lane layout (RPW 4, U 4): 16-row tiles, one key each
+    constexpr int bpb1 = window_bytes_per_block<1, 4>(), bpb2 = window_bytes_per_block<2, 4>();
+    const int win = window_blocks(K, 1, mode == 1 ? bpb1 : bpb2);
+    const int ntiles = (int)gemv_tiles(N);
+    const dim3 grid((unsigned)ntiles), block(WG);
+    if (mode == 1)
+      hipLaunchKernelGGL((k_gemv_dot4<1, 4, 4, false, false, true>), grid, block, (size_t)win * bpb1, st, wq, ws, xq,
+                         xl, xs, nullptr, N, K, 1, win, ntiles, 0, y, nullptr, nullptr, keys);
+    else
+      hipLaunchKernelGGL((k_gemv_dot4<2, 4, 4, false, false, true>), grid, block, (size_t)win * bpb2, st, wq, ws, xq,
+                         xl, xs, nullptr, N, K, 1, win, ntiles, 0, y, nullptr, nullptr, keys);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  return launch_argmax_final(keys, 1, (int)gemv_tiles(N), idx, st);
 }
 
 hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,

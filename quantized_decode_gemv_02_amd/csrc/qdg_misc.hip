@@ -16,19 +16,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
   y[i] = a;
 }
 
-// Arg-max keys (megakernel page, amax_key): the float's bits mapped to an
-// unsigned integer that orders as the floats do, above the complement of the
-// index, so the largest key is the largest value and, among equal values, the
-// smallest index.  -0 is folded onto +0 first so that the two compare equal as
-// IEEE floats do; the maximum of keys is order-free, which makes the result
-// independent of how the values are split over lanes and workgroups.
-__device__ __forceinline__ unsigned long long amax_key(float v, unsigned idx) {
-  unsigned u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) == 0u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - idx);
-}
-
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -70,16 +57,36 @@ __global__ __launch_bounds__(AM_THREADS) void k_argmax_part(const float* __restr
 }
 
 // Stage 2: one workgroup per row reduces the row's G keys and decodes the index.
-__global__ __launch_bounds__(AM_THREADS) void k_argmax_final(const unsigned long long* __restrict__ keys, int G,
+// The keys can number in the thousands (one per GEMV tile when the LM-head
+// GEMV's epilogue writes them), so each thread issues AF_UNROLL loads before it
+// compares any: a pass costs one memory round trip, not one per key.
+constexpr int AF_THREADS = 1024;
+constexpr int AF_UNROLL = 8;
+
+__global__ __launch_bounds__(AF_THREADS) void k_argmax_final(const unsigned long long* __restrict__ keys, int G,
                                                             int32_t* __restrict__ idx) {
-  const int t = blockIdx.x;
+  const unsigned long long* row = keys + (int64_t)blockIdx.x * G;
   unsigned long long best = 0ull;
-  for (int i = threadIdx.x; i < G; i += AM_THREADS) {
-    const unsigned long long k = keys[(int64_t)t * G + i];
-    best = k > best ? k : best;
+  for (int base = threadIdx.x; base < G; base += AF_THREADS * AF_UNROLL) {
+    unsigned long long k[AF_UNROLL];
+#pragma unroll
+    for (int u = 0; u < AF_UNROLL; ++u) {
+      const int i = base + u * AF_THREADS;
+      k[u] = i < G ? row[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < AF_UNROLL; ++u) best = k[u] > best ? k[u] : best;
   }
-  best = block_max_u64(best);
-  if (threadIdx.x == 0) idx[t] = (int32_t)(0xffffffffu - (unsigned)(best & 0xffffffffull));
+  __shared__ unsigned long long red[AF_THREADS / 64];
+  best = wave_max_u64(best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = red[0];
+#pragma unroll
+    for (int w = 1; w < AF_THREADS / 64; ++w) m = red[w] > m ? red[w] : m;
+    idx[blockIdx.x] = (int32_t)(0xffffffffu - (unsigned)(m & 0xffffffffull));
+  }
 }
 
 // Test hook: the exact per-block int32 dots through the GEMV's own block dot.
@@ -158,7 +165,12 @@ hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, uns
   hipLaunchKernelGGL(k_argmax_part, dim3((unsigned)G, (unsigned)B), dim3(AM_THREADS), 0, st, y, N, per, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AM_THREADS), 0, st, ws, G, idx);
+  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, ws, G, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, keys, G, idx);
   return hipGetLastError();
 }
 

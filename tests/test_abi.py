@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -132,6 +132,26 @@ def test_fused_validation():
     assert call(wq=A + 8) == EALIGN
     assert call(wsp=A + 8) == EALIGN
     assert call(nbytes=need - 4) == EWORKSPACE
+
+
+def test_gemv_argmax_validation():
+    f = lib.qdg_gemv_q8_argmax
+    need = q.gemv_argmax_workspace_bytes(151936)
+    assert need == 8 * (151936 // 16)
+    assert q.gemv_argmax_workspace_bytes(0) == 0
+
+    def call(mode=1, wq=A, ws=A, N=64, K=512, x=None, xq=A, xl=None, xs=A, y=A, idx=A, wsp=A, nbytes=8 * 4):
+        return f(mode, P(wq), P(ws), N, K, P(x), P(xq), P(xl), P(xs), P(y), P(idx), P(wsp), nbytes, None)
+
+    assert call(mode=3) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(wsp=None) == EINVAL
+    assert call(mode=0) == EINVAL                     # Dequant reads x, not words
+    assert call(mode=2) == EINVAL                     # TwoPass needs xl
+    assert call(K=500) == ESHAPE
+    assert call(idx=A + 2) == EALIGN
+    assert call(wsp=A + 4) == EALIGN
+    assert call(nbytes=8 * 3) == EWORKSPACE
 
 
 def test_stream_read_validation():

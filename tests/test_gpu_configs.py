@@ -105,6 +105,22 @@ def test_lm_head_argmax_planted_ties(lm_head):
             assert y[0, a] == y[0, b]
             assert idx == a, (idx, a, b)
             assert idx == int(oracle.argmax(y)[0])      # the index is exact on the GPU's own logits
+            # the two-launch tail (keys from the GEMV's epilogue): same logits, same index
+            y2 = torch.empty((1, N), dtype=torch.float32, device=DEV)
+            i2 = torch.empty(1, dtype=torch.int32, device=DEV)
+            wsp = q.gemv_argmax_workspace(N)
+            xd = torch.from_numpy(x).to(DEV)
+            if mode == 0:
+                q.gemv_q8_argmax(0, w.wq, w.ws, y2, i2, wsp, x=xd)
+            else:
+                xq = torch.empty((1, x.shape[1]), dtype=torch.int8, device=DEV)
+                xl = torch.empty_like(xq) if mode == 2 else None
+                xs = torch.empty((1, x.shape[1] // 32), dtype=torch.float32, device=DEV)
+                q.quantize_act(mode, xd, xq, xl, xs)
+                q.gemv_q8_argmax(mode, w.wq, w.ws, y2, i2, wsp, xq=xq, xl=xl, xs=xs)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(y2.cpu().numpy(), y)
+            assert int(i2.cpu().numpy()[0]) == a
             if (a, b) == (a0, b0):
                 check(mode, y, wq, ws, x)
                 assert int(oracle.argmax(oracle_y(mode, wq, ws, x))[0]) == a

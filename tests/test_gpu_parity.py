@@ -384,3 +384,34 @@ def test_fused_dequant_split_k(N, K, S):
         assert (got == want32).mean() > 0.99
     tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
     assert not tickets.any()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("N,K", [(4097, 512), (33, 1600), (5000, 544), (16, 96)])
+def test_gemv_argmax_epilogue(mode, N, K):
+    """qdg_gemv_q8_argmax: the logits equal qdg_gemv_q8's bit for bit, and the index
+    is the first of the maxima -- planted exact ties inside one 16-row tile, across
+    a tile boundary, and at (0, N-1), each with the later row in the later tile."""
+    announce(f"gemv_q8_argmax mode={mode} N={N} K={K}")
+    wq, ws, x = _quant_case(N, K, 1, 19 * N + K + mode)
+    wsp = q.gemv_argmax_workspace(N)
+    for a, b in [(2, 5), (15, 16), (0, N - 1), (N // 2, N - 2)]:
+        if not 0 <= a < b < N:
+            continue
+        w2, s2, x2 = wq.copy(), ws.copy(), x.copy()
+        workloads.plant_tie(w2, s2, x2[0], a, b)
+        wqd, wsd = dev(w2), dev(s2)
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        idx = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        y_ref = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        if mode == 0:
+            xd = dev(x2)
+            q.gemv_q8_argmax(0, wqd, wsd, y, idx, wsp, x=xd)
+            q.gemv_q8(0, wqd, wsd, y_ref, x=xd)
+        else:
+            xq, xl, xs = quantize_gpu(mode, x2)
+            q.gemv_q8_argmax(mode, wqd, wsd, y, idx, wsp, xq=xq, xl=xl, xs=xs)
+            q.gemv_q8(mode, wqd, wsd, y_ref, xq=xq, xl=xl, xs=xs)
+        got = host(y)
+        np.testing.assert_array_equal(got, host(y_ref))
+        assert int(host(idx)[0]) == int(oracle.argmax(got)[0]) == a
