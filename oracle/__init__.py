@@ -14,6 +14,8 @@ Functions (each mirrors one step of the method; citations in ``qdg_oracle.c``):
 * ``combine(part)`` -> ``y``
 * ``argmax(y)`` -> first index of the maximum, per row
 * ``reference_f64(mode, ...)`` -> ``(Y, tnorm)`` binary64 anchor of the tolerance
+* ``rmsnorm(x, r=None, w=None, eps)`` -> ``(s, y)``: residual sum and RMSNorm
+* ``swiglu(g, u)`` -> ``h = silu(g) * u``
 """
 from __future__ import annotations
 
@@ -47,10 +49,13 @@ def _load():
         lib.orc_combine.argtypes = [P, I, I64, I64, P]
         lib.orc_argmax.argtypes = [P, I64, I64, P]
         lib.orc_reference_f64.argtypes = [I, P, P, I64, I64, P, P, P, P, I64, P, P, I]
+        lib.orc_rmsnorm.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P]
+        lib.orc_swiglu.argtypes = [P, P, I64, P]
         lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
         lib.orc_half_to_float.restype = ctypes.c_float
         for name in ("orc_quantize", "orc_block_dots", "orc_gemv", "orc_split_bounds",
-                     "orc_gemv_split", "orc_combine", "orc_argmax", "orc_reference_f64"):
+                     "orc_gemv_split", "orc_combine", "orc_argmax", "orc_reference_f64",
+                     "orc_rmsnorm", "orc_swiglu"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -165,3 +170,29 @@ def within_tolerance(y: np.ndarray, Y: np.ndarray, tnorm: np.ndarray, rel: float
     """The f32 criterion: ``|y - Y| <= rel * max(|Y|, ||t||_2)`` elementwise."""
     y = np.asarray(y, np.float64)
     return np.abs(y - Y) <= rel * np.maximum(np.abs(Y), tnorm)
+
+
+def rmsnorm(x: np.ndarray, r: np.ndarray | None = None, w: np.ndarray | None = None, eps: float = 1e-6):
+    """``(s, y)`` for rows ``x[B][K]``: ``s = fl32(x + r)`` (``None`` without ``r``) and
+    ``y = fl32((s / sqrt(mean(s^2) + eps)) * w)`` evaluated in binary64."""
+    x = _c(np.atleast_2d(x), np.float32)
+    B, K = x.shape
+    r = None if r is None else _c(np.atleast_2d(r), np.float32)
+    w = None if w is None else _c(w, np.float32)
+    if r is not None and r.shape != x.shape or w is not None and w.shape != (K,):
+        raise ValueError("rmsnorm: shapes of x, r and w disagree")
+    s = np.empty_like(x) if r is not None else None
+    y = np.empty_like(x)
+    _check(_load().orc_rmsnorm(_p(x), _p(r), _p(w), ctypes.c_float(eps), B, K, _p(s), _p(y)), "rmsnorm")
+    return s, y
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """``h = fl32((g / (1 + exp(-g))) * u)`` evaluated in binary64, elementwise."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    if g.shape != u.shape:
+        raise ValueError("swiglu: g and u differ in shape")
+    h = np.empty_like(g)
+    _check(_load().orc_swiglu(_p(g), _p(u), g.size, _p(h)), "swiglu")
+    return h

@@ -20,6 +20,8 @@
  *        (gk_gemv_hl_sk, gk_sk_combine).
  *   [P3] "model-as-a-kernel mak_cuda/megakernel.cu" -- amax_key, ph_argmax_part,
  *        ph_argmax_fin (first index among equal maxima).
+ *   The producers of the quantized activation: [P1] RMSNORM (lk_rmsnorm_row),
+ *   lk_act, GLU; [P2] gk_add_rmsnorm_q8f, gk_silu_had_q8.
  *
  * Modes: 0 Dequant (f32 activation, f64 sums), 1 Int8Act, 2 TwoPassInt8 ([P1]
  * mode()).
@@ -349,6 +351,64 @@ int orc_reference_f64(int mode, const int8_t *wq, const uint16_t *ws, int64_t N,
             Y[t * N + o] = acc;
             tnorm[t * N + o] = sqrt(sq);
         }
+    }
+    return 0;
+}
+
+/*
+ * rmsnorm -- [P1] RMSNORM (the doc of lk_rmsnorm and lk_rmsnorm_row: per row,
+ * v = x (+ r), y = v / sqrt(mean(v^2) + eps) * w, the sum v written out as the
+ * next residual stream when asked); [P2] gk_add_rmsnorm_q8f (the residual add
+ * folded into the norm that follows it, its result stored back).
+ *
+ * Readings: the residual sum is one binary32 addition, v = fl32(x + r), and is
+ * the value stored to s.  The norm is then evaluated in binary64 from those
+ * binary32 values -- the squares are exact there, the sum runs in ascending
+ * index order, then mean + eps, sqrt, (v / den) * w in that order -- and y is
+ * rounded once to binary32.  w NULL means no weight (y = v / den).  K need not
+ * be a multiple of 32 here.
+ */
+int orc_rmsnorm(const float *x, const float *r, const float *w, float eps, int64_t B, int64_t K,
+                float *s, float *y)
+{
+    if (K < 1 || B < 0) return -1;
+    for (int64_t t = 0; t < B; ++t) {
+        const float *xr = x + t * K;
+        double sum = 0.0;
+        for (int64_t i = 0; i < K; ++i) {
+            float v = xr[i];
+            if (r) v = v + r[t * K + i];
+            if (s) s[t * K + i] = v;
+            sum += (double)v * (double)v;
+        }
+        const double den = sqrt(sum / (double)K + (double)eps);
+        for (int64_t i = 0; i < K; ++i) {
+            float v = xr[i];
+            if (r) v = v + r[t * K + i];
+            double o = (double)v / den;
+            if (w) o = o * (double)w[i];
+            y[t * K + i] = (float)o;
+        }
+    }
+    return 0;
+}
+
+/*
+ * swiglu -- [P1] lk_act (silu is g / (1 + e^-g)) and GLU (the gated product
+ * act(g) * u that feeds the next quantized GEMV); [P2] gk_silu_had_q8 (silu(g)
+ * times u, then the 32-value block quantizer).
+ *
+ * Reading: h = (g / (1 + exp(-g))) * u in that order, evaluated in binary64 from
+ * the binary32 inputs and rounded once to binary32.  exp(-g) overflows to +inf
+ * for g below about -709, where g / inf is a signed zero, which is the limit.
+ */
+int orc_swiglu(const float *g, const float *u, int64_t n, float *h)
+{
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double gv = (double)g[i];
+        const double silu = gv / (1.0 + exp(-gv));
+        h[i] = (float)(silu * (double)u[i]);
     }
     return 0;
 }
