@@ -211,6 +211,49 @@ int qdg_gemv_q8_argmax(int mode, const int8_t *wq, const uint16_t *ws, int64_t N
                        qdg_stream stream);
 
 /*
+ * The residual add and RMSNorm, then the activation quantizer, in one launch:
+ * the producer of the words a quantized GEMV reads (lane kernel library page,
+ * RMSNORM: v = x + r, y = v / sqrt(mean(v^2) + eps) * w, the sum written out
+ * as the next residual stream; QWEN38 page, gk_add_rmsnorm_q8f).  Per row t:
+ *   v = x[t] + r[t]   one binary32 addition per value (v = x[t] when r is NULL);
+ *                     s[t] = v when s is given (s needs r);
+ *   y = v / sqrt(mean(v^2) + eps) * w   evaluated in binary64 from the binary32
+ *                     v and w, rounded once to binary32 (no w when w is NULL);
+ *                     written to y when y is given;
+ *   xq, xl, xs        y quantized as qdg_quantize_act quantizes it.
+ * The binary32 y is within one unit in the last place of the exactly rounded
+ * value, and is the same on every run.  QDG_DEQUANT writes only y (required;
+ * xq, xl and xs must be NULL), for the Dequant GEMV that reads f32 activations.
+ * QDG_INT8ACT needs xq and xs (xl NULL), QDG_TWOPASS all three.
+ * Device pointers: x, r, s, y [B][K] (16-byte aligned); w [K] (16-byte
+ * aligned); xq, xl [B][K] (16-byte aligned); xs [B][K/32].  s and y may be x
+ * itself (an in-place residual update); no other buffers may overlap.
+ * 1 <= B < 2^31, K a multiple of 32 with 32 <= K <= qdg_rmsnorm_max_k();
+ * eps >= 0 and finite.  A row of zeros with eps == 0 gives NaN (0/0) as the
+ * formula does; its words are then unspecified.
+ */
+int qdg_rmsnorm_quantize(int mode, const float *x, const float *r, float *s, const float *w,
+                         float eps, int64_t B, int64_t K, float *y, int8_t *xq, int8_t *xl,
+                         float *xs, qdg_stream stream);
+
+/* The largest K qdg_rmsnorm_quantize accepts (one workgroup holds a row). */
+int64_t qdg_rmsnorm_max_k(void);
+
+/*
+ * SwiGLU, then the activation quantizer, in one launch (lane kernel library
+ * page, lk_act and GLU: silu(g) = g / (1 + e^-g), times u; QWEN38 page,
+ * gk_silu_had_q8): h = (g / (1 + exp(-g))) * u per value, evaluated in binary64
+ * from the binary32 g and u and rounded once to binary32 (within one unit in
+ * the last place of the exactly rounded value); written to h when h is given;
+ * then quantized as qdg_quantize_act quantizes it.  QDG_DEQUANT writes only h
+ * (required; xq, xl, xs NULL).  Device pointers: g, u, h [B][K] (16-byte
+ * aligned; h may be g or u); xq, xl [B][K] (16-byte aligned), xs [B][K/32].
+ * B >= 1, K >= 32 and a multiple of 32, B*K < 2^62.
+ */
+int qdg_swiglu_quantize(int mode, const float *g, const float *u, int64_t B, int64_t K,
+                        float *h, int8_t *xq, int8_t *xl, float *xs, qdg_stream stream);
+
+/*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
  * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,
  * under QDG_TWOPASS, dl[t][o][g] with xl (dl must be NULL for QDG_INT8ACT).

@@ -69,6 +69,9 @@ _SIGS = {
     "qdg_block_dots": ([_I, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P], _I),
     "qdg_split_bounds": ([_I64, _I, _P], _I),
     "qdg_stream_read": ([_P, _I64, _P, _P], _I),
+    "qdg_rmsnorm_quantize": ([_I, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "qdg_rmsnorm_max_k": ([], _I64),
+    "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -147,6 +150,51 @@ def quantize_act(mode: int, x, xq, xl, xs) -> None:
     _check("qdg_quantize_act", _lib.qdg_quantize_act(
         mode, _ptr(x, _f32(), "x"), B, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
         _stream()))
+
+
+def _rows(t):
+    return t.shape if t.dim() == 2 else (1, t.shape[0])
+
+
+def _rmsnorm_args(mode, x, w, r, s, y, xq, xl, xs, eps):
+    B, K = _rows(x)
+    return (mode, _ptr(x, _f32(), "x"), _ptr(r, _f32(), "r"), _ptr(s, _f32(), "s"), _ptr(w, _f32(), "w"),
+            float(eps), B, K, _ptr(y, _f32(), "y"), _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"),
+            _ptr(xs, _f32(), "xs"), _stream())
+
+
+def rmsnorm_quantize(mode: int, x, w=None, r=None, s=None, y=None, xq=None, xl=None, xs=None,
+                     eps: float = 1e-6) -> None:
+    """Residual add + RMSNorm + the activation quantizer in one launch: ``s = x + r``
+    (optional), ``y = (x + r) / sqrt(mean((x + r)^2) + eps) * w`` (optional output
+    under the quantized modes, the only output under Dequant), then ``xq/xl/xs``."""
+    _check("qdg_rmsnorm_quantize", _lib.qdg_rmsnorm_quantize(*_rmsnorm_args(mode, x, w, r, s, y, xq, xl, xs, eps)))
+
+
+def bind_rmsnorm_quantize(mode: int, x, w=None, r=None, s=None, y=None, xq=None, xl=None, xs=None,
+                          eps: float = 1e-6) -> Bound:
+    return Bound("qdg_rmsnorm_quantize", *_rmsnorm_args(mode, x, w, r, s, y, xq, xl, xs, eps))
+
+
+def rmsnorm_max_k() -> int:
+    return int(_lib.qdg_rmsnorm_max_k())
+
+
+def _swiglu_args(mode, g, u, h, xq, xl, xs):
+    B, K = _rows(g)
+    if tuple(u.shape) != tuple(g.shape):
+        raise ValueError("swiglu_quantize: g and u differ in shape")
+    return (mode, _ptr(g, _f32(), "g"), _ptr(u, _f32(), "u"), B, K, _ptr(h, _f32(), "h"),
+            _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _stream())
+
+
+def swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> None:
+    """``h = silu(g) * u`` (optional output under the quantized modes) and its quantized words."""
+    _check("qdg_swiglu_quantize", _lib.qdg_swiglu_quantize(*_swiglu_args(mode, g, u, h, xq, xl, xs)))
+
+
+def bind_swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> Bound:
+    return Bound("qdg_swiglu_quantize", *_swiglu_args(mode, g, u, h, xq, xl, xs))
 
 
 def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: int = 1) -> None:

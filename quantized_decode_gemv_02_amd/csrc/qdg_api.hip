@@ -174,6 +174,48 @@ int qdg_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, void* workspa
       qdg::launch_argmax(y, B, N, idx, (unsigned long long*)workspace, as_stream(stream)));
 }
 
+namespace {
+// The output arguments of a producer: QDG_DEQUANT writes only the f32 vector; the
+// quantized modes need their words (xl exactly under QDG_TWOPASS).
+int producer_outputs(int mode, const float* f, const int8_t* xq, const int8_t* xl, const float* xs) {
+  if (mode == QDG_DEQUANT) return (f && !xq && !xl && !xs) ? QDG_OK : QDG_EINVAL;
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!xq || !xs) return QDG_EINVAL;
+  if ((mode == QDG_TWOPASS) != (xl != nullptr)) return QDG_EINVAL;
+  return QDG_OK;
+}
+bool words_aligned(const float* f, const int8_t* xq, const int8_t* xl, const float* xs) {
+  return (!f || aligned(f, 16)) && (!xq || aligned(xq, 16)) && (!xl || aligned(xl, 16)) && (!xs || aligned(xs, 4));
+}
+}  // namespace
+
+int64_t qdg_rmsnorm_max_k(void) { return qdg::rmsnorm_max_k(); }
+
+int qdg_rmsnorm_quantize(int mode, const float* x, const float* r, float* s, const float* w, float eps, int64_t B,
+                         int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, qdg_stream stream) {
+  if (!x) return QDG_EINVAL;
+  const int st = producer_outputs(mode, y, xq, xl, xs);
+  if (st != QDG_OK) return st;
+  if (s && !r) return QDG_EINVAL;
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return QDG_EINVAL;
+  if (B < 1 || B >= ((int64_t)1 << 31) || K < qdg::QK || K % qdg::QK || K > qdg::rmsnorm_max_k()) return QDG_ESHAPE;
+  if (!aligned(x, 16) || (r && !aligned(r, 16)) || (s && !aligned(s, 16)) || (w && !aligned(w, 16)) ||
+      !words_aligned(y, xq, xl, xs))
+    return QDG_EALIGN;
+  return hip_status(qdg::launch_rmsnorm_quant(mode, x, r, s, w, eps, B, K, y, xq, xl, xs, as_stream(stream)));
+}
+
+int qdg_swiglu_quantize(int mode, const float* g, const float* u, int64_t B, int64_t K, float* h, int8_t* xq,
+                        int8_t* xl, float* xs, qdg_stream stream) {
+  if (!g || !u) return QDG_EINVAL;
+  const int st = producer_outputs(mode, h, xq, xl, xs);
+  if (st != QDG_OK) return st;
+  if (!shape_ok(B, K)) return QDG_ESHAPE;
+  if ((B * K / qdg::QK) * 8 / 256 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(g, 16) || !aligned(u, 16) || !words_aligned(h, xq, xl, xs)) return QDG_EALIGN;
+  return hip_status(qdg::launch_swiglu_quant(mode, g, u, B * K / qdg::QK, h, xq, xl, xs, as_stream(stream)));
+}
+
 int qdg_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
                    int64_t B, int32_t* dh, int32_t* dl, qdg_stream stream) {
   if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;

@@ -207,6 +207,11 @@ hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t
                          int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st);
+int64_t rmsnorm_max_k();
+hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
+                                int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
+hipError_t launch_swiglu_quant(int mode, const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq,
+                               int8_t* xl, float* xs, hipStream_t st);
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st);
 int64_t gemv_tiles(int64_t N);
 hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -152,6 +152,57 @@ def test_gemv_argmax_validation():
     assert call(idx=A + 2) == EALIGN
     assert call(wsp=A + 4) == EALIGN
     assert call(nbytes=8 * 3) == EWORKSPACE
+
+
+def test_rmsnorm_quantize_validation():
+    f = lib.qdg_rmsnorm_quantize
+    kmax = q.rmsnorm_max_k()
+    assert kmax >= 16384 and kmax % 32 == 0
+
+    def call(mode=1, x=A, r=A, s=A, w=A, eps=1e-6, B=1, K=512, y=None, xq=A, xl=None, xs=A):
+        return f(mode, P(x), P(r), P(s), P(w), eps, B, K, P(y), P(xq), P(xl), P(xs), None)
+
+    assert call(mode=3) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(r=None) == EINVAL                         # s needs r
+    assert call(mode=0) == EINVAL                         # Dequant writes y only
+    assert call(mode=0, y=A, xq=None, xs=None, xl=A) == EINVAL
+    assert call(mode=1, xl=A) == EINVAL
+    assert call(mode=2) == EINVAL                         # TwoPass needs xl
+    assert call(xs=None) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+    assert call(eps=float("nan")) == EINVAL
+    assert call(eps=float("inf")) == EINVAL
+    assert call(K=500) == ESHAPE
+    assert call(K=0) == ESHAPE
+    assert call(K=kmax + 32) == ESHAPE
+    assert call(B=0) == ESHAPE
+    assert call(x=A + 4) == EALIGN
+    assert call(w=A + 8) == EALIGN
+    assert call(s=A + 4) == EALIGN
+    assert call(xq=A + 4) == EALIGN
+    assert call(xs=A + 2) == EALIGN
+    assert call(mode=0, y=A + 4, xq=None, xs=None) == EALIGN
+
+
+def test_swiglu_quantize_validation():
+    f = lib.qdg_swiglu_quantize
+
+    def call(mode=1, g=A, u=A, B=1, K=512, h=None, xq=A, xl=None, xs=A):
+        return f(mode, P(g), P(u), B, K, P(h), P(xq), P(xl), P(xs), None)
+
+    assert call(mode=-1) == EINVAL
+    assert call(g=None) == EINVAL
+    assert call(u=None) == EINVAL
+    assert call(mode=0) == EINVAL                         # Dequant writes h only
+    assert call(mode=2) == EINVAL
+    assert call(mode=1, xl=A) == EINVAL
+    assert call(K=48) == ESHAPE
+    assert call(B=0) == ESHAPE
+    assert call(g=A + 4) == EALIGN
+    assert call(u=A + 8) == EALIGN
+    assert call(h=A + 4) == EALIGN
+    assert call(mode=2, xl=A + 4) == EALIGN
 
 
 def test_stream_read_validation():

@@ -129,3 +129,19 @@ def plant_tie(wq: np.ndarray, ws: np.ndarray, x: np.ndarray, a: int, b: int) -> 
 
 def random_logits(N: int, seed: int) -> np.ndarray:
     return _rng(seed).standard_normal(N, dtype=np.float32)
+
+
+def norm_weight(K: int, seed: int) -> np.ndarray:
+    """An RMSNorm weight ``[K]``: 1 + 0.25 * N(0, 1), so a few entries are small or negative."""
+    return (1.0 + 0.25 * _rng(seed).standard_normal(K)).astype(np.float32)
+
+
+def glu_inputs(B: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Gate and up projections ``[B][K]`` of one activation: the gate N(0, 2^2) with 1%
+    of its entries 8x larger (silu's linear and vanishing tails), the up N(0, 1)."""
+    rng = _rng(seed)
+    g = (2.0 * rng.standard_normal((B, K))).astype(np.float32)
+    tail = rng.random((B, K)) < 0.01
+    g[tail] *= np.float32(8.0)
+    u = rng.standard_normal((B, K)).astype(np.float32)
+    return g, u
