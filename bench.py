@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--path", choices=("single", "fused", "staged"), default="staged")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the timing of the fused producers (RMSNorm / SwiGLU + quantizer)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
@@ -261,7 +263,7 @@ def main() -> int:
         t = json.load(open(tpath))
         dom_grid = 256 * -(-shapes[dom_key[1]].N // 16) * chosen[dom_key]
         flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[args.path]
-        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {flags}>"
+        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {flags}, false>"
         if (t.get("kernel_source_sha") == profiling.kernel_source_sha() and t.get("grid") == dom_grid
                 and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
@@ -337,6 +339,34 @@ def main() -> int:
                 if sname in ceiling:
                     rec["pct_of_read_ceiling"] = round(100 * rec["gemv_GBs"] / ceiling[sname]["GBs"], 1)
 
+    # The producers of the activation words, beside the step: the residual add + RMSNorm and
+    # SwiGLU, each fused with the quantizer, against the same work in two launches (the f32
+    # result, then qdg_quantize_act).  Inputs of the projections' shapes: the norm over the
+    # hidden size (the o-proj's N), SwiGLU over the down-proj's K.
+    producers = {}
+    if not args.no_producers:
+        hid, inter = shapes[0].N, shapes[-1].K
+        xr = torch.from_numpy(workloads.batch_activation(1, hid, 11, True, 12)).to(dev)
+        rr = torch.from_numpy(workloads.batch_activation(1, hid, 13)).to(dev)
+        wn = torch.from_numpy(workloads.norm_weight(hid, 14)).to(dev)
+        gg, uu = (torch.from_numpy(a).to(dev) for a in workloads.glu_inputs(1, inter, 15))
+        for mode in modes:
+            for name, K_, fused, f32_only, f32 in (
+                    ("rmsnorm", hid,
+                     lambda xq, xl, xs: q.bind_rmsnorm_quantize(mode, xr, wn, rr, None, None, xq, xl, xs),
+                     lambda y: q.bind_rmsnorm_quantize(0, xr, wn, rr, None, y), torch.empty_like(xr)),
+                    ("swiglu", inter,
+                     lambda xq, xl, xs: q.bind_swiglu_quantize(mode, gg, uu, None, xq, xl, xs),
+                     lambda y: q.bind_swiglu_quantize(0, gg, uu, y), torch.empty_like(gg))):
+                xq_ = torch.empty((1, K_), dtype=torch.int8, device=dev)
+                xl_ = torch.empty_like(xq_) if mode == 2 else None
+                xs_ = torch.empty((1, K_ // 32), dtype=torch.float32, device=dev)
+                one = fused(xq_, xl_, xs_)
+                a, b = f32_only(f32), q.bind_quantize_act(mode, f32, xq_, xl_, xs_)
+                producers[f"{name}_{names[mode]}_K{K_}"] = {
+                    "fused_us": round(mean_launch_us([one], 200), 2),
+                    "two_launches_us": round(mean_launch_us([lambda: (a(), b())], 200), 2)}
+
     # ---- CPU baseline: the oracle on the same step (whole steps, repeated for a bounded time)
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,7 +407,7 @@ def main() -> int:
                    "path": args.path, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
-                   "read_ceiling": ceiling,
+                   "read_ceiling": ceiling, "producers": producers,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
