@@ -4,11 +4,13 @@
 One step is one decode pass over the narrow projections (o-proj 5120x8192 and
 down-proj 5120x25600, batch 1): for each of the Int8Act and TwoPass numerics and
 each projection, quantize the activation, run the split-K GEMV and the ascending
-combine.  The default path makes the three calls of the pages' own structure
-(qdg_quantize_act, qdg_gemv_q8 with S chunks, qdg_sk_combine); --path fused
-makes two (qdg_quantize_act, then qdg_gemv_q8_sk, the split-K GEMV whose
-last-arriving workgroups do the ascending combine).  Each run reports the other
-path's step time beside its own, and times Dequant (qdg_gemv_q8_fused with the
+combine.  The default path makes two calls (qdg_quantize_act, then
+qdg_gemv_q8_sk: the split-K GEMV whose chunks are the waves of one workgroup and
+meet in LDS for the ascending combine); --path staged makes the three calls of
+the pages' own structure (qdg_quantize_act, qdg_gemv_q8 with S chunks,
+qdg_sk_combine) and --path single one (qdg_gemv_q8_fused, the quantizer in every
+workgroup).  All three give the same bits.  Each run reports the other paths'
+step times beside its own, and times Dequant (qdg_gemv_q8_fused with the
 same S) on the same projections.  Inputs are seeded synthetic tensors resident in HBM before
 timing; the weights rotate over enough copies (>= 1 GiB between reuses of a
 copy) that the 256 MB Infinity Cache cannot serve them.
@@ -49,18 +51,32 @@ def alg_bytes(mode: int, N: int, K: int, B: int = 1) -> int:
     return N * K + N * K // 16 + B * act + 4 * B * N
 
 
+def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
+    """The GEMV kernel a path launches for one projection, as the kernel trace names
+    it, and its grid in threads."""
+    import quantized_decode_gemv_02_amd as q
+    shape = q.sk_workgroup_shape(mode, sh.K, S) if path == "fused" else None
+    if shape is not None:
+        rows, waves = shape
+        local = "true" if rows == 4 else "false"
+        return f"k_gemv_wsplit<{mode}, {rows // 4}, 4, {local}>", 64 * waves * -(-sh.N // rows)
+    flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
+    return f"k_gemv_dot4<{mode}, 4, 4, {flags}, false>", 256 * -(-sh.N // 16) * S
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--splits", default="4,16",
-                    help="split-K chunks: 'auto' (timed choice), one S for both projections, or 'S_o,S_down'")
+    ap.add_argument("--splits", default=None,
+                    help="split-K chunks: 'auto' (timed choice), one S for both projections, or 'S_o,S_down'; "
+                         "default per path: 5,5 for the in-workgroup combine (fused), 4,16 otherwise")
     ap.add_argument("--modes", default="1,2")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
-    ap.add_argument("--path", choices=("single", "fused", "staged"), default="staged")
+    ap.add_argument("--path", choices=("single", "fused", "staged"), default="fused")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--no-producers", action="store_true",
@@ -139,27 +155,40 @@ def main() -> int:
         }
 
     # ---- S per (mode, shape): fixed (default 4 for the o-proj, 8 for the down-proj), or timed
+    # Measured best (back-to-back, rotated copies): the in-workgroup combine at S = 5 on both
+    # projections (5120x25600: five chunks of 5120 values, three row groups, one round of
+    # workgroups; 5120x8192: the same four chunks as S = 4); the workspace paths at 4 and 16.
+    default_splits = {"fused": "5,5", "staged": "4,16", "single": "4,16"}
+
+    def splits_for(path):
+        spec = args.splits or default_splits[path]
+        if spec == "auto":
+            return None
+        v = [int(t) for t in spec.split(",")]
+        return {(mode, si): v[min(si, len(v) - 1)] for mode in modes for si in range(len(shapes))}
+
     chosen = {}
-    fixed = None if args.splits == "auto" else [int(v) for v in args.splits.split(",")]
+    fixed = splits_for(args.path)
     for mode in modes:
         for si in range(len(shapes)):
             if fixed is not None:
-                chosen[(mode, si)] = fixed[min(si, len(fixed) - 1)]
+                chosen[(mode, si)] = fixed[(mode, si)]
                 ensure_buffers(mode, si, chosen[(mode, si)])
                 continue
             best = None
-            for S in (1, 2, 3, 4, 6, 8, 12, 16):
+            for S in (1, 2, 3, 4, 5, 6, 8, 10, 12, 13, 16):
                 ensure_buffers(mode, si, S)
-                seqs = [make_calls(mode, si, S, c) for c in range(R)]
+                seqs = [make_calls(mode, si, S, c, args.path) for c in range(R)]
                 for c in seqs:
                     for f in c:
                         f()
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 reps = 8 * R
+                skip = 0 if args.path == "single" else 1  # the quantizer does not depend on S
                 e0.record()
                 for i in range(reps):
-                    for f in seqs[i % R][1:]:
+                    for f in seqs[i % R][skip:]:
                         f()
                 e1.record()
                 torch.cuda.synchronize()
@@ -172,13 +201,16 @@ def main() -> int:
     dom_key = (2 if 2 in modes else modes[-1], len(shapes) - 1)
 
     def build_steps(path):
+        ch = chosen if path == args.path else (splits_for(path) or chosen)
+        for key, S in ch.items():
+            ensure_buffers(key[0], key[1], S)
         steps = []
         for copy_pair in range(R):
             seq = []
             for mi, mode in enumerate(modes):
                 cidx = (copy_pair * len(modes) + mi) % R
                 for si in range(len(shapes)):
-                    seq.append(((mode, si), make_calls(mode, si, chosen[(mode, si)], cidx, path)))
+                    seq.append(((mode, si), make_calls(mode, si, ch[(mode, si)], cidx, path)))
             steps.append(seq)
         return steps
 
@@ -257,13 +289,11 @@ def main() -> int:
     # HBM bytes per launch of the dominant kernel from the committed profiler counters, used
     # only if they were taken on the current kernel sources at the same launch shape
     traffic = None
+    dom_name, dom_grid = dominant_kernel(args.path, dom_key[0], shapes[dom_key[1]], chosen[dom_key])
     tpath = os.path.join(ROOT, "profiles", "gemv_q8_narrow_projections_traffic.json")
     if os.path.exists(tpath):
         from quantized_decode_gemv_02_amd import profiling
         t = json.load(open(tpath))
-        dom_grid = 256 * -(-shapes[dom_key[1]].N // 16) * chosen[dom_key]
-        flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[args.path]
-        dom_name = f"k_gemv_dot4<{dom_key[0]}, 4, 4, {flags}, false>"
         if (t.get("kernel_source_sha") == profiling.kernel_source_sha() and t.get("grid") == dom_grid
                 and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
@@ -298,7 +328,7 @@ def main() -> int:
         per_mode["dequant"] = {}
         for si, sh in enumerate(shapes):
             y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
-            S = chosen[(modes[0], si)]
+            S = (splits_for("staged") or chosen)[(modes[0], si)]  # Dequant splits through the workspace
             dws = q.sk_workspace(sh.N, S)
             calls = [q.bind_gemv_q8_fused(0, copies[c][si][0], copies[c][si][1], y0, acts[si], S, dws)
                      for c in range(R)]
@@ -411,7 +441,7 @@ def main() -> int:
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"k_gemv_dot4 ({args.path} path) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
+                     "kernel": f"{dom_name} ({args.path} path) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
                      "alg_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_ms * 1e3, 3)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

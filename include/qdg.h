@@ -131,6 +131,13 @@ int qdg_gemv_q8(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64
 int qdg_sk_combine(const float *partials, int splits, int64_t B, int64_t N, float *y,
                    qdg_stream stream);
 
+/* Host only: 1 when qdg_gemv_q8_sk combines the chunks of (mode, K, splits)
+ * inside a workgroup (in LDS, workspace untouched), 0 when it goes through the
+ * workspace, negative status on bad arguments.  shape (host, 2 entries, or
+ * NULL) receives the in-workgroup launch's rows and waves per workgroup (0, 0
+ * for the workspace path). */
+int qdg_gemv_sk_combines_in_workgroup(int mode, int64_t K, int splits, int32_t *shape);
+
 /* Bytes of device workspace qdg_gemv_q8_sk and qdg_gemv_q8_fused need (0 for an
  * unsupported shape): tickets, then room for S x N binary64 partials. */
 size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
@@ -138,11 +145,17 @@ size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
 /*
  * The split-K GEMV and its combine in one launch (QDG_INT8ACT, QDG_TWOPASS;
  * B == 1): the chunks of the QWEN38 page's chunk rule run as in qdg_gemv_q8,
- * and the last workgroup of each 16-row tile to finish (an atomic ticket per
- * tile; the lane kernel library page's last-arriving-block pattern, in place of
- * the QWEN38 page's separate combine kernel) sums the tile's partials in
- * ascending chunk order from 0.  y [1][N] is bit-identical to qdg_gemv_q8(splits)
- * + qdg_sk_combine: which chunk finishes last changes nothing.  Inputs as
+ * and each row's chunk partials are added in ascending chunk order from 0, in
+ * place of the QWEN38 page's separate combine kernel.  Two placements, with the
+ * same bits:
+ *   - splits 4, 8 or 16, when the activation row fits in LDS (K up to 25600 for
+ *     QDG_TWOPASS at splits 16, more otherwise): a row tile's chunks are the
+ *     waves of one workgroup and meet in LDS; the workspace is not touched;
+ *   - otherwise the last workgroup of each 16-row tile to finish (an atomic
+ *     ticket per tile; the lane kernel library page's last-arriving-block
+ *     pattern) sums the tile's partials through the workspace.
+ * y [1][N] is bit-identical to qdg_gemv_q8(splits) + qdg_sk_combine: which
+ * chunk finishes last changes nothing.  Inputs as
  * qdg_gemv_q8 (xq, xl, xs from qdg_quantize_act); workspace: device memory of at
  * least qdg_gemv_sk_workspace_bytes(1, N, splits) bytes, 256-byte aligned and
  * zero-filled before its first use; every call that completes leaves its tickets

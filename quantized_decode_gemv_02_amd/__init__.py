@@ -60,6 +60,7 @@ _SIGS = {
     "qdg_gemv_q8": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _I64, _I, _P, _P], _I),
     "qdg_sk_combine": ([_P, _I, _I64, _I64, _P, _P], _I),
     "qdg_gemv_sk_workspace_bytes": ([_I64, _I64, _I], ctypes.c_size_t),
+    "qdg_gemv_sk_combines_in_workgroup": ([_I, _I64, _I, _P], _I),
     "qdg_gemv_q8_sk": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_gemv_q8_fused": ([_I, _P, _P, _I64, _I64, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_gemv_argmax_workspace_bytes": ([_I64], ctypes.c_size_t),
@@ -210,6 +211,20 @@ def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: i
 
 def gemv_sk_workspace_bytes(B: int, N: int, splits: int) -> int:
     return int(_lib.qdg_gemv_sk_workspace_bytes(B, N, splits))
+
+
+def sk_combines_in_workgroup(mode: int, K: int, splits: int) -> bool:
+    """Whether ``gemv_q8_sk`` adds the chunk partials inside a workgroup (LDS) for this shape."""
+    return sk_workgroup_shape(mode, K, splits) is not None
+
+
+def sk_workgroup_shape(mode: int, K: int, splits: int):
+    """``(rows, waves)`` per workgroup of the in-workgroup launch, or ``None`` (workspace path)."""
+    arr = (ctypes.c_int32 * 2)()
+    r = int(_lib.qdg_gemv_sk_combines_in_workgroup(mode, K, splits, ctypes.cast(arr, ctypes.c_void_p)))
+    if r < 0:
+        _check("qdg_gemv_sk_combines_in_workgroup", r)
+    return (int(arr[0]), int(arr[1])) if r == 1 else None
 
 
 def sk_workspace(N: int, splits: int):

@@ -117,6 +117,19 @@ int qdg_gemv_q8_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, in
   return hip_status(qdg::launch_gemv_sk(mode, wq, ws, N, K, xq, xl, xs, splits, y, workspace, as_stream(stream)));
 }
 
+int qdg_gemv_sk_combines_in_workgroup(int mode, int64_t K, int splits, int32_t* shape) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (K < qdg::QK || K % qdg::QK || splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  int rows = 0, waves = 0;
+  const bool in_wg = splits > 1 && qdg::wsplit_fits(mode, K, splits);
+  if (in_wg) qdg::wsplit_shape(K, splits, rows, waves);
+  if (shape) {
+    shape[0] = rows;
+    shape[1] = waves;
+  }
+  return in_wg ? 1 : 0;
+}
+
 int qdg_gemv_q8_fused(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                       int splits, float* y, void* workspace, size_t workspace_bytes, qdg_stream stream) {
   if (mode < QDG_DEQUANT || mode > QDG_TWOPASS) return QDG_EINVAL;

@@ -207,6 +207,11 @@ hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t
                          int splits, float* y, void* workspace, hipStream_t st);
 int argmax_groups(int64_t N);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st);
+bool wsplit_fits(int mode, int64_t K, int splits);
+void wsplit_shape(int64_t K, int splits, int& rows, int& waves);
+hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                              const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                              hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);

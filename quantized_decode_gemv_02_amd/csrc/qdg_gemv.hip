@@ -326,6 +326,11 @@ size_t sk_workspace_bytes(int64_t N, int splits) {
 hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
                           const int8_t* xl, const float* xs, int splits, float* y, void* workspace, hipStream_t st) {
   if (splits == 1) return launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, 1, y, st);
+  // the chunks as waves of one workgroup, combined in LDS, where the activation
+  // fits (QDG_SK_WSPLIT=0 forces the workspace path; read on every call)
+  const char* e = getenv("QDG_SK_WSPLIT");
+  if (!(e && e[0] == '0') && wsplit_fits(mode, K, splits))
+    return launch_gemv_wsplit(mode, wq, ws, N, K, xq, xl, xs, splits, y, st);
   unsigned* tickets = (unsigned*)workspace;
   float* part = (float*)((char*)workspace + sk_partials_offset(N));
   if (mode == 1) return launch_mode<1, true, false>(wq, ws, N, K, xq, xl, xs, nullptr, splits, part, tickets, y, st);

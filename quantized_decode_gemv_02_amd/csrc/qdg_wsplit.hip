@@ -1,0 +1,243 @@
+// qdg_wsplit.hip -- the split-K GEMV with its combine inside one workgroup: the
+// S chunks of a row tile are S waves of the same workgroup, and their partials
+// meet in LDS.  It computes exactly what the QWEN38 page's split-K GEMV
+// (gk_gemv_hl_sk) followed by its ascending combine (gk_sk_combine) computes:
+// wave c forms chunk c's partial of its four rows in the lane kernel library
+// page's row order (lk_q8_rows_dot restricted to the chunk, as k_gemv_dot4
+// does), and one thread per row then adds the S partials in ascending chunk
+// order from +0.  No partial leaves the workgroup, so there is no workspace, no
+// ticket and no second launch.
+//
+// Layout: a workgroup has R row groups of four rows times one wave per
+// non-empty chunk (at most 16 waves).  The workgroup stages the whole activation
+// row (words, scales)
+// and its rows' weight scales in LDS, since its waves between them cover all of
+// K.  A wave's lanes work as in k_gemv_dot4 with four rows a wave: 16 lanes a
+// row, a lane pair a block, partial q of the row in lane pair q.
+#include <stdlib.h>
+
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+constexpr int WS_NT = 1024;               // sixteen waves
+constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with the static part
+
+template <int MODE, int ROWS>
+constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
+
+// LOCAL: each wave stages only its own chunk (and its rows' scales over it) and
+// starts as soon as its own stores are done, with no workgroup barrier before
+// the dot products; waves of different row groups that share a chunk write the
+// same bytes.
+template <int MODE, int R, int U, bool LOCAL>
+// eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
+__global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(const int8_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ ws,
+                                                       const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                       const float* __restrict__ xs, int64_t N, int64_t K, int S,
+                                                       int m, int ceff, float* __restrict__ y) {
+  constexpr int ROWS = 4 * R;   // rows of the workgroup
+  constexpr int LPR = 16, BPS = 8;
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ float lpart[WS_NT / 64][4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave c of a row group takes the c-th non-empty chunk: chunks 0..m-1, then
+  // chunk S-1 when it holds the K mod 512 tail; the empty chunks' partials are
+  // +0 and adding +0 changes no partial sum (none is -0), so they are skipped
+  const int rg = wave / ceff, c = wave % ceff;
+  const int chunk = c < m ? c : S - 1;
+  const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
+  const int64_t nb = K / QK;
+  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  const int rr = rg * 4 + r;
+  const int64_t o = o_wg + rr;
+  const bool row_ok = o < N;
+  const int8_t* wrow = wq + (row_ok ? o : N - 1) * K + hf * 16;
+  int32_t g0, g1;
+  split_range(K, S, chunk, g0, g1);
+  const int nwb = g1 - g0;
+  const int nsteps = (nwb + BPS - 1) / BPS;
+  const int ngroups = (nsteps + U - 1) / U;
+
+  int8_t* lq = (int8_t*)lds;                                               // [nb][32]
+  int8_t* ll = lq + nb * QK;                                               // [nb][32] (TwoPass)
+  float* lsx = (float*)(lds + nb * QK * (MODE == 2 ? 2 : 1));              // [nb]
+  uint16_t* lsg = (uint16_t*)(lsx + nb);                                   // [ROWS][nb]
+  const uint16_t* my_sg = lsg + rr * nb;
+
+  // the wave's first weights are requested before the staging barrier
+  int4 wcur[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = g0 + u * BPS + j;
+    wcur[u] = b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+  }
+  if constexpr (LOCAL) {
+    for (int i = lane; i < nwb * 2; i += 64) {
+      const int64_t k = (int64_t)g0 * 2 + i;
+      ((int4*)lq)[k] = ld16(xq + 16 * k);
+      if constexpr (MODE == 2) ((int4*)ll)[k] = ld16(xl + 16 * k);
+    }
+    for (int i = lane; i < nwb; i += 64) lsx[g0 + i] = xs[g0 + i];
+    // stage_scales writes columns [0, n) of dst: point dst at column g0 of the row group's rows
+    stage_scales(lsg + rg * 4 * nb + g0, (int)nb, ws, nb, N, o_wg + rg * 4, 4, g0, nwb, lane, 64);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    const int nt = (int)blockDim.x;
+    for (int64_t i = tid; i < nb * 2; i += nt) {
+      ((int4*)lq)[i] = ld16(xq + 16 * i);
+      if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + 16 * i);
+    }
+    for (int64_t i = tid; i < nb; i += nt) lsx[i] = xs[i];
+    stage_scales(lsg, (int)nb, ws, nb, N, o_wg, ROWS, 0, (int)nb, tid, nt);
+    __syncthreads();
+  }
+
+  float p = 0.0f;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    int4 wnxt[U];
+    const bool more = gi + 1 < ngroups;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = g0 + ((gi + 1) * U + u) * BPS + j;
+      wnxt[u] = more && b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int bl = (gi * U + u) * BPS + j;  // block within the chunk
+      const bool ok = bl < nwb;
+      const int blc = g0 + (ok ? bl : 0);
+      const int4 a = *(const int4*)(lq + blc * QK + hf * 16);
+      const int d = block_dot_pair(wcur[u], a);
+      int e = 0;
+      if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
+      float ta, tb;
+      q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
+      p = ok ? __fmaf_rn(ta, tb, p) : p;
+      const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
+      p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
+  }
+  // (P0 + P2) + (P1 + P3): the chunk's partial of the row, in lane 0 of the row
+  const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
+  const float yv = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+  if (li == 0) lpart[wave][r] = yv;
+  __syncthreads();
+  if (tid < ROWS && o_wg + tid < N) {
+    // row tid of the workgroup: row group tid/4, row tid%4; its partials are the
+    // row group's waves in ascending chunk order
+    const int g = tid >> 2, q = tid & 3;
+    float a = 0.0f;
+    for (int cc = 0; cc < ceff; ++cc) a = __fadd_rn(a, lpart[g * ceff + cc][q]);
+    y[o_wg + tid] = a;
+  }
+}
+
+// The chunk waves of one row group: the non-empty chunks of the S-chunk rule.
+void ws_chunks(int64_t K, int S, int& m, int& ceff) {
+  const int64_t nq = K / 512, per = (nq + S - 1) / S;
+  m = per > 0 ? (int)((nq + per - 1) / per) : 0;  // chunks with superblocks (head)
+  if (m > S) m = S;
+  const bool tail = (K % 512) != 0;
+  ceff = m;
+  if (m < S && (tail || m == 0)) ceff = m + 1;      // chunk S-1: the tail (or all of K when nq = 0)
+  if (m == S) ceff = S;
+}
+
+template <int MODE, int R>
+size_t ws_lds_bytes(int64_t K) { return (size_t)(K / QK) * ws_bytes_per_block<MODE, 4 * R>(); }
+
+template <int MODE, int R, bool LOCAL>
+hipError_t launch_ws(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int S, float* y, hipStream_t st) {
+  constexpr int ROWS = 4 * R;
+  int m, ceff;
+  ws_chunks(K, S, m, ceff);
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, 4, LOCAL>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS)), block((unsigned)(64 * R * ceff));
+  const size_t lds = ws_lds_bytes<MODE, R>(K);
+  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, LOCAL>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, S, m, ceff,
+                     y);
+  return hipGetLastError();
+}
+
+// Per-wave staging when a row group is the whole workgroup (each wave's chunk is
+// its own), the workgroup barrier otherwise (row groups share the staged chunks).
+// Measured on 5120x25600 / 5120x8192: per-wave staging is 4% faster with one row
+// group, 1-6% slower with two or four.  QDG_WS_LOCAL=0/1 overrides (read on every call).
+bool ws_local(int R) {
+  if (const char* e = getenv("QDG_WS_LOCAL")) return e[0] == '1';
+  return R == 1;
+}
+
+// Row groups a workgroup: QDG_WS_ROWS (1..4 groups of four rows) overrides the
+// default of as many as fit in 16 waves, at most 4.
+int ws_groups(int ceff) {
+  int R = 16 / ceff;
+  if (const char* e = getenv("QDG_WS_ROWS")) R = atoi(e);
+  if (R > 4) R = 4;
+  if (R < 1) R = 1;
+  while (R > 1 && R * ceff > 16) --R;
+  return R;
+}
+
+template <int MODE, int R>
+hipError_t launch_ws_local(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                           const int8_t* xl, const float* xs, int S, float* y, hipStream_t st) {
+  if (ws_local(R)) return launch_ws<MODE, R, true>(wq, ws, N, K, xq, xl, xs, S, y, st);
+  return launch_ws<MODE, R, false>(wq, ws, N, K, xq, xl, xs, S, y, st);
+}
+
+template <int MODE>
+hipError_t launch_ws_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                          const int8_t* xl, const float* xs, int S, int R, float* y, hipStream_t st) {
+  switch (R) {
+    case 1: return launch_ws_local<MODE, 1>(wq, ws, N, K, xq, xl, xs, S, y, st);
+    case 2: return launch_ws_local<MODE, 2>(wq, ws, N, K, xq, xl, xs, S, y, st);
+    case 3: return launch_ws_local<MODE, 3>(wq, ws, N, K, xq, xl, xs, S, y, st);
+    default: return launch_ws_local<MODE, 4>(wq, ws, N, K, xq, xl, xs, S, y, st);
+  }
+}
+
+}  // namespace
+
+// Whether the in-workgroup split serves (mode, K, splits) for one activation row:
+// the non-empty chunks fit in 16 waves and the staged row in the LDS budget.
+bool wsplit_fits(int mode, int64_t K, int splits) {
+  if (splits < 2 || splits > 16) return false;
+  int m, ceff;
+  ws_chunks(K, splits, m, ceff);
+  if (ceff < 2) return false;
+  const int R = ws_groups(ceff);
+  const int64_t bpb = (mode == 2 ? 2 : 1) * QK + 4 + 2 * 4 * R;
+  return (K / QK) * bpb <= WS_LDS_MAX;
+}
+
+void wsplit_shape(int64_t K, int splits, int& rows, int& waves) {
+  int m, ceff;
+  ws_chunks(K, splits, m, ceff);
+  const int R = ws_groups(ceff);
+  rows = 4 * R;
+  waves = R * ceff;
+}
+
+hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                              const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                              hipStream_t st) {
+  int m, ceff;
+  ws_chunks(K, splits, m, ceff);
+  const int R = ws_groups(ceff);
+  if (mode == 1) return launch_ws_mode<1>(wq, ws, N, K, xq, xl, xs, splits, R, y, st);
+  return launch_ws_mode<2>(wq, ws, N, K, xq, xl, xs, splits, R, y, st);
+}
+
+}  // namespace qdg

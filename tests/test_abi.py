@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -132,6 +132,27 @@ def test_fused_validation():
     assert call(wq=A + 8) == EALIGN
     assert call(wsp=A + 8) == EALIGN
     assert call(nbytes=need - 4) == EWORKSPACE
+
+
+def test_sk_placement_query():
+    def f(mode, K, S):
+        return lib.qdg_gemv_sk_combines_in_workgroup(mode, K, S, None)
+    assert f(0, 512, 4) == EINVAL
+    assert f(1, 500, 4) == ESHAPE
+    assert f(1, 512, 0) == ESHAPE
+    assert f(1, 25600, 16) == 1 and f(2, 25600, 16) == 1
+    assert f(1, 25600, 4) == 1 and f(2, 25600, 4) == 1
+    assert f(1, 8192, 1) == 0                                  # no split, nothing to combine
+    assert f(1, 8192, 3) == 1 and f(2, 12288, 5) == 1
+    assert f(1, 8192, 17) == 0 and f(1, 8192, 64) == 0       # more chunk waves than a workgroup holds
+    assert f(1, 512, 16) == 0                                  # one non-empty chunk
+    assert f(2, 65536, 16) == 0                                # the staged row exceeds the LDS budget
+    # launch shape: one wave per non-empty chunk, row groups of four rows up to 16 waves
+    assert q.sk_workgroup_shape(2, 25600, 16) == (4, 13)       # 13 chunks of 4 superblocks, 3 empty
+    assert q.sk_workgroup_shape(2, 25600, 5) == (12, 15)       # 5 chunks, three row groups
+    assert q.sk_workgroup_shape(1, 8192, 5) == (16, 16)        # 4 chunks of 4 superblocks, 1 empty
+    assert q.sk_workgroup_shape(1, 25632, 16) == (4, 14)       # the tail makes chunk 15 non-empty
+    assert q.sk_workgroup_shape(1, 8192, 1) is None
 
 
 def test_gemv_argmax_validation():

@@ -305,8 +305,11 @@ def test_repeat_and_fresh_buffers_bitwise():
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 8), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
                                    (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4)])
-def test_in_kernel_combine_bit_exact(mode, N, K, S):
-    announce(f"gemv_q8_sk mode={mode} N={N} K={K} S={S}")
+@pytest.mark.parametrize("path", ["default", "workspace"])
+def test_in_kernel_combine_bit_exact(mode, N, K, S, path, monkeypatch):
+    announce(f"gemv_q8_sk mode={mode} N={N} K={K} S={S} {path}")
+    if path == "workspace":
+        monkeypatch.setenv("QDG_SK_WSPLIT", "0")
     wq, ws, x = _quant_case(N, K, 1, 11 * N + K + S, outliers=True)
     oq, ol, os_ = oracle.quantize(mode, x)
     want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
@@ -319,6 +322,38 @@ def test_in_kernel_combine_bit_exact(mode, N, K, S):
         np.testing.assert_array_equal(host(y), want)
     tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
     assert not tickets.any()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K,S", [(5120, 25600, 16), (5120, 8192, 4), (77, 8192, 8), (4097, 1600, 16),
+                                   (33, 544, 4), (9, 256, 8), (1, 32, 16), (130, 12288, 8), (20, 25632, 16),
+                                   (5120, 25600, 5), (640, 25600, 10), (300, 25600, 13), (50, 25632, 12),
+                                   (21, 8192, 3), (64, 4608, 2), (19, 1056, 7)])
+@pytest.mark.parametrize("variant", ["barrier", "wave-local"])
+def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
+    """The split-K GEMV whose chunks are the waves of one workgroup (partials
+    combined in LDS) against the oracle's chunk partials and ascending combine,
+    with the workgroup-wide or the per-wave staging of the activation."""
+    announce(f"gemv_q8_sk in-workgroup split mode={mode} N={N} K={K} S={S} {variant}")
+    monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
+    wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    if N > 1000:  # the oracle on every 7th row (the rows are independent)
+        rows = np.arange(0, N, 7)
+        want = oracle.combine(oracle.gemv_split(mode, wq[rows], ws[rows], oq, ol, os_, S, nthreads=8))
+    else:
+        rows, want = np.arange(N), oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    wqd, wsd = dev(wq), dev(ws)
+    xq, xl, xs = quantize_gpu(mode, x)
+    wsp = q.sk_workspace(N, S)
+    for rep in range(2):
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_sk(mode, wqd, wsd, y, xq, xl, xs, S, wsp)
+        np.testing.assert_array_equal(host(y)[:, rows], want)
+    monkeypatch.setenv("QDG_SK_WSPLIT", "0")  # the workspace path: the same bits
+    y2 = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    q.gemv_q8_sk(mode, wqd, wsd, y2, xq, xl, xs, S, wsp)
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
 
 
 @pytest.mark.parametrize("mode", [1, 2])
