@@ -79,6 +79,7 @@ def parse():
     ap.add_argument("--path", choices=("single", "fused", "staged"), default="fused")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the S in {1,2,4,8} sweep beside the step")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the timing of the fused producers (RMSNorm / SwiGLU + quantizer)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -349,6 +350,26 @@ def main() -> int:
                                             "gemv_GBs": round(b / us / 1e3, 1),
                                             "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
 
+    # The configuration's own split counts, S in {1, 2, 4, 8}, beside the chosen S: the GEMV with
+    # its combine (the default path's qdg_gemv_q8_sk) per mode and projection, events around
+    # each launch, rotated copies.
+    splits_sweep = {}
+    if not args.no_sweep:
+        for mode in modes:
+            for si, sh in enumerate(shapes):
+                rec = {}
+                for S in (1, 2, 4, 8):
+                    ensure_buffers(mode, si, S)
+                    b = buffers[(mode, si, S)]
+                    calls = [q.bind_gemv_q8_sk(mode, copies[c][si][0], copies[c][si][1], b["y"], b["xq"], b["xl"],
+                                               b["xs"], S, b["fws"]) for c in range(R)]
+                    q.quantize_act(mode, acts[si], b["xq"], b["xl"], b["xs"])
+                    us = mean_launch_us(calls, max(40, 4 * R))
+                    rec[str(S)] = {"gemv_us": round(us, 3),
+                                   "gemv_GBs": round(alg_bytes(mode, sh.N, sh.K) / us / 1e3, 1),
+                                   "in_workgroup": q.sk_combines_in_workgroup(mode, sh.K, S)}
+                splits_sweep[f"{names[mode]}_{sh.name}"] = rec
+
     # The practical read ceiling: qdg_stream_read (contiguous 64 KiB slabs a workgroup, nothing
     # but 16-byte nontemporal loads) over as many bytes as each GEMV launch moves, rotated over
     # a pool larger than the Infinity Cache, and over 1 GiB.
@@ -437,7 +458,7 @@ def main() -> int:
                    "path": args.path, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
-                   "read_ceiling": ceiling, "producers": producers,
+                   "read_ceiling": ceiling, "producers": producers, "splits_sweep": splits_sweep,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,

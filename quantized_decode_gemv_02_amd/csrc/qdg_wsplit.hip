@@ -179,10 +179,13 @@ bool ws_local(int R) {
   return R == 1;
 }
 
-// Row groups a workgroup: QDG_WS_ROWS (1..4 groups of four rows) overrides the
-// default of as many as fit in 16 waves, at most 4.
+// Row groups a workgroup: three where they fit in 16 waves, else as many as fit.
+// Measured on the 5120-row projections over R = 1..4 and S = 2, 4, 5, 8: three
+// groups (427 workgroups, one round at two workgroups a CU) is the fastest or
+// within 1% of it in every case, and four is 7-20% slower than three.
+// QDG_WS_ROWS (1..4) overrides (read on every call).
 int ws_groups(int ceff) {
-  int R = 16 / ceff;
+  int R = 3 * ceff <= 16 ? 3 : 16 / ceff;
   if (const char* e = getenv("QDG_WS_ROWS")) R = atoi(e);
   if (R > 4) R = 4;
   if (R < 1) R = 1;

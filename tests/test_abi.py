@@ -150,7 +150,8 @@ def test_sk_placement_query():
     # launch shape: one wave per non-empty chunk, row groups of four rows up to 16 waves
     assert q.sk_workgroup_shape(2, 25600, 16) == (4, 13)       # 13 chunks of 4 superblocks, 3 empty
     assert q.sk_workgroup_shape(2, 25600, 5) == (12, 15)       # 5 chunks, three row groups
-    assert q.sk_workgroup_shape(1, 8192, 5) == (16, 16)        # 4 chunks of 4 superblocks, 1 empty
+    assert q.sk_workgroup_shape(1, 8192, 5) == (12, 12)        # 4 chunks of 4 superblocks, 1 empty
+    assert q.sk_workgroup_shape(1, 25600, 8) == (8, 16)        # 8 chunks: two row groups fit
     assert q.sk_workgroup_shape(1, 25632, 16) == (4, 14)       # the tail makes chunk 15 non-empty
     assert q.sk_workgroup_shape(1, 8192, 1) is None
 
