@@ -243,6 +243,10 @@ hipError_t launch_gemv_dequant_argmax(const int8_t* wq, const uint16_t* ws, int6
 
 hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                   int splits, float* y, void* workspace, hipStream_t st) {
+  // the chunks as waves of one workgroup (qdg_dequant_seg.hip) wherever that
+  // kernel serves the shape; QDG_DQ_SEG=0 forces this file's kernel (read on every call)
+  const char* e = getenv("QDG_DQ_SEG");
+  if (!(e && e[0] == '0') && dq_seg_chunks(K, splits) > 0) return launch_gemv_dq_seg(wq, ws, N, K, x, splits, y, st);
   if (dq_x64()) return launch_dq<true>(wq, ws, N, K, x, splits, y, workspace, st);
   return launch_dq<false>(wq, ws, N, K, x, splits, y, workspace, st);
 }

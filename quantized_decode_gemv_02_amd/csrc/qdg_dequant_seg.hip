@@ -1,0 +1,185 @@
+// qdg_dequant_seg.hip -- the batch-1 Q8_0 GEMV under the Dequant numerics with
+// the chunks of a row tile as the waves of one workgroup (lane kernel library
+// page: module doc on the Dequant mode, lk_acc<0>; QWEN38 page: the split-K
+// chunk rule of gk_gemv_hl_sk, partials added in ascending chunk order as
+// gk_sk_combine adds them).  Every product and sum is binary64 and the row is
+// rounded once to binary32, as in k_gemv_dequant; only the fixed order and the
+// mapping onto the GPU differ.
+//
+// Mapping: a wave takes four rows of one chunk.  Lane l takes the l-th 8-value
+// piece of each 512-value step of the chunk (four lanes are a block) for all
+// four rows, so the piece's activation -- read once from the L1/L2-resident f32
+// vector and widened to binary64 in registers -- serves four rows, and each
+// weight load instruction reads 512 contiguous bytes of one row.
+//
+// Order (fixed, so repeats are bit-identical):
+//  * a lane's 8 products w_i*x_i (exact in binary64) are summed in two chains by
+//    i mod 2 from +0 in ascending i, then c0 + c1;
+//  * the block's four lane sums are added as (l0 + l1) + (l2 + l3), times sigma
+//    (one rounding): the block's term, the same in all four lanes;
+//  * a lane adds its blocks' terms in ascending step order from +0;
+//  * the chunk's partial is the sum over the 16 blocks of a step position by a
+//    butterfly over lane distances 4, 8, 16, 32;
+//  * the row adds its chunks' partials in ascending chunk order from +0 (empty
+//    chunks skipped: their partial is +0) and rounds once to binary32.
+#include <stdlib.h>
+
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+constexpr int DS_NT = 1024;
+
+constexpr int DPP_QUAD_SWAP2 = 0x4E;  // quad_perm [2,3,0,1]: lane i <- lane i^2
+
+__device__ __forceinline__ double piece_dot8(int2 w, const double* xd) {
+  const int ww[2] = {w.x, w.y};
+  double c0 = 0.0, c1 = 0.0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      c0 = __fma_rn((double)(int)(signed char)((ww[q] >> (8 * i)) & 255), xd[4 * q + i], c0);
+      c1 = __fma_rn((double)(int)(signed char)((ww[q] >> (8 * i + 8)) & 255), xd[4 * q + i + 1], c1);
+    }
+  }
+  return __dadd_rn(c0, c1);
+}
+
+__device__ __forceinline__ int2 ld8_stream(const int8_t* p) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i t = __builtin_nontemporal_load((const v2i*)p);
+  return make_int2(t[0], t[1]);
+}
+
+// At most 80 VGPRs (the kernel needs 70, so seven waves a SIMD): capped at 64 it
+// spills, and a register ring for the next step's weights (8 more VGPRs) costs a
+// wave a SIMD; measured, both are slower than letting the SIMD's other waves
+// cover the load latency.
+template <int R>
+__global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_dq_seg(
+    const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const float* __restrict__ x, int64_t N, int64_t K,
+    int S, int m, int ceff, float* __restrict__ y) {
+  constexpr int ROWS = 4 * R;
+  __shared__ double lpart[DS_NT / 64][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave / ceff, c = wave % ceff;
+  const int chunk = c < m ? c : S - 1;
+  const int64_t nb = K / QK;
+  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  int32_t g0, g1;
+  split_range(K, S, chunk, g0, g1);
+  // 8-value pieces of the row (32-bit offsets: K < 2^31, so the base + offset
+  // addressing keeps the per-lane address in one register)
+  const int p0 = 4 * g0, p1 = 4 * g1;
+
+  const int8_t* wrow[4];
+  const uint16_t* srow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int64_t o = o_wg + rg * 4 + r;
+    if (o >= N) o = N - 1;
+    wrow[r] = wq + o * K;
+    srow[r] = ws + o * nb;
+  }
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int st = p0; st < p1; st += 64) {
+    const int p = st + lane;
+    const bool act = p < p1;
+    int2 wc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wc[r] = act ? ld8_stream(wrow[r] + (unsigned)(8 * p)) : make_int2(0, 0);
+    double xd[8];
+    unsigned short sg[4];
+    if (act) {
+      const float4 f0 = *(const float4*)(x + (unsigned)(8 * p)), f1 = *(const float4*)(x + (unsigned)(8 * p + 4));
+      xd[0] = f0.x; xd[1] = f0.y; xd[2] = f0.z; xd[3] = f0.w;
+      xd[4] = f1.x; xd[5] = f1.y; xd[6] = f1.z; xd[7] = f1.w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sg[r] = srow[r][(unsigned)(p >> 2)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xd[i] = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sg[r] = 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const double v = piece_dot8(wc[r], xd);
+      const double s1 = __dadd_rn(v, dpp_f64<DPP_QUAD_SWAP1>(v));     // l0+l1 | l2+l3
+      const double blk = __dadd_rn(s1, dpp_f64<DPP_QUAD_SWAP2>(s1));  // (l0+l1)+(l2+l3)
+      const double term = __dmul_rn((double)half_bits_to_float(sg[r]), blk);
+      acc[r] = act ? __dadd_rn(acc[r], term) : acc[r];
+    }
+  }
+  // the 16 block positions' sums by a fixed butterfly (the four lanes of a block hold the same value)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int d = 4; d <= 32; d <<= 1) acc[r] = __dadd_rn(acc[r], __shfl_xor(acc[r], d, 64));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lpart[wave][r] = acc[r];
+  }
+  __syncthreads();
+  if (tid < ROWS && o_wg + tid < N) {
+    const int g = tid >> 2, q = tid & 3;
+    double a = 0.0;
+    for (int cc = 0; cc < ceff; ++cc) a = __dadd_rn(a, lpart[g * ceff + cc][q]);
+    y[o_wg + tid] = (float)a;
+  }
+}
+
+void ds_chunks(int64_t K, int S, int& m, int& ceff) {
+  const int64_t nq = K / 512, per = (nq + S - 1) / S;
+  m = per > 0 ? (int)((nq + per - 1) / per) : 0;
+  if (m > S) m = S;
+  ceff = m;
+  if (m < S && ((K % 512) != 0 || m == 0)) ceff = m + 1;
+}
+
+template <int R>
+hipError_t launch_ds(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int S, int m,
+                     int ceff, float* y, hipStream_t st) {
+  constexpr int ROWS = 4 * R;
+  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS)), block((unsigned)(64 * R * ceff));
+  hipLaunchKernelGGL((k_gemv_dq_seg<R>), grid, block, 0, st, wq, ws, x, N, K, S, m, ceff, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The chunk count the kernel uses: the caller's S, or 5 when it asks for none
+// (the order is the kernel's own; five chunks of 5120 values make one round of
+// workgroups on the 5120-row projections).  0 when the kernel does not serve the
+// shape (more than 16 chunk waves).
+int dq_seg_chunks(int64_t K, int splits) {
+  const int S = splits == 1 ? 5 : splits;
+  int m, ceff;
+  ds_chunks(K, S, m, ceff);
+  return ceff <= 16 ? S : 0;
+}
+
+hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
+                              float* y, hipStream_t st) {
+  const int S = dq_seg_chunks(K, splits);
+  int m, ceff;
+  ds_chunks(K, S, m, ceff);
+  // one row group a workgroup (measured on the 5120-row projections: R = 1 is
+  // 10-25% faster than 2-4 at S = 4, 5 and 8); QDG_DQ_ROWS overrides
+  int R = 1;
+  if (const char* e = getenv("QDG_DQ_ROWS")) R = atoi(e);
+  if (R < 1) R = 1;
+  if (R > 4) R = 4;
+  while (R > 1 && R * ceff > 16) --R;
+  switch (R) {
+    case 1: return launch_ds<1>(wq, ws, N, K, x, S, m, ceff, y, st);
+    case 2: return launch_ds<2>(wq, ws, N, K, x, S, m, ceff, y, st);
+    case 3: return launch_ds<3>(wq, ws, N, K, x, S, m, ceff, y, st);
+    default: return launch_ds<4>(wq, ws, N, K, x, S, m, ceff, y, st);
+  }
+}
+
+}  // namespace qdg

@@ -208,6 +208,9 @@ hipError_t launch_gemv_x(int mode, const int8_t* wq, const uint16_t* ws, int64_t
 int argmax_groups(int64_t N);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st);
 bool wsplit_fits(int mode, int64_t K, int splits);
+int dq_seg_chunks(int64_t K, int splits);
+hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
+                              float* y, hipStream_t st);
 void wsplit_shape(int64_t K, int splits, int& rows, int& waves);
 hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                               const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,

@@ -222,8 +222,11 @@ def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, monkeypatch)
 # ---------------------------------------------------------------- Dequant
 
 @pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (37, 1600), (64, 12288), (20, 5120), (5, 25600)])
-def test_dequant_tolerance(N, K):
-    announce(f"dequant N={N} K={K}")
+@pytest.mark.parametrize("kernel", ["chunk-waves", "workspace"])
+def test_dequant_tolerance(N, K, kernel, monkeypatch):
+    announce(f"dequant N={N} K={K} {kernel}")
+    if kernel == "workspace":
+        monkeypatch.setenv("QDG_DQ_SEG", "0")
     wq, ws, x = _quant_case(N, K, 1, N + 3 * K, outliers=True)
     y = host(gemv_gpu(0, dev(wq), dev(ws), 1, N, x=dev(x)))
     Y, tn = oracle.reference_f64(0, wq, ws, x=x)
@@ -402,11 +405,14 @@ def test_fused_single_launch_dequant_and_edge_inputs():
 
 
 @pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7)])
-def test_fused_dequant_split_k(N, K, S):
+@pytest.mark.parametrize("kernel", ["chunk-waves", "workspace"])
+def test_fused_dequant_split_k(N, K, S, kernel, monkeypatch):
     """Dequant split-K (binary64 chunk partials, ascending binary64 combine, one
     rounding): within the Dequant tolerance of the binary64 reference, and almost
     always the oracle's own binary32 result."""
-    announce(f"gemv_q8_fused dequant N={N} K={K} S={S}")
+    announce(f"gemv_q8_fused dequant N={N} K={K} S={S} {kernel}")
+    if kernel == "workspace":
+        monkeypatch.setenv("QDG_DQ_SEG", "0")
     wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
     Y, tn = oracle.reference_f64(0, wq, ws, x=x, nthreads=8)
     want32 = oracle.gemv(0, wq, ws, x=x, nthreads=8)
@@ -419,6 +425,33 @@ def test_fused_dequant_split_k(N, K, S):
         assert (got == want32).mean() > 0.99
     tickets = host(wsp).view(np.uint32)[: -(-N // 16)]
     assert not tickets.any()
+
+
+@pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7),
+                                   (5120, 25600, 5), (300, 25600, 1), (1, 32, 1), (130, 12288, 8), (21, 4608, 3)])
+@pytest.mark.parametrize("variant", ["R1", "R2", "R3", "R4"])
+def test_dequant_chunk_waves(N, K, S, variant, monkeypatch):
+    """The Dequant GEMV whose chunks are waves of one workgroup (8 values a lane,
+    binary64 throughout, chunk partials added in LDS): within the Dequant
+    tolerance of the binary64 reference, almost always the oracle's binary32
+    result, and bit-identical on repeat."""
+    announce(f"dequant chunk waves N={N} K={K} S={S} {variant}")
+    monkeypatch.setenv("QDG_DQ_ROWS", variant[1])
+    wq, ws, x = _quant_case(N, K, 1, 23 * N + K + S, outliers=True)
+    rows = np.arange(0, N, 7) if N > 1000 else np.arange(N)
+    Y, tn = oracle.reference_f64(0, wq[rows], ws[rows], x=x, nthreads=8)
+    want32 = oracle.gemv(0, wq[rows], ws[rows], x=x, nthreads=8)
+    wsp = q.sk_workspace(N, S)
+    outs = []
+    for rep in range(2):
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_fused(0, dev(wq), dev(ws), y, dev(x.reshape(1, K)), S, wsp)
+        outs.append(host(y))
+    got = outs[0][:, rows]
+    assert oracle.within_tolerance(got, Y, tn).all()
+    if len(rows) >= 20:
+        assert (got == want32).mean() > 0.95
+    assert outs[0].tobytes() == outs[1].tobytes()
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
