@@ -70,6 +70,16 @@ enum {
 
 typedef void *qdg_stream; /* a hipStream_t */
 
+/* One weight matrix of a multi-matrix call (qdg_gemv_q8_parts): device
+ * pointers wq int8 [N][K], ws binary16 bits [N][K/32], y f32 [N]. */
+#define QDG_MAX_PARTS 6
+typedef struct qdg_part {
+  const int8_t *wq;
+  const uint16_t *ws;
+  int64_t N;
+  float *y;
+} qdg_part;
+
 /* QDG_ABI_VERSION of the built library. */
 int qdg_abi_version(void);
 
@@ -265,6 +275,24 @@ int64_t qdg_rmsnorm_max_k(void);
  */
 int qdg_swiglu_quantize(int mode, const float *g, const float *u, int64_t B, int64_t K,
                         float *h, int8_t *xq, int8_t *xl, float *xs, qdg_stream stream);
+
+/*
+ * Up to QDG_MAX_PARTS weight matrices over one activation row in one launch:
+ * q, k and v, or gate and up, side by side (lane kernel library page,
+ * GEMV_PARTS, lk_parts, lk_part_y).  parts (host array of nparts) gives each
+ * matrix and its output; all share K and the activation.  Every part's y is
+ * bit-identical to the single-matrix call with the same splits:
+ *   QDG_INT8ACT, QDG_TWOPASS: qdg_gemv_q8_sk with (xq, xl, xs) -- splits must
+ *     be one it combines inside a workgroup (qdg_gemv_sk_combines_in_workgroup
+ *     == 1), else QDG_EMODE;
+ *   QDG_DEQUANT: qdg_gemv_q8_fused with x (splits at most 16 non-empty chunks,
+ *     else QDG_EMODE).
+ * Needs no workspace.  Alignment as the single-matrix calls; 1 <= nparts <=
+ * QDG_MAX_PARTS, every N >= 1, K >= 32 and a multiple of 32.
+ */
+int qdg_gemv_q8_parts(int mode, const qdg_part *parts, int nparts, int64_t K, const float *x,
+                      const int8_t *xq, const int8_t *xl, const float *xs, int splits,
+                      qdg_stream stream);
 
 /*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library

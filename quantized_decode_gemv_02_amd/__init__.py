@@ -73,6 +73,7 @@ _SIGS = {
     "qdg_rmsnorm_quantize": ([_I, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_rmsnorm_max_k": ([], _I64),
     "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -196,6 +197,39 @@ def swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> None:
 
 def bind_swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> Bound:
     return Bound("qdg_swiglu_quantize", *_swiglu_args(mode, g, u, h, xq, xl, xs))
+
+
+MAX_PARTS = 6
+
+
+class _Part(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("N", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
+def _parts_args(mode, parts, x, xq, xl, xs, splits):
+    if not 1 <= len(parts) <= MAX_PARTS:
+        raise ValueError(f"gemv_q8_parts: 1 to {MAX_PARTS} parts")
+    K = parts[0][0].shape[1]
+    arr = (_Part * len(parts))()
+    for i, (wq, ws, y) in enumerate(parts):
+        if wq.shape[1] != K:
+            raise ValueError("gemv_q8_parts: every part must have the same K")
+        arr[i] = _Part(_ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), wq.shape[0], _ptr(y, _f32(), "y"))
+    return (mode, ctypes.cast(arr, ctypes.c_void_p), len(parts), K, _ptr(x, _f32(), "x"), _ptr(xq, _i8(), "xq"),
+            _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), int(splits), _stream()), arr
+
+
+def gemv_q8_parts(mode: int, parts, x=None, xq=None, xl=None, xs=None, splits: int = 4) -> None:
+    """``parts``: list of ``(wq [N_p][K], ws, y [N_p])``; one launch computes every ``y_p = W_p x``."""
+    args, _keep = _parts_args(mode, parts, x, xq, xl, xs, splits)
+    _check("qdg_gemv_q8_parts", _lib.qdg_gemv_q8_parts(*args))
+
+
+def bind_gemv_q8_parts(mode: int, parts, x=None, xq=None, xl=None, xs=None, splits: int = 4) -> Bound:
+    args, keep = _parts_args(mode, parts, x, xq, xl, xs, splits)
+    b = Bound("qdg_gemv_q8_parts", *args)
+    b.keep = keep  # the host part table must outlive the bound call
+    return b
 
 
 def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: int = 1) -> None:

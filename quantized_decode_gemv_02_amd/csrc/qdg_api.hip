@@ -177,6 +177,47 @@ size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
   return (size_t)B * (size_t)qdg::argmax_groups(N) * sizeof(unsigned long long);
 }
 
+int qdg_gemv_q8_parts(int mode, const qdg_part* parts, int nparts, int64_t K, const float* x, const int8_t* xq,
+                      const int8_t* xl, const float* xs, int splits, qdg_stream stream) {
+  if (mode < QDG_DEQUANT || mode > QDG_TWOPASS || !parts) return QDG_EINVAL;
+  if (nparts < 1 || nparts > QDG_MAX_PARTS) return QDG_ESHAPE;
+  if (mode == QDG_DEQUANT) {
+    if (!x || xq || xl || xs) return QDG_EINVAL;
+  } else {
+    if (x || !xq || !xs) return QDG_EINVAL;
+    if ((mode == QDG_TWOPASS) != (xl != nullptr)) return QDG_EINVAL;
+  }
+  const int8_t* wq[QDG_MAX_PARTS];
+  const uint16_t* ws[QDG_MAX_PARTS];
+  float* y[QDG_MAX_PARTS];
+  int64_t N[QDG_MAX_PARTS];
+  for (int p = 0; p < nparts; ++p) {
+    if (!parts[p].wq || !parts[p].ws || !parts[p].y) return QDG_EINVAL;
+    if (!shape_ok(parts[p].N, K)) return QDG_ESHAPE;
+    if (!aligned(parts[p].wq, 16) || !aligned(parts[p].ws, 2) || !aligned(parts[p].y, 4)) return QDG_EALIGN;
+    wq[p] = parts[p].wq;
+    ws[p] = parts[p].ws;
+    y[p] = parts[p].y;
+    N[p] = parts[p].N;
+  }
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (mode == QDG_DEQUANT) {
+    if (!aligned(x, 16)) return QDG_EALIGN;
+    if (qdg::dq_seg_chunks(K, splits) == 0) return QDG_EMODE;
+  } else {
+    if (!aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4)) return QDG_EALIGN;
+    if (splits < 2 || !qdg::wsplit_fits(mode, K, splits)) return QDG_EMODE;
+  }
+  // the grid (every part's row tiles) must fit an int: at least 4 rows a workgroup
+  int64_t tiles = 0;
+  for (int p = 0; p < nparts; ++p) tiles += (N[p] + 3) / 4;
+  if (tiles >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (mode == QDG_DEQUANT)
+    return hip_status(qdg::launch_gemv_dq_seg_parts(nparts, wq, ws, N, y, K, x, splits, as_stream(stream)));
+  return hip_status(
+      qdg::launch_gemv_wsplit_parts(mode, nparts, wq, ws, N, y, K, xq, xl, xs, splits, as_stream(stream)));
+}
+
 int qdg_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, void* workspace, size_t workspace_bytes,
                qdg_stream stream) {
   if (!y || !idx || !workspace) return QDG_EINVAL;

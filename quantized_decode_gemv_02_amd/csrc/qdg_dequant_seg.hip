@@ -59,15 +59,19 @@ __device__ __forceinline__ int2 ld8_stream(const int8_t* p) {
 // cover the load latency.
 template <int R>
 __global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_dq_seg(
-    const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws, const float* __restrict__ x, int64_t N, int64_t K,
-    int S, int m, int ceff, float* __restrict__ y) {
+    const PartTable tab, const float* __restrict__ x, int64_t K, int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;
   __shared__ double lpart[DS_NT / 64][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = wave / ceff, c = wave % ceff;
   const int chunk = c < m ? c : S - 1;
   const int64_t nb = K / QK;
-  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  int64_t o_wg;
+  const int part = find_part(tab, (int)blockIdx.x, ROWS, o_wg);
+  const int8_t* __restrict__ wq = tab.wq[part];
+  const uint16_t* __restrict__ ws = tab.ws[part];
+  float* __restrict__ y = tab.y[part];
+  const int64_t N = tab.N[part];
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
   // 8-value pieces of the row (32-bit offsets: K < 2^31, so the base + offset
@@ -141,11 +145,9 @@ void ds_chunks(int64_t K, int S, int& m, int& ceff) {
 }
 
 template <int R>
-hipError_t launch_ds(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int S, int m,
-                     int ceff, float* y, hipStream_t st) {
-  constexpr int ROWS = 4 * R;
-  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS)), block((unsigned)(64 * R * ceff));
-  hipLaunchKernelGGL((k_gemv_dq_seg<R>), grid, block, 0, st, wq, ws, x, N, K, S, m, ceff, y);
+hipError_t launch_ds(const PartTable& tab, int64_t K, const float* x, int S, int m, int ceff, hipStream_t st) {
+  const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
+  hipLaunchKernelGGL((k_gemv_dq_seg<R>), grid, block, 0, st, tab, x, K, S, m, ceff);
   return hipGetLastError();
 }
 
@@ -162,8 +164,8 @@ int dq_seg_chunks(int64_t K, int splits) {
   return ceff <= 16 ? S : 0;
 }
 
-hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
-                              float* y, hipStream_t st) {
+hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
+                                    float* const* y, int64_t K, const float* x, int splits, hipStream_t st) {
   const int S = dq_seg_chunks(K, splits);
   int m, ceff;
   ds_chunks(K, S, m, ceff);
@@ -174,12 +176,19 @@ hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, i
   if (R < 1) R = 1;
   if (R > 4) R = 4;
   while (R > 1 && R * ceff > 16) --R;
+  PartTable tab;
+  if (!make_parts(tab, nparts, wq, ws, y, N, 4 * R)) return hipErrorInvalidValue;
   switch (R) {
-    case 1: return launch_ds<1>(wq, ws, N, K, x, S, m, ceff, y, st);
-    case 2: return launch_ds<2>(wq, ws, N, K, x, S, m, ceff, y, st);
-    case 3: return launch_ds<3>(wq, ws, N, K, x, S, m, ceff, y, st);
-    default: return launch_ds<4>(wq, ws, N, K, x, S, m, ceff, y, st);
+    case 1: return launch_ds<1>(tab, K, x, S, m, ceff, st);
+    case 2: return launch_ds<2>(tab, K, x, S, m, ceff, st);
+    case 3: return launch_ds<3>(tab, K, x, S, m, ceff, st);
+    default: return launch_ds<4>(tab, K, x, S, m, ceff, st);
   }
+}
+
+hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
+                              float* y, hipStream_t st) {
+  return launch_gemv_dq_seg_parts(1, &wq, &ws, &N, &y, K, x, splits, st);
 }
 
 }  // namespace qdg

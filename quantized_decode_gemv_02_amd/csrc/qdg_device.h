@@ -180,6 +180,45 @@ __device__ __forceinline__ float quant_lane4(float4 v, int* h, int* l) {
 
 }  // namespace qdg
 
+// Up to MAX_PARTS weight matrices over one activation in one launch (lane kernel
+// library page, GEMV_PARTS and lk_part_y: q, k and v, or gate and up, side by
+// side).  Workgroups [tile_end[p-1], tile_end[p]) take part p's row tiles; a
+// single matrix is a table of one part.  Passed by value as a kernel argument.
+constexpr int MAX_PARTS = 6;
+struct PartTable {
+  const int8_t* wq[MAX_PARTS];
+  const uint16_t* ws[MAX_PARTS];
+  float* y[MAX_PARTS];
+  int64_t N[MAX_PARTS];
+  int tile_end[MAX_PARTS];
+  int n;
+};
+
+// The part of workgroup `tile` and its first row (a scan of at most six uniform values).
+__device__ __forceinline__ int find_part(const PartTable& t, int tile, int rows, int64_t& o_wg) {
+  int p = 0;
+  while (p + 1 < t.n && tile >= t.tile_end[p]) ++p;
+  o_wg = (int64_t)(tile - (p > 0 ? t.tile_end[p - 1] : 0)) * rows;
+  return p;
+}
+
+// A table of `n` parts of `rows`-row workgroups; false if it overflows an int grid.
+inline bool make_parts(PartTable& t, int n, const int8_t* const* wq, const uint16_t* const* ws, float* const* y,
+                       const int64_t* N, int rows) {
+  int64_t end = 0;
+  t.n = n;
+  for (int p = 0; p < MAX_PARTS; ++p) {
+    t.wq[p] = p < n ? wq[p] : nullptr;
+    t.ws[p] = p < n ? ws[p] : nullptr;
+    t.y[p] = p < n ? y[p] : nullptr;
+    t.N[p] = p < n ? N[p] : 0;
+    if (p < n) end += (N[p] + rows - 1) / rows;
+    if (end >= ((int64_t)1 << 31)) return false;
+    t.tile_end[p] = (int)end;
+  }
+  return true;
+}
+
 // Launchers (one translation unit each); all return the launch's hipError_t.
 namespace qdg {
 hipError_t launch_quantize(int mode, const float* x, int64_t nblocks, int8_t* xq, int8_t* xl, float* xs,
@@ -211,10 +250,15 @@ bool wsplit_fits(int mode, int64_t K, int splits);
 int dq_seg_chunks(int64_t K, int splits);
 hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
                               float* y, hipStream_t st);
+hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
+                                    float* const* y, int64_t K, const float* x, int splits, hipStream_t st);
 void wsplit_shape(int64_t K, int splits, int& rows, int& waves);
 hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                               const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
                               hipStream_t st);
+hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* wq, const uint16_t* const* ws,
+                                    const int64_t* N, float* const* y, int64_t K, const int8_t* xq,
+                                    const int8_t* xl, const float* xs, int splits, hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);

@@ -33,11 +33,9 @@ constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * R
 // same bytes.
 template <int MODE, int R, int U, bool LOCAL>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
-__global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(const int8_t* __restrict__ wq,
-                                                       const uint16_t* __restrict__ ws,
-                                                       const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
-                                                       const float* __restrict__ xs, int64_t N, int64_t K, int S,
-                                                       int m, int ceff, float* __restrict__ y) {
+__global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
+    const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
+    int64_t K, int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;   // rows of the workgroup
   constexpr int LPR = 16, BPS = 8;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -51,7 +49,12 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   const int chunk = c < m ? c : S - 1;
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
-  const int64_t o_wg = (int64_t)blockIdx.x * ROWS;
+  int64_t o_wg;
+  const int part = find_part(tab, (int)blockIdx.x, ROWS, o_wg);
+  const int8_t* __restrict__ wq = tab.wq[part];
+  const uint16_t* __restrict__ ws = tab.ws[part];
+  float* __restrict__ y = tab.y[part];
+  const int64_t N = tab.N[part];
   const int rr = rg * 4 + r;
   const int64_t o = o_wg + rr;
   const bool row_ok = o < N;
@@ -155,18 +158,16 @@ template <int MODE, int R>
 size_t ws_lds_bytes(int64_t K) { return (size_t)(K / QK) * ws_bytes_per_block<MODE, 4 * R>(); }
 
 template <int MODE, int R, bool LOCAL>
-hipError_t launch_ws(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
-                     const float* xs, int S, float* y, hipStream_t st) {
-  constexpr int ROWS = 4 * R;
+hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
+                     hipStream_t st) {
   int m, ceff;
   ws_chunks(K, S, m, ceff);
   static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, 4, LOCAL>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS)), block((unsigned)(64 * R * ceff));
+  const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
   const size_t lds = ws_lds_bytes<MODE, R>(K);
-  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, LOCAL>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, S, m, ceff,
-                     y);
+  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, LOCAL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
   return hipGetLastError();
 }
 
@@ -194,20 +195,20 @@ int ws_groups(int ceff) {
 }
 
 template <int MODE, int R>
-hipError_t launch_ws_local(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
-                           const int8_t* xl, const float* xs, int S, float* y, hipStream_t st) {
-  if (ws_local(R)) return launch_ws<MODE, R, true>(wq, ws, N, K, xq, xl, xs, S, y, st);
-  return launch_ws<MODE, R, false>(wq, ws, N, K, xq, xl, xs, S, y, st);
+hipError_t launch_ws_local(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
+                           int S, hipStream_t st) {
+  if (ws_local(R)) return launch_ws<MODE, R, true>(tab, K, xq, xl, xs, S, st);
+  return launch_ws<MODE, R, false>(tab, K, xq, xl, xs, S, st);
 }
 
 template <int MODE>
-hipError_t launch_ws_mode(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
-                          const int8_t* xl, const float* xs, int S, int R, float* y, hipStream_t st) {
+hipError_t launch_ws_mode(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
+                          int R, hipStream_t st) {
   switch (R) {
-    case 1: return launch_ws_local<MODE, 1>(wq, ws, N, K, xq, xl, xs, S, y, st);
-    case 2: return launch_ws_local<MODE, 2>(wq, ws, N, K, xq, xl, xs, S, y, st);
-    case 3: return launch_ws_local<MODE, 3>(wq, ws, N, K, xq, xl, xs, S, y, st);
-    default: return launch_ws_local<MODE, 4>(wq, ws, N, K, xq, xl, xs, S, y, st);
+    case 1: return launch_ws_local<MODE, 1>(tab, K, xq, xl, xs, S, st);
+    case 2: return launch_ws_local<MODE, 2>(tab, K, xq, xl, xs, S, st);
+    case 3: return launch_ws_local<MODE, 3>(tab, K, xq, xl, xs, S, st);
+    default: return launch_ws_local<MODE, 4>(tab, K, xq, xl, xs, S, st);
   }
 }
 
@@ -233,14 +234,22 @@ void wsplit_shape(int64_t K, int splits, int& rows, int& waves) {
   waves = R * ceff;
 }
 
-hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
-                              const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
-                              hipStream_t st) {
+hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* wq, const uint16_t* const* ws,
+                                    const int64_t* N, float* const* y, int64_t K, const int8_t* xq,
+                                    const int8_t* xl, const float* xs, int splits, hipStream_t st) {
   int m, ceff;
   ws_chunks(K, splits, m, ceff);
   const int R = ws_groups(ceff);
-  if (mode == 1) return launch_ws_mode<1>(wq, ws, N, K, xq, xl, xs, splits, R, y, st);
-  return launch_ws_mode<2>(wq, ws, N, K, xq, xl, xs, splits, R, y, st);
+  PartTable tab;
+  if (!make_parts(tab, nparts, wq, ws, y, N, 4 * R)) return hipErrorInvalidValue;
+  if (mode == 1) return launch_ws_mode<1>(tab, K, xq, xl, xs, splits, R, st);
+  return launch_ws_mode<2>(tab, K, xq, xl, xs, splits, R, st);
+}
+
+hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                              const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                              hipStream_t st) {
+  return launch_gemv_wsplit_parts(mode, 1, &wq, &ws, &N, &y, K, xq, xl, xs, splits, st);
 }
 
 }  // namespace qdg

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -225,6 +225,40 @@ def test_swiglu_quantize_validation():
     assert call(u=A + 8) == EALIGN
     assert call(h=A + 4) == EALIGN
     assert call(mode=2, xl=A + 4) == EALIGN
+
+
+def test_parts_validation():
+    f = lib.qdg_gemv_q8_parts
+    Part = q._Part
+
+    def table(n=3, wq=A, ws=A, N=64, y=A):
+        arr = (Part * max(n, 1))()
+        for i in range(max(n, 1)):
+            arr[i] = Part(wq, ws, N, y)
+        return arr
+
+    def call(mode=1, parts=None, n=3, K=8192, x=None, xq=A, xl=None, xs=A, S=4, **kw):
+        arr = parts if parts is not None else table(n, **kw)
+        return f(mode, ctypes.cast(arr, P), n, K, P(x), P(xq), P(xl), P(xs), S, None)
+
+    assert f(1, None, 1, 8192, None, P(A), None, P(A), 4, None) == EINVAL
+    assert call(mode=3) == EINVAL
+    assert call(n=0) == ESHAPE
+    assert call(n=7) == ESHAPE
+    assert call(wq=None) == EINVAL
+    assert call(y=None) == EINVAL
+    assert call(x=A) == EINVAL                          # quantized modes take words, not x
+    assert call(mode=2) == EINVAL                       # TwoPass needs xl
+    assert call(mode=0, xq=None, xs=None) == EINVAL     # Dequant needs x
+    assert call(N=0) == ESHAPE
+    assert call(K=500) == ESHAPE
+    assert call(wq=A + 8) == EALIGN
+    assert call(ws=A + 1) == EALIGN
+    assert call(xq=A + 4) == EALIGN
+    assert call(S=1) == EMODE                           # no split: nothing to combine in a workgroup
+    assert call(S=64) == EMODE                          # more chunk waves than a workgroup holds
+    assert call(mode=2, xl=A, K=65536, S=16) == EMODE   # the staged row exceeds the LDS budget
+    assert call(mode=0, x=A + 4, xq=None, xs=None) == EALIGN
 
 
 def test_stream_read_validation():

@@ -483,3 +483,44 @@ def test_gemv_argmax_epilogue(mode, N, K):
         got = host(y)
         np.testing.assert_array_equal(got, host(y_ref))
         assert int(host(idx)[0]) == int(oracle.argmax(got)[0]) == a
+
+
+# ---------------------------------------------------------------- several matrices in one launch
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("Ns,K,S", [((4096, 1024, 1024), 4096, 4), ((37, 1, 200), 1600, 2),
+                                    ((12288, 12288), 4096, 2), ((5, 7, 9, 11, 13, 15), 544, 4),
+                                    ((300,), 25600, 5), ((64, 65), 8192, 8)])
+def test_parts_match_single_calls(mode, Ns, K, S):
+    """qdg_gemv_q8_parts: every part's output is bit-identical to the single-matrix
+    call with the same splits, and (quantized modes) to the oracle's chunk
+    partials and ascending combine; Dequant within its tolerance."""
+    announce(f"gemv_q8_parts mode={mode} Ns={Ns} K={K} S={S}")
+    x = workloads.batch_activation(1, K, 31 + K, True, 32 + K)
+    mats = [workloads.weights(n, K, 100 * i + n, 100 * i + n + 1) for i, n in enumerate(Ns)]
+    dev_m = [(dev(wq), dev(ws)) for wq, ws in mats]
+    ys = [torch.full((n,), float("nan"), dtype=torch.float32, device=DEV) for n in Ns]
+    if mode == 0:
+        xd = dev(x.reshape(1, K))
+        q.gemv_q8_parts(0, [(w, s, y) for (w, s), y in zip(dev_m, ys)], x=xd, splits=S)
+    else:
+        xq, xl, xs = quantize_gpu(mode, x)
+        q.gemv_q8_parts(mode, [(w, s, y) for (w, s), y in zip(dev_m, ys)], xq=xq, xl=xl, xs=xs, splits=S)
+        oq, ol, os_ = oracle.quantize(mode, x)
+    for i, n in enumerate(Ns):
+        single = torch.empty((1, n), dtype=torch.float32, device=DEV)
+        wsp = q.sk_workspace(n, S)
+        if mode == 0:
+            q.gemv_q8_fused(0, dev_m[i][0], dev_m[i][1], single, xd, S, wsp)
+        else:
+            q.gemv_q8_sk(mode, dev_m[i][0], dev_m[i][1], single, xq, xl, xs, S, wsp)
+        got = host(ys[i]).reshape(1, n)
+        assert got.tobytes() == host(single).tobytes(), i
+        rows = np.arange(0, n, 7) if n > 2000 else np.arange(n)
+        wq, ws = mats[i]
+        if mode == 0:
+            Y, tn = oracle.reference_f64(0, wq[rows], ws[rows], x=x, nthreads=8)
+            assert oracle.within_tolerance(got[:, rows], Y, tn).all()
+        else:
+            want = oracle.combine(oracle.gemv_split(mode, wq[rows], ws[rows], oq, ol, os_, S, nthreads=8))
+            np.testing.assert_array_equal(got[:, rows], want)
