@@ -65,7 +65,8 @@ enum {
 };
 
 /* Limits. */
-#define QDG_MAX_B 16        /* activation rows per call                              */
+#define QDG_MAX_B 64        /* activation rows per call (above 16: K % 256 == 0,     */
+                            /* ws 16-byte aligned)                                     */
 #define QDG_MAX_SPLITS 64   /* split-K chunks                                        */
 
 typedef void *qdg_stream; /* a hipStream_t */
@@ -120,7 +121,9 @@ int qdg_quantize_act(int mode, const float *x, int64_t B, int64_t K,
  *               exact int32 block dots; step g goes into partial g mod 4, each
  *               partial takes its blocks in ascending order from +0, and the
  *               result is (P0 + P2) + (P1 + P3).  1 <= B <= QDG_MAX_B (B > 1
- *               runs on int8 MFMA and sums every row exactly as B == 1 does).
+ *               runs on int8 MFMA and sums every row exactly as B == 1 does;
+ *               B > 16, a prefill chunk, needs K a multiple of 256 and ws
+ *               16-byte aligned, else QDG_EMODE).
  *
  * splits == 1: out is y [B][N].  splits > 1 (quantized modes): out is
  * partials [splits][B][N]; chunk s covers the blocks the QWEN38 page's chunk

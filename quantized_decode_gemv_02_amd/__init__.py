@@ -29,7 +29,7 @@ import os
 
 DEQUANT, INT8ACT, TWOPASS = 0, 1, 2
 QK = 32
-MAX_B = 16
+MAX_B = 64
 MAX_SPLITS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

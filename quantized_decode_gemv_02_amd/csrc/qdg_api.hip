@@ -78,6 +78,9 @@ int qdg_gemv_q8(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64
   if (xl && !aligned(xl, 16)) return QDG_EALIGN;
   if (xs && !aligned(xs, 4)) return QDG_EALIGN;
   if (mode == QDG_DEQUANT && (B != 1 || splits != 1)) return QDG_EMODE;
+  // more than 16 activation rows run on the LDS-direct MFMA layout: whole 8-block
+  // steps (K a multiple of 256) and 16-byte weight-scale words
+  if (B > 16 && ((K / qdg::QK) % 8 != 0 || !aligned(ws, 16))) return QDG_EMODE;
   const hipStream_t st = as_stream(stream);
   if (mode == QDG_DEQUANT) return hip_status(qdg::launch_gemv_dequant(wq, ws, N, K, x, out, st));
   if (B == 1) return hip_status(qdg::launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, splits, out, st));

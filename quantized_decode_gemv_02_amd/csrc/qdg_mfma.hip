@@ -280,26 +280,26 @@ hipError_t launch_mp(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
 // order, so lane (r4 = l/16, j = l%16) fetches global chunk j ^ row to land it
 // in place; SX [16][8] activation scales; SG [rows][8] weight scales; JUNK for
 // the placeholders.
-template <int MODE, int WV, int TPW>
+template <int MODE, int WV, int TPW, int AT = 1>
 struct DSlot {
   static constexpr int TG = WV / 4;  // tile groups
   static constexpr int DROWS = 16 * TG * TPW;
   static constexpr int W = 0;
-  static constexpr int A = W + DROWS * 256;
-  static constexpr int L = A + 16 * 256;
-  static constexpr int SX = L + (MODE == 2 ? 16 * 256 : 0);
-  static constexpr int SG = SX + 16 * STEP * 4;
+  static constexpr int A = W + DROWS * 256;                 // AT activation tiles of 16 rows
+  static constexpr int L = A + AT * 16 * 256;
+  static constexpr int SX = L + (MODE == 2 ? AT * 16 * 256 : 0);
+  static constexpr int SG = SX + AT * 16 * STEP * 4;
   static constexpr int NG = (DROWS * 16 + 1023) / 1024;  // weight-scale loads (1 KiB each)
   static constexpr int JUNK = SG + NG * 1024;
   static constexpr int BYTES = JUNK + 64 * 4;
-  static constexpr int JOBS = (MODE == 2 ? 8 : 4) + 2 + NG;
+  static constexpr int JOBS = AT * ((MODE == 2 ? 8 : 4) + 2) + NG;
   static constexpr int AUX = (JOBS + WV - 1) / WV;  // aux loads a wave a step
   static constexpr int WLOADS = DROWS / (4 * WV);   // weight loads a wave a step
   static constexpr int DMA_LOADS = WLOADS + AUX;
   static_assert(DROWS % (4 * WV) == 0, "whole weight loads per wave");
 };
-template <int MODE, int WV, int TPW, int P>
-constexpr int dma_lds_bytes() { return P * DSlot<MODE, WV, TPW>::BYTES; }
+template <int MODE, int WV, int TPW, int P, int AT = 1>
+constexpr int dma_lds_bytes() { return P * DSlot<MODE, WV, TPW, AT>::BYTES; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -327,16 +327,18 @@ __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int MODE, int WV, int TPW, int P>
+// AT activation tiles of 16 rows (B up to 16*AT): every weight step is
+// multiplied against all of them, so the weights are read once for the batch.
+template <int MODE, int WV, int TPW, int P, int AT = 1>
 __global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restrict__ wq,
                                                           const uint16_t* __restrict__ ws,
                                                           const int8_t* __restrict__ xq,
                                                           const int8_t* __restrict__ xl,
                                                           const float* __restrict__ xs, int64_t N, int64_t K, int B,
                                                           int S, float* __restrict__ out) {
-  using SL = DSlot<MODE, WV, TPW>;
+  using SL = DSlot<MODE, WV, TPW, AT>;
   constexpr int DROWS = SL::DROWS, TG = SL::TG;
-  static_assert(SL::BYTES >= WV * TPW * 4 * 64 * 4, "the final reduction reuses slot 0");
+  static_assert(P * SL::BYTES >= WV * TPW * AT * 4 * 64 * 4, "the final reduction reuses the slots");
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -363,25 +365,29 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restr
     wcb[m] = c >> 1;
   }
 
-  // one aux job (uniform over the wave): 0..3 high words of rows 4k.., 4..7 low
-  // words (TwoPass), then 2 activation-scale loads, then NG weight-scale loads
-  constexpr int NW_JOBS = MODE == 2 ? 8 : 4;
+  // one aux job (uniform over the wave): 4*AT high-word loads (tile at = job/4,
+  // rows 4*(job%4)..), 4*AT low-word loads (TwoPass), then 2 activation-scale
+  // loads a tile, then NG weight-scale loads
+  constexpr int NW_JOBS = AT * (MODE == 2 ? 8 : 4);
   auto issue_job = [&](int job, int blk0, unsigned char* slot) {
     if (job < NW_JOBS) {
-      const int q = job & 3;
-      const int arow = 4 * q + r4;
+      const bool low = MODE == 2 && job >= 4 * AT;
+      const int jj = low ? job - 4 * AT : job;
+      const int at = jj >> 2, q = jj & 3;
+      const int arow = 4 * q + r4;  // row within the tile
       const int ac = (j ^ arow) & 15;
-      const int8_t* src = (MODE == 2 && job >= 4) ? xl : xq;
+      const int8_t* src = low ? xl : xq;
       const int blk = min(blk0 + (ac >> 1), g1 - 1);
-      dma<16, 0>(src + (int64_t)min(arow, B - 1) * K + (int64_t)blk * QK + 16 * (ac & 1),
-                 slot + ((MODE == 2 && job >= 4) ? SL::L : SL::A) + q * 1024);
-    } else if (job < NW_JOBS + 2) {
+      dma<16, 0>(src + (int64_t)min(16 * at + arow, B - 1) * K + (int64_t)blk * QK + 16 * (ac & 1),
+                 slot + (low ? SL::L : SL::A) + at * 4096 + q * 1024);
+    } else if (job < NW_JOBS + 2 * AT) {
       const int sq = job - NW_JOBS;
-      const int sidx = 64 * sq + lane;  // [t][k] = sidx
-      dma<4, 0>(xs + (int64_t)min(sidx >> 3, B - 1) * nb + min(blk0 + (sidx & 7), g1 - 1),
-                slot + SL::SX + sq * 256);
+      const int at = sq >> 1, sh = sq & 1;
+      const int sidx = 64 * sh + lane;  // [t][k] = sidx within the tile
+      dma<4, 0>(xs + (int64_t)min(16 * at + (sidx >> 3), B - 1) * nb + min(blk0 + (sidx & 7), g1 - 1),
+                slot + SL::SX + at * 512 + sh * 256);
     } else if (job < SL::JOBS) {
-      const int gq = job - NW_JOBS - 2;
+      const int gq = job - NW_JOBS - 2 * AT;
       int64_t o = o_wg + ((64 * gq + lane) % DROWS);
       if (o >= N) o = N - 1;
       // steps are whole when this path runs; the clamp keeps the look-ahead in bounds
@@ -415,12 +421,14 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restr
 #pragma unroll
   for (int m = 0; m < TPW; ++m) sg_rd[m] = SL::SG + (16 * (tg + TG * m) + col) * 16;
 
-  // partial `res` of (t = 4*grp + i, o = o_wg + 16*(tg + TG*m) + col)
-  float p[TPW][4];
+  // partial `res` of (t = 16*at + 4*grp + i, o = o_wg + 16*(tg + TG*m) + col)
+  float p[TPW][AT][4];
 #pragma unroll
   for (int m = 0; m < TPW; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][at][i] = 0.0f;
   // an empty chunk (K < 512 with several chunks) loads nothing: its partials stay +0
   if (nsteps > 0) {
 #pragma unroll
@@ -433,66 +441,78 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restr
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = res + 4 * h;
-      const long ak = *(const long*)(slot + a_rd[h]);
-      long lk = 0;
-      if constexpr (MODE == 2) lk = *(const long*)(slot + a_rd[h] + (SL::L - SL::A));
-      float sig[4];
+      long ak[AT], lk[AT];
+      float sig[AT][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sig[i] = *(const float*)(slot + sx_rd + (i * STEP + k) * 4);
+      for (int at = 0; at < AT; ++at) {
+        ak[at] = *(const long*)(slot + a_rd[h] + at * 4096);
+        lk[at] = 0;
+        if constexpr (MODE == 2) lk[at] = *(const long*)(slot + a_rd[h] + at * 4096 + (SL::L - SL::A));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sig[at][i] = *(const float*)(slot + sx_rd + at * 512 + (i * STEP + k) * 4);
+      }
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
         const long wk = *(const long*)(slot + w_rd[m][h]);
-        const v4i D = mfma16x16x32(ak, wk);
-        v4i E = {0, 0, 0, 0};
-        if constexpr (MODE == 2) E = mfma16x16x32(lk, wk);
         const float sgm = half_bits_to_float(*(const unsigned short*)(slot + sg_rd[m] + 2 * k));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ta, tb;
-          q8_term<MODE>(sgm, sig[i], D[i], E[i], ta, tb);
-          p[m][i] = __fmaf_rn(ta, tb, p[m][i]);
+        for (int at = 0; at < AT; ++at) {
+          const v4i D = mfma16x16x32(ak[at], wk);
+          v4i E = {0, 0, 0, 0};
+          if constexpr (MODE == 2) E = mfma16x16x32(lk[at], wk);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ta, tb;
+            q8_term<MODE>(sgm, sig[at][i], D[i], E[i], ta, tb);
+            p[m][at][i] = __fmaf_rn(ta, tb, p[m][at][i]);
+          }
         }
       }
     }
   }
   // the four partials of each output meet in a fixed order: (P0 + P2) + (P1 + P3)
   wait_and_barrier<0>();  // every load has landed and every wave is done with the slots
-  float* red = (float*)lds;  // [wave][m][i][lane]
+  float* red = (float*)lds;  // [wave][m][at][i][lane]
 #pragma unroll
   for (int m = 0; m < TPW; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wave * TPW + m) * 4 + i) * 64 + lane] = p[m][i];
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(((wave * TPW + m) * AT + at) * 4 + i) * 64 + lane] = p[m][at][i];
   wait_and_barrier<0>();
   if (res == 0) {
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
       const int64_t oo = o_wg + 16 * (tg + TG * m) + col;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = grp * 4 + i;
-        float q[4];
+      for (int at = 0; at < AT; ++at) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) q[r] = red[(((4 * tg + r) * TPW + m) * 4 + i) * 64 + lane];
-        const float y = __fadd_rn(__fadd_rn(q[0], q[2]), __fadd_rn(q[1], q[3]));
-        if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * at + grp * 4 + i;
+          float q[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q[r] = red[((((4 * tg + r) * TPW + m) * AT + at) * 4 + i) * 64 + lane];
+          const float y = __fadd_rn(__fadd_rn(q[0], q[2]), __fadd_rn(q[1], q[3]));
+          if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+        }
       }
     }
   }
 }
 
-template <int MODE, int WV, int TPW, int P>
+template <int MODE, int WV, int TPW, int P, int AT = 1>
 hipError_t launch_dma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
                       const int8_t* xl, const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
-  constexpr int rows = DSlot<MODE, WV, TPW>::DROWS;
+  constexpr int rows = DSlot<MODE, WV, TPW, AT>::DROWS;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)splits), block(64 * WV);
-  constexpr int lds = dma_lds_bytes<MODE, WV, TPW, P>();
+  constexpr int lds = dma_lds_bytes<MODE, WV, TPW, P, AT>();
   static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   // above 64 KiB of LDS the kernel's dynamic-LDS limit is raised (once)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, WV, TPW, P>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, WV, TPW, P, AT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, WV, TPW, P>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B,
-                     splits, out);
+  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, WV, TPW, P, AT>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K,
+                     (int)B, splits, out);
   return hipGetLastError();
 }
 
@@ -518,6 +538,25 @@ DmaShape dma_shape() {
 template <int MODE>
 hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
                     const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
+  // more than 16 activation rows: 2 or 4 activation tiles against each weight
+  // step (the fast path's layout; the caller has checked its conditions)
+  if (B > 16) {
+    // QDG_MFMA_WIDE = "WV,TPW,P" among the compiled shapes (read on every call, for sweeps)
+    int wv = 8, tpw = 2, ring = 2;
+    if (const char* e = getenv("QDG_MFMA_WIDE")) sscanf(e, "%d,%d,%d", &wv, &tpw, &ring);
+#define QDG_WIDE(WV_, TPW_, P_)                                                                   \
+  if (wv == WV_ && tpw == TPW_ && ring == P_) {                                                    \
+    if (B <= 32) return launch_dma<MODE, WV_, TPW_, P_, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st); \
+    return launch_dma<MODE, WV_, TPW_, P_, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);            \
+  }
+    QDG_WIDE(8, 1, 3)
+    QDG_WIDE(4, 2, 3)
+    QDG_WIDE(8, 2, 3)
+    QDG_WIDE(4, 1, 3)
+#undef QDG_WIDE
+    if (B <= 32) return launch_dma<MODE, 8, 2, 2, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+    return launch_dma<MODE, 8, 2, 2, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+  }
   // the fast path needs whole steps (K/32 a multiple of 8) and 16-byte weight-scale words
   if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && !getenv("QDG_MFMA_GENERAL")) {
     const DmaShape d = dma_shape();

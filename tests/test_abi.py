@@ -68,7 +68,9 @@ def test_gemv_validation():
     assert gemv(K=16) == ESHAPE
     assert gemv(N=0) == ESHAPE
     assert gemv(B=0) == ESHAPE
-    assert gemv(B=17) == ESHAPE
+    assert gemv(B=65) == ESHAPE
+    assert gemv(B=17, K=544) == EMODE                         # prefill chunks need K % 256 == 0
+    assert gemv(B=17, K=512, ws=A + 2) == EMODE               # ... and 16-byte weight-scale words
     assert gemv(S=0) == ESHAPE
     assert gemv(S=65) == ESHAPE
     assert gemv(wq=A + 8) == EALIGN
@@ -110,7 +112,7 @@ def test_combine_argmax_blockdots_validation():
     assert bd(2, P(A), 4, 64, P(A), None, 1, P(A), P(A), None) == EINVAL
     assert bd(1, P(A), 4, 64, P(A), None, 1, P(A), P(A), None) == EINVAL
     assert bd(1, P(A), 4, 60, P(A), None, 1, P(A), None, None) == ESHAPE
-    assert bd(1, P(A), 4, 64, P(A), None, 17, P(A), None, None) == ESHAPE
+    assert bd(1, P(A), 4, 64, P(A), None, 65, P(A), None, None) == ESHAPE
 
 
 def test_fused_validation():

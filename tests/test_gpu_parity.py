@@ -181,6 +181,31 @@ def test_batched_bit_exact_and_batch_invariant(mode, B, N, K, S):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,N,K,S", [(64, 100, 5120, 1), (17, 33, 256, 1), (32, 64, 2048, 2), (33, 65, 512, 1),
+                                     (48, 130, 8192, 3), (64, 16, 256, 2), (40, 300, 25600, 4)])
+def test_prefill_chunk_bit_exact_and_batch_invariant(mode, B, N, K, S):
+    """More than 16 activation rows (a prefill chunk): every weight step meets 2 or
+    4 activation tiles.  Bit-exact with the oracle; each row equals the batch-1
+    kernel's result, and the first 16 rows equal a 16-row call."""
+    announce(f"prefill chunk mode={mode} B={B} N={N} K={K} S={S}")
+    wq, ws, x = _quant_case(N, K, B, 13 * B + N + K)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    xq, xl, xs = quantize_gpu(mode, x)
+    wqd, wsd = dev(wq), dev(ws)
+    got = host(gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs))
+    want = (oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=8) if S == 1
+            else oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    np.testing.assert_array_equal(got, want)
+    for t in (0, 16, B - 1):
+        y1 = host(gemv_gpu(mode, wqd, wsd, 1, N, splits=S, xq=xq[t:t + 1].contiguous(),
+                           xl=None if xl is None else xl[t:t + 1].contiguous(), xs=xs[t:t + 1].contiguous()))
+        np.testing.assert_array_equal(got[:, t] if S > 1 else got[t], y1[:, 0] if S > 1 else y1[0])
+    y16 = host(gemv_gpu(mode, wqd, wsd, 16, N, splits=S, xq=xq[:16].contiguous(),
+                        xl=None if xl is None else xl[:16].contiguous(), xs=xs[:16].contiguous()))
+    np.testing.assert_array_equal(got[:, :16] if S > 1 else got[:16], y16)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B", [1, 16])
 def test_weight_scales_at_a_two_byte_offset(mode, B):
     """The header asks only 2-byte alignment of ws: scales that start 2 bytes past a
