@@ -298,6 +298,25 @@ int qdg_gemv_q8_parts(int mode, const qdg_part *parts, int nparts, int64_t K, co
                       qdg_stream stream);
 
 /*
+ * The gate and up projections of one activation row with the SwiGLU and the
+ * quantizer as the epilogue, in one launch (lane kernel library page, GLU,
+ * lk_gemv_glu with a quantized output; lk_act): g = Wg x and u = Wu x as
+ * qdg_gemv_q8 computes them (splits 1), h = silu(g) * u as qdg_swiglu_quantize
+ * computes it, and (hq, hl, hs) = h quantized in the same mode -- the words the
+ * down projection reads.  Bit-identical to those three calls; g and u never
+ * reach memory.  QDG_INT8ACT or QDG_TWOPASS (hl exactly under TwoPass).
+ * Device pointers: wg, wu int8 [F][K] (16-byte aligned); sg, su binary16 bits
+ * [F][K/32]; xq, xl [K], xs [K/32] (from qdg_quantize_act or a producer); h f32
+ * [F] or NULL (16-byte aligned); hq, hl [F]; hs [F/32].  F a positive multiple
+ * of 32 (one quantized block per 32 outputs); K a multiple of 32 whose
+ * activation row and 64 rows of scales fit the LDS budget (K up to 13184 for
+ * QDG_TWOPASS, 15776 for QDG_INT8ACT), else QDG_EMODE.
+ */
+int qdg_gemv_glu_q8(int mode, const int8_t *wg, const uint16_t *sg, const int8_t *wu,
+                    const uint16_t *su, int64_t F, int64_t K, const int8_t *xq, const int8_t *xl,
+                    const float *xs, float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
+
+/*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
  * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,
  * under QDG_TWOPASS, dl[t][o][g] with xl (dl must be NULL for QDG_INT8ACT).

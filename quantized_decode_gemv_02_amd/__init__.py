@@ -74,6 +74,7 @@ _SIGS = {
     "qdg_rmsnorm_max_k": ([], _I64),
     "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
+    "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -197,6 +198,25 @@ def swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> None:
 
 def bind_swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> Bound:
     return Bound("qdg_swiglu_quantize", *_swiglu_args(mode, g, u, h, xq, xl, xs))
+
+
+def _glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs):
+    F, K = wg.shape
+    if tuple(wu.shape) != (F, K):
+        raise ValueError("gemv_glu_q8: gate and up must have the same shape")
+    return (mode, _ptr(wg, _i8(), "wg"), _ptr(sg, _scales(), "sg"), _ptr(wu, _i8(), "wu"), _ptr(su, _scales(), "su"),
+            F, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(h, _f32(), "h"),
+            _ptr(hq, _i8(), "hq"), _ptr(hl, _i8(), "hl"), _ptr(hs, _f32(), "hs"), _stream())
+
+
+def gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> None:
+    """Gate and up GEMVs with the SwiGLU and quantizer epilogue: ``(hq, hl, hs)`` is
+    ``silu(Wg x) * (Wu x)`` quantized (``h``, optional, the f32 SwiGLU output)."""
+    _check("qdg_gemv_glu_q8", _lib.qdg_gemv_glu_q8(*_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs)))
+
+
+def bind_gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> Bound:
+    return Bound("qdg_gemv_glu_q8", *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs))
 
 
 MAX_PARTS = 6

@@ -221,6 +221,21 @@ int qdg_gemv_q8_parts(int mode, const qdg_part* parts, int nparts, int64_t K, co
       qdg::launch_gemv_wsplit_parts(mode, nparts, wq, ws, N, y, K, xq, xl, xs, splits, as_stream(stream)));
 }
 
+int qdg_gemv_glu_q8(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
+                    int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq, int8_t* hl,
+                    float* hs, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!wg || !sg || !wu || !su || !xq || !xs || !hq || !hs) return QDG_EINVAL;
+  if ((mode == QDG_TWOPASS) != (xl != nullptr) || (mode == QDG_TWOPASS) != (hl != nullptr)) return QDG_EINVAL;
+  if (!shape_ok(F, K) || F % qdg::QK != 0 || F / qdg::QK >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(sg, 2) || !aligned(su, 2) || !aligned(xq, 16) ||
+      (xl && !aligned(xl, 16)) || !aligned(xs, 4) || (h && !aligned(h, 16)) || !aligned(hq, 4) ||
+      (hl && !aligned(hl, 4)) || !aligned(hs, 4))
+    return QDG_EALIGN;
+  if (!qdg::glu_fits(mode, K)) return QDG_EMODE;
+  return hip_status(qdg::launch_gemv_glu(mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, as_stream(stream)));
+}
+
 int qdg_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, void* workspace, size_t workspace_bytes,
                qdg_stream stream) {
   if (!y || !idx || !workspace) return QDG_EINVAL;

@@ -178,7 +178,60 @@ __device__ __forceinline__ float quant_lane4(float4 v, int* h, int* l) {
   return s;
 }
 
-}  // namespace qdg
+// SwiGLU of one value (lane kernel library page, lk_act: silu(g) = g / (1 + e^-g),
+// times u): evaluated in binary64 from the binary32 operands and rounded once.
+// Shared by the SwiGLU producer and the gate/up GEMV epilogue, so the two give
+// the same bits.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const double gd = (double)g;
+  return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+// One wave's chunk partial of four rows (16 lanes a row, a lane pair a block),
+// the lane kernel library page's row order restricted to blocks [g0, g1): block
+// g's step p <- fma(a, b, p) goes into partial g mod 4 (lane pair g mod 4 of the
+// row, blocks j and j+4 of each 8-block step), each partial ascending from +0,
+// then (P0 + P2) + (P1 + P3), returned in lane 0 of the row (the other lanes
+// hold partial sums).  wrow points at the lane's row plus 16*hf; lq, ll and lsx
+// hold the activation words and scales by absolute block, my_sg the row's
+// weight scales by absolute block.  wcur holds the first U steps' weights,
+// requested by the caller (so they can be in flight across its staging).
+template <int MODE, int U>
+__device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
+                                            const uint16_t* my_sg, int g0, int g1, int j, int hf, int4 (&wcur)[U]) {
+  constexpr int BPS = 8;
+  const int nwb = g1 - g0;
+  const int ngroups = ((nwb + BPS - 1) / BPS + U - 1) / U;
+  float p = 0.0f;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    int4 wnxt[U];
+    const bool more = gi + 1 < ngroups;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = g0 + ((gi + 1) * U + u) * BPS + j;
+      wnxt[u] = more && b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int bl = (gi * U + u) * BPS + j;  // block within the chunk
+      const bool ok = bl < nwb;
+      const int blc = g0 + (ok ? bl : 0);
+      const int4 a = *(const int4*)(lq + blc * QK + hf * 16);
+      const int d = block_dot_pair(wcur[u], a);
+      int e = 0;
+      if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
+      float ta, tb;
+      q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
+      p = ok ? __fmaf_rn(ta, tb, p) : p;
+      const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
+      p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
+  }
+  const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
+  return __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+}
 
 // Up to MAX_PARTS weight matrices over one activation in one launch (lane kernel
 // library page, GEMV_PARTS and lk_part_y: q, k and v, or gate and up, side by
@@ -220,7 +273,6 @@ inline bool make_parts(PartTable& t, int n, const int8_t* const* wq, const uint1
 }
 
 // Launchers (one translation unit each); all return the launch's hipError_t.
-namespace qdg {
 hipError_t launch_quantize(int mode, const float* x, int64_t nblocks, int8_t* xq, int8_t* xl, float* xs,
                            hipStream_t st);
 hipError_t launch_gemv_dot4(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
@@ -262,6 +314,10 @@ hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* w
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
+bool glu_fits(int mode, int64_t K);
+hipError_t launch_gemv_glu(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                           int64_t F, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h,
+                           int8_t* hq, int8_t* hl, float* hs, hipStream_t st);
 hipError_t launch_swiglu_quant(int mode, const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq,
                                int8_t* xl, float* xs, hipStream_t st);
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st);

@@ -120,11 +120,6 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant(const float* x, const floa
   }
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const double gd = (double)g;
-  return (float)(gd / (1.0 + exp(-gd)) * (double)u);
-}
-
 // Eight lanes a 32-value block, four values a lane, as k_quantize.  h may be g or u.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_swiglu_quant(const float* g, const float* u, float* h,

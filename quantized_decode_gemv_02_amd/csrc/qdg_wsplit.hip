@@ -62,8 +62,6 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
   const int nwb = g1 - g0;
-  const int nsteps = (nwb + BPS - 1) / BPS;
-  const int ngroups = (nsteps + U - 1) / U;
 
   int8_t* lq = (int8_t*)lds;                                               // [nb][32]
   int8_t* ll = lq + nb * QK;                                               // [nb][32] (TwoPass)
@@ -101,36 +99,8 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     __syncthreads();
   }
 
-  float p = 0.0f;
-  for (int gi = 0; gi < ngroups; ++gi) {
-    int4 wnxt[U];
-    const bool more = gi + 1 < ngroups;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = g0 + ((gi + 1) * U + u) * BPS + j;
-      wnxt[u] = more && b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bl = (gi * U + u) * BPS + j;  // block within the chunk
-      const bool ok = bl < nwb;
-      const int blc = g0 + (ok ? bl : 0);
-      const int4 a = *(const int4*)(lq + blc * QK + hf * 16);
-      const int d = block_dot_pair(wcur[u], a);
-      int e = 0;
-      if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
-      float ta, tb;
-      q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
-      p = ok ? __fmaf_rn(ta, tb, p) : p;
-      const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
-      p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
-  }
-  // (P0 + P2) + (P1 + P3): the chunk's partial of the row, in lane 0 of the row
-  const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
-  const float yv = __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+  // the chunk's partial of the row, in lane 0 of the row
+  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, wcur);
   if (li == 0) lpart[wave][r] = yv;
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {

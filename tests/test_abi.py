@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -261,6 +261,27 @@ def test_parts_validation():
     assert call(S=64) == EMODE                          # more chunk waves than a workgroup holds
     assert call(mode=2, xl=A, K=65536, S=16) == EMODE   # the staged row exceeds the LDS budget
     assert call(mode=0, x=A + 4, xq=None, xs=None) == EALIGN
+
+
+def test_glu_validation():
+    f = lib.qdg_gemv_glu_q8
+
+    def call(mode=1, wg=A, sg=A, wu=A, su=A, F=128, K=4096, xq=A, xl=None, xs=A, h=None, hq=A, hl=None, hs=A):
+        return f(mode, P(wg), P(sg), P(wu), P(su), F, K, P(xq), P(xl), P(xs), P(h), P(hq), P(hl), P(hs), None)
+
+    assert call(mode=0) == EINVAL
+    assert call(wu=None) == EINVAL
+    assert call(hq=None) == EINVAL
+    assert call(mode=2, xl=A) == EINVAL                 # TwoPass needs hl too
+    assert call(mode=1, hl=A) == EINVAL
+    assert call(F=100) == ESHAPE                        # one quantized block per 32 outputs
+    assert call(F=0) == ESHAPE
+    assert call(K=4100) == ESHAPE
+    assert call(wg=A + 8) == EALIGN
+    assert call(h=A + 4) == EALIGN
+    assert call(hs=A + 2) == EALIGN
+    assert call(mode=2, xl=A, hl=A, K=13216) == EMODE   # the activation and 64 rows of scales exceed LDS
+    assert call(mode=1, K=15808) == EMODE
 
 
 def test_stream_read_validation():

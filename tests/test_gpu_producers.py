@@ -226,3 +226,44 @@ def test_producer_words_drive_the_gemv(mode):
     oq, ol, os_ = oracle.quantize(mode, host(h))
     want = oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_)
     assert np.array_equal(host(y).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("F,K", [(32, 32), (64, 544), (12288, 4096), (96, 13184), (160, 15776)])
+def test_glu_matches_the_three_calls(mode, F, K):
+    """qdg_gemv_glu_q8 (gate and up GEMVs with the SwiGLU and quantizer epilogue)
+    against two qdg_gemv_q8 calls and qdg_swiglu_quantize, bit for bit, and the
+    oracle: g and u bit-exact, h within one ulp, words bit-exact on the kernel's h."""
+    if mode == 2 and K > 13184:
+        pytest.skip("the TwoPass activation row and scales exceed the LDS budget at this K")
+    announce(f"gemv_glu mode={mode} F={F} K={K}")
+    wg, sg = workloads.weights(F, K, 71 + K, 72 + K)
+    wu, su = workloads.weights(F, K, 73 + K, 74 + K)
+    x = workloads.batch_activation(1, K, 75 + K, True, 76 + K)
+    dwg, dsg = dev(wg), dev(sg.view(np.int16))
+    dwu, dsu = dev(wu), dev(su.view(np.int16))
+    xq, xl, xs = words(mode, 1, K)
+    q.quantize_act(mode, dev(x), xq, xl, xs)
+    h = torch.empty((F,), dtype=torch.float32, device=DEV)
+    hq, hl, hs = words(mode, 1, F)
+    q.gemv_glu_q8(mode, dwg, dsg, dwu, dsu, xq, xl, xs, hq, hl, hs, h=h)
+    # the three calls
+    g = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    u = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    q.gemv_q8(mode, dwg, dsg, g, xq=xq, xl=xl, xs=xs)
+    q.gemv_q8(mode, dwu, dsu, u, xq=xq, xl=xl, xs=xs)
+    h2 = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    hq2, hl2, hs2 = words(mode, 1, F)
+    q.swiglu_quantize(mode, g, u, h2, hq2, hl2, hs2)
+    assert torch.equal(h.view(torch.int32), h2.view(-1).view(torch.int32))
+    assert torch.equal(hq.view(-1), hq2.view(-1)) and torch.equal(hs.view(torch.int32).view(-1), hs2.view(torch.int32).view(-1))
+    if mode == 2:
+        assert torch.equal(hl.view(-1), hl2.view(-1))
+    # the oracle
+    oq, ol, os_ = oracle.quantize(mode, x)
+    og = oracle.gemv(mode, wg, sg, xq=oq, xl=ol, xs=os_, nthreads=8)
+    ou = oracle.gemv(mode, wu, su, xq=oq, xl=ol, xs=os_, nthreads=8)
+    assert np.array_equal(host(g), og) and np.array_equal(host(u), ou)
+    gh = host(h).reshape(1, F)
+    check_f32(gh, oracle.swiglu(og, ou), "glu h")
+    check_words(mode, gh, hq.view(1, F), None if hl is None else hl.view(1, F), hs.view(1, F // 32), "glu")
