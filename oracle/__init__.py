@@ -16,6 +16,9 @@ Functions (each mirrors one step of the method; citations in ``qdg_oracle.c``):
 * ``reference_f64(mode, ...)`` -> ``(Y, tnorm)`` binary64 anchor of the tolerance
 * ``rmsnorm(x, r=None, w=None, eps)`` -> ``(s, y)``: residual sum and RMSNorm
 * ``swiglu(g, u)`` -> ``h = silu(g) * u``
+* ``fmt_geometry(fmt)``, ``fmt_row_bytes(fmt, K)``, ``fmt_decode(fmt, w, N, K)`` ->
+  ``(levels [N][K], d [N][K/16], c [N][K/16])``, ``gemv_fmt(fmt, mode, w, N, K, ...)``:
+  the other GGUF block formats
 """
 from __future__ import annotations
 
@@ -51,11 +54,16 @@ def _load():
         lib.orc_reference_f64.argtypes = [I, P, P, I64, I64, P, P, P, P, I64, P, P, I]
         lib.orc_rmsnorm.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P]
         lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_fmt_geometry.argtypes = [I, P, P]
+        lib.orc_fmt_row_bytes.argtypes = [I, I64]
+        lib.orc_fmt_row_bytes.restype = I64
+        lib.orc_fmt_decode.argtypes = [I, P, I64, I64, P, P, P]
+        lib.orc_gemv_fmt.argtypes = [I, I, P, I64, I64, P, P, P, P, P, I]
         lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
         lib.orc_half_to_float.restype = ctypes.c_float
         for name in ("orc_quantize", "orc_block_dots", "orc_gemv", "orc_split_bounds",
                      "orc_gemv_split", "orc_combine", "orc_argmax", "orc_reference_f64",
-                     "orc_rmsnorm", "orc_swiglu"):
+                     "orc_rmsnorm", "orc_swiglu", "orc_fmt_geometry", "orc_fmt_decode", "orc_gemv_fmt"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -196,3 +204,40 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     h = np.empty_like(g)
     _check(_load().orc_swiglu(_p(g), _p(u), g.size, _p(h)), "swiglu")
     return h
+
+
+# GGUF type numbers of the block formats
+Q4_0, Q4_1, Q5_0, Q5_1, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, IQ4_NL, IQ4_XS, MXFP4 = 2, 3, 6, 7, 10, 11, 12, 13, 14, 20, 23, 39
+FORMATS = (Q4_0, Q4_1, Q5_0, Q5_1, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, IQ4_NL, IQ4_XS, MXFP4)
+
+
+def fmt_geometry(fmt: int) -> tuple[int, int]:
+    """``(values, bytes)`` per block of the format."""
+    v, b = ctypes.c_int(), ctypes.c_int()
+    _check(_load().orc_fmt_geometry(fmt, ctypes.byref(v), ctypes.byref(b)), "fmt_geometry")
+    return v.value, b.value
+
+
+def fmt_row_bytes(fmt: int, K: int) -> int:
+    return int(_load().orc_fmt_row_bytes(fmt, K))
+
+
+def fmt_decode(fmt: int, w: np.ndarray, N: int, K: int):
+    """``(levels int8 [N][K], d f32 [N][K/16], c f32 [N][K/16])``: weight k of row o is
+    ``fl(fl(d[o][k/16] * levels[o][k]) + c[o][k/16])``."""
+    w = _c(w, np.uint8)
+    lv = np.empty((N, K), np.int8)
+    d = np.empty((N, K // 16), np.float32)
+    c = np.empty((N, K // 16), np.float32)
+    _check(_load().orc_fmt_decode(fmt, _p(w), N, K, _p(lv), _p(d), _p(c)), "fmt_decode")
+    return lv, d, c
+
+
+def gemv_fmt(fmt: int, mode: int, w: np.ndarray, N: int, K: int, x=None, xq=None, xl=None, xs=None,
+             nthreads: int = 1) -> np.ndarray:
+    """``y [1][N]`` of a block-format matrix (batch 1) under the mode's numerics."""
+    w = _c(w, np.uint8)
+    x, xq, xl, xs = _c(x, np.float32), _c(xq, np.int8), _c(xl, np.int8), _c(xs, np.float32)
+    y = np.empty((1, N), np.float32)
+    _check(_load().orc_gemv_fmt(fmt, mode, _p(w), N, K, _p(x), _p(xq), _p(xl), _p(xs), _p(y), nthreads), "gemv_fmt")
+    return y

@@ -22,6 +22,8 @@
  *        ph_argmax_fin (first index among equal maxima).
  *   The producers of the quantized activation: [P1] RMSNORM (lk_rmsnorm_row),
  *   lk_act, GLU; [P2] gk_add_rmsnorm_q8f, gk_silu_had_q8.
+ *   The other block formats: [P1] module doc, BLOCKS (lk_sub and its helpers),
+ *   lk_row_dot, lk_sub_dot.
  *
  * Modes: 0 Dequant (f32 activation, f64 sums), 1 Int8Act, 2 TwoPassInt8 ([P1]
  * mode()).
@@ -411,6 +413,280 @@ int orc_swiglu(const float *g, const float *u, int64_t n, float *h)
         h[i] = (float)(silu * (double)u[i]);
     }
     return 0;
+}
+
+/*
+ * Block formats other than the split Q8_0 -- [P1] module doc (a matrix in any
+ * other GGUF format keeps its blocks as stored; a 32-weight sub-block decodes to
+ * int8 levels with a scale d and an offset c per half of 16, weight = d*level +
+ * c) and BLOCKS (lk_sub: the per-format decoders, lk_h, lk_e8m0_half,
+ * lk_scale_min_k4, lk_iq4_level, lk_iq4xs_scale).  Format ids are the GGUF type
+ * numbers.  The byte layouts below are those decoders' reading of each block.
+ *
+ * Geometry: values per block (32, or 256 for a super-block) and bytes per block.
+ */
+enum {
+    ORC_Q4_0 = 2, ORC_Q4_1 = 3, ORC_Q5_0 = 6, ORC_Q5_1 = 7, ORC_Q2_K = 10, ORC_Q3_K = 11,
+    ORC_Q4_K = 12, ORC_Q5_K = 13, ORC_Q6_K = 14, ORC_IQ4_NL = 20, ORC_IQ4_XS = 23, ORC_MXFP4 = 39
+};
+
+int orc_fmt_geometry(int fmt, int *values, int *bytes)
+{
+    int v = 32, b;
+    switch (fmt) {
+    case ORC_Q4_0: b = 18; break;
+    case ORC_Q4_1: b = 20; break;
+    case ORC_Q5_0: b = 22; break;
+    case ORC_Q5_1: b = 24; break;
+    case ORC_IQ4_NL: b = 18; break;
+    case ORC_MXFP4: b = 17; break;
+    case ORC_Q2_K: v = 256; b = 84; break;
+    case ORC_Q3_K: v = 256; b = 110; break;
+    case ORC_Q4_K: v = 256; b = 144; break;
+    case ORC_Q5_K: v = 256; b = 176; break;
+    case ORC_Q6_K: v = 256; b = 210; break;
+    case ORC_IQ4_XS: v = 256; b = 136; break;
+    default: return -1;
+    }
+    *values = v;
+    *bytes = b;
+    return 0;
+}
+
+/* A little-endian binary16 at p, as a float (exact widening). */
+static float orc_h16(const uint8_t *p) { return orc_half((uint16_t)(p[0] | (p[1] << 8))); }
+
+/* [P1] lk_e8m0_half: the E8M0 scale 2^(e-127), halved because the E2M1 level
+ * table below is doubled (so its levels are integers): 2^(e-128). */
+static float orc_e8m0_half(uint8_t e) { return ldexpf(1.0f, (int)e - 128); }
+
+/* [P1] lk_scale_min_k4: the 6-bit scale and min of sub-block j (0..7) of a
+ * Q4_K / Q5_K super-block from its 12 packed bytes q. */
+static void orc_scale_min_k4(int j, const uint8_t *q, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = q[j] & 63;
+        *m = q[j + 4] & 63;
+    } else {
+        *sc = (q[j + 4] & 15) | ((q[j - 4] >> 6) << 4);
+        *m = (q[j + 4] >> 4) | ((q[j] >> 6) << 4);
+    }
+}
+
+/* [P1] lk_iq4_level: the sixteen non-linear IQ4 levels. */
+static const int8_t ORC_IQ4[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
+/* [P1] the doubled E2M1 values of MXFP4, by nibble. */
+static const int8_t ORC_E2M1X2[16] = {0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12};
+
+/* Sub-block sb (32 weights) of a row: levels v[32], and per half h (weights
+ * 16h .. 16h+15) the scale d[h] and offset c[h] (binary32). */
+static int orc_decode_sub(int fmt, const uint8_t *row, int64_t sb, int8_t *v, float *d, float *c)
+{
+    c[0] = c[1] = 0.0f;
+    if (fmt == ORC_Q4_0 || fmt == ORC_Q4_1 || fmt == ORC_IQ4_NL) {
+        const int bytes = fmt == ORC_Q4_1 ? 20 : 18;
+        const uint8_t *b = row + sb * bytes;
+        d[0] = d[1] = orc_h16(b);
+        if (fmt == ORC_Q4_1) c[0] = c[1] = orc_h16(b + 2);
+        const uint8_t *qs = b + (fmt == ORC_Q4_1 ? 4 : 2);
+        for (int i = 0; i < 16; ++i) {
+            const int lo = qs[i] & 15, hi = qs[i] >> 4;
+            if (fmt == ORC_IQ4_NL) {
+                v[i] = ORC_IQ4[lo];
+                v[i + 16] = ORC_IQ4[hi];
+            } else {
+                v[i] = (int8_t)(lo - (fmt == ORC_Q4_0 ? 8 : 0));
+                v[i + 16] = (int8_t)(hi - (fmt == ORC_Q4_0 ? 8 : 0));
+            }
+        }
+    } else if (fmt == ORC_Q5_0 || fmt == ORC_Q5_1) {
+        const int bytes = fmt == ORC_Q5_1 ? 24 : 22;
+        const uint8_t *b = row + sb * bytes;
+        d[0] = d[1] = orc_h16(b);
+        if (fmt == ORC_Q5_1) c[0] = c[1] = orc_h16(b + 2);
+        const uint8_t *hb = b + (fmt == ORC_Q5_1 ? 4 : 2);
+        const uint32_t qh = (uint32_t)hb[0] | ((uint32_t)hb[1] << 8) | ((uint32_t)hb[2] << 16) | ((uint32_t)hb[3] << 24);
+        const uint8_t *qs = hb + 4;
+        const int off = fmt == ORC_Q5_0 ? 16 : 0;
+        for (int i = 0; i < 16; ++i) {
+            /* bit i of qh is the fifth bit of weight i, bit i + 16 that of weight i + 16 */
+            v[i] = (int8_t)(((qs[i] & 15) | (((qh >> i) & 1) << 4)) - off);
+            v[i + 16] = (int8_t)(((qs[i] >> 4) | (((qh >> (i + 16)) & 1) << 4)) - off);
+        }
+    } else if (fmt == ORC_MXFP4) {
+        const uint8_t *b = row + sb * 17;
+        d[0] = d[1] = orc_e8m0_half(b[0]);
+        for (int i = 0; i < 16; ++i) {
+            v[i] = ORC_E2M1X2[b[1 + i] & 15];
+            v[i + 16] = ORC_E2M1X2[b[1 + i] >> 4];
+        }
+    } else if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {
+        const uint8_t *b = row + (sb >> 3) * (fmt == ORC_Q4_K ? 144 : 176);
+        const int j = (int)(sb & 7), pair = j >> 1, upper = j & 1;
+        int sc, m;
+        orc_scale_min_k4(j, b + 4, &sc, &m);
+        d[0] = d[1] = orc_h16(b) * (float)sc;
+        c[0] = c[1] = -(orc_h16(b + 2) * (float)m);
+        /* 32 bytes of nibbles per pair of sub-blocks: the low nibbles are the even
+         * sub-block, the high nibbles the odd one; Q5_K's fifth bits sit in 32
+         * bytes after the scales, bit 2*pair + upper of byte l for weight l */
+        const uint8_t *ql = b + (fmt == ORC_Q4_K ? 16 : 48) + 32 * pair;
+        for (int l = 0; l < 32; ++l) {
+            int lv = upper ? ql[l] >> 4 : ql[l] & 15;
+            if (fmt == ORC_Q5_K && (b[16 + l] >> (2 * pair + upper)) & 1) lv += 16;
+            v[l] = (int8_t)lv;
+        }
+    } else if (fmt == ORC_Q2_K) {
+        const uint8_t *b = row + (sb >> 3) * 84;
+        const int j = (int)(sb & 7), half = j >> 2, k = j & 3;
+        const uint8_t *q = b + 16 + 32 * half;
+        const float dd = orc_h16(b + 80), dm = orc_h16(b + 82);
+        for (int l = 0; l < 32; ++l) v[l] = (int8_t)((q[l] >> (2 * k)) & 3);
+        for (int h = 0; h < 2; ++h) {
+            const int sc = b[8 * half + 2 * k + h];
+            d[h] = dd * (float)(sc & 15);
+            c[h] = -(dm * (float)(sc >> 4));
+        }
+    } else if (fmt == ORC_Q3_K) {
+        const uint8_t *b = row + (sb >> 3) * 110;
+        const int j = (int)(sb & 7), half = j >> 2, k = j & 3;
+        const uint8_t *q = b + 32 + 32 * half;  /* two-bit low parts */
+        const uint8_t *hm = b;                  /* 32 bytes of high-bit masks */
+        const uint8_t *sp = b + 96;             /* 12 bytes: 16 six-bit scales */
+        const float dd = orc_h16(b + 108);
+        const int mbit = 4 * half + k;
+        for (int l = 0; l < 32; ++l) {
+            const int low = (q[l] >> (2 * k)) & 3;
+            v[l] = (int8_t)(low - (((hm[l] >> mbit) & 1) ? 0 : 4));
+        }
+        for (int h = 0; h < 2; ++h) {
+            /* six-bit scale i (0..15): its low 4 bits are nibble i / 8 of byte
+             * i mod 8, its high 2 bits are bits 2*(i / 4) of byte 8 + i mod 4 */
+            const int i = 8 * half + 2 * k + h;
+            const int lo4 = (sp[i & 7] >> (4 * (i >> 3))) & 15;
+            const int hi2 = (sp[8 + (i & 3)] >> (2 * (i >> 2))) & 3;
+            d[h] = dd * (float)((lo4 | (hi2 << 4)) - 32);
+        }
+    } else if (fmt == ORC_Q6_K) {
+        const uint8_t *b = row + (sb >> 3) * 210;
+        const int j = (int)(sb & 7), half = j >> 2, k = j & 3;
+        const uint8_t *ql = b + 64 * half;
+        const uint8_t *qh = b + 128 + 32 * half;
+        const int8_t *sc = (const int8_t *)(b + 192 + 8 * half);
+        const float dd = orc_h16(b + 208);
+        for (int l = 0; l < 32; ++l) {
+            int lo = (k & 1) ? ql[l + 32] : ql[l];
+            lo = (k & 2) ? lo >> 4 : lo & 15;
+            v[l] = (int8_t)((lo | (((qh[l] >> (2 * k)) & 3) << 4)) - 32);
+        }
+        d[0] = dd * (float)sc[2 * k];
+        d[1] = dd * (float)sc[2 * k + 1];
+    } else if (fmt == ORC_IQ4_XS) {
+        const uint8_t *b = row + (sb >> 3) * 136;
+        const int ib = (int)(sb & 7);
+        const unsigned sh = (unsigned)b[2] | ((unsigned)b[3] << 8);
+        const unsigned sl = b[4 + (ib >> 1)];
+        const int ls = (int)((sl >> (4 * (ib & 1))) & 15) | (int)(((sh >> (2 * ib)) & 3) << 4);
+        d[0] = d[1] = orc_h16(b) * (float)(ls - 32);
+        const uint8_t *qs = b + 8 + 16 * ib;
+        for (int i = 0; i < 16; ++i) {
+            v[i] = ORC_IQ4[qs[i] & 15];
+            v[i + 16] = ORC_IQ4[qs[i] >> 4];
+        }
+    } else {
+        return -1;
+    }
+    return 0;
+}
+
+/* Row bytes of a K-value row in format fmt (0 if K does not fit the format). */
+int64_t orc_fmt_row_bytes(int fmt, int64_t K)
+{
+    int v, b;
+    if (orc_fmt_geometry(fmt, &v, &b) || K % v) return 0;
+    return K / v * b;
+}
+
+/* Every sub-block of N rows: levels [N][K], d and c [N][K/16] (one per half). */
+int orc_fmt_decode(int fmt, const uint8_t *w, int64_t N, int64_t K, int8_t *levels, float *d, float *c)
+{
+    const int64_t rb = orc_fmt_row_bytes(fmt, K);
+    if (!rb) return -1;
+    for (int64_t o = 0; o < N; ++o)
+        for (int64_t sb = 0; sb < K / 32; ++sb)
+            if (orc_decode_sub(fmt, w + o * rb, sb, levels + o * K + 32 * sb, d + o * (K / 16) + 2 * sb,
+                               c + o * (K / 16) + 2 * sb))
+                return -1;
+    return 0;
+}
+
+/*
+ * The GEMV of a block-format matrix, batch 1 -- [P1] lk_row_dot, lk_sub_dot.
+ *  Dequant: each weight is fl(fl(d*level) + c) as the CPU dequantizer rounds
+ *    it; the products with x and their sum are binary64 (ascending k), rounded
+ *    once to binary32.
+ *  Int8Act / TwoPass: per sub-block g, the exact int32 dots of each half with
+ *    the activation words, dh_h = sum level*h and sh_h = sum h (and dl, sl with
+ *    the low words); part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1, every product
+ *    and sum one binary32 rounding, left to right; TwoPass adds
+ *    fl(2^-7 * (the same with dl, sl)).  The row is the Q8_0 row's structure:
+ *    step p <- fma(s_g, part, p) into partial g mod 4 in ascending g from +0,
+ *    then (P0 + P2) + (P1 + P3).
+ */
+int orc_gemv_fmt(int fmt, int mode, const uint8_t *w, int64_t N, int64_t K, const float *x,
+                 const int8_t *xq, const int8_t *xl, const float *xs, float *y, int nthreads)
+{
+    const int64_t rb = orc_fmt_row_bytes(fmt, K);
+    if (!rb || mode < 0 || mode > 2) return -1;
+    const int64_t nb = K / 32;
+    orc_set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t o = 0; o < N; ++o) {
+        const uint8_t *row = w + o * rb;
+        int8_t v[32];
+        float d[2], c[2];
+        if (mode == 0) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < nb; ++g) {
+                if (orc_decode_sub(fmt, row, g, v, d, c)) { bad = 1; break; }
+                for (int i = 0; i < 32; ++i) {
+                    const float wv = (d[i >> 4] * (float)v[i]) + c[i >> 4];
+                    acc += (double)wv * (double)x[32 * g + i];
+                }
+            }
+            y[o] = (float)acc;
+            continue;
+        }
+        float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t g = 0; g < nb; ++g) {
+            if (orc_decode_sub(fmt, row, g, v, d, c)) { bad = 1; break; }
+            int32_t dh[2] = {0, 0}, sh[2] = {0, 0}, dl[2] = {0, 0}, sl[2] = {0, 0};
+            for (int i = 0; i < 32; ++i) {
+                const int h = i >> 4;
+                dh[h] += (int32_t)v[i] * xq[32 * g + i];
+                sh[h] += xq[32 * g + i];
+                if (mode == 2) {
+                    dl[h] += (int32_t)v[i] * xl[32 * g + i];
+                    sl[h] += xl[32 * g + i];
+                }
+            }
+            float part = d[0] * (float)dh[0];
+            part = part + c[0] * (float)sh[0];
+            part = part + d[1] * (float)dh[1];
+            part = part + c[1] * (float)sh[1];
+            if (mode == 2) {
+                float lo = d[0] * (float)dl[0];
+                lo = lo + c[0] * (float)sl[0];
+                lo = lo + d[1] * (float)dl[1];
+                lo = lo + c[1] * (float)sl[1];
+                part = part + 0.0078125f * lo;
+            }
+            P[g & 3] = fmaf(xs[g], part, P[g & 3]);
+        }
+        y[o] = (P[0] + P[2]) + (P[1] + P[3]);
+    }
+    return bad ? -1 : 0;
 }
 
 int orc_version(void) { return 1; }
