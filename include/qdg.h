@@ -316,6 +316,39 @@ int qdg_gemv_glu_q8(int mode, const int8_t *wg, const uint16_t *sg, const int8_t
                     const uint16_t *su, int64_t F, int64_t K, const int8_t *xq, const int8_t *xl,
                     const float *xs, float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
 
+/* GGUF type numbers of the other block formats (qdg_gemv_fmt). */
+enum {
+  QDG_FMT_Q4_0 = 2, QDG_FMT_Q4_1 = 3, QDG_FMT_Q5_0 = 6, QDG_FMT_Q5_1 = 7,
+  QDG_FMT_Q2_K = 10, QDG_FMT_Q3_K = 11, QDG_FMT_Q4_K = 12, QDG_FMT_Q5_K = 13,
+  QDG_FMT_Q6_K = 14, QDG_FMT_IQ4_NL = 20, QDG_FMT_IQ4_XS = 23, QDG_FMT_MXFP4 = 39
+};
+
+/* Host only: bytes of one K-value row in block format fmt (K/32 blocks of 17-24
+ * bytes, or K/256 super-blocks of 84-210 bytes); 0 for an unknown format or a K
+ * that is not a whole number of its blocks. */
+int64_t qdg_fmt_row_bytes(int fmt, int64_t K);
+
+/*
+ * y[o] = sum_k W[o][k] x[k] for a matrix kept in another GGUF block format, its
+ * blocks as the checkpoint stores them, row o at w + o*qdg_fmt_row_bytes(fmt, K)
+ * (lane kernel library page: module doc on the other formats; BLOCKS / lk_sub
+ * for the layouts; lk_row_dot, lk_sub_dot for the sums).  A 32-weight sub-block
+ * decodes to int8 levels with a scale d and an offset c per half of 16,
+ * weight = d*level + c.
+ *  QDG_DEQUANT  reads x; each weight fl(fl(d*level) + c), products and sums in
+ *               binary64, rounded once.
+ *  QDG_INT8ACT  reads xq, xs (xq, xl, xs under QDG_TWOPASS); per sub-block g the
+ *  QDG_TWOPASS  exact dots dh = sum level*h and sh = sum h of each half, part =
+ *               ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with one rounding per
+ *               operation, TwoPass adding fl(2^-7 * the same with the low
+ *               words); p <- fma(xs[g], part, p) into partial g mod 4 in
+ *               ascending g, then (P0 + P2) + (P1 + P3).
+ * Batch 1.  w 16-byte aligned; x, xq, xl 16-byte aligned; y [N].  N >= 1 and K
+ * a positive whole number of the format's blocks.
+ */
+int qdg_gemv_fmt(int fmt, int mode, const uint8_t *w, int64_t N, int64_t K, const float *x,
+                 const int8_t *xq, const int8_t *xl, const float *xs, float *y, qdg_stream stream);
+
 /*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
  * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,

@@ -58,7 +58,7 @@ def _load():
         lib.orc_fmt_row_bytes.argtypes = [I, I64]
         lib.orc_fmt_row_bytes.restype = I64
         lib.orc_fmt_decode.argtypes = [I, P, I64, I64, P, P, P]
-        lib.orc_gemv_fmt.argtypes = [I, I, P, I64, I64, P, P, P, P, P, I]
+        lib.orc_gemv_fmt.argtypes = [I, I, P, I64, I64, P, P, P, P, I, P, I]
         lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
         lib.orc_half_to_float.restype = ctypes.c_float
         for name in ("orc_quantize", "orc_block_dots", "orc_gemv", "orc_split_bounds",
@@ -234,10 +234,12 @@ def fmt_decode(fmt: int, w: np.ndarray, N: int, K: int):
 
 
 def gemv_fmt(fmt: int, mode: int, w: np.ndarray, N: int, K: int, x=None, xq=None, xl=None, xs=None,
-             nthreads: int = 1) -> np.ndarray:
-    """``y [1][N]`` of a block-format matrix (batch 1) under the mode's numerics."""
+             splits: int = 1, nthreads: int = 1) -> np.ndarray:
+    """``y [1][N]`` of a block-format matrix (batch 1) under the mode's numerics; with
+    ``splits`` > 1 the chunk partials of the split rule added in ascending order."""
     w = _c(w, np.uint8)
     x, xq, xl, xs = _c(x, np.float32), _c(xq, np.int8), _c(xl, np.int8), _c(xs, np.float32)
     y = np.empty((1, N), np.float32)
-    _check(_load().orc_gemv_fmt(fmt, mode, _p(w), N, K, _p(x), _p(xq), _p(xl), _p(xs), _p(y), nthreads), "gemv_fmt")
+    _check(_load().orc_gemv_fmt(fmt, mode, _p(w), N, K, _p(x), _p(xq), _p(xl), _p(xs), splits, _p(y), nthreads),
+           "gemv_fmt")
     return y

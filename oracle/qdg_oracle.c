@@ -633,58 +633,92 @@ int orc_fmt_decode(int fmt, const uint8_t *w, int64_t N, int64_t K, int8_t *leve
  *    step p <- fma(s_g, part, p) into partial g mod 4 in ascending g from +0,
  *    then (P0 + P2) + (P1 + P3).
  */
+/* The quantized row dot of one row over sub-blocks [g0, g1) (the steps below). */
+static float orc_fmt_row_quant(int fmt, int mode, const uint8_t *row, int64_t g0, int64_t g1,
+                               const int8_t *xq, const int8_t *xl, const float *xs, int *bad)
+{
+    int8_t v[32];
+    float d[2], c[2];
+    float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t g = g0; g < g1; ++g) {
+        if (orc_decode_sub(fmt, row, g, v, d, c)) { *bad = 1; return 0.0f; }
+        int32_t dh[2] = {0, 0}, sh[2] = {0, 0}, dl[2] = {0, 0}, sl[2] = {0, 0};
+        for (int i = 0; i < 32; ++i) {
+            const int h = i >> 4;
+            dh[h] += (int32_t)v[i] * xq[32 * g + i];
+            sh[h] += xq[32 * g + i];
+            if (mode == 2) {
+                dl[h] += (int32_t)v[i] * xl[32 * g + i];
+                sl[h] += xl[32 * g + i];
+            }
+        }
+        float part = d[0] * (float)dh[0];
+        part = part + c[0] * (float)sh[0];
+        part = part + d[1] * (float)dh[1];
+        part = part + c[1] * (float)sh[1];
+        if (mode == 2) {
+            float lo = d[0] * (float)dl[0];
+            lo = lo + c[0] * (float)sl[0];
+            lo = lo + d[1] * (float)dl[1];
+            lo = lo + c[1] * (float)sl[1];
+            part = part + 0.0078125f * lo;
+        }
+        P[g & 3] = fmaf(xs[g], part, P[g & 3]);
+    }
+    return (P[0] + P[2]) + (P[1] + P[3]);
+}
+
+/* The Dequant sum of one row over sub-blocks [g0, g1), binary64, ascending k. */
+static double orc_fmt_row_dequant(int fmt, const uint8_t *row, int64_t g0, int64_t g1, const float *x, int *bad)
+{
+    int8_t v[32];
+    float d[2], c[2];
+    double acc = 0.0;
+    for (int64_t g = g0; g < g1; ++g) {
+        if (orc_decode_sub(fmt, row, g, v, d, c)) { *bad = 1; return 0.0; }
+        for (int i = 0; i < 32; ++i) {
+            const float wv = (d[i >> 4] * (float)v[i]) + c[i >> 4];
+            acc += (double)wv * (double)x[32 * g + i];
+        }
+    }
+    return acc;
+}
+
+/*
+ * splits == 1: the row as above.  splits > 1: the QWEN38 page's chunk rule in
+ * sub-blocks (orc_split_bounds: 512-value superblocks), each chunk's partial
+ * summed as a whole row is over the chunk's sub-blocks, then added in
+ * ascending chunk order from 0 (gk_sk_combine) -- binary32 under the quantized
+ * modes, binary64 under Dequant with one final rounding.
+ */
 int orc_gemv_fmt(int fmt, int mode, const uint8_t *w, int64_t N, int64_t K, const float *x,
-                 const int8_t *xq, const int8_t *xl, const float *xs, float *y, int nthreads)
+                 const int8_t *xq, const int8_t *xl, const float *xs, int splits, float *y, int nthreads)
 {
     const int64_t rb = orc_fmt_row_bytes(fmt, K);
-    if (!rb || mode < 0 || mode > 2) return -1;
+    if (!rb || mode < 0 || mode > 2 || splits < 1 || splits > 64) return -1;
     const int64_t nb = K / 32;
+    int32_t first[65];
+    if (orc_split_bounds(K, splits, first)) return -1;
     orc_set_threads(nthreads);
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t o = 0; o < N; ++o) {
         const uint8_t *row = w + o * rb;
-        int8_t v[32];
-        float d[2], c[2];
-        if (mode == 0) {
-            double acc = 0.0;
-            for (int64_t g = 0; g < nb; ++g) {
-                if (orc_decode_sub(fmt, row, g, v, d, c)) { bad = 1; break; }
-                for (int i = 0; i < 32; ++i) {
-                    const float wv = (d[i >> 4] * (float)v[i]) + c[i >> 4];
-                    acc += (double)wv * (double)x[32 * g + i];
-                }
-            }
-            y[o] = (float)acc;
+        if (splits == 1) {
+            y[o] = mode == 0 ? (float)orc_fmt_row_dequant(fmt, row, 0, nb, x, &bad)
+                             : orc_fmt_row_quant(fmt, mode, row, 0, nb, xq, xl, xs, &bad);
             continue;
         }
-        float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t g = 0; g < nb; ++g) {
-            if (orc_decode_sub(fmt, row, g, v, d, c)) { bad = 1; break; }
-            int32_t dh[2] = {0, 0}, sh[2] = {0, 0}, dl[2] = {0, 0}, sl[2] = {0, 0};
-            for (int i = 0; i < 32; ++i) {
-                const int h = i >> 4;
-                dh[h] += (int32_t)v[i] * xq[32 * g + i];
-                sh[h] += xq[32 * g + i];
-                if (mode == 2) {
-                    dl[h] += (int32_t)v[i] * xl[32 * g + i];
-                    sl[h] += xl[32 * g + i];
-                }
-            }
-            float part = d[0] * (float)dh[0];
-            part = part + c[0] * (float)sh[0];
-            part = part + d[1] * (float)dh[1];
-            part = part + c[1] * (float)sh[1];
-            if (mode == 2) {
-                float lo = d[0] * (float)dl[0];
-                lo = lo + c[0] * (float)sl[0];
-                lo = lo + d[1] * (float)dl[1];
-                lo = lo + c[1] * (float)sl[1];
-                part = part + 0.0078125f * lo;
-            }
-            P[g & 3] = fmaf(xs[g], part, P[g & 3]);
+        if (mode == 0) {
+            double a = 0.0;
+            for (int s = 0; s < splits; ++s) a += orc_fmt_row_dequant(fmt, row, first[s], first[s + 1], x, &bad);
+            y[o] = (float)a;
+        } else {
+            float a = 0.0f;
+            for (int s = 0; s < splits; ++s)
+                a = a + orc_fmt_row_quant(fmt, mode, row, first[s], first[s + 1], xq, xl, xs, &bad);
+            y[o] = a;
         }
-        y[o] = (P[0] + P[2]) + (P[1] + P[3]);
     }
     return bad ? -1 : 0;
 }

@@ -75,6 +75,8 @@ _SIGS = {
     "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "qdg_fmt_row_bytes": ([_I, _I64], _I64),
+    "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -217,6 +219,31 @@ def gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> No
 
 def bind_gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> Bound:
     return Bound("qdg_gemv_glu_q8", *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs))
+
+
+# GGUF type numbers of the other block formats
+FMT_Q4_0, FMT_Q4_1, FMT_Q5_0, FMT_Q5_1, FMT_Q2_K, FMT_Q3_K = 2, 3, 6, 7, 10, 11
+FMT_Q4_K, FMT_Q5_K, FMT_Q6_K, FMT_IQ4_NL, FMT_IQ4_XS, FMT_MXFP4 = 12, 13, 14, 20, 23, 39
+
+
+def fmt_row_bytes(fmt: int, K: int) -> int:
+    return int(_lib.qdg_fmt_row_bytes(fmt, K))
+
+
+def _fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs):
+    if w.numel() < N * fmt_row_bytes(fmt, K):
+        raise ValueError("gemv_fmt: w is smaller than N rows of the format")
+    return (fmt, mode, _ptr(w, (_torch().uint8, _torch().int8), "w"), N, K, _ptr(x, _f32(), "x"),
+            _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(y, _f32(), "y"), _stream())
+
+
+def gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None) -> None:
+    """``y [N] = W x`` for ``w``, N rows of K values in GGUF block format ``fmt`` (bytes as stored)."""
+    _check("qdg_gemv_fmt", _lib.qdg_gemv_fmt(*_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs)))
+
+
+def bind_gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None) -> Bound:
+    return Bound("qdg_gemv_fmt", *_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs))
 
 
 MAX_PARTS = 6

@@ -1,0 +1,452 @@
+// qdg_formats.hip -- the batch-1 GEMV of a matrix in another GGUF block format
+// (lane kernel library page: module doc on the other formats; BLOCKS, lk_sub
+// and its helpers for the layouts; lk_row_dot and lk_sub_dot for the sums).
+//
+// A 32-weight sub-block decodes to int8 levels with a scale d and an offset c
+// per half of 16: weight = d*level + c.
+//  * Int8Act / TwoPass: per sub-block, the exact int32 dots of each half with
+//    the activation words, dh = sum level*h and sh = sum h (the latter a v_dot4
+//    against ones; dl, sl with the low words); part = ((d0*dh0 + c0*sh0) +
+//    d1*dh1) + c1*sh1, one rounding per operation; TwoPass adds fl(2^-7 * the
+//    same with dl, sl).  The row is the Q8_0 row: p <- fma(s_g, part, p) into
+//    partial g mod 4, ascending, then (P0 + P2) + (P1 + P3).
+//  * Dequant: each weight fl(fl(d*level) + c), its products with x and their
+//    sums in binary64 (a lane's 32 in ascending order, then the row's partials
+//    as above), one rounding to binary32.
+// A format whose levels carry a constant offset (Q4_0: nibble - 8, Q5_0: - 16,
+// Q3_K: - 4, Q6_K: - 32) is dotted on its raw unsigned levels and corrected by
+// the offset times the activation sum, which is the same integer.
+//
+// Mapping: a wave takes 8 rows, 8 lanes a row, one sub-block a lane, so a step
+// covers 8 consecutive sub-blocks of a row (one super-block of the K-quants).
+// Lane j < 4 of a row owns partial j: it folds its own sub-block, then the one
+// of lane j + 4 (one DPP row shift).  The activation window is staged in LDS.
+#include <stdlib.h>
+
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+constexpr int FWG = 256;                // four waves, 32 rows
+constexpr int FROWS = 32;
+constexpr int F_LDS_BUDGET = 24 * 1024;
+
+enum : int {
+  F_Q4_0 = 2, F_Q4_1 = 3, F_Q5_0 = 6, F_Q5_1 = 7, F_Q2_K = 10, F_Q3_K = 11, F_Q4_K = 12,
+  F_Q5_K = 13, F_Q6_K = 14, F_IQ4_NL = 20, F_IQ4_XS = 23, F_MXFP4 = 39
+};
+constexpr int DPP_ROW_SHL1 = 0x101;
+
+// GGUF geometry: values per block and bytes per block.
+template <int F>
+struct Geo;
+template <> struct Geo<F_Q4_0> { static constexpr int V = 32, B = 18; };
+template <> struct Geo<F_Q4_1> { static constexpr int V = 32, B = 20; };
+template <> struct Geo<F_Q5_0> { static constexpr int V = 32, B = 22; };
+template <> struct Geo<F_Q5_1> { static constexpr int V = 32, B = 24; };
+template <> struct Geo<F_IQ4_NL> { static constexpr int V = 32, B = 18; };
+template <> struct Geo<F_MXFP4> { static constexpr int V = 32, B = 17; };
+template <> struct Geo<F_Q2_K> { static constexpr int V = 256, B = 84; };
+template <> struct Geo<F_Q3_K> { static constexpr int V = 256, B = 110; };
+template <> struct Geo<F_Q4_K> { static constexpr int V = 256, B = 144; };
+template <> struct Geo<F_Q5_K> { static constexpr int V = 256, B = 176; };
+template <> struct Geo<F_Q6_K> { static constexpr int V = 256, B = 210; };
+template <> struct Geo<F_IQ4_XS> { static constexpr int V = 256, B = 136; };
+
+__device__ __forceinline__ unsigned ld_u8(const uint8_t* p) { return *p; }
+__device__ __forceinline__ unsigned ld_u16(const uint8_t* p) { return *(const unsigned short*)p; }
+__device__ __forceinline__ unsigned ld_u32(const uint8_t* p) { return *(const unsigned*)p; }
+__device__ __forceinline__ float h16(unsigned bits) { return half_bits_to_float((unsigned short)(bits & 0xffff)); }
+
+// n dwords from p: whole dword loads when p is 4-byte aligned, else pairs of
+// 2-byte loads (every block format keeps its fields 2-byte aligned but MXFP4).
+template <int NW>
+__device__ __forceinline__ void ld_words(const uint8_t* p, unsigned* w) {
+  if (((uintptr_t)p & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = ld_u32(p + 4 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = ld_u16(p + 4 * i) | (ld_u16(p + 4 * i + 2) << 16);
+  }
+}
+
+// The low nibbles of a word's four bytes and the high ones, as bytes.
+__device__ __forceinline__ unsigned lo_nib(unsigned q) { return q & 0x0f0f0f0fu; }
+__device__ __forceinline__ unsigned hi_nib(unsigned q) { return (q >> 4) & 0x0f0f0f0fu; }
+
+// Four nibbles (one a byte) mapped through a 16-entry int8 table held four
+// entries a word (t[0] entries 0-3 ... t[3] 12-15), by byte permutes: the low
+// three bits select within entries 0-7 and within 8-15, the fourth bit between.
+__device__ __forceinline__ unsigned table16(unsigned nib, const unsigned (&t)[4]) {
+  // v_perm_b32(a, b, sel): selector byte k < 4 picks byte k of b, 4..7 byte k-4 of a
+  const unsigned sel = nib & 0x07070707u;
+  const unsigned lo = __builtin_amdgcn_perm(t[1], t[0], sel);
+  const unsigned hi = __builtin_amdgcn_perm(t[3], t[2], sel);
+  const unsigned m = ((nib >> 3) & 0x01010101u) * 0xffu;  // 0xff in the bytes whose nibble is >= 8
+  return (lo & ~m) | (hi & m);
+}
+
+// IQ4's sixteen levels and MXFP4's doubled E2M1 values, four to a word (little-endian).
+__device__ __forceinline__ void iq4_table(unsigned (&t)[4]) {
+  t[0] = 0xBFAD9881u; t[1] = 0xF6EADDCFu; t[2] = 0x26190D01u; t[3] = 0x71594535u;
+}
+__device__ __forceinline__ void e2m1_table(unsigned (&t)[4]) {
+  t[0] = 0x03020100u; t[1] = 0x0C080604u; t[2] = 0xFDFEFF00u; t[3] = 0xF4F8FAFCu;
+}
+
+// The five-bit levels' fifth bits: bit i (i < 4) of x to bit 4 of byte i.
+__device__ __forceinline__ unsigned spread4(unsigned x) {
+  return ((x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21)) << 4;
+}
+
+// One decoded sub-block: raw int8 levels, four a word, level = raw - off; the
+// scale d and offset c of each half.
+struct Sub {
+  unsigned w[8];
+  int off;
+  float d[2], c[2];
+};
+
+// Sub-block sb of a row (lane kernel library page, lk_sub: the same layouts).
+template <int F>
+__device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, Sub& s) {
+  s.off = 0;
+  s.c[0] = s.c[1] = 0.0f;
+  if constexpr (F == F_Q4_0 || F == F_IQ4_NL || F == F_Q4_1) {
+    const uint8_t* b = row + (int64_t)sb * Geo<F>::B;
+    unsigned q[4];
+    if constexpr (F == F_Q4_1) {
+      const unsigned hd = ld_u32(b);
+      s.d[0] = s.d[1] = h16(hd);
+      s.c[0] = s.c[1] = h16(hd >> 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = ld_u32(b + 4 + 4 * i);
+    } else {
+      s.d[0] = s.d[1] = h16(ld_u16(b));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = ld_u16(b + 2 + 4 * i) | (ld_u16(b + 4 + 4 * i) << 16);
+    }
+    if constexpr (F == F_IQ4_NL) {
+      unsigned t[4];
+      iq4_table(t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s.w[i] = table16(lo_nib(q[i]), t);
+        s.w[4 + i] = table16(hi_nib(q[i]), t);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s.w[i] = lo_nib(q[i]);
+        s.w[4 + i] = hi_nib(q[i]);
+      }
+      if constexpr (F == F_Q4_0) s.off = 8;
+    }
+  } else if constexpr (F == F_Q5_0 || F == F_Q5_1) {
+    const uint8_t* b = row + (int64_t)sb * Geo<F>::B;
+    unsigned qh, q[4];
+    if constexpr (F == F_Q5_1) {
+      const unsigned hd = ld_u32(b);
+      s.d[0] = s.d[1] = h16(hd);
+      s.c[0] = s.c[1] = h16(hd >> 16);
+      qh = ld_u32(b + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = ld_u32(b + 8 + 4 * i);
+    } else {
+      s.d[0] = s.d[1] = h16(ld_u16(b));
+      qh = ld_u16(b + 2) | (ld_u16(b + 4) << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = ld_u16(b + 6 + 4 * i) | (ld_u16(b + 8 + 4 * i) << 16);
+      s.off = 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s.w[i] = lo_nib(q[i]) | spread4((qh >> (4 * i)) & 15u);
+      s.w[4 + i] = hi_nib(q[i]) | spread4((qh >> (16 + 4 * i)) & 15u);
+    }
+  } else if constexpr (F == F_MXFP4) {
+    const uint8_t* b = row + (int64_t)sb * 17;
+    const unsigned e = ld_u8(b);
+    const unsigned bits = e < 2 ? (0x00200000u << e) : ((e - 1) << 23);  // 2^(e - 128)
+    s.d[0] = s.d[1] = __uint_as_float(bits);
+    unsigned t[4];
+    e2m1_table(t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned q = ld_u8(b + 1 + 4 * i) | (ld_u8(b + 2 + 4 * i) << 8) | (ld_u8(b + 3 + 4 * i) << 16) |
+                         (ld_u8(b + 4 + 4 * i) << 24);
+      s.w[i] = table16(lo_nib(q), t);
+      s.w[4 + i] = table16(hi_nib(q), t);
+    }
+  } else if constexpr (F == F_Q4_K || F == F_Q5_K) {
+    const uint8_t* b = row + (int64_t)(sb >> 3) * Geo<F>::B;
+    const int j = sb & 7, pair = j >> 1, upper = j & 1;
+    const int4 hd = *(const int4*)b;  // d, dmin, 12 scale bytes
+    const unsigned sw[3] = {(unsigned)hd.y, (unsigned)hd.z, (unsigned)hd.w};
+    auto sbyte = [&](int i) { return (sw[i >> 2] >> (8 * (i & 3))) & 255u; };
+    int sc, mn;
+    if (j < 4) {
+      sc = (int)(sbyte(j) & 63);
+      mn = (int)(sbyte(j + 4) & 63);
+    } else {
+      sc = (int)((sbyte(j + 4) & 15) | ((sbyte(j - 4) >> 6) << 4));
+      mn = (int)((sbyte(j + 4) >> 4) | ((sbyte(j) >> 6) << 4));
+    }
+    s.d[0] = s.d[1] = __fmul_rn(h16((unsigned)hd.x), (float)sc);
+    s.c[0] = s.c[1] = -__fmul_rn(h16((unsigned)hd.x >> 16), (float)mn);
+    const uint8_t* ql = b + (F == F_Q4_K ? 16 : 48) + 32 * pair;
+    const int4 a0 = *(const int4*)ql, a1 = *(const int4*)(ql + 16);
+    const unsigned q[8] = {(unsigned)a0.x, (unsigned)a0.y, (unsigned)a0.z, (unsigned)a0.w,
+                           (unsigned)a1.x, (unsigned)a1.y, (unsigned)a1.z, (unsigned)a1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.w[i] = upper ? hi_nib(q[i]) : lo_nib(q[i]);
+    if constexpr (F == F_Q5_K) {
+      const int4 h0 = *(const int4*)(b + 16), h1 = *(const int4*)(b + 32);
+      const unsigned qh[8] = {(unsigned)h0.x, (unsigned)h0.y, (unsigned)h0.z, (unsigned)h0.w,
+                              (unsigned)h1.x, (unsigned)h1.y, (unsigned)h1.z, (unsigned)h1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s.w[i] |= ((qh[i] >> j) & 0x01010101u) << 4;
+    }
+  } else if constexpr (F == F_Q6_K) {
+    const uint8_t* b = row + (int64_t)(sb >> 3) * 210;
+    const int j = sb & 7, half = j >> 2, k = j & 3;
+    unsigned ql[8], qh[8];
+    ld_words<8>(b + 64 * half + 32 * (k & 1), ql);
+    ld_words<8>(b + 128 + 32 * half, qh);
+    const unsigned scw = ld_u16(b + 192 + 8 * half + 2 * k);
+    const float dd = h16(ld_u16(b + 208));
+    s.d[0] = __fmul_rn(dd, (float)(int)(signed char)(scw & 255));
+    s.d[1] = __fmul_rn(dd, (float)(int)(signed char)(scw >> 8));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      s.w[i] = ((k & 2) ? hi_nib(ql[i]) : lo_nib(ql[i])) | (((qh[i] >> (2 * k)) & 0x03030303u) << 4);
+    s.off = 32;
+  } else if constexpr (F == F_Q2_K) {
+    const uint8_t* b = row + (int64_t)(sb >> 3) * 84;  // 4-byte aligned: 84 is a multiple of 4
+    const int j = sb & 7, half = j >> 2, k = j & 3;
+    unsigned q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = ld_u32(b + 16 + 32 * half + 4 * i);
+    const unsigned scw = ld_u16(b + 8 * half + 2 * k);
+    const unsigned dw = ld_u32(b + 80);
+    const float dd = h16(dw), dm = h16(dw >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const unsigned sc = (scw >> (8 * h)) & 255u;
+      s.d[h] = __fmul_rn(dd, (float)(sc & 15u));
+      s.c[h] = -__fmul_rn(dm, (float)(sc >> 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.w[i] = (q[i] >> (2 * k)) & 0x03030303u;
+  } else if constexpr (F == F_Q3_K) {
+    const uint8_t* b = row + (int64_t)(sb >> 3) * 110;
+    const int j = sb & 7, half = j >> 2, k = j & 3;
+    unsigned hm[8], q[8], sp[3];
+    ld_words<8>(b, hm);
+    ld_words<8>(b + 32 + 32 * half, q);
+    ld_words<3>(b + 96, sp);
+    const float dd = h16(ld_u16(b + 108));
+    auto spb = [&](int i) { return (sp[i >> 2] >> (8 * (i & 3))) & 255u; };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 8 * half + 2 * k + h;
+      const unsigned lo4 = (spb(i & 7) >> (4 * (i >> 3))) & 15u;
+      const unsigned hi2 = (spb(8 + (i & 3)) >> (2 * (i >> 2))) & 3u;
+      s.d[h] = __fmul_rn(dd, (float)((int)(lo4 | (hi2 << 4)) - 32));
+    }
+    const int mbit = 4 * half + k;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.w[i] = ((q[i] >> (2 * k)) & 0x03030303u) | (((hm[i] >> mbit) & 0x01010101u) << 2);
+    s.off = 4;  // level = low2 - 4 + 4*high bit
+  } else if constexpr (F == F_IQ4_XS) {
+    const uint8_t* b = row + (int64_t)(sb >> 3) * 136;  // 8-byte aligned
+    const int ib = sb & 7;
+    const unsigned h0 = ld_u32(b), h1 = ld_u32(b + 4);
+    const unsigned sh = h0 >> 16, sl = (h1 >> (8 * (ib >> 1))) & 255u;
+    const int ls = (int)((sl >> (4 * (ib & 1))) & 15u) | (int)(((sh >> (2 * ib)) & 3u) << 4);
+    s.d[0] = s.d[1] = __fmul_rn(h16(h0), (float)(ls - 32));
+    unsigned t[4];
+    iq4_table(t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned q = ld_u32(b + 8 + 16 * ib + 4 * i);
+      s.w[i] = table16(lo_nib(q), t);
+      s.w[4 + i] = table16(hi_nib(q), t);
+    }
+  }
+}
+
+// part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8]
+__device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8]) {
+  int dh0 = 0, dh1 = 0, sh0 = 0, sh1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dh0 = __builtin_amdgcn_sdot4((int)s.w[i], a[i], dh0, false);
+    sh0 = __builtin_amdgcn_sdot4(0x01010101, a[i], sh0, false);
+    dh1 = __builtin_amdgcn_sdot4((int)s.w[4 + i], a[4 + i], dh1, false);
+    sh1 = __builtin_amdgcn_sdot4(0x01010101, a[4 + i], sh1, false);
+  }
+  dh0 -= s.off * sh0;
+  dh1 -= s.off * sh1;
+  float part = __fmul_rn(s.d[0], (float)dh0);
+  part = __fadd_rn(part, __fmul_rn(s.c[0], (float)sh0));
+  part = __fadd_rn(part, __fmul_rn(s.d[1], (float)dh1));
+  return __fadd_rn(part, __fmul_rn(s.c[1], (float)sh1));
+}
+
+template <int F, int MODE>
+__global__ __launch_bounds__(FWG) void k_gemv_fmt(const uint8_t* __restrict__ w, int64_t rb, int64_t N, int64_t K,
+                                                  const float* __restrict__ x, const int8_t* __restrict__ xq,
+                                                  const int8_t* __restrict__ xl, const float* __restrict__ xs,
+                                                  int win, float* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 3, j = lane & 7;
+  const int64_t nb = K / QK;
+  const int64_t o = (int64_t)blockIdx.x * FROWS + wave * 8 + r;
+  const bool row_ok = o < N;
+  const uint8_t* row = w + (row_ok ? o : N - 1) * rb;
+  // window: quantized modes [win][32] words (+ low words) and [win] scales; Dequant [win][32] f32
+  int8_t* lq = (int8_t*)lds;
+  int8_t* ll = lq + (int64_t)win * QK;
+  float* lsx = (float*)(lds + (int64_t)win * QK * (MODE == 2 ? 2 : 1));
+  float* lx = (float*)lds;
+
+  using Acc = typename std::conditional<MODE == 0, double, float>::type;
+  Acc p = 0;
+  for (int wb0 = 0; wb0 < nb; wb0 += win) {
+    const int nwb = (int)((nb - wb0) < win ? (nb - wb0) : win);
+    __syncthreads();
+    if constexpr (MODE == 0) {
+      for (int i = threadIdx.x; i < nwb * 8; i += FWG) ((float4*)lx)[i] = *(const float4*)(x + (int64_t)wb0 * QK + 4 * i);
+    } else {
+      for (int i = threadIdx.x; i < nwb * 2; i += FWG) {
+        ((int4*)lq)[i] = *(const int4*)(xq + (int64_t)wb0 * QK + 16 * i);
+        if constexpr (MODE == 2) ((int4*)ll)[i] = *(const int4*)(xl + (int64_t)wb0 * QK + 16 * i);
+      }
+      for (int i = threadIdx.x; i < nwb; i += FWG) lsx[i] = xs[wb0 + i];
+    }
+    __syncthreads();
+    for (int st = 0; st < nwb; st += 8) {
+      const int bl = st + j;  // sub-block within the window
+      const bool ok = bl < nwb;
+      Sub s;
+      decode<F>(row, (int)(wb0 + (ok ? bl : 0)), s);
+      Acc ta, tb;  // the term is fma(ta, tb, p) (quantized) or ta + tb*0 (Dequant)
+      if constexpr (MODE == 0) {
+        // a lane's 32 products in ascending order, binary64
+        const float* xv = lx + (ok ? bl : 0) * QK;
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
+          const float wt = __fadd_rn(__fmul_rn(s.d[i >> 4], (float)lvl), s.c[i >> 4]);
+          acc = __fma_rn((double)wt, (double)xv[i], acc);
+        }
+        ta = acc;
+        tb = 0.0;
+      } else {
+        const int blc = ok ? bl : 0;
+        int a[8];
+        {
+          const int4 a0 = *(const int4*)(lq + blc * QK), a1 = *(const int4*)(lq + blc * QK + 16);
+          a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+        }
+        float part = sub_part(s, a);
+        if constexpr (MODE == 2) {
+          int l8[8];
+          const int4 b0 = *(const int4*)(ll + blc * QK), b1 = *(const int4*)(ll + blc * QK + 16);
+          l8[0] = b0.x; l8[1] = b0.y; l8[2] = b0.z; l8[3] = b0.w; l8[4] = b1.x; l8[5] = b1.y; l8[6] = b1.z; l8[7] = b1.w;
+          part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, l8)));
+        }
+        ta = lsx[blc];
+        tb = part;
+      }
+      // lane j < 4 folds its own sub-block, then lane j + 4's (row shift by 4 inside the 8-lane group)
+      if constexpr (MODE == 0) {
+        const double t2 = dpp_f64<DPP_ROW_SHL4>(ta);
+        p = ok ? __dadd_rn(p, ta) : p;
+        p = bl + 4 < nwb ? __dadd_rn(p, t2) : p;
+      } else {
+        const float ta2 = dpp_f32<DPP_ROW_SHL4>(ta), tb2 = dpp_f32<DPP_ROW_SHL4>(tb);
+        p = ok ? __fmaf_rn(ta, tb, p) : p;
+        p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+      }
+    }
+  }
+  // (P0 + P2) + (P1 + P3): partial q in lane q of the row's eight
+  if constexpr (MODE == 0) {
+    const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL2>(p));
+    const double v = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
+    if (j == 0 && row_ok) y[o] = (float)v;
+  } else {
+    const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL2>(p));
+    const float v = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
+    if (j == 0 && row_ok) y[o] = v;
+  }
+}
+
+template <int F, int MODE>
+hipError_t launch_f(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
+                    const float* xs, float* y, hipStream_t st) {
+  const int64_t rb = K / Geo<F>::V * Geo<F>::B;
+  const int bpb = MODE == 0 ? 4 * QK : (MODE == 2 ? 2 : 1) * QK + 4;  // LDS bytes per staged block
+  int win = (F_LDS_BUDGET / bpb) / 8 * 8;
+  const int64_t nb = K / QK;
+  if (win > nb) win = (int)((nb + 7) / 8 * 8);
+  const dim3 grid((unsigned)((N + FROWS - 1) / FROWS)), block(FWG);
+  hipLaunchKernelGGL((k_gemv_fmt<F, MODE>), grid, block, (size_t)win * bpb, st, w, rb, N, K, x, xq, xl, xs, win, y);
+  return hipGetLastError();
+}
+
+template <int F>
+hipError_t launch_fm(int mode, const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq,
+                     const int8_t* xl, const float* xs, float* y, hipStream_t st) {
+  if (mode == 0) return launch_f<F, 0>(w, N, K, x, xq, xl, xs, y, st);
+  if (mode == 1) return launch_f<F, 1>(w, N, K, x, xq, xl, xs, y, st);
+  return launch_f<F, 2>(w, N, K, x, xq, xl, xs, y, st);
+}
+
+}  // namespace
+
+// Values per block and bytes per block of a format (0, 0 if unknown).
+void fmt_geometry(int fmt, int& values, int& bytes) {
+  values = 32;
+  switch (fmt) {
+    case F_Q4_0: bytes = 18; break;
+    case F_Q4_1: bytes = 20; break;
+    case F_Q5_0: bytes = 22; break;
+    case F_Q5_1: bytes = 24; break;
+    case F_IQ4_NL: bytes = 18; break;
+    case F_MXFP4: bytes = 17; break;
+    case F_Q2_K: values = 256; bytes = 84; break;
+    case F_Q3_K: values = 256; bytes = 110; break;
+    case F_Q4_K: values = 256; bytes = 144; break;
+    case F_Q5_K: values = 256; bytes = 176; break;
+    case F_Q6_K: values = 256; bytes = 210; break;
+    case F_IQ4_XS: values = 256; bytes = 136; break;
+    default: values = 0; bytes = 0;
+  }
+}
+
+hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
+                           const int8_t* xq, const int8_t* xl, const float* xs, float* y, hipStream_t st) {
+  switch (fmt) {
+    case F_Q4_0: return launch_fm<F_Q4_0>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q4_1: return launch_fm<F_Q4_1>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q5_0: return launch_fm<F_Q5_0>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q5_1: return launch_fm<F_Q5_1>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_IQ4_NL: return launch_fm<F_IQ4_NL>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_MXFP4: return launch_fm<F_MXFP4>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q2_K: return launch_fm<F_Q2_K>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q3_K: return launch_fm<F_Q3_K>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q4_K: return launch_fm<F_Q4_K>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q5_K: return launch_fm<F_Q5_K>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q6_K: return launch_fm<F_Q6_K>(mode, w, N, K, x, xq, xl, xs, y, st);
+    default: return launch_fm<F_IQ4_XS>(mode, w, N, K, x, xq, xl, xs, y, st);
+  }
+}
+
+}  // namespace qdg

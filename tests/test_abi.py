@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -282,6 +282,30 @@ def test_glu_validation():
     assert call(hs=A + 2) == EALIGN
     assert call(mode=2, xl=A, hl=A, K=13216) == EMODE   # the activation and 64 rows of scales exceed LDS
     assert call(mode=1, K=15808) == EMODE
+
+
+def test_fmt_validation():
+    for fmt in oracle.FORMATS:
+        for K in (256, 512, 5120):
+            assert q.fmt_row_bytes(fmt, K) == oracle.fmt_row_bytes(fmt, K), (fmt, K)
+    assert q.fmt_row_bytes(8, 256) == 0            # Q8_0 is the split layout, not this call's
+    assert q.fmt_row_bytes(12, 300) == 0
+    f = lib.qdg_gemv_fmt
+
+    def call(fmt=2, mode=1, w=A, N=64, K=512, x=None, xq=A, xl=None, xs=A, y=A):
+        return f(fmt, mode, P(w), N, K, P(x), P(xq), P(xl), P(xs), P(y), None)
+
+    assert call(fmt=8) == EINVAL
+    assert call(mode=3) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(mode=0) == EINVAL                       # Dequant reads x
+    assert call(mode=2) == EINVAL                       # TwoPass needs xl
+    assert call(K=500) == ESHAPE
+    assert call(fmt=12, K=480) == ESHAPE                # Q4_K needs whole 256-value super-blocks
+    assert call(N=0) == ESHAPE
+    assert call(w=A + 8) == EALIGN
+    assert call(xq=A + 4) == EALIGN
+    assert call(y=A + 2) == EALIGN
 
 
 def test_stream_read_validation():

@@ -1,0 +1,82 @@
+"""GPU parity of the block-format GEMV (qdg_gemv_fmt) against the CPU oracle,
+for all twelve GGUF formats and all three numerics modes.
+
+Bar: the quantized modes bit-exact (the kernel runs the oracle's order); Dequant
+(a binary64 sum in the kernel's own fixed order) within one unit in the last
+place of the oracle's binary32 result and equal to it almost everywhere; every
+call byte-identical on repeat.  Row sizes include ones that leave rows 2 bytes
+off a 4-byte boundary (the loaders' 2-byte path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_gemv_02_amd as q
+from gguf_blocks import SUPER, encode
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def shapes(fmt):
+    if fmt in SUPER:
+        return [(37, 256), (5, 512), (70, 2560), (300, 5120)]
+    return [(37, 288), (5, 512), (70, 1600), (300, 5120)]
+
+
+CASES = [(f, N, K) for f in oracle.FORMATS for (N, K) in shapes(f)]
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("fmt,N,K", CASES)
+def test_fmt_quantized_bit_exact(fmt, N, K, mode):
+    announce(f"gemv_fmt fmt={fmt} mode={mode} N={N} K={K}")
+    rng = np.random.default_rng(1000 * fmt + N + K + mode)
+    w, _, _, _ = encode(fmt, N, K, rng)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    x[0, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.gemv_fmt(fmt, mode, w, N, K, xq=oq, xl=ol, xs=os_, nthreads=8)
+    dw = dev(w.reshape(-1))
+    xq, xl, xs = dev(oq), None if ol is None else dev(ol), dev(os_)
+    outs = []
+    for rep in range(2):
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_fmt(fmt, mode, dw, N, K, y, xq=xq, xl=xl, xs=xs)
+        outs.append(host(y))
+    np.testing.assert_array_equal(outs[0], want[0])
+    assert outs[0].tobytes() == outs[1].tobytes()
+
+
+@pytest.mark.parametrize("fmt,N,K", CASES)
+def test_fmt_dequant(fmt, N, K):
+    announce(f"gemv_fmt fmt={fmt} dequant N={N} K={K}")
+    rng = np.random.default_rng(2000 * fmt + N + K)
+    w, _, _, _ = encode(fmt, N, K, rng)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    want = oracle.gemv_fmt(fmt, 0, w, N, K, x=x, nthreads=8)[0]
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_fmt(fmt, 0, dev(w.reshape(-1)), N, K, y, x=dev(x))
+    got = host(y)
+    d = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert d.max() <= 1, (int(d.max()), int(d.argmax()))
+    if N >= 20:
+        assert np.mean(d == 0) >= 0.95
+    y2 = torch.empty_like(y)
+    q.gemv_fmt(fmt, 0, dev(w.reshape(-1)), N, K, y2, x=dev(x))
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))

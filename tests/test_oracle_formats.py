@@ -145,3 +145,26 @@ def test_twopass_low_words_weigh_one_128th():
     y = oracle.gemv_fmt(Q4_0, 2, w, N, K, xq=xq, xl=xl, xs=xs)
     want = (d.repeat(16, axis=1) * lv) @ xl[0].astype(np.float64) / 128.0
     np.testing.assert_array_equal(y[0], want.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, 12, 14, MXFP4])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_split_integer_case(fmt, mode):
+    """Split into chunks (the split-K chunk rule) and added in ascending order: in
+    the integer case every split count gives the exact integer product, so every
+    sub-block is summed once, in one chunk."""
+    rng = np.random.default_rng(400 + fmt + mode)
+    N, K = 4, 2560
+    w, lv, d, c = encode(fmt, N, K, rng, small=True)
+    wt = (d.repeat(16, axis=1).astype(np.int64) * lv + c.repeat(16, axis=1).astype(np.int64))
+    if mode == 0:
+        x = rng.integers(-20, 21, (1, K)).astype(np.float32)
+        want = wt @ x[0].astype(np.int64)
+        kw = dict(x=x)
+    else:
+        xq, xl, xs = _act(mode, K, rng, True)
+        want = wt @ (xq[0].astype(np.int64) * (128 if mode == 2 else 1) + (xl[0].astype(np.int64) if mode == 2 else 0))
+        kw = dict(xq=xq, xl=xl, xs=xs)
+    for S in (1, 2, 3, 5, 16):
+        y = oracle.gemv_fmt(fmt, mode, w, N, K, splits=S, **kw)
+        np.testing.assert_array_equal(y[0], want.astype(np.float32), err_msg=f"S={S}")
