@@ -343,11 +343,20 @@ int64_t qdg_fmt_row_bytes(int fmt, int64_t K);
  *               operation, TwoPass adding fl(2^-7 * the same with the low
  *               words); p <- fma(xs[g], part, p) into partial g mod 4 in
  *               ascending g, then (P0 + P2) + (P1 + P3).
+ * splits: the row is cut into the chunks of the QWEN38 page's split-K rule
+ * (gk_gemv_hl_sk: 512-value groups, ceil(groups / splits) a chunk, the K mod 512
+ * tail in the last), each chunk summed as above from +0 and the chunk partials
+ * added in ascending chunk order from +0 (gk_sk_combine) -- in binary32 for the
+ * quantized modes, binary64 before the one rounding for QDG_DEQUANT.  splits == 1
+ * is the unsplit row.  The chunks run as waves of one workgroup: at most 16
+ * non-empty chunks (QDG_EMODE otherwise).
  * Batch 1.  w 16-byte aligned; x, xq, xl 16-byte aligned; y [N].  N >= 1 and K
- * a positive whole number of the format's blocks.
+ * a positive whole number of the format's blocks; 1 <= splits <= QDG_MAX_SPLITS
+ * (QDG_EINVAL otherwise).
  */
 int qdg_gemv_fmt(int fmt, int mode, const uint8_t *w, int64_t N, int64_t K, const float *x,
-                 const int8_t *xq, const int8_t *xl, const float *xs, float *y, qdg_stream stream);
+                 const int8_t *xq, const int8_t *xl, const float *xs, int splits, float *y,
+                 qdg_stream stream);
 
 /*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library

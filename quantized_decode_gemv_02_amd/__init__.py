@@ -76,7 +76,7 @@ _SIGS = {
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
-    "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P], _I),
+    "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -230,20 +230,23 @@ def fmt_row_bytes(fmt: int, K: int) -> int:
     return int(_lib.qdg_fmt_row_bytes(fmt, K))
 
 
-def _fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs):
+def _fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs, splits):
     if w.numel() < N * fmt_row_bytes(fmt, K):
         raise ValueError("gemv_fmt: w is smaller than N rows of the format")
     return (fmt, mode, _ptr(w, (_torch().uint8, _torch().int8), "w"), N, K, _ptr(x, _f32(), "x"),
-            _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(y, _f32(), "y"), _stream())
+            _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), splits, _ptr(y, _f32(), "y"),
+            _stream())
 
 
-def gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None) -> None:
-    """``y [N] = W x`` for ``w``, N rows of K values in GGUF block format ``fmt`` (bytes as stored)."""
-    _check("qdg_gemv_fmt", _lib.qdg_gemv_fmt(*_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs)))
+def gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None, splits: int = 1) -> None:
+    """``y [N] = W x`` for ``w``, N rows of K values in GGUF block format ``fmt`` (bytes as stored),
+    the row cut into ``splits`` split-K chunks added in ascending order."""
+    _check("qdg_gemv_fmt", _lib.qdg_gemv_fmt(*_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs, splits)))
 
 
-def bind_gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None) -> Bound:
-    return Bound("qdg_gemv_fmt", *_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs))
+def bind_gemv_fmt(fmt: int, mode: int, w, N: int, K: int, y, x=None, xq=None, xl=None, xs=None,
+                  splits: int = 1) -> Bound:
+    return Bound("qdg_gemv_fmt", *_fmt_args(fmt, mode, w, N, K, y, x, xq, xl, xs, splits))
 
 
 MAX_PARTS = 6

@@ -244,7 +244,7 @@ int64_t qdg_fmt_row_bytes(int fmt, int64_t K) {
 }
 
 int qdg_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq,
-                 const int8_t* xl, const float* xs, float* y, qdg_stream stream) {
+                 const int8_t* xl, const float* xs, int splits, float* y, qdg_stream stream) {
   if (mode < QDG_DEQUANT || mode > QDG_TWOPASS || !w || !y) return QDG_EINVAL;
   int values, bytes;
   qdg::fmt_geometry(fmt, values, bytes);
@@ -252,11 +252,13 @@ int qdg_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, cons
   if (mode == QDG_DEQUANT && (!x || xq || xl || xs)) return QDG_EINVAL;
   if (mode != QDG_DEQUANT && (x || !xq || !xs)) return QDG_EINVAL;
   if ((mode == QDG_TWOPASS) != (xl != nullptr)) return QDG_EINVAL;
-  if (!shape_ok(N, K) || K % values || N / 32 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_EINVAL;
+  if (!shape_ok(N, K) || K % values || N / 8 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
   if (!aligned(w, 16) || !aligned(y, 4) || (x && !aligned(x, 16)) || (xq && !aligned(xq, 16)) ||
       (xl && !aligned(xl, 16)) || (xs && !aligned(xs, 4)))
     return QDG_EALIGN;
-  return hip_status(qdg::launch_gemv_fmt(fmt, mode, w, N, K, x, xq, xl, xs, y, as_stream(stream)));
+  if (qdg::fmt_chunk_waves(K, splits) > 16) return QDG_EMODE;
+  return hip_status(qdg::launch_gemv_fmt(fmt, mode, w, N, K, x, xq, xl, xs, splits, y, as_stream(stream)));
 }
 
 int qdg_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, void* workspace, size_t workspace_bytes,

@@ -316,8 +316,10 @@ hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float*
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
 bool glu_fits(int mode, int64_t K);
 void fmt_geometry(int fmt, int& values, int& bytes);
+int fmt_chunk_waves(int64_t K, int splits);
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
-                           const int8_t* xq, const int8_t* xl, const float* xs, float* y, hipStream_t st);
+                           const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                           hipStream_t st);
 hipError_t launch_gemv_glu(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
                            int64_t F, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h,
                            int8_t* hq, int8_t* hl, float* hs, hipStream_t st);

@@ -20,7 +20,9 @@
 // Mapping: a wave takes 8 rows, 8 lanes a row, one sub-block a lane, so a step
 // covers 8 consecutive sub-blocks of a row (one super-block of the K-quants).
 // Lane j < 4 of a row owns partial j: it folds its own sub-block, then the one
-// of lane j + 4 (one DPP row shift).  The activation window is staged in LDS.
+// of lane j + 4 (one DPP row shift).  Split-K (the QWEN38 page's chunk rule,
+// gk_gemv_hl_sk / gk_sk_combine): the chunks are waves of one workgroup and
+// their partials are added in ascending order in LDS.
 #include <stdlib.h>
 
 #include "qdg_device.h"
@@ -28,9 +30,6 @@
 namespace qdg {
 namespace {
 
-constexpr int FWG = 256;                // four waves, 32 rows
-constexpr int FROWS = 32;
-constexpr int F_LDS_BUDGET = 24 * 1024;
 
 enum : int {
   F_Q4_0 = 2, F_Q4_1 = 3, F_Q5_0 = 6, F_Q5_1 = 7, F_Q2_K = 10, F_Q3_K = 11, F_Q4_K = 12,
@@ -296,117 +295,144 @@ __device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8]) {
   return __fadd_rn(part, __fmul_rn(s.c[1], (float)sh1));
 }
 
-template <int F, int MODE>
-__global__ __launch_bounds__(FWG) void k_gemv_fmt(const uint8_t* __restrict__ w, int64_t rb, int64_t N, int64_t K,
-                                                  const float* __restrict__ x, const int8_t* __restrict__ xq,
-                                                  const int8_t* __restrict__ xl, const float* __restrict__ xs,
-                                                  int win, float* __restrict__ y) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane >> 3, j = lane & 7;
-  const int64_t nb = K / QK;
-  const int64_t o = (int64_t)blockIdx.x * FROWS + wave * 8 + r;
-  const bool row_ok = o < N;
-  const uint8_t* row = w + (row_ok ? o : N - 1) * rb;
-  // window: quantized modes [win][32] words (+ low words) and [win] scales; Dequant [win][32] f32
-  int8_t* lq = (int8_t*)lds;
-  int8_t* ll = lq + (int64_t)win * QK;
-  float* lsx = (float*)(lds + (int64_t)win * QK * (MODE == 2 ? 2 : 1));
-  float* lx = (float*)lds;
-
+// A workgroup: R row groups of 8 rows times one wave per non-empty chunk of the
+// S-chunk split rule (S = 1: the whole row).  Wave (rg, c) sums chunk c of its
+// 8 rows; the chunk partials meet in LDS and a thread per row adds them in
+// ascending chunk order from 0 (empty chunks, whose partial is +0, skipped).
+// The activation is read straight from global memory (L1/L2-resident): the 8
+// rows of a wave share each sub-block's activation.
+template <int F, int MODE, int R>
+__global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w, int64_t rb, int64_t N, int64_t K,
+                                                   const float* __restrict__ x, const int8_t* __restrict__ xq,
+                                                   const int8_t* __restrict__ xl, const float* __restrict__ xs, int S,
+                                                   int m, int ceff, float* __restrict__ y) {
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
+  __shared__ Acc lpart[16][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = wave / ceff, cw = wave % ceff;
+  const int chunk = cw < m ? cw : S - 1;
+  const int r = lane >> 3, j = lane & 7;
+  const int64_t o_wg = (int64_t)blockIdx.x * (8 * R);
+  const int64_t o = o_wg + 8 * rg + r;
+  const uint8_t* row = w + (o < N ? o : N - 1) * rb;
+  int32_t g0, g1;
+  split_range(K, S, chunk, g0, g1);
+
   Acc p = 0;
-  for (int wb0 = 0; wb0 < nb; wb0 += win) {
-    const int nwb = (int)((nb - wb0) < win ? (nb - wb0) : win);
-    __syncthreads();
+  for (int st = g0; st < g1; st += 8) {
+    const int g = st + j;  // this lane's sub-block
+    const bool ok = g < g1;
+    const int gc = ok ? g : g0;
+    Sub s;
+    decode<F>(row, gc, s);
+    Acc ta, tb;
     if constexpr (MODE == 0) {
-      for (int i = threadIdx.x; i < nwb * 8; i += FWG) ((float4*)lx)[i] = *(const float4*)(x + (int64_t)wb0 * QK + 4 * i);
-    } else {
-      for (int i = threadIdx.x; i < nwb * 2; i += FWG) {
-        ((int4*)lq)[i] = *(const int4*)(xq + (int64_t)wb0 * QK + 16 * i);
-        if constexpr (MODE == 2) ((int4*)ll)[i] = *(const int4*)(xl + (int64_t)wb0 * QK + 16 * i);
-      }
-      for (int i = threadIdx.x; i < nwb; i += FWG) lsx[i] = xs[wb0 + i];
-    }
-    __syncthreads();
-    for (int st = 0; st < nwb; st += 8) {
-      const int bl = st + j;  // sub-block within the window
-      const bool ok = bl < nwb;
-      Sub s;
-      decode<F>(row, (int)(wb0 + (ok ? bl : 0)), s);
-      Acc ta, tb;  // the term is fma(ta, tb, p) (quantized) or ta + tb*0 (Dequant)
-      if constexpr (MODE == 0) {
-        // a lane's 32 products in ascending order, binary64
-        const float* xv = lx + (ok ? bl : 0) * QK;
-        double acc = 0.0;
+      // a lane's 32 products in ascending order, binary64
+      const float4* xv = (const float4*)(x + (int64_t)gc * QK);
+      double acc = 0.0;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 xx = xv[q4];
+        const float xe[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
           const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
           const float wt = __fadd_rn(__fmul_rn(s.d[i >> 4], (float)lvl), s.c[i >> 4]);
-          acc = __fma_rn((double)wt, (double)xv[i], acc);
+          acc = __fma_rn((double)wt, (double)xe[e], acc);
         }
-        ta = acc;
-        tb = 0.0;
-      } else {
-        const int blc = ok ? bl : 0;
-        int a[8];
-        {
-          const int4 a0 = *(const int4*)(lq + blc * QK), a1 = *(const int4*)(lq + blc * QK + 16);
-          a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-        }
-        float part = sub_part(s, a);
-        if constexpr (MODE == 2) {
-          int l8[8];
-          const int4 b0 = *(const int4*)(ll + blc * QK), b1 = *(const int4*)(ll + blc * QK + 16);
-          l8[0] = b0.x; l8[1] = b0.y; l8[2] = b0.z; l8[3] = b0.w; l8[4] = b1.x; l8[5] = b1.y; l8[6] = b1.z; l8[7] = b1.w;
-          part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, l8)));
-        }
-        ta = lsx[blc];
-        tb = part;
       }
-      // lane j < 4 folds its own sub-block, then lane j + 4's (row shift by 4 inside the 8-lane group)
-      if constexpr (MODE == 0) {
-        const double t2 = dpp_f64<DPP_ROW_SHL4>(ta);
-        p = ok ? __dadd_rn(p, ta) : p;
-        p = bl + 4 < nwb ? __dadd_rn(p, t2) : p;
-      } else {
-        const float ta2 = dpp_f32<DPP_ROW_SHL4>(ta), tb2 = dpp_f32<DPP_ROW_SHL4>(tb);
-        p = ok ? __fmaf_rn(ta, tb, p) : p;
-        p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+      ta = acc;
+      tb = 0.0;
+    } else {
+      int a[8];
+      {
+        const int4 a0 = *(const int4*)(xq + (int64_t)gc * QK), a1 = *(const int4*)(xq + (int64_t)gc * QK + 16);
+        a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
       }
+      float part = sub_part(s, a);
+      if constexpr (MODE == 2) {
+        int l8[8];
+        const int4 b0 = *(const int4*)(xl + (int64_t)gc * QK), b1 = *(const int4*)(xl + (int64_t)gc * QK + 16);
+        l8[0] = b0.x; l8[1] = b0.y; l8[2] = b0.z; l8[3] = b0.w; l8[4] = b1.x; l8[5] = b1.y; l8[6] = b1.z; l8[7] = b1.w;
+        part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, l8)));
+      }
+      ta = xs[gc];
+      tb = part;
+    }
+    // lane j < 4 folds its own sub-block, then lane j + 4's (row shift by 4 inside the 8-lane group)
+    if constexpr (MODE == 0) {
+      const double t2 = dpp_f64<DPP_ROW_SHL4>(ta);
+      p = ok ? __dadd_rn(p, ta) : p;
+      p = g + 4 < g1 ? __dadd_rn(p, t2) : p;
+    } else {
+      const float ta2 = dpp_f32<DPP_ROW_SHL4>(ta), tb2 = dpp_f32<DPP_ROW_SHL4>(tb);
+      p = ok ? __fmaf_rn(ta, tb, p) : p;
+      p = g + 4 < g1 ? __fmaf_rn(ta2, tb2, p) : p;
     }
   }
   // (P0 + P2) + (P1 + P3): partial q in lane q of the row's eight
+  Acc v;
   if constexpr (MODE == 0) {
     const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL2>(p));
-    const double v = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
-    if (j == 0 && row_ok) y[o] = (float)v;
+    v = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
   } else {
     const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL2>(p));
-    const float v = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
-    if (j == 0 && row_ok) y[o] = v;
+    v = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
   }
+  if (j == 0) lpart[wave][r] = v;
+  __syncthreads();
+  if ((int)threadIdx.x < 8 * R) {
+    const int gq = threadIdx.x >> 3, rq = threadIdx.x & 7;
+    const int64_t oo = o_wg + threadIdx.x;
+    if (oo < N) {
+      if (ceff == 1) {
+        y[oo] = (float)lpart[gq][rq];
+      } else {
+        Acc a = 0;
+        for (int cc = 0; cc < ceff; ++cc) a = a + lpart[gq * ceff + cc][rq];
+        y[oo] = (float)a;
+      }
+    }
+  }
+}
+
+// The non-empty chunks of the S-chunk rule: chunks 0..m-1, then chunk S-1 when
+// it holds the K mod 512 tail (or all of K when K < 512).
+void f_chunks(int64_t K, int S, int& m, int& ceff) {
+  const int64_t nq = K / 512, per = (nq + S - 1) / S;
+  m = per > 0 ? (int)((nq + per - 1) / per) : 0;
+  if (m > S) m = S;
+  ceff = m;
+  if (m < S && ((K % 512) != 0 || m == 0)) ceff = m + 1;
+}
+
+template <int F, int MODE, int R>
+hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int S, int m, int ceff, float* y, hipStream_t st) {
+  const int64_t rb = K / Geo<F>::V * Geo<F>::B;
+  const dim3 grid((unsigned)((N + 8 * R - 1) / (8 * R))), block((unsigned)(64 * R * ceff));
+  hipLaunchKernelGGL((k_gemv_fmt<F, MODE, R>), grid, block, 0, st, w, rb, N, K, x, xq, xl, xs, S, m, ceff, y);
+  return hipGetLastError();
 }
 
 template <int F, int MODE>
 hipError_t launch_f(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
-                    const float* xs, float* y, hipStream_t st) {
-  const int64_t rb = K / Geo<F>::V * Geo<F>::B;
-  const int bpb = MODE == 0 ? 4 * QK : (MODE == 2 ? 2 : 1) * QK + 4;  // LDS bytes per staged block
-  int win = (F_LDS_BUDGET / bpb) / 8 * 8;
-  const int64_t nb = K / QK;
-  if (win > nb) win = (int)((nb + 7) / 8 * 8);
-  const dim3 grid((unsigned)((N + FROWS - 1) / FROWS)), block(FWG);
-  hipLaunchKernelGGL((k_gemv_fmt<F, MODE>), grid, block, (size_t)win * bpb, st, w, rb, N, K, x, xq, xl, xs, win, y);
-  return hipGetLastError();
+                    const float* xs, int S, float* y, hipStream_t st) {
+  int m, ceff;
+  f_chunks(K, S, m, ceff);
+  if (S == 1) m = 1, ceff = 1;
+  // two row groups a workgroup where the chunk waves leave room, else one
+  if (2 * ceff <= 16) return launch_fr<F, MODE, 2>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
+  return launch_fr<F, MODE, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
 }
 
 template <int F>
 hipError_t launch_fm(int mode, const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq,
-                     const int8_t* xl, const float* xs, float* y, hipStream_t st) {
-  if (mode == 0) return launch_f<F, 0>(w, N, K, x, xq, xl, xs, y, st);
-  if (mode == 1) return launch_f<F, 1>(w, N, K, x, xq, xl, xs, y, st);
-  return launch_f<F, 2>(w, N, K, x, xq, xl, xs, y, st);
+                     const int8_t* xl, const float* xs, int S, float* y, hipStream_t st) {
+  if (mode == 0) return launch_f<F, 0>(w, N, K, x, xq, xl, xs, S, y, st);
+  if (mode == 1) return launch_f<F, 1>(w, N, K, x, xq, xl, xs, S, y, st);
+  return launch_f<F, 2>(w, N, K, x, xq, xl, xs, S, y, st);
 }
 
 }  // namespace
@@ -431,21 +457,27 @@ void fmt_geometry(int fmt, int& values, int& bytes) {
   }
 }
 
+int fmt_chunk_waves(int64_t K, int splits) {
+  int m, ceff;
+  f_chunks(K, splits, m, ceff);
+  return splits == 1 ? 1 : ceff;
+}
+
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
-                           const int8_t* xq, const int8_t* xl, const float* xs, float* y, hipStream_t st) {
+                           const int8_t* xq, const int8_t* xl, const float* xs, int S, float* y, hipStream_t st) {
   switch (fmt) {
-    case F_Q4_0: return launch_fm<F_Q4_0>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q4_1: return launch_fm<F_Q4_1>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q5_0: return launch_fm<F_Q5_0>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q5_1: return launch_fm<F_Q5_1>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_IQ4_NL: return launch_fm<F_IQ4_NL>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_MXFP4: return launch_fm<F_MXFP4>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q2_K: return launch_fm<F_Q2_K>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q3_K: return launch_fm<F_Q3_K>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q4_K: return launch_fm<F_Q4_K>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q5_K: return launch_fm<F_Q5_K>(mode, w, N, K, x, xq, xl, xs, y, st);
-    case F_Q6_K: return launch_fm<F_Q6_K>(mode, w, N, K, x, xq, xl, xs, y, st);
-    default: return launch_fm<F_IQ4_XS>(mode, w, N, K, x, xq, xl, xs, y, st);
+    case F_Q4_0: return launch_fm<F_Q4_0>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q4_1: return launch_fm<F_Q4_1>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q5_0: return launch_fm<F_Q5_0>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q5_1: return launch_fm<F_Q5_1>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_IQ4_NL: return launch_fm<F_IQ4_NL>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_MXFP4: return launch_fm<F_MXFP4>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q2_K: return launch_fm<F_Q2_K>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q3_K: return launch_fm<F_Q3_K>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q4_K: return launch_fm<F_Q4_K>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q5_K: return launch_fm<F_Q5_K>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    case F_Q6_K: return launch_fm<F_Q6_K>(mode, w, N, K, x, xq, xl, xs, S, y, st);
+    default: return launch_fm<F_IQ4_XS>(mode, w, N, K, x, xq, xl, xs, S, y, st);
   }
 }
 

@@ -292,8 +292,8 @@ def test_fmt_validation():
     assert q.fmt_row_bytes(12, 300) == 0
     f = lib.qdg_gemv_fmt
 
-    def call(fmt=2, mode=1, w=A, N=64, K=512, x=None, xq=A, xl=None, xs=A, y=A):
-        return f(fmt, mode, P(w), N, K, P(x), P(xq), P(xl), P(xs), P(y), None)
+    def call(fmt=2, mode=1, w=A, N=64, K=512, x=None, xq=A, xl=None, xs=A, y=A, splits=1):
+        return f(fmt, mode, P(w), N, K, P(x), P(xq), P(xl), P(xs), splits, P(y), None)
 
     assert call(fmt=8) == EINVAL
     assert call(mode=3) == EINVAL
@@ -306,6 +306,9 @@ def test_fmt_validation():
     assert call(w=A + 8) == EALIGN
     assert call(xq=A + 4) == EALIGN
     assert call(y=A + 2) == EALIGN
+    assert call(splits=0) == EINVAL
+    assert call(splits=65) == EINVAL
+    assert call(K=512 * 17, splits=17) == EMODE          # 17 non-empty chunks: more waves than a workgroup holds
 
 
 def test_stream_read_validation():

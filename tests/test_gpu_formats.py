@@ -80,3 +80,42 @@ def test_fmt_dequant(fmt, N, K):
     y2 = torch.empty_like(y)
     q.gemv_fmt(fmt, 0, dev(w.reshape(-1)), N, K, y2, x=dev(x))
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+
+
+def split_cases(fmt):
+    ragged = 2816 if fmt in SUPER else 1600          # whole 512-value groups plus a tail
+    small = 256 if fmt in SUPER else 288             # below one group: all of it in the last chunk
+    return [(300, 5120, 5), (300, 5120, 16), (70, ragged, 3), (37, small, 4), (45, 4608, 2)]
+
+
+SPLIT_CASES = [(f, N, K, S) for f in oracle.FORMATS for (N, K, S) in split_cases(f)]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("fmt,N,K,S", SPLIT_CASES)
+def test_fmt_split(fmt, N, K, S, mode):
+    """Split-K chunks as waves of a workgroup, added in ascending order: the
+    quantized modes bit-exact with the oracle's chunked sum, Dequant within one
+    unit in the last place of it."""
+    announce(f"gemv_fmt split fmt={fmt} mode={mode} N={N} K={K} S={S}")
+    rng = np.random.default_rng(3000 * fmt + N + K + 7 * S + mode)
+    w, _, _, _ = encode(fmt, N, K, rng)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    dw = dev(w.reshape(-1))
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    y2 = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    if mode == 0:
+        want = oracle.gemv_fmt(fmt, 0, w, N, K, x=x, splits=S, nthreads=8)[0]
+        for t in (y, y2):
+            q.gemv_fmt(fmt, 0, dw, N, K, t, x=dev(x), splits=S)
+        got = host(y)
+        d = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert d.max() <= 1, (int(d.max()), int(d.argmax()))
+    else:
+        oq, ol, os_ = oracle.quantize(mode, x)
+        want = oracle.gemv_fmt(fmt, mode, w, N, K, xq=oq, xl=ol, xs=os_, splits=S, nthreads=8)[0]
+        xq, xl, xs = dev(oq), None if ol is None else dev(ol), dev(os_)
+        for t in (y, y2):
+            q.gemv_fmt(fmt, mode, dw, N, K, t, xq=xq, xl=xl, xs=xs, splits=S)
+        np.testing.assert_array_equal(host(y), want)
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
