@@ -108,13 +108,14 @@ struct Sub {
   float d[2], c[2];
 };
 
-// Sub-block sb of a row (lane kernel library page, lk_sub: the same layouts).
+// One sub-block (lane kernel library page, lk_sub: the same layouts): b is its
+// 32-value block, or for the K-quants and IQ4_XS its 256-value super-block with
+// the sub-block at position j (0-7).
 template <int F>
-__device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, Sub& s) {
+__device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub& s) {
   s.off = 0;
   s.c[0] = s.c[1] = 0.0f;
   if constexpr (F == F_Q4_0 || F == F_IQ4_NL || F == F_Q4_1) {
-    const uint8_t* b = row + (int64_t)sb * Geo<F>::B;
     unsigned q[4];
     if constexpr (F == F_Q4_1) {
       const unsigned hd = ld_u32(b);
@@ -144,7 +145,6 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
       if constexpr (F == F_Q4_0) s.off = 8;
     }
   } else if constexpr (F == F_Q5_0 || F == F_Q5_1) {
-    const uint8_t* b = row + (int64_t)sb * Geo<F>::B;
     unsigned qh, q[4];
     if constexpr (F == F_Q5_1) {
       const unsigned hd = ld_u32(b);
@@ -166,7 +166,6 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
       s.w[4 + i] = hi_nib(q[i]) | spread4((qh >> (16 + 4 * i)) & 15u);
     }
   } else if constexpr (F == F_MXFP4) {
-    const uint8_t* b = row + (int64_t)sb * 17;
     const unsigned e = ld_u8(b);
     const unsigned bits = e < 2 ? (0x00200000u << e) : ((e - 1) << 23);  // 2^(e - 128)
     s.d[0] = s.d[1] = __uint_as_float(bits);
@@ -180,8 +179,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
       s.w[4 + i] = table16(hi_nib(q), t);
     }
   } else if constexpr (F == F_Q4_K || F == F_Q5_K) {
-    const uint8_t* b = row + (int64_t)(sb >> 3) * Geo<F>::B;
-    const int j = sb & 7, pair = j >> 1, upper = j & 1;
+    const int pair = j >> 1, upper = j & 1;
     const int4 hd = *(const int4*)b;  // d, dmin, 12 scale bytes
     const unsigned sw[3] = {(unsigned)hd.y, (unsigned)hd.z, (unsigned)hd.w};
     auto sbyte = [&](int i) { return (sw[i >> 2] >> (8 * (i & 3))) & 255u; };
@@ -209,8 +207,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
       for (int i = 0; i < 8; ++i) s.w[i] |= ((qh[i] >> j) & 0x01010101u) << 4;
     }
   } else if constexpr (F == F_Q6_K) {
-    const uint8_t* b = row + (int64_t)(sb >> 3) * 210;
-    const int j = sb & 7, half = j >> 2, k = j & 3;
+    const int half = j >> 2, k = j & 3;
     unsigned ql[8], qh[8];
     ld_words<8>(b + 64 * half + 32 * (k & 1), ql);
     ld_words<8>(b + 128 + 32 * half, qh);
@@ -223,8 +220,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
       s.w[i] = ((k & 2) ? hi_nib(ql[i]) : lo_nib(ql[i])) | (((qh[i] >> (2 * k)) & 0x03030303u) << 4);
     s.off = 32;
   } else if constexpr (F == F_Q2_K) {
-    const uint8_t* b = row + (int64_t)(sb >> 3) * 84;  // 4-byte aligned: 84 is a multiple of 4
-    const int j = sb & 7, half = j >> 2, k = j & 3;
+    const int half = j >> 2, k = j & 3;  // b 4-byte aligned: 84 is a multiple of 4
     unsigned q[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[i] = ld_u32(b + 16 + 32 * half + 4 * i);
@@ -240,8 +236,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) s.w[i] = (q[i] >> (2 * k)) & 0x03030303u;
   } else if constexpr (F == F_Q3_K) {
-    const uint8_t* b = row + (int64_t)(sb >> 3) * 110;
-    const int j = sb & 7, half = j >> 2, k = j & 3;
+    const int half = j >> 2, k = j & 3;
     unsigned hm[8], q[8], sp[3];
     ld_words<8>(b, hm);
     ld_words<8>(b + 32 + 32 * half, q);
@@ -260,8 +255,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ row, int sb, 
     for (int i = 0; i < 8; ++i) s.w[i] = ((q[i] >> (2 * k)) & 0x03030303u) | (((hm[i] >> mbit) & 0x01010101u) << 2);
     s.off = 4;  // level = low2 - 4 + 4*high bit
   } else if constexpr (F == F_IQ4_XS) {
-    const uint8_t* b = row + (int64_t)(sb >> 3) * 136;  // 8-byte aligned
-    const int ib = sb & 7;
+    const int ib = j;  // b 8-byte aligned
     const unsigned h0 = ld_u32(b), h1 = ld_u32(b + 4);
     const unsigned sh = h0 >> 16, sl = (h1 >> (8 * (ib >> 1))) & 255u;
     const int ls = (int)((sl >> (4 * (ib & 1))) & 15u) | (int)(((sh >> (2 * ib)) & 3u) << 4);
@@ -295,103 +289,233 @@ __device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8]) {
   return __fadd_rn(part, __fmul_rn(s.c[1], (float)sh1));
 }
 
-// A workgroup: R row groups of 8 rows times one wave per non-empty chunk of the
-// S-chunk split rule (S = 1: the whole row).  Wave (rg, c) sums chunk c of its
-// 8 rows; the chunk partials meet in LDS and a thread per row adds them in
+// The activation of one 32-value block in registers: Dequant's 32 binary32
+// values, or the quantized modes' words (h, and l under TwoPass) and scale.
+template <int MODE>
+struct Act {
+  int a[8], l[8];
+  float s;
+};
+template <>
+struct Act<0> {
+  float4 x[8];
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_act(int gc, const float* __restrict__ x, const int8_t* __restrict__ xq,
+                                         const int8_t* __restrict__ xl, const float* __restrict__ xs, Act<MODE>& A) {
+  if constexpr (MODE == 0) {
+    const float4* xv = (const float4*)(x + (int64_t)gc * QK);
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) A.x[q4] = xv[q4];
+  } else {
+    const int4 a0 = *(const int4*)(xq + (int64_t)gc * QK), a1 = *(const int4*)(xq + (int64_t)gc * QK + 16);
+    A.a[0] = a0.x; A.a[1] = a0.y; A.a[2] = a0.z; A.a[3] = a0.w; A.a[4] = a1.x; A.a[5] = a1.y; A.a[6] = a1.z; A.a[7] = a1.w;
+    if constexpr (MODE == 2) {
+      const int4 b0 = *(const int4*)(xl + (int64_t)gc * QK), b1 = *(const int4*)(xl + (int64_t)gc * QK + 16);
+      A.l[0] = b0.x; A.l[1] = b0.y; A.l[2] = b0.z; A.l[3] = b0.w; A.l[4] = b1.x; A.l[5] = b1.y; A.l[6] = b1.z; A.l[7] = b1.w;
+    }
+    A.s = xs[gc];
+  }
+}
+
+// A sub-block (decoded from b, j) against its activation: Dequant's binary64
+// sum of its 32 products (ta, in ascending order), or the quantized modes'
+// scale (ta) and part (tb).
+template <int F, int MODE, typename Acc>
+__device__ __forceinline__ void sub_term(const uint8_t* __restrict__ b, int j, const Act<MODE>& A, Acc& ta, Acc& tb) {
+  Sub s;
+  decode<F>(b, j, s);
+  if constexpr (MODE == 0) {
+    double acc = 0.0;
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) {
+      const float xe[4] = {A.x[q4].x, A.x[q4].y, A.x[q4].z, A.x[q4].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q4 + e;
+        const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
+        const float wt = __fadd_rn(__fmul_rn(s.d[i >> 4], (float)lvl), s.c[i >> 4]);
+        acc = __fma_rn((double)wt, (double)xe[e], acc);
+      }
+    }
+    ta = acc;
+    tb = 0.0;
+  } else {
+    float part = sub_part(s, A.a);
+    if constexpr (MODE == 2) part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, A.l)));
+    ta = A.s;
+    tb = part;
+  }
+}
+
+// A wave's geometry: ROWS rows of LPR = 64/ROWS lanes, one sub-block a lane,
+// so a step covers LPR consecutive sub-blocks of each row (LPR/8 super-blocks
+// of the K-quants); the row's step bytes and the 16-byte pieces that cover
+// them at any offset.
+template <int F, int ROWS>
+struct Seg {
+  static constexpr bool SUP = Geo<F>::V == 256;
+  static constexpr int LPR = 64 / ROWS;
+  static constexpr int L = SUP ? LPR / 8 * Geo<F>::B : LPR * Geo<F>::B;
+  static constexpr int CPR = (L + 30) / 16;
+  static constexpr int NCH = ROWS * CPR;  // pieces a wave stages a step
+  static_assert(NCH <= 128, "two pieces a lane");
+};
+
+// The 16 bytes at w + a with those at or past `total` read as 0 (a < total),
+// in two halves so that every piece is one 16-byte load: piece_addr gives the
+// load's offset -- a, or for the last piece of a matrix whose size is not a
+// multiple of 16 the 16 bytes that end at `total` (every matrix holds at least
+// 17) -- and the count of bytes to drop from its bottom; piece_fix drops them.
+__device__ __forceinline__ int64_t piece_addr(int64_t a, int64_t total, int& sh) {
+  const bool tail = a + 16 > total;
+  sh = tail ? (int)(16 - (total - a)) : 0;
+  return tail ? total - 16 : a;
+}
+__device__ __forceinline__ uint4 piece_fix(uint4 t, int sh) {
+  if (sh == 0) return t;
+  uint64_t lo = (uint64_t)t.x | ((uint64_t)t.y << 32), hi = (uint64_t)t.z | ((uint64_t)t.w << 32);
+  if (sh >= 8) {
+    lo = sh == 8 ? hi : hi >> (8 * (sh - 8));
+    hi = 0;
+  } else {
+    lo = (lo >> (8 * sh)) | (hi << (64 - 8 * sh));
+    hi >>= 8 * sh;
+  }
+  return make_uint4((unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32));
+}
+
+constexpr int DPP_ROW_SHL12 = 0x10C;
+
+// A workgroup: R row groups of ROWS rows times one wave per non-empty chunk of
+// the S-chunk split rule (S = 1: the whole row).  Wave (rg, c) sums chunk c of
+// its rows; the chunk partials meet in LDS and a thread per row adds them in
 // ascending chunk order from 0 (empty chunks, whose partial is +0, skipped).
-// The activation is read straight from global memory (L1/L2-resident): the 8
-// rows of a wave share each sub-block's activation.
-template <int F, int MODE, int R>
-__global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w, int64_t rb, int64_t N, int64_t K,
+// Each step the wave copies its rows' bytes for the step into its own LDS slot
+// with aligned 16-byte loads (issued one step ahead), and the lanes decode their
+// sub-blocks from there; the LDS copy keeps every byte's address mod 16, so the
+// decoders' alignment holds.  The activation is read straight from global
+// memory (L1/L2-resident): the rows of a wave share each sub-block's.
+// Lane j < 4 of a row owns partial j (blocks g = j mod 4): it folds its own
+// sub-block, then those of lanes j + 4, j + 8, j + 12 (DPP row shifts), so each
+// partial takes its blocks in ascending order.
+template <int F, int MODE, int ROWS, int R>
+__global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w, int64_t rb, int64_t N, int64_t total,
                                                    const float* __restrict__ x, const int8_t* __restrict__ xq,
-                                                   const int8_t* __restrict__ xl, const float* __restrict__ xs, int S,
-                                                   int m, int ceff, float* __restrict__ y) {
+                                                   const int8_t* __restrict__ xl, const float* __restrict__ xs,
+                                                   int64_t K, int S, int m, int ceff, float* __restrict__ y) {
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
-  __shared__ Acc lpart[16][8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using G = Seg<F, ROWS>;
+  constexpr bool SUP = G::SUP;
+  constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH;
+  extern __shared__ uint4 lds_dyn[];  // [waves][NCH] pieces, then the chunk partials
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  uint4* lw = lds_dyn + wave * NCH;
+  Acc* lpart = (Acc*)(lds_dyn + nwaves * NCH);  // [waves][ROWS]
   const int rg = wave / ceff, cw = wave % ceff;
   const int chunk = cw < m ? cw : S - 1;
-  const int r = lane >> 3, j = lane & 7;
-  const int64_t o_wg = (int64_t)blockIdx.x * (8 * R);
-  const int64_t o = o_wg + 8 * rg + r;
-  const uint8_t* row = w + (o < N ? o : N - 1) * rb;
+  const int r = lane / LPR, j = lane % LPR;
+  const int64_t o_wg = (int64_t)blockIdx.x * (ROWS * R);
+  const int64_t o = o_wg + ROWS * rg + r;
+  const int64_t myrow = (o < N ? o : N - 1) * rb;
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
 
+  // staging: piece t = lane + 64k is piece t % CPR of row t / CPR
+  int64_t prow[2];
+  int pc[2];
+  bool has[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = lane + 64 * k;
+    has[k] = t < NCH;
+    const int64_t po = o_wg + ROWS * rg + (has[k] ? t / CPR : 0);
+    prow[k] = (po < N ? po : N - 1) * rb;
+    pc[k] = t % CPR;
+  }
+  auto seg_off = [&](int st) -> int64_t { return SUP ? (int64_t)(st >> 3) * B : (int64_t)st * B; };
+  auto seg_len = [&](int st) -> int {
+    const int n = g1 - st < LPR ? g1 - st : LPR;  // sub-blocks of the step (whole super-blocks for SUP)
+    return SUP ? (n >> 3) * B : n * B;
+  };
+  // The next step's pieces are fetched into registers while this step is
+  // summed.  Every fetch issues the same loads whatever the step (pieces past
+  // a row's bytes, and the slots past the wave's pieces, reread the row's first
+  // piece), so no load sits behind a branch.
+  uint4 v[2];
+  int vsh[2];
+  auto fetch = [&](int st) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t so = prow[k] + seg_off(st);
+      const bool need = has[k] && 16 * pc[k] < (int)(so & 15) + seg_len(st);
+      const int64_t at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc[k] : 0), total, vsh[k]);
+      typedef unsigned v4u __attribute__((ext_vector_type(4)));
+      const v4u t = __builtin_nontemporal_load((const v4u*)(w + at));
+      v[k] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
+  };
+  fetch(g0);
+
   Acc p = 0;
-  for (int st = g0; st < g1; st += 8) {
-    const int g = st + j;  // this lane's sub-block
-    const bool ok = g < g1;
-    const int gc = ok ? g : g0;
-    Sub s;
-    decode<F>(row, gc, s);
-    Acc ta, tb;
-    if constexpr (MODE == 0) {
-      // a lane's 32 products in ascending order, binary64
-      const float4* xv = (const float4*)(x + (int64_t)gc * QK);
-      double acc = 0.0;
+  for (int st = g0; st < g1; st += LPR) {
+    {
+      const int g = st + j;  // this lane's sub-block
+      const bool ok = g < g1;
 #pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const float4 xx = xv[q4];
-        const float xe[4] = {xx.x, xx.y, xx.z, xx.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
-          const float wt = __fadd_rn(__fmul_rn(s.d[i >> 4], (float)lvl), s.c[i >> 4]);
-          acc = __fma_rn((double)wt, (double)xe[e], acc);
+      for (int k = 0; k < 2; ++k)
+        if (has[k]) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
+      if (st + LPR < g1) fetch(st + LPR);
+      Act<MODE> A;
+      load_act<MODE>(ok ? g : st, x, xq, xl, xs, A);
+      const uint8_t* seg = (const uint8_t*)(lw + r * CPR) + (int)((myrow + seg_off(st)) & 15);
+      const int jj = ok ? j : 0;
+      Acc ta, tb;
+      sub_term<F, MODE>(SUP ? seg + (jj >> 3) * B : seg + jj * B, jj & 7, A, ta, tb);
+      if constexpr (MODE == 0) {
+        p = ok ? __dadd_rn(p, ta) : p;
+        const double t4 = dpp_f64<DPP_ROW_SHL4>(ta);
+        p = g + 4 < g1 ? __dadd_rn(p, t4) : p;
+        if constexpr (LPR == 16) {
+          const double t8 = dpp_f64<DPP_ROW_SHL8>(ta), t12 = dpp_f64<DPP_ROW_SHL12>(ta);
+          p = g + 8 < g1 ? __dadd_rn(p, t8) : p;
+          p = g + 12 < g1 ? __dadd_rn(p, t12) : p;
+        }
+      } else {
+        p = ok ? __fmaf_rn(ta, tb, p) : p;
+        const float a4 = dpp_f32<DPP_ROW_SHL4>(ta), b4 = dpp_f32<DPP_ROW_SHL4>(tb);
+        p = g + 4 < g1 ? __fmaf_rn(a4, b4, p) : p;
+        if constexpr (LPR == 16) {
+          const float a8 = dpp_f32<DPP_ROW_SHL8>(ta), b8 = dpp_f32<DPP_ROW_SHL8>(tb);
+          const float a12 = dpp_f32<DPP_ROW_SHL12>(ta), b12 = dpp_f32<DPP_ROW_SHL12>(tb);
+          p = g + 8 < g1 ? __fmaf_rn(a8, b8, p) : p;
+          p = g + 12 < g1 ? __fmaf_rn(a12, b12, p) : p;
         }
       }
-      ta = acc;
-      tb = 0.0;
-    } else {
-      int a[8];
-      {
-        const int4 a0 = *(const int4*)(xq + (int64_t)gc * QK), a1 = *(const int4*)(xq + (int64_t)gc * QK + 16);
-        a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-      }
-      float part = sub_part(s, a);
-      if constexpr (MODE == 2) {
-        int l8[8];
-        const int4 b0 = *(const int4*)(xl + (int64_t)gc * QK), b1 = *(const int4*)(xl + (int64_t)gc * QK + 16);
-        l8[0] = b0.x; l8[1] = b0.y; l8[2] = b0.z; l8[3] = b0.w; l8[4] = b1.x; l8[5] = b1.y; l8[6] = b1.z; l8[7] = b1.w;
-        part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, l8)));
-      }
-      ta = xs[gc];
-      tb = part;
-    }
-    // lane j < 4 folds its own sub-block, then lane j + 4's (row shift by 4 inside the 8-lane group)
-    if constexpr (MODE == 0) {
-      const double t2 = dpp_f64<DPP_ROW_SHL4>(ta);
-      p = ok ? __dadd_rn(p, ta) : p;
-      p = g + 4 < g1 ? __dadd_rn(p, t2) : p;
-    } else {
-      const float ta2 = dpp_f32<DPP_ROW_SHL4>(ta), tb2 = dpp_f32<DPP_ROW_SHL4>(tb);
-      p = ok ? __fmaf_rn(ta, tb, p) : p;
-      p = g + 4 < g1 ? __fmaf_rn(ta2, tb2, p) : p;
     }
   }
-  // (P0 + P2) + (P1 + P3): partial q in lane q of the row's eight
-  Acc v;
+  // (P0 + P2) + (P1 + P3): partial q in lane q of the row's lanes
+  Acc pr;
   if constexpr (MODE == 0) {
     const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL2>(p));
-    v = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
+    pr = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
   } else {
     const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL2>(p));
-    v = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
+    pr = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
   }
-  if (j == 0) lpart[wave][r] = v;
+  if (j == 0) lpart[wave * ROWS + r] = pr;
   __syncthreads();
-  if ((int)threadIdx.x < 8 * R) {
-    const int gq = threadIdx.x >> 3, rq = threadIdx.x & 7;
+  if ((int)threadIdx.x < ROWS * R) {
+    const int gq = threadIdx.x / ROWS, rq = threadIdx.x % ROWS;
     const int64_t oo = o_wg + threadIdx.x;
     if (oo < N) {
       if (ceff == 1) {
-        y[oo] = (float)lpart[gq][rq];
+        y[oo] = (float)lpart[gq * ROWS + rq];
       } else {
-        Acc a = 0;
-        for (int cc = 0; cc < ceff; ++cc) a = a + lpart[gq * ceff + cc][rq];
-        y[oo] = (float)a;
+        Acc acc = 0;
+        for (int cc = 0; cc < ceff; ++cc) acc = acc + lpart[(gq * ceff + cc) * ROWS + rq];
+        y[oo] = (float)acc;
       }
     }
   }
@@ -407,24 +531,30 @@ void f_chunks(int64_t K, int S, int& m, int& ceff) {
   if (m < S && ((K % 512) != 0 || m == 0)) ceff = m + 1;
 }
 
-template <int F, int MODE, int R>
+template <int F, int MODE, int ROWS, int R>
 hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
                      const float* xs, int S, int m, int ceff, float* y, hipStream_t st) {
+  using Acc = typename std::conditional<MODE == 0, double, float>::type;
   const int64_t rb = K / Geo<F>::V * Geo<F>::B;
-  const dim3 grid((unsigned)((N + 8 * R - 1) / (8 * R))), block((unsigned)(64 * R * ceff));
-  hipLaunchKernelGGL((k_gemv_fmt<F, MODE, R>), grid, block, 0, st, w, rb, N, K, x, xq, xl, xs, S, m, ceff, y);
+  const int waves = R * ceff;
+  const size_t lds = (size_t)waves * Seg<F, ROWS>::NCH * 16 + (size_t)waves * ROWS * sizeof(Acc);
+  const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * waves));
+  hipLaunchKernelGGL((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
+                     ceff, y);
   return hipGetLastError();
 }
 
+// Four rows a wave (16 lanes a row) and one row group a workgroup: on the
+// 5120-row projections that is 1280 workgroups, five a compute unit in one
+// round at four or five chunk waves (measured: ahead of 8 rows a wave, of two
+// row groups a workgroup, and of fetching two or three steps ahead).
 template <int F, int MODE>
 hipError_t launch_f(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
                     const float* xs, int S, float* y, hipStream_t st) {
   int m, ceff;
   f_chunks(K, S, m, ceff);
   if (S == 1) m = 1, ceff = 1;
-  // two row groups a workgroup where the chunk waves leave room, else one
-  if (2 * ceff <= 16) return launch_fr<F, MODE, 2>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
-  return launch_fr<F, MODE, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
+  return launch_fr<F, MODE, 4, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
 }
 
 template <int F>
