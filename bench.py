@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--no-sweep", action="store_true", help="skip the S in {1,2,4,8} sweep beside the step")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the timing of the other GGUF block formats beside the step")
     ap.add_argument("--no-producers", action="store_true",
                     help="skip the timing of the fused producers (RMSNorm / SwiGLU + quantizer)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -418,6 +420,38 @@ def main() -> int:
                     "fused_us": round(mean_launch_us([one], 200), 2),
                     "two_launches_us": round(mean_launch_us([lambda: (a(), b())], 200), 2)}
 
+    # The other GGUF block formats on the down-proj's shape, beside the step: qdg_gemv_fmt in the
+    # two quantized modes at S=8 (one round of 1280 five-wave workgroups), over rotated copies.
+    formats = {}
+    if not args.no_formats:
+        fsh = shapes[-1]
+        fnames = {2: "Q4_0", 3: "Q4_1", 6: "Q5_0", 7: "Q5_1", 20: "IQ4_NL", 39: "MXFP4", 10: "Q2_K",
+                  11: "Q3_K", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K", 23: "IQ4_XS"}
+        fx = acts[-1]
+        fy = torch.empty((fsh.N,), dtype=torch.float32, device=dev)
+        fq = {}
+        for mode in modes:
+            xq_ = torch.empty((1, fsh.K), dtype=torch.int8, device=dev)
+            xl_ = torch.empty_like(xq_) if mode == 2 else None
+            xs_ = torch.empty((1, fsh.K // 32), dtype=torch.float32, device=dev)
+            q.quantize_act(mode, fx, xq_, xl_, xs_)
+            fq[mode] = (xq_, xl_, xs_)
+        for fmt, fname in fnames.items():
+            Kf = fsh.K // workloads.BLOCK_FORMATS[fmt][0] * workloads.BLOCK_FORMATS[fmt][0]
+            wb = torch.from_numpy(workloads.block_matrix(fmt, fsh.N, Kf, 2000 + fmt).reshape(-1)).to(dev)
+            nbytes = wb.numel()
+            fc = [wb] + [wb.clone() for _ in range(max(1, int(args.min_rotate_bytes // nbytes)))]
+            rec = {"K": Kf, "bytes": nbytes, "S": 8}
+            for mode in modes:
+                xq_, xl_, xs_ = fq[mode]
+                calls = [q.bind_gemv_fmt(fmt, mode, c, fsh.N, Kf, fy, xq=xq_, xl=xl_, xs=xs_, splits=8) for c in fc]
+                us = mean_launch_us(calls, max(40, 2 * len(fc)))
+                rec[names[mode]] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
+                                    "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 1)}
+            formats[fname] = rec
+            del fc, wb
+        torch.cuda.empty_cache()
+
     # ---- CPU baseline: the oracle on the same step (whole steps, repeated for a bounded time)
     cpu = None
     if not args.no_cpu_baseline:
@@ -458,7 +492,7 @@ def main() -> int:
                    "path": args.path, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
-                   "read_ceiling": ceiling, "producers": producers, "splits_sweep": splits_sweep,
+                   "read_ceiling": ceiling, "producers": producers, "formats": formats, "splits_sweep": splits_sweep,
                    "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,

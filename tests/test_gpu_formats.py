@@ -119,3 +119,26 @@ def test_fmt_split(fmt, N, K, S, mode):
             q.gemv_fmt(fmt, mode, dw, N, K, t, xq=xq, xl=xl, xs=xs, splits=S)
         np.testing.assert_array_equal(host(y), want)
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("fmt", oracle.FORMATS)
+def test_fmt_bench_shape(fmt, mode):
+    """The down-projection's shape, 5120 x 25600 (25600 is a whole number of
+    super-blocks), at the launch configuration the benchmark times (S=8), on the
+    benchmark's generator: sampled rows bit-exact with the oracle."""
+    import workloads
+    N, K, S = 5120, 25600, 8
+    announce(f"gemv_fmt bench shape fmt={fmt} mode={mode} N={N} K={K} S={S}")
+    w = workloads.block_matrix(fmt, N, K, 2000 + fmt)
+    x = workloads.activation(K, 77, True, 78)[None, :]
+    oq, ol, os_ = oracle.quantize(mode, x)
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_fmt(fmt, mode, dev(w.reshape(-1)), N, K, y, xq=dev(oq), xl=None if ol is None else dev(ol), xs=dev(os_),
+               splits=S)
+    got = host(y)
+    rows = np.unique(np.concatenate([[0, 1, 2, 3, 4095, N - 1], np.random.default_rng(fmt).choice(N, 58, False)]))
+    want = oracle.gemv_fmt(fmt, mode, np.ascontiguousarray(w[rows]), len(rows), K, xq=oq, xl=ol, xs=os_, splits=S,
+                           nthreads=8)[0]
+    np.testing.assert_array_equal(got[rows], want)
+    assert np.all(np.isfinite(got))

@@ -168,3 +168,17 @@ def test_split_integer_case(fmt, mode):
     for S in (1, 2, 3, 5, 16):
         y = oracle.gemv_fmt(fmt, mode, w, N, K, splits=S, **kw)
         np.testing.assert_array_equal(y[0], want.astype(np.float32), err_msg=f"S={S}")
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_workload_block_matrix_is_a_valid_matrix(fmt):
+    """The seeded block-format generator (random bytes, binary16 scales drawn on
+    [1e-3, 1e-2), E8M0 on [118, 134)) makes rows of the format's size whose every
+    scale and offset decodes finite, and is reproducible from its seed."""
+    import workloads
+    K = 512
+    b = workloads.block_matrix(fmt, 4, K, 9)
+    assert b.dtype == np.uint8 and b.shape == (4, oracle.fmt_row_bytes(fmt, K))
+    _, d, c = oracle.fmt_decode(fmt, b, 4, K)
+    assert np.all(np.isfinite(d)) and np.all(np.isfinite(c)) and np.any(d != 0)
+    np.testing.assert_array_equal(b, workloads.block_matrix(fmt, 4, K, 9))

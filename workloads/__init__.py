@@ -145,3 +145,36 @@ def glu_inputs(B: int, K: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
     g[tail] *= np.float32(8.0)
     u = rng.standard_normal((B, K)).astype(np.float32)
     return g, u
+
+
+# Other GGUF block formats: GGUF type number -> (values per block, bytes per block,
+# byte offsets of the binary16 scale fields inside a block).  Only where the
+# scale fields sit, so that random bytes make a valid matrix: the levels, sub-scales
+# and masks of every format are valid for any byte values.  MXFP4's one-byte E8M0
+# scale sits at offset 0.
+BLOCK_FORMATS = {
+    2: (32, 18, (0,)), 3: (32, 20, (0, 2)), 6: (32, 22, (0,)), 7: (32, 24, (0, 2)),
+    20: (32, 18, (0,)), 39: (32, 17, ()),
+    10: (256, 84, (80, 82)), 11: (256, 110, (108,)), 12: (256, 144, (0, 2)), 13: (256, 176, (0, 2)),
+    14: (256, 210, (208,)), 23: (256, 136, (0,)),
+}
+
+
+def block_matrix(fmt: int, N: int, K: int, seed: int) -> np.ndarray:
+    """``N`` rows of ``K`` values in GGUF block format ``fmt`` as uint8 ``[N][row bytes]``:
+    uniform random bytes, with every binary16 scale field drawn uniform on
+    [1e-3, 1e-2) (rounded once to binary16) and MXFP4's E8M0 scales uniform on
+    [118, 134) (2^-10 .. 2^5)."""
+    vals, nbytes, fields = BLOCK_FORMATS[fmt]
+    if K % vals:
+        raise ValueError("K must be a whole number of the format's blocks")
+    nblk = K // vals
+    rng = _rng(seed)
+    b = rng.integers(0, 256, size=(N, nblk, nbytes), dtype=np.uint8)
+    for off in fields:
+        h = rng.uniform(1e-3, 1e-2, size=(N, nblk)).astype(np.float16).view(np.uint16)
+        b[:, :, off] = (h & 0xFF).astype(np.uint8)
+        b[:, :, off + 1] = (h >> 8).astype(np.uint8)
+    if fmt == 39:
+        b[:, :, 0] = rng.integers(118, 134, size=(N, nblk), dtype=np.uint8)
+    return b.reshape(N, nblk * nbytes)
