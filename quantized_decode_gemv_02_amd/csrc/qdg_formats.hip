@@ -58,17 +58,12 @@ __device__ __forceinline__ unsigned ld_u16(const uint8_t* p) { return *(const un
 __device__ __forceinline__ unsigned ld_u32(const uint8_t* p) { return *(const unsigned*)p; }
 __device__ __forceinline__ float h16(unsigned bits) { return half_bits_to_float((unsigned short)(bits & 0xffff)); }
 
-// n dwords from p: whole dword loads when p is 4-byte aligned, else pairs of
-// 2-byte loads (every block format keeps its fields 2-byte aligned but MXFP4).
+// n dwords from p at any alignment: one byte copy, which the compiler turns into
+// the widest loads the address allows (the decoders read the wave's LDS copy
+// of the blocks, where unaligned multi-dword reads are single instructions).
 template <int NW>
 __device__ __forceinline__ void ld_words(const uint8_t* p, unsigned* w) {
-  if (((uintptr_t)p & 3) == 0) {
-#pragma unroll
-    for (int i = 0; i < NW; ++i) w[i] = ld_u32(p + 4 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < NW; ++i) w[i] = ld_u16(p + 4 * i) | (ld_u16(p + 4 * i + 2) << 16);
-  }
+  __builtin_memcpy(w, p, 4 * NW);
 }
 
 // The low nibbles of a word's four bytes and the high ones, as bytes.
@@ -125,8 +120,7 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
       for (int i = 0; i < 4; ++i) q[i] = ld_u32(b + 4 + 4 * i);
     } else {
       s.d[0] = s.d[1] = h16(ld_u16(b));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = ld_u16(b + 2 + 4 * i) | (ld_u16(b + 4 + 4 * i) << 16);
+      ld_words<4>(b + 2, q);
     }
     if constexpr (F == F_IQ4_NL) {
       unsigned t[4];
@@ -155,9 +149,8 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
       for (int i = 0; i < 4; ++i) q[i] = ld_u32(b + 8 + 4 * i);
     } else {
       s.d[0] = s.d[1] = h16(ld_u16(b));
-      qh = ld_u16(b + 2) | (ld_u16(b + 4) << 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = ld_u16(b + 6 + 4 * i) | (ld_u16(b + 8 + 4 * i) << 16);
+      ld_words<1>(b + 2, &qh);
+      ld_words<4>(b + 6, q);
       s.off = 16;
     }
 #pragma unroll
@@ -171,12 +164,12 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
     s.d[0] = s.d[1] = __uint_as_float(bits);
     unsigned t[4];
     e2m1_table(t);
+    unsigned q[4];
+    ld_words<4>(b + 1, q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const unsigned q = ld_u8(b + 1 + 4 * i) | (ld_u8(b + 2 + 4 * i) << 8) | (ld_u8(b + 3 + 4 * i) << 16) |
-                         (ld_u8(b + 4 + 4 * i) << 24);
-      s.w[i] = table16(lo_nib(q), t);
-      s.w[4 + i] = table16(hi_nib(q), t);
+      s.w[i] = table16(lo_nib(q[i]), t);
+      s.w[4 + i] = table16(hi_nib(q[i]), t);
     }
   } else if constexpr (F == F_Q4_K || F == F_Q5_K) {
     const int pair = j >> 1, upper = j & 1;
