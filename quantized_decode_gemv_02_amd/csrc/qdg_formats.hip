@@ -264,16 +264,32 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
   }
 }
 
-// part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8]
+// Formats whose halves carry an offset c, or whose levels are dotted raw and
+// corrected by a constant (both need the activation sums sh).
+template <int F>
+constexpr bool needs_sums() {
+  return F == F_Q4_1 || F == F_Q5_1 || F == F_Q2_K || F == F_Q4_K || F == F_Q5_K ||  // c
+         F == F_Q4_0 || F == F_Q5_0 || F == F_Q3_K || F == F_Q6_K;                     // raw levels
+}
+
+// part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8].
+// Where c = 0 and the levels are signed (IQ4_NL, IQ4_XS, MXFP4) the c terms are
+// left out: each is a zero, which can change only the sign of a zero part, and
+// fma(s, +-0, p) is p for every p the row can hold (it starts at +0 and a sum
+// of nonzero terms that cancels rounds to +0), so the row's bits are the same.
+template <int F>
 __device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8]) {
   int dh0 = 0, dh1 = 0, sh0 = 0, sh1 = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dh0 = __builtin_amdgcn_sdot4((int)s.w[i], a[i], dh0, false);
-    sh0 = __builtin_amdgcn_sdot4(0x01010101, a[i], sh0, false);
     dh1 = __builtin_amdgcn_sdot4((int)s.w[4 + i], a[4 + i], dh1, false);
-    sh1 = __builtin_amdgcn_sdot4(0x01010101, a[4 + i], sh1, false);
+    if constexpr (needs_sums<F>()) {
+      sh0 = __builtin_amdgcn_sdot4(0x01010101, a[i], sh0, false);
+      sh1 = __builtin_amdgcn_sdot4(0x01010101, a[4 + i], sh1, false);
+    }
   }
+  if constexpr (!needs_sums<F>()) return __fadd_rn(__fmul_rn(s.d[0], (float)dh0), __fmul_rn(s.d[1], (float)dh1));
   dh0 -= s.off * sh0;
   dh1 -= s.off * sh1;
   float part = __fmul_rn(s.d[0], (float)dh0);
@@ -335,8 +351,8 @@ __device__ __forceinline__ void sub_term(const uint8_t* __restrict__ b, int j, c
     ta = acc;
     tb = 0.0;
   } else {
-    float part = sub_part(s, A.a);
-    if constexpr (MODE == 2) part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part(s, A.l)));
+    float part = sub_part<F>(s, A.a);
+    if constexpr (MODE == 2) part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part<F>(s, A.l)));
     ta = A.s;
     tb = part;
   }
