@@ -235,7 +235,10 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
     ld_words<8>(b + 32 + 32 * half, q);
     ld_words<3>(b + 96, sp);
     const float dd = h16(ld_u16(b + 108));
-    auto spb = [&](int i) { return (sp[i >> 2] >> (8 * (i & 3))) & 255u; };
+    auto spb = [&](int i) {  // byte i of the 12 scale bytes (word picked by selects, not an indexed array)
+      const unsigned wd = (i >> 2) == 0 ? sp[0] : (i >> 2) == 1 ? sp[1] : sp[2];
+      return (wd >> (8 * (i & 3))) & 255u;
+    };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 8 * half + 2 * k + h;
@@ -368,8 +371,24 @@ struct Seg {
   static constexpr int LPR = 64 / ROWS;
   static constexpr int L = SUP ? LPR / 8 * Geo<F>::B : LPR * Geo<F>::B;
   static constexpr int CPR = (L + 30) / 16;
-  static constexpr int NCH = ROWS * CPR;  // pieces a wave stages a step
-  static_assert(NCH <= 128, "two pieces a lane");
+  static constexpr int NCH = ROWS * CPR;  // weight pieces a wave stages a step
+};
+
+// A wave's LDS slot for one step: the rows' weight pieces, then under Dequant
+// the step's activation (LPR sub-blocks of 32 binary32 values, 8 pieces each).
+// The quantized modes read their activation words and scales from global
+// memory instead (L1/L2-resident): measured on the 5120-row projections,
+// staging them too left Int8Act unchanged and made TwoPass 5-15% slower (a
+// third load a lane a step), while Dequant, whose activation is four times
+// larger, gains 25-30%.
+template <int F, int MODE, int ROWS>
+struct Stage {
+  using G = Seg<F, ROWS>;
+  static constexpr bool ACT = MODE == 0;            // activation staged with the weights
+  static constexpr int NA = ACT ? 8 * G::LPR : 0;
+  static constexpr int NT = G::NCH + NA;           // pieces a step
+  static constexpr int NPL = (NT + 63) / 64;       // loads a lane a step
+  static constexpr int SLOT = NT * 16;
 };
 
 // The 16 bytes at w + a with those at or past `total` read as 0 (a < total),
@@ -416,12 +435,14 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
                                                    int64_t K, int S, int m, int ceff, float* __restrict__ y) {
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
   using G = Seg<F, ROWS>;
+  using T = Stage<F, MODE, ROWS>;
   constexpr bool SUP = G::SUP;
-  constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH;
-  extern __shared__ uint4 lds_dyn[];  // [waves][NCH] pieces, then the chunk partials
+  constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NA = T::NA, NT = T::NT, NPL = T::NPL;
+  extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  uint4* lw = lds_dyn + wave * NCH;
-  Acc* lpart = (Acc*)(lds_dyn + nwaves * NCH);  // [waves][ROWS]
+  uint8_t* slot = (uint8_t*)lds_dyn + wave * T::SLOT;
+  uint4* lw = (uint4*)slot;
+  Acc* lpart = (Acc*)((uint8_t*)lds_dyn + nwaves * T::SLOT);  // [waves][ROWS]
   const int rg = wave / ceff, cw = wave % ceff;
   const int chunk = cw < m ? cw : S - 1;
   const int r = lane / LPR, j = lane % LPR;
@@ -431,55 +452,70 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
 
-  // staging: piece t = lane + 64k is piece t % CPR of row t / CPR
-  int64_t prow[2];
-  int pc[2];
-  bool has[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int t = lane + 64 * k;
-    has[k] = t < NCH;
-    const int64_t po = o_wg + ROWS * rg + (has[k] ? t / CPR : 0);
-    prow[k] = (po < N ? po : N - 1) * rb;
-    pc[k] = t % CPR;
-  }
   auto seg_off = [&](int st) -> int64_t { return SUP ? (int64_t)(st >> 3) * B : (int64_t)st * B; };
   auto seg_len = [&](int st) -> int {
     const int n = g1 - st < LPR ? g1 - st : LPR;  // sub-blocks of the step (whole super-blocks for SUP)
     return SUP ? (n >> 3) * B : n * B;
   };
-  // The next step's pieces are fetched into registers while this step is
-  // summed.  Every fetch issues the same loads whatever the step (pieces past
-  // a row's bytes, and the slots past the wave's pieces, reread the row's first
-  // piece), so no load sits behind a branch.
-  uint4 v[2];
-  int vsh[2];
+  // A fetch: piece t = lane + 64k is weight piece t % CPR of row t / CPR
+  // (t < NCH), or under Dequant activation piece t - NCH (t < NT).  The next
+  // step's fetch is issued before this step is summed.  Every fetch issues the
+  // same loads whatever the step (pieces past a row's bytes, past the chunk's
+  // sub-blocks, or past the wave's pieces reread a valid piece), so no load
+  // sits behind a branch.
+  uint4 v[NPL];
+  int vsh[NPL];
   auto fetch = [&](int st) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t so = prow[k] + seg_off(st);
-      const bool need = has[k] && 16 * pc[k] < (int)(so & 15) + seg_len(st);
-      const int64_t at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc[k] : 0), total, vsh[k]);
+    for (int k = 0; k < NPL; ++k) {
+      const int t = lane + 64 * k;
+      const bool wpiece = t < NCH || t >= NT;
+      const int tw = t < NCH ? t : 0;
+      const int64_t po = o_wg + ROWS * rg + tw / CPR;
+      const int pc = tw % CPR;
+      const int64_t so = (po < N ? po : N - 1) * rb + seg_off(st);
+      const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st);
+      int sh;
+      const int64_t at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh);
+      const uint8_t* src = w + at;
+      if (!wpiece) {
+        const int i = t - NCH;
+        const int sb = st + (i >> 3);
+        src = (const uint8_t*)(x + (int64_t)(sb < g1 ? sb : st) * QK) + 16 * (i & 7);
+        sh = 0;
+      }
+      vsh[k] = sh;
       typedef unsigned v4u __attribute__((ext_vector_type(4)));
-      const v4u t = __builtin_nontemporal_load((const v4u*)(w + at));
-      v[k] = make_uint4(t[0], t[1], t[2], t[3]);
+      v4u tt;
+      if (64 * k + 63 < NCH) {  // a constant once the loop is unrolled
+        tt = __builtin_nontemporal_load((const v4u*)src);  // weights only: streamed once
+      } else {
+        tt = *(const v4u*)src;
+      }
+      v[k] = make_uint4(tt[0], tt[1], tt[2], tt[3]);
     }
   };
   fetch(g0);
 
   Acc p = 0;
   for (int st = g0; st < g1; st += LPR) {
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (lane + 64 * k < NT) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
+    if (st + LPR < g1) fetch(st + LPR);  // the next step's bytes, in flight while this one is summed
     {
       const int g = st + j;  // this lane's sub-block
       const bool ok = g < g1;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        if (has[k]) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
-      if (st + LPR < g1) fetch(st + LPR);
-      Act<MODE> A;
-      load_act<MODE>(ok ? g : st, x, xq, xl, xs, A);
-      const uint8_t* seg = (const uint8_t*)(lw + r * CPR) + (int)((myrow + seg_off(st)) & 15);
       const int jj = ok ? j : 0;
+      Act<MODE> A;
+      if constexpr (T::ACT) {
+        const float4* xa = (const float4*)(slot + 16 * NCH + 128 * jj);
+#pragma unroll
+        for (int q4 = 0; q4 < 8; ++q4) A.x[q4] = xa[q4];
+      } else {
+        load_act<MODE>(ok ? g : st, x, xq, xl, xs, A);
+      }
+      const uint8_t* seg = slot + 16 * r * CPR + (int)((myrow + seg_off(st)) & 15);
       Acc ta, tb;
       sub_term<F, MODE>(SUP ? seg + (jj >> 3) * B : seg + jj * B, jj & 7, A, ta, tb);
       if constexpr (MODE == 0) {
@@ -546,7 +582,7 @@ hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, con
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
   const int64_t rb = K / Geo<F>::V * Geo<F>::B;
   const int waves = R * ceff;
-  const size_t lds = (size_t)waves * Seg<F, ROWS>::NCH * 16 + (size_t)waves * ROWS * sizeof(Acc);
+  const size_t lds = (size_t)waves * Stage<F, MODE, ROWS>::SLOT + (size_t)waves * ROWS * sizeof(Acc);
   const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * waves));
   hipLaunchKernelGGL((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
                      ceff, y);
