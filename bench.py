@@ -469,10 +469,31 @@ def main() -> int:
                     oracle.combine(part)
             t_cpu += time.perf_counter() - tb
             n_steps += 1
+        # the same steps on one thread (row-parallel OpenMP does not change any row's order), for a
+        # quarter of the budget
+        t1, n1 = 0.0, 0
+        while n1 == 0 or t1 < args.cpu_seconds / 4:
+            tb = time.perf_counter()
+            for mode in modes:
+                for si, sh in enumerate(shapes):
+                    d = host[si]
+                    xq, xl, xs = oracle.quantize(mode, d["x"])
+                    oracle.combine(oracle.gemv_split(mode, d["wq"], d["ws"], xq, xl, xs, chosen[(mode, si)],
+                                                     nthreads=1))
+            t1 += time.perf_counter() - tb
+            n1 += 1
+        model = ""
+        try:
+            model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+        except (OSError, StopIteration):
+            pass
         cpu = {"value": round(step_bytes * n_steps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{n_steps} whole steps ({t_cpu:.1f} s): quantize + split-K GEMV + combine of both "
-                         f"projections in every mode, OpenMP over rows"}
+                         f"projections in every mode, OpenMP over rows",
+               "single_thread_value": round(step_bytes * n1 / t1 / 1e9, 3),
+               "single_thread_sample": f"{n1} whole steps ({t1:.1f} s) on one thread",
+               "host": {"cpu_count": os.cpu_count(), "model": model}}
 
     line = {
         "metric": "Q8_0 GEMV achieved HBM GB/s and % of peak per mode (Dequant/Int8/TwoPass)",

@@ -142,3 +142,40 @@ def test_fmt_bench_shape(fmt, mode):
                            nthreads=8)[0]
     np.testing.assert_array_equal(got[rows], want)
     assert np.all(np.isfinite(got))
+
+
+def tiny_cases():
+    out = []
+    for f in oracle.FORMATS:
+        k1 = 256 if f in SUPER else 32          # one block: the matrix is 17..210 bytes
+        for N, K in ((1, k1), (2, k1), (3, 2 * k1), (5, 3 * k1), (1, 768 if f in SUPER else 544)):
+            out.append((f, N, K))
+    return out
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("fmt,N,K", tiny_cases())
+def test_fmt_tiny(fmt, N, K, mode):
+    """The smallest matrices: one block a row (the last 16-byte piece of the
+    matrix ends past it and is read as the 16 bytes that end at the matrix end),
+    fewer rows than a wave's four, and K past one 512-value group with S=2 (a
+    tail chunk)."""
+    announce(f"gemv_fmt tiny fmt={fmt} mode={mode} N={N} K={K}")
+    rng = np.random.default_rng(5000 * fmt + 10 * N + K + mode)
+    w, _, _, _ = encode(fmt, N, K, rng)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    dw = dev(w.reshape(-1))
+    assert dw.numel() == N * q.fmt_row_bytes(fmt, K)
+    for S in (1, 2):
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+        if mode == 0:
+            want = oracle.gemv_fmt(fmt, 0, w, N, K, x=x, splits=S)[0]
+            q.gemv_fmt(fmt, 0, dw, N, K, y, x=dev(x), splits=S)
+            got = host(y)
+            d = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+            assert d.max() <= 1, (S, int(d.max()))
+        else:
+            oq, ol, os_ = oracle.quantize(mode, x)
+            want = oracle.gemv_fmt(fmt, mode, w, N, K, xq=oq, xl=ol, xs=os_, splits=S)[0]
+            q.gemv_fmt(fmt, mode, dw, N, K, y, xq=dev(oq), xl=None if ol is None else dev(ol), xs=dev(os_), splits=S)
+            np.testing.assert_array_equal(host(y), want, err_msg=f"S={S}")
