@@ -17,19 +17,20 @@
 // Q3_K: - 4, Q6_K: - 32) is dotted on its raw unsigned levels and corrected by
 // the offset times the activation sum, which is the same integer.
 //
-// Mapping: a wave takes 8 rows, 8 lanes a row, one sub-block a lane, so a step
-// covers 8 consecutive sub-blocks of a row (one super-block of the K-quants).
-// Lane j < 4 of a row owns partial j: it folds its own sub-block, then the one
-// of lane j + 4 (one DPP row shift).  Split-K (the QWEN38 page's chunk rule,
-// gk_gemv_hl_sk / gk_sk_combine): the chunks are waves of one workgroup and
-// their partials are added in ascending order in LDS.
+// Mapping: a wave takes 4 rows, 16 lanes a row, one sub-block a lane, so a
+// step covers 16 consecutive sub-blocks of a row (two super-blocks of the
+// K-quants).  Lane j < 4 of a row owns partial j: it folds its own sub-block,
+// then those of lanes j + 4, j + 8 and j + 12 (DPP row shifts).  Each step's
+// bytes are staged in the wave's LDS slot by aligned 16-byte loads, a step
+// ahead.  Split-K (the QWEN38 page's chunk rule, gk_gemv_hl_sk /
+// gk_sk_combine): the chunks are waves of one workgroup and their partials are
+// added in ascending order in LDS.
 #include <stdlib.h>
 
 #include "qdg_device.h"
 
 namespace qdg {
 namespace {
-
 
 enum : int {
   F_Q4_0 = 2, F_Q4_1 = 3, F_Q5_0 = 6, F_Q5_1 = 7, F_Q2_K = 10, F_Q3_K = 11, F_Q4_K = 12,
@@ -267,12 +268,16 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
   }
 }
 
-// Formats whose halves carry an offset c, or whose levels are dotted raw and
-// corrected by a constant (both need the activation sums sh).
+// Formats whose halves carry an offset c.
+template <int F>
+constexpr bool has_offsets() {
+  return F == F_Q4_1 || F == F_Q5_1 || F == F_Q2_K || F == F_Q4_K || F == F_Q5_K;
+}
+// Formats that need the activation sums sh: an offset c, or levels dotted raw
+// and corrected by a constant.
 template <int F>
 constexpr bool needs_sums() {
-  return F == F_Q4_1 || F == F_Q5_1 || F == F_Q2_K || F == F_Q4_K || F == F_Q5_K ||  // c
-         F == F_Q4_0 || F == F_Q5_0 || F == F_Q3_K || F == F_Q6_K;                     // raw levels
+  return has_offsets<F>() || F == F_Q4_0 || F == F_Q5_0 || F == F_Q3_K || F == F_Q6_K;
 }
 
 // part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8].
@@ -339,19 +344,37 @@ __device__ __forceinline__ void sub_term(const uint8_t* __restrict__ b, int j, c
   Sub s;
   decode<F>(b, j, s);
   if constexpr (MODE == 0) {
-    double acc = 0.0;
+    // four binary64 chains (products i mod 4, ascending), then (c0 + c2) + (c1 + c3)
+    // per half; any fixed binary64 order meets the Dequant tolerance
+    double h[2];
 #pragma unroll
-    for (int q4 = 0; q4 < 8; ++q4) {
-      const float xe[4] = {A.x[q4].x, A.x[q4].y, A.x[q4].z, A.x[q4].w};
+    for (int half = 0; half < 2; ++half) {
+      double c4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * q4 + e;
-        const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
-        const float wt = __fadd_rn(__fmul_rn(s.d[i >> 4], (float)lvl), s.c[i >> 4]);
-        acc = __fma_rn((double)wt, (double)xe[e], acc);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 xv = A.x[4 * half + q4];
+        const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * half + 4 * q4 + e;
+          const int lvl = (int)(signed char)((s.w[i >> 2] >> (8 * (i & 3))) & 255u) - s.off;
+          if constexpr (has_offsets<F>()) {
+            const float wt = __fadd_rn(__fmul_rn(s.d[half], (float)lvl), s.c[half]);
+            c4[e] = __fma_rn((double)wt, (double)xe[e], c4[e]);
+          } else {
+            c4[e] = __fma_rn((double)lvl, (double)xe[e], c4[e]);  // the scale is applied per half below
+          }
+        }
       }
+      h[half] = __dadd_rn(__dadd_rn(c4[0], c4[2]), __dadd_rn(c4[1], c4[3]));
     }
-    ta = acc;
+    if constexpr (has_offsets<F>()) {
+      ta = __dadd_rn(h[0], h[1]);
+    } else {
+      // c = 0: every weight fl(d*level) is d*level exactly (at most 23 significant
+      // bits in every such format), so d factors out of the half's products
+      ta = __fma_rn((double)s.d[0], h[0], __dmul_rn((double)s.d[1], h[1]));
+    }
     tb = 0.0;
   } else {
     float part = sub_part<F>(s, A.a);
