@@ -412,6 +412,9 @@ struct Stage {
   static constexpr int NT = G::NCH + NA;           // pieces a step
   static constexpr int NPL = (NT + 63) / 64;       // loads a lane a step
   static constexpr int SLOT = NT * 16;
+  // 16 chunk waves' slots and partials stay within the 64 KiB a launch gets
+  // without raising the kernel's LDS limit
+  static_assert(16 * SLOT + 16 * ROWS * 8 <= 65536, "LDS of a 16-wave workgroup");
 };
 
 // The 16 bytes at w + a with those at or past `total` read as 0 (a < total),
