@@ -438,33 +438,73 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_mfma_dma(const int8_t* __restr
     wait_and_barrier<(P - 2) * SL::DMA_LOADS>();  // step s is in LDS, slot (s-1) mod P is free
     issue(s + P - 1);
     const unsigned char* slot = lds + (s % P) * SL::BYTES;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = res + 4 * h;
-      long ak[AT], lk[AT];
-      float sig[AT][4];
-#pragma unroll
-      for (int at = 0; at < AT; ++at) {
-        ak[at] = *(const long*)(slot + a_rd[h] + at * 4096);
-        lk[at] = 0;
-        if constexpr (MODE == 2) lk[at] = *(const long*)(slot + a_rd[h] + at * 4096 + (SL::L - SL::A));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sig[at][i] = *(const float*)(slot + sx_rd + at * 512 + (i * STEP + k) * 4);
-      }
-#pragma unroll
-      for (int m = 0; m < TPW; ++m) {
-        const long wk = *(const long*)(slot + w_rd[m][h]);
-        const float sgm = half_bits_to_float(*(const unsigned short*)(slot + sg_rd[m] + 2 * k));
-#pragma unroll
+    // One activation tile: all operands first, then the products.  Several tiles
+    // (prefill): one tile at a time, so its operands and products are dead before
+    // the next tile's; each partial still takes one step per h, in order.
+    // Measured: the first is 3% faster at B = 16 (TwoPass), the second 5% faster
+    // at B = 64 (Int8Act), with 121 VGPRs instead of 171 (TwoPass, four tiles).
+    if constexpr (AT == 1) {
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = res + 4 * h;
+        long ak[AT], lk[AT];
+        float sig[AT][4];
+  #pragma unroll
         for (int at = 0; at < AT; ++at) {
-          const v4i D = mfma16x16x32(ak[at], wk);
-          v4i E = {0, 0, 0, 0};
-          if constexpr (MODE == 2) E = mfma16x16x32(lk[at], wk);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float ta, tb;
-            q8_term<MODE>(sgm, sig[at][i], D[i], E[i], ta, tb);
-            p[m][at][i] = __fmaf_rn(ta, tb, p[m][at][i]);
+          ak[at] = *(const long*)(slot + a_rd[h] + at * 4096);
+          lk[at] = 0;
+          if constexpr (MODE == 2) lk[at] = *(const long*)(slot + a_rd[h] + at * 4096 + (SL::L - SL::A));
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sig[at][i] = *(const float*)(slot + sx_rd + at * 512 + (i * STEP + k) * 4);
+        }
+  #pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          const long wk = *(const long*)(slot + w_rd[m][h]);
+          const float sgm = half_bits_to_float(*(const unsigned short*)(slot + sg_rd[m] + 2 * k));
+  #pragma unroll
+          for (int at = 0; at < AT; ++at) {
+            const v4i D = mfma16x16x32(ak[at], wk);
+            v4i E = {0, 0, 0, 0};
+            if constexpr (MODE == 2) E = mfma16x16x32(lk[at], wk);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float ta, tb;
+              q8_term<MODE>(sgm, sig[at][i], D[i], E[i], ta, tb);
+              p[m][at][i] = __fmaf_rn(ta, tb, p[m][at][i]);
+            }
+          }
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = res + 4 * h;
+        long wk[TPW];
+        float sgm[TPW];
+  #pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          wk[m] = *(const long*)(slot + w_rd[m][h]);
+          sgm[m] = half_bits_to_float(*(const unsigned short*)(slot + sg_rd[m] + 2 * k));
+        }
+  #pragma unroll
+        for (int at = 0; at < AT; ++at) {
+          const long ak = *(const long*)(slot + a_rd[h] + at * 4096);
+          long lk = 0;
+          if constexpr (MODE == 2) lk = *(const long*)(slot + a_rd[h] + at * 4096 + (SL::L - SL::A));
+          float sig[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) sig[i] = *(const float*)(slot + sx_rd + at * 512 + (i * STEP + k) * 4);
+  #pragma unroll
+          for (int m = 0; m < TPW; ++m) {
+            const v4i D = mfma16x16x32(ak, wk[m]);
+            v4i E = {0, 0, 0, 0};
+            if constexpr (MODE == 2) E = mfma16x16x32(lk, wk[m]);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float ta, tb;
+              q8_term<MODE>(sgm[m], sig[i], D[i], E[i], ta, tb);
+              p[m][at][i] = __fmaf_rn(ta, tb, p[m][at][i]);
+            }
           }
         }
       }
