@@ -11,8 +11,9 @@
 //    same with dl, sl).  The row is the Q8_0 row: p <- fma(s_g, part, p) into
 //    partial g mod 4, ascending, then (P0 + P2) + (P1 + P3).
 //  * Dequant: each weight fl(fl(d*level) + c), its products with x and their
-//    sums in binary64 (a lane's 32 in ascending order, then the row's partials
-//    as above), one rounding to binary32.
+//    sums in binary64 (a sub-block's half in four chains; where c = 0 the
+//    half's scale applied once to its level-times-x sum, d*level being exact;
+//    then the row's partials as above), one rounding to binary32.
 // A format whose levels carry a constant offset (Q4_0: nibble - 8, Q5_0: - 16,
 // Q3_K: - 4, Q6_K: - 32) is dotted on its raw unsigned levels and corrected by
 // the offset times the activation sum, which is the same integer.
@@ -337,8 +338,7 @@ __device__ __forceinline__ void load_act(int gc, const float* __restrict__ x, co
 }
 
 // A sub-block (decoded from b, j) against its activation: Dequant's binary64
-// sum of its 32 products (ta, in ascending order), or the quantized modes'
-// scale (ta) and part (tb).
+// sum of its 32 products (ta), or the quantized modes' scale (ta) and part (tb).
 template <int F, int MODE, typename Acc>
 __device__ __forceinline__ void sub_term(const uint8_t* __restrict__ b, int j, const Act<MODE>& A, Acc& ta, Acc& tb) {
   Sub s;
@@ -449,8 +449,9 @@ constexpr int DPP_ROW_SHL12 = 0x10C;
 // Each step the wave copies its rows' bytes for the step into its own LDS slot
 // with aligned 16-byte loads (issued one step ahead), and the lanes decode their
 // sub-blocks from there; the LDS copy keeps every byte's address mod 16, so the
-// decoders' alignment holds.  The activation is read straight from global
-// memory (L1/L2-resident): the rows of a wave share each sub-block's.
+// decoders' alignment holds.  The quantized modes read the activation straight
+// from global memory (L1/L2-resident; the rows of a wave share each
+// sub-block's); Dequant's travels with the weight pieces into the slot.
 // Lane j < 4 of a row owns partial j (blocks g = j mod 4): it folds its own
 // sub-block, then those of lanes j + 4, j + 8, j + 12 (DPP row shifts), so each
 // partial takes its blocks in ascending order.
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   using G = Seg<F, ROWS>;
   using T = Stage<F, MODE, ROWS>;
   constexpr bool SUP = G::SUP;
-  constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NA = T::NA, NT = T::NT, NPL = T::NPL;
+  constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NT = T::NT, NPL = T::NPL;
   extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   uint8_t* slot = (uint8_t*)lds_dyn + wave * T::SLOT;
