@@ -93,7 +93,7 @@ def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by output "
-              "rows across GPUs, but this build runs and times a single GPU)", file=sys.stderr)
+              "rows across GPUs, but only the one-GPU path is implemented and timed)", file=sys.stderr)
         return 2
 
     import numpy as np
