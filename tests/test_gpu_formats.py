@@ -179,3 +179,33 @@ def test_fmt_tiny(fmt, N, K, mode):
             want = oracle.gemv_fmt(fmt, mode, w, N, K, xq=oq, xl=ol, xs=os_, splits=S)[0]
             q.gemv_fmt(fmt, mode, dw, N, K, y, xq=dev(oq), xl=None if ol is None else dev(ol), xs=dev(os_), splits=S)
             np.testing.assert_array_equal(host(y), want, err_msg=f"S={S}")
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_fmt_mxfp4_scale_extremes(mode):
+    """MXFP4 blocks whose E8M0 scale byte is 0 or 1 (binary32 subnormal scales),
+    2, 127 or 200, mixed along the rows: the GPU keeps binary32 subnormals as the
+    oracle does (quantized modes bit-exact, Dequant within one ulp)."""
+    from gguf_blocks import MXFP4
+    N, K = 40, 1024
+    announce(f"gemv_fmt mxfp4 scale extremes mode={mode}")
+    rng = np.random.default_rng(77 + mode)
+    w, _, _, _ = encode(MXFP4, N, K, rng)
+    blocks = w.reshape(N, K // 32, 17)
+    blocks[:, :, 0] = rng.choice(np.array([0, 1, 2, 127, 200], np.uint8), size=(N, K // 32))
+    blocks[:8, :, 0] = 0  # whole rows of subnormal scales
+    w = blocks.reshape(N, -1)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+    if mode == 0:
+        want = oracle.gemv_fmt(MXFP4, 0, w, N, K, x=x)[0]
+        q.gemv_fmt(MXFP4, 0, dev(w.reshape(-1)), N, K, y, x=dev(x))
+        got = host(y)
+        d = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert d.max() <= 1, int(d.max())
+    else:
+        oq, ol, os_ = oracle.quantize(mode, x)
+        want = oracle.gemv_fmt(MXFP4, mode, w, N, K, xq=oq, xl=ol, xs=os_)[0]
+        q.gemv_fmt(MXFP4, mode, dev(w.reshape(-1)), N, K, y, xq=dev(oq), xl=None if ol is None else dev(ol), xs=dev(os_))
+        np.testing.assert_array_equal(host(y), want)
+    assert np.all(np.isfinite(want)) and np.any(np.abs(want[:8]) < 1e-30)

@@ -182,3 +182,14 @@ def test_workload_block_matrix_is_a_valid_matrix(fmt):
     _, d, c = oracle.fmt_decode(fmt, b, 4, K)
     assert np.all(np.isfinite(d)) and np.all(np.isfinite(c)) and np.any(d != 0)
     np.testing.assert_array_equal(b, workloads.block_matrix(fmt, 4, K, 9))
+
+
+def test_mxfp4_e8m0_extremes():
+    """MXFP4's E8M0 byte e gives the scale 2^(e-128) for the doubled E2M1 levels:
+    e = 0 and 1 are binary32 subnormals (2^-128, 2^-127), 127 and 128 are 1/2
+    and 1, and 255 (E8M0's NaN code) decodes as 2^127 like every other byte."""
+    nib = np.arange(16)
+    for e, want in ((0, 2.0 ** -128), (1, 2.0 ** -127), (127, 0.5), (128, 1.0), (254, 2.0 ** 126), (255, 2.0 ** 127)):
+        blk = np.array([e] + [int(a) | (int(b) << 4) for a, b in zip(nib, nib[::-1])], np.uint8)
+        _, d, c = oracle.fmt_decode(MXFP4, blk[None, :], 1, 32)
+        assert float(d[0, 0]) == want and float(d[0, 1]) == want and not np.any(c), (e, d[0])
