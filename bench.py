@@ -58,8 +58,13 @@ def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
     shape = q.sk_workgroup_shape(mode, sh.K, S) if path == "fused" else None
     if shape is not None:
         rows, waves = shape
-        local = "true" if rows == 4 else "false"
-        return f"k_gemv_wsplit<{mode}, {rows // 4}, 4, {local}>", 64 * waves * -(-sh.N // rows)
+        # the library's staging rule (its STAGE template argument): per-wave copies (1) for one
+        # row group, else LDS DMA (2) when K is a multiple of 256 (torch's buffers are 256-byte
+        # aligned), else the workgroup copy (0); QDG_WS_LOCAL / QDG_WS_DMA override as in the library
+        loc = os.environ.get("QDG_WS_LOCAL")
+        dma = sh.K % 256 == 0 and not os.environ.get("QDG_WS_DMA", "1").startswith("0")
+        stage = 1 if (loc.startswith("1") if loc else rows == 4) else (2 if dma else 0)
+        return f"k_gemv_wsplit<{mode}, {rows // 4}, 4, {stage}>", 64 * waves * -(-sh.N // rows)
     flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
     return f"k_gemv_dot4<{mode}, 4, 4, {flags}, false>", 256 * -(-sh.N // 16) * S
 
@@ -158,9 +163,11 @@ def main() -> int:
         }
 
     # ---- S per (mode, shape): fixed (default 4 for the o-proj, 8 for the down-proj), or timed
-    # Measured best (back-to-back, rotated copies): the in-workgroup combine at S = 5 on both
-    # projections (5120x25600: five chunks of 5120 values, three row groups, one round of
-    # workgroups; 5120x8192: the same four chunks as S = 4); the workspace paths at 4 and 16.
+    # Measured best: the in-workgroup combine at S = 5 on both projections (5120x25600: five
+    # chunks of 5120 values, three row groups, one round of 427 workgroups of 15 waves;
+    # 5120x8192: four non-empty chunks, 427 workgroups of 12 waves); the workspace paths at 4
+    # and 16.  Back-to-back launches of the o-proj alone favour S = 3 by 2-4%, but whole steps
+    # at S = 3 on the o-proj ran 1-2% slower than at S = 5.
     default_splits = {"fused": "5,5", "staged": "4,16", "single": "4,16"}
 
     def splits_for(path):

@@ -187,6 +187,53 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (float)(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
+// LDS DMA (gfx950 global_load_lds_dwordx4): each active lane's 16 bytes at g
+// land at l + 16*lane, with l the same for the whole wave (it goes to M0).  The
+// load counts in vmcnt like any other; it needs no VGPR for the data.
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// Requests step group gi's weights of the lane (U loads of 16 bytes, blocks
+// g0 + (gi*U + u)*8 + j).  The loads are always issued, so every wave has the
+// same number in flight and the compiler can count them: a lane whose block lies
+// at or past g1 reads block g1 - 1 again, and chunk_dot4 never adds its term.
+// The scheduling barriers keep the requests where they are written.
+template <int U>
+__device__ __forceinline__ void group_load(int4 (&w)[U], const int8_t* wrow, int g0, int g1, int gi, int j) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = g0 + (gi * U + u) * 8 + j;
+    w[u] = ld16_stream(wrow + (int64_t)(b < g1 ? b : g1 - 1) * QK);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step group gi's terms: U steps of 8 blocks; block bl of the chunk (lane pair
+// j = bl mod 8) adds its step to partial bl mod 4 -- lanes j < 4 take blocks j
+// and then j + 4 of each step, the latter moved over by DPP.  Blocks at or past
+// nwb add nothing.
+template <int MODE, int U>
+__device__ __forceinline__ void group_terms(const int4 (&w)[U], const int8_t* lq, const int8_t* ll, const float* lsx,
+                                            const uint16_t* my_sg, int g0, int nwb, int j, int hf, int gi, float& p) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int bl = (gi * U + u) * 8 + j;  // block within the chunk
+    const bool ok = bl < nwb;
+    const int blc = g0 + (ok ? bl : 0);
+    const int d = block_dot_pair(w[u], *(const int4*)(lq + blc * QK + hf * 16));
+    int e = 0;
+    if constexpr (MODE == 2) e = block_dot_pair(w[u], *(const int4*)(ll + blc * QK + hf * 16));
+    float ta, tb;
+    q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
+    p = ok ? __fmaf_rn(ta, tb, p) : p;
+    const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
+    p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
+  }
+}
+
 // One wave's chunk partial of four rows (16 lanes a row, a lane pair a block),
 // the lane kernel library page's row order restricted to blocks [g0, g1): block
 // g's step p <- fma(a, b, p) goes into partial g mod 4 (lane pair g mod 4 of the
@@ -194,40 +241,37 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // then (P0 + P2) + (P1 + P3), returned in lane 0 of the row (the other lanes
 // hold partial sums).  wrow points at the lane's row plus 16*hf; lq, ll and lsx
 // hold the activation words and scales by absolute block, my_sg the row's
-// weight scales by absolute block.  wcur holds the first U steps' weights,
-// requested by the caller (so they can be in flight across its staging).
+// weight scales by absolute block.
+//
+// The weights stream through two named buffers of U steps: wa holds group 0 and
+// wb group 1 on entry (requested by the caller with group_load, so they can be
+// in flight across its staging), and each is refilled two groups ahead right
+// after its terms are taken.  One to two groups stay in flight, and no register
+// copy has to wait for a load (a copy-based double buffer drains every load at
+// each copy).  The wave-uniform bounds keep the loop scalar.
 template <int MODE, int U>
 __device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
-                                            const uint16_t* my_sg, int g0, int g1, int j, int hf, int4 (&wcur)[U]) {
-  constexpr int BPS = 8;
+                                            const uint16_t* my_sg, int g0, int g1, int j, int hf, int4 (&wa)[U],
+                                            int4 (&wb)[U]) {
   const int nwb = g1 - g0;
-  const int ngroups = ((nwb + BPS - 1) / BPS + U - 1) / U;
+  const int ngroups = ((nwb + 7) / 8 + U - 1) / U;
   float p = 0.0f;
-  for (int gi = 0; gi < ngroups; ++gi) {
-    int4 wnxt[U];
-    const bool more = gi + 1 < ngroups;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = g0 + ((gi + 1) * U + u) * BPS + j;
-      wnxt[u] = more && b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bl = (gi * U + u) * BPS + j;  // block within the chunk
-      const bool ok = bl < nwb;
-      const int blc = g0 + (ok ? bl : 0);
-      const int4 a = *(const int4*)(lq + blc * QK + hf * 16);
-      const int d = block_dot_pair(wcur[u], a);
-      int e = 0;
-      if constexpr (MODE == 2) e = block_dot_pair(wcur[u], *(const int4*)(ll + blc * QK + hf * 16));
-      float ta, tb;
-      q8_term<MODE>(half_bits_to_float(my_sg[blc]), lsx[blc], d, e, ta, tb);
-      p = ok ? __fmaf_rn(ta, tb, p) : p;
-      const float ta2 = dpp_f32<DPP_ROW_SHL8>(ta), tb2 = dpp_f32<DPP_ROW_SHL8>(tb);
-      p = bl + 4 < nwb ? __fmaf_rn(ta2, tb2, p) : p;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
+  int gi = 0;
+  // while both refills are due: no branch inside, so each group waits for its own loads only
+  for (; gi + 3 < ngroups; gi += 2) {
+    group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi, p);
+    group_load<U>(wa, wrow, g0, g1, gi + 2, j);
+    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
+    group_load<U>(wb, wrow, g0, g1, gi + 3, j);
+  }
+  // the last one to three groups (a group past the chunk adds nothing)
+  group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi, p);
+  if (ngroups - gi == 3) {
+    group_load<U>(wa, wrow, g0, g1, gi + 2, j);
+    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
+    group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 2, p);
+  } else {
+    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
   }
   const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
   return __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));

@@ -11,6 +11,14 @@
 // one block (quant_lane4).  So g, u, h and the words are bit-identical to two
 // qdg_gemv_q8 calls followed by qdg_swiglu_quantize, without the g/u round trip
 // or the extra launch.
+//
+// Staging (DMA): as in the split-K GEMV, the activation and the 64 rows' weight
+// scales go straight from global memory into LDS (global_load_lds_dwordx4)
+// while each wave's first two step groups of weights are in flight, when K is a
+// multiple of 256 and every staged array is 16-byte aligned; otherwise they are
+// copied through registers.
+#include <stdlib.h>
+
 #include "qdg_device.h"
 
 namespace qdg {
@@ -23,7 +31,7 @@ constexpr int GL_LDS_MAX = 79 * 1024;      // two workgroups a CU
 template <int MODE>
 constexpr int gl_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * GL_ROWS; }
 
-template <int MODE>
+template <int MODE, bool DMA>
 __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_glu(
     const int8_t* __restrict__ wg, const uint16_t* __restrict__ sg, const int8_t* __restrict__ wu,
     const uint16_t* __restrict__ su, int64_t K, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
@@ -32,7 +40,7 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   constexpr int U = 4, LPR = 16;
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ float lout[GL_ROWS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
   const int64_t o0 = (int64_t)blockIdx.x * 32;
@@ -45,23 +53,47 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   float* lsx = (float*)(lds + nb * QK * (MODE == 2 ? 2 : 1));  // [nb]
   uint16_t* lsg = (uint16_t*)(lsx + nb);                       // [64][nb]: gate rows, then up rows
 
-  int4 wcur[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int b = u * 8 + j;
-    wcur[u] = b < nb ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+  // the first step groups of weights are requested before the staging (the
+  // second one too where the staging needs no registers)
+  int4 wa[U], wb[U];
+  group_load<U>(wa, wrow, 0, (int)nb, 0, j);
+  if constexpr (DMA) {
+    group_load<U>(wb, wrow, 0, (int)nb, 1, j);
+    const int64_t nsx = nb * 4, nsg = 32 * nb * 2;  // multiples of 16 bytes (nb is a multiple of 8)
+    for (int64_t base = (int64_t)wave * 1024; base < K; base += 16 * 1024) {
+      if (base + lane * 16 < K) {
+        lds_dma16(xq + base + lane * 16, lq + base);
+        if constexpr (MODE == 2) lds_dma16(xl + base + lane * 16, ll + base);
+      }
+    }
+    for (int64_t base = (int64_t)wave * 1024; base < nsx; base += 16 * 1024)
+      if (base + lane * 16 < nsx) lds_dma16((const int8_t*)xs + base + lane * 16, (int8_t*)lsx + base);
+    // the 32 gate rows, then the 32 up rows: each a consecutive run of scales
+    for (int64_t base = (int64_t)wave * 1024; base < 2 * nsg; base += 16 * 1024) {
+      const int64_t off = base + lane * 16;  // a wave's piece may straddle the two runs: each lane picks its own
+      if (off < 2 * nsg) {
+        const int8_t* src = off < nsg ? (const int8_t*)(sg + o0 * nb) + off : (const int8_t*)(su + o0 * nb) + (off - nsg);
+        lds_dma16(src, (int8_t*)lsg + base);
+      }
+    }
+    // every load of the wave (the staged bytes and both weight groups) has landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    for (int64_t i = tid; i < nb * 2; i += GL_NT) {
+      ((int4*)lq)[i] = ld16(xq + 16 * i);
+      if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + 16 * i);
+    }
+    for (int64_t i = tid; i < nb; i += GL_NT) lsx[i] = xs[i];
+    // rows past F do not occur: F is a multiple of 32
+    stage_scales(lsg, (int)nb, sg, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
+    stage_scales(lsg + 32 * nb, (int)nb, su, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
+    __syncthreads();
+    group_load<U>(wb, wrow, 0, (int)nb, 1, j);
   }
-  for (int64_t i = tid; i < nb * 2; i += GL_NT) {
-    ((int4*)lq)[i] = ld16(xq + 16 * i);
-    if constexpr (MODE == 2) ((int4*)ll)[i] = ld16(xl + 16 * i);
-  }
-  for (int64_t i = tid; i < nb; i += GL_NT) lsx[i] = xs[i];
-  // rows past F do not occur: F is a multiple of 32
-  stage_scales(lsg, (int)nb, sg, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
-  stage_scales(lsg + 32 * nb, (int)nb, su, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
-  __syncthreads();
 
-  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, lsg + (up ? 32 + rr : rr) * nb, 0, (int)nb, j, hf, wcur);
+  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, lsg + (up ? 32 + rr : rr) * nb, 0, (int)nb, j, hf, wa, wb);
   if (li == 0) lout[(up ? 32 : 0) + rr] = yv;
   __syncthreads();
   if (wave == 0) {
@@ -83,17 +115,30 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   }
 }
 
+template <int MODE, bool DMA>
+hipError_t launch_glu_s(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
+                        int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq,
+                        int8_t* hl, float* hs, hipStream_t st) {
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_glu<MODE, DMA>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, GL_LDS_MAX);
+  if (attr != hipSuccess) return attr;
+  const size_t lds = (size_t)(K / QK) * gl_bytes_per_block<MODE>();
+  const dim3 grid((unsigned)(F / 32)), block(GL_NT);
+  hipLaunchKernelGGL((k_gemv_glu<MODE, DMA>), grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
+  return hipGetLastError();
+}
+
+// LDS DMA staging when K is a multiple of 256 and every staged array starts
+// 16-byte aligned; QDG_WS_DMA=0 turns it off (read on every call).
 template <int MODE>
 hipError_t launch_glu_m(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
                         int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq,
                         int8_t* hl, float* hs, hipStream_t st) {
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)&k_gemv_glu<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, GL_LDS_MAX);
-  if (attr != hipSuccess) return attr;
-  const size_t lds = (size_t)(K / QK) * gl_bytes_per_block<MODE>();
-  const dim3 grid((unsigned)(F / 32)), block(GL_NT);
-  hipLaunchKernelGGL(k_gemv_glu<MODE>, grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
-  return hipGetLastError();
+  bool dma = K % 256 == 0 && (((uintptr_t)xq | (uintptr_t)xs | (uintptr_t)sg | (uintptr_t)su) & 15) == 0 &&
+             (MODE == 1 || ((uintptr_t)xl & 15) == 0);
+  if (const char* e = getenv("QDG_WS_DMA")) dma = dma && e[0] != '0';
+  if (dma) return launch_glu_s<MODE, true>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  return launch_glu_s<MODE, false>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
 }
 
 }  // namespace

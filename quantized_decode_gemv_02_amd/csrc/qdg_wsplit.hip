@@ -10,10 +10,19 @@
 //
 // Layout: a workgroup has R row groups of four rows times one wave per
 // non-empty chunk (at most 16 waves).  The workgroup stages the whole activation
-// row (words, scales)
-// and its rows' weight scales in LDS, since its waves between them cover all of
-// K.  A wave's lanes work as in k_gemv_dot4 with four rows a wave: 16 lanes a
-// row, a lane pair a block, partial q of the row in lane pair q.
+// row (words, scales) and its rows' weight scales in LDS, since its waves
+// between them cover all of K.  A wave's lanes work as in k_gemv_dot4 with four
+// rows a wave: 16 lanes a row, a lane pair a block, partial q of the row in lane
+// pair q.
+//
+// Staging (STAGE): WS_DMA moves the staged bytes straight from global memory
+// into LDS (global_load_lds_dwordx4) after each wave has requested its first two
+// step groups of weights, so the weights, the activation and the scales are all
+// in flight together and one wait covers them; it needs 16-byte aligned inputs
+// and K a multiple of 256.  WS_BARRIER (the others) copies through registers
+// with the whole workgroup; WS_LOCAL has each wave copy only its own chunk and
+// start without a workgroup barrier (waves of different row groups that share a
+// chunk write the same bytes).
 #include <stdlib.h>
 
 #include "qdg_device.h"
@@ -22,16 +31,13 @@ namespace qdg {
 namespace {
 
 constexpr int WS_NT = 1024;               // sixteen waves
+enum { WS_BARRIER = 0, WS_LOCAL = 1, WS_DMA = 2 };
 constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with the static part
 
 template <int MODE, int ROWS>
 constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
 
-// LOCAL: each wave stages only its own chunk (and its rows' scales over it) and
-// starts as soon as its own stores are done, with no workgroup barrier before
-// the dot products; waves of different row groups that share a chunk write the
-// same bytes.
-template <int MODE, int R, int U, bool LOCAL>
+template <int MODE, int R, int U, int STAGE>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
 __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
     const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
@@ -41,7 +47,8 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ float lpart[WS_NT / 64][4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: every per-chunk bound below is then wave-uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // wave c of a row group takes the c-th non-empty chunk: chunks 0..m-1, then
   // chunk S-1 when it holds the K mod 512 tail; the empty chunks' partials are
   // +0 and adding +0 changes no partial sum (none is -0), so they are skipped
@@ -69,14 +76,33 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   uint16_t* lsg = (uint16_t*)(lsx + nb);                                   // [ROWS][nb]
   const uint16_t* my_sg = lsg + rr * nb;
 
-  // the wave's first weights are requested before the staging barrier
-  int4 wcur[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int b = g0 + u * BPS + j;
-    wcur[u] = b < g1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
-  }
-  if constexpr (LOCAL) {
+  // the wave's first step groups of weights are requested before the staging
+  // (the second one too where the staging needs no registers)
+  int4 wa[U], wb[U];
+  group_load<U>(wa, wrow, g0, g1, 0, j);
+  if constexpr (STAGE == WS_DMA) {
+    group_load<U>(wb, wrow, g0, g1, 1, j);
+    // whole 1 KiB pieces a wave instruction; the byte counts are multiples of 16
+    // (K and nb are multiples of 256 and 8), so a lane's 16 bytes are all in range
+    const int nwv = (int)(blockDim.x >> 6);
+    const int64_t rows_ok = N - o_wg < ROWS ? N - o_wg : ROWS;  // rows past N stay unstaged; their results are dropped
+    const int64_t nsx = nb * 4, nsg = rows_ok * nb * 2;
+    const int8_t* sgsrc = (const int8_t*)(ws + o_wg * nb);      // the workgroup's rows are consecutive
+    for (int64_t base = (int64_t)wave * 1024; base < K; base += (int64_t)nwv * 1024) {
+      if (base + lane * 16 < K) {
+        lds_dma16(xq + base + lane * 16, lq + base);
+        if constexpr (MODE == 2) lds_dma16(xl + base + lane * 16, ll + base);
+      }
+    }
+    for (int64_t base = (int64_t)wave * 1024; base < nsx; base += (int64_t)nwv * 1024)
+      if (base + lane * 16 < nsx) lds_dma16((const int8_t*)xs + base + lane * 16, (int8_t*)lsx + base);
+    for (int64_t base = (int64_t)wave * 1024; base < nsg; base += (int64_t)nwv * 1024)
+      if (base + lane * 16 < nsg) lds_dma16(sgsrc + base + lane * 16, (int8_t*)lsg + base);
+    // every load of the wave (the staged bytes and both weight groups) has landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (STAGE == WS_LOCAL) {
     for (int i = lane; i < nwb * 2; i += 64) {
       const int64_t k = (int64_t)g0 * 2 + i;
       ((int4*)lq)[k] = ld16(xq + 16 * k);
@@ -98,9 +124,10 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     stage_scales(lsg, (int)nb, ws, nb, N, o_wg, ROWS, 0, (int)nb, tid, nt);
     __syncthreads();
   }
+  if constexpr (STAGE != WS_DMA) group_load<U>(wb, wrow, g0, g1, 1, j);
 
   // the chunk's partial of the row, in lane 0 of the row
-  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, wcur);
+  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, wa, wb);
   if (li == 0) lpart[wave][r] = yv;
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
@@ -127,27 +154,39 @@ void ws_chunks(int64_t K, int S, int& m, int& ceff) {
 template <int MODE, int R>
 size_t ws_lds_bytes(int64_t K) { return (size_t)(K / QK) * ws_bytes_per_block<MODE, 4 * R>(); }
 
-template <int MODE, int R, bool LOCAL>
+template <int MODE, int R, int STAGE>
 hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
                      hipStream_t st) {
   int m, ceff;
   ws_chunks(K, S, m, ceff);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, 4, LOCAL>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, 4, STAGE>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
   const size_t lds = ws_lds_bytes<MODE, R>(K);
-  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, LOCAL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
+  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, STAGE>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
   return hipGetLastError();
 }
 
-// Per-wave staging when a row group is the whole workgroup (each wave's chunk is
-// its own), the workgroup barrier otherwise (row groups share the staged chunks).
-// Measured on 5120x25600 / 5120x8192: per-wave staging is 4% faster with one row
-// group, 1-6% slower with two or four.  QDG_WS_LOCAL=0/1 overrides (read on every call).
-bool ws_local(int R) {
-  if (const char* e = getenv("QDG_WS_LOCAL")) return e[0] == '1';
-  return R == 1;
+// The staging: per-wave copies when a row group is the whole workgroup (each
+// wave's chunk is its own); otherwise LDS DMA when every staged array starts
+// 16-byte aligned and K is a multiple of 256 (whole 16-byte pieces of every
+// array), else the workgroup copy.  Measured on 5120x25600 / 5120x8192:
+//   - three row groups (S = 5): the DMA staging is 4-10% faster than the copy;
+//   - one row group (S = 16): per-wave copies beat the DMA on the 25600-value
+//     rows by 2-8% and lose on the 8192-value rows by 4-8%;
+//   - with the copy, per-wave staging was 4% faster with one row group and 1-6%
+//     slower with two or four.
+// QDG_WS_LOCAL=1 forces the per-wave copies, QDG_WS_LOCAL=0 the workgroup-wide
+// staging; QDG_WS_DMA=0 turns the DMA off (both read on every call).
+int ws_stage(int R, const PartTable& tab, int64_t K, int mode, const int8_t* xq, const int8_t* xl, const float* xs) {
+  bool dma = K % 256 == 0 && ((uintptr_t)xq & 15) == 0 && ((uintptr_t)xs & 15) == 0 &&
+             (mode == 1 || ((uintptr_t)xl & 15) == 0);
+  for (int p = 0; p < tab.n; ++p) dma = dma && ((uintptr_t)tab.ws[p] & 15) == 0;
+  if (const char* e = getenv("QDG_WS_DMA")) dma = dma && e[0] != '0';
+  const char* loc = getenv("QDG_WS_LOCAL");
+  if (loc ? loc[0] == '1' : R == 1) return WS_LOCAL;
+  return dma ? WS_DMA : WS_BARRIER;
 }
 
 // Row groups a workgroup: three where they fit in 16 waves, else as many as fit.
@@ -165,20 +204,23 @@ int ws_groups(int ceff) {
 }
 
 template <int MODE, int R>
-hipError_t launch_ws_local(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
-                           int S, hipStream_t st) {
-  if (ws_local(R)) return launch_ws<MODE, R, true>(tab, K, xq, xl, xs, S, st);
-  return launch_ws<MODE, R, false>(tab, K, xq, xl, xs, S, st);
+hipError_t launch_ws_staged(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
+                            int S, hipStream_t st) {
+  switch (ws_stage(R, tab, K, MODE, xq, xl, xs)) {
+    case WS_DMA: return launch_ws<MODE, R, WS_DMA>(tab, K, xq, xl, xs, S, st);
+    case WS_LOCAL: return launch_ws<MODE, R, WS_LOCAL>(tab, K, xq, xl, xs, S, st);
+    default: return launch_ws<MODE, R, WS_BARRIER>(tab, K, xq, xl, xs, S, st);
+  }
 }
 
 template <int MODE>
 hipError_t launch_ws_mode(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
                           int R, hipStream_t st) {
   switch (R) {
-    case 1: return launch_ws_local<MODE, 1>(tab, K, xq, xl, xs, S, st);
-    case 2: return launch_ws_local<MODE, 2>(tab, K, xq, xl, xs, S, st);
-    case 3: return launch_ws_local<MODE, 3>(tab, K, xq, xl, xs, S, st);
-    default: return launch_ws_local<MODE, 4>(tab, K, xq, xl, xs, S, st);
+    case 1: return launch_ws_staged<MODE, 1>(tab, K, xq, xl, xs, S, st);
+    case 2: return launch_ws_staged<MODE, 2>(tab, K, xq, xl, xs, S, st);
+    case 3: return launch_ws_staged<MODE, 3>(tab, K, xq, xl, xs, S, st);
+    default: return launch_ws_staged<MODE, 4>(tab, K, xq, xl, xs, S, st);
   }
 }
 

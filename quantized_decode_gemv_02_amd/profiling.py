@@ -59,6 +59,11 @@ def trace_by_grid(trace_dir: str) -> dict:
 # MI355X (gfx950): 256 CUs of 4 SIMDs; 512 VGPRs (arch + accumulation) a SIMD lane,
 # allocated in granules of 8; at most 8 waves a SIMD; 160 KiB of LDS a CU.
 CUS, SIMDS, VGPR_FILE, VGPR_GRANULE, WAVES_PER_SIMD, LDS_BYTES = 256, 4, 512, 8, 8, 160 * 1024
+# rocprofv3's VGPR_Count for these gfx950 dispatches is half the allocation: the
+# compiler's resource report (hipcc -Rpass-analysis=kernel-resource-usage) gives
+# 60, 66 and 72 VGPRs for kernels the trace lists at 32, 36 and 36 (allocations
+# 64, 72, 72 in granules of 8), so the trace's figure is doubled here.
+TRACE_VGPR_SCALE = 2
 
 
 def occupancy(vgpr: int, agpr: int, lds: int, wg_size: int, grid: int) -> dict:
@@ -83,7 +88,8 @@ def trace_shapes(trace_dir: str) -> dict:
     for r in csv.DictReader(open(_one(trace_dir, "*kernel_trace.csv"))):
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
         wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
-        out[(short(r["Kernel_Name"]), grid)] = (int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]),
+        out[(short(r["Kernel_Name"]), grid)] = (TRACE_VGPR_SCALE * int(r["VGPR_Count"]),
+                                                TRACE_VGPR_SCALE * int(r["Accum_VGPR_Count"]),
                                                 int(r["LDS_Block_Size"]), wg)
     return out
 
@@ -151,9 +157,11 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
     shapes = trace_shapes(trace_dir)
     occ_meas = per_kernel_counters(occ_dir) if occ_dir else {}
     lines += ["", "## Occupancy and split-K block fill", "",
-              "Theoretical residency from each dispatch's registers as the kernel trace reports them (VGPR + "
-              "AGPR, granule 8, 512 a lane), its LDS (160 KiB a CU; the trace reports the static allocation only "
-              "-- the B = 1 kernels' dynamic windows are a few KB and never the limit) and workgroup size, on 256 "
+              "Theoretical residency from each dispatch's registers (VGPR + AGPR, granule 8, 512 a lane; the "
+              "kernel trace's counts doubled, as they are half the allocation the compiler reports on gfx950), "
+              "its LDS (160 KiB a CU; the trace reports the static allocation only -- the split-K workgroup's "
+              "dynamic window, K/32 x (36 or 68 + 2 x rows) bytes, at most 79 KiB, allows two workgroups a CU, "
+              "as its waves do) and workgroup size, on 256 "
               "CUs x 4 SIMDs with at most 8 waves a SIMD; fill = workgroups / resident capacity (capped at 1), "
               "rounds = workgroups / capacity.  Waves launched: SQ_WAVES from a third pass (--pmc SQ_WAVES "
               "SQ_WAVE_CYCLES GRBM_GUI_ACTIVE), which checks the grid.", "",

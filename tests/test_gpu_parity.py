@@ -357,13 +357,19 @@ def test_in_kernel_combine_bit_exact(mode, N, K, S, path, monkeypatch):
                                    (33, 544, 4), (9, 256, 8), (1, 32, 16), (130, 12288, 8), (20, 25632, 16),
                                    (5120, 25600, 5), (640, 25600, 10), (300, 25600, 13), (50, 25632, 12),
                                    (21, 8192, 3), (64, 4608, 2), (19, 1056, 7)])
-@pytest.mark.parametrize("variant", ["barrier", "wave-local"])
+@pytest.mark.parametrize("variant", ["dma", "barrier", "wave-local"])
 def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
     """The split-K GEMV whose chunks are the waves of one workgroup (partials
     combined in LDS) against the oracle's chunk partials and ascending combine,
-    with the workgroup-wide or the per-wave staging of the activation."""
+    with each staging of the activation: LDS DMA (K a multiple of 256; other K
+    fall back to the workgroup copy), the workgroup-wide copy, the per-wave copy."""
     announce(f"gemv_q8_sk in-workgroup split mode={mode} N={N} K={K} S={S} {variant}")
-    monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
+    if variant == "dma":
+        monkeypatch.delenv("QDG_WS_DMA", raising=False)
+        monkeypatch.setenv("QDG_WS_LOCAL", "0")
+    else:
+        monkeypatch.setenv("QDG_WS_DMA", "0")
+        monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
     wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
     oq, ol, os_ = oracle.quantize(mode, x)
     if N > 1000:  # the oracle on every 7th row (the rows are independent)
