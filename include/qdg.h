@@ -161,9 +161,11 @@ size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
  * and each row's chunk partials are added in ascending chunk order from 0, in
  * place of the QWEN38 page's separate combine kernel.  Two placements, with the
  * same bits:
- *   - splits 4, 8 or 16, when the activation row fits in LDS (K up to 25600 for
- *     QDG_TWOPASS at splits 16, more otherwise): a row tile's chunks are the
- *     waves of one workgroup and meet in LDS; the workspace is not touched;
+ *   - 2 <= splits <= 16 with at least two non-empty chunks, when the activation
+ *     row and the workgroup's weight scales fit in 79 KiB of LDS (K/32 x (36 or
+ *     68 + 8 x row groups) bytes; for QDG_TWOPASS K up to 28128 at splits 5,
+ *     34048 at splits 13 to 16, more for QDG_INT8ACT): a row tile's chunks are
+ *     the waves of one workgroup and meet in LDS; the workspace is not touched;
  *   - otherwise the last workgroup of each 16-row tile to finish (an atomic
  *     ticket per tile; the lane kernel library page's last-arriving-block
  *     pattern) sums the tile's partials through the workspace.

@@ -149,6 +149,11 @@ def test_sk_placement_query():
     assert f(1, 8192, 17) == 0 and f(1, 8192, 64) == 0       # more chunk waves than a workgroup holds
     assert f(1, 512, 16) == 0                                  # one non-empty chunk
     assert f(2, 65536, 16) == 0                                # the staged row exceeds the LDS budget
+    # the LDS budget's edges: K/32 x (68 + 8 x row groups) bytes of at most 79 KiB under TwoPass
+    assert f(2, 28128, 5) == 1 and f(2, 28160, 5) == 0         # three row groups
+    assert f(2, 30816, 8) == 1 and f(2, 30848, 8) == 0         # two row groups
+    assert f(2, 34048, 16) == 1 and f(2, 34080, 16) == 0       # one row group
+    assert f(1, 28160, 5) == 1                                 # Int8Act stages half the words
     # launch shape: one wave per non-empty chunk, row groups of four rows up to 16 waves
     assert q.sk_workgroup_shape(2, 25600, 16) == (4, 13)       # 13 chunks of 4 superblocks, 3 empty
     assert q.sk_workgroup_shape(2, 25600, 5) == (12, 15)       # 5 chunks, three row groups

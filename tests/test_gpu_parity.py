@@ -356,7 +356,9 @@ def test_in_kernel_combine_bit_exact(mode, N, K, S, path, monkeypatch):
 @pytest.mark.parametrize("N,K,S", [(5120, 25600, 16), (5120, 8192, 4), (77, 8192, 8), (4097, 1600, 16),
                                    (33, 544, 4), (9, 256, 8), (1, 32, 16), (130, 12288, 8), (20, 25632, 16),
                                    (5120, 25600, 5), (640, 25600, 10), (300, 25600, 13), (50, 25632, 12),
-                                   (21, 8192, 3), (64, 4608, 2), (19, 1056, 7)])
+                                   (21, 8192, 3), (64, 4608, 2), (19, 1056, 7),
+                                   # the largest TwoPass rows the LDS budget takes (three, two, one row groups)
+                                   (24, 28128, 5), (24, 30720, 8), (8, 34048, 16)])
 @pytest.mark.parametrize("variant", ["dma", "barrier", "wave-local"])
 def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
     """The split-K GEMV whose chunks are the waves of one workgroup (partials
