@@ -10,10 +10,14 @@
 //    by i mod 4, each by fused multiply-adds from +0 in ascending i (every
 //    product w_i*x_i is exact), then (c0 + c1) + (c2 + c3) -- four independent
 //    chains keep the FMA pipeline busy;
-//  * the pair's two half-block sums are added (low half + high half), and the
-//    block's term is sigma * that sum (one binary64 rounding);
-//  * terms go into partial g mod 4 in ascending block order, and the row is
-//    (P0 + P2) + (P1 + P3), then one rounding to binary32.
+//  * the lane folds each half-block sum h into its accumulator as
+//    acc <- fma(sigma, h, acc), in ascending block order from +0 (its blocks are
+//    j, j + BPS, ... of the window, sigma the block's scale);
+//  * the row's lanes meet by a butterfly over lane distances 1, 2, 4 (, 8), then
+//    one rounding to binary32.
+// One FMA a half block replaces the pair's addition, the multiplication by sigma
+// and the DPP moves of a block-sum-first order: 11-12% faster on the 5120-row
+// projections and the 151936-row LM head at S = 1.
 // The lane layout, the LDS staging of the window (the f32 activation and the
 // rows' weight scales) and the load pipeline are those of the quantized kernel
 // (qdg_gemv.hip).
@@ -134,21 +138,16 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
         const bool ok = bl < nwb;
         const int blc = ok ? bl : 0;
         const double hsum = half_dot16<XF64>(wcur[u], lx + (2 * blc + hf) * SEG);
-        const double other = dpp_f64<DPP_QUAD_SWAP1>(hsum);
-        const double blk = __dadd_rn(hsum, other);  // the same bits in both lanes of the pair
-        const double term = __dmul_rn((double)half_bits_to_float(my_sg[blc]), blk);
-        p = ok ? __dadd_rn(p, term) : p;
-        if constexpr (TPP == 2) {
-          const double term2 = dpp_f64<DPP_ROW_SHL8>(term);
-          p = bl + 4 < nwb ? __dadd_rn(p, term2) : p;
-        }
+        p = ok ? __fma_rn((double)half_bits_to_float(my_sg[blc]), hsum, p) : p;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) wcur[u] = wnxt[u];
     }
   }
-  const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL4>(p));
-  const double y = __dadd_rn(t, dpp_f64<DPP_ROW_SHL2>(t));
+  // the row's LPR lanes (a contiguous, aligned group of the wave) by a butterfly
+  double y = p;
+#pragma unroll
+  for (int d = 1; d < LPR; d <<= 1) y = __dadd_rn(y, __shfl_xor(y, d, 64));
   if constexpr (AMAX) {
     __shared__ unsigned long long row_keys[ROWS];
     if (li == 0) {
