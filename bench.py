@@ -64,7 +64,8 @@ def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
         loc = os.environ.get("QDG_WS_LOCAL")
         dma = sh.K % 256 == 0 and not os.environ.get("QDG_WS_DMA", "1").startswith("0")
         stage = 1 if (loc.startswith("1") if loc else rows == 4) else (2 if dma else 0)
-        return f"k_gemv_wsplit<{mode}, {rows // 4}, 4, {stage}>", 64 * waves * -(-sh.N // rows)
+        # template arguments: mode, row groups, steps a weight group (1), groups in flight (4), staging
+        return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}>", 64 * waves * -(-sh.N // rows)
     flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
     return f"k_gemv_dot4<{mode}, 4, 4, {flags}, false>", 256 * -(-sh.N // 16) * S
 

@@ -243,36 +243,37 @@ __device__ __forceinline__ void group_terms(const int4 (&w)[U], const int8_t* lq
 // hold the activation words and scales by absolute block, my_sg the row's
 // weight scales by absolute block.
 //
-// The weights stream through two named buffers of U steps: wa holds group 0 and
-// wb group 1 on entry (requested by the caller with group_load, so they can be
-// in flight across its staging), and each is refilled two groups ahead right
-// after its terms are taken.  One to two groups stay in flight, and no register
-// copy has to wait for a load (a copy-based double buffer drains every load at
-// each copy).  The wave-uniform bounds keep the loop scalar.
-template <int MODE, int U>
+// The weights stream through NB named buffers of U steps: w[k] holds step group
+// k on entry (requested by the caller with group_load, so they can be in flight
+// across its staging), and each buffer is refilled NB groups ahead right after
+// its terms are taken.  Up to NB groups stay in flight, and no register copy has
+// to wait for a load (a copy-based double buffer drains every load at each
+// copy).  The wave-uniform bounds keep the loop scalar.
+template <int MODE, int U, int NB>
 __device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
-                                            const uint16_t* my_sg, int g0, int g1, int j, int hf, int4 (&wa)[U],
-                                            int4 (&wb)[U]) {
+                                            const uint16_t* my_sg, int g0, int g1, int j, int hf,
+                                            int4 (&w)[NB][U]) {
   const int nwb = g1 - g0;
   const int ngroups = ((nwb + 7) / 8 + U - 1) / U;
   float p = 0.0f;
   int gi = 0;
-  // while both refills are due: no branch inside, so each group waits for its own loads only
-  for (; gi + 3 < ngroups; gi += 2) {
-    group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi, p);
-    group_load<U>(wa, wrow, g0, g1, gi + 2, j);
-    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
-    group_load<U>(wb, wrow, g0, g1, gi + 3, j);
+  // while every refill is due: no branch inside, so each group waits for its own loads only
+  for (; gi + 2 * NB - 1 < ngroups; gi += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p);
+      group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
+    }
   }
-  // the last one to three groups (a group past the chunk adds nothing)
-  group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi, p);
-  if (ngroups - gi == 3) {
-    group_load<U>(wa, wrow, g0, g1, gi + 2, j);
-    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
-    group_terms<MODE, U>(wa, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 2, p);
-  } else {
-    group_terms<MODE, U>(wb, lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + 1, p);
+  // the last 1 .. 2*NB - 1 groups, in order (a group past the chunk adds nothing)
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p);
+    if (gi + NB + k < ngroups) group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
   }
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k)
+    if (gi + NB + k < ngroups) group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + NB + k, p);
   const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
   return __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
 }

@@ -14,7 +14,7 @@
 //
 // Staging (DMA): as in the split-K GEMV, the activation and the 64 rows' weight
 // scales go straight from global memory into LDS (global_load_lds_dwordx4)
-// while each wave's first two step groups of weights are in flight, when K is a
+// while each wave's first step groups of weights are in flight, when K is a
 // multiple of 256 and every staged array is 16-byte aligned; otherwise they are
 // copied through registers.
 #include <stdlib.h>
@@ -26,6 +26,7 @@ namespace {
 
 constexpr int GL_NT = 1024;
 constexpr int GL_ROWS = 64;                // 32 gate rows + 32 up rows
+constexpr int GL_U = 1, GL_NB = 4;         // steps a group, groups in flight
 constexpr int GL_LDS_MAX = 79 * 1024;      // two workgroups a CU
 
 template <int MODE>
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     const uint16_t* __restrict__ su, int64_t K, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
     const float* __restrict__ xs, float* __restrict__ h, int8_t* __restrict__ hq, int8_t* __restrict__ hl,
     float* __restrict__ hs) {
-  constexpr int U = 4, LPR = 16;
+  constexpr int U = GL_U, NB = GL_NB, LPR = 16;
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ float lout[GL_ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -55,10 +56,11 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
 
   // the first step groups of weights are requested before the staging (the
   // second one too where the staging needs no registers)
-  int4 wa[U], wb[U];
-  group_load<U>(wa, wrow, 0, (int)nb, 0, j);
+  int4 w[NB][U];
+  group_load<U>(w[0], wrow, 0, (int)nb, 0, j);
   if constexpr (DMA) {
-    group_load<U>(wb, wrow, 0, (int)nb, 1, j);
+#pragma unroll
+    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, 0, (int)nb, k, j);
     const int64_t nsx = nb * 4, nsg = 32 * nb * 2;  // multiples of 16 bytes (nb is a multiple of 8)
     for (int64_t base = (int64_t)wave * 1024; base < K; base += 16 * 1024) {
       if (base + lane * 16 < K) {
@@ -90,10 +92,11 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     stage_scales(lsg, (int)nb, sg, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
     stage_scales(lsg + 32 * nb, (int)nb, su, nb, o0 + 32, o0, 32, 0, (int)nb, tid, GL_NT);
     __syncthreads();
-    group_load<U>(wb, wrow, 0, (int)nb, 1, j);
+#pragma unroll
+    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, 0, (int)nb, k, j);
   }
 
-  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, lsg + (up ? 32 + rr : rr) * nb, 0, (int)nb, j, hf, wa, wb);
+  const float yv = chunk_dot4<MODE, U, NB>(wrow, lq, ll, lsx, lsg + (up ? 32 + rr : rr) * nb, 0, (int)nb, j, hf, w);
   if (li == 0) lout[(up ? 32 : 0) + rr] = yv;
   __syncthreads();
   if (wave == 0) {

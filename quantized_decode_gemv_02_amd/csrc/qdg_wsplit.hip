@@ -16,7 +16,7 @@
 // pair q.
 //
 // Staging (STAGE): WS_DMA moves the staged bytes straight from global memory
-// into LDS (global_load_lds_dwordx4) after each wave has requested its first two
+// into LDS (global_load_lds_dwordx4) after each wave has requested its first NB
 // step groups of weights, so the weights, the activation and the scales are all
 // in flight together and one wait covers them; it needs 16-byte aligned inputs
 // and K a multiple of 256.  WS_BARRIER (the others) copies through registers
@@ -32,12 +32,13 @@ namespace {
 
 constexpr int WS_NT = 1024;               // sixteen waves
 enum { WS_BARRIER = 0, WS_LOCAL = 1, WS_DMA = 2 };
+constexpr int WS_U = 1, WS_NB = 4;  // steps a group, groups in flight
 constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with the static part
 
 template <int MODE, int ROWS>
 constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
 
-template <int MODE, int R, int U, int STAGE>
+template <int MODE, int R, int U, int NB, int STAGE>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
 __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
     const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
@@ -77,11 +78,12 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   const uint16_t* my_sg = lsg + rr * nb;
 
   // the wave's first step groups of weights are requested before the staging
-  // (the second one too where the staging needs no registers)
-  int4 wa[U], wb[U];
-  group_load<U>(wa, wrow, g0, g1, 0, j);
+  // (all NB where the staging needs no registers, else the first)
+  int4 w[NB][U];
+  group_load<U>(w[0], wrow, g0, g1, 0, j);
   if constexpr (STAGE == WS_DMA) {
-    group_load<U>(wb, wrow, g0, g1, 1, j);
+#pragma unroll
+    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, g0, g1, k, j);
     // whole 1 KiB pieces a wave instruction; the byte counts are multiples of 16
     // (K and nb are multiples of 256 and 8), so a lane's 16 bytes are all in range
     const int nwv = (int)(blockDim.x >> 6);
@@ -124,10 +126,13 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     stage_scales(lsg, (int)nb, ws, nb, N, o_wg, ROWS, 0, (int)nb, tid, nt);
     __syncthreads();
   }
-  if constexpr (STAGE != WS_DMA) group_load<U>(wb, wrow, g0, g1, 1, j);
+  if constexpr (STAGE != WS_DMA) {
+#pragma unroll
+    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, g0, g1, k, j);
+  }
 
   // the chunk's partial of the row, in lane 0 of the row
-  const float yv = chunk_dot4<MODE, U>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, wa, wb);
+  const float yv = chunk_dot4<MODE, U, NB>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w);
   if (li == 0) lpart[wave][r] = yv;
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
@@ -159,12 +164,12 @@ hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const in
                      hipStream_t st) {
   int m, ceff;
   ws_chunks(K, S, m, ceff);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, 4, STAGE>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
   const size_t lds = ws_lds_bytes<MODE, R>(K);
-  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, 4, STAGE>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
+  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
   return hipGetLastError();
 }
 
