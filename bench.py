@@ -56,6 +56,8 @@ def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
     it, and its grid in threads."""
     import quantized_decode_gemv_02_amd as q
     shape = q.sk_workgroup_shape(mode, sh.K, S) if path == "fused" else None
+    if os.environ.get("QDG_SK_WSPLIT", "1").startswith("0"):  # the library's override of the placement
+        shape = None
     if shape is not None:
         rows, waves = shape
         # the library's staging rule (its STAGE template argument): per-wave copies (1) for one

@@ -214,15 +214,16 @@ __device__ __forceinline__ void group_load(int4 (&w)[U], const int8_t* wrow, int
 // Step group gi's terms: U steps of 8 blocks; block bl of the chunk (lane pair
 // j = bl mod 8) adds its step to partial bl mod 4 -- lanes j < 4 take blocks j
 // and then j + 4 of each step, the latter moved over by DPP.  Blocks at or past
-// nwb add nothing.
+// nwb add nothing.  The LDS arrays hold block b at index b - lb.
 template <int MODE, int U>
 __device__ __forceinline__ void group_terms(const int4 (&w)[U], const int8_t* lq, const int8_t* ll, const float* lsx,
-                                            const uint16_t* my_sg, int g0, int nwb, int j, int hf, int gi, float& p) {
+                                            const uint16_t* my_sg, int g0, int nwb, int j, int hf, int gi, float& p,
+                                            int lb = 0) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int bl = (gi * U + u) * 8 + j;  // block within the chunk
     const bool ok = bl < nwb;
-    const int blc = g0 + (ok ? bl : 0);
+    const int blc = g0 - lb + (ok ? bl : 0);  // LDS index
     const int d = block_dot_pair(w[u], *(const int4*)(lq + blc * QK + hf * 16));
     int e = 0;
     if constexpr (MODE == 2) e = block_dot_pair(w[u], *(const int4*)(ll + blc * QK + hf * 16));
@@ -249,33 +250,50 @@ __device__ __forceinline__ void group_terms(const int4 (&w)[U], const int8_t* lq
 // its terms are taken.  Up to NB groups stay in flight, and no register copy has
 // to wait for a load (a copy-based double buffer drains every load at each
 // copy).  The wave-uniform bounds keep the loop scalar.
+//
+// chunk_fold adds blocks [g0, g1) into the lane's partial p (so a row split into
+// LDS windows keeps one chain per partial across them; the window's arrays hold
+// block b at index b - lb); chunk_dot4 starts from +0 and ends with the
+// (P0 + P2) + (P1 + P3) reduction.
 template <int MODE, int U, int NB>
-__device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
-                                            const uint16_t* my_sg, int g0, int g1, int j, int hf,
-                                            int4 (&w)[NB][U]) {
+__device__ __forceinline__ void chunk_fold(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
+                                           const uint16_t* my_sg, int g0, int g1, int j, int hf,
+                                           int4 (&w)[NB][U], float& p, int lb = 0) {
   const int nwb = g1 - g0;
   const int ngroups = ((nwb + 7) / 8 + U - 1) / U;
-  float p = 0.0f;
   int gi = 0;
   // while every refill is due: no branch inside, so each group waits for its own loads only
   for (; gi + 2 * NB - 1 < ngroups; gi += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p);
+      group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p, lb);
       group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
     }
   }
   // the last 1 .. 2*NB - 1 groups, in order (a group past the chunk adds nothing)
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p);
+    group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p, lb);
     if (gi + NB + k < ngroups) group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
   }
 #pragma unroll
   for (int k = 0; k + 1 < NB; ++k)
-    if (gi + NB + k < ngroups) group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + NB + k, p);
+    if (gi + NB + k < ngroups) group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + NB + k, p, lb);
+}
+
+// (P0 + P2) + (P1 + P3): partial q sits in lane pair q of the row's 16 lanes.
+__device__ __forceinline__ float row_sum4(float p) {
   const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL4>(p));
   return __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
+}
+
+template <int MODE, int U, int NB>
+__device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
+                                            const uint16_t* my_sg, int g0, int g1, int j, int hf,
+                                            int4 (&w)[NB][U]) {
+  float p = 0.0f;
+  chunk_fold<MODE, U, NB>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w, p);
+  return row_sum4(p);
 }
 
 // Up to MAX_PARTS weight matrices over one activation in one launch (lane kernel

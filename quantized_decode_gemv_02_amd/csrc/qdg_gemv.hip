@@ -21,10 +21,13 @@
 //    words too) and scales, and the weight scales of the workgroup's rows -- is
 //    staged in LDS with 16-byte loads; a lane reads its block's activation with
 //    one ds_read_b128 and its scales with two small LDS reads.
-//  * U steps of weight loads are issued ahead of the steps being computed, so
-//    each wave keeps up to 2*U*1 KB of weights in flight; the first group is
-//    issued before the window's barrier.  Weights are read with the
-//    nontemporal hint (streamed once, never re-read).
+//  * With four rows a wave (the default) the weights stream through four named
+//    one-step buffers (chunk_fold), each refilled four steps ahead, so four
+//    steps (4 KiB a wave) stay in flight and the compiler's waits count exactly;
+//    the four are requested before the window's barrier.  With eight rows a
+//    wave, U steps are issued ahead of the steps being computed through a
+//    copy-based double buffer.  Weights are read with the nontemporal hint
+//    (streamed once, never re-read).
 //  * one workgroup per (row tile, split): the split s of a row covers the QWEN38 chunk
 //    [g0, g1) and writes partial[s][o]; an empty chunk writes +0.
 //  * QX = true (one launch for a whole projection): the workgroup quantizes its
@@ -40,6 +43,7 @@ namespace qdg {
 namespace {
 
 constexpr int WG = 256;                // four waves
+constexpr int DOT_U = 1, DOT_NB = 4;   // four rows a wave: one-step weight groups, four in flight
 constexpr int LDS_BUDGET = 56 * 1024;  // window bytes per workgroup
 
 // LDS bytes per block of the window: activation words (two under TwoPass), the
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
   static_assert(TPP == 1 || TPP == 2, "RPW must be 4 or 8");
   extern __shared__ __align__(16) unsigned char lds[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
   // one workgroup per (row tile, chunk) on a 1-D grid: chunk-major order walks
@@ -99,13 +103,21 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
     const int nwb = wb1 - wb0;
     const int nsteps = (nwb + BPS - 1) / BPS;
     const int ngroups = (nsteps + U - 1) / U;
-    // the first group's weights are requested before the window is staged, so
-    // the weight stream is already in flight across the barrier
+    // the first weights are requested before the window is staged, so the weight
+    // stream is already in flight across the barrier: with four rows a wave, the
+    // first DOT_NB one-step groups of the named-buffer pipeline (chunk_fold);
+    // with eight, the first U steps of the copy-based double buffer
+    int4 w[DOT_NB][DOT_U];
     int4 wcur[U];
+    if constexpr (RPW == 4) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = wb0 + u * BPS + j;
-      wcur[u] = b < wb1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+      for (int k = 0; k < DOT_NB; ++k) group_load<DOT_U>(w[k], wrow, wb0, wb1, k, j);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = wb0 + u * BPS + j;
+        wcur[u] = b < wb1 ? ld16_stream(wrow + (int64_t)b * QK) : make_int4(0, 0, 0, 0);
+      }
     }
     __syncthreads();
     if constexpr (QX) {
@@ -143,6 +155,10 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
     stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
     __syncthreads();
 
+    if constexpr (RPW == 4) {
+      chunk_fold<MODE, DOT_U, DOT_NB>(wrow, lq, ll, lsx, my_sg, (int)wb0, (int)wb1, j, hf, w, p, (int)wb0);
+      continue;
+    }
     for (int gi = 0; gi < ngroups; ++gi) {
       int4 wnxt[U];
       const bool more = gi + 1 < ngroups;
@@ -231,7 +247,8 @@ struct Tuning {
   int order = -1;  // -1: by S (chunk-major for S <= 4), 0: tile-major, 1: chunk-major
 };
 
-// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8}, QDG_ORDER
+// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8} -- the load depth of
+// the eight-rows-a-wave layout only --, QDG_ORDER
 // in {chunk, tile}); they change the lane layout, load depth and workgroup
 // order only, never the arithmetic or its order.
 Tuning tuning() {
