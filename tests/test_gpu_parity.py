@@ -110,7 +110,8 @@ def _quant_case(N, K, B, seed, outliers=False):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-@pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (7, 96), (33, 544), (129, 1600), (70, 4096), (300, 25600)])
+@pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (7, 96), (33, 544), (129, 1600), (70, 4096), (300, 25600),
+                                 (40, 28672)])  # rows longer than one LDS window in both modes
 def test_gemv_quantized_bit_exact(mode, N, K):
     announce(f"gemv mode={mode} N={N} K={K}")
     wq, ws, x = _quant_case(N, K, 1, 10 * N + K)
