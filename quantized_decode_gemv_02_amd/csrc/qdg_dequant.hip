@@ -86,7 +86,7 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
   unsigned char* lx = lds;                                   // [win][2] segments
   uint16_t* lsg = (uint16_t*)(lds + (int64_t)win * 2 * SEG);  // [ROWS][win]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR, li = lane % LPR, j = li >> 1, hf = li & 1;
   const int64_t nb = K / QK;
   int32_t g0, g1;

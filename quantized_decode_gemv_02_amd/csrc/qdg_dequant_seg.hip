@@ -56,16 +56,19 @@ __device__ __forceinline__ int2 ld8_stream(const int8_t* p) {
   return make_int2(t[0], t[1]);
 }
 
-// At most 80 VGPRs (the kernel needs 72, so seven waves a SIMD): capped at 64 it
-// spills, and a register ring for the next step's weights (8 more VGPRs) costs a
-// wave a SIMD; measured, both are slower than letting the SIMD's other waves
-// cover the load latency.
+// At most 80 VGPRs.  With the wave index a scalar (readfirstlane) the chunk
+// bounds and the four rows' pointers sit in SGPRs and the kernel needs 52 VGPRs,
+// eight waves a SIMD (72 and seven without): 5120x25600 at S=8 33.6 -> 31.2 us,
+// the LM head at S=2 181 -> 159 us.  A one-step prefetch of the next step's
+// weights through two named buffers added about 1% more on the larger shapes
+// and lost on the smallest, so the SIMD's other waves cover the load latency.
 template <int R>
 __global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_dq_seg(
     const PartTable tab, const float* __restrict__ x, int64_t K, int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;
   __shared__ double lpart[DS_NT / 64][4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar, so the chunk bounds and row pointers live in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave / ceff, c = wave % ceff;
   const int chunk = c < m ? c : S - 1;
   const int64_t nb = K / QK;

@@ -466,7 +466,7 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   constexpr bool SUP = G::SUP;
   constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NT = T::NT, NPL = T::NPL;
   extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwaves = blockDim.x >> 6;
   uint8_t* slot = (uint8_t*)lds_dyn + wave * T::SLOT;
   uint4* lw = (uint4*)slot;
   Acc* lpart = (Acc*)((uint8_t*)lds_dyn + nwaves * T::SLOT);  // [waves][ROWS]

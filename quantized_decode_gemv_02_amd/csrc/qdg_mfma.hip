@@ -131,7 +131,7 @@ __global__ __launch_bounds__(WG) void k_gemv_mfma(const int8_t* __restrict__ wq,
                                                  const float* __restrict__ xs, int64_t N, int64_t K, int B, int S,
                                                  float* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tau = wave >> 2, res = wave & 3;  // row tile, owned partial
   unsigned char* wtile = lds;                 // [2 slots][32 rows][256 bytes]
   unsigned char* slots = lds + 2 * WTILE;     // [2 slots] of Slot<MODE>
