@@ -78,10 +78,10 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
         lds_dma16(src, (int8_t*)lsg + base);
       }
     }
-    // every load of the wave (the staged bytes and both weight groups) has landed
+    // every load of the wave (the staged bytes and the first weight groups) has
+    // landed; the barrier's workgroup fences keep every LDS read below it
     __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   } else {
     for (int64_t i = tid; i < nb * 2; i += GL_NT) {
       ((int4*)lq)[i] = ld16(xq + 16 * i);

@@ -100,10 +100,10 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
       if (base + lane * 16 < nsx) lds_dma16((const int8_t*)xs + base + lane * 16, (int8_t*)lsx + base);
     for (int64_t base = (int64_t)wave * 1024; base < nsg; base += (int64_t)nwv * 1024)
       if (base + lane * 16 < nsg) lds_dma16(sgsrc + base + lane * 16, (int8_t*)lsg + base);
-    // every load of the wave (the staged bytes and both weight groups) has landed
+    // every load of the wave (the staged bytes and the first weight groups) has
+    // landed; the barrier's workgroup fences keep every LDS read below it
     __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   } else if constexpr (STAGE == WS_LOCAL) {
     for (int i = lane; i < nwb * 2; i += 64) {
       const int64_t k = (int64_t)g0 * 2 + i;
