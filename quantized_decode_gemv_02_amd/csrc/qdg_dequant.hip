@@ -20,7 +20,7 @@
 // projections and the 151936-row LM head at S = 1.
 // The lane layout, the LDS staging of the window (the f32 activation and the
 // rows' weight scales) and the load pipeline are those of the quantized kernel
-// (qdg_gemv.hip).
+// (qdg_gemv.hip): four named one-step weight buffers at four rows a wave (dq_fold).
 //
 // Split-K (S > 1, the QWEN38 page's chunk rule, gk_gemv_hl_sk): chunk s of a row
 // sums its blocks in the order above into a binary64 partial; the last workgroup
@@ -64,6 +64,50 @@ __device__ __forceinline__ double half_dot16(int4 w, const void* __restrict__ xv
   return __dadd_rn(__dadd_rn(c[0], c[1]), __dadd_rn(c[2], c[3]));
 }
 
+// One step group's half blocks (four rows a wave: lane pair j takes block j of
+// each 8-block step, lane hf its half): acc <- fma(sigma, half-block sum, acc) in
+// ascending block order.  lx and my_sg are the window's (index = block - wb0).
+template <bool XF64, int U, int SEG>
+__device__ __forceinline__ void dq_terms(const int4 (&w)[U], const unsigned char* lx, const uint16_t* my_sg, int nwb,
+                                         int j, int hf, int gi, double& p) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int bl = (gi * U + u) * 8 + j;
+    const bool ok = bl < nwb;
+    const int blc = ok ? bl : 0;
+    const double hsum = half_dot16<XF64>(w[u], lx + (2 * blc + hf) * SEG);
+    p = ok ? __fma_rn((double)half_bits_to_float(my_sg[blc]), hsum, p) : p;
+  }
+}
+
+// The window [wb0, wb1) through NB named one-step buffers (w[k] holds step group k
+// on entry), each refilled NB groups ahead: the quantized kernels' chunk_fold with
+// the binary64 half-block terms.
+template <bool XF64, int U, int NB, int SEG>
+__device__ __forceinline__ void dq_fold(const int8_t* wrow, const unsigned char* lx, const uint16_t* my_sg, int wb0,
+                                        int wb1, int j, int hf, int4 (&w)[NB][U], double& p) {
+  const int nwb = wb1 - wb0;
+  const int ngroups = ((nwb + 7) / 8 + U - 1) / U;
+  int gi = 0;
+  for (; gi + 2 * NB - 1 < ngroups; gi += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      dq_terms<XF64, U, SEG>(w[k], lx, my_sg, nwb, j, hf, gi + k, p);
+      group_load<U>(w[k], wrow, wb0, wb1, gi + NB + k, j);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    dq_terms<XF64, U, SEG>(w[k], lx, my_sg, nwb, j, hf, gi + k, p);
+    if (gi + NB + k < ngroups) group_load<U>(w[k], wrow, wb0, wb1, gi + NB + k, j);
+  }
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k)
+    if (gi + NB + k < ngroups) dq_terms<XF64, U, SEG>(w[k], lx, my_sg, nwb, j, hf, gi + NB + k, p);
+}
+
+constexpr int DQ_U = 1, DQ_NB = 4;  // four rows a wave: one-step weight groups, four in flight
+
 // AMAX (S == 1): the workgroup also writes the arg-max key of its rows' largest
 // output to keys[blockIdx.x] (as the quantized kernel's epilogue does).
 template <int RPW, int U, bool XF64, bool AMAX = false>
@@ -104,11 +148,19 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
     const int nwb = (int)(wb1 - wb0);
     const int nsteps = (nwb + BPS - 1) / BPS;
     const int ngroups = (nsteps + U - 1) / U;
+    // four rows a wave: the first DQ_NB one-step groups of the named-buffer
+    // pipeline; eight rows a wave: the first U steps of a copy-based double buffer
+    int4 w[DQ_NB][DQ_U];
     int4 wcur[U];
+    if constexpr (RPW == 4) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bl = u * BPS + j;
-      wcur[u] = bl < nwb ? ld16_stream(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
+      for (int k = 0; k < DQ_NB; ++k) group_load<DQ_U>(w[k], wrow, (int)wb0, (int)wb1, k, j);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int bl = u * BPS + j;
+        wcur[u] = bl < nwb ? ld16_stream(wrow + (wb0 + bl) * QK) : make_int4(0, 0, 0, 0);
+      }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nwb * 8; i += WG) {  // i: 4 values, segment i/4, quarter i%4
@@ -124,6 +176,10 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
     stage_scales(lsg, win, ws, nb, N, o_wg, ROWS, wb0, nwb, threadIdx.x, WG);
     __syncthreads();
 
+    if constexpr (RPW == 4) {
+      dq_fold<XF64, DQ_U, DQ_NB, SEG>(wrow, lx, my_sg, (int)wb0, (int)wb1, j, hf, w, p);
+      continue;
+    }
     for (int gi = 0; gi < ngroups; ++gi) {
       int4 wnxt[U];
       const bool more = gi + 1 < ngroups;
