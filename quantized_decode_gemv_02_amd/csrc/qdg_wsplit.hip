@@ -44,7 +44,7 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
     int64_t K, int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;   // rows of the workgroup
-  constexpr int LPR = 16, BPS = 8;
+  constexpr int LPR = 16;  // lanes a row (a lane pair a block, eight blocks a step)
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ float lpart[WS_NT / 64][4];
 
