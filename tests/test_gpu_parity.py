@@ -394,6 +394,38 @@ def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K,S", [(70, 5120, 5), (300, 25600, 5), (21, 8192, 3)])
+def test_in_workgroup_split_unaligned_scales(mode, N, K, S):
+    """The in-workgroup split-K GEMV with the weight scales 2 bytes and the activation
+    scales 4 bytes past a 16-byte boundary (what the header allows): K is a multiple
+    of 256, so aligned inputs would be staged by LDS DMA; these fall back to the
+    copy through registers and give the oracle's bits, and the aligned call's."""
+    announce(f"gemv_q8_sk unaligned scales mode={mode} N={N} K={K} S={S}")
+    assert q.sk_combines_in_workgroup(mode, K, S)
+    wq, ws, x = _quant_case(N, K, 1, 31 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
+    nb = K // 32
+    wbuf = torch.empty(N * nb + 8, dtype=torch.int16, device=DEV)
+    wsd = wbuf[1:1 + N * nb].view(N, nb)
+    wsd.copy_(dev(ws))
+    assert wsd.data_ptr() % 16 == 2
+    xq, xl, xs = quantize_gpu(mode, x)
+    sbuf = torch.empty(nb + 4, dtype=torch.float32, device=DEV)
+    xs_off = sbuf[1:1 + nb].view(1, nb)
+    xs_off.copy_(xs.view(1, nb))
+    assert xs_off.data_ptr() % 16 == 4
+    wsp = q.sk_workspace(N, S)
+    wqd = dev(wq)
+    y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_sk(mode, wqd, wsd, y, xq, xl, xs_off, S, wsp)
+    np.testing.assert_array_equal(host(y), want)
+    y2 = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_sk(mode, wqd, dev(ws), y2, xq, xl, xs, S, wsp)  # aligned: the DMA staging
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 16), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
                                    (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4),
                                    (40, 25632, 7)])

@@ -274,3 +274,36 @@ def test_glu_matches_the_three_calls(mode, F, K, staging, monkeypatch):
     gh = host(h).reshape(1, F)
     check_f32(gh, oracle.swiglu(og, ou), "glu h")
     check_words(mode, gh, hq.view(1, F), None if hl is None else hl.view(1, F), hs.view(1, F // 32), "glu")
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_glu_unaligned_scales(mode):
+    """qdg_gemv_glu_q8 with the gate and up scales 2 bytes past a 16-byte boundary (K a
+    multiple of 256, so aligned scales would be staged by LDS DMA): the register-copy
+    staging gives the aligned call's bits."""
+    F, K = 96, 4096
+    announce(f"gemv_glu unaligned scales mode={mode} F={F} K={K}")
+    wg, sg = workloads.weights(F, K, 81, 82)
+    wu, su = workloads.weights(F, K, 83, 84)
+    x = workloads.batch_activation(1, K, 85, True, 86)
+    nb = K // 32
+
+    def offset_copy(s):
+        buf = torch.empty(F * nb + 8, dtype=torch.int16, device=DEV)
+        v = buf[1:1 + F * nb].view(F, nb)
+        v.copy_(dev(s.view(np.int16)))
+        assert v.data_ptr() % 16 == 2
+        return v
+
+    dwg, dwu = dev(wg), dev(wu)
+    xq, xl, xs = words(mode, 1, K)
+    q.quantize_act(mode, dev(x), xq, xl, xs)
+    outs = []
+    for sgd, sud in ((dev(sg.view(np.int16)), dev(su.view(np.int16))), (offset_copy(sg), offset_copy(su))):
+        h = torch.empty((F,), dtype=torch.float32, device=DEV)
+        hq, hl, hs = words(mode, 1, F)
+        q.gemv_glu_q8(mode, dwg, sgd, dwu, sud, xq, xl, xs, hq, hl, hs, h=h)
+        outs.append((host(h), host(hq), None if hl is None else host(hl), host(hs)))
+    for a, b in zip(*outs):
+        if a is not None:
+            assert a.tobytes() == b.tobytes()
