@@ -13,6 +13,7 @@ Functions (each mirrors one step of the method; citations in ``qdg_oracle.c``):
 * ``gemv_split(mode, wq, ws, xq, xl, xs, S)`` -> partials ``[S][B][N]``
 * ``combine(part)`` -> ``y``
 * ``argmax(y)`` -> first index of the maximum, per row
+* ``tile_rows(wq)`` -> the weight values in row tiles of four rows by 256 values
 * ``reference_f64(mode, ...)`` -> ``(Y, tnorm)`` binary64 anchor of the tolerance
 * ``rmsnorm(x, r=None, w=None, eps)`` -> ``(s, y)``: residual sum and RMSNorm
 * ``swiglu(g, u)`` -> ``h = silu(g) * u``
@@ -163,6 +164,25 @@ def argmax(y: np.ndarray) -> np.ndarray:
     idx = np.empty(B, np.int32)
     _check(_load().orc_argmax(_p(y), B, N, _p(idx)), "argmax")
     return idx
+
+
+def tile_rows(wq: np.ndarray) -> np.ndarray:
+    """The row-tiled weight layout: the values of four consecutive rows and 256
+    consecutive columns are stored together, tile after tile.
+
+    The megakernel page ("model-as-a-kernel mak_cuda/megakernel.cu", the GEMV's
+    tiled-weights option) stores bf16 weights as [N/8][K/8][8][8] so that the
+    eight warps of a block, on eight consecutive rows, read one contiguous
+    stream; only addresses change, each lane reads the same values in the same
+    order.  Here the tile is four rows by 256 values: byte
+    ((t*(K/256) + s)*4 + r)*256 + c holds row 4t + r, column 256s + c.  N must
+    be a multiple of 4 and K of 256.  The scales keep their plain layout.
+    """
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    N, K = wq.shape
+    if N % 4 or K % 256:
+        raise ValueError("tile_rows: N must be a multiple of 4 and K of 256")
+    return np.ascontiguousarray(wq.reshape(N // 4, 4, K // 256, 256).transpose(0, 2, 1, 3)).reshape(N, K)
 
 
 def reference_f64(mode, wq, ws, x=None, xq=None, xl=None, xs=None, nthreads: int = 1):
