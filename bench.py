@@ -51,7 +51,7 @@ def alg_bytes(mode: int, N: int, K: int, B: int = 1) -> int:
     return N * K + N * K // 16 + B * act + 4 * B * N
 
 
-def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
+def dominant_kernel(path: str, mode: int, sh, S: int, tiled: bool = False) -> tuple[str, int]:
     """The GEMV kernel a path launches for one projection, as the kernel trace names
     it, and its grid in threads."""
     import quantized_decode_gemv_02_amd as q
@@ -67,7 +67,8 @@ def dominant_kernel(path: str, mode: int, sh, S: int) -> tuple[str, int]:
         dma = sh.K % 256 == 0 and not os.environ.get("QDG_WS_DMA", "1").startswith("0")
         stage = 1 if (loc.startswith("1") if loc else rows == 4) else (2 if dma else 0)
         # template arguments: mode, row groups, steps a weight group (1), groups in flight (4), staging
-        return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}>", 64 * waves * -(-sh.N // rows)
+        tl = "true" if tiled else "false"
+        return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}, {tl}>", 64 * waves * -(-sh.N // rows)
     flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
     return f"k_gemv_dot4<{mode}, 4, 4, {flags}, false>", 256 * -(-sh.N // 16) * S
 
@@ -85,6 +86,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--path", choices=("single", "fused", "staged"), default="fused")
+    ap.add_argument("--weights", choices=("plain", "tiled"), default="plain",
+                    help="the step's weight layout: plain [N][K], or row tiles of four rows by 256 values "
+                         "(qdg_q8_tile_rows, done before timing; --path fused only)")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--no-sweep", action="store_true", help="skip the S in {1,2,4,8} sweep beside the step")
@@ -102,6 +106,9 @@ def main() -> int:
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by output "
               "rows across GPUs, but only the one-GPU path is implemented and timed)", file=sys.stderr)
+        return 2
+    if args.weights == "tiled" and args.path != "fused":
+        print("bench.py: --weights tiled needs --path fused (the in-workgroup split-K GEMV)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -126,6 +133,12 @@ def main() -> int:
     set_bytes = sum(w.numel() + 2 * s.numel() for w, s, _ in base)
     R = max(2, math.ceil(args.min_rotate_bytes / set_bytes))
     copies = [[(w.clone(), s.clone()) for (w, s, _) in base] for _ in range(R)]
+    if args.weights == "tiled":  # each copy also in row tiles (the other legs keep the plain weights)
+        for cs in copies:
+            for i, (w, s) in enumerate(cs):
+                wt = torch.empty_like(w)
+                q.q8_tile_rows(w, wt)
+                cs[i] = (w, s, wt)
     del base  # keep only the rotated copies (the x tensors live in `acts`)
     acts = [torch.from_numpy(d["x"]).to(dev) for d in host]
     torch.cuda.synchronize()
@@ -137,7 +150,12 @@ def main() -> int:
         sh = shapes[si]
         N, K = sh.N, sh.K
         bufs = buffers[(mode, si, S)]
-        w, s = copies[copy_idx][si]
+        w, s = copies[copy_idx][si][:2]
+        if path == "fused" and args.weights == "tiled":
+            calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
+            calls.append(q.bind_gemv_q8_sk_tiled(mode, copies[copy_idx][si][2], s, bufs["y"], bufs["xq"], bufs["xl"],
+                                                 bufs["xs"], S))
+            return calls
         if path == "single":
             return [q.bind_gemv_q8_fused(mode, w, s, bufs["y"], acts[si], S, bufs["fws"])]
         calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
@@ -302,7 +320,8 @@ def main() -> int:
     # HBM bytes per launch of the dominant kernel from the committed profiler counters, used
     # only if they were taken on the current kernel sources at the same launch shape
     traffic = None
-    dom_name, dom_grid = dominant_kernel(args.path, dom_key[0], shapes[dom_key[1]], chosen[dom_key])
+    dom_name, dom_grid = dominant_kernel(args.path, dom_key[0], shapes[dom_key[1]], chosen[dom_key],
+                                         args.weights == "tiled")
     tpath = os.path.join(ROOT, "profiles", "gemv_q8_narrow_projections_traffic.json")
     if os.path.exists(tpath):
         from quantized_decode_gemv_02_amd import profiling
@@ -520,7 +539,7 @@ def main() -> int:
         "data": "synthetic (seeded; int8 weights uniform [-127,127], fp16 scales U[1e-3,1e-2), N(0,1) activations with 1% x20 outliers)",
         "config": {"workload": "narrow projections with split-K: o-proj K=8192 N=5120 and down-proj K=25600 N=5120, "
                                "batch 1, Int8Act + TwoPass, quantize + GEMV + ascending combine",
-                   "path": args.path, **other_ms,
+                   "path": args.path, "weights": args.weights, **other_ms,
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
                    "read_ceiling": ceiling, "producers": producers, "formats": formats, "splits_sweep": splits_sweep,

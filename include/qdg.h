@@ -382,6 +382,32 @@ int qdg_block_dots(int mode, const int8_t *wq, int64_t N, int64_t K,
 int qdg_stream_read(const void *buf, int64_t bytes, uint32_t *sink, qdg_stream stream);
 
 /*
+ * Row-tiled weights (megakernel page, the GEMV's tiled-weights option: weight
+ * tiles of consecutive rows stored together, so the loads that one group of
+ * rows issues at once form one contiguous stream; only addresses change).  The
+ * tile here is four rows by 256 values, the bytes of one 64-lane request of the
+ * split-K GEMV: wt byte ((t*(K/256) + s)*4 + r)*256 + c holds wq row 4t + r,
+ * column 256s + c.  wq [N][K] and wt [N*K] are device arrays, 16-byte aligned,
+ * not overlapping (QDG_EINVAL if they do); N a positive multiple of 4, K a
+ * positive multiple of 256 (else QDG_ESHAPE).  The weight scales keep their
+ * plain [N][K/32] layout.  The caller owns both arrays.
+ */
+int qdg_q8_tile_rows(const int8_t *wq, int64_t N, int64_t K, int8_t *wt, qdg_stream stream);
+
+/*
+ * qdg_gemv_q8_sk's in-workgroup placement over row-tiled weights wt (from
+ * qdg_q8_tile_rows): the same terms in the same order, so y [1][N] is
+ * bit-identical to qdg_gemv_q8_sk over the plain weights with the same splits.
+ * QDG_INT8ACT or QDG_TWOPASS (xl as qdg_gemv_q8_sk); splits must be one that
+ * qdg_gemv_sk_combines_in_workgroup accepts for (mode, K), else QDG_EMODE; N a
+ * multiple of 4 and K of 256 (else QDG_ESHAPE).  Alignment as qdg_gemv_q8_sk
+ * (wt 16 bytes).  Needs no workspace.
+ */
+int qdg_gemv_q8_sk_tiled(int mode, const int8_t *wt, const uint16_t *ws, int64_t N, int64_t K,
+                         const int8_t *xq, const int8_t *xl, const float *xs, int splits, float *y,
+                         qdg_stream stream);
+
+/*
  * Host only: the split-K chunk boundaries in 32-value blocks (QWEN38 page,
  * gk_gemv_hl_sk): K runs in 512-value superblocks, per = ceil((K/512)/splits),
  * chunk s takes superblocks [s*per, min((s+1)*per, K/512)) and the last chunk

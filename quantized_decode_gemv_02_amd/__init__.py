@@ -10,6 +10,7 @@ functions carry the names of the C entry points in ``include/qdg.h`` without the
 * ``sk_combine(partials, y)``
 * ``gemv_q8_sk(mode, wq, ws, y, xq, xl, xs, splits, workspace)`` / ``gemv_sk_workspace_bytes(B, N, S)``
 * ``gemv_q8_fused(mode, wq, ws, y, x, splits, workspace)`` (quantize + GEMV + combine, one launch)
+* ``q8_tile_rows(wq, wt)`` / ``gemv_q8_sk_tiled(mode, wt, ws, y, xq, xl, xs, splits)`` (row-tiled weights)
 * ``argmax(y, idx, workspace)`` / ``argmax_workspace_bytes(B, N)``
 * ``gemv_q8_argmax(mode, wq, ws, y, idx, workspace, x=, xq=, xl=, xs=)`` / ``gemv_argmax_workspace(N)``
 * ``block_dots(mode, wq, xq, xl, dh, dl)``
@@ -63,6 +64,8 @@ _SIGS = {
     "qdg_gemv_sk_combines_in_workgroup": ([_I, _I64, _I, _P], _I),
     "qdg_gemv_q8_sk": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_gemv_q8_fused": ([_I, _P, _P, _I64, _I64, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
+    "qdg_q8_tile_rows": ([_P, _I64, _I64, _P, _P], _I),
+    "qdg_gemv_q8_sk_tiled": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I, _P, _P], _I),
     "qdg_gemv_argmax_workspace_bytes": ([_I64], ctypes.c_size_t),
     "qdg_gemv_q8_argmax": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
@@ -329,6 +332,22 @@ def gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> None
         _stream()))
 
 
+def q8_tile_rows(wq, wt) -> None:
+    """The weight values ``wq [N][K]`` in row tiles of four rows by 256 values, into ``wt`` (same shape)."""
+    N, K = wq.shape
+    if tuple(wt.shape) != (N, K):
+        raise ValueError("q8_tile_rows: wt must have the shape of wq")
+    _check("qdg_q8_tile_rows", _lib.qdg_q8_tile_rows(_ptr(wq, _i8(), "wq"), N, K, _ptr(wt, _i8(), "wt"), _stream()))
+
+
+def gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> None:
+    """``gemv_q8_sk``'s in-workgroup placement over row-tiled weights ``wt`` (from ``q8_tile_rows``)."""
+    N, K = wt.shape
+    _check("qdg_gemv_q8_sk_tiled", _lib.qdg_gemv_q8_sk_tiled(
+        mode, _ptr(wt, _i8(), "wt"), _ptr(ws, _scales(), "ws"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"),
+        _ptr(xs, _f32(), "xs"), int(splits), _ptr(y, _f32(), "y"), _stream()))
+
+
 def gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> None:
     """One launch for a batch-1 projection: quantize ``x [1][K]`` (f32), split-K GEMV and ascending
     combine into ``y [1][N]`` (``workspace`` from ``sk_workspace(N, splits)``; may be None when S == 1)."""
@@ -442,6 +461,13 @@ def bind_gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) ->
         _ptr(t, None, n)
     nbytes = workspace.numel() * workspace.element_size()
     return Bound("qdg_gemv_q8_sk", mode, wq, ws, N, K, xq, xl, xs, B, int(splits), y, workspace, nbytes, _stream())
+
+
+def bind_gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> Bound:
+    N, K = wt.shape
+    for t, n in ((wt, "wt"), (ws, "ws"), (y, "y"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    return Bound("qdg_gemv_q8_sk_tiled", mode, wt, ws, N, K, xq, xl, xs, int(splits), y, _stream())
 
 
 def bind_gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> Bound:

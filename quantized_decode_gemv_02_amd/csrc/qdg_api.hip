@@ -120,6 +120,30 @@ int qdg_gemv_q8_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, in
   return hip_status(qdg::launch_gemv_sk(mode, wq, ws, N, K, xq, xl, xs, splits, y, workspace, as_stream(stream)));
 }
 
+int qdg_q8_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, qdg_stream stream) {
+  if (!wq || !wt) return QDG_EINVAL;
+  if (N < 4 || N % 4 || K < 256 || K % 256 || N > ((int64_t)1 << 40) / K) return QDG_ESHAPE;
+  if (!aligned(wq, 16) || !aligned(wt, 16)) return QDG_EALIGN;
+  const uintptr_t a = (uintptr_t)wq, b = (uintptr_t)wt, n = (uintptr_t)(N * K);
+  if (a < b + n && b < a + n) return QDG_EINVAL;
+  return hip_status(qdg::launch_tile_rows(wq, N, K, wt, as_stream(stream)));
+}
+
+int qdg_gemv_q8_sk_tiled(int mode, const int8_t* wt, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                         const int8_t* xl, const float* xs, int splits, float* y, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return mode == QDG_DEQUANT ? QDG_EMODE : QDG_EINVAL;
+  if (!wt || !ws || !xq || !xs || !y) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!shape_ok(N, K) || N % 4 || K % 256 || N / 4 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (!qdg::wsplit_fits(mode, K, splits)) return QDG_EMODE;
+  if (!aligned(wt, 16) || !aligned(ws, 2) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) ||
+      !aligned(y, 4))
+    return QDG_EALIGN;
+  return hip_status(qdg::launch_gemv_wsplit(mode, wt, ws, N, K, xq, xl, xs, splits, y, as_stream(stream), true));
+}
+
 int qdg_gemv_sk_combines_in_workgroup(int mode, int64_t K, int splits, int32_t* shape) {
   if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
   if (K < qdg::QK || K % qdg::QK || splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;

@@ -200,13 +200,25 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
 // same number in flight and the compiler can count them: a lane whose block lies
 // at or past g1 reads block g1 - 1 again, and chunk_dot4 never adds its term.
 // The scheduling barriers keep the requests where they are written.
-template <int U>
+//
+// TL selects the row-tiled weight layout (tiles of four rows by 256 values,
+// tile after tile; the megakernel page's tiled-weights option with a tile that
+// is one wave instruction's bytes): block b of a row then sits at
+// (b/8)*1024 + (b%8)*32 from the row's first piece, wrow pointing at the row's
+// tile plus 256 * (row mod 4) + 16*hf, so a wave's 64 lanes read one
+// contiguous KiB.  The values and their order are those of the plain layout.
+template <bool TL>
+__device__ __forceinline__ int64_t block_offset(int b) {
+  return TL ? ((int64_t)(b >> 3) << 10) + ((b & 7) << 5) : (int64_t)b * QK;
+}
+
+template <int U, bool TL = false>
 __device__ __forceinline__ void group_load(int4 (&w)[U], const int8_t* wrow, int g0, int g1, int gi, int j) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int b = g0 + (gi * U + u) * 8 + j;
-    w[u] = ld16_stream(wrow + (int64_t)(b < g1 ? b : g1 - 1) * QK);
+    w[u] = ld16_stream(wrow + block_offset<TL>(b < g1 ? b : g1 - 1));
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -255,7 +267,7 @@ __device__ __forceinline__ void group_terms(const int4 (&w)[U], const int8_t* lq
 // LDS windows keeps one chain per partial across them; the window's arrays hold
 // block b at index b - lb); chunk_dot4 starts from +0 and ends with the
 // (P0 + P2) + (P1 + P3) reduction.
-template <int MODE, int U, int NB>
+template <int MODE, int U, int NB, bool TL = false>
 __device__ __forceinline__ void chunk_fold(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
                                            const uint16_t* my_sg, int g0, int g1, int j, int hf,
                                            int4 (&w)[NB][U], float& p, int lb = 0) {
@@ -267,14 +279,14 @@ __device__ __forceinline__ void chunk_fold(const int8_t* wrow, const int8_t* lq,
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p, lb);
-      group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
+      group_load<U, TL>(w[k], wrow, g0, g1, gi + NB + k, j);
     }
   }
   // the last 1 .. 2*NB - 1 groups, in order (a group past the chunk adds nothing)
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     group_terms<MODE, U>(w[k], lq, ll, lsx, my_sg, g0, nwb, j, hf, gi + k, p, lb);
-    if (gi + NB + k < ngroups) group_load<U>(w[k], wrow, g0, g1, gi + NB + k, j);
+    if (gi + NB + k < ngroups) group_load<U, TL>(w[k], wrow, g0, g1, gi + NB + k, j);
   }
 #pragma unroll
   for (int k = 0; k + 1 < NB; ++k)
@@ -287,12 +299,12 @@ __device__ __forceinline__ float row_sum4(float p) {
   return __fadd_rn(t, dpp_f32<DPP_ROW_SHL2>(t));
 }
 
-template <int MODE, int U, int NB>
+template <int MODE, int U, int NB, bool TL = false>
 __device__ __forceinline__ float chunk_dot4(const int8_t* wrow, const int8_t* lq, const int8_t* ll, const float* lsx,
                                             const uint16_t* my_sg, int g0, int g1, int j, int hf,
                                             int4 (&w)[NB][U]) {
   float p = 0.0f;
-  chunk_fold<MODE, U, NB>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w, p);
+  chunk_fold<MODE, U, NB, TL>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w, p);
   return row_sum4(p);
 }
 
@@ -368,12 +380,15 @@ hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, i
 hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
                                     float* const* y, int64_t K, const float* x, int splits, hipStream_t st);
 void wsplit_shape(int64_t K, int splits, int& rows, int& waves);
+// tiled: the weights in row tiles of four rows by 256 values (launch_tile_rows)
 hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                               const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
-                              hipStream_t st);
+                              hipStream_t st, bool tiled = false);
 hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* wq, const uint16_t* const* ws,
                                     const int64_t* N, float* const* y, int64_t K, const int8_t* xq,
-                                    const int8_t* xl, const float* xs, int splits, hipStream_t st);
+                                    const int8_t* xl, const float* xs, int splits, hipStream_t st,
+                                    bool tiled = false);
+hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);

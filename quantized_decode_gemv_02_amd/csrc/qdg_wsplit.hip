@@ -23,6 +23,11 @@
 // with the whole workgroup; WS_LOCAL has each wave copy only its own chunk and
 // start without a workgroup barrier (waves of different row groups that share a
 // chunk write the same bytes).
+//
+// TL: the weight values in row tiles of four rows by 256 values (tile_rows
+// below).  A row group's four rows are one tile row, so each weight request of
+// a wave reads one contiguous KiB and a chunk wave streams one contiguous range;
+// the terms, their order and the result are those of the plain layout.
 #include <stdlib.h>
 
 #include "qdg_device.h"
@@ -38,7 +43,7 @@ constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with 
 template <int MODE, int ROWS>
 constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
 
-template <int MODE, int R, int U, int NB, int STAGE>
+template <int MODE, int R, int U, int NB, int STAGE, bool TL>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
 __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
     const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
@@ -66,7 +71,8 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   const int rr = rg * 4 + r;
   const int64_t o = o_wg + rr;
   const bool row_ok = o < N;
-  const int8_t* wrow = wq + (row_ok ? o : N - 1) * K + hf * 16;
+  const int64_t ro = row_ok ? o : N - 1;  // with tiled weights N is a multiple of 4: ro's tile is whole
+  const int8_t* wrow = TL ? wq + (ro >> 2) * 4 * K + (ro & 3) * 256 + hf * 16 : wq + ro * K + hf * 16;
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
   const int nwb = g1 - g0;
@@ -80,10 +86,10 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   // the wave's first step groups of weights are requested before the staging
   // (all NB where the staging needs no registers, else the first)
   int4 w[NB][U];
-  group_load<U>(w[0], wrow, g0, g1, 0, j);
+  group_load<U, TL>(w[0], wrow, g0, g1, 0, j);
   if constexpr (STAGE == WS_DMA) {
 #pragma unroll
-    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, g0, g1, k, j);
+    for (int k = 1; k < NB; ++k) group_load<U, TL>(w[k], wrow, g0, g1, k, j);
     // whole 1 KiB pieces a wave instruction; the byte counts are multiples of 16
     // (K and nb are multiples of 256 and 8), so a lane's 16 bytes are all in range
     const int nwv = (int)(blockDim.x >> 6);
@@ -128,11 +134,11 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   }
   if constexpr (STAGE != WS_DMA) {
 #pragma unroll
-    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, g0, g1, k, j);
+    for (int k = 1; k < NB; ++k) group_load<U, TL>(w[k], wrow, g0, g1, k, j);
   }
 
   // the chunk's partial of the row, in lane 0 of the row
-  const float yv = chunk_dot4<MODE, U, NB>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w);
+  const float yv = chunk_dot4<MODE, U, NB, TL>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w);
   if (li == 0) lpart[wave][r] = yv;
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
@@ -159,17 +165,17 @@ void ws_chunks(int64_t K, int S, int& m, int& ceff) {
 template <int MODE, int R>
 size_t ws_lds_bytes(int64_t K) { return (size_t)(K / QK) * ws_bytes_per_block<MODE, 4 * R>(); }
 
-template <int MODE, int R, int STAGE>
+template <int MODE, int R, int STAGE, bool TL>
 hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
                      hipStream_t st) {
   int m, ceff;
   ws_chunks(K, S, m, ceff);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
   const size_t lds = ws_lds_bytes<MODE, R>(K);
-  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
+  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
   return hipGetLastError();
 }
 
@@ -208,24 +214,38 @@ int ws_groups(int ceff) {
   return R;
 }
 
-template <int MODE, int R>
+template <int MODE, int R, bool TL>
 hipError_t launch_ws_staged(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
                             int S, hipStream_t st) {
   switch (ws_stage(R, tab, K, MODE, xq, xl, xs)) {
-    case WS_DMA: return launch_ws<MODE, R, WS_DMA>(tab, K, xq, xl, xs, S, st);
-    case WS_LOCAL: return launch_ws<MODE, R, WS_LOCAL>(tab, K, xq, xl, xs, S, st);
-    default: return launch_ws<MODE, R, WS_BARRIER>(tab, K, xq, xl, xs, S, st);
+    case WS_DMA: return launch_ws<MODE, R, WS_DMA, TL>(tab, K, xq, xl, xs, S, st);
+    case WS_LOCAL: return launch_ws<MODE, R, WS_LOCAL, TL>(tab, K, xq, xl, xs, S, st);
+    default: return launch_ws<MODE, R, WS_BARRIER, TL>(tab, K, xq, xl, xs, S, st);
   }
 }
 
-template <int MODE>
+template <int MODE, bool TL>
 hipError_t launch_ws_mode(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
                           int R, hipStream_t st) {
   switch (R) {
-    case 1: return launch_ws_staged<MODE, 1>(tab, K, xq, xl, xs, S, st);
-    case 2: return launch_ws_staged<MODE, 2>(tab, K, xq, xl, xs, S, st);
-    case 3: return launch_ws_staged<MODE, 3>(tab, K, xq, xl, xs, S, st);
-    default: return launch_ws_staged<MODE, 4>(tab, K, xq, xl, xs, S, st);
+    case 1: return launch_ws_staged<MODE, 1, TL>(tab, K, xq, xl, xs, S, st);
+    case 2: return launch_ws_staged<MODE, 2, TL>(tab, K, xq, xl, xs, S, st);
+    case 3: return launch_ws_staged<MODE, 3, TL>(tab, K, xq, xl, xs, S, st);
+    default: return launch_ws_staged<MODE, 4, TL>(tab, K, xq, xl, xs, S, st);
+  }
+}
+
+// Row tiles: thread i moves the i-th 16 bytes of the tiled array, byte
+// ((t*(K/256) + s)*4 + r)*256 + c <- row 4t + r, column 256s + c (c a multiple
+// of 16).  Both sides are read and written in 256-byte runs.
+__global__ __launch_bounds__(256) void k_tile_rows(const int8_t* __restrict__ wq, int64_t K, int64_t n16,
+                                                   int8_t* __restrict__ wt) {
+  const int64_t steps = K >> 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = (i & 15) << 4, q = i >> 4;
+    const int64_t r = q & 3, q2 = q >> 2;
+    const int64_t sidx = q2 % steps, t = q2 / steps;
+    *(v4i*)(wt + (i << 4)) = *(const v4i*)(wq + (4 * t + r) * K + (sidx << 8) + c);
   }
 }
 
@@ -253,20 +273,32 @@ void wsplit_shape(int64_t K, int splits, int& rows, int& waves) {
 
 hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* wq, const uint16_t* const* ws,
                                     const int64_t* N, float* const* y, int64_t K, const int8_t* xq,
-                                    const int8_t* xl, const float* xs, int splits, hipStream_t st) {
+                                    const int8_t* xl, const float* xs, int splits, hipStream_t st, bool tiled) {
   int m, ceff;
   ws_chunks(K, splits, m, ceff);
   const int R = ws_groups(ceff);
   PartTable tab;
   if (!make_parts(tab, nparts, wq, ws, y, N, 4 * R)) return hipErrorInvalidValue;
-  if (mode == 1) return launch_ws_mode<1>(tab, K, xq, xl, xs, splits, R, st);
-  return launch_ws_mode<2>(tab, K, xq, xl, xs, splits, R, st);
+  if (tiled) {
+    if (mode == 1) return launch_ws_mode<1, true>(tab, K, xq, xl, xs, splits, R, st);
+    return launch_ws_mode<2, true>(tab, K, xq, xl, xs, splits, R, st);
+  }
+  if (mode == 1) return launch_ws_mode<1, false>(tab, K, xq, xl, xs, splits, R, st);
+  return launch_ws_mode<2, false>(tab, K, xq, xl, xs, splits, R, st);
 }
 
 hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
                               const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
-                              hipStream_t st) {
-  return launch_gemv_wsplit_parts(mode, 1, &wq, &ws, &N, &y, K, xq, xl, xs, splits, st);
+                              hipStream_t st, bool tiled) {
+  return launch_gemv_wsplit_parts(mode, 1, &wq, &ws, &N, &y, K, xq, xl, xs, splits, st, tiled);
+}
+
+hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, hipStream_t st) {
+  const int64_t n16 = N * K / 16;
+  const int64_t blocks = (n16 + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(k_tile_rows, dim3(grid), dim3(256), 0, st, wq, K, n16, wt);
+  return hipGetLastError();
 }
 
 }  // namespace qdg

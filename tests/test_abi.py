@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -353,3 +353,32 @@ def test_one_hip_runtime_in_the_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.split()[0] == "1", r.stdout
+
+
+def test_tiled_layout_validation():
+    tile = lib.qdg_q8_tile_rows
+    assert tile(None, 8, 512, P(A), None) == EINVAL
+    assert tile(P(A), 8, 512, None, None) == EINVAL
+    assert tile(P(A), 6, 512, P(A + 8192), None) == ESHAPE  # N not a multiple of 4
+    assert tile(P(A), 8, 288, P(A + 8192), None) == ESHAPE  # K not a multiple of 256
+    assert tile(P(A), 0, 512, P(A + 8192), None) == ESHAPE
+    assert tile(P(A + 8), 8, 512, P(A + 8192), None) == EALIGN
+    assert tile(P(A), 8, 512, P(A + 4080), None) == EINVAL  # overlaps wq's 4096 bytes
+    assert tile(P(A + 4080), 8, 512, P(A), None) == EINVAL
+
+    def sk(mode=1, wt=A, N=64, K=5120, xl=None, S=5, xs=A, y=A):
+        return lib.qdg_gemv_q8_sk_tiled(mode, P(wt), P(A), N, K, P(A), P(xl), P(xs), S, P(y), None)
+
+    assert sk(mode=0) == EMODE
+    assert sk(mode=3) == EINVAL
+    assert sk(wt=None) == EINVAL
+    assert sk(mode=2) == EINVAL            # TwoPass without xl
+    assert sk(mode=1, xl=A) == EINVAL      # Int8Act with xl
+    assert sk(N=66) == ESHAPE
+    assert sk(K=5120 + 32) == ESHAPE
+    assert sk(S=1) == EMODE                # not an in-workgroup split
+    assert sk(S=17) == EMODE               # more than 16 chunk waves
+    assert sk(S=0) == ESHAPE
+    assert sk(mode=2, xl=A, K=32768, S=5) == EMODE  # the staged row exceeds the LDS budget
+    assert sk(wt=A + 4) == EALIGN
+    assert sk(xs=A + 2) == EALIGN

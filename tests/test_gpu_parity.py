@@ -425,6 +425,50 @@ def test_in_workgroup_split_unaligned_scales(mode, N, K, S):
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
 
 
+@pytest.mark.parametrize("N,K", [(4, 256), (8, 512), (20, 2304), (516, 5120), (5120, 25600)])
+def test_tile_rows_bit_exact(N, K):
+    """Row tiles of four rows by 256 values: every byte where the oracle's layout puts it."""
+    announce(f"q8_tile_rows N={N} K={K}")
+    wq = np.random.default_rng(N + K).integers(-128, 128, size=(N, K), dtype=np.int8)
+    wt = torch.empty((N, K), dtype=torch.int8, device=DEV)
+    q.q8_tile_rows(dev(wq), wt)
+    np.testing.assert_array_equal(host(wt), oracle.tile_rows(wq))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("N,K,S", [(5120, 25600, 5), (5120, 8192, 5), (5120, 25600, 16), (640, 25600, 10),
+                                   (40, 25600, 5), (100, 8192, 4), (4, 1024, 2), (12, 768, 3), (36, 1280, 5),
+                                   (24, 27904, 5), (8, 33792, 16), (64, 4608, 2)])
+@pytest.mark.parametrize("variant", ["dma", "barrier", "wave-local"])
+def test_in_workgroup_split_tiled_bit_exact(mode, N, K, S, variant, monkeypatch):
+    """The in-workgroup split-K GEMV over row-tiled weights: the oracle's chunk
+    partials and ascending combine bit for bit, and the plain-layout call's bits,
+    with each staging of the activation (the weight addressing is the same in all)."""
+    announce(f"gemv_q8_sk_tiled mode={mode} N={N} K={K} S={S} {variant}")
+    if variant == "dma":
+        monkeypatch.delenv("QDG_WS_DMA", raising=False)
+        monkeypatch.setenv("QDG_WS_LOCAL", "0")
+    else:
+        monkeypatch.setenv("QDG_WS_DMA", "0")
+        monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
+    assert q.sk_combines_in_workgroup(mode, K, S)
+    wq, ws, x = _quant_case(N, K, 1, 23 * N + K + S, outliers=True)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    rows = np.arange(0, N, 7) if N > 1000 else np.arange(N)
+    want = oracle.combine(oracle.gemv_split(mode, wq[rows], ws[rows], oq, ol, os_, S, nthreads=8))
+    wqd, wsd = dev(wq), dev(ws)
+    wt = torch.empty_like(wqd)
+    q.q8_tile_rows(wqd, wt)
+    xq, xl, xs = quantize_gpu(mode, x)
+    for rep in range(2):
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_sk_tiled(mode, wt, wsd, y, xq, xl, xs, S)
+        np.testing.assert_array_equal(host(y)[:, rows], want)
+    y2 = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_sk(mode, wqd, wsd, y2, xq, xl, xs, S, q.sk_workspace(N, S))
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+
+
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 16), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
                                    (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4),
