@@ -9,26 +9,31 @@ qdg_gemv_q8_sk: the split-K GEMV whose chunks are the waves of one workgroup and
 meet in LDS for the ascending combine); --path staged makes the three calls of
 the pages' own structure (qdg_quantize_act, qdg_gemv_q8 with S chunks,
 qdg_sk_combine) and --path single one (qdg_gemv_q8_fused, the quantizer in every
-workgroup).  All three give the same bits.  Each run reports the other paths'
-step times beside its own, and times Dequant (qdg_gemv_q8_fused with the
-same S) on the same projections.  Inputs are seeded synthetic tensors resident in HBM before
-timing; the weights rotate over enough copies (>= 1 GiB between reuses of a
-copy) that the 256 MB Infinity Cache cannot serve them.
+workgroup).  All three give the same bits.  Inputs are seeded synthetic tensors
+resident in HBM before timing; the weights rotate over enough copies (>= 1 GiB
+between reuses of a copy) that the 256 MB Infinity Cache cannot serve them.
+
+Timing.  The step (``value``) is timed over K whole steps with nothing else in
+the stream.  Every kernel figure is a device duration: the library binds a pair
+of HIP events to the measured kernel's own dispatch (qdg_time_next_launch,
+hipExtLaunchKernel), so the events add no stream work and give the time a
+kernel trace reports; each figure is the median over the measured launches
+(>= 50 after >= 5 warm-up launches, rotated weight copies).
 
 Prints ONE JSON line:
-  value      = algorithmic GEMV bytes of a step / step time (GB/s), timed over K
-               steps with no events in the stream; algorithmic
+  value      = algorithmic GEMV bytes of a step / step time (GB/s); algorithmic
                bytes per GEMV = N*K weight bytes + N*K/16 scale bytes + the
-               activation in the mode's encoding (K + K/8 Int8Act, 2K + K/8
-               TwoPass) + 4N output bytes (split-K partial traffic not counted);
+               activation in the mode's encoding (4K Dequant, K + K/8 Int8Act,
+               2K + K/8 TwoPass) + 4N output bytes (split-K partials not counted);
   roofline   = the down-proj TwoPass GEMV (the step's dominant kernel): its
-               algorithmic bytes / its mean launch duration from HIP events
-               around each of its launches in a second timed pass of the same K
-               steps (events around every GEMV), against 8 TB/s;
-  config.modes = per mode and projection: S, the GEMV's mean launch time (the
-               same second pass), GB/s, and its share of the read ceiling;
-  config.read_ceiling = qdg_stream_read over each projection's bytes and 1 GiB:
-               the practical ceiling of a launch that only reads;
+               algorithmic bytes / its median device duration over the K steps of
+               a second pass of the same step with the events bound, against 8 TB/s;
+  config.modes   = per mode and projection of the step: S, device µs, GB/s, % of
+               peak and of the read ceiling (Dequant: qdg_gemv_q8_fused beside it);
+  config.configs = every workload configuration (tiny, 8B projections, narrow
+               projections with S in {1,2,4,8}, LM head + arg-max, 16-row batch)
+               in its modes: device µs, GB/s, % of peak, and end-to-end times;
+  config.read_ceiling = qdg_stream_read over each projection's bytes and 1 GiB;
   cpu_baseline = the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
@@ -37,6 +42,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -44,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0  # MI355X HBM3E
+NAMES = {0: "dequant", 1: "int8act", 2: "twopass"}
 
 
 def alg_bytes(mode: int, N: int, K: int, B: int = 1) -> int:
@@ -51,22 +58,22 @@ def alg_bytes(mode: int, N: int, K: int, B: int = 1) -> int:
     return N * K + N * K // 16 + B * act + 4 * B * N
 
 
+def rate(nbytes: int, us: float) -> dict:
+    gbs = nbytes / us / 1e3
+    return {"us": round(us, 3), "GBs": round(gbs, 1), "pct_of_peak": round(100 * gbs / PEAK_GBS, 2)}
+
+
 def dominant_kernel(path: str, mode: int, sh, S: int, tiled: bool = False) -> tuple[str, int]:
     """The GEMV kernel a path launches for one projection, as the kernel trace names
-    it, and its grid in threads."""
+    it, and its grid in threads (the library's defaults: no tuning knob set)."""
     import quantized_decode_gemv_02_amd as q
     shape = q.sk_workgroup_shape(mode, sh.K, S) if path == "fused" else None
-    if os.environ.get("QDG_SK_WSPLIT", "1").startswith("0"):  # the library's override of the placement
-        shape = None
     if shape is not None:
         rows, waves = shape
-        # the library's staging rule (its STAGE template argument): per-wave copies (1) for one
+        # the staging rule of the library (its STAGE template argument): per-wave copies (1) for one
         # row group, else LDS DMA (2) when K is a multiple of 256 (torch's buffers are 256-byte
-        # aligned), else the workgroup copy (0); QDG_WS_LOCAL / QDG_WS_DMA override as in the library
-        loc = os.environ.get("QDG_WS_LOCAL")
-        dma = sh.K % 256 == 0 and not os.environ.get("QDG_WS_DMA", "1").startswith("0")
-        stage = 1 if (loc.startswith("1") if loc else rows == 4) else (2 if dma else 0)
-        # template arguments: mode, row groups, steps a weight group (1), groups in flight (4), staging
+        # aligned), else the workgroup copy (0)
+        stage = 1 if rows == 4 else (2 if sh.K % 256 == 0 else 0)
         tl = "true" if tiled else "false"
         return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}, {tl}>", 64 * waves * -(-sh.N // rows)
     flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
@@ -79,19 +86,24 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--splits", default=None,
-                    help="split-K chunks: 'auto' (timed choice), one S for both projections, or 'S_o,S_down'; "
-                         "default per path: 5,5 for the in-workgroup combine (fused), 4,16 otherwise")
+                    help="split-K chunks: one S for both projections, or 'S_o,S_down'; default per path: 5,5 "
+                         "for the in-workgroup combine (fused), 4,16 otherwise")
     ap.add_argument("--modes", default="1,2")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-baseline sample")
+    ap.add_argument("--launches", type=int, default=60, help="timed launches per kernel figure (after 5 warm-up)")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="length of one timed CPU-baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotate-bytes", type=float, default=1.1 * 2 ** 30)
     ap.add_argument("--path", choices=("single", "fused", "staged"), default="fused")
     ap.add_argument("--weights", choices=("plain", "tiled"), default="plain",
                     help="the step's weight layout: plain [N][K], or row tiles of four rows by 256 values "
                          "(qdg_q8_tile_rows, done before timing; --path fused only)")
+    ap.add_argument("--no-other-paths", action="store_true", help="skip the other paths' step times")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload configurations (tiny, 8B, LM head, batch 16, the S sweep)")
+    ap.add_argument("--only-configs", default=None,
+                    help="comma list among tiny,8b,narrow,lm_head,batched: time only these beside the step")
     ap.add_argument("--no-dequant", action="store_true", help="skip the Dequant timing beside the step")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the S in {1,2,4,8} sweep beside the step")
     ap.add_argument("--no-formats", action="store_true",
                     help="skip the timing of the other GGUF block formats beside the step")
     ap.add_argument("--no-producers", action="store_true",
@@ -99,6 +111,58 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain device copy of 256 MiB (for scaling profiler byte counters)")
     return ap.parse_args()
+
+
+class DeviceTimer:
+    """Device durations of library kernels: a pool of HIP event pairs, each bound to one
+    launch's own dispatch by qdg_time_next_launch (the first kernel the call launches)."""
+
+    def __init__(self, torch, q, n: int):
+        self.torch, self.q = torch, q
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+        for a, b in self.pairs:  # torch creates the HIP events at their first record
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+
+    def bind(self, i: int) -> None:
+        self.q.time_next_launch(*self.pairs[i])
+
+    def ms(self, i: int) -> float:
+        a, b = self.pairs[i]
+        return a.elapsed_time(b)
+
+    def median_us(self, calls, launches: int, warm: int = 5) -> float:
+        """Median device duration (µs) of the first kernel of ``calls[i % len(calls)]()`` over
+        ``launches`` launches after ``warm`` untimed ones."""
+        for i in range(warm):
+            calls[i % len(calls)]()
+        self.torch.cuda.synchronize()
+        n = min(launches, len(self.pairs))
+        for i in range(n):
+            self.bind(i)
+            calls[i % len(calls)]()
+        self.torch.cuda.synchronize()
+        return statistics.median(self.ms(i) for i in range(n)) * 1e3
+
+    def wall_us(self, calls, launches: int, warm: int = 5) -> float:
+        """Mean time a call takes in a back-to-back sequence: one event pair around ``launches``
+        calls (every kernel of the call, and the gaps between launches, counted)."""
+        for i in range(warm):
+            calls[i % len(calls)]()
+        e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        self.torch.cuda.synchronize()
+        e0.record()
+        for i in range(launches):
+            calls[i % len(calls)]()
+        e1.record()
+        self.torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / launches
+
+
+def rotation(nbytes: int, min_bytes: float) -> int:
+    return max(2, math.ceil(min_bytes / nbytes))
 
 
 def main() -> int:
@@ -120,6 +184,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     modes = [int(m) for m in args.modes.split(",")]
     shapes = workloads.CONFIGS[2]
+    timer = DeviceTimer(torch, q, max(args.steps * len(modes) * len(shapes), args.launches, 64))
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # ---- inputs (seeded, uploaded once), rotated copies of the weights
     t0 = time.time()
@@ -128,45 +196,21 @@ def main() -> int:
     for si, sh in enumerate(shapes):
         d = workloads.make(2, si)
         host.append(d)
-        base.append((torch.from_numpy(d["wq"]).to(dev), torch.from_numpy(d["ws"].view(np.int16)).to(dev),
-                     torch.from_numpy(d["x"]).to(dev)))
-    set_bytes = sum(w.numel() + 2 * s.numel() for w, s, _ in base)
-    R = max(2, math.ceil(args.min_rotate_bytes / set_bytes))
-    copies = [[(w.clone(), s.clone()) for (w, s, _) in base] for _ in range(R)]
+        base.append((torch.from_numpy(d["wq"]).to(dev), torch.from_numpy(d["ws"].view(np.int16)).to(dev)))
+    set_bytes = sum(w.numel() + 2 * s.numel() for w, s in base)
+    R = rotation(set_bytes, args.min_rotate_bytes)
+    copies = [[(w.clone(), s.clone()) for (w, s) in base] for _ in range(R)]
     if args.weights == "tiled":  # each copy also in row tiles (the other legs keep the plain weights)
         for cs in copies:
             for i, (w, s) in enumerate(cs):
                 wt = torch.empty_like(w)
                 q.q8_tile_rows(w, wt)
                 cs[i] = (w, s, wt)
-    del base  # keep only the rotated copies (the x tensors live in `acts`)
+    del base
     acts = [torch.from_numpy(d["x"]).to(dev) for d in host]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
-
-    # ---- per (mode, shape) buffers and pre-bound launches
-    def make_calls(mode, si, S, copy_idx, path="staged"):
-        # the GEMV is always the last call but one (staged) or the last call
-        sh = shapes[si]
-        N, K = sh.N, sh.K
-        bufs = buffers[(mode, si, S)]
-        w, s = copies[copy_idx][si][:2]
-        if path == "fused" and args.weights == "tiled":
-            calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
-            calls.append(q.bind_gemv_q8_sk_tiled(mode, copies[copy_idx][si][2], s, bufs["y"], bufs["xq"], bufs["xl"],
-                                                 bufs["xs"], S))
-            return calls
-        if path == "single":
-            return [q.bind_gemv_q8_fused(mode, w, s, bufs["y"], acts[si], S, bufs["fws"])]
-        calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
-        if path == "fused":
-            calls.append(q.bind_gemv_q8_sk(mode, w, s, bufs["y"], bufs["xq"], bufs["xl"], bufs["xs"], S, bufs["fws"]))
-            return calls
-        out = bufs["y"] if S == 1 else bufs["part"]
-        calls.append(q.bind_gemv_q8(mode, w, s, out, xq=bufs["xq"], xl=bufs["xl"], xs=bufs["xs"], splits=S))
-        if S > 1:
-            calls.append(q.bind_sk_combine(bufs["part"], bufs["y"]))
-        return calls
+    progress(f"narrow projections uploaded ({R} copies, {setup_s:.1f} s)")
 
     buffers = {}
 
@@ -183,56 +227,45 @@ def main() -> int:
             "fws": q.sk_workspace(sh.N, S),
         }
 
-    # ---- S per (mode, shape): fixed (default 4 for the o-proj, 8 for the down-proj), or timed
-    # Measured best: the in-workgroup combine at S = 5 on both projections (5120x25600: five
-    # chunks of 5120 values, three row groups, one round of 427 workgroups of 15 waves;
-    # 5120x8192: four non-empty chunks, 427 workgroups of 12 waves); the workspace paths at 4
-    # and 16.  Back-to-back launches of the o-proj alone favour S = 3 by 2-4%, but whole steps
-    # at S = 3 on the o-proj ran 1-2% slower than at S = 5.
+    def make_calls(mode, si, S, copy_idx, path):
+        """The calls of one projection; the GEMV is the last call but one (staged) or the last."""
+        bufs = buffers[(mode, si, S)]
+        w, s = copies[copy_idx][si][:2]
+        if path == "fused" and args.weights == "tiled":
+            return [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"]),
+                    q.bind_gemv_q8_sk_tiled(mode, copies[copy_idx][si][2], s, bufs["y"], bufs["xq"], bufs["xl"],
+                                            bufs["xs"], S)]
+        if path == "single":
+            return [q.bind_gemv_q8_fused(mode, w, s, bufs["y"], acts[si], S, bufs["fws"])]
+        calls = [q.bind_quantize_act(mode, acts[si], bufs["xq"], bufs["xl"], bufs["xs"])]
+        if path == "fused":
+            calls.append(q.bind_gemv_q8_sk(mode, w, s, bufs["y"], bufs["xq"], bufs["xl"], bufs["xs"], S, bufs["fws"]))
+            return calls
+        out = bufs["y"] if S == 1 else bufs["part"]
+        calls.append(q.bind_gemv_q8(mode, w, s, out, xq=bufs["xq"], xl=bufs["xl"], xs=bufs["xs"], splits=S))
+        if S > 1:
+            calls.append(q.bind_sk_combine(bufs["part"], bufs["y"]))
+        return calls
+
+    # S per (mode, shape).  Measured best: the in-workgroup combine at S = 5 on both projections
+    # (5120x25600: five chunks of 5120 values, three row groups, one round of 427 workgroups of 15
+    # waves; 5120x8192: four non-empty chunks, 427 workgroups of 12 waves); the workspace paths at
+    # 4 and 16.
     default_splits = {"fused": "5,5", "staged": "4,16", "single": "4,16"}
 
     def splits_for(path):
-        spec = args.splits or default_splits[path]
-        if spec == "auto":
-            return None
-        v = [int(t) for t in spec.split(",")]
+        v = [int(t) for t in (args.splits or default_splits[path]).split(",")]
         return {(mode, si): v[min(si, len(v) - 1)] for mode in modes for si in range(len(shapes))}
 
-    chosen = {}
-    fixed = splits_for(args.path)
-    for mode in modes:
-        for si in range(len(shapes)):
-            if fixed is not None:
-                chosen[(mode, si)] = fixed[(mode, si)]
-                ensure_buffers(mode, si, chosen[(mode, si)])
-                continue
-            best = None
-            for S in (1, 2, 3, 4, 5, 6, 8, 10, 12, 13, 16):
-                ensure_buffers(mode, si, S)
-                seqs = [make_calls(mode, si, S, c, args.path) for c in range(R)]
-                for c in seqs:
-                    for f in c:
-                        f()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 8 * R
-                skip = 0 if args.path == "single" else 1  # the quantizer does not depend on S
-                e0.record()
-                for i in range(reps):
-                    for f in seqs[i % R][skip:]:
-                        f()
-                e1.record()
-                torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / reps
-                if best is None or ms < best[1]:
-                    best = (S, ms)
-            chosen[(mode, si)] = best[0]
+    chosen = splits_for(args.path)
+    for key, S in chosen.items():
+        ensure_buffers(key[0], key[1], S)
 
-    # ---- the step: every (mode, shape) once, each mode on its own weight copy
     dom_key = (2 if 2 in modes else modes[-1], len(shapes) - 1)
+    keys = [(mode, si) for mode in modes for si in range(len(shapes))]
 
     def build_steps(path):
-        ch = chosen if path == args.path else (splits_for(path) or chosen)
+        ch = chosen if path == args.path else splits_for(path)
         for key, S in ch.items():
             ensure_buffers(key[0], key[1], S)
         steps = []
@@ -246,28 +279,16 @@ def main() -> int:
         return steps
 
     steps_calls = build_steps(args.path)
-
     step_bytes = sum(alg_bytes(m, shapes[si].N, shapes[si].K) for m in modes for si in range(len(shapes)))
     dom_bytes = alg_bytes(dom_key[0], shapes[dom_key[1]].N, shapes[dom_key[1]].K)
 
-    keys = [(mode, si) for mode in modes for si in range(len(shapes))]
+    def run_step(i, steps=None):
+        for _, calls in (steps or steps_calls)[i % R]:
+            for f in calls:
+                f()
 
-    def run_step(i, events=None, steps=None):
-        # events: {key: list of (start, end)} -- one pair around every GEMV launch of the step
-        for key, calls in (steps or steps_calls)[i % R]:
-            if events is not None and key in events:
-                g = 0 if len(calls) == 1 else 1  # the GEMV's position (single: the only call)
-                for f in calls[:g]:
-                    f()
-                ev0, ev1 = events[key][i]
-                ev0.record()
-                calls[g]()
-                ev1.record()
-                for f in calls[g + 1:]:
-                    f()
-            else:
-                for f in calls:
-                    f()
+    def gemv_position(calls):
+        return 0 if len(calls) == 1 else 1  # single: the only call; else after the quantizer
 
     for i in range(args.warmup):
         run_step(i)
@@ -279,43 +300,54 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # Timed region 1 (value): K steps with no events.  HIP events between the kernels of a
-    # step add stream work of their own (about 7 us a step here), so the step is timed bare.
+    # Timed region (value): K whole steps, nothing else in the stream.
     K = args.steps
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
         run_step(i)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / K
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    progress(f"step: {ms_per_step * 1e3:.2f} us, {value:.0f} GB/s")
 
-    # Timed region 2 (roofline and the per-mode table): the same K steps again, with a HIP event
-    # pair around every GEMV launch; the dominant kernel's mean launch time comes from here.
-    ev_all = {key: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for _ in range(K)] for key in keys}
-    for i in range(K):
-        run_step(i, ev_all)
+    # Second pass of the same K steps with the events bound to each GEMV's and each quantizer's
+    # own dispatch (no stream work added): the device duration of every launch of the step.
+    quant_ms = {key: [] for key in keys}
     torch.cuda.synchronize()
-    gemv_ms = {key: sum(a.elapsed_time(b) for a, b in ev_all[key]) / K for key in keys}
-    dom_ms = gemv_ms[dom_key]
+    t_h = time.perf_counter()
+    for i in range(K):
+        for ki, (key, calls) in enumerate(steps_calls[i % R]):
+            g = gemv_position(calls)
+            for ci, f in enumerate(calls):
+                if ci == g:
+                    timer.bind(i * len(keys) + ki)
+                f()
+    torch.cuda.synchronize()
+    hook_pass_ms = (time.perf_counter() - t_h) * 1e3 / K
+    gemv_ms = {key: [timer.ms(i * len(keys) + ki) for i in range(K)] for ki, key in enumerate(keys)}
+    if args.path != "single":  # the quantizer launches on their own (the same calls as in the step)
+        for key in keys:
+            qcalls = [seq[keys.index(key)][1][0] for seq in steps_calls]
+            quant_ms[key] = timer.median_us(qcalls, args.launches) / 1e3
+    dom_us = statistics.median(gemv_ms[dom_key]) * 1e3
+    achieved = dom_bytes / dom_us / 1e3
 
     # the other paths' step times, for reference (same steps, same rotation)
     other_ms = {}
-    for other in ("single", "fused", "staged"):
-        if other == args.path:
-            continue
-        other_steps = build_steps(other)
-        for i in range(args.warmup):
-            run_step(i, steps=other_steps)
-        torch.cuda.synchronize()
-        t_o = time.perf_counter()
-        for i in range(K):
-            run_step(i, steps=other_steps)
-        torch.cuda.synchronize()
-        other_ms[f"{other}_ms_per_step"] = round((time.perf_counter() - t_o) * 1e3 / K, 5)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    if not args.no_other_paths:
+        for other in ("single", "fused", "staged"):
+            if other == args.path:
+                continue
+            other_steps = build_steps(other)
+            for i in range(args.warmup):
+                run_step(i, other_steps)
+            torch.cuda.synchronize()
+            t_o = time.perf_counter()
+            for i in range(K):
+                run_step(i, other_steps)
+            torch.cuda.synchronize()
+            other_ms[f"{other}_ms_per_step"] = round((time.perf_counter() - t_o) * 1e3 / K, 5)
 
     # HBM bytes per launch of the dominant kernel from the committed profiler counters, used
     # only if they were taken on the current kernel sources at the same launch shape
@@ -330,80 +362,8 @@ def main() -> int:
                 and t.get("kernel") == dom_name and "traffic_bytes" in t):
             traffic = int(round(t["traffic_bytes"]))
 
-    # per mode and projection: the GEMV launch's mean duration (HIP events in the timed region)
-    names = {0: "dequant", 1: "int8act", 2: "twopass"}
-    per_mode = {}
-    for mode in modes:
-        per_mode[names[mode]] = {}
-        for si in range(len(shapes)):
-            b = alg_bytes(mode, shapes[si].N, shapes[si].K)
-            us = gemv_ms[(mode, si)] * 1e3
-            per_mode[names[mode]][shapes[si].name] = {
-                "splits": chosen[(mode, si)], "alg_bytes": b, "gemv_us": round(us, 3),
-                "gemv_GBs": round(b / us / 1e3, 1), "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
-
-    def mean_launch_us(calls, reps):
-        for c in calls:
-            c()
-        torch.cuda.synchronize()
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i in range(reps):
-            pairs[i][0].record()
-            calls[i % len(calls)]()
-            pairs[i][1].record()
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in pairs) / reps * 1e3
-
-    # Dequant on the same projections, beside the step: one launch with the same S (binary64
-    # chunk partials and an ascending binary64 combine in the last workgroup of each row tile)
-    if not args.no_dequant:
-        per_mode["dequant"] = {}
-        for si, sh in enumerate(shapes):
-            y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
-            S = (4, 8)[min(si, 1)]  # Dequant's measured best: four chunks (o-proj), eight (down-proj)
-            dws = q.sk_workspace(sh.N, S)
-            calls = [q.bind_gemv_q8_fused(0, copies[c][si][0], copies[c][si][1], y0, acts[si], S, dws)
-                     for c in range(R)]
-            for c in calls:
-                c()
-            torch.cuda.synchronize()
-            reps = max(K // 4, 2 * R)
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(reps)]
-            for i in range(reps):
-                pairs[i][0].record()
-                calls[i % R]()
-                pairs[i][1].record()
-            torch.cuda.synchronize()
-            us = sum(a.elapsed_time(b) for a, b in pairs) / reps * 1e3
-            b = alg_bytes(0, sh.N, sh.K)
-            per_mode["dequant"][sh.name] = {"splits": S, "alg_bytes": b, "gemv_us": round(us, 3),
-                                            "gemv_GBs": round(b / us / 1e3, 1),
-                                            "pct_of_peak": round(100 * b / us / 1e3 / PEAK_GBS, 2)}
-
-    # The configuration's own split counts, S in {1, 2, 4, 8}, beside the chosen S: the GEMV with
-    # its combine (the default path's qdg_gemv_q8_sk) per mode and projection, events around
-    # each launch, rotated copies.
-    splits_sweep = {}
-    if not args.no_sweep:
-        for mode in modes:
-            for si, sh in enumerate(shapes):
-                rec = {}
-                for S in (1, 2, 4, 8):
-                    ensure_buffers(mode, si, S)
-                    b = buffers[(mode, si, S)]
-                    calls = [q.bind_gemv_q8_sk(mode, copies[c][si][0], copies[c][si][1], b["y"], b["xq"], b["xl"],
-                                               b["xs"], S, b["fws"]) for c in range(R)]
-                    q.quantize_act(mode, acts[si], b["xq"], b["xl"], b["xs"])
-                    us = mean_launch_us(calls, max(40, 4 * R))
-                    rec[str(S)] = {"gemv_us": round(us, 3),
-                                   "gemv_GBs": round(alg_bytes(mode, sh.N, sh.K) / us / 1e3, 1),
-                                   "in_workgroup": q.sk_combines_in_workgroup(mode, sh.K, S)}
-                splits_sweep[f"{names[mode]}_{sh.name}"] = rec
-
-    # The practical read ceiling: qdg_stream_read (contiguous 64 KiB slabs a workgroup, nothing
-    # but 16-byte nontemporal loads) over as many bytes as each GEMV launch moves, rotated over
-    # a pool larger than the Infinity Cache, and over 1 GiB.
+    # ---- the streaming-read ceiling (qdg_stream_read: contiguous 64 KiB slabs a workgroup, only
+    # 16-byte nontemporal loads), over as many bytes as each GEMV moves and over 1 GiB
     ceiling = {}
     if not args.no_ceiling:
         pool = torch.empty(3 << 29, dtype=torch.uint8, device=dev)  # 1.5 GiB
@@ -413,25 +373,190 @@ def main() -> int:
         for name, nb_ in sizes.items():
             regions = max(1, pool.numel() // nb_)
             calls = [q.bind_stream_read(pool[r * nb_:], nb_, sink) for r in range(regions)]
-            us = mean_launch_us(calls, max(20, 4 * regions))
-            ceiling[name] = {"bytes": nb_, "us": round(us, 3), "GBs": round(nb_ / us / 1e3, 1)}
+            ceiling[name] = {"bytes": nb_, **rate(nb_, timer.median_us(calls, args.launches))}
         del pool
-        for mname, per_shape in per_mode.items():
-            for sname, rec in per_shape.items():
-                if sname in ceiling:
-                    rec["pct_of_read_ceiling"] = round(100 * rec["gemv_GBs"] / ceiling[sname]["GBs"], 1)
+        progress("read ceiling done")
 
-    # The producers of the activation words, beside the step: the residual add + RMSNorm and
-    # SwiGLU, each fused with the quantizer, against the same work in two launches (the f32
-    # result, then qdg_quantize_act).  Inputs of the projections' shapes: the norm over the
-    # hidden size (the o-proj's N), SwiGLU over the down-proj's K.
+    # ---- per mode and projection of the step
+    per_mode = {}
+    for mode in modes:
+        per_mode[NAMES[mode]] = {}
+        for si, sh in enumerate(shapes):
+            b = alg_bytes(mode, sh.N, sh.K)
+            rec = {"splits": chosen[(mode, si)], "alg_bytes": b,
+                   **rate(b, statistics.median(gemv_ms[(mode, si)]) * 1e3),
+                   "launches": len(gemv_ms[(mode, si)])}
+            if quant_ms[(mode, si)]:
+                rec["quantize_us"] = round(quant_ms[(mode, si)] * 1e3, 3)
+            if sh.name in ceiling:
+                rec["pct_of_read_ceiling"] = round(100 * rec["GBs"] / ceiling[sh.name]["GBs"], 1)
+            per_mode[NAMES[mode]][sh.name] = rec
+
+    # Dequant on the same projections, beside the step: one launch with binary64 chunk partials
+    # added in ascending order in the workgroup (qdg_gemv_q8_fused)
+    if not args.no_dequant:
+        per_mode["dequant"] = {}
+        for si, sh in enumerate(shapes):
+            y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+            S = (4, 8)[min(si, 1)]  # Dequant's measured best: four chunks (o-proj), eight (down-proj)
+            dws = q.sk_workspace(sh.N, S)
+            calls = [q.bind_gemv_q8_fused(0, copies[c][si][0], copies[c][si][1], y0, acts[si], S, dws)
+                     for c in range(R)]
+            b = alg_bytes(0, sh.N, sh.K)
+            rec = {"splits": S, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches))}
+            if sh.name in ceiling:
+                rec["pct_of_read_ceiling"] = round(100 * rec["GBs"] / ceiling[sh.name]["GBs"], 1)
+            per_mode["dequant"][sh.name] = rec
+
+    # ---- every workload configuration, device-timed
+    configs = {}
+    only = set(args.only_configs.split(",")) if args.only_configs else None
+
+    def want(name):
+        return not args.no_configs and (only is None or name in only)
+
+    def upload_set(config, si, rot_min=args.min_rotate_bytes):
+        d = workloads.make(config, si)
+        w = torch.from_numpy(d["wq"]).to(dev)
+        s = torch.from_numpy(d["ws"].view(np.int16)).to(dev)
+        n = rotation(w.numel() + 2 * s.numel(), rot_min)
+        ws_ = [(w, s)] + [(w.clone(), s.clone()) for _ in range(n - 1)]
+        return d, ws_
+
+    def quantized(mode, x):
+        B, Kx = x.shape
+        xq = torch.empty((B, Kx), dtype=torch.int8, device=dev)
+        xl = torch.empty((B, Kx), dtype=torch.int8, device=dev) if mode == 2 else None
+        xs = torch.empty((B, Kx // 32), dtype=torch.float32, device=dev)
+        q.quantize_act(mode, x, xq, xl, xs)
+        return xq, xl, xs
+
+    def projection_record(mode, sh, wsets, x, S):
+        """One projection in one mode through its default call: Dequant qdg_gemv_q8_fused,
+        the quantized modes qdg_gemv_q8_sk (in-workgroup combine where it fits) after the
+        quantizer.  Device µs of the GEMV, plus the quantizer's."""
+        y = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+        wsp = q.sk_workspace(sh.N, S)
+        rec = {"splits": S, "alg_bytes": alg_bytes(mode, sh.N, sh.K)}
+        if mode == 0:
+            calls = [q.bind_gemv_q8_fused(0, w, s, y, x, S, wsp) for w, s in wsets]
+        else:
+            xq, xl, xs = quantized(mode, x)
+            calls = [q.bind_gemv_q8_sk(mode, w, s, y, xq, xl, xs, S, wsp) for w, s in wsets]
+            rec["in_workgroup"] = q.sk_combines_in_workgroup(mode, sh.K, S)
+            rec["quantize_us"] = round(timer.median_us([q.bind_quantize_act(mode, x, xq, xl, xs)], args.launches), 3)
+        rec.update(rate(rec["alg_bytes"], timer.median_us(calls, args.launches)))
+        return rec
+
+    if want("tiny"):
+        sh = workloads.CONFIGS[0][0]
+        d, wsets = upload_set(0, 0, 0)
+        x = torch.from_numpy(d["x"]).to(dev)
+        rec = {}
+        for mode in (0, 1, 2):
+            y = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+            if mode == 0:
+                calls = [q.bind_gemv_q8(0, w, s, y, x=x) for w, s in wsets]
+            else:
+                xq, xl, xs = quantized(mode, x)
+                calls = [q.bind_gemv_q8(mode, w, s, y, xq=xq, xl=xl, xs=xs) for w, s in wsets]
+            rec[NAMES[mode]] = {"splits": 1, **rate(alg_bytes(mode, sh.N, sh.K), timer.median_us(calls, args.launches))}
+        configs["tiny_512x256"] = rec
+        progress("tiny done")
+
+    if want("8b"):
+        # S per projection (measured best, in-workgroup combine / Dequant chunk waves)
+        s_q8 = {"qkv": 2, "gate_up": 2, "down": 6}
+        s_dq = {"qkv": 5, "gate_up": 2, "down": 4}
+        for si, sh in enumerate(workloads.CONFIGS[1]):
+            d, wsets = upload_set(1, si)
+            x = torch.from_numpy(d["x"]).to(dev)
+            rec = {}
+            for mode in (0, 1, 2):
+                rec[NAMES[mode]] = projection_record(mode, sh, wsets, x, s_dq[sh.name] if mode == 0 else s_q8[sh.name])
+            configs[f"8b_{sh.name}_{sh.N}x{sh.K}"] = rec
+            del wsets
+        torch.cuda.empty_cache()
+        progress("8B projections done")
+
+    if want("narrow"):
+        # the configuration's own split counts S in {1, 2, 4, 8} through qdg_gemv_q8_sk (the
+        # in-workgroup combine where it serves the shape, else the last-arriving workgroup)
+        for si, sh in enumerate(shapes):
+            rec = {}
+            for mode in modes:
+                rec[NAMES[mode]] = {}
+                xq, xl, xs = quantized(mode, acts[si])
+                for S in (1, 2, 4, 8):
+                    y = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+                    wsp = q.sk_workspace(sh.N, S)
+                    calls = [q.bind_gemv_q8_sk(mode, copies[c][si][0], copies[c][si][1], y, xq, xl, xs, S, wsp)
+                             for c in range(R)]
+                    rec[NAMES[mode]][f"S{S}"] = {"in_workgroup": q.sk_combines_in_workgroup(mode, sh.K, S),
+                                                 **rate(alg_bytes(mode, sh.N, sh.K), timer.median_us(calls, args.launches))}
+            configs[f"narrow_{sh.name}_{sh.N}x{sh.K}_splits"] = rec
+        progress("narrow S sweep done")
+
+    if want("lm_head"):
+        sh = workloads.CONFIGS[3][0]
+        d = workloads.make(3, 0)
+        a, b = workloads.tie_rows(sh.N, workloads.seed_of(3, 0, 4))
+        workloads.plant_tie(d["wq"], d["ws"], d["x"][0], a, b)
+        w = torch.from_numpy(d["wq"]).to(dev)
+        s = torch.from_numpy(d["ws"].view(np.int16)).to(dev)
+        wsets = [(w, s), (w.clone(), s.clone())]
+        x = torch.from_numpy(d["x"]).to(dev)
+        del d
+        y = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+        idx = torch.empty(1, dtype=torch.int32, device=dev)
+        kws = q.gemv_argmax_workspace(sh.N)
+        rec = {"tie_rows": [a, b]}
+        for mode in (0, 1, 2):
+            if mode == 0:
+                calls = [q.bind_gemv_q8_argmax(0, ww, ss, y, idx, kws, x=x) for ww, ss in wsets]
+                qus = 0.0
+            else:
+                xq, xl, xs = quantized(mode, x)
+                calls = [q.bind_gemv_q8_argmax(mode, ww, ss, y, idx, kws, xq=xq, xl=xl, xs=xs) for ww, ss in wsets]
+                qus = timer.median_us([q.bind_quantize_act(mode, x, xq, xl, xs)], args.launches)
+            r = {"gemv": rate(alg_bytes(mode, sh.N, sh.K), timer.median_us(calls, args.launches))}
+            r["end_to_end_us"] = round(timer.wall_us(calls, args.launches) + qus, 3)
+            if qus:
+                r["quantize_us"] = round(qus, 3)
+            torch.cuda.synchronize()
+            r["index"] = int(idx.item())
+            r["index_is_first_tie"] = r["index"] == a
+            rec[NAMES[mode]] = r
+        configs[f"lm_head_{sh.N}x{sh.K}_argmax"] = rec
+        del wsets, w, s
+        torch.cuda.empty_cache()
+        progress("LM head done")
+
+    if want("batched"):
+        sh = workloads.CONFIGS[4][0]
+        d, wsets = upload_set(4, 0)
+        x = torch.from_numpy(d["x"]).to(dev)
+        rec = {}
+        for mode in (1, 2):
+            xq, xl, xs = quantized(mode, x)
+            y = torch.empty((sh.B, sh.N), dtype=torch.float32, device=dev)
+            calls = [q.bind_gemv_q8(mode, w, s, y, xq=xq, xl=xl, xs=xs) for w, s in wsets]
+            rec[NAMES[mode]] = {"B": sh.B, "alg_bytes": alg_bytes(mode, sh.N, sh.K, sh.B),
+                                **rate(alg_bytes(mode, sh.N, sh.K, sh.B), timer.median_us(calls, args.launches))}
+        configs[f"batched_B{sh.B}_{sh.N}x{sh.K}"] = rec
+        del wsets
+        torch.cuda.empty_cache()
+        progress("batched done")
+
+    # ---- the producers of the activation words, beside the step: the residual add + RMSNorm
+    # and SwiGLU, each fused with the quantizer, against the same work in two launches
     producers = {}
     if not args.no_producers:
         hid, inter = shapes[0].N, shapes[-1].K
         xr = torch.from_numpy(workloads.batch_activation(1, hid, 11, True, 12)).to(dev)
         rr = torch.from_numpy(workloads.batch_activation(1, hid, 13)).to(dev)
         wn = torch.from_numpy(workloads.norm_weight(hid, 14)).to(dev)
-        gg, uu = (torch.from_numpy(a).to(dev) for a in workloads.glu_inputs(1, inter, 15))
+        gg, uu = (torch.from_numpy(a_).to(dev) for a_ in workloads.glu_inputs(1, inter, 15))
         for mode in modes:
             for name, K_, fused, f32_only, f32 in (
                     ("rmsnorm", hid,
@@ -444,13 +569,14 @@ def main() -> int:
                 xl_ = torch.empty_like(xq_) if mode == 2 else None
                 xs_ = torch.empty((1, K_ // 32), dtype=torch.float32, device=dev)
                 one = fused(xq_, xl_, xs_)
-                a, b = f32_only(f32), q.bind_quantize_act(mode, f32, xq_, xl_, xs_)
-                producers[f"{name}_{names[mode]}_K{K_}"] = {
-                    "fused_us": round(mean_launch_us([one], 200), 2),
-                    "two_launches_us": round(mean_launch_us([lambda: (a(), b())], 200), 2)}
+                a_, b_ = f32_only(f32), q.bind_quantize_act(mode, f32, xq_, xl_, xs_)
+                producers[f"{name}_{NAMES[mode]}_K{K_}"] = {
+                    "fused_us": round(timer.median_us([one], args.launches), 2),
+                    "f32_producer_us": round(timer.median_us([a_], args.launches), 2),
+                    "quantize_us": round(timer.median_us([b_], args.launches), 2)}
 
-    # The other GGUF block formats on the down-proj's shape, beside the step: qdg_gemv_fmt in the
-    # two quantized modes at S=8 (one round of 1280 five-wave workgroups), over rotated copies.
+    # ---- the other GGUF block formats on the down-proj's shape: qdg_gemv_fmt in the two
+    # quantized modes at S=8 (one round of 1280 five-wave workgroups), over rotated copies
     formats = {}
     if not args.no_formats:
         fsh = shapes[-1]
@@ -458,13 +584,7 @@ def main() -> int:
                   11: "Q3_K", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K", 23: "IQ4_XS"}
         fx = acts[-1]
         fy = torch.empty((fsh.N,), dtype=torch.float32, device=dev)
-        fq = {}
-        for mode in modes:
-            xq_ = torch.empty((1, fsh.K), dtype=torch.int8, device=dev)
-            xl_ = torch.empty_like(xq_) if mode == 2 else None
-            xs_ = torch.empty((1, fsh.K // 32), dtype=torch.float32, device=dev)
-            q.quantize_act(mode, fx, xq_, xl_, xs_)
-            fq[mode] = (xq_, xl_, xs_)
+        fq = {mode: quantized(mode, fx) for mode in modes}
         for fmt, fname in fnames.items():
             Kf = fsh.K // workloads.BLOCK_FORMATS[fmt][0] * workloads.BLOCK_FORMATS[fmt][0]
             wb = torch.from_numpy(workloads.block_matrix(fmt, fsh.N, Kf, 2000 + fmt).reshape(-1)).to(dev)
@@ -474,55 +594,53 @@ def main() -> int:
             for mode in modes:
                 xq_, xl_, xs_ = fq[mode]
                 calls = [q.bind_gemv_fmt(fmt, mode, c, fsh.N, Kf, fy, xq=xq_, xl=xl_, xs=xs_, splits=8) for c in fc]
-                us = mean_launch_us(calls, max(40, 2 * len(fc)))
-                rec[names[mode]] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
-                                    "pct_of_peak": round(100 * nbytes / us / 1e3 / PEAK_GBS, 1)}
+                rec[NAMES[mode]] = rate(nbytes, timer.median_us(calls, args.launches))
             formats[fname] = rec
             del fc, wb
         torch.cuda.empty_cache()
+        progress("formats done")
 
-    # ---- CPU baseline: the oracle on the same step (whole steps, repeated for a bounded time)
+    # ---- CPU baseline: the oracle on the same step.  One warm-up run, then five timed runs of
+    # whole steps (each run as many steps as fill --cpu-seconds); the median run's throughput.
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         threads = min(16, os.cpu_count() or 1)
-        t_cpu, n_steps = 0.0, 0
-        while n_steps == 0 or t_cpu < args.cpu_seconds:
-            tb = time.perf_counter()
+
+        def oracle_step(nthreads):
             for mode in modes:
-                for si, sh in enumerate(shapes):
-                    d = host[si]
-                    xq, xl, xs = oracle.quantize(mode, d["x"])
-                    part = oracle.gemv_split(mode, d["wq"], d["ws"], xq, xl, xs, chosen[(mode, si)],
-                                             nthreads=threads)
-                    oracle.combine(part)
-            t_cpu += time.perf_counter() - tb
-            n_steps += 1
-        # the same steps on one thread (row-parallel OpenMP does not change any row's order), for a
-        # quarter of the budget
-        t1, n1 = 0.0, 0
-        while n1 == 0 or t1 < args.cpu_seconds / 4:
-            tb = time.perf_counter()
-            for mode in modes:
-                for si, sh in enumerate(shapes):
+                for si in range(len(shapes)):
                     d = host[si]
                     xq, xl, xs = oracle.quantize(mode, d["x"])
                     oracle.combine(oracle.gemv_split(mode, d["wq"], d["ws"], xq, xl, xs, chosen[(mode, si)],
-                                                     nthreads=1))
-            t1 += time.perf_counter() - tb
-            n1 += 1
+                                                     nthreads=nthreads))
+
+        def cpu_runs(nthreads):
+            tb = time.perf_counter()
+            oracle_step(nthreads)  # warm-up run of one step also sizes the runs
+            per = max(1, int(args.cpu_seconds / max(time.perf_counter() - tb, 1e-3)))
+            rates = []
+            for _ in range(5):
+                tb = time.perf_counter()
+                for _ in range(per):
+                    oracle_step(nthreads)
+                rates.append(step_bytes * per / (time.perf_counter() - tb) / 1e9)
+            return statistics.median(rates), per
+
+        v_all, per_all = cpu_runs(threads)
+        v_one, per_one = cpu_runs(1)
         model = ""
         try:
             model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
         except (OSError, StopIteration):
             pass
-        cpu = {"value": round(step_bytes * n_steps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{n_steps} whole steps ({t_cpu:.1f} s): quantize + split-K GEMV + combine of both "
-                         f"projections in every mode, OpenMP over rows",
-               "single_thread_value": round(step_bytes * n1 / t1 / 1e9, 3),
-               "single_thread_sample": f"{n1} whole steps ({t1:.1f} s) on one thread",
+        cpu = {"value": round(v_all, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"median of 5 runs of {per_all} whole steps each after one warm-up step: quantize + "
+                         f"split-K GEMV + combine of both projections in every mode, OpenMP over rows",
+               "single_thread_value": round(v_one, 3),
+               "single_thread_sample": f"median of 5 runs of {per_one} whole steps on one thread",
                "host": {"cpu_count": os.cpu_count(), "model": model}}
+        progress("cpu baseline done")
 
     line = {
         "metric": "Q8_0 GEMV achieved HBM GB/s and % of peak per mode (Dequant/Int8/TwoPass)",
@@ -536,18 +654,23 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 dot / f32 sum",
-        "data": "synthetic (seeded; int8 weights uniform [-127,127], fp16 scales U[1e-3,1e-2), N(0,1) activations with 1% x20 outliers)",
+        "data": "synthetic (seeded; int8 weights uniform [-127,127], fp16 scales U[1e-3,1e-2), N(0,1) activations "
+                "with 1% x20 outliers)",
         "config": {"workload": "narrow projections with split-K: o-proj K=8192 N=5120 and down-proj K=25600 N=5120, "
                                "batch 1, Int8Act + TwoPass, quantize + GEMV + ascending combine",
                    "path": args.path, "weights": args.weights, **other_ms,
+                   "timed_pass_ms_per_step": round(hook_pass_ms, 5),
                    "global_batch": 1, "seq_len": 1, "parallelism": "single GPU",
                    "weight_copies": R, "rotated_bytes": R * set_bytes, "modes": per_mode,
-                   "read_ceiling": ceiling, "producers": producers, "formats": formats, "splits_sweep": splits_sweep,
-                   "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2)},
+                   "configs": configs, "read_ceiling": ceiling, "producers": producers, "formats": formats,
+                   "step_alg_bytes": step_bytes, "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+                   "timing": "device durations: events bound to each kernel's own dispatch "
+                             "(qdg_time_next_launch), median over the measured launches"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"{dom_name} ({args.path} path) down-proj 5120x25600 TwoPass S={chosen[dom_key]}",
-                     "alg_bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_ms * 1e3, 3)},
+                     "alg_bytes_per_launch": dom_bytes, "median_launch_us": round(dom_us, 3),
+                     "launches": len(gemv_ms[dom_key])},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }

@@ -408,6 +408,52 @@ int qdg_gemv_q8_sk_tiled(int mode, const int8_t *wt, const uint16_t *ws, int64_t
                          qdg_stream stream);
 
 /*
+ * Tuning and test hooks.  Process-wide settings that choose among the library's
+ * kernels, staging forms and launch shapes for the same call -- never the
+ * arithmetic or its order, so every setting gives the same output bits -- for
+ * tests that compare two kernels on one shape and for sweeps.  Every knob starts
+ * at -1 (the library's own choice) and only these calls change it: the
+ * environment is never read.  Not meant to be changed while another thread is
+ * inside the library.
+ */
+enum {
+  QDG_TUNE_SK_WSPLIT = 0,  /* 0: qdg_gemv_q8_sk always combines through the workspace      */
+  QDG_TUNE_WS_DMA = 1,     /* 0: the in-workgroup split and the GLU kernel copy their staged */
+                           /*    bytes through registers instead of LDS DMA                  */
+  QDG_TUNE_WS_LOCAL = 2,   /* 1: per-wave staging, 0: workgroup-wide staging                 */
+  QDG_TUNE_WS_ROWS = 3,    /* 1..4: row groups a workgroup of the in-workgroup split         */
+  QDG_TUNE_DQ_SEG = 4,     /* 0: Dequant split-K takes the last-arriver kernel               */
+  QDG_TUNE_DQ_ROWS = 5,    /* 1..4: row groups a workgroup of the Dequant chunk waves        */
+  QDG_TUNE_DQ_X64 = 6,     /* 0: the unsplit Dequant kernel keeps its window in binary32     */
+  QDG_TUNE_MFMA_GENERAL = 7, /* 1: the batched GEMV on its general (register) path           */
+  QDG_TUNE_MFMA_SHAPE = 8, /* 100*waves + 10*tiles + ring of the batched fast path (B <= 16)  */
+  QDG_TUNE_MFMA_WIDE = 9,  /* the same for 16 < B <= 64                                      */
+  QDG_TUNE_GEMV_ORDER = 10, /* 0: tile-major, 1: chunk-major workgroup order (split GEMV)    */
+  QDG_TUNE_GEMV_RPW = 11,  /* 4 or 8 rows a wave (batch-1 GEMV)                              */
+  QDG_TUNE_GEMV_UNROLL = 12, /* 2, 4 or 8 steps in flight with eight rows a wave             */
+  QDG_TUNE_REJECT_LAUNCH = 13, /* 1: every launch asks for a 2048-thread workgroup, which the */
+                           /*    HIP runtime refuses before anything is enqueued: the calls  */
+                           /*    then return QDG_EHIP (the error path's test hook)           */
+  QDG_TUNE_COUNT = 14
+};
+
+/* Sets knob to value (-1 restores the default).  QDG_EINVAL for an unknown knob. */
+int qdg_set_tuning(int knob, int value);
+/* The knob's current value (-1: default); QDG_EINVAL for an unknown knob. */
+int qdg_get_tuning(int knob);
+
+/*
+ * Measurement hook: the next kernel that a call of this thread launches carries
+ * the two events (hipEvent_t, created by the caller) on its own dispatch
+ * (hipExtLaunchKernel): hipEventElapsedTime(start, stop) is then that kernel's
+ * device duration, the time a kernel trace reports, without the stream work of
+ * separately recorded events.  The binding covers one launch and is cleared by
+ * it; for a call that launches more than one kernel, the first is timed.
+ * Passing NULLs clears it.  Returns QDG_OK.
+ */
+int qdg_time_next_launch(void *start, void *stop);
+
+/*
  * Host only: the split-K chunk boundaries in 32-value blocks (QWEN38 page,
  * gk_gemv_hl_sk): K runs in 512-value superblocks, per = ceil((K/512)/splits),
  * chunk s takes superblocks [s*per, min((s+1)*per, K/512)) and the last chunk

@@ -25,6 +25,7 @@ no fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -80,6 +81,9 @@ _SIGS = {
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
+    "qdg_set_tuning": ([_I, _I], _I),
+    "qdg_get_tuning": ([_I], _I),
+    "qdg_time_next_launch": ([_P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -101,6 +105,41 @@ class QdgError(RuntimeError):
 def _check(fn: str, status: int) -> None:
     if status != 0:
         raise QdgError(fn, status)
+
+
+# qdg_set_tuning's knobs (include/qdg.h): they choose among kernels, stagings and
+# launch shapes that give the same bits; -1 is the library's own choice.
+TUNE = {"sk_wsplit": 0, "ws_dma": 1, "ws_local": 2, "ws_rows": 3, "dq_seg": 4, "dq_rows": 5, "dq_x64": 6,
+        "mfma_general": 7, "mfma_shape": 8, "mfma_wide": 9, "gemv_order": 10, "gemv_rpw": 11,
+        "gemv_unroll": 12, "reject_launch": 13}
+
+
+def set_tuning(knob: str, value: int) -> None:
+    _check("qdg_set_tuning", _lib.qdg_set_tuning(TUNE[knob], int(value)))
+
+
+def get_tuning(knob: str) -> int:
+    return int(_lib.qdg_get_tuning(TUNE[knob]))
+
+
+@contextlib.contextmanager
+def tuning(**knobs):
+    """Sets the named knobs (``tuning(ws_dma=0, ws_local=1)``) for the block and restores them after."""
+    old = {k: get_tuning(k) for k in knobs}
+    try:
+        for k, v in knobs.items():
+            set_tuning(k, -1 if v is None else v)
+        yield
+    finally:
+        for k, v in old.items():
+            set_tuning(k, v)
+
+
+def time_next_launch(start, stop) -> None:
+    """Binds two recorded ``torch.cuda.Event(enable_timing=True)`` to the next kernel this thread's
+    calls launch: ``start.elapsed_time(stop)`` is then that kernel's device duration."""
+    _check("qdg_time_next_launch", _lib.qdg_time_next_launch(ctypes.c_void_p(start.cuda_event),
+                                                              ctypes.c_void_p(stop.cuda_event)))
 
 
 def abi_version() -> int:
@@ -139,6 +178,24 @@ def _ptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(**sized) -> None:
+    """Host-side size checks before a call: each keyword is ``name=(tensor, elements)``; a tensor
+    (when given) holding fewer elements than the call reads or writes raises ValueError, so an
+    undersized buffer never reaches the device."""
+    for name, (t, n) in sized.items():
+        if t is not None and t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _gemv_sizes(mode, wq_shape, ws, B, x=None, xq=None, xl=None, xs=None, **outs) -> None:
+    """The sizes every GEMV entry point assumes: ws [N][K/32], the activation of B rows in the
+    mode's encoding, and each output's element count (``outs``: name=(tensor, elements))."""
+    N, K = wq_shape
+    if ws is not None and tuple(ws.shape) != (N, K // QK) and ws.numel() != N * (K // QK):
+        raise ValueError(f"ws must hold [N][K/32] = [{N}][{K // QK}] scales, got shape {tuple(ws.shape)}")
+    _need(x=(x, B * K), xq=(xq, B * K), xl=(xl, B * K), xs=(xs, B * (K // QK)), **outs)
+
+
 def _i8():
     return (_torch().int8,)
 
@@ -155,6 +212,7 @@ def _scales():
 def quantize_act(mode: int, x, xq, xl, xs) -> None:
     """``x [B][K]`` float32 -> ``xq`` (and ``xl`` under TwoPass) int8 ``[B][K]``, ``xs [B][K/32]``."""
     B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    _need(xq=(xq, B * K), xl=(xl, B * K), xs=(xs, B * (K // QK)))
     _check("qdg_quantize_act", _lib.qdg_quantize_act(
         mode, _ptr(x, _f32(), "x"), B, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
         _stream()))
@@ -290,6 +348,7 @@ def gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, splits: i
     N, K = wq.shape
     act = x if mode == DEQUANT else xq
     B = act.shape[0] if act.dim() == 2 else 1
+    _gemv_sizes(mode, wq.shape, ws, B, x, xq, xl, xs, out=(out, int(splits) * B * N))
     _check("qdg_gemv_q8", _lib.qdg_gemv_q8(
         mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"),
         _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), B, int(splits),
@@ -325,6 +384,7 @@ def gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> None
     """Split-K GEMV whose last-arriving workgroups do the ascending combine: ``y [1][N]``."""
     N, K = wq.shape
     B = xq.shape[0] if xq.dim() == 2 else 1
+    _gemv_sizes(mode, wq.shape, ws, B, None, xq, xl, xs, y=(y, B * N))
     nbytes = workspace.numel() * workspace.element_size()
     _check("qdg_gemv_q8_sk", _lib.qdg_gemv_q8_sk(
         mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"),
@@ -343,6 +403,7 @@ def q8_tile_rows(wq, wt) -> None:
 def gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> None:
     """``gemv_q8_sk``'s in-workgroup placement over row-tiled weights ``wt`` (from ``q8_tile_rows``)."""
     N, K = wt.shape
+    _gemv_sizes(mode, wt.shape, ws, 1, None, xq, xl, xs, y=(y, N))
     _check("qdg_gemv_q8_sk_tiled", _lib.qdg_gemv_q8_sk_tiled(
         mode, _ptr(wt, _i8(), "wt"), _ptr(ws, _scales(), "ws"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"),
         _ptr(xs, _f32(), "xs"), int(splits), _ptr(y, _f32(), "y"), _stream()))
@@ -352,6 +413,7 @@ def gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> N
     """One launch for a batch-1 projection: quantize ``x [1][K]`` (f32), split-K GEMV and ascending
     combine into ``y [1][N]`` (``workspace`` from ``sk_workspace(N, splits)``; may be None when S == 1)."""
     N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, x, y=(y, N))
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("qdg_gemv_q8_fused", _lib.qdg_gemv_q8_fused(
         mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), int(splits),
@@ -379,6 +441,7 @@ def gemv_argmax_workspace(N: int):
 def gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, xl=None, xs=None) -> None:
     """LM-head tail: ``y [1][N]`` logits and ``idx [1]`` int32 first index of their maximum, in two launches."""
     N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, x, xq, xl, xs, y=(y, N), idx=(idx, 1))
     nbytes = workspace.numel() * workspace.element_size()
     _check("qdg_gemv_q8_argmax", _lib.qdg_gemv_q8_argmax(
         mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), _ptr(xq, _i8(), "xq"),
@@ -388,6 +451,7 @@ def gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, xl=Non
 
 def bind_gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, xl=None, xs=None) -> Bound:
     N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, x, xq, xl, xs, y=(y, N), idx=(idx, 1))
     for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (idx, "idx"), (workspace, "workspace"), (x, "x"), (xq, "xq"),
                  (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
@@ -449,6 +513,7 @@ def bind_gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, spli
     N, K = wq.shape
     act = x if mode == DEQUANT else xq
     B = act.shape[0] if act.dim() == 2 else 1
+    _gemv_sizes(mode, wq.shape, ws, B, x, xq, xl, xs, out=(out, int(splits) * B * N))
     for t, n in ((wq, "wq"), (ws, "ws"), (out, "out"), (x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_gemv_q8", mode, wq, ws, N, K, x, xq, xl, xs, B, int(splits), out, _stream())
@@ -457,6 +522,7 @@ def bind_gemv_q8(mode: int, wq, ws, out, x=None, xq=None, xl=None, xs=None, spli
 def bind_gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) -> Bound:
     N, K = wq.shape
     B = xq.shape[0] if xq.dim() == 2 else 1
+    _gemv_sizes(mode, wq.shape, ws, B, None, xq, xl, xs, y=(y, B * N))
     for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (xq, "xq"), (xl, "xl"), (xs, "xs"), (workspace, "workspace")):
         _ptr(t, None, n)
     nbytes = workspace.numel() * workspace.element_size()
@@ -465,6 +531,7 @@ def bind_gemv_q8_sk(mode: int, wq, ws, y, xq, xl, xs, splits: int, workspace) ->
 
 def bind_gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> Bound:
     N, K = wt.shape
+    _gemv_sizes(mode, wt.shape, ws, 1, None, xq, xl, xs, y=(y, N))
     for t, n in ((wt, "wt"), (ws, "ws"), (y, "y"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_gemv_q8_sk_tiled", mode, wt, ws, N, K, xq, xl, xs, int(splits), y, _stream())
@@ -472,6 +539,7 @@ def bind_gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> Boun
 
 def bind_gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> Bound:
     N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, x, y=(y, N))
     for t, n in ((wq, "wq"), (ws, "ws"), (y, "y"), (x, "x"), (workspace, "workspace")):
         _ptr(t, None, n)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -487,6 +555,7 @@ def bind_stream_read(buf, nbytes: int, sink) -> Bound:
 
 def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:
     B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    _need(xq=(xq, B * K), xl=(xl, B * K), xs=(xs, B * (K // QK)))
     for t, n in ((x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_quantize_act", mode, x, B, K, xq, xl, xs, _stream())

@@ -3,12 +3,20 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/qdg.h"
 #include "qdg_device.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+// qdg_time_next_launch's events, taken by the thread's next launch
+thread_local qdg::LaunchTiming g_timing = {nullptr, nullptr};
+
+// qdg_set_tuning's knobs (-1: the library's own choice)
+std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QDG_TUNE_COUNT == 14, "one initializer a knob");
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -28,7 +36,32 @@ hipStream_t as_stream(qdg_stream s) { return (hipStream_t)s; }
 
 }  // namespace
 
+namespace qdg {
+int tune(int knob) { return g_tune[knob].load(std::memory_order_relaxed); }
+LaunchTiming take_launch_timing() {
+  const LaunchTiming t = g_timing;
+  g_timing = LaunchTiming{nullptr, nullptr};
+  return t;
+}
+}  // namespace qdg
+
 extern "C" {
+
+int qdg_set_tuning(int knob, int value) {
+  if (knob < 0 || knob >= QDG_TUNE_COUNT) return QDG_EINVAL;
+  g_tune[knob].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+  return QDG_OK;
+}
+
+int qdg_get_tuning(int knob) {
+  if (knob < 0 || knob >= QDG_TUNE_COUNT) return QDG_EINVAL;
+  return g_tune[knob].load(std::memory_order_relaxed);
+}
+
+int qdg_time_next_launch(void* start, void* stop) {
+  g_timing = qdg::LaunchTiming{(hipEvent_t)start, (hipEvent_t)stop};
+  return QDG_OK;
+}
 
 int qdg_abi_version(void) { return QDG_ABI_VERSION; }
 

@@ -29,7 +29,6 @@
 // ascending chunk order in binary64 and rounds once to binary32.  Every sum is
 // still binary64 and there is still one rounding to binary32, so the result
 // stays within the Dequant tolerance of the plain definition.
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -224,20 +223,21 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
     if (li == 0 && row_ok) out[o] = (float)y;
     return;
   }
-  // Publish the chunk's partial and let the tile's last workgroup combine: the
-  // partial stores and the last arriver's loads are agent-scope atomic accesses,
-  // each writer waits for its store (vmcnt(0)) before the barrier, and only then
-  // does one thread take the ticket.
+  // Publish the chunk's partial and let the tile's last workgroup combine, under
+  // the HIP memory model: each writer's store, then an agent-scope release fence,
+  // the barrier, one agent-scope acq_rel ticket RMW, the barrier, and an
+  // agent-scope acquire fence in every reader before its loads.
   if (li == 0 && row_ok)
     __hip_atomic_store(part + (int64_t)blockIdx.y * N + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   __shared__ int last_arrival;
   if (threadIdx.x == 0)
-    last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(S - 1);
   __syncthreads();
   if (!last_arrival) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
     const int64_t oo = o_wg + threadIdx.x;
     double a = 0.0;
@@ -268,20 +268,13 @@ hipError_t launch_dq(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
   unsigned* tickets = (unsigned*)workspace;
   double* part = splits == 1 ? nullptr : (double*)((char*)workspace + sk_partials_offset(N));
   const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)splits), block(WG);
-  hipLaunchKernelGGL((k_gemv_dequant<RPW, U, XF64, AMAX>), grid, block, lds, st, wq, ws, x, N, K, splits, win, y,
+  return launch((k_gemv_dequant<RPW, U, XF64, AMAX>), grid, block, lds, st, wq, ws, x, N, K, splits, win, y,
                      part, tickets, keys);
-  return hipGetLastError();
 }
 
 // Activation staged in binary32 (converted by every row's lanes) or binary64
-// (converted once per workgroup); QDG_DQ_X64 = 0 or 1, read once.
-bool dq_x64() {
-  static const bool v = [] {
-    const char* e = getenv("QDG_DQ_X64");
-    return e ? atoi(e) != 0 : true;
-  }();
-  return v;
-}
+// (converted once per workgroup, the default); QDG_TUNE_DQ_X64 = 0 picks binary32.
+bool dq_x64() { return tune(QDG_TUNE_DQ_X64) != 0; }
 
 }  // namespace
 
@@ -299,9 +292,8 @@ hipError_t launch_gemv_dequant_argmax(const int8_t* wq, const uint16_t* ws, int6
 hipError_t launch_gemv_dequant_sk(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                   int splits, float* y, void* workspace, hipStream_t st) {
   // the chunks as waves of one workgroup (qdg_dequant_seg.hip) wherever that
-  // kernel serves the shape; QDG_DQ_SEG=0 forces this file's kernel (read on every call)
-  const char* e = getenv("QDG_DQ_SEG");
-  if (!(e && e[0] == '0') && dq_seg_chunks(K, splits) > 0) return launch_gemv_dq_seg(wq, ws, N, K, x, splits, y, st);
+  // kernel serves the shape; QDG_TUNE_DQ_SEG = 0 forces this file's kernel
+  if (tune(QDG_TUNE_DQ_SEG) != 0 && dq_seg_chunks(K, splits) > 0) return launch_gemv_dq_seg(wq, ws, N, K, x, splits, y, st);
   if (dq_x64()) return launch_dq<true>(wq, ws, N, K, x, splits, y, workspace, st);
   return launch_dq<false>(wq, ws, N, K, x, splits, y, workspace, st);
 }

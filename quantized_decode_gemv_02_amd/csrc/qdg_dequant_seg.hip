@@ -27,7 +27,6 @@
 // row and step, where summing the block's four pieces across its lanes first
 // took two DPP moves, two additions and a multiplication: 8% faster on the
 // 5120x25600 projection at S = 8 (35.7 -> 32.7 us).
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -150,8 +149,7 @@ void ds_chunks(int64_t K, int S, int& m, int& ceff) {
 template <int R>
 hipError_t launch_ds(const PartTable& tab, int64_t K, const float* x, int S, int m, int ceff, hipStream_t st) {
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
-  hipLaunchKernelGGL((k_gemv_dq_seg<R>), grid, block, 0, st, tab, x, K, S, m, ceff);
-  return hipGetLastError();
+  return launch((k_gemv_dq_seg<R>), grid, block, 0, st, tab, x, K, S, m, ceff);
 }
 
 }  // namespace
@@ -173,9 +171,9 @@ hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const u
   int m, ceff;
   ds_chunks(K, S, m, ceff);
   // one row group a workgroup (measured on the 5120-row projections: R = 1 is
-  // 10-25% faster than 2-4 at S = 4, 5 and 8); QDG_DQ_ROWS overrides
+  // 10-25% faster than 2-4 at S = 4, 5 and 8); QDG_TUNE_DQ_ROWS overrides
   int R = 1;
-  if (const char* e = getenv("QDG_DQ_ROWS")) R = atoi(e);
+  if (tune(QDG_TUNE_DQ_ROWS) > 0) R = tune(QDG_TUNE_DQ_ROWS);
   if (R < 1) R = 1;
   if (R > 4) R = 4;
   while (R > 1 && R * ceff > 16) --R;

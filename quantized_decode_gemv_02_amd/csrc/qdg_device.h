@@ -3,10 +3,48 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
+#include "../../include/qdg.h"
+
 namespace qdg {
+
+// The process-wide tuning knobs (qdg_set_tuning; -1 = the library's choice) and
+// the calling thread's measurement events for its next launch
+// (qdg_time_next_launch), taken and cleared by that launch.  Both live in
+// qdg_api.hip.
+int tune(int knob);
+struct LaunchTiming {
+  hipEvent_t start, stop;
+};
+LaunchTiming take_launch_timing();
+
+// Every kernel of the library is launched through here.  The dispatch carries
+// the thread's measurement events when some are bound (hipExtLaunchKernel takes
+// them on the kernel's own packet), and the error-path test hook
+// (QDG_TUNE_REJECT_LAUNCH) asks for a workgroup of 2048 threads, which the
+// runtime refuses before anything is enqueued.  A refused launch leaves no
+// pending error behind for the caller's next HIP call.
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<std::decay_t<P>...> vals{static_cast<std::decay_t<P>>(args)...};
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&v), ...);
+  }, vals);
+  if (tune(QDG_TUNE_REJECT_LAUNCH) == 1) block = dim3(2048, 1, 1);
+  const LaunchTiming t = take_launch_timing();
+  const hipError_t e = hipExtLaunchKernel((const void*)kernel, grid, block, ptrs, lds, st, t.start, t.stop, 0);
+  if (e != hipSuccess) (void)hipGetLastError();
+  return e;
+}
 
 constexpr int QK = 32;          // values per Q8_0 block
 constexpr int SUPER = 16;       // blocks per 512-value superblock of the split-K chunk rule

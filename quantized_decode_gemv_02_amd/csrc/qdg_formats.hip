@@ -26,7 +26,6 @@
 // ahead.  Split-K (the QWEN38 page's chunk rule, gk_gemv_hl_sk /
 // gk_sk_combine): the chunks are waves of one workgroup and their partials are
 // added in ascending order in LDS.
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -611,9 +610,8 @@ hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, con
   const int waves = R * ceff;
   const size_t lds = (size_t)waves * Stage<F, MODE, ROWS>::SLOT + (size_t)waves * ROWS * sizeof(Acc);
   const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * waves));
-  hipLaunchKernelGGL((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
+  return launch((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
                      ceff, y);
-  return hipGetLastError();
 }
 
 // Four rows a wave (16 lanes a row) and one row group a workgroup: on the

@@ -35,7 +35,6 @@
 //    routine, eight lanes a block -- instead of copying words quantized by an
 //    earlier launch; every workgroup of a chunk quantizes the same blocks, so
 //    they all hold the words the quantizer kernel would write, bit for bit.
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -214,22 +213,24 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
       if (li == 0 && row_ok) y[o] = yv;
       return;
     }
-    // Publish the partials without an L2-wide release: the partial stores and the
-    // last arriver's loads are agent-scope atomic accesses (coherent across the
-    // XCDs' L2s by themselves), each writer waits until its store has completed
-    // (s_waitcnt vmcnt(0)) before the workgroup barrier, and only then does one
-    // thread take the ticket (an agent-scope RMW).  The last arriver's loads are
-    // issued after it has seen the ticket, so they return every chunk's partial.
+    // Publish the partials under the HIP memory model: every writer's partial
+    // store is followed by an agent-scope release fence before the workgroup
+    // barrier; one thread then takes the ticket with an agent-scope acq_rel RMW
+    // (releasing the workgroup's partials to the tile's other workgroups and, in
+    // the last arriver, acquiring theirs); after the second barrier every reader
+    // takes an agent-scope acquire fence before it loads the partials.  Which
+    // chunk arrives last changes nothing in the sum.
     if (li == 0 && row_ok)
       __hip_atomic_store(out + (int64_t)s_idx * N + o, yv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     __shared__ int last_arrival;
     if (threadIdx.x == 0)
-      last_arrival = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_arrival = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                      (unsigned)(S - 1);
     __syncthreads();
     if (!last_arrival) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
       const int64_t oo = o_wg + threadIdx.x;
       float a = 0.0f;
@@ -247,22 +248,17 @@ struct Tuning {
   int order = -1;  // -1: by S (chunk-major for S <= 4), 0: tile-major, 1: chunk-major
 };
 
-// Tuning knobs for sweeps (QDG_RPW in {4, 8}, QDG_UNROLL in {2, 4, 8} -- the load depth of
-// the eight-rows-a-wave layout only --, QDG_ORDER
-// in {chunk, tile}); they change the lane layout, load depth and workgroup
-// order only, never the arithmetic or its order.
+// Tuning knobs for sweeps (QDG_TUNE_GEMV_RPW in {4, 8}, QDG_TUNE_GEMV_UNROLL in
+// {2, 4, 8} -- the load depth of the eight-rows-a-wave layout only --,
+// QDG_TUNE_GEMV_ORDER 0 tile-major / 1 chunk-major); they change the lane
+// layout, load depth and workgroup order only, never the arithmetic or its order.
 Tuning tuning() {
-  static Tuning t = [] {
-    Tuning v;
-    if (const char* e = getenv("QDG_ORDER")) v.order = e[0] == 't' ? 0 : 1;
-    if (const char* e = getenv("QDG_RPW")) v.rpw = atoi(e) == 8 ? 8 : 4;
-    if (const char* e = getenv("QDG_UNROLL")) {
-      const int u = atoi(e);
-      v.unroll = (u == 2 || u == 8) ? u : 4;
-    }
-    return v;
-  }();
-  return t;
+  Tuning v;
+  const int order = tune(QDG_TUNE_GEMV_ORDER), rpw = tune(QDG_TUNE_GEMV_RPW), u = tune(QDG_TUNE_GEMV_UNROLL);
+  if (order >= 0) v.order = order ? 1 : 0;
+  if (rpw >= 0) v.rpw = rpw == 8 ? 8 : 4;
+  if (u >= 0) v.unroll = (u == 2 || u == 8) ? u : 4;
+  return v;
 }
 
 // Workgroup order.  Measured on the narrow projections: walking a tile's chunks
@@ -296,9 +292,8 @@ hipError_t launch_t(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
   const int rows_per_wg = (WG / 64) * RPW;
   const int ntiles = (int)((N + rows_per_wg - 1) / rows_per_wg);
   const dim3 grid((unsigned)((int64_t)ntiles * splits)), block(WG);
-  hipLaunchKernelGGL((k_gemv_dot4<MODE, RPW, U, FUSED, QX>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs,
-                     x, N, K, splits, win, ntiles, chunk_major(splits), out, tickets, y);
-  return hipGetLastError();
+  return launch((k_gemv_dot4<MODE, RPW, U, FUSED, QX>), grid, block, (size_t)win * bpb, st, wq, ws, xq, xl, xs,
+                     x, N, K, splits, win, ntiles, chunk_major(splits), out, tickets, y, nullptr);
 }
 
 template <int MODE, bool FUSED, bool QX>
@@ -344,9 +339,8 @@ hipError_t launch_gemv_sk(int mode, const int8_t* wq, const uint16_t* ws, int64_
                           const int8_t* xl, const float* xs, int splits, float* y, void* workspace, hipStream_t st) {
   if (splits == 1) return launch_gemv_dot4(mode, wq, ws, N, K, xq, xl, xs, 1, y, st);
   // the chunks as waves of one workgroup, combined in LDS, where the activation
-  // fits (QDG_SK_WSPLIT=0 forces the workspace path; read on every call)
-  const char* e = getenv("QDG_SK_WSPLIT");
-  if (!(e && e[0] == '0') && wsplit_fits(mode, K, splits))
+  // fits (QDG_TUNE_SK_WSPLIT = 0 forces the workspace path)
+  if (tune(QDG_TUNE_SK_WSPLIT) != 0 && wsplit_fits(mode, K, splits))
     return launch_gemv_wsplit(mode, wq, ws, N, K, xq, xl, xs, splits, y, st);
   unsigned* tickets = (unsigned*)workspace;
   float* part = (float*)((char*)workspace + sk_partials_offset(N));
@@ -368,13 +362,15 @@ hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, in
     const int win = window_blocks(K, 1, mode == 1 ? bpb1 : bpb2);
     const int ntiles = (int)gemv_tiles(N);
     const dim3 grid((unsigned)ntiles), block(WG);
+    const float* nox = nullptr;
+    unsigned* not_ = nullptr;
+    float* noy = nullptr;
     if (mode == 1)
-      hipLaunchKernelGGL((k_gemv_dot4<1, 4, 4, false, false, true>), grid, block, (size_t)win * bpb1, st, wq, ws, xq,
-                         xl, xs, nullptr, N, K, 1, win, ntiles, 0, y, nullptr, nullptr, keys);
+      e = launch(k_gemv_dot4<1, 4, 4, false, false, true>, grid, block, (size_t)win * bpb1, st, wq, ws, xq, xl, xs,
+                 nox, N, K, 1, win, ntiles, 0, y, not_, noy, keys);
     else
-      hipLaunchKernelGGL((k_gemv_dot4<2, 4, 4, false, false, true>), grid, block, (size_t)win * bpb2, st, wq, ws, xq,
-                         xl, xs, nullptr, N, K, 1, win, ntiles, 0, y, nullptr, nullptr, keys);
-    e = hipGetLastError();
+      e = launch(k_gemv_dot4<2, 4, 4, false, false, true>, grid, block, (size_t)win * bpb2, st, wq, ws, xq, xl, xs,
+                 nox, N, K, 1, win, ntiles, 0, y, not_, noy, keys);
   }
   if (e != hipSuccess) return e;
   return launch_argmax_final(keys, 1, (int)gemv_tiles(N), idx, st);

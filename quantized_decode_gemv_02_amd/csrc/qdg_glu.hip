@@ -17,7 +17,6 @@
 // while each wave's first step groups of weights are in flight, when K is a
 // multiple of 256 and every staged array is 16-byte aligned; otherwise they are
 // copied through registers.
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -127,8 +126,7 @@ hipError_t launch_glu_s(const int8_t* wg, const uint16_t* sg, const int8_t* wu, 
   if (attr != hipSuccess) return attr;
   const size_t lds = (size_t)(K / QK) * gl_bytes_per_block<MODE>();
   const dim3 grid((unsigned)(F / 32)), block(GL_NT);
-  hipLaunchKernelGGL((k_gemv_glu<MODE, DMA>), grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
-  return hipGetLastError();
+  return launch((k_gemv_glu<MODE, DMA>), grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
 }
 
 // LDS DMA staging when K is a multiple of 256 and every staged array starts
@@ -139,7 +137,7 @@ hipError_t launch_glu_m(const int8_t* wg, const uint16_t* sg, const int8_t* wu, 
                         int8_t* hl, float* hs, hipStream_t st) {
   bool dma = K % 256 == 0 && (((uintptr_t)xq | (uintptr_t)xs | (uintptr_t)sg | (uintptr_t)su) & 15) == 0 &&
              (MODE == 1 || ((uintptr_t)xl & 15) == 0);
-  if (const char* e = getenv("QDG_WS_DMA")) dma = dma && e[0] != '0';
+  if (tune(QDG_TUNE_WS_DMA) == 0) dma = false;
   if (dma) return launch_glu_s<MODE, true>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
   return launch_glu_s<MODE, false>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
 }

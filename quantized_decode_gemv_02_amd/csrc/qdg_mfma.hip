@@ -36,8 +36,6 @@
 //    -P, so the compiler's wait counts keep the look-ahead in flight.
 //  * Weight rows past N read row N-1 and store nothing; activation rows t >= B
 //    read row B-1 and store nothing (an MFMA row never mixes into another).
-#include <stdio.h>
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -239,9 +237,8 @@ template <int MODE, int P, bool WIDE>
 hipError_t launch_mg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
                      const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
   const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)splits), block(WG);
-  hipLaunchKernelGGL((k_gemv_mfma<MODE, P, WIDE>), grid, block, lds_bytes<MODE>(), st, wq, ws, xq, xl, xs, N, K,
+  return launch((k_gemv_mfma<MODE, P, WIDE>), grid, block, lds_bytes<MODE>(), st, wq, ws, xq, xl, xs, N, K,
                      (int)B, splits, out);
-  return hipGetLastError();
 }
 
 template <int MODE, int P>
@@ -551,29 +548,23 @@ hipError_t launch_dma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K
   static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_dma<MODE, WV, TPW, P, AT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gemv_mfma_dma<MODE, WV, TPW, P, AT>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K,
+  return launch((k_gemv_mfma_dma<MODE, WV, TPW, P, AT>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K,
                      (int)B, splits, out);
-  return hipGetLastError();
 }
 
-// Fast-path shape (read once): QDG_MFMA_SHAPE = "WV,TPW,P" among the compiled
+// Fast-path shape: QDG_TUNE_MFMA_SHAPE = 100*WV + 10*TPW + P among the compiled
 // ones -- 4,4,2 (the default), 4,4,3, 4,2,2, 8,2,3.  On 25600x5120, B = 16:
 // 4,4,2 streams 4.30 / 3.96 TB/s (Int8Act / TwoPass), 8,2,3 4.27 / 3.73,
 // 4,4,3 4.06 / 3.80, 4,2,3 3.73 / 3.24.
 struct DmaShape {
   int wv, tpw, ring;
 };
-DmaShape dma_shape() {
-  static const DmaShape d = [] {
-    DmaShape v{4, 4, 2};
-    if (const char* e = getenv("QDG_MFMA_SHAPE")) {
-      DmaShape t{0, 0, 0};
-      if (sscanf(e, "%d,%d,%d", &t.wv, &t.tpw, &t.ring) == 3) v = t;
-    }
-    return v;
-  }();
-  return d;
+DmaShape shape_knob(int knob, DmaShape def) {
+  const int v = tune(knob);
+  if (v < 0) return def;
+  return DmaShape{v / 100, (v / 10) % 10, v % 10};
 }
+DmaShape dma_shape() { return shape_knob(QDG_TUNE_MFMA_SHAPE, DmaShape{4, 4, 2}); }
 
 template <int MODE>
 hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
@@ -581,9 +572,9 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
   // more than 16 activation rows: 2 or 4 activation tiles against each weight
   // step (the fast path's layout; the caller has checked its conditions)
   if (B > 16) {
-    // QDG_MFMA_WIDE = "WV,TPW,P" among the compiled shapes (read on every call, for sweeps)
-    int wv = 8, tpw = 2, ring = 2;
-    if (const char* e = getenv("QDG_MFMA_WIDE")) sscanf(e, "%d,%d,%d", &wv, &tpw, &ring);
+    // QDG_TUNE_MFMA_WIDE = 100*WV + 10*TPW + P among the compiled shapes (for sweeps)
+    const DmaShape wide = shape_knob(QDG_TUNE_MFMA_WIDE, DmaShape{8, 2, 2});
+    const int wv = wide.wv, tpw = wide.tpw, ring = wide.ring;
 #define QDG_WIDE(WV_, TPW_, P_)                                                                   \
   if (wv == WV_ && tpw == TPW_ && ring == P_) {                                                    \
     if (B <= 32) return launch_dma<MODE, WV_, TPW_, P_, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st); \
@@ -598,7 +589,7 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
     return launch_dma<MODE, 8, 2, 2, 4>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
   }
   // the fast path needs whole steps (K/32 a multiple of 8) and 16-byte weight-scale words
-  if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && !getenv("QDG_MFMA_GENERAL")) {
+  if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && tune(QDG_TUNE_MFMA_GENERAL) != 1) {
     const DmaShape d = dma_shape();
 #define QDG_DMA(WV_, TPW_, P_)                   \
   if (d.wv == WV_ && d.tpw == TPW_ && d.ring == P_) \

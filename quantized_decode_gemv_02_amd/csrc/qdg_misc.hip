@@ -141,14 +141,12 @@ __global__ __launch_bounds__(256) void k_stream_read(const int4* __restrict__ bu
 hipError_t launch_stream_read(const void* buf, int64_t bytes, unsigned* sink, hipStream_t st) {
   const int64_t nwords = bytes / 16;
   const dim3 grid((unsigned)((bytes + SLAB - 1) / SLAB)), block(256);
-  hipLaunchKernelGGL(k_stream_read, grid, block, 0, st, (const int4*)buf, nwords, sink);
-  return hipGetLastError();
+  return launch(k_stream_read, grid, block, 0, st, (const int4*)buf, nwords, sink);
 }
 
 hipError_t launch_combine(const float* part, int splits, int64_t count, float* y, hipStream_t st) {
   const dim3 grid((unsigned)((count + 255) / 256)), block(256);
-  hipLaunchKernelGGL(k_combine, grid, block, 0, st, part, splits, count, y);
-  return hipGetLastError();
+  return launch(k_combine, grid, block, 0, st, part, splits, count, y);
 }
 
 int argmax_groups(int64_t N) {
@@ -162,25 +160,21 @@ hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, uns
                          hipStream_t st) {
   const int G = argmax_groups(N);
   const int64_t per = (N + G - 1) / G;
-  hipLaunchKernelGGL(k_argmax_part, dim3((unsigned)G, (unsigned)B), dim3(AM_THREADS), 0, st, y, N, per, ws);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch(k_argmax_part, dim3((unsigned)G, (unsigned)B), dim3(AM_THREADS), 0, st, y, N, per, ws);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, ws, G, idx);
-  return hipGetLastError();
+  return launch(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, ws, G, idx);
 }
 
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, keys, G, idx);
-  return hipGetLastError();
+  return launch(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, keys, G, idx);
 }
 
 hipError_t launch_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq,
                              const int8_t* xl, int64_t B, int32_t* dh, int32_t* dl, hipStream_t st) {
   const int64_t nb = K / QK;
   const dim3 grid((unsigned)((nb + 31) / 32), (unsigned)N, (unsigned)B), block(64);
-  hipLaunchKernelGGL(k_block_dots, grid, block, 0, st, wq, N, K, xq, mode == 2 ? xl : nullptr, dh,
+  return launch(k_block_dots, grid, block, 0, st, wq, N, K, xq, mode == 2 ? xl : nullptr, dh,
                      mode == 2 ? dl : nullptr);
-  return hipGetLastError();
 }
 
 }  // namespace qdg

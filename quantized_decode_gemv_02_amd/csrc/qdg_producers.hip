@@ -151,8 +151,7 @@ hipError_t launch_rms(const float* x, const float* r, float* s, const float* w, 
   const int64_t per = (K / 4 + NT - 1) / NT;
   const dim3 grid((unsigned)B), block(NT);
 #define QDG_RMS(P, KEEP)                                                                                      \
-  hipLaunchKernelGGL((k_rmsnorm_quant<MODE, P, KEEP>), grid, block, 0, st, x, r, s, w, eps, K, y, xq, xl, xs); \
-  return hipGetLastError();
+  return launch((k_rmsnorm_quant<MODE, P, KEEP>), grid, block, 0, st, x, r, s, w, eps, K, y, xq, xl, xs);
   if (per <= 1) { QDG_RMS(1, true) }
   if (per <= 2) { QDG_RMS(2, true) }
   if (per <= 4) { QDG_RMS(4, true) }
@@ -165,8 +164,7 @@ hipError_t launch_swiglu_m(const float* g, const float* u, int64_t nblocks, floa
                            float* xs, hipStream_t st) {
   const int64_t threads = nblocks * 8;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  hipLaunchKernelGGL(k_swiglu_quant<MODE>, grid, block, 0, st, g, u, h, xq, xl, xs, nblocks);
-  return hipGetLastError();
+  return launch(k_swiglu_quant<MODE>, grid, block, 0, st, g, u, h, xq, xl, xs, nblocks);
 }
 
 }  // namespace

@@ -40,10 +40,9 @@ hipError_t launch_quantize(int mode, const float* x, int64_t nblocks, int8_t* xq
   const int64_t threads = nblocks * 8;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (mode == 1)
-    hipLaunchKernelGGL(k_quantize<1>, grid, block, 0, st, x, xq, xl, xs, nblocks);
+    return launch(k_quantize<1>, grid, block, 0, st, x, xq, xl, xs, nblocks);
   else
-    hipLaunchKernelGGL(k_quantize<2>, grid, block, 0, st, x, xq, xl, xs, nblocks);
-  return hipGetLastError();
+    return launch(k_quantize<2>, grid, block, 0, st, x, xq, xl, xs, nblocks);
 }
 
 }  // namespace qdg

@@ -28,7 +28,6 @@
 // below).  A row group's four rows are one tile row, so each weight request of
 // a wave reads one contiguous KiB and a chunk wave streams one contiguous range;
 // the terms, their order and the result are those of the plain layout.
-#include <stdlib.h>
 
 #include "qdg_device.h"
 
@@ -175,8 +174,7 @@ hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const in
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
   const size_t lds = ws_lds_bytes<MODE, R>(K);
-  hipLaunchKernelGGL((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
-  return hipGetLastError();
+  return launch((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
 }
 
 // The staging: per-wave copies when a row group is the whole workgroup (each
@@ -188,15 +186,15 @@ hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const in
 //     rows by 2-8% and lose on the 8192-value rows by 4-8%;
 //   - with the copy, per-wave staging was 4% faster with one row group and 1-6%
 //     slower with two or four.
-// QDG_WS_LOCAL=1 forces the per-wave copies, QDG_WS_LOCAL=0 the workgroup-wide
-// staging; QDG_WS_DMA=0 turns the DMA off (both read on every call).
+// QDG_TUNE_WS_LOCAL = 1 forces the per-wave copies, 0 the workgroup-wide
+// staging; QDG_TUNE_WS_DMA = 0 turns the DMA off.
 int ws_stage(int R, const PartTable& tab, int64_t K, int mode, const int8_t* xq, const int8_t* xl, const float* xs) {
   bool dma = K % 256 == 0 && ((uintptr_t)xq & 15) == 0 && ((uintptr_t)xs & 15) == 0 &&
              (mode == 1 || ((uintptr_t)xl & 15) == 0);
   for (int p = 0; p < tab.n; ++p) dma = dma && ((uintptr_t)tab.ws[p] & 15) == 0;
-  if (const char* e = getenv("QDG_WS_DMA")) dma = dma && e[0] != '0';
-  const char* loc = getenv("QDG_WS_LOCAL");
-  if (loc ? loc[0] == '1' : R == 1) return WS_LOCAL;
+  if (tune(QDG_TUNE_WS_DMA) == 0) dma = false;
+  const int loc = tune(QDG_TUNE_WS_LOCAL);
+  if (loc >= 0 ? loc == 1 : R == 1) return WS_LOCAL;
   return dma ? WS_DMA : WS_BARRIER;
 }
 
@@ -204,10 +202,10 @@ int ws_stage(int R, const PartTable& tab, int64_t K, int mode, const int8_t* xq,
 // Measured on the 5120-row projections over R = 1..4 and S = 2, 4, 5, 8: three
 // groups (427 workgroups, one round at two workgroups a CU) is the fastest or
 // within 1% of it in every case, and four is 7-20% slower than three.
-// QDG_WS_ROWS (1..4) overrides (read on every call).
+// QDG_TUNE_WS_ROWS (1..4) overrides.
 int ws_groups(int ceff) {
   int R = 3 * ceff <= 16 ? 3 : 16 / ceff;
-  if (const char* e = getenv("QDG_WS_ROWS")) R = atoi(e);
+  if (tune(QDG_TUNE_WS_ROWS) > 0) R = tune(QDG_TUNE_WS_ROWS);
   if (R > 4) R = 4;
   if (R < 1) R = 1;
   while (R > 1 && R * ceff > 16) --R;
@@ -297,8 +295,7 @@ hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, 
   const int64_t n16 = N * K / 16;
   const int64_t blocks = (n16 + 255) / 256;
   const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
-  hipLaunchKernelGGL(k_tile_rows, dim3(grid), dim3(256), 0, st, wq, K, n16, wt);
-  return hipGetLastError();
+  return launch(k_tile_rows, dim3(grid), dim3(256), 0, st, wq, K, n16, wt);
 }
 
 }  // namespace qdg

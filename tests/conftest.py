@@ -18,3 +18,18 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return GOLDEN
+
+
+@pytest.fixture
+def tune():
+    """Sets the library's tuning knobs for one test (``tune(ws_dma=0)``); every knob is back at
+    the library's own choice afterwards, so no test leaks a setting into the next."""
+    import quantized_decode_gemv_02_amd as q
+
+    def set_knobs(**knobs):
+        for k, v in knobs.items():
+            q.set_tuning(k, v)
+
+    yield set_knobs
+    for k in q.TUNE:
+        q.set_tuning(k, -1)

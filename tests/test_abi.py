@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 26
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -382,3 +382,66 @@ def test_tiled_layout_validation():
     assert sk(mode=2, xl=A, K=32768, S=5) == EMODE  # the staged row exceeds the LDS budget
     assert sk(wt=A + 4) == EALIGN
     assert sk(xs=A + 2) == EALIGN
+
+
+def test_tuning_knobs():
+    """The tuning hooks start at the library's own choice (-1), never read the
+    environment, reject unknown knobs, and the binding's context manager puts
+    every knob back."""
+    for k in range(14):
+        assert lib.qdg_get_tuning(k) == -1, k
+    assert lib.qdg_get_tuning(14) == EINVAL
+    assert lib.qdg_get_tuning(-1) == EINVAL
+    assert lib.qdg_set_tuning(14, 0) == EINVAL
+    assert lib.qdg_set_tuning(2, 1) == OK and lib.qdg_get_tuning(2) == 1
+    assert lib.qdg_set_tuning(2, -7) == OK and lib.qdg_get_tuning(2) == -1
+    with q.tuning(ws_dma=0, ws_local=1):
+        assert q.get_tuning("ws_dma") == 0 and q.get_tuning("ws_local") == 1
+        with q.tuning(ws_local=0):
+            assert q.get_tuning("ws_local") == 0
+        assert q.get_tuning("ws_local") == 1
+    assert q.get_tuning("ws_dma") == -1 and q.get_tuning("ws_local") == -1
+    assert sorted(q.TUNE.values()) == list(range(14))
+    assert lib.qdg_time_next_launch(None, None) == OK
+
+
+def test_knobs_ignore_the_environment():
+    """A process whose environment names the old variables still starts with every knob at -1
+    and the same in-workgroup placement."""
+    import subprocess
+    import sys
+    code = ("import quantized_decode_gemv_02_amd as q\n"
+            "print([q.get_tuning(k) for k in q.TUNE], q.sk_workgroup_shape(2, 25600, 5))\n")
+    env = dict(os.environ, QDG_WS_ROWS="1", QDG_SK_WSPLIT="0", QDG_WS_DMA="0", QDG_MFMA_GENERAL="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == str([-1] * 14) + " (12, 15)", r.stdout
+
+
+def test_binding_checks_sizes_before_the_call():
+    """Undersized buffers raise ValueError on the host, before any pointer reaches the library."""
+    torch = pytest.importorskip("torch")
+    N, K = 8, 512
+    w = torch.zeros((N, K), dtype=torch.int8)
+    ws = torch.zeros((N, K // 32), dtype=torch.int16)
+    xq, xl = torch.zeros((1, K), dtype=torch.int8), torch.zeros((1, K), dtype=torch.int8)
+    xs, y = torch.zeros((1, K // 32)), torch.zeros((1, N))
+    wsp = torch.zeros(64, dtype=torch.int64)
+    cases = [
+        lambda: q.gemv_q8_sk(q.TWOPASS, w, ws, torch.zeros(N - 1), xq, xl, xs, 4, wsp),
+        lambda: q.gemv_q8_sk(q.TWOPASS, w, torch.zeros((N, K // 64), dtype=torch.int16), y, xq, xl, xs, 4, wsp),
+        lambda: q.gemv_q8_sk(q.TWOPASS, w, ws, y, xq[:, :K - 32].contiguous(), xl, xs, 4, wsp),
+        lambda: q.gemv_q8_sk(q.TWOPASS, w, ws, y, xq, xl[:, :16].contiguous(), xs, 4, wsp),
+        lambda: q.gemv_q8_sk(q.TWOPASS, w, ws, y, xq, xl, xs[:, :3].contiguous(), 4, wsp),
+        lambda: q.gemv_q8_sk_tiled(q.INT8ACT, w, ws, torch.zeros(4), xq, None, xs, 4),
+        lambda: q.bind_gemv_q8_sk(q.INT8ACT, w, ws, torch.zeros(3), xq, None, xs, 4, wsp),
+        lambda: q.bind_gemv_q8_sk_tiled(q.INT8ACT, w, ws, y, xq, None, xs[:, :1].contiguous(), 4),
+        lambda: q.gemv_q8(q.INT8ACT, w, ws, torch.zeros((3, 1, N)), xq=xq, xs=xs, splits=4),
+        lambda: q.gemv_q8_fused(q.INT8ACT, w, ws, y, torch.zeros((1, K - 32)), 4, wsp),
+        lambda: q.quantize_act(q.TWOPASS, torch.zeros((1, K)), xq, xl[:, :8].contiguous(), xs),
+        lambda: q.gemv_q8_argmax(q.INT8ACT, w, ws, torch.zeros(N - 2), torch.zeros(1, dtype=torch.int32), wsp,
+                                 xq=xq, xs=xs),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(ValueError, match="holds|ws must"):
+            c()

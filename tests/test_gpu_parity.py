@@ -228,9 +228,9 @@ def test_weight_scales_at_a_two_byte_offset(mode, B):
 
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B,N,K,S", [(16, 100, 5120, 1), (7, 64, 2048, 2), (16, 33, 256, 2)])
-def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, monkeypatch):
+def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, tune):
     """Shapes with K a multiple of 256 take the LDS-direct batched kernel; the
-    general kernel (forced by QDG_MFMA_GENERAL) must give the same bits there."""
+    general kernel (forced by the mfma_general tuning knob) must give the same bits there."""
     announce(f"batched general path mode={mode} B={B} N={N} K={K} S={S}")
     wq, ws, x = _quant_case(N, K, B, 9 * B + N + K)
     oq, ol, os_ = oracle.quantize(mode, x)
@@ -239,7 +239,7 @@ def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, monkeypatch)
     xq, xl, xs = quantize_gpu(mode, x)
     wqd, wsd = dev(wq), dev(ws)
     fast = host(gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs))
-    monkeypatch.setenv("QDG_MFMA_GENERAL", "1")
+    tune(mfma_general=1)
     general = host(gemv_gpu(mode, wqd, wsd, B, N, splits=S, xq=xq, xl=xl, xs=xs))
     np.testing.assert_array_equal(fast, want)
     np.testing.assert_array_equal(general, want)
@@ -249,10 +249,10 @@ def test_batched_general_path_on_fast_path_shapes(mode, B, N, K, S, monkeypatch)
 
 @pytest.mark.parametrize("N,K", [(256, 512), (1, 32), (37, 1600), (64, 12288), (20, 5120), (5, 25600)])
 @pytest.mark.parametrize("kernel", ["chunk-waves", "workspace"])
-def test_dequant_tolerance(N, K, kernel, monkeypatch):
+def test_dequant_tolerance(N, K, kernel, tune):
     announce(f"dequant N={N} K={K} {kernel}")
     if kernel == "workspace":
-        monkeypatch.setenv("QDG_DQ_SEG", "0")
+        tune(dq_seg=0)
     wq, ws, x = _quant_case(N, K, 1, N + 3 * K, outliers=True)
     y = host(gemv_gpu(0, dev(wq), dev(ws), 1, N, x=dev(x)))
     Y, tn = oracle.reference_f64(0, wq, ws, x=x)
@@ -335,10 +335,10 @@ def test_repeat_and_fresh_buffers_bitwise():
 @pytest.mark.parametrize("N,K,S", [(256, 512, 1), (100, 25600, 8), (33, 1600, 4), (70, 8192, 3), (9, 256, 2),
                                    (17, 1600, 64), (129, 4096, 1), (1, 32, 1), (5, 544, 5), (5120, 8192, 4)])
 @pytest.mark.parametrize("path", ["default", "workspace"])
-def test_in_kernel_combine_bit_exact(mode, N, K, S, path, monkeypatch):
+def test_in_kernel_combine_bit_exact(mode, N, K, S, path, tune):
     announce(f"gemv_q8_sk mode={mode} N={N} K={K} S={S} {path}")
     if path == "workspace":
-        monkeypatch.setenv("QDG_SK_WSPLIT", "0")
+        tune(sk_wsplit=0)
     wq, ws, x = _quant_case(N, K, 1, 11 * N + K + S, outliers=True)
     oq, ol, os_ = oracle.quantize(mode, x)
     want = oracle.combine(oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=8))
@@ -361,18 +361,18 @@ def test_in_kernel_combine_bit_exact(mode, N, K, S, path, monkeypatch):
                                    # the largest TwoPass rows the LDS budget takes (three, two, one row groups)
                                    (24, 28128, 5), (24, 30720, 8), (8, 34048, 16)])
 @pytest.mark.parametrize("variant", ["dma", "barrier", "wave-local"])
-def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
+def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, tune):
     """The split-K GEMV whose chunks are the waves of one workgroup (partials
     combined in LDS) against the oracle's chunk partials and ascending combine,
     with each staging of the activation: LDS DMA (K a multiple of 256; other K
     fall back to the workgroup copy), the workgroup-wide copy, the per-wave copy."""
     announce(f"gemv_q8_sk in-workgroup split mode={mode} N={N} K={K} S={S} {variant}")
     if variant == "dma":
-        monkeypatch.delenv("QDG_WS_DMA", raising=False)
-        monkeypatch.setenv("QDG_WS_LOCAL", "0")
+        tune(ws_dma=-1)
+        tune(ws_local=0)
     else:
-        monkeypatch.setenv("QDG_WS_DMA", "0")
-        monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
+        tune(ws_dma=0)
+        tune(ws_local=1 if variant == "wave-local" else 0)
     wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
     oq, ol, os_ = oracle.quantize(mode, x)
     if N > 1000:  # the oracle on every 7th row (the rows are independent)
@@ -387,7 +387,7 @@ def test_in_workgroup_split_bit_exact(mode, N, K, S, variant, monkeypatch):
         y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
         q.gemv_q8_sk(mode, wqd, wsd, y, xq, xl, xs, S, wsp)
         np.testing.assert_array_equal(host(y)[:, rows], want)
-    monkeypatch.setenv("QDG_SK_WSPLIT", "0")  # the workspace path: the same bits
+    tune(sk_wsplit=0)  # the workspace path: the same bits
     y2 = torch.empty((1, N), dtype=torch.float32, device=DEV)
     q.gemv_q8_sk(mode, wqd, wsd, y2, xq, xl, xs, S, wsp)
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
@@ -440,17 +440,17 @@ def test_tile_rows_bit_exact(N, K):
                                    (40, 25600, 5), (100, 8192, 4), (4, 1024, 2), (12, 768, 3), (36, 1280, 5),
                                    (24, 27904, 5), (8, 33792, 16), (64, 4608, 2)])
 @pytest.mark.parametrize("variant", ["dma", "barrier", "wave-local"])
-def test_in_workgroup_split_tiled_bit_exact(mode, N, K, S, variant, monkeypatch):
+def test_in_workgroup_split_tiled_bit_exact(mode, N, K, S, variant, tune):
     """The in-workgroup split-K GEMV over row-tiled weights: the oracle's chunk
     partials and ascending combine bit for bit, and the plain-layout call's bits,
     with each staging of the activation (the weight addressing is the same in all)."""
     announce(f"gemv_q8_sk_tiled mode={mode} N={N} K={K} S={S} {variant}")
     if variant == "dma":
-        monkeypatch.delenv("QDG_WS_DMA", raising=False)
-        monkeypatch.setenv("QDG_WS_LOCAL", "0")
+        tune(ws_dma=-1)
+        tune(ws_local=0)
     else:
-        monkeypatch.setenv("QDG_WS_DMA", "0")
-        monkeypatch.setenv("QDG_WS_LOCAL", "1" if variant == "wave-local" else "0")
+        tune(ws_dma=0)
+        tune(ws_local=1 if variant == "wave-local" else 0)
     assert q.sk_combines_in_workgroup(mode, K, S)
     wq, ws, x = _quant_case(N, K, 1, 23 * N + K + S, outliers=True)
     oq, ol, os_ = oracle.quantize(mode, x)
@@ -516,13 +516,13 @@ def test_fused_single_launch_dequant_and_edge_inputs():
 
 @pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7)])
 @pytest.mark.parametrize("kernel", ["chunk-waves", "workspace"])
-def test_fused_dequant_split_k(N, K, S, kernel, monkeypatch):
+def test_fused_dequant_split_k(N, K, S, kernel, tune):
     """Dequant split-K (binary64 chunk partials, ascending binary64 combine, one
     rounding): within the Dequant tolerance of the binary64 reference, and almost
     always the oracle's own binary32 result."""
     announce(f"gemv_q8_fused dequant N={N} K={K} S={S} {kernel}")
     if kernel == "workspace":
-        monkeypatch.setenv("QDG_DQ_SEG", "0")
+        tune(dq_seg=0)
     wq, ws, x = _quant_case(N, K, 1, 17 * N + K + S, outliers=True)
     Y, tn = oracle.reference_f64(0, wq, ws, x=x, nthreads=8)
     want32 = oracle.gemv(0, wq, ws, x=x, nthreads=8)
@@ -540,13 +540,13 @@ def test_fused_dequant_split_k(N, K, S, kernel, monkeypatch):
 @pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7),
                                    (5120, 25600, 5), (300, 25600, 1), (1, 32, 1), (130, 12288, 8), (21, 4608, 3)])
 @pytest.mark.parametrize("variant", ["R1", "R2", "R3", "R4"])
-def test_dequant_chunk_waves(N, K, S, variant, monkeypatch):
+def test_dequant_chunk_waves(N, K, S, variant, tune):
     """The Dequant GEMV whose chunks are waves of one workgroup (8 values a lane,
     binary64 throughout, chunk partials added in LDS): within the Dequant
     tolerance of the binary64 reference, almost always the oracle's binary32
     result, and bit-identical on repeat."""
     announce(f"dequant chunk waves N={N} K={K} S={S} {variant}")
-    monkeypatch.setenv("QDG_DQ_ROWS", variant[1])
+    tune(dq_rows=int(variant[1]))
     wq, ws, x = _quant_case(N, K, 1, 23 * N + K + S, outliers=True)
     rows = np.arange(0, N, 7) if N > 1000 else np.arange(N)
     Y, tn = oracle.reference_f64(0, wq[rows], ws[rows], x=x, nthreads=8)

@@ -232,17 +232,26 @@ def test_producer_words_drive_the_gemv(mode):
 @pytest.mark.parametrize("F,K", [(32, 32), (64, 544), (12288, 4096), (96, 13184), (160, 15776), (64, 256),
                                  (96, 12800)])
 @pytest.mark.parametrize("staging", ["default", "copy"])
-def test_glu_matches_the_three_calls(mode, F, K, staging, monkeypatch):
+def test_glu_matches_the_three_calls(mode, F, K, staging, tune):
     """qdg_gemv_glu_q8 (gate and up GEMVs with the SwiGLU and quantizer epilogue)
     against two qdg_gemv_q8 calls and qdg_swiglu_quantize, bit for bit, and the
     oracle: g and u bit-exact, h within one ulp, words bit-exact on the kernel's h.
     "default" stages by LDS DMA where K is a multiple of 256, "copy" through registers."""
     if mode == 2 and K > 13184:
-        pytest.skip("the TwoPass activation row and scales exceed the LDS budget at this K")
+        # the TwoPass activation row and 64 rows of scales exceed the LDS budget: the call is
+        # refused before anything is enqueued
+        xq, xl, xs = words(mode, 1, K)
+        hq, hl, hs = words(mode, 1, F)
+        w0 = torch.zeros((F, K), dtype=torch.int8, device=DEV)
+        s0 = torch.zeros((F, K // 32), dtype=torch.int16, device=DEV)
+        with pytest.raises(q.QdgError) as err:
+            q.gemv_glu_q8(mode, w0, s0, w0, s0, xq, xl, xs, hq, hl, hs)
+        assert err.value.status == -4  # QDG_EMODE
+        return
     if staging == "copy":
-        monkeypatch.setenv("QDG_WS_DMA", "0")
+        tune(ws_dma=0)
     else:
-        monkeypatch.delenv("QDG_WS_DMA", raising=False)
+        tune(ws_dma=-1)
     announce(f"gemv_glu mode={mode} F={F} K={K} {staging}")
     wg, sg = workloads.weights(F, K, 71 + K, 72 + K)
     wu, su = workloads.weights(F, K, 73 + K, 74 + K)
