@@ -173,9 +173,11 @@ size_t qdg_gemv_sk_workspace_bytes(int64_t B, int64_t N, int splits);
  * chunk finishes last changes nothing.  Inputs as
  * qdg_gemv_q8 (xq, xl, xs from qdg_quantize_act); workspace: device memory of at
  * least qdg_gemv_sk_workspace_bytes(1, N, splits) bytes, 256-byte aligned and
- * zero-filled before its first use; every call that completes leaves its tickets
- * zero again, so it needs no clearing between calls.  Calls that share a
- * workspace must not overlap in time (one stream, or events between them).
+ * zero-filled before its first use; every call that completes leaves all of it
+ * zero again (the tickets and the partial slots, which the last arriver reads
+ * until it finds them published, then clears), so it needs no clearing between
+ * calls.  Calls that share a workspace must not overlap in time (one stream, or
+ * events between them).
  */
 int qdg_gemv_q8_sk(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
                    const int8_t *xq, const int8_t *xl, const float *xs, int64_t B, int splits,

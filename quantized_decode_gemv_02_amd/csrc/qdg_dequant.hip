@@ -223,26 +223,21 @@ __global__ __launch_bounds__(WG) void k_gemv_dequant(const int8_t* __restrict__ 
     if (li == 0 && row_ok) out[o] = (float)y;
     return;
   }
-  // Publish the chunk's partial and let the tile's last workgroup combine, under
-  // the HIP memory model: each writer's store, then an agent-scope release fence,
-  // the barrier, one agent-scope acq_rel ticket RMW, the barrier, and an
-  // agent-scope acquire fence in every reader before its loads.
-  if (li == 0 && row_ok)
-    __hip_atomic_store(part + (int64_t)blockIdx.y * N + o, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Hand the chunk's binary64 partial to the tile's last-arriving workgroup
+  // (publish_partial / take_partial: marked slots, all accesses atomic).
+  unsigned long long* slots = (unsigned long long*)part;
+  if (li == 0 && row_ok) publish_partial(slots + (int64_t)blockIdx.y * N + o, y);
   __syncthreads();
   __shared__ int last_arrival;
   if (threadIdx.x == 0)
-    last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+    last_arrival = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(S - 1);
   __syncthreads();
   if (!last_arrival) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
     const int64_t oo = o_wg + threadIdx.x;
     double a = 0.0;
-    for (int s = 0; s < S; ++s)
-      a = __dadd_rn(a, __hip_atomic_load(part + (int64_t)s * N + oo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    for (int s = 0; s < S; ++s) a = __dadd_rn(a, take_partial(slots + (int64_t)s * N + oo));
     out[oo] = (float)a;
   }
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

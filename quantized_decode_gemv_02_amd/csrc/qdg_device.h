@@ -159,6 +159,41 @@ __device__ __forceinline__ unsigned long long amax_key(float v, unsigned idx) {
   return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - idx);
 }
 
+// Split-K partials handed to the last-arriving workgroup of a row tile.  A slot
+// holds the partial's bits XOR a signalling-NaN pattern: no arithmetic result is
+// a signalling NaN, so no published slot is zero, and a zero slot means "not yet
+// published".  Every access to a slot (and to the tile's ticket) is an
+// agent-scope atomic, so nothing races; the result does not rest on the order in
+// which another workgroup's stores become visible: the last arriver waits,
+// boundedly, until each slot it adds is nonzero, then clears it for the next
+// call (the workspace is zero-filled before its first use).  Were the bound ever
+// reached, the stale zero decodes to the pattern itself, a NaN in the output.
+constexpr unsigned PART_MARK32 = 0x7f80deadu;                 // binary32 signalling NaN
+constexpr unsigned long long PART_MARK64 = 0x7ff0deadbeef0001ull;  // binary64 signalling NaN
+constexpr int PART_SPIN_LIMIT = 1 << 22;
+
+__device__ __forceinline__ void publish_partial(unsigned* slot, float v) {
+  __hip_atomic_store(slot, __float_as_uint(v) ^ PART_MARK32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_partial(unsigned long long* slot, double v) {
+  __hip_atomic_store(slot, (unsigned long long)__double_as_longlong(v) ^ PART_MARK64, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T take_slot(T* slot) {
+  T v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int spin = 0; v == 0 && spin < PART_SPIN_LIMIT; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_store(slot, (T)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+__device__ __forceinline__ float take_partial(unsigned* slot) { return __uint_as_float(take_slot(slot) ^ PART_MARK32); }
+__device__ __forceinline__ double take_partial(unsigned long long* slot) {
+  return __longlong_as_double((long long)(take_slot(slot) ^ PART_MARK64));
+}
+
 // One quantized step's factors (lane kernel library page, lk_q8_term):
 // Int8Act a = fl(sigma*s), b = D; TwoPass a = sigma, b = fma(s, D, fl(fl(s/128)*E)).
 template <int MODE>

@@ -213,29 +213,23 @@ __global__ __launch_bounds__(WG) void k_gemv_dot4(const int8_t* __restrict__ wq,
       if (li == 0 && row_ok) y[o] = yv;
       return;
     }
-    // Publish the partials under the HIP memory model: every writer's partial
-    // store is followed by an agent-scope release fence before the workgroup
-    // barrier; one thread then takes the ticket with an agent-scope acq_rel RMW
-    // (releasing the workgroup's partials to the tile's other workgroups and, in
-    // the last arriver, acquiring theirs); after the second barrier every reader
-    // takes an agent-scope acquire fence before it loads the partials.  Which
-    // chunk arrives last changes nothing in the sum.
-    if (li == 0 && row_ok)
-      __hip_atomic_store(out + (int64_t)s_idx * N + o, yv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Hand the partials to the tile's last-arriving workgroup (publish_partial /
+    // take_partial: marked slots, all accesses atomic, no ordering assumed).  The
+    // barrier only makes the ticket come after the workgroup's own stores are
+    // issued; which chunk arrives last changes nothing in the sum.
+    unsigned* slots = (unsigned*)out;
+    if (li == 0 && row_ok) publish_partial(slots + (int64_t)s_idx * N + o, yv);
     __syncthreads();
     __shared__ int last_arrival;
     if (threadIdx.x == 0)
-      last_arrival = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_arrival = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      (unsigned)(S - 1);
     __syncthreads();
     if (!last_arrival) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (threadIdx.x < ROWS && o_wg + threadIdx.x < N) {
       const int64_t oo = o_wg + threadIdx.x;
       float a = 0.0f;
-      for (int s = 0; s < S; ++s)
-        a = __fadd_rn(a, __hip_atomic_load(out + (int64_t)s * N + oo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      for (int s = 0; s < S; ++s) a = __fadd_rn(a, take_partial(slots + (int64_t)s * N + oo));
       y[oo] = a;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
