@@ -10,8 +10,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers named as device pointers are HIP device memory the caller owns.
- *    The library allocates nothing, keeps no pointer after it returns, and keeps
- *    no state besides the thread-local error code of qdg_last_hip_error().
+ *    The library allocates no device memory per call and keeps no pointer to a
+ *    caller's buffer after it returns.  Its state: the thread-local error code
+ *    of qdg_last_hip_error() and event binding of qdg_time_next_launch(), the
+ *    process-wide tuning knobs (qdg_set_tuning), and, once
+ *    qdg_gemv_q8_argmax_noalloc has run on a GPU, that GPU's 1 MiB key array.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *    runs asynchronously; nothing synchronises.
  *  - Every argument is checked before anything is enqueued.  A negative status
@@ -239,6 +242,24 @@ int qdg_gemv_q8_argmax(int mode, const int8_t *wq, const uint16_t *ws, int64_t N
                        const float *x, const int8_t *xq, const int8_t *xl, const float *xs,
                        float *y, int32_t *idx, void *workspace, size_t workspace_bytes,
                        qdg_stream stream);
+
+/*
+ * qdg_gemv_q8_argmax without a caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same launches, logits and index as
+ * qdg_gemv_q8_argmax, with the per-tile arg-max keys in a 1 MiB array that the
+ * library holds on each GPU it runs on (taken at the first call on a device,
+ * kept until the process ends; nothing is allocated per call).  N up to
+ * 2,097,152 rows (131072 keys); larger N returns QDG_EWORKSPACE before anything
+ * is enqueued.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (two streams, or two threads) race on it: order
+ * them.  The array needs no clearing: each call writes every key it reads.  The
+ * stream must belong to the current device.  Other arguments, checks and
+ * statuses as qdg_gemv_q8_argmax.
+ */
+int qdg_gemv_q8_argmax_noalloc(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                               const float *x, const int8_t *xq, const int8_t *xl, const float *xs,
+                               float *y, int32_t *idx, qdg_stream stream);
 
 /*
  * The residual add and RMSNorm, then the activation quantizer, in one launch:

@@ -81,6 +81,7 @@ _SIGS = {
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
+    "qdg_gemv_q8_argmax_noalloc": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_set_tuning": ([_I, _I], _I),
     "qdg_get_tuning": ([_I], _I),
     "qdg_time_next_launch": ([_P, _P], _I),
@@ -457,6 +458,17 @@ def bind_gemv_q8_argmax(mode: int, wq, ws, y, idx, workspace, x=None, xq=None, x
         _ptr(t, None, n)
     nbytes = workspace.numel() * workspace.element_size()
     return Bound("qdg_gemv_q8_argmax", mode, wq, ws, N, K, x, xq, xl, xs, y, idx, workspace, nbytes, _stream())
+
+
+def gemv_q8_argmax_noalloc(mode: int, wq, ws, y, idx, x=None, xq=None, xl=None, xs=None) -> None:
+    """``gemv_q8_argmax`` with the keys in the library's own per-GPU array (no workspace,
+    nothing allocated; calls on one GPU must not overlap in time)."""
+    N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, x, xq, xl, xs, y=(y, N), idx=(idx, 1))
+    _check("qdg_gemv_q8_argmax_noalloc", _lib.qdg_gemv_q8_argmax_noalloc(
+        mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), _ptr(xq, _i8(), "xq"),
+        _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(y, _f32(), "y"), _ptr(idx, (_torch().int32,), "idx"),
+        _stream()))
 
 
 def argmax_workspace_bytes(B: int, N: int) -> int:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/qdg.h"
 #include "qdg_device.h"
@@ -230,6 +231,53 @@ int qdg_gemv_q8_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N
   if (workspace_bytes < qdg_gemv_argmax_workspace_bytes(N)) return QDG_EWORKSPACE;
   return hip_status(qdg::launch_gemv_argmax(mode, wq, ws, N, K, x, xq, xl, xs, y, idx,
                                             (unsigned long long*)workspace, as_stream(stream)));
+}
+
+}  // extern "C"
+
+// The arg-max keys of qdg_gemv_q8_argmax_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  In host code
+// its name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and that
+// address is what the launches receive.
+namespace {
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)1 << 20;
+static __device__ __align__(256) unsigned long long scratch[NOALLOC_SCRATCH_BYTES / sizeof(unsigned long long)];
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The current device's address of `scratch` (looked up at the first call on that device).
+hipError_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int qdg_gemv_q8_argmax_noalloc(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                               const int8_t* xq, const int8_t* xl, const float* xs, float* y, int32_t* idx,
+                               qdg_stream stream) {
+  if (N < 1 || N >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (qdg_gemv_argmax_workspace_bytes(N) > NOALLOC_SCRATCH_BYTES) return QDG_EWORKSPACE;
+  void* keys = nullptr;
+  const hipError_t e = device_scratch(&keys);
+  if (e != hipSuccess) return hip_status(e);
+  // every key the final pass reads is written by the GEMV of the same call, so
+  // nothing in the scratch needs clearing
+  return qdg_gemv_q8_argmax(mode, wq, ws, N, K, x, xq, xl, xs, y, idx, keys, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t qdg_argmax_workspace_bytes(int64_t B, int64_t N) {
