@@ -55,18 +55,53 @@ __device__ __forceinline__ int2 ld8_stream(const int8_t* p) {
   return make_int2(t[0], t[1]);
 }
 
-// At most 80 VGPRs.  With the wave index a scalar (readfirstlane) the chunk
-// bounds and the four rows' pointers sit in SGPRs and the kernel needs 52 VGPRs,
-// eight waves a SIMD (72 and seven without): 5120x25600 at S=8 33.6 -> 31.2 us,
-// the LM head at S=2 181 -> 159 us.  A one-step prefetch of the next step's
-// weights through two named buffers added about 1% more on the larger shapes
-// and lost on the smallest, so the SIMD's other waves cover the load latency.
-template <int R>
-__global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_dq_seg(
-    const PartTable tab, const float* __restrict__ x, int64_t K, int S, int m, int ceff) {
+// One step's operands of a lane: the piece's weights in the wave's four rows,
+// its eight activation values and the four rows' scales of its block.
+struct DqStep {
+  int2 w[4];
+  float4 x0, x1;
+  unsigned short sg[4];
+};
+
+// Requests piece p's operands (p already clamped into the chunk: a lane past the
+// chunk's end re-reads its last piece, whose step dq_fold then drops, so every
+// wave issues the same loads and the compiler's wait counts stay exact).
+__device__ __forceinline__ void dq_load(DqStep& b, const int8_t* const (&wrow)[4], const uint16_t* const (&srow)[4],
+                                        const float* __restrict__ x, int p) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b.w[r] = ld8_stream(wrow[r] + (unsigned)(8 * p));
+  b.x0 = *(const float4*)(x + (unsigned)(8 * p));
+  b.x1 = *(const float4*)(x + (unsigned)(8 * p + 4));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b.sg[r] = srow[r][(unsigned)(p >> 2)];
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The step's terms: each row's piece sum v, folded as acc <- fma(sigma, v, acc)
+// when the lane's piece lies in the chunk.
+__device__ __forceinline__ void dq_fold(const DqStep& b, bool act, double (&acc)[4]) {
+  const double xd[8] = {b.x0.x, b.x0.y, b.x0.z, b.x0.w, b.x1.x, b.x1.y, b.x1.z, b.x1.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const double v = piece_dot8(b.w[r], xd);
+    const double f = __fma_rn((double)half_bits_to_float(b.sg[r]), v, acc[r]);
+    acc[r] = act ? f : acc[r];
+  }
+}
+
+// The wave index is a scalar (readfirstlane), so the chunk bounds and the four
+// rows' pointers sit in SGPRs.  The operands stream through NB named step
+// buffers: buffer k's terms are taken, then it is refilled NB steps ahead, so
+// NB - 1 later steps stay in flight while a step is folded and no register copy
+// waits for a load.  The earlier loop loaded a step and waited for all of it
+// before its terms (one step in flight a wave), with a predicate that made every
+// load and term a branch.
+template <int R, int NB>
+__global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, const float* __restrict__ x, int64_t K,
+                                                        int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;
   __shared__ double lpart[DS_NT / 64][4];
-  // the wave index as a scalar, so the chunk bounds and row pointers live in SGPRs
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave / ceff, c = wave % ceff;
   const int chunk = c < m ? c : S - 1;
@@ -79,9 +114,9 @@ __global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void
   const int64_t N = tab.N[part];
   int32_t g0, g1;
   split_range(K, S, chunk, g0, g1);
-  // 8-value pieces of the row (32-bit offsets: K < 2^31, so the base + offset
-  // addressing keeps the per-lane address in one register)
+  // 8-value pieces of the row (32-bit offsets: K < 2^31)
   const int p0 = 4 * g0, p1 = 4 * g1;
+  const int nsteps = (p1 - p0 + 63) / 64;
 
   const int8_t* wrow[4];
   const uint16_t* srow[4];
@@ -93,31 +128,33 @@ __global__ __launch_bounds__(DS_NT) __attribute__((amdgpu_waves_per_eu(6))) void
     srow[r] = ws + o * nb;
   }
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int st = p0; st < p1; st += 64) {
-    const int p = st + lane;
-    const bool act = p < p1;
-    int2 wc[4];
+  if (nsteps > 0) {
+    const int plast = p1 - 1;
+    auto piece = [&](int st) { return p0 + 64 * st + lane; };
+    auto clamp = [&](int p) { return p < plast ? p : plast; };
+    DqStep b[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wc[r] = act ? ld8_stream(wrow[r] + (unsigned)(8 * p)) : make_int2(0, 0);
-    double xd[8];
-    unsigned short sg[4];
-    if (act) {
-      const float4 f0 = *(const float4*)(x + (unsigned)(8 * p)), f1 = *(const float4*)(x + (unsigned)(8 * p + 4));
-      xd[0] = f0.x; xd[1] = f0.y; xd[2] = f0.z; xd[3] = f0.w;
-      xd[4] = f1.x; xd[5] = f1.y; xd[6] = f1.z; xd[7] = f1.w;
+    for (int k = 0; k < NB; ++k) dq_load(b[k], wrow, srow, x, clamp(piece(k)));
+    int st = 0;
+    // while every refill is due (only a chunk's last step can be partial -- a
+    // chunk is whole 512-value superblocks, 64 pieces, but for the K mod 512
+    // tail -- so every lane's piece here lies in the chunk)
+    for (; st + 2 * NB - 1 < nsteps; st += NB) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sg[r] = srow[r][(unsigned)(p >> 2)];
-    } else {
+      for (int k = 0; k < NB; ++k) {
+        dq_fold(b[k], true, acc);
+        dq_load(b[k], wrow, srow, x, clamp(piece(st + k + NB)));
+      }
+    }
+    // the last 1 .. 2*NB - 1 steps, in order
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xd[i] = 0.0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sg[r] = 0;
+    for (int k = 0; k < NB; ++k) {
+      if (st + k < nsteps) dq_fold(b[k], piece(st + k) < p1, acc);
+      if (st + k + NB < nsteps) dq_load(b[k], wrow, srow, x, clamp(piece(st + k + NB)));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const double v = piece_dot8(wc[r], xd);
-      acc[r] = act ? __fma_rn((double)half_bits_to_float(sg[r]), v, acc[r]) : acc[r];
-    }
+    for (int k = 0; k + 1 < NB; ++k)
+      if (st + NB + k < nsteps) dq_fold(b[k], piece(st + NB + k) < p1, acc);
   }
   // the 64 lanes' accumulators by a fixed butterfly
 #pragma unroll
@@ -146,10 +183,15 @@ void ds_chunks(int64_t K, int S, int& m, int& ceff) {
   if (m < S && ((K % 512) != 0 || m == 0)) ceff = m + 1;
 }
 
+#ifndef QDG_DS_NB
+#define QDG_DS_NB 2
+#endif
+constexpr int DS_NB = QDG_DS_NB;  // step buffers: DS_NB - 1 steps in flight beyond the one being folded
+
 template <int R>
 hipError_t launch_ds(const PartTable& tab, int64_t K, const float* x, int S, int m, int ceff, hipStream_t st) {
   const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
-  return launch((k_gemv_dq_seg<R>), grid, block, 0, st, tab, x, K, S, m, ceff);
+  return launch((k_gemv_dq_seg<R, DS_NB>), grid, block, 0, st, tab, x, K, S, m, ceff);
 }
 
 }  // namespace

@@ -260,6 +260,27 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return (float)(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
+// The s_waitcnt operand that waits until at most n vector-memory loads of the
+// wave are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt at their no-wait maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+// Waits until at most N of the wave's vector-memory loads are outstanding and
+// its LDS accesses are done, then meets the workgroup.  Unlike __syncthreads(),
+// whose workgroup fences wait for every outstanding global load (LDS DMA writes
+// count as such), the wave's last N loads stay in flight across it; loads
+// complete in issue order, so every earlier load -- LDS DMA included -- has
+// landed.  The empty asm statements keep the compiler from moving memory
+// accesses across.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS DMA (gfx950 global_load_lds_dwordx4): each active lane's 16 bytes at g
 // land at l + 16*lane, with l the same for the whole wave (it goes to M0).  The
 // load counts in vmcnt like any other; it needs no VGPR for the data.

@@ -53,13 +53,13 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   float* lsx = (float*)(lds + nb * QK * (MODE == 2 ? 2 : 1));  // [nb]
   uint16_t* lsg = (uint16_t*)(lsx + nb);                       // [64][nb]: gate rows, then up rows
 
-  // the first step groups of weights are requested before the staging (the
-  // second one too where the staging needs no registers)
+  // With LDS DMA the staged bytes are requested first and the first NB step
+  // groups of weights after them, and the barrier waits for the staging only (the
+  // weights stay in flight; loads complete in issue order).  With the register
+  // copies the first group is requested ahead of the copies.
   int4 w[NB][U];
-  group_load<U>(w[0], wrow, 0, (int)nb, 0, j);
+  if constexpr (!DMA) group_load<U>(w[0], wrow, 0, (int)nb, 0, j);
   if constexpr (DMA) {
-#pragma unroll
-    for (int k = 1; k < NB; ++k) group_load<U>(w[k], wrow, 0, (int)nb, k, j);
     const int64_t nsx = nb * 4, nsg = 32 * nb * 2;  // multiples of 16 bytes (nb is a multiple of 8)
     for (int64_t base = (int64_t)wave * 1024; base < K; base += 16 * 1024) {
       if (base + lane * 16 < K) {
@@ -77,10 +77,9 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
         lds_dma16(src, (int8_t*)lsg + base);
       }
     }
-    // every load of the wave (the staged bytes and the first weight groups) has
-    // landed; the barrier's workgroup fences keep every LDS read below it
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) group_load<U>(w[k], wrow, 0, (int)nb, k, j);
+    wait_barrier<NB * U>();
   } else {
     for (int64_t i = tid; i < nb * 2; i += GL_NT) {
       ((int4*)lq)[i] = ld16(xq + 16 * i);

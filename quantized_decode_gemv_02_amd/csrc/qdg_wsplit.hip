@@ -42,6 +42,23 @@ constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with 
 template <int MODE, int ROWS>
 constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
 
+#ifdef QDG_PHASE_STAMPS
+// Phase-stamp build only (never in the release library): each wave's lane 0
+// records the 100 MHz constant clock at five points of its life -- 0 entry, 1
+// all first loads issued, 2 staged bytes landed (after the barrier), 3 chunk
+// terms done, 4 exit -- and, in word 5, the XCC and hardware id it ran on.  The
+// stamps go to LDS (so they never wait on, or count in, the wave's outstanding
+// global loads) and are written to stamp_buf[(workgroup * 16 + wave) * 8 + k] at
+// exit.
+__device__ unsigned long long* stamp_buf;
+#define QDG_STAMP(w, k) \
+  do {                                                                            \
+    if ((threadIdx.x & 63) == 0) st_lds[w][k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define QDG_STAMP(w, k) ((void)0)
+#endif
+
 template <int MODE, int R, int U, int NB, int STAGE, bool TL>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
 __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
@@ -54,6 +71,13 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
 
   // the wave index as a scalar: every per-chunk bound below is then wave-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#ifdef QDG_PHASE_STAMPS
+  __shared__ unsigned long long st_lds[16][8];
+  QDG_STAMP(wave, 0);
+  if (lane == 0)  // XCC id (HW_REG_XCC_ID) and hardware id (HW_REG_HW_ID: CU, SE)
+    st_lds[wave][5] = ((unsigned long long)__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (15 << 11)) << 32) |
+                      (unsigned)__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));
+#endif
   // wave c of a row group takes the c-th non-empty chunk: chunks 0..m-1, then
   // chunk S-1 when it holds the K mod 512 tail; the empty chunks' partials are
   // +0 and adding +0 changes no partial sum (none is -0), so they are skipped
@@ -82,14 +106,17 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   uint16_t* lsg = (uint16_t*)(lsx + nb);                                   // [ROWS][nb]
   const uint16_t* my_sg = lsg + rr * nb;
 
-  // the wave's first step groups of weights are requested before the staging
-  // (all NB where the staging needs no registers, else the first)
   int4 w[NB][U];
-  group_load<U, TL>(w[0], wrow, g0, g1, 0, j);
+  if constexpr (STAGE != WS_DMA) group_load<U, TL>(w[0], wrow, g0, g1, 0, j);  // ahead of the register copies
   if constexpr (STAGE == WS_DMA) {
-#pragma unroll
-    for (int k = 1; k < NB; ++k) group_load<U, TL>(w[k], wrow, g0, g1, k, j);
-    // whole 1 KiB pieces a wave instruction; the byte counts are multiples of 16
+    // The staged bytes are requested first and the wave's first NB step groups of
+    // weights after them.  Loads complete in issue order, so the wait below for
+    // all but the last NB*U loads covers exactly the staging, and the barrier
+    // (wait_barrier: no workgroup fence, which would wait for every load) lets
+    // the weights stay in flight.  Requesting the weights first made every wave
+    // wait for them at the barrier: 0.2 us (5120x25600) and 0.3 us (5120x8192) a
+    // launch.
+    // Whole 1 KiB pieces a wave instruction; the byte counts are multiples of 16
     // (K and nb are multiples of 256 and 8), so a lane's 16 bytes are all in range
     const int nwv = (int)(blockDim.x >> 6);
     const int64_t rows_ok = N - o_wg < ROWS ? N - o_wg : ROWS;  // rows past N stay unstaged; their results are dropped
@@ -105,10 +132,11 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
       if (base + lane * 16 < nsx) lds_dma16((const int8_t*)xs + base + lane * 16, (int8_t*)lsx + base);
     for (int64_t base = (int64_t)wave * 1024; base < nsg; base += (int64_t)nwv * 1024)
       if (base + lane * 16 < nsg) lds_dma16(sgsrc + base + lane * 16, (int8_t*)lsg + base);
-    // every load of the wave (the staged bytes and the first weight groups) has
-    // landed; the barrier's workgroup fences keep every LDS read below it
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) group_load<U, TL>(w[k], wrow, g0, g1, k, j);
+    QDG_STAMP(wave, 1);
+    // the wave's staged bytes have landed (the NB*U weight loads may not have)
+    wait_barrier<NB * U>();
   } else if constexpr (STAGE == WS_LOCAL) {
     for (int i = lane; i < nwb * 2; i += 64) {
       const int64_t k = (int64_t)g0 * 2 + i;
@@ -137,7 +165,9 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   }
 
   // the chunk's partial of the row, in lane 0 of the row
+  QDG_STAMP(wave, 2);
   const float yv = chunk_dot4<MODE, U, NB, TL>(wrow, lq, ll, lsx, my_sg, g0, g1, j, hf, w);
+  QDG_STAMP(wave, 3);
   if (li == 0) lpart[wave][r] = yv;
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
@@ -148,6 +178,10 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     for (int cc = 0; cc < ceff; ++cc) a = __fadd_rn(a, lpart[g * ceff + cc][q]);
     y[o_wg + tid] = a;
   }
+  QDG_STAMP(wave, 4);
+#ifdef QDG_PHASE_STAMPS
+  if (lane < 6 && stamp_buf) stamp_buf[((int64_t)blockIdx.x * 16 + wave) * 8 + lane] = st_lds[wave][lane];
+#endif
 }
 
 // The chunk waves of one row group: the non-empty chunks of the S-chunk rule.
@@ -290,6 +324,15 @@ hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, in
                               hipStream_t st, bool tiled) {
   return launch_gemv_wsplit_parts(mode, 1, &wq, &ws, &N, &y, K, xq, xl, xs, splits, st, tiled);
 }
+
+#ifdef QDG_PHASE_STAMPS
+// Phase-stamp build only: points the in-workgroup split kernel's stamps at buf
+// (device, 8 words a wave of 16 a workgroup; NULL stops stamping).
+extern "C" int qdg_debug_phase_stamps(void* buf) {
+  unsigned long long* p = (unsigned long long*)buf;
+  return hipMemcpyToSymbol(HIP_SYMBOL(stamp_buf), &p, sizeof(p)) == hipSuccess ? 0 : -6;
+}
+#endif
 
 hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, hipStream_t st) {
   const int64_t n16 = N * K / 16;
