@@ -449,7 +449,8 @@ enum {
   QDG_TUNE_DQ_ROWS = 5,    /* 1..4: row groups a workgroup of the Dequant chunk waves        */
   QDG_TUNE_DQ_X64 = 6,     /* 0: the unsplit Dequant kernel keeps its window in binary32     */
   QDG_TUNE_MFMA_GENERAL = 7, /* 1: the batched GEMV on its general (register) path           */
-  QDG_TUNE_MFMA_SHAPE = 8, /* 100*waves + 10*tiles + ring of the batched fast path (B <= 16)  */
+  QDG_TUNE_MFMA_SHAPE = 8, /* 100*waves + 10*tiles + ring of the batched fast path (B <= 16);
+                              1000 + 10*tiles + ring: one wave per workgroup, own ring       */
   QDG_TUNE_MFMA_WIDE = 9,  /* the same for 16 < B <= 64                                      */
   QDG_TUNE_GEMV_ORDER = 10, /* 0: tile-major, 1: chunk-major workgroup order (split GEMV)    */
   QDG_TUNE_GEMV_RPW = 11,  /* 4 or 8 rows a wave (batch-1 GEMV)                              */

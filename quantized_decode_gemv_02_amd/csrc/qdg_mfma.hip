@@ -552,6 +552,189 @@ hipError_t launch_dma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K
                      (int)B, splits, out);
 }
 
+// ---------------------------------------------------------------------------
+// The batched fast path for up to 16 activation rows: one wave a workgroup, with
+// a ring of its own in LDS, so no wave ever waits for another.  Wave = TPW row
+// tiles of 16 weight rows over the whole chunk; every step of 8 blocks moves the
+// tiles' weights (4 rows x 256 bytes a DMA instruction, whole lines), the 16
+// activation rows' words of the step (both words under TwoPass), their scales
+// and the tiles' weight scales from global memory straight into the wave's slot
+// (global_load_lds), P - 1 steps ahead.  The wave waits only for its own loads
+// (s_waitcnt vmcnt: loads complete in issue order) -- no barrier -- and takes
+// all 8 blocks of the step itself: block k's v_mfma_i32_16x16x32_i8 gives the
+// dots of activation rows 4*grp + i against weight row col of a tile, and each
+// output's step goes into partial k mod 4 in the lane that holds the output, so
+// the four partial chains of an output (blocks r, r + 4, ... in ascending
+// order) and their (P0 + P2) + (P1 + P3) stay in one lane: the batch-1 sums,
+// bit for bit.  (The workgroup-shared ring above waits at a barrier every step,
+// so a workgroup keeps one step in flight; a copy of it with the barrier taken
+// out streamed the same loads a third faster.)
+//
+// Slot: W [16*TPW rows][256] and A (L) [16 rows][256] with 16-byte chunk c of
+// row r at c ^ (r mod 16) -- lane (r4 = l/16, j = l%16) of a DMA instruction
+// fetches global chunk j ^ row so that its lane-ordered write lands in place --;
+// SX [16][8] activation scales; SG [16*TPW rows][8] weight scales.
+// s_waitcnt vmcnt(min(after, A) * L), `after` wave-uniform, the count an immediate
+template <int L, int A>
+__device__ __forceinline__ void wait_steps(int after) {
+  if constexpr (A == 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    if (after >= A) __builtin_amdgcn_s_waitcnt(vmcnt_imm(A * L));
+    else wait_steps<L, A - 1>(after);
+  }
+}
+
+template <int MODE, int TPW>
+struct RSlot {
+  static constexpr int W = 0;
+  static constexpr int A = W + 16 * TPW * 256;
+  static constexpr int L = A + 16 * 256;
+  static constexpr int SX = L + (MODE == 2 ? 16 * 256 : 0);
+  static constexpr int SG = SX + 16 * STEP * 4;
+  static constexpr int BYTES = SG + 16 * TPW * STEP * 2;
+  static constexpr int LOADS = 4 * TPW + (MODE == 2 ? 8 : 4) + 2 + 1;  // DMA instructions a step
+};
+
+template <int MODE, int TPW, int P>
+__global__ __launch_bounds__(64) void k_gemv_mfma_ring(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+                                                       const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                       const float* __restrict__ xs, int64_t N, int64_t K, int B,
+                                                       int S, float* __restrict__ out) {
+  using SL = RSlot<MODE, TPW>;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int s_idx = blockIdx.y;
+  int32_t g0, g1;
+  split_range(K, S, s_idx, g0, g1);
+  const int nsteps = (g1 - g0) / STEP;  // whole steps: K/32 and chunk ends are multiples of 8 here
+  const int64_t nb = K / QK;
+  const int64_t o_wg = (int64_t)blockIdx.x * 16 * TPW;
+
+  // ---- load side: instruction m of the weights reads rows 4m .. 4m+3 of the wave
+  const int r4 = lane >> 4, j = lane & 15;
+  const int8_t* wsrc[4 * TPW];
+#pragma unroll
+  for (int m = 0; m < 4 * TPW; ++m) {
+    const int row = 4 * m + r4;
+    int64_t o = o_wg + row;
+    if (o >= N) o = N - 1;
+    wsrc[m] = wq + o * K + 16 * ((j ^ row) & 15);  // global chunk j ^ row of the row's step
+  }
+  int64_t aoff[4];  // activation rows 4q + r4, chunk j ^ row
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = 4 * q + r4;
+    aoff[q] = (int64_t)min(t, B - 1) * K + 16 * ((j ^ t) & 15);
+  }
+  const float* xsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sidx = 64 * h + lane;  // [t][k] within the step
+    xsrc[h] = xs + (int64_t)min(sidx >> 3, B - 1) * nb + (sidx & 7);
+  }
+  int64_t so = o_wg + (lane < 16 * TPW ? lane : 0);
+  if (so >= N) so = N - 1;
+  const uint16_t* ssrc = ws + so * nb;
+
+  // every load of step s, into slot s mod P: the same count (SL::LOADS) each step
+  auto issue = [&](int s) {
+    unsigned char* slot = lds + (s % P) * SL::BYTES;
+    const int64_t b0 = g0 + (int64_t)s * STEP;
+#pragma unroll
+    for (int m = 0; m < 4 * TPW; ++m)  // nontemporal: the weights are streamed once
+      dma<16, 2>(wsrc[m] + b0 * QK, slot + SL::W + m * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma<16, 0>(xq + aoff[q] + b0 * QK, slot + SL::A + q * 1024);
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma<16, 0>(xl + aoff[q] + b0 * QK, slot + SL::L + q * 1024);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dma<4, 0>(xsrc[h] + b0, slot + SL::SX + h * 256);
+    // lane i < 16*TPW moves row i's 8 scales (16 bytes); the other lanes are masked off
+    if (lane < 16 * TPW) dma<16, 0>(ssrc + b0, slot + SL::SG);
+  };
+  // waits until step s has landed: after it, `after` later steps' loads may be outstanding
+  auto wait_step = [&](int after) {
+    asm volatile("" ::: "memory");
+    wait_steps<SL::LOADS, P - 1>(after);
+    asm volatile("" ::: "memory");
+  };
+  static_assert(P >= 2 && (P - 1) * SL::LOADS < 64, "ring depth and wait counts");
+
+  // ---- read side (lane col, grp): block k's 8 bytes of row col of a tile
+  float p[TPW][4][4];  // [tile][partial][i]: output (t = 4*grp + i, o = o_wg + 16*tile + col)
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][r][i] = 0.0f;
+
+  // Only the chunk's own steps are loaded (an empty chunk, K < 512 with several
+  // chunks, loads nothing: its partials stay +0); near the end fewer steps are in
+  // flight, and the waits count them.
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q)
+    if (q < nsteps) issue(q);
+  for (int s = 0; s < nsteps; ++s) {
+    asm volatile("" ::: "memory");
+    if (s + P - 1 < nsteps) issue(s + P - 1);  // into slot (s - 1) mod P, whose reads (step s - 1) are done
+    wait_step(min(P - 1, nsteps - 1 - s));
+    const unsigned char* slot = lds + (s % P) * SL::BYTES;
+#pragma unroll
+    for (int k = 0; k < STEP; ++k) {
+      const int off = ((((2 * k + (grp >> 1)) ^ col) & 15) << 4) + 8 * (grp & 1);
+      const long ak = *(const long*)(slot + SL::A + col * 256 + off);
+      long lk = 0;
+      if constexpr (MODE == 2) lk = *(const long*)(slot + SL::L + col * 256 + off);
+      float sig[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sig[i] = *(const float*)(slot + SL::SX + ((4 * grp + i) * STEP + k) * 4);
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const long wk = *(const long*)(slot + SL::W + (16 * m + col) * 256 + off);
+        const float sgm =
+            half_bits_to_float(*(const unsigned short*)(slot + SL::SG + ((16 * m + col) * STEP + k) * 2));
+        const v4i D = mfma16x16x32(ak, wk);
+        v4i E = {0, 0, 0, 0};
+        if constexpr (MODE == 2) E = mfma16x16x32(lk, wk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float ta, tb;
+          q8_term<MODE>(sgm, sig[i], D[i], E[i], ta, tb);
+          p[m][k & 3][i] = __fmaf_rn(ta, tb, p[m][k & 3][i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int64_t oo = o_wg + 16 * m + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * grp + i;
+      const float y = __fadd_rn(__fadd_rn(p[m][0][i], p[m][2][i]), __fadd_rn(p[m][1][i], p[m][3][i]));
+      if (t < B && oo < N) out[((int64_t)s_idx * B + t) * N + oo] = y;
+    }
+  }
+}
+
+template <int MODE, int TPW, int P>
+hipError_t launch_ring(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                       const int8_t* xl, const float* xs, int64_t B, int splits, float* out, hipStream_t st) {
+  constexpr int lds = P * RSlot<MODE, TPW>::BYTES;
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_mfma_ring<MODE, TPW, P>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((N + 16 * TPW - 1) / (16 * TPW)), (unsigned)splits), block(64);
+  return launch((k_gemv_mfma_ring<MODE, TPW, P>), grid, block, lds, st, wq, ws, xq, xl, xs, N, K, (int)B, splits,
+                out);
+}
+
 // Fast-path shape: QDG_TUNE_MFMA_SHAPE = 100*WV + 10*TPW + P among the compiled
 // ones -- 4,4,2 (the default), 4,4,3, 4,2,2, 8,2,3.  On 25600x5120, B = 16:
 // 4,4,2 streams 4.30 / 3.96 TB/s (Int8Act / TwoPass), 8,2,3 4.27 / 3.73,
@@ -590,13 +773,30 @@ hipError_t launch_m(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, 
   }
   // the fast path needs whole steps (K/32 a multiple of 8) and 16-byte weight-scale words
   if ((K / QK) % 8 == 0 && ((uintptr_t)ws & 15) == 0 && tune(QDG_TUNE_MFMA_GENERAL) != 1) {
+    // the workgroup-shared ring (default; QDG_TUNE_MFMA_SHAPE = 100*WV + 10*TPW + P),
+    // or the per-wave ring (1000 + 10*TPW + P), which measured slower: each wave
+    // fetches the activation tile itself and its own steps serialise behind its loads
+    const int knob = tune(QDG_TUNE_MFMA_SHAPE);
+    if (knob >= 1000) {
+      const int rt = (knob / 10) % 10, rp = knob % 10;
+#define QDG_RING(T_, P_) \
+  if (rt == T_ && rp == P_) return launch_ring<MODE, T_, P_>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+      QDG_RING(1, 3) QDG_RING(2, 2)
+#undef QDG_RING
+      return launch_ring<MODE, 2, 3>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
+    }
     const DmaShape d = dma_shape();
 #define QDG_DMA(WV_, TPW_, P_)                   \
   if (d.wv == WV_ && d.tpw == TPW_ && d.ring == P_) \
     return launch_dma<MODE, WV_, TPW_, P_>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
     QDG_DMA(4, 4, 3);
+    QDG_DMA(4, 4, 4);
     QDG_DMA(4, 2, 2);
+    QDG_DMA(4, 2, 3);
+    QDG_DMA(4, 2, 4);
     QDG_DMA(8, 2, 3);
+    QDG_DMA(8, 1, 3);
+    QDG_DMA(8, 1, 4);
 #undef QDG_DMA
     return launch_dma<MODE, 4, 4, 2>(wq, ws, N, K, xq, xl, xs, B, splits, out, st);
   }
