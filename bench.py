@@ -574,6 +574,43 @@ def main() -> int:
                     "fused_us": round(timer.median_us([one], args.launches), 2),
                     "f32_producer_us": round(timer.median_us([a_], args.launches), 2),
                     "quantize_us": round(timer.median_us([b_], args.launches), 2)}
+        # the projection that feeds the norm, with the residual add, RMSNorm and quantizer as its
+        # epilogue (qdg_gemv_q8_rmsnorm), against the GEMV alone and against the GEMV followed by
+        # the norm producer (two launches), on each narrow projection at the step's S
+        for si, sh in enumerate(shapes):
+            rn = torch.from_numpy(workloads.activation(sh.N, 21 + si)).to(dev)
+            wn2 = torch.from_numpy(workloads.norm_weight(sh.N, 23 + si)).to(dev)
+            for mode in modes:
+                S = chosen[(mode, si)]
+                if not q.sk_combines_in_workgroup(mode, sh.K, S):
+                    continue
+                xq, xl, xs = quantized(mode, acts[si])
+                y = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
+                s_ = torch.empty_like(y)
+                hq = torch.empty((1, sh.N), dtype=torch.int8, device=dev)
+                hl = torch.empty_like(hq) if mode == 2 else None
+                hs = torch.empty((1, sh.N // 32), dtype=torch.float32, device=dev)
+                nws = q.gemv_rmsnorm_workspace(sh.N)
+                sws = q.sk_workspace(sh.N, S)
+                fused_calls = [q.bind_gemv_q8_rmsnorm(mode, copies[c][si][0], copies[c][si][1], xq, xl, xs, S, nws,
+                                                      y=y, r=rn, s=s_, w=wn2, qmode=mode, hq=hq, hl=hl, hs=hs)
+                               for c in range(R)]
+                gemv_calls = [q.bind_gemv_q8_sk(mode, copies[c][si][0], copies[c][si][1], y, xq, xl, xs, S, sws)
+                              for c in range(R)]
+                norm_call = q.bind_rmsnorm_quantize(mode, y, wn2, rn, s_, None, hq, hl, hs)
+                two = [lambda g=g: (g(), norm_call()) for g in gemv_calls]
+                f_us = timer.median_us(fused_calls, args.launches)
+                g_us = timer.median_us(gemv_calls, args.launches)
+                n_us = timer.median_us([norm_call], args.launches)
+                producers[f"gemv_rmsnorm_{NAMES[mode]}_{sh.name}_{sh.N}x{sh.K}_S{S}"] = {
+                    "fused_us": round(f_us, 2), "gemv_us": round(g_us, 2), "rmsnorm_quantize_us": round(n_us, 2),
+                    "two_launches_us": round(g_us + n_us, 2),
+                    "fused_wall_us": round(timer.wall_us(fused_calls, args.launches), 2),
+                    "two_launches_wall_us": round(timer.wall_us(two, args.launches), 2),
+                    # the GEMV's bytes plus the norm's: r, s and w (4 bytes a row each) and the words
+                    **rate(alg_bytes(mode, sh.N, sh.K) + 12 * sh.N + (2 if mode == 2 else 1) * sh.N + sh.N // 8,
+                           f_us)}
+        progress("producers done")
 
     # ---- the other GGUF block formats on the down-proj's shape: qdg_gemv_fmt in the two
     # quantized modes at S=8 (one round of 1280 five-wave workgroups), over rotated copies

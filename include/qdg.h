@@ -290,6 +290,50 @@ int qdg_rmsnorm_quantize(int mode, const float *x, const float *r, float *s, con
 /* The largest K qdg_rmsnorm_quantize accepts (one workgroup holds a row). */
 int64_t qdg_rmsnorm_max_k(void);
 
+/* Bytes of device workspace qdg_gemv_q8_rmsnorm needs for N output rows (0 if N
+ * is out of its range): one word a row, in whole 256-byte lines. */
+size_t qdg_gemv_rmsnorm_workspace_bytes(int64_t N);
+
+/* The largest N qdg_gemv_q8_rmsnorm accepts: the last workgroup holds the row's
+ * N binary32 values in its LDS between the norm's two passes. */
+int64_t qdg_gemv_rmsnorm_max_n(void);
+
+/*
+ * A projection with the residual add, the RMSNorm and the quantizer of the next
+ * projection's activation in its epilogue, in one launch (lane kernel library
+ * page, GEMV_Q8_NORM, lk_gemv_q8_norm: the blocks write their rows, and one
+ * block then norms the row they make up).  Here every workgroup publishes its
+ * rows to the workspace's slots, and one more workgroup gathers them as they
+ * fill and runs the norm and the quantizer.  One activation row (B == 1).  Its
+ * outputs are bit-identical to
+ *   qdg_gemv_q8_sk(mode, wq, ws, N, K, xq, xl, xs, 1, splits, y, ...)
+ *   qdg_rmsnorm_quantize(qmode, y, r, s, w, eps, 1, N, yn, hq, hl, hs, ...)
+ * run one after the other: y [N] is the projection, s = y + r the next residual
+ * stream, yn the normed row and (hq, hl, hs) its words in mode qmode, ready for
+ * the next projection's qdg_gemv_q8_sk.
+ *   mode   QDG_INT8ACT or QDG_TWOPASS (QDG_DEQUANT: QDG_EMODE), with xq, xl, xs
+ *          as qdg_gemv_q8_sk takes them;
+ *   splits one that qdg_gemv_sk_combines_in_workgroup accepts for (mode, K),
+ *          else QDG_EMODE: the chunks of every row meet inside a workgroup;
+ *   qmode  QDG_DEQUANT (writes only yn, required; hq, hl, hs NULL),
+ *          QDG_INT8ACT (hq, hs; hl NULL) or QDG_TWOPASS (hq, hl, hs), as
+ *          qdg_rmsnorm_quantize's mode;
+ *   y, yn  f32 [N] or NULL each; r, s [N], r or NULL, s only with r; w [N] or
+ *          NULL; eps >= 0 and finite.
+ * Device pointers; wq, ws, xq, xl, xs aligned as qdg_gemv_q8_sk asks; y 4-byte
+ * aligned; r, s, w, yn, hq, hl 16-byte aligned, hs 4-byte aligned.  N a
+ * multiple of 32 with 32 <= N <= qdg_gemv_rmsnorm_max_n(); K >= 32, a multiple
+ * of 32.  s may be r (an in-place residual update); no other buffers overlap.
+ * workspace: at least qdg_gemv_rmsnorm_workspace_bytes(N) bytes, 256-byte
+ * aligned, zero-filled before its first use and left zeroed by every call that
+ * completes; calls that share a workspace must not overlap in time.
+ */
+int qdg_gemv_q8_rmsnorm(int mode, const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K,
+                        const int8_t *xq, const int8_t *xl, const float *xs, int splits, float *y,
+                        const float *r, float *s, const float *w, float eps, int qmode, float *yn,
+                        int8_t *hq, int8_t *hl, float *hs, void *workspace, size_t workspace_bytes,
+                        qdg_stream stream);
+
 /*
  * SwiGLU, then the activation quantizer, in one launch (lane kernel library
  * page, lk_act and GLU: silu(g) = g / (1 + e^-g), times u; QWEN38 page,

@@ -76,6 +76,10 @@ _SIGS = {
     "qdg_stream_read": ([_P, _I64, _P, _P], _I),
     "qdg_rmsnorm_quantize": ([_I, _P, _P, _P, _P, ctypes.c_float, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_rmsnorm_max_k": ([], _I64),
+    "qdg_gemv_rmsnorm_workspace_bytes": ([_I64], ctypes.c_size_t),
+    "qdg_gemv_rmsnorm_max_n": ([], _I64),
+    "qdg_gemv_q8_rmsnorm": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _P, ctypes.c_float, _I, _P, _P, _P,
+                             _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
@@ -469,6 +473,48 @@ def gemv_q8_argmax_noalloc(mode: int, wq, ws, y, idx, x=None, xq=None, xl=None, 
         mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(x, _f32(), "x"), _ptr(xq, _i8(), "xq"),
         _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(y, _f32(), "y"), _ptr(idx, (_torch().int32,), "idx"),
         _stream()))
+
+
+def gemv_rmsnorm_workspace_bytes(N: int) -> int:
+    return int(_lib.qdg_gemv_rmsnorm_workspace_bytes(N))
+
+
+def gemv_rmsnorm_max_n() -> int:
+    return int(_lib.qdg_gemv_rmsnorm_max_n())
+
+
+def gemv_rmsnorm_workspace(N: int):
+    """A zero-filled device workspace for ``gemv_q8_rmsnorm`` (int64 words, 256-byte aligned)."""
+    torch = _torch()
+    nbytes = max(gemv_rmsnorm_workspace_bytes(N), 8)
+    return torch.zeros((nbytes + 7) // 8, dtype=torch.int64, device="cuda")
+
+
+def _gemv_rmsnorm_args(mode, wq, ws, xq, xl, xs, splits, y, r, s, w, eps, qmode, yn, hq, hl, hs, workspace):
+    N, K = wq.shape
+    _gemv_sizes(mode, wq.shape, ws, 1, None, xq, xl, xs, y=(y, N), r=(r, N), s=(s, N), w=(w, N), yn=(yn, N),
+                hq=(hq, N), hl=(hl, N), hs=(hs, N // QK))
+    nbytes = workspace.numel() * workspace.element_size()
+    return (mode, _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(xq, _i8(), "xq"),
+            _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), int(splits), _ptr(y, _f32(), "y"), _ptr(r, _f32(), "r"),
+            _ptr(s, _f32(), "s"), _ptr(w, _f32(), "w"), float(eps), int(qmode), _ptr(yn, _f32(), "yn"),
+            _ptr(hq, _i8(), "hq"), _ptr(hl, _i8(), "hl"), _ptr(hs, _f32(), "hs"), _ptr(workspace, None, "workspace"),
+            nbytes, _stream())
+
+
+def gemv_q8_rmsnorm(mode: int, wq, ws, xq, xl, xs, splits: int, workspace, y=None, r=None, s=None, w=None,
+                    eps: float = 1e-6, qmode: int = INT8ACT, yn=None, hq=None, hl=None, hs=None) -> None:
+    """One launch: the split-K projection ``y = W x`` (``gemv_q8_sk``), then in its last workgroup
+    ``s = y + r``, the RMSNorm ``yn`` and its words ``hq/hl/hs`` in mode ``qmode``
+    (``rmsnorm_quantize``); ``workspace`` from ``gemv_rmsnorm_workspace(N)``."""
+    _check("qdg_gemv_q8_rmsnorm", _lib.qdg_gemv_q8_rmsnorm(*_gemv_rmsnorm_args(
+        mode, wq, ws, xq, xl, xs, splits, y, r, s, w, eps, qmode, yn, hq, hl, hs, workspace)))
+
+
+def bind_gemv_q8_rmsnorm(mode: int, wq, ws, xq, xl, xs, splits: int, workspace, y=None, r=None, s=None, w=None,
+                         eps: float = 1e-6, qmode: int = INT8ACT, yn=None, hq=None, hl=None, hs=None) -> "Bound":
+    return Bound("qdg_gemv_q8_rmsnorm", *_gemv_rmsnorm_args(
+        mode, wq, ws, xq, xl, xs, splits, y, r, s, w, eps, qmode, yn, hq, hl, hs, workspace))
 
 
 def argmax_workspace_bytes(B: int, N: int) -> int:

@@ -407,6 +407,41 @@ int qdg_rmsnorm_quantize(int mode, const float* x, const float* r, float* s, con
   return hip_status(qdg::launch_rmsnorm_quant(mode, x, r, s, w, eps, B, K, y, xq, xl, xs, as_stream(stream)));
 }
 
+size_t qdg_gemv_rmsnorm_workspace_bytes(int64_t N) {
+  if (N < qdg::QK || N % qdg::QK || N > qdg::gemv_norm_max_n()) return 0;
+  return qdg::gemv_norm_workspace_bytes(N);
+}
+
+int64_t qdg_gemv_rmsnorm_max_n(void) {
+  const int64_t a = qdg::gemv_norm_max_n(), b = qdg::rmsnorm_max_k();
+  return (a < b ? a : b) / qdg::QK * qdg::QK;
+}
+
+int qdg_gemv_q8_rmsnorm(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const int8_t* xq,
+                        const int8_t* xl, const float* xs, int splits, float* y, const float* r, float* s,
+                        const float* w, float eps, int qmode, float* yn, int8_t* hq, int8_t* hl, float* hs,
+                        void* workspace, size_t workspace_bytes, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return mode == QDG_DEQUANT ? QDG_EMODE : QDG_EINVAL;
+  if (!wq || !ws || !xq || !xs || !workspace) return QDG_EINVAL;
+  if ((mode == QDG_TWOPASS) != (xl != nullptr)) return QDG_EINVAL;
+  const int st = producer_outputs(qmode, yn, hq, hl, hs);
+  if (st != QDG_OK) return st;
+  if (s && !r) return QDG_EINVAL;
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return QDG_EINVAL;
+  if (!shape_ok(N, K)) return QDG_ESHAPE;
+  if (N < qdg::QK || N % qdg::QK || N > qdg_gemv_rmsnorm_max_n()) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (!qdg::wsplit_fits(mode, K, splits)) return QDG_EMODE;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) ||
+      (y && !aligned(y, 4)) || (r && !aligned(r, 16)) || (s && !aligned(s, 16)) || (w && !aligned(w, 16)) ||
+      !words_aligned(yn, hq, hl, hs))
+    return QDG_EALIGN;
+  if (!aligned(workspace, 256)) return QDG_EALIGN;
+  if (workspace_bytes < qdg::gemv_norm_workspace_bytes(N)) return QDG_EWORKSPACE;
+  return hip_status(qdg::launch_gemv_wsplit_norm(mode, wq, ws, N, K, xq, xl, xs, splits, y, r, s, w, eps, qmode, yn,
+                                                 hq, hl, hs, workspace, as_stream(stream)));
+}
+
 int qdg_swiglu_quantize(int mode, const float* g, const float* u, int64_t B, int64_t K, float* h, int8_t* xq,
                         int8_t* xl, float* xs, qdg_stream stream) {
   if (!g || !u) return QDG_EINVAL;

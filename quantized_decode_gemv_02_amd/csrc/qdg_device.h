@@ -251,6 +251,38 @@ __device__ __forceinline__ float quant_lane4(float4 v, int* h, int* l) {
   return s;
 }
 
+// The RMSNorm's arithmetic (lane kernel library page, RMSNORM: v = x + r,
+// y = v / sqrt(mean(v^2) + eps) * w), shared by the norm producer and the norm
+// epilogue of the split-K GEMV so that the two give the same bits: the residual
+// add is one binary32 addition a value; the squares are exact in binary64 and
+// summed there; the divisor is the correctly rounded binary64 square root; each
+// value is divided and scaled in binary64 and rounded once to binary32.
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(__fadd_rn(a.x, b.x), __fadd_rn(a.y, b.y), __fadd_rn(a.z, b.z), __fadd_rn(a.w, b.w));
+}
+__device__ __forceinline__ double sq4(float4 v) {
+  double a = (double)v.x * (double)v.x;
+  a += (double)v.y * (double)v.y;
+  a += (double)v.z * (double)v.z;
+  a += (double)v.w * (double)v.w;
+  return a;
+}
+__device__ __forceinline__ double norm_den(double sumsq, int64_t n, float eps) {
+  return __dsqrt_rn(sumsq / (double)n + (double)eps);
+}
+// four values of the row, normed; g holds their four weights when has_w
+__device__ __forceinline__ float4 norm4(float4 t, double den, bool has_w, float4 g) {
+  double ox = (double)t.x / den, oy = (double)t.y / den;
+  double oz = (double)t.z / den, ow = (double)t.w / den;
+  if (has_w) {
+    ox *= (double)g.x;
+    oy *= (double)g.y;
+    oz *= (double)g.z;
+    ow *= (double)g.w;
+  }
+  return make_float4((float)ox, (float)oy, (float)oz, (float)ow);
+}
+
 // SwiGLU of one value (lane kernel library page, lk_act: silu(g) = g / (1 + e^-g),
 // times u): evaluated in binary64 from the binary32 operands and rounded once.
 // Shared by the SwiGLU producer and the gate/up GEMV epilogue, so the two give
@@ -280,6 +312,10 @@ __device__ __forceinline__ void wait_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// A workgroup barrier for LDS only: the wave's global loads and stores stay in
+// flight (a store need not be acknowledged before the wave goes on).
+__device__ __forceinline__ void lds_barrier() { wait_barrier<63>(); }
 
 // LDS DMA (gfx950 global_load_lds_dwordx4): each active lane's 16 bytes at g
 // land at l + 16*lane, with l the same for the whole wave (it goes to M0).  The
@@ -482,6 +518,15 @@ hipError_t launch_gemv_wsplit_parts(int mode, int nparts, const int8_t* const* w
                                     const int64_t* N, float* const* y, int64_t K, const int8_t* xq,
                                     const int8_t* xl, const float* xs, int splits, hipStream_t st,
                                     bool tiled = false);
+// the in-workgroup split with the residual add, RMSNorm and quantizer run by
+// one more workgroup over the published rows (one activation row; workspace:
+// one word a row)
+size_t gemv_norm_workspace_bytes(int64_t N);
+int64_t gemv_norm_max_n();
+hipError_t launch_gemv_wsplit_norm(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                                   const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                                   const float* r, float* s, const float* w, float eps, int qmode, float* yn,
+                                   int8_t* hq, int8_t* hl, float* hs, void* workspace, hipStream_t st);
 hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,

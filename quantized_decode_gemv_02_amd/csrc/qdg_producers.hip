@@ -29,14 +29,6 @@ namespace {
 
 constexpr int NT = 1024;  // threads of a norm workgroup (one workgroup per row)
 
-__device__ __forceinline__ double sq4(float4 v) {
-  double a = (double)v.x * (double)v.x;
-  a += (double)v.y * (double)v.y;
-  a += (double)v.z * (double)v.z;
-  a += (double)v.w * (double)v.w;
-  return a;
-}
-
 // x, s and y may be the same buffer: every chunk is read and written by one
 // thread only, each read before that thread's write.  KEEP holds the row's
 // values in registers between the two passes; without it (the largest K, where
@@ -50,15 +42,8 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant(const float* x, const floa
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x, nc = K / 4;
   auto sum_in = [&](int64_t c) {
-    float4 v = *(const float4*)(x + row * K + 4 * c);
-    if (r) {
-      const float4 b = *(const float4*)(r + row * K + 4 * c);
-      v.x = __fadd_rn(v.x, b.x);
-      v.y = __fadd_rn(v.y, b.y);
-      v.z = __fadd_rn(v.z, b.z);
-      v.w = __fadd_rn(v.w, b.w);
-    }
-    return v;
+    const float4 v = *(const float4*)(x + row * K + 4 * c);
+    return r ? add4(v, *(const float4*)(r + row * K + 4 * c)) : v;
   };
   float4 v[KEEP ? PER : 1];
   double acc = 0.0;
@@ -82,7 +67,7 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant(const float* x, const floa
   double sum = red[0];
 #pragma unroll
   for (int i = 1; i < NT / 64; ++i) sum += red[i];
-  const double den = __dsqrt_rn(sum / (double)K + (double)eps);
+  const double den = norm_den(sum, K, eps);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int64_t c = tid + (int64_t)j * NT;
@@ -94,16 +79,7 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant(const float* x, const floa
         t = v[j];
       else
         t = s ? *(const float4*)(s + row * K + 4 * c) : sum_in(c);
-      double ox = (double)t.x / den, oy = (double)t.y / den;
-      double oz = (double)t.z / den, ow = (double)t.w / den;
-      if (w) {
-        const float4 g = *(const float4*)(w + 4 * c);
-        ox *= (double)g.x;
-        oy *= (double)g.y;
-        oz *= (double)g.z;
-        ow *= (double)g.w;
-      }
-      o = make_float4((float)ox, (float)oy, (float)oz, (float)ow);
+      o = norm4(t, den, w != nullptr, w ? *(const float4*)(w + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f));
       if (y) *(float4*)(y + row * K + 4 * c) = o;
     }
     if constexpr (MODE != 0) {

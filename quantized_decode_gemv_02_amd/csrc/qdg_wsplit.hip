@@ -28,6 +28,19 @@
 // below).  A row group's four rows are one tile row, so each weight request of
 // a wave reads one contiguous KiB and a chunk wave streams one contiguous range;
 // the terms, their order and the result are those of the plain layout.
+//
+// NORM (lane kernel library page, GEMV_Q8_NORM, lk_gemv_q8_norm: a projection
+// with the residual add and the next norm in its epilogue): each workgroup
+// writes its rows and publishes them to marked slots; one more workgroup, the
+// grid's last, gathers the whole row from the slots as they fill (it starts with
+// the others, so the gather overlaps the projection) and runs the residual add,
+// the RMSNorm and the block quantizer over it exactly as k_rmsnorm_quant's
+// 1024-thread workgroup does, its waves playing that workgroup's sixteen waves in
+// turn (norm_tail).  So its outputs are the bits of qdg_gemv_q8_sk followed by
+// qdg_rmsnorm_quantize, in one launch.  The page's kernel elects the norm's block
+// by an arrival count instead; with one count for the whole grid, its hundreds
+// of atomics on one word cost more (2.6 us on 5120x8192) than the norm workgroup
+// waiting on the slots.
 
 #include "qdg_device.h"
 
@@ -38,6 +51,120 @@ constexpr int WS_NT = 1024;               // sixteen waves
 enum { WS_BARRIER = 0, WS_LOCAL = 1, WS_DMA = 2 };
 constexpr int WS_U = 1, WS_NB = 4;  // steps a group, groups in flight
 constexpr int WS_LDS_MAX = 79 * 1024;     // two workgroups a CU (160 KiB) with the static part
+
+// The norm epilogue's operands.  slots: one marked word a row (zero between
+// launches).
+struct NormArgs {
+  const float* r;   // residual operand, or null
+  float* s;         // y + r written back, or null
+  const float* w;   // norm weight, or null
+  float* yn;        // the normed row (binary32), or null
+  int8_t* hq;       // the normed row's words (qmode 1, 2), or null (qmode 0)
+  int8_t* hl;
+  float* hs;
+  float eps;
+  int qmode;
+  unsigned* slots;
+};
+
+// The norm workgroup's work over the n-value row in the slots, in three steps.
+//  1. Gather: the workgroup's threads take the row's values in turn (value i to
+//     thread i mod blockDim, coalesced), NT_BATCH a thread at a time: its slot,
+//     r and w are all requested before the first is used, and the slots still
+//     unwritten are requested again, together, until all are in (at most
+//     PART_SPIN_LIMIT rounds a thread); each slot is cleared once read.  The sum
+//     t = y + r goes to s and to vbuf, w to wbuf (both LDS).
+//  2. k_rmsnorm_quant's sum of squares with its 1024 threads played by this
+//     workgroup's nw waves, real wave w taking the norm's waves w, w + nw, ... in
+//     turn: a norm thread's chunks are c = t, t + 1024, ...; its sum runs over
+//     them in that order, then the butterfly inside its wave, then the sixteen
+//     wave sums in ascending order.
+//  3. The same waves norm and quantize their chunks from vbuf and wbuf.
+// wbuf is used when both rows fit the LDS (w_lds); otherwise step 3 reads w
+// from global memory.  The barriers wait for LDS only: no store of the tail
+// waits to be acknowledged before the next step.
+constexpr int NT_BATCH = 8;
+__device__ __forceinline__ void norm_tail(const NormArgs& nm, int64_t n, float* vbuf, float* wbuf, bool w_lds,
+                                          int tid, int nt, int wave, int nw, int lane) {
+  constexpr int NW = 16;
+  __shared__ double red[NW];
+  int spins = 0;
+  for (int64_t i0 = tid; i0 < n; i0 += (int64_t)nt * NT_BATCH) {
+    unsigned u[NT_BATCH];
+    float rv[NT_BATCH], wv[NT_BATCH];
+#pragma unroll
+    for (int b = 0; b < NT_BATCH; ++b) {
+      const int64_t i = i0 + (int64_t)b * nt;
+      const bool on = i < n;
+      u[b] = on ? __hip_atomic_load(nm.slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+      rv[b] = on && nm.r ? nm.r[i] : 0.0f;
+      wv[b] = on && w_lds ? nm.w[i] : 0.0f;
+    }
+    for (;;) {
+      bool waiting = false;
+#pragma unroll
+      for (int b = 0; b < NT_BATCH; ++b) waiting |= u[b] == 0;
+      if (!waiting || spins >= PART_SPIN_LIMIT) break;
+      ++spins;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int b = 0; b < NT_BATCH; ++b)
+        if (u[b] == 0) u[b] = __hip_atomic_load(nm.slots + i0 + (int64_t)b * nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int b = 0; b < NT_BATCH; ++b) {
+      const int64_t i = i0 + (int64_t)b * nt;
+      if (i >= n) break;
+      __hip_atomic_store(nm.slots + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float t = __uint_as_float(u[b] ^ PART_MARK32);
+      if (nm.r) t = __fadd_rn(t, rv[b]);
+      if (nm.s) nm.s[i] = t;
+      vbuf[i] = t;
+      if (w_lds) wbuf[i] = wv[b];
+    }
+  }
+  lds_barrier();
+  const int64_t nc = n / 4;
+  const int per = (int)((nc + NW * 64 - 1) / (NW * 64));
+  for (int vw = wave; vw < NW; vw += nw) {
+    double acc = 0.0;
+    for (int j = 0; j < per; ++j) {
+      const int64_t c = vw * 64 + lane + (int64_t)j * NW * 64;
+      if (c < nc) acc += sq4(*(const float4*)(vbuf + 4 * c));  // past the row: +0 to a sum that is +0 or more
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (lane == 0) red[vw] = acc;
+  }
+  lds_barrier();
+  double sum = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) sum += red[i];
+  const double den = norm_den(sum, n, nm.eps);
+  for (int vw = wave; vw < NW; vw += nw) {
+    for (int j = 0; j < per; ++j) {
+      const int64_t c = vw * 64 + lane + (int64_t)j * NW * 64;
+      const bool on = c < nc;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (on) {
+        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (nm.w) g = *(const float4*)((w_lds ? wbuf : nm.w) + 4 * c);
+        o = norm4(*(const float4*)(vbuf + 4 * c), den, nm.w != nullptr, g);
+        if (nm.yn) *(float4*)(nm.yn + 4 * c) = o;
+      }
+      // every lane of the wave takes part in the block maximum; a block is wholly in or out
+      if (nm.qmode != 0) {
+        int h, l;
+        const float sc = nm.qmode == 1 ? quant_lane4<1>(o, &h, &l) : quant_lane4<2>(o, &h, &l);
+        if (on) {
+          *(int*)(nm.hq + 4 * c) = h;
+          if (nm.qmode == 2) *(int*)(nm.hl + 4 * c) = l;
+          if ((c & 7) == 0) nm.hs[c / 8] = sc;
+        }
+      }
+    }
+  }
+}
 
 template <int MODE, int ROWS>
 constexpr int ws_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * ROWS; }
@@ -59,11 +186,11 @@ __device__ unsigned long long* stamp_buf;
 #define QDG_STAMP(w, k) ((void)0)
 #endif
 
-template <int MODE, int R, int U, int NB, int STAGE, bool TL>
+template <int MODE, int R, int U, int NB, int STAGE, bool TL, bool NORM>
 // eight waves a SIMD (64 VGPRs): two sixteen-wave workgroups a CU
 __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_wsplit(
     const PartTable tab, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl, const float* __restrict__ xs,
-    int64_t K, int S, int m, int ceff) {
+    int64_t K, int S, int m, int ceff, const NormArgs nm) {
   constexpr int ROWS = 4 * R;   // rows of the workgroup
   constexpr int LPR = 16;  // lanes a row (a lane pair a block, eight blocks a step)
   extern __shared__ __align__(16) unsigned char lds[];
@@ -71,6 +198,14 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
 
   // the wave index as a scalar: every per-chunk bound below is then wave-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (NORM) {
+    if (blockIdx.x == gridDim.x - 1) {  // the norm workgroup
+      const int64_t n = tab.N[0];
+      const bool w_lds = nm.w != nullptr && 8 * n <= WS_LDS_MAX;
+      norm_tail(nm, n, (float*)lds, (float*)lds + n, w_lds, tid, (int)blockDim.x, wave, (int)(blockDim.x >> 6), lane);
+      return;
+    }
+  }
 #ifdef QDG_PHASE_STAMPS
   __shared__ unsigned long long st_lds[16][8];
   QDG_STAMP(wave, 0);
@@ -176,7 +311,8 @@ __global__ __launch_bounds__(WS_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     const int g = tid >> 2, q = tid & 3;
     float a = 0.0f;
     for (int cc = 0; cc < ceff; ++cc) a = __fadd_rn(a, lpart[g * ceff + cc][q]);
-    y[o_wg + tid] = a;
+    if (!NORM || y) y[o_wg + tid] = a;
+    if constexpr (NORM) publish_partial(nm.slots + o_wg + tid, a);
   }
   QDG_STAMP(wave, 4);
 #ifdef QDG_PHASE_STAMPS
@@ -198,17 +334,25 @@ void ws_chunks(int64_t K, int S, int& m, int& ceff) {
 template <int MODE, int R>
 size_t ws_lds_bytes(int64_t K) { return (size_t)(K / QK) * ws_bytes_per_block<MODE, 4 * R>(); }
 
-template <int MODE, int R, int STAGE, bool TL>
+template <int MODE, int R, int STAGE, bool TL, bool NORM>
 hipError_t launch_ws(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
-                     hipStream_t st) {
+                     const NormArgs& nm, hipStream_t st) {
   int m, ceff;
   ws_chunks(K, S, m, ceff);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, WS_LDS_MAX);
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)&k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL, NORM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      WS_LDS_MAX);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
-  const size_t lds = ws_lds_bytes<MODE, R>(K);
-  return launch((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL>), grid, block, lds, st, tab, xq, xl, xs, K, S, m, ceff);
+  // NORM: one more workgroup, the norm's
+  const dim3 grid((unsigned)tab.tile_end[tab.n - 1] + (NORM ? 1 : 0)), block((unsigned)(64 * R * ceff));
+  size_t lds = ws_lds_bytes<MODE, R>(K);
+  if (NORM) {  // the norm's row, and its weights where both fit
+    const size_t row = (size_t)tab.N[0] * 4, both = 2 * row;
+    const size_t need = nm.w != nullptr && both <= (size_t)WS_LDS_MAX ? both : row;
+    if (lds < need) lds = need;
+  }
+  return launch((k_gemv_wsplit<MODE, R, WS_U, WS_NB, STAGE, TL, NORM>), grid, block, lds, st, tab, xq, xl, xs, K, S,
+                m, ceff, nm);
 }
 
 // The staging: per-wave copies when a row group is the whole workgroup (each
@@ -246,24 +390,24 @@ int ws_groups(int ceff) {
   return R;
 }
 
-template <int MODE, int R, bool TL>
+template <int MODE, int R, bool TL, bool NORM>
 hipError_t launch_ws_staged(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
-                            int S, hipStream_t st) {
+                            int S, const NormArgs& nm, hipStream_t st) {
   switch (ws_stage(R, tab, K, MODE, xq, xl, xs)) {
-    case WS_DMA: return launch_ws<MODE, R, WS_DMA, TL>(tab, K, xq, xl, xs, S, st);
-    case WS_LOCAL: return launch_ws<MODE, R, WS_LOCAL, TL>(tab, K, xq, xl, xs, S, st);
-    default: return launch_ws<MODE, R, WS_BARRIER, TL>(tab, K, xq, xl, xs, S, st);
+    case WS_DMA: return launch_ws<MODE, R, WS_DMA, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
+    case WS_LOCAL: return launch_ws<MODE, R, WS_LOCAL, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
+    default: return launch_ws<MODE, R, WS_BARRIER, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
   }
 }
 
-template <int MODE, bool TL>
+template <int MODE, bool TL, bool NORM = false>
 hipError_t launch_ws_mode(const PartTable& tab, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, int S,
-                          int R, hipStream_t st) {
+                          int R, hipStream_t st, const NormArgs& nm = NormArgs{}) {
   switch (R) {
-    case 1: return launch_ws_staged<MODE, 1, TL>(tab, K, xq, xl, xs, S, st);
-    case 2: return launch_ws_staged<MODE, 2, TL>(tab, K, xq, xl, xs, S, st);
-    case 3: return launch_ws_staged<MODE, 3, TL>(tab, K, xq, xl, xs, S, st);
-    default: return launch_ws_staged<MODE, 4, TL>(tab, K, xq, xl, xs, S, st);
+    case 1: return launch_ws_staged<MODE, 1, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
+    case 2: return launch_ws_staged<MODE, 2, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
+    case 3: return launch_ws_staged<MODE, 3, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
+    default: return launch_ws_staged<MODE, 4, TL, NORM>(tab, K, xq, xl, xs, S, nm, st);
   }
 }
 
@@ -323,6 +467,33 @@ hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, in
                               const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
                               hipStream_t st, bool tiled) {
   return launch_gemv_wsplit_parts(mode, 1, &wq, &ws, &N, &y, K, xq, xl, xs, splits, st, tiled);
+}
+
+size_t gemv_norm_workspace_bytes(int64_t N) { return (size_t)((N * 4 + 255) / 256) * 256; }
+int64_t gemv_norm_max_n() { return WS_LDS_MAX / 4; }
+
+hipError_t launch_gemv_wsplit_norm(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,
+                                   const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
+                                   const float* r, float* s, const float* w, float eps, int qmode, float* yn,
+                                   int8_t* hq, int8_t* hl, float* hs, void* workspace, hipStream_t st) {
+  int m, ceff;
+  ws_chunks(K, splits, m, ceff);
+  const int R = ws_groups(ceff);
+  PartTable tab;
+  if (!make_parts(tab, 1, &wq, &ws, &y, &N, 4 * R)) return hipErrorInvalidValue;
+  NormArgs nm;
+  nm.r = r;
+  nm.s = s;
+  nm.w = w;
+  nm.yn = yn;
+  nm.hq = hq;
+  nm.hl = hl;
+  nm.hs = hs;
+  nm.eps = eps;
+  nm.qmode = qmode;
+  nm.slots = (unsigned*)workspace;
+  if (mode == 1) return launch_ws_mode<1, false, true>(tab, K, xq, xl, xs, splits, R, st, nm);
+  return launch_ws_mode<2, false, true>(tab, K, xq, xl, xs, splits, R, st, nm);
 }
 
 #ifdef QDG_PHASE_STAMPS

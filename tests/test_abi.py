@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 30
+    assert len(names) == 33
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -212,6 +212,58 @@ def test_rmsnorm_quantize_validation():
     assert call(xq=A + 4) == EALIGN
     assert call(xs=A + 2) == EALIGN
     assert call(mode=0, y=A + 4, xq=None, xs=None) == EALIGN
+
+
+def test_gemv_rmsnorm_validation():
+    f = lib.qdg_gemv_q8_rmsnorm
+    nmax = q.gemv_rmsnorm_max_n()
+    assert nmax % 32 == 0 and 16384 <= nmax <= q.rmsnorm_max_k()
+    assert q.gemv_rmsnorm_workspace_bytes(5120) == 5120 * 4
+    assert q.gemv_rmsnorm_workspace_bytes(96) == 512                # one word a row, in 256-byte lines
+    assert q.gemv_rmsnorm_workspace_bytes(0) == 0
+    assert q.gemv_rmsnorm_workspace_bytes(100) == 0                 # not whole 32-value blocks
+    assert q.gemv_rmsnorm_workspace_bytes(nmax + 32) == 0
+    need = q.gemv_rmsnorm_workspace_bytes(512)
+
+    def call(mode=1, wq=A, ws=A, N=512, K=8192, xq=A, xl=None, xs=A, S=4, y=A, r=A, s=A, w=A, eps=1e-6, qm=1,
+             yn=None, hq=A, hl=None, hs=A, wsp=A, nbytes=None):
+        return f(mode, P(wq), P(ws), N, K, P(xq), P(xl), P(xs), S, P(y), P(r), P(s), P(w), eps, qm, P(yn), P(hq),
+                 P(hl), P(hs), P(wsp), need if nbytes is None else nbytes, None)
+
+    assert call(mode=0) == EMODE                          # the GEMV side reads words
+    assert call(mode=3) == EINVAL
+    assert call(mode=2) == EINVAL                         # TwoPass needs xl
+    assert call(xl=A) == EINVAL
+    assert call(wq=None) == EINVAL
+    assert call(wsp=None) == EINVAL
+    assert call(qm=3) == EINVAL
+    assert call(qm=2) == EINVAL                           # TwoPass words need hl
+    assert call(qm=1, hl=A) == EINVAL
+    assert call(qm=0) == EINVAL                           # Dequant writes yn only
+    assert call(qm=0, yn=A, hq=None, hs=None, N=500) == ESHAPE   # Dequant outputs pass to the shape checks
+    assert call(qm=0, yn=A + 4, hq=None, hs=None) == EALIGN
+    assert call(hs=None) == EINVAL
+    assert call(r=None) == EINVAL                         # s needs r
+    assert call(eps=-1.0) == EINVAL
+    assert call(eps=float("nan")) == EINVAL
+    assert call(N=500) == ESHAPE                          # whole 32-value blocks of the norm
+    assert call(N=nmax + 32) == ESHAPE
+    assert call(K=500) == ESHAPE
+    assert call(S=0) == ESHAPE
+    assert call(S=65) == ESHAPE
+    assert call(S=1) == EMODE                             # no split: nothing meets in a workgroup
+    assert call(S=17) == EMODE
+    assert call(mode=2, xl=A, K=65536, S=16) == EMODE     # the staged row exceeds the LDS budget
+    assert call(wq=A + 8) == EALIGN
+    assert call(ws=A + 1) == EALIGN
+    assert call(y=A + 2) == EALIGN
+    assert call(r=A + 4) == EALIGN
+    assert call(s=A + 8) == EALIGN
+    assert call(w=A + 4) == EALIGN
+    assert call(hq=A + 4) == EALIGN
+    assert call(hs=A + 2) == EALIGN
+    assert call(wsp=A + 8) == EALIGN
+    assert call(nbytes=need - 4) == EWORKSPACE
 
 
 def test_swiglu_quantize_validation():
