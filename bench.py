@@ -75,7 +75,7 @@ def dominant_kernel(path: str, mode: int, sh, S: int, tiled: bool = False) -> tu
         # aligned), else the workgroup copy (0)
         stage = 1 if rows == 4 else (2 if sh.K % 256 == 0 else 0)
         tl = "true" if tiled else "false"
-        return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}, {tl}>", 64 * waves * -(-sh.N // rows)
+        return f"k_gemv_wsplit<{mode}, {rows // 4}, 1, 4, {stage}, {tl}, false>", 64 * waves * -(-sh.N // rows)
     flags = {"staged": "false, false", "fused": "true, false", "single": "true, true"}[path]
     return f"k_gemv_dot4<{mode}, 4, 4, {flags}, false>", 256 * -(-sh.N // 16) * S
 

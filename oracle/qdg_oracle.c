@@ -419,9 +419,9 @@ int orc_swiglu(const float *g, const float *u, int64_t n, float *h)
  * Block formats other than the split Q8_0 -- [P1] module doc (a matrix in any
  * other GGUF format keeps its blocks as stored; a 32-weight sub-block decodes to
  * int8 levels with a scale d and an offset c per half of 16, weight = d*level +
- * c) and BLOCKS (lk_sub: the per-format decoders, lk_h, lk_e8m0_half,
- * lk_scale_min_k4, lk_iq4_level, lk_iq4xs_scale).  Format ids are the GGUF type
- * numbers.  The byte layouts below are those decoders' reading of each block.
+ * c) and BLOCKS (which formats, and what each block's fields mean).  Format ids
+ * are the GGUF type numbers.  Each decoder below is written from the GGUF block
+ * layout itself, every field located by its byte or bit position in the block.
  *
  * Geometry: values per block (32, or 256 for a super-block) and bytes per block.
  */
@@ -460,17 +460,28 @@ static float orc_h16(const uint8_t *p) { return orc_half((uint16_t)(p[0] | (p[1]
  * table below is doubled (so its levels are integers): 2^(e-128). */
 static float orc_e8m0_half(uint8_t e) { return ldexpf(1.0f, (int)e - 128); }
 
-/* [P1] lk_scale_min_k4: the 6-bit scale and min of sub-block j (0..7) of a
- * Q4_K / Q5_K super-block from its 12 packed bytes q. */
-static void orc_scale_min_k4(int j, const uint8_t *q, int *sc, int *m)
+/* Bits [pos, pos + width) of the block at p, read as one little-endian bit
+ * string (bit pos is bit pos mod 8 of byte pos / 8), lowest bit first. */
+static unsigned orc_bits(const uint8_t *p, int pos, int width)
 {
-    if (j < 4) {
-        *sc = q[j] & 63;
-        *m = q[j + 4] & 63;
-    } else {
-        *sc = (q[j + 4] & 15) | ((q[j - 4] >> 6) << 4);
-        *m = (q[j + 4] >> 4) | ((q[j] >> 6) << 4);
-    }
+    unsigned v = 0;
+    for (int i = 0; i < width; ++i) v |= (unsigned)((p[(pos + i) >> 3] >> ((pos + i) & 7)) & 1u) << i;
+    return v;
+}
+
+/* The 12-byte (96-bit) scale field of a Q4_K / Q5_K super-block holds eight
+ * six-bit scales and eight six-bit mins, one pair per 32-weight sub-block j:
+ *   j < 4:  scale = bits 8j .. 8j+5,            min = bits 32+8j .. 32+8j+5;
+ *   j >= 4 (i = j - 4): the low four bits of scale are bits 64+8i .. 64+8i+3 and
+ *           of min bits 64+8i+4 .. 64+8i+7; their high two bits are the spare
+ *           top bits of the first two groups, bits 8i+6, 8i+7 (scale) and
+ *           32+8i+6, 32+8i+7 (min). */
+static int orc_k4_field(const uint8_t *s12, int j, int is_min)
+{
+    const int base = is_min ? 32 : 0;
+    if (j < 4) return (int)orc_bits(s12, base + 8 * j, 6);
+    const int i = j - 4;
+    return (int)(orc_bits(s12, 64 + 8 * i + (is_min ? 4 : 0), 4) | (orc_bits(s12, base + 8 * i + 6, 2) << 4));
 }
 
 /* [P1] lk_iq4_level: the sixteen non-linear IQ4 levels. */
@@ -521,31 +532,42 @@ static int orc_decode_sub(int fmt, const uint8_t *row, int64_t sb, int8_t *v, fl
             v[i + 16] = ORC_E2M1X2[b[1 + i] >> 4];
         }
     } else if (fmt == ORC_Q4_K || fmt == ORC_Q5_K) {
-        const uint8_t *b = row + (sb >> 3) * (fmt == ORC_Q4_K ? 144 : 176);
-        const int j = (int)(sb & 7), pair = j >> 1, upper = j & 1;
-        int sc, m;
-        orc_scale_min_k4(j, b + 4, &sc, &m);
-        d[0] = d[1] = orc_h16(b) * (float)sc;
-        c[0] = c[1] = -(orc_h16(b + 2) * (float)m);
-        /* 32 bytes of nibbles per pair of sub-blocks: the low nibbles are the even
-         * sub-block, the high nibbles the odd one; Q5_K's fifth bits sit in 32
-         * bytes after the scales, bit 2*pair + upper of byte l for weight l */
-        const uint8_t *ql = b + (fmt == ORC_Q4_K ? 16 : 48) + 32 * pair;
+        /* Q4_K, 144 bytes: d (binary16, bytes 0-1), dmin (binary16, bytes 2-3),
+         * the scale field (bytes 4-15), 128 bytes of four-bit levels (from byte 16).
+         * Q5_K, 176 bytes: the same head, then 32 bytes of fifth bits (bytes
+         * 16-47), then the four-bit levels (from byte 48).  Weight l (0..31) of
+         * sub-block j: its four bits are bits 4*(j mod 2) .. +3 of level byte
+         * 32*(j/2) + l (two sub-blocks share 32 bytes, the even one in the low
+         * nibbles); under Q5_K its fifth bit (worth 16) is bit j of fifth-bit
+         * byte l.  weight = d*scale_j*level - dmin*min_j. */
+        const int q5 = fmt == ORC_Q5_K;
+        const uint8_t *b = row + (sb >> 3) * (q5 ? 176 : 144);
+        const int j = (int)(sb & 7);
+        const int lev0 = q5 ? 48 : 16;
+        d[0] = d[1] = orc_h16(b) * (float)orc_k4_field(b + 4, j, 0);
+        c[0] = c[1] = -(orc_h16(b + 2) * (float)orc_k4_field(b + 4, j, 1));
         for (int l = 0; l < 32; ++l) {
-            int lv = upper ? ql[l] >> 4 : ql[l] & 15;
-            if (fmt == ORC_Q5_K && (b[16 + l] >> (2 * pair + upper)) & 1) lv += 16;
+            unsigned lv = orc_bits(b, 8 * (lev0 + 32 * (j / 2) + l) + 4 * (j % 2), 4);
+            if (q5) lv |= orc_bits(b, 8 * (16 + l) + j, 1) << 4;
             v[l] = (int8_t)lv;
         }
     } else if (fmt == ORC_Q2_K) {
+        /* Q2_K, 84 bytes: sixteen scale bytes (one per 16-weight group g: scale in
+         * bits 0-3, min in bits 4-7), 64 bytes of two-bit levels (bytes 16-79),
+         * d (binary16, bytes 80-81), dmin (binary16, bytes 82-83).  Weight w
+         * (0..255) of the super-block: with h = w / 128, k = (w mod 128) / 32 and
+         * l = w mod 32, its level is bits 2k, 2k+1 of level byte 32h + l.
+         * weight = d*scale_g*level - dmin*min_g with g = w / 16. */
         const uint8_t *b = row + (sb >> 3) * 84;
-        const int j = (int)(sb & 7), half = j >> 2, k = j & 3;
-        const uint8_t *q = b + 16 + 32 * half;
         const float dd = orc_h16(b + 80), dm = orc_h16(b + 82);
-        for (int l = 0; l < 32; ++l) v[l] = (int8_t)((q[l] >> (2 * k)) & 3);
+        for (int l = 0; l < 32; ++l) {
+            const int w = 32 * (int)(sb & 7) + l;
+            v[l] = (int8_t)orc_bits(b, 8 * (16 + 32 * (w / 128) + w % 32) + 2 * ((w % 128) / 32), 2);
+        }
         for (int h = 0; h < 2; ++h) {
-            const int sc = b[8 * half + 2 * k + h];
-            d[h] = dd * (float)(sc & 15);
-            c[h] = -(dm * (float)(sc >> 4));
+            const int g = 2 * (int)(sb & 7) + h;
+            d[h] = dd * (float)orc_bits(b, 8 * g, 4);
+            c[h] = -(dm * (float)orc_bits(b, 8 * g + 4, 4));
         }
     } else if (fmt == ORC_Q3_K) {
         const uint8_t *b = row + (sb >> 3) * 110;
@@ -582,17 +604,17 @@ static int orc_decode_sub(int fmt, const uint8_t *row, int64_t sb, int8_t *v, fl
         d[0] = dd * (float)sc[2 * k];
         d[1] = dd * (float)sc[2 * k + 1];
     } else if (fmt == ORC_IQ4_XS) {
+        /* IQ4_XS, 136 bytes: d (binary16, bytes 0-1); the high two bits of the
+         * eight six-bit sub-block scales (bits 16 + 2j, 16 + 2j + 1: bytes 2-3);
+         * their low four bits (bits 32 + 4j .. 32 + 4j + 3: bytes 4-7); 128 bytes
+         * of four-bit indices (from byte 8).  Sub-block j's scale is
+         * d * (six-bit value - 32); weight l (0..31) of it is the IQ4 level of
+         * bits 4*(l / 16) .. +3 of index byte 16j + l mod 16. */
         const uint8_t *b = row + (sb >> 3) * 136;
-        const int ib = (int)(sb & 7);
-        const unsigned sh = (unsigned)b[2] | ((unsigned)b[3] << 8);
-        const unsigned sl = b[4 + (ib >> 1)];
-        const int ls = (int)((sl >> (4 * (ib & 1))) & 15) | (int)(((sh >> (2 * ib)) & 3) << 4);
+        const int j = (int)(sb & 7);
+        const int ls = (int)(orc_bits(b, 32 + 4 * j, 4) | (orc_bits(b, 16 + 2 * j, 2) << 4));
         d[0] = d[1] = orc_h16(b) * (float)(ls - 32);
-        const uint8_t *qs = b + 8 + 16 * ib;
-        for (int i = 0; i < 16; ++i) {
-            v[i] = ORC_IQ4[qs[i] & 15];
-            v[i + 16] = ORC_IQ4[qs[i] >> 4];
-        }
+        for (int l = 0; l < 32; ++l) v[l] = ORC_IQ4[orc_bits(b, 8 * (8 + 16 * j + l % 16) + 4 * (l / 16), 4)];
     } else {
         return -1;
     }
