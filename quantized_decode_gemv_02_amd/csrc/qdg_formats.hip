@@ -59,12 +59,30 @@ __device__ __forceinline__ unsigned ld_u16(const uint8_t* p) { return *(const un
 __device__ __forceinline__ unsigned ld_u32(const uint8_t* p) { return *(const unsigned*)p; }
 __device__ __forceinline__ float h16(unsigned bits) { return half_bits_to_float((unsigned short)(bits & 0xffff)); }
 
-// n dwords from p at any alignment: one byte copy, which the compiler turns into
-// the widest loads the address allows (the decoders read the wave's LDS copy
-// of the blocks, where unaligned multi-dword reads are single instructions).
-template <int NW>
+// n dwords from p (in the wave's LDS slot) at any alignment.  REALIGN: the
+// n + 1 aligned dwords that hold them, realigned by byte shifts (v_alignbyte);
+// the extra dword is read only when p is misaligned, and then holds the last
+// bytes wanted, so no read leaves the block.  Otherwise one byte copy, which
+// the compiler turns into multi-dword reads at p's alignment.  The hardware
+// splits a misaligned multi-dword LDS read into many accesses: the super-blocks
+// of Q3_K (110 bytes) and Q6_K (210) decoded at the speed of those splits, and
+// the realigned reads cut their GEMV from 40 to 27 and from 39 to 29 us on
+// 5120x25600; on the 32-value blocks (17-22 bytes, fewer words a lane) the
+// byte copy is 3-6% faster.
+template <int NW, bool REALIGN = false>
 __device__ __forceinline__ void ld_words(const uint8_t* p, unsigned* w) {
-  __builtin_memcpy(w, p, 4 * NW);
+  if constexpr (REALIGN) {
+    const unsigned mis = (unsigned)(uintptr_t)p & 3u;
+    const unsigned* a = (const unsigned*)(p - mis);  // pointer arithmetic keeps the LDS address space
+    unsigned d[NW + 1];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) d[i] = a[i];
+    d[NW] = a[mis ? NW : NW - 1];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], mis);
+  } else {
+    __builtin_memcpy(w, p, 4 * NW);
+  }
 }
 
 // The low nibbles of a word's four bytes and the high ones, as bytes.
@@ -203,8 +221,8 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
   } else if constexpr (F == F_Q6_K) {
     const int half = j >> 2, k = j & 3;
     unsigned ql[8], qh[8];
-    ld_words<8>(b + 64 * half + 32 * (k & 1), ql);
-    ld_words<8>(b + 128 + 32 * half, qh);
+    ld_words<8, true>(b + 64 * half + 32 * (k & 1), ql);
+    ld_words<8, true>(b + 128 + 32 * half, qh);
     const unsigned scw = ld_u16(b + 192 + 8 * half + 2 * k);
     const float dd = h16(ld_u16(b + 208));
     s.d[0] = __fmul_rn(dd, (float)(int)(signed char)(scw & 255));
@@ -232,9 +250,9 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
   } else if constexpr (F == F_Q3_K) {
     const int half = j >> 2, k = j & 3;
     unsigned hm[8], q[8], sp[3];
-    ld_words<8>(b, hm);
-    ld_words<8>(b + 32 + 32 * half, q);
-    ld_words<3>(b + 96, sp);
+    ld_words<8, true>(b, hm);
+    ld_words<8, true>(b + 32 + 32 * half, q);
+    ld_words<3, true>(b + 96, sp);
     const float dd = h16(ld_u16(b + 108));
     auto spb = [&](int i) {  // byte i of the 12 scale bytes (word picked by selects, not an indexed array)
       const unsigned wd = (i >> 2) == 0 ? sp[0] : (i >> 2) == 1 ? sp[1] : sp[2];

@@ -1,9 +1,14 @@
 """Summaries of rocprofv3 runs of the benchmark (kernel-trace statistics and the
 FETCH_SIZE / WRITE_SIZE byte counters), written as short text under profiles/.
 
-The byte counters are scaled by what the same counter reads for a plain device
-copy of 256 MiB (``bench.py --calibrate-copy``): the copy reads and writes exactly
-268435456 bytes, so ``factor = 262144 KiB / counter(copy)`` per counter.
+FETCH_SIZE is scaled by what it reads for the library's own streaming read of
+1 GiB (k_stream_read over exactly 2^30 bytes, the benchmark's read-ceiling
+pass): factor = 2^30 bytes / counter(that dispatch).  On gfx950 the counter
+gives half the bytes for every kernel of this library (the streaming read, the
+GEMVs, the LDS-DMA batched kernel alike), which are all 16-byte loads; the
+runtime's copy kernel reads 1.0-1.6x its bytes on the same counter, so it is
+not used.  WRITE_SIZE is reported as counted (KiB x 1024): the library's
+kernels write only their outputs.
 
 Usage (from the repository root, after the rocprofv3 runs):
     python -m quantized_decode_gemv_02_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT.md OUT.json \
@@ -19,15 +24,21 @@ import os
 import sys
 from collections import defaultdict
 
-COPY_BYTES = 256 << 20
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
+READ_BYTES = 1 << 30
+READ_KERNEL = "k_stream_read"
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-def kernel_source_sha() -> str:
-    """Hash of the kernel sources, so a stored byte count is used only for the code it was taken on."""
+# The translation unit of the step's dominant kernel (the in-workgroup split-K GEMV):
+# a stored byte count stands only while these sources are unchanged.
+DOMINANT_SOURCES = (os.path.join(CSRC, "qdg_wsplit.hip"), os.path.join(CSRC, "qdg_device.h"),
+                    os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdg.h"))
+
+
+def kernel_source_sha(paths=DOMINANT_SOURCES) -> str:
+    """Hash of the dominant kernel's sources, so a stored byte count is used only for the code it was taken on."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for p in paths:
         h.update(os.path.basename(p).encode())
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
@@ -104,9 +115,9 @@ def short(name: str) -> str:
 
 
 def scale_factor(rows: list[dict]) -> float:
-    """KiB-to-bytes factor from the largest copy dispatch (the 256 MiB calibration copy)."""
-    best = max(float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith(COPY_KERNEL))
-    return COPY_BYTES / best
+    """KiB-to-bytes factor from the largest streaming-read dispatch (the 1 GiB read)."""
+    best = max(float(r["Counter_Value"]) for r in rows if short(r["Kernel_Name"]) == READ_KERNEL)
+    return READ_BYTES / best
 
 
 def per_kernel_grid(rows: list[dict]) -> dict:
@@ -129,7 +140,7 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
               occ_dir: str | None = None):
     ks = kernel_stats(trace_dir)
     fr, wr = counters(fetch_dir), counters(write_dir)
-    ff, wf = scale_factor(fr), scale_factor(wr)
+    ff, wf = scale_factor(fr), 1024.0
     fk, wk = per_kernel_grid(fr), per_kernel_grid(wr)
     lines = [f"# rocprofv3 summary: {os.path.basename(out_md)[:-3]}", "",
              "Commands (from the repository root):", "", "```", command, "```", "",
@@ -145,8 +156,8 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
         a, lo, hi, n = tg[key]
         lines.append(f"| {key[0]} | {key[1]} | {n} | {a / 1e3:.2f} | {lo / 1e3:.2f} | {hi / 1e3:.2f} |")
     lines += ["", "## HBM bytes per dispatch (--pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
-              f"Scale: the 256 MiB calibration copy reads FETCH_SIZE x {ff:.4f} and WRITE_SIZE x {wf:.4f} "
-              "bytes per KiB counted.", "",
+              f"Scale: FETCH_SIZE x {ff:.2f} bytes per KiB counted (the 1 GiB streaming read, k_stream_read, "
+              "counts 2^30 bytes); WRITE_SIZE x 1024 (as counted).", "",
               "| kernel | grid (work-items) | dispatches | fetch MB (mean) | fetch MB (min..max) | write MB (mean) |",
               "|---|---|---|---|---|---|"]
     for key in sorted(fk):
