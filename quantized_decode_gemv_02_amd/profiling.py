@@ -35,6 +35,16 @@ DOMINANT_SOURCES = (os.path.join(CSRC, "qdg_wsplit.hip"), os.path.join(CSRC, "qd
                     os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdg.h"))
 
 
+def sources_for(kernel: str) -> tuple:
+    """The translation unit of a traced kernel, for the hash stored beside its byte count."""
+    unit = {"k_gemv_fmt": "qdg_formats.hip", "k_gemv_dq_seg": "qdg_dequant_seg.hip",
+            "k_gemv_mfma": "qdg_mfma.hip", "k_gemv_dot4": "qdg_gemv.hip"}
+    for prefix, f in unit.items():
+        if kernel.startswith(prefix):
+            return (os.path.join(CSRC, f),) + DOMINANT_SOURCES[1:]
+    return DOMINANT_SOURCES
+
+
 def kernel_source_sha(paths=DOMINANT_SOURCES) -> str:
     """Hash of the dominant kernel's sources, so a stored byte count is used only for the code it was taken on."""
     h = hashlib.sha256()
@@ -187,7 +197,7 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
         waves = f"{m['SQ_WAVES']:.0f}" if "SQ_WAVES" in m else "-"
         lines.append(f"| {key[0]} | {key[1]} | {v}+{a} | {l} | {o['waves_per_simd']} | {o['wg_per_cu']} | "
                      f"{o['workgroups']} | {o['fill']:.2f} | {o['rounds']:.2f} | {waves} |")
-    dom = {"kernel": dominant[0], "grid": dominant[1], "kernel_source_sha": kernel_source_sha()}
+    dom = {"kernel": dominant[0], "grid": dominant[1], "kernel_source_sha": kernel_source_sha(sources_for(dominant[0]))}
     if (dominant[0], dominant[1]) in tg:
         dom["trace_avg_us"] = tg[(dominant[0], dominant[1])][0] / 1e3
     if (dominant[0], dominant[1]) in fk:
