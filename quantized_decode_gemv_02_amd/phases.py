@@ -10,8 +10,15 @@ is also timed by its own dispatch (qdg_time_next_launch).  The summary gives,
 per projection and mode, the launch duration, the spread of wave entries, the
 staging latency, the streaming time of a wave, and the spread of exits.
 
+Each timed launch follows the buffer clearing and the stamp set-up (a fill
+kernel and a copy).  With --step it also follows a fresh run of the activation
+quantizer into the words the GEMV stages, as in the benchmark's step.  With
+--pair the same GEMV (another weight copy) runs once more right before it, so
+the timed launch follows a launch of itself, as in back-to-back timing; the
+stamps are those of the second launch, which overwrites the first's.
+
 Usage (from the repository root, on a GPU):
-    python -m quantized_decode_gemv_02_amd.phases [OUT.md] [--reps N]
+    python -m quantized_decode_gemv_02_amd.phases [OUT.md] [--reps N] [--step | --pair]
 """
 from __future__ import annotations
 
@@ -57,7 +64,7 @@ def pct(v, p):
     return v[min(len(v) - 1, int(p / 100 * len(v)))]
 
 
-def measure(reps: int) -> dict:
+def measure(reps: int, step: bool = False, pair: bool = False) -> dict:
     """Runs in the process whose sys.path starts with the variant build."""
     import ctypes
 
@@ -96,7 +103,11 @@ def measure(reps: int) -> dict:
                    "last_entry": [], "first_exit": [], "xcc_exit": {}}
             for i in range(reps):
                 buf.zero_()
+                if step:
+                    q.quantize_act(mode, x, xq, xl, xs)
                 lib.qdg_debug_phase_stamps(ctypes.c_void_p(buf.data_ptr()))
+                if pair:
+                    calls[(i + 1) % len(calls)]()
                 q.time_next_launch(*ev)
                 calls[i % len(calls)]()
                 lib.qdg_debug_phase_stamps(None)
@@ -137,8 +148,11 @@ def measure(reps: int) -> dict:
     return out
 
 
-def to_markdown(res: dict, cmd: str) -> str:
-    lines = ["# Phase stamps of k_gemv_wsplit (in-workgroup split-K GEMV), narrow projections", "",
+def to_markdown(res: dict, cmd: str, step: bool = False, pair: bool = False) -> str:
+    title = "# Phase stamps of k_gemv_wsplit (in-workgroup split-K GEMV), narrow projections" + \
+        (", each launch right after the activation quantizer" if step else "") + \
+        (", each launch right after a launch of itself" if pair else "")
+    lines = [title, "",
              "Command (from the repository root, on one MI355X):", "", "```", cmd, "```", "",
              "A debug build (`-DQDG_PHASE_STAMPS`, built by the command into `_build/phase_stamps/`) has every "
              "wave record the 100 MHz constant clock at its entry, after issuing its first loads, when its "
@@ -164,14 +178,15 @@ def to_markdown(res: dict, cmd: str) -> str:
 def main(argv: list[str]) -> int:
     if len(argv) > 1 and argv[1] == "--child":
         reps = int(argv[2])
-        print("PHASES_JSON " + json.dumps(measure(reps)), flush=True)
+        print("PHASES_JSON " + json.dumps(measure(reps, "--step" in argv, "--pair" in argv)), flush=True)
         return 0
     out_md = argv[1] if len(argv) > 1 and not argv[1].startswith("--") else None
     reps = int(argv[argv.index("--reps") + 1]) if "--reps" in argv else 30
     variant = build_variant()
     print(f"phase-stamp build in {variant}", flush=True)
     env = dict(os.environ, PYTHONPATH=os.pathsep.join([variant, ROOT]))
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--child", str(reps)],
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--child", str(reps)] +
+                       [a for a in ("--step", "--pair") if a in argv],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     sys.stderr.write(r.stderr[-2000:])
     if r.returncode != 0:
@@ -180,7 +195,7 @@ def main(argv: list[str]) -> int:
     if out_md:
         open(os.path.splitext(out_md)[0] + ".json", "w").write(json.dumps(res, indent=1))
     cmd = "python -m quantized_decode_gemv_02_amd.phases " + " ".join(argv[1:])
-    md = to_markdown(res, cmd)
+    md = to_markdown(res, cmd, "--step" in argv, "--pair" in argv)
     if out_md:
         os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
         open(out_md, "w").write(md)
