@@ -73,7 +73,9 @@ enum : int {
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  // bound_ctrl: a lane whose source is outside its row reads 0 (the same as an
+  // old value of 0 with bound_ctrl off, without the move that sets it up)
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

@@ -227,9 +227,12 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
     const float dd = h16(ld_u16(b + 208));
     s.d[0] = __fmul_rn(dd, (float)(int)(signed char)(scw & 255));
     s.d[1] = __fmul_rn(dd, (float)(int)(signed char)(scw >> 8));
+    // the nibble (low for k < 2, high otherwise) and bits 2k, 2k+1 of each qh byte
+    // rotated to bits 4, 5 of the same byte
+    const unsigned nsh = 4u * (unsigned)(k >> 1), rot = (unsigned)(2 * k - 4) & 31u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      s.w[i] = ((k & 2) ? hi_nib(ql[i]) : lo_nib(ql[i])) | (((qh[i] >> (2 * k)) & 0x03030303u) << 4);
+      s.w[i] = ((ql[i] >> nsh) & 0x0f0f0f0fu) | (__builtin_amdgcn_alignbit(qh[i], qh[i], rot) & 0x30303030u);
     s.off = 32;
   } else if constexpr (F == F_Q2_K) {
     const int half = j >> 2, k = j & 3;  // b 4-byte aligned: 84 is a multiple of 4
@@ -265,9 +268,11 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
       const unsigned hi2 = (spb(8 + (i & 3)) >> (2 * (i >> 2))) & 3u;
       s.d[h] = __fmul_rn(dd, (float)((int)(lo4 | (hi2 << 4)) - 32));
     }
-    const int mbit = 4 * half + k;
+    // bit mbit of each high-mask byte rotated to bit 2 of the same byte
+    const unsigned rot = (unsigned)(4 * half + k - 2) & 31u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s.w[i] = ((q[i] >> (2 * k)) & 0x03030303u) | (((hm[i] >> mbit) & 0x01010101u) << 2);
+    for (int i = 0; i < 8; ++i)
+      s.w[i] = ((q[i] >> (2 * k)) & 0x03030303u) | (__builtin_amdgcn_alignbit(hm[i], hm[i], rot) & 0x04040404u);
     s.off = 4;  // level = low2 - 4 + 4*high bit
   } else if constexpr (F == F_IQ4_XS) {
     const int ib = j;  // b 8-byte aligned
@@ -298,24 +303,36 @@ constexpr bool needs_sums() {
   return has_offsets<F>() || F == F_Q4_0 || F == F_Q5_0 || F == F_Q3_K || F == F_Q6_K;
 }
 
-// part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8].
+// The activation sums of a sub-block's two halves (sh0, sh1): each half's
+// four words dotted with ones.  Each lane forms them for its own sub-block (a
+// wave's four rows repeat them): forming them once per wave into LDS measured
+// 5-15% slower, its registers and LDS reads costing more than the dots.
+__device__ __forceinline__ int2 act_sums(const int (&a)[8]) {
+  int s0 = 0, s1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s0 = __builtin_amdgcn_sdot4(0x01010101, a[i], s0, false);
+    s1 = __builtin_amdgcn_sdot4(0x01010101, a[4 + i], s1, false);
+  }
+  return make_int2(s0, s1);
+}
+
+// part = ((d0*dh0 + c0*sh0) + d1*dh1) + c1*sh1 with the activation words a[8]
+// and their half sums sh (for the formats that need them).
 // Where c = 0 and the levels are signed (IQ4_NL, IQ4_XS, MXFP4) the c terms are
 // left out: each is a zero, which can change only the sign of a zero part, and
 // fma(s, +-0, p) is p for every p the row can hold (it starts at +0 and a sum
 // of nonzero terms that cancels rounds to +0), so the row's bits are the same.
 template <int F>
-__device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8]) {
-  int dh0 = 0, dh1 = 0, sh0 = 0, sh1 = 0;
+__device__ __forceinline__ float sub_part(const Sub& s, const int (&a)[8], int2 sh) {
+  int dh0 = 0, dh1 = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dh0 = __builtin_amdgcn_sdot4((int)s.w[i], a[i], dh0, false);
     dh1 = __builtin_amdgcn_sdot4((int)s.w[4 + i], a[4 + i], dh1, false);
-    if constexpr (needs_sums<F>()) {
-      sh0 = __builtin_amdgcn_sdot4(0x01010101, a[i], sh0, false);
-      sh1 = __builtin_amdgcn_sdot4(0x01010101, a[4 + i], sh1, false);
-    }
   }
   if constexpr (!needs_sums<F>()) return __fadd_rn(__fmul_rn(s.d[0], (float)dh0), __fmul_rn(s.d[1], (float)dh1));
+  const int sh0 = sh.x, sh1 = sh.y;
   dh0 -= s.off * sh0;
   dh1 -= s.off * sh1;
   float part = __fmul_rn(s.d[0], (float)dh0);
@@ -330,6 +347,7 @@ template <int MODE>
 struct Act {
   int a[8], l[8];
   float s;
+  int2 sh, sl;  // half sums of a and of l (formats that need them)
 };
 template <>
 struct Act<0> {
@@ -394,8 +412,8 @@ __device__ __forceinline__ void sub_term(const uint8_t* __restrict__ b, int j, c
     }
     tb = 0.0;
   } else {
-    float part = sub_part<F>(s, A.a);
-    if constexpr (MODE == 2) part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part<F>(s, A.l)));
+    float part = sub_part<F>(s, A.a, A.sh);
+    if constexpr (MODE == 2) part = __fadd_rn(part, __fmul_rn(0.0078125f, sub_part<F>(s, A.l, A.sl)));
     ta = A.s;
     tb = part;
   }
@@ -504,23 +522,45 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   // A fetch: piece t = lane + 64k is weight piece t % CPR of row t / CPR
   // (t < NCH), or under Dequant activation piece t - NCH (t < NT).  The next
   // step's fetch is issued before this step is summed.  Every fetch issues the
-  // same loads whatever the step (pieces past a row's bytes, past the chunk's
-  // sub-blocks, or past the wave's pieces reread a valid piece), so no load
-  // sits behind a branch.
+  // same loads whatever the step, so no load sits behind a branch.  A piece's
+  // row base is fixed for the launch; away from the matrix end (a scalar test
+  // on the wave's last row) every piece is simply the 16 bytes at the row's
+  // step offset plus 16*pc -- bytes past the step's are loaded and never
+  // decoded -- and only a step that reaches the matrix end takes the clamped
+  // form (pieces past the chunk's sub-blocks reread a valid piece; the last
+  // piece of a matrix whose size is not a multiple of 16 is shifted into place).
+  int64_t rbase[NPL];
+  int pcs[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int t = lane + 64 * k;
+    const int tw = t < NCH ? t : 0;
+    const int64_t po = o_wg + ROWS * rg + tw / CPR;
+    rbase[k] = (po < N ? po : N - 1) * rb;
+    pcs[k] = tw % CPR;
+  }
+  const int64_t last_row = o_wg + ROWS * rg + ROWS - 1 < N ? o_wg + ROWS * rg + ROWS - 1 : N - 1;
+  const int64_t last_base = last_row * rb;  // the wave's highest row: its pieces reach furthest
   uint4 v[NPL];
   int vsh[NPL];
+  bool fixed = false;  // whether the fetch in v took the clamped form (wave-uniform)
   auto fetch = [&](int st) {
+    const bool plain = ((last_base + seg_off(st)) & ~(int64_t)15) + 16 * CPR <= total;
+    fixed = !plain;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       const int t = lane + 64 * k;
       const bool wpiece = t < NCH || t >= NT;
-      const int tw = t < NCH ? t : 0;
-      const int64_t po = o_wg + ROWS * rg + tw / CPR;
-      const int pc = tw % CPR;
-      const int64_t so = (po < N ? po : N - 1) * rb + seg_off(st);
-      const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st);
-      int sh;
-      const int64_t at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh);
+      const int pc = pcs[k];
+      const int64_t so = rbase[k] + seg_off(st);
+      int sh = 0;
+      int64_t at;
+      if (plain) {
+        at = (so & ~(int64_t)15) + 16 * pc;
+      } else {
+        const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st);
+        at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh);
+      }
       const uint8_t* src = w + at;
       if (!wpiece) {
         const int i = t - NCH;
@@ -541,48 +581,67 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   };
   fetch(g0);
 
+  // One step's terms.  FULL: the step's LPR sub-blocks all lie in the chunk, so
+  // every lane's own term and the three it folds from lanes j + 4, j + 8, j + 12
+  // are taken without a test (lanes j >= 4 fold values that are never used);
+  // the chunk's last step, when partial, tests each one.
   Acc p = 0;
-  for (int st = g0; st < g1; st += LPR) {
+  auto terms = [&](int st, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int g = st + j;  // this lane's sub-block
+    const bool ok = FULL || g < g1;
+    const int jj = ok ? j : 0;
+    Act<MODE> A;
+    if constexpr (T::ACT) {
+      const float4* xa = (const float4*)(slot + 16 * NCH + 128 * jj);
 #pragma unroll
-    for (int k = 0; k < NPL; ++k)
-      if (lane + 64 * k < NT) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
-    if (st + LPR < g1) fetch(st + LPR);  // the next step's bytes, in flight while this one is summed
-    {
-      const int g = st + j;  // this lane's sub-block
-      const bool ok = g < g1;
-      const int jj = ok ? j : 0;
-      Act<MODE> A;
-      if constexpr (T::ACT) {
-        const float4* xa = (const float4*)(slot + 16 * NCH + 128 * jj);
-#pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) A.x[q4] = xa[q4];
-      } else {
-        load_act<MODE>(ok ? g : st, x, xq, xl, xs, A);
-      }
-      const uint8_t* seg = slot + 16 * r * CPR + (int)((myrow + seg_off(st)) & 15);
-      Acc ta, tb;
-      sub_term<F, MODE>(SUP ? seg + (jj >> 3) * B : seg + jj * B, jj & 7, A, ta, tb);
-      if constexpr (MODE == 0) {
-        p = ok ? __dadd_rn(p, ta) : p;
-        const double t4 = dpp_f64<DPP_ROW_SHL4>(ta);
-        p = g + 4 < g1 ? __dadd_rn(p, t4) : p;
-        if constexpr (LPR == 16) {
-          const double t8 = dpp_f64<DPP_ROW_SHL8>(ta), t12 = dpp_f64<DPP_ROW_SHL12>(ta);
-          p = g + 8 < g1 ? __dadd_rn(p, t8) : p;
-          p = g + 12 < g1 ? __dadd_rn(p, t12) : p;
-        }
-      } else {
-        p = ok ? __fmaf_rn(ta, tb, p) : p;
-        const float a4 = dpp_f32<DPP_ROW_SHL4>(ta), b4 = dpp_f32<DPP_ROW_SHL4>(tb);
-        p = g + 4 < g1 ? __fmaf_rn(a4, b4, p) : p;
-        if constexpr (LPR == 16) {
-          const float a8 = dpp_f32<DPP_ROW_SHL8>(ta), b8 = dpp_f32<DPP_ROW_SHL8>(tb);
-          const float a12 = dpp_f32<DPP_ROW_SHL12>(ta), b12 = dpp_f32<DPP_ROW_SHL12>(tb);
-          p = g + 8 < g1 ? __fmaf_rn(a8, b8, p) : p;
-          p = g + 12 < g1 ? __fmaf_rn(a12, b12, p) : p;
-        }
+      for (int q4 = 0; q4 < 8; ++q4) A.x[q4] = xa[q4];
+    } else {
+      load_act<MODE>(ok ? g : st, x, xq, xl, xs, A);
+      if constexpr (needs_sums<F>()) {
+        A.sh = act_sums(A.a);
+        if constexpr (MODE == 2) A.sl = act_sums(A.l);
       }
     }
+    const uint8_t* seg = slot + 16 * r * CPR + (int)((myrow + seg_off(st)) & 15);
+    Acc ta, tb;
+    sub_term<F, MODE>(SUP ? seg + (jj >> 3) * B : seg + jj * B, jj & 7, A, ta, tb);
+    if constexpr (MODE == 0) {
+      p = ok ? __dadd_rn(p, ta) : p;
+      const double t4 = dpp_f64<DPP_ROW_SHL4>(ta);
+      p = FULL || g + 4 < g1 ? __dadd_rn(p, t4) : p;
+      if constexpr (LPR == 16) {
+        const double t8 = dpp_f64<DPP_ROW_SHL8>(ta), t12 = dpp_f64<DPP_ROW_SHL12>(ta);
+        p = FULL || g + 8 < g1 ? __dadd_rn(p, t8) : p;
+        p = FULL || g + 12 < g1 ? __dadd_rn(p, t12) : p;
+      }
+    } else {
+      p = ok ? __fmaf_rn(ta, tb, p) : p;
+      const float a4 = dpp_f32<DPP_ROW_SHL4>(ta), b4 = dpp_f32<DPP_ROW_SHL4>(tb);
+      p = FULL || g + 4 < g1 ? __fmaf_rn(a4, b4, p) : p;
+      if constexpr (LPR == 16) {
+        const float a8 = dpp_f32<DPP_ROW_SHL8>(ta), b8 = dpp_f32<DPP_ROW_SHL8>(tb);
+        const float a12 = dpp_f32<DPP_ROW_SHL12>(ta), b12 = dpp_f32<DPP_ROW_SHL12>(tb);
+        p = FULL || g + 8 < g1 ? __fmaf_rn(a8, b8, p) : p;
+        p = FULL || g + 12 < g1 ? __fmaf_rn(a12, b12, p) : p;
+      }
+    }
+  };
+  for (int st = g0; st < g1; st += LPR) {
+    if (fixed) {
+#pragma unroll
+      for (int k = 0; k < NPL; ++k)
+        if (lane + 64 * k < NT) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NPL; ++k)
+        if (lane + 64 * k < NT) lw[lane + 64 * k] = v[k];
+    }
+    if (st + LPR < g1) fetch(st + LPR);  // the next step's bytes, in flight while this one is summed
+    if (st + LPR <= g1)
+      terms(st, std::integral_constant<bool, true>());
+    else
+      terms(st, std::integral_constant<bool, false>());
   }
   // (P0 + P2) + (P1 + P3): partial q in lane q of the row's lanes
   Acc pr;
@@ -629,7 +688,7 @@ hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, con
   const size_t lds = (size_t)waves * Stage<F, MODE, ROWS>::SLOT + (size_t)waves * ROWS * sizeof(Acc);
   const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * waves));
   return launch((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
-                     ceff, y);
+                ceff, y);
 }
 
 // Four rows a wave (16 lanes a row) and one row group a workgroup: on the
