@@ -357,18 +357,20 @@ struct Act<0> {
 template <int MODE>
 __device__ __forceinline__ void load_act(int gc, const float* __restrict__ x, const int8_t* __restrict__ xq,
                                          const int8_t* __restrict__ xl, const float* __restrict__ xs, Act<MODE>& A) {
+  // 32-bit offsets (K < 2^31): a scalar base plus a lane offset, no 64-bit address arithmetic
+  const unsigned e = (unsigned)gc * QK;
   if constexpr (MODE == 0) {
-    const float4* xv = (const float4*)(x + (int64_t)gc * QK);
+    const float4* xv = (const float4*)(x + e);
 #pragma unroll
     for (int q4 = 0; q4 < 8; ++q4) A.x[q4] = xv[q4];
   } else {
-    const int4 a0 = *(const int4*)(xq + (int64_t)gc * QK), a1 = *(const int4*)(xq + (int64_t)gc * QK + 16);
+    const int4 a0 = *(const int4*)(xq + e), a1 = *(const int4*)(xq + e + 16u);
     A.a[0] = a0.x; A.a[1] = a0.y; A.a[2] = a0.z; A.a[3] = a0.w; A.a[4] = a1.x; A.a[5] = a1.y; A.a[6] = a1.z; A.a[7] = a1.w;
     if constexpr (MODE == 2) {
-      const int4 b0 = *(const int4*)(xl + (int64_t)gc * QK), b1 = *(const int4*)(xl + (int64_t)gc * QK + 16);
+      const int4 b0 = *(const int4*)(xl + e), b1 = *(const int4*)(xl + e + 16u);
       A.l[0] = b0.x; A.l[1] = b0.y; A.l[2] = b0.z; A.l[3] = b0.w; A.l[4] = b1.x; A.l[5] = b1.y; A.l[6] = b1.z; A.l[7] = b1.w;
     }
-    A.s = xs[gc];
+    A.s = xs[(unsigned)gc];
   }
 }
 
