@@ -417,8 +417,9 @@ int64_t qdg_fmt_row_bytes(int fmt, int64_t K);
  * tail in the last), each chunk summed as above from +0 and the chunk partials
  * added in ascending chunk order from +0 (gk_sk_combine) -- in binary32 for the
  * quantized modes, binary64 before the one rounding for QDG_DEQUANT.  splits == 1
- * is the unsplit row.  The chunks run as waves of one workgroup: at most 16
- * non-empty chunks (QDG_EMODE otherwise).
+ * is the unsplit row.  The chunks are summed by the waves of one workgroup,
+ * several chunks a wave in turn where that lets every workgroup be resident at
+ * once.
  * Batch 1.  w 16-byte aligned; x, xq, xl 16-byte aligned; y [N].  N >= 1 and K
  * a positive whole number of the format's blocks; 1 <= splits <= QDG_MAX_SPLITS
  * (QDG_EINVAL otherwise).
@@ -502,7 +503,9 @@ enum {
   QDG_TUNE_REJECT_LAUNCH = 13, /* 1: every launch asks for a 2048-thread workgroup, which the */
                            /*    HIP runtime refuses before anything is enqueued: the calls  */
                            /*    then return QDG_EHIP (the error path's test hook)           */
-  QDG_TUNE_COUNT = 14
+  QDG_TUNE_FMT_WAVES = 14, /* 1..16 chunk waves a row group of the block-format GEMV; each   */
+                           /*    wave sums every W-th non-empty chunk in turn               */
+  QDG_TUNE_COUNT = 15
 };
 
 /* Sets knob to value (-1 restores the default).  QDG_EINVAL for an unknown knob. */

@@ -116,7 +116,7 @@ def _check(fn: str, status: int) -> None:
 # launch shapes that give the same bits; -1 is the library's own choice.
 TUNE = {"sk_wsplit": 0, "ws_dma": 1, "ws_local": 2, "ws_rows": 3, "dq_seg": 4, "dq_rows": 5, "dq_x64": 6,
         "mfma_general": 7, "mfma_shape": 8, "mfma_wide": 9, "gemv_order": 10, "gemv_rpw": 11,
-        "gemv_unroll": 12, "reject_launch": 13}
+        "gemv_unroll": 12, "reject_launch": 13, "fmt_waves": 14}
 
 
 def set_tuning(knob: str, value: int) -> None:

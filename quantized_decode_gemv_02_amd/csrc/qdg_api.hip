@@ -16,8 +16,8 @@ thread_local int g_last_hip_error = 0;
 thread_local qdg::LaunchTiming g_timing = {nullptr, nullptr};
 
 // qdg_set_tuning's knobs (-1: the library's own choice)
-std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-static_assert(QDG_TUNE_COUNT == 14, "one initializer a knob");
+std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QDG_TUNE_COUNT == 15, "one initializer a knob");
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -362,7 +362,6 @@ int qdg_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, cons
   if (!aligned(w, 16) || !aligned(y, 4) || (x && !aligned(x, 16)) || (xq && !aligned(xq, 16)) ||
       (xl && !aligned(xl, 16)) || (xs && !aligned(xs, 4)))
     return QDG_EALIGN;
-  if (qdg::fmt_chunk_waves(K, splits) > 16) return QDG_EMODE;
   return hip_status(qdg::launch_gemv_fmt(fmt, mode, w, N, K, x, xq, xl, xs, splits, y, as_stream(stream)));
 }
 

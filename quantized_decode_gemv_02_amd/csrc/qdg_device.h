@@ -52,6 +52,14 @@ constexpr int SUPER = 16;       // blocks per 512-value superblock of the split-
 // The split-K chunk rule of the QWEN38 page (gk_gemv_hl_sk): 512-value
 // superblocks, per = ceil(nq/S), chunk s = superblocks [s*per, min((s+1)*per, nq)),
 // the K mod 512 tail in the last chunk.  Returned as 32-value block bounds.
+// The same with K < 2^31 given as nq = K/512 superblocks, nb = K/32 blocks and
+// per = ceil(nq/S), in 32-bit arithmetic (a kernel that walks several chunks
+// forms these once).
+__host__ __device__ inline void split_range32(int nq, int nb, int per, int S, int s, int32_t& g0, int32_t& g1) {
+  const int q0 = s * per < nq ? s * per : nq, q1 = (s + 1) * per < nq ? (s + 1) * per : nq;
+  g0 = q0 * SUPER;
+  g1 = s == S - 1 ? nb : q1 * SUPER;
+}
 __host__ __device__ inline void split_range(int64_t K, int S, int s, int32_t& g0, int32_t& g1) {
   const int64_t nq = K / 512, nb = K / QK, per = (nq + S - 1) / S;
   int64_t q0 = (int64_t)s * per;
@@ -535,7 +543,6 @@ hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float*
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
 bool glu_fits(int mode, int64_t K);
 void fmt_geometry(int fmt, int& values, int& bytes);
-int fmt_chunk_waves(int64_t K, int splits);
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
                            const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
                            hipStream_t st);

@@ -24,8 +24,11 @@
 // then those of lanes j + 4, j + 8 and j + 12 (DPP row shifts).  Each step's
 // bytes are staged in the wave's LDS slot by aligned 16-byte loads, a step
 // ahead.  Split-K (the QWEN38 page's chunk rule, gk_gemv_hl_sk /
-// gk_sk_combine): the chunks are waves of one workgroup and their partials are
-// added in ascending order in LDS.
+// gk_sk_combine): the chunks are summed by the waves of one workgroup, each
+// wave taking one or more in turn, and their partials are added in ascending
+// order in LDS.
+
+#include <atomic>
 
 #include "qdg_device.h"
 
@@ -449,9 +452,9 @@ struct Stage {
   static constexpr int NT = G::NCH + NA;           // pieces a step
   static constexpr int NPL = (NT + 63) / 64;       // loads a lane a step
   static constexpr int SLOT = NT * 16;
-  // 16 chunk waves' slots and partials stay within the 64 KiB a launch gets
-  // without raising the kernel's LDS limit
-  static_assert(16 * SLOT + 16 * ROWS * 8 <= 65536, "LDS of a 16-wave workgroup");
+  // 16 chunk waves' slots and the partials of QDG_MAX_SPLITS chunks stay within
+  // the 64 KiB a launch gets without raising the kernel's LDS limit
+  static_assert(16 * SLOT + QDG_MAX_SPLITS * ROWS * 8 <= 65536, "LDS of a 16-wave workgroup");
 };
 
 // The 16 bytes at w + a with those at or past `total` read as 0 (a < total),
@@ -479,10 +482,12 @@ __device__ __forceinline__ uint4 piece_fix(uint4 t, int sh) {
 
 constexpr int DPP_ROW_SHL12 = 0x10C;
 
-// A workgroup: R row groups of ROWS rows times one wave per non-empty chunk of
-// the S-chunk split rule (S = 1: the whole row).  Wave (rg, c) sums chunk c of
-// its rows; the chunk partials meet in LDS and a thread per row adds them in
-// ascending chunk order from 0 (empty chunks, whose partial is +0, skipped).
+// A workgroup: R row groups of ROWS rows times W chunk waves a group.  The
+// non-empty chunks of the S-chunk split rule (S = 1: the whole row), ceff of
+// them, go to the group's waves in turn: wave w sums chunks w, w + W, ... one
+// after another, each from +0 into its own partial (W = ceff: a wave a chunk).
+// The chunk partials meet in LDS and a thread per row adds them in ascending
+// chunk order from 0 (empty chunks, whose partial is +0, skipped).
 // Each step the wave copies its rows' bytes for the step into its own LDS slot
 // with aligned 16-byte loads (issued one step ahead), and the lanes decode their
 // sub-blocks from there; the LDS copy keeps every byte's address mod 16, so the
@@ -502,28 +507,34 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   using T = Stage<F, MODE, ROWS>;
   constexpr bool SUP = G::SUP;
   constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NT = T::NT, NPL = T::NPL;
-  extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials
+  extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials [R][ceff][ROWS]
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwaves = blockDim.x >> 6;
   uint8_t* slot = (uint8_t*)lds_dyn + wave * T::SLOT;
   uint4* lw = (uint4*)slot;
-  Acc* lpart = (Acc*)((uint8_t*)lds_dyn + nwaves * T::SLOT);  // [waves][ROWS]
-  const int rg = wave / ceff, cw = wave % ceff;
-  const int chunk = cw < m ? cw : S - 1;
+  Acc* lpart = (Acc*)((uint8_t*)lds_dyn + nwaves * T::SLOT);
+  const int W = nwaves / R;  // chunk waves a row group
+  const int rg = wave / W, cw = wave % W;
   const int r = lane / LPR, j = lane % LPR;
   const int64_t o_wg = (int64_t)blockIdx.x * (ROWS * R);
   const int64_t o = o_wg + ROWS * rg + r;
   const int64_t myrow = (o < N ? o : N - 1) * rb;
+  // chunk c of the wave's list: chunks 0..m-1, then S-1 (the tail chunk); every
+  // one of them holds at least one sub-block
+  const int nq = (int)(K >> 9), nb = (int)(K / QK), per = (nq + S - 1) / S;  // K < 2^31
+  auto range = [&](int c, int32_t& a, int32_t& b) { split_range32(nq, nb, per, S, c < m ? c : S - 1, a, b); };
+  int c = cw;
   int32_t g0, g1;
-  split_range(K, S, chunk, g0, g1);
+  range(c, g0, g1);
 
   auto seg_off = [&](int st) -> int64_t { return SUP ? (int64_t)(st >> 3) * B : (int64_t)st * B; };
-  auto seg_len = [&](int st) -> int {
-    const int n = g1 - st < LPR ? g1 - st : LPR;  // sub-blocks of the step (whole super-blocks for SUP)
+  auto seg_len = [&](int st, int32_t ge) -> int {
+    const int n = ge - st < LPR ? ge - st : LPR;  // sub-blocks of the step (whole super-blocks for SUP)
     return SUP ? (n >> 3) * B : n * B;
   };
   // A fetch: piece t = lane + 64k is weight piece t % CPR of row t / CPR
   // (t < NCH), or under Dequant activation piece t - NCH (t < NT).  The next
-  // step's fetch is issued before this step is summed.  Every fetch issues the
+  // step's fetch (the first of the wave's next chunk after a chunk's last step)
+  // is issued before this step is summed.  Every fetch issues the
   // same loads whatever the step, so no load sits behind a branch.  A piece's
   // row base is fixed for the launch; away from the matrix end (a scalar test
   // on the wave's last row) every piece is simply the 16 bytes at the row's
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   uint4 v[NPL];
   int vsh[NPL];
   bool fixed = false;  // whether the fetch in v took the clamped form (wave-uniform)
-  auto fetch = [&](int st) {
+  auto fetch = [&](int st, int32_t ge) {  // ge: the end of st's chunk
     const bool plain = ((last_base + seg_off(st)) & ~(int64_t)15) + 16 * CPR <= total;
     fixed = !plain;
 #pragma unroll
@@ -560,14 +571,14 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
       if (plain) {
         at = (so & ~(int64_t)15) + 16 * pc;
       } else {
-        const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st);
+        const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st, ge);
         at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh);
       }
       const uint8_t* src = w + at;
       if (!wpiece) {
         const int i = t - NCH;
         const int sb = st + (i >> 3);
-        src = (const uint8_t*)(x + (int64_t)(sb < g1 ? sb : st) * QK) + 16 * (i & 7);
+        src = (const uint8_t*)(x + (int64_t)(sb < ge ? sb : st) * QK) + 16 * (i & 7);
         sh = 0;
       }
       vsh[k] = sh;
@@ -581,7 +592,7 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
       v[k] = make_uint4(tt[0], tt[1], tt[2], tt[3]);
     }
   };
-  fetch(g0);
+  fetch(g0, g1);
 
   // One step's terms.  FULL: the step's LPR sub-blocks all lie in the chunk, so
   // every lane's own term and the three it folds from lanes j + 4, j + 8, j + 12
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
       }
     }
   };
-  for (int st = g0; st < g1; st += LPR) {
+  for (int st = g0;;) {
     if (fixed) {
 #pragma unroll
       for (int k = 0; k < NPL; ++k)
@@ -639,22 +650,34 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
       for (int k = 0; k < NPL; ++k)
         if (lane + 64 * k < NT) lw[lane + 64 * k] = v[k];
     }
-    if (st + LPR < g1) fetch(st + LPR);  // the next step's bytes, in flight while this one is summed
+    // the next step's bytes (the first of the wave's next chunk after a chunk's
+    // last step), in flight while this one is summed
+    int32_t ns = st + LPR, ne = g1;
+    const bool more = ns < g1 || c + W < ceff;
+    if (ns >= g1 && more) range(c + W, ns, ne);
+    if (more) fetch(ns, ne);
     if (st + LPR <= g1)
       terms(st, std::integral_constant<bool, true>());
     else
       terms(st, std::integral_constant<bool, false>());
+    st += LPR;
+    if (st < g1) continue;
+    // the chunk's partial: (P0 + P2) + (P1 + P3), partial q in lane q of the row's lanes
+    Acc pr;
+    if constexpr (MODE == 0) {
+      const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL2>(p));
+      pr = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
+    } else {
+      const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL2>(p));
+      pr = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
+    }
+    if (j == 0) lpart[(rg * ceff + c) * ROWS + r] = pr;
+    if (!more) break;
+    c += W;
+    st = ns;
+    g1 = ne;
+    p = 0;
   }
-  // (P0 + P2) + (P1 + P3): partial q in lane q of the row's lanes
-  Acc pr;
-  if constexpr (MODE == 0) {
-    const double t = __dadd_rn(p, dpp_f64<DPP_ROW_SHL2>(p));
-    pr = __dadd_rn(t, dpp_f64<DPP_ROW_SHL1>(t));
-  } else {
-    const float t = __fadd_rn(p, dpp_f32<DPP_ROW_SHL2>(p));
-    pr = __fadd_rn(t, dpp_f32<DPP_ROW_SHL1>(t));
-  }
-  if (j == 0) lpart[wave * ROWS + r] = pr;
   __syncthreads();
   if ((int)threadIdx.x < ROWS * R) {
     const int gq = threadIdx.x / ROWS, rq = threadIdx.x % ROWS;
@@ -682,28 +705,105 @@ void f_chunks(int64_t K, int S, int& m, int& ceff) {
 }
 
 template <int F, int MODE, int ROWS, int R>
-hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
-                     const float* xs, int S, int m, int ceff, float* y, hipStream_t st) {
+size_t fr_lds(int W, int ceff) {
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
-  const int64_t rb = K / Geo<F>::V * Geo<F>::B;
-  const int waves = R * ceff;
-  const size_t lds = (size_t)waves * Stage<F, MODE, ROWS>::SLOT + (size_t)waves * ROWS * sizeof(Acc);
-  const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * waves));
-  return launch((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, lds, st, w, rb, N, N * rb, x, xq, xl, xs, K, S, m,
-                ceff, y);
+  return (size_t)R * W * Stage<F, MODE, ROWS>::SLOT + (size_t)R * ceff * ROWS * sizeof(Acc);
 }
 
-// Four rows a wave (16 lanes a row) and one row group a workgroup: on the
-// 5120-row projections that is 1280 workgroups, five a compute unit in one
-// round at four or five chunk waves (measured: ahead of 8 rows a wave, of two
-// row groups a workgroup, and of fetching two or three steps ahead).
+template <int F, int MODE, int ROWS, int R>
+hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int S, int m, int ceff, int W, float* y, hipStream_t st) {
+  const int64_t rb = K / Geo<F>::V * Geo<F>::B;
+  const dim3 grid((unsigned)((N + ROWS * R - 1) / (ROWS * R))), block((unsigned)(64 * R * W));
+  return launch((k_gemv_fmt<F, MODE, ROWS, R>), grid, block, fr_lds<F, MODE, ROWS, R>(W, ceff), st, w, rb, N,
+                N * rb, x, xq, xl, xs, K, S, m, ceff, y);
+}
+
+// Compute units of the current device (256 on the MI355X), asked once a device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of W chunk waves that a compute unit holds at once: the HIP
+// occupancy calculator over the kernel's VGPRs, LDS and wave slots (8 waves a
+// SIMD at most 64 VGPRs, 7 at 72, 6 at 80, 5 at 96), asked once a kernel and W
+// with the partials of QDG_MAX_SPLITS chunks.
+template <int F, int MODE, int ROWS, int R>
+int fr_resident(int W) {
+  static std::atomic<int> cache[17];
+  int n = cache[W].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)k_gemv_fmt<F, MODE, ROWS, R>, 64 * R * W,
+                                                     fr_lds<F, MODE, ROWS, R>(W, QDG_MAX_SPLITS)) != hipSuccess) {
+      (void)hipGetLastError();
+      b = 1;
+    }
+    n = b > 0 ? b : 1;
+    cache[W].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Chunk waves a row group, W (at most 16).  With a wave a chunk, the 5120-row
+// projections at S = 8 -- 1280 workgroups, five a CU, eight waves each -- ask a
+// CU for 40 waves where it holds 32 at best, and run a fifth of their
+// workgroups as a second, thinly occupied round: measured 5-18% slower than
+// S = 4 on the same matrix.  W is the smallest count whose workgroups are all
+// resident at once and whose busiest wave (chunks w, w + W, ...) holds the
+// fewest sub-blocks: four waves of two chunks there.  Where no count lets every
+// workgroup be resident, min(ceff, 16).  QDG_TUNE_FMT_WAVES (1..16) overrides.
+template <int F, int MODE, int ROWS, int R>
+int fr_waves(int64_t N, int64_t K, int S, int m, int ceff) {
+  const int cap = ceff < 16 ? ceff : 16;
+  const int forced = tune(QDG_TUNE_FMT_WAVES);
+  if (forced > 0) return forced < cap ? forced : cap;
+  const int64_t wgs = (N + ROWS * R - 1) / (ROWS * R), cus = device_cus();
+  int best = cap;
+  int64_t best_load = INT64_MAX;
+  for (int W = 1; W <= cap; ++W) {
+    if ((int64_t)fr_resident<F, MODE, ROWS, R>(W) * cus < wgs) break;
+    int64_t load = 0;
+    for (int w = 0; w < W; ++w) {
+      int64_t l = 0;
+      for (int c = w; c < ceff; c += W) {
+        int32_t g0, g1;
+        split_range(K, S, c < m ? c : S - 1, g0, g1);
+        l += g1 - g0;
+      }
+      load = l > load ? l : load;
+    }
+    if (load < best_load) best_load = load, best = W;
+  }
+  return best;
+}
+
+// Four rows a wave (16 lanes a row) and one row group a workgroup.  Measured on
+// the 5120 x 25600 projection: 8 rows a wave was slower in 70 of 72 format,
+// mode and S (4, 5, 8) cases, by up to 43%; two row groups a workgroup and
+// fetching two or three steps ahead were slower too.
 template <int F, int MODE>
 hipError_t launch_f(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
                     const float* xs, int S, float* y, hipStream_t st) {
   int m, ceff;
   f_chunks(K, S, m, ceff);
   if (S == 1) m = 1, ceff = 1;
-  return launch_fr<F, MODE, 4, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, y, st);
+  const int W = fr_waves<F, MODE, 4, 1>(N, K, S, m, ceff);
+  return launch_fr<F, MODE, 4, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, W, y, st);
 }
 
 template <int F>
@@ -734,12 +834,6 @@ void fmt_geometry(int fmt, int& values, int& bytes) {
     case F_IQ4_XS: values = 256; bytes = 136; break;
     default: values = 0; bytes = 0;
   }
-}
-
-int fmt_chunk_waves(int64_t K, int splits) {
-  int m, ceff;
-  f_chunks(K, splits, m, ceff);
-  return splits == 1 ? 1 : ceff;
 }
 
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,

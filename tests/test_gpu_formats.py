@@ -121,6 +121,48 @@ def test_fmt_split(fmt, N, K, S, mode):
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
 
 
+def wave_cases(fmt):
+    """(N, K, S, W): W chunk waves forced below the chunk count, and more chunks
+    than a workgroup has waves (S = 40, the last chunk with the K mod 512 tail)."""
+    tail = 256 if fmt in SUPER else 32
+    return [(300, 5120, 8, 1), (300, 5120, 8, 3), (300, 5120, 5, 2), (70, 512 * 40 + tail, 40, -1),
+            (37, 512 * 64, 64, 5)]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("fmt", oracle.FORMATS)
+def test_fmt_several_chunks_a_wave(fmt, mode):
+    """A wave that sums several chunks one after another, each into its own
+    partial: the quantized modes bit-exact with the oracle's chunked sum, Dequant
+    within one unit in the last place of it, and every wave count the same bits."""
+    for N, K, S, W in wave_cases(fmt):
+        announce(f"gemv_fmt chunks a wave fmt={fmt} mode={mode} N={N} K={K} S={S} W={W}")
+        rng = np.random.default_rng(7000 * fmt + N + K + 7 * S + mode)
+        w, _, _, _ = encode(fmt, N, K, rng)
+        x = rng.standard_normal((1, K)).astype(np.float32)
+        dw = dev(w.reshape(-1))
+        y = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+        y1 = torch.full((N,), float("nan"), dtype=torch.float32, device=DEV)
+        if mode == 0:
+            args = dict(x=dev(x))
+            want = oracle.gemv_fmt(fmt, 0, w, N, K, x=x, splits=S, nthreads=8)[0]
+        else:
+            oq, ol, os_ = oracle.quantize(mode, x)
+            args = dict(xq=dev(oq), xl=None if ol is None else dev(ol), xs=dev(os_))
+            want = oracle.gemv_fmt(fmt, mode, w, N, K, xq=oq, xl=ol, xs=os_, splits=S, nthreads=8)[0]
+        with q.tuning(fmt_waves=W):
+            q.gemv_fmt(fmt, mode, dw, N, K, y, splits=S, **args)
+        with q.tuning(fmt_waves=1):
+            q.gemv_fmt(fmt, mode, dw, N, K, y1, splits=S, **args)
+        got = host(y)
+        if mode == 0:
+            d = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+            assert d.max() <= 1, (N, K, S, W, int(d.max()))
+        else:
+            np.testing.assert_array_equal(got, want, err_msg=f"N={N} K={K} S={S} W={W}")
+        assert torch.equal(y1.view(torch.int32), y.view(torch.int32)), (N, K, S, W)
+
+
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("fmt", oracle.FORMATS)
 def test_fmt_bench_shape(fmt, mode):
