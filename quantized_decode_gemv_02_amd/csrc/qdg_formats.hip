@@ -542,52 +542,64 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   // decoded -- and only a step that reaches the matrix end takes the clamped
   // form (pieces past the chunk's sub-blocks reread a valid piece; the last
   // piece of a matrix whose size is not a multiple of 16 is shifted into place).
-  int64_t rbase[NPL];
+  // pbase[k]: w + the piece's row start + 16*pc, so that a plain step's piece
+  // is the 16 bytes at (pbase[k] + step offset) rounded down to 16 (w is
+  // 16-byte aligned).
+  uintptr_t pbase[NPL];
   int pcs[NPL];
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int t = lane + 64 * k;
     const int tw = t < NCH ? t : 0;
     const int64_t po = o_wg + ROWS * rg + tw / CPR;
-    rbase[k] = (po < N ? po : N - 1) * rb;
     pcs[k] = tw % CPR;
+    pbase[k] = (uintptr_t)w + (uintptr_t)((po < N ? po : N - 1) * rb) + 16u * (unsigned)pcs[k];
   }
+  // Steps st <= st_plain are plain: the wave's highest row (its pieces reach
+  // furthest) keeps all CPR pieces inside the matrix, i.e. its step offset
+  // rounded down to 16 plus 16*CPR is at most total.
   const int64_t last_row = o_wg + ROWS * rg + ROWS - 1 < N ? o_wg + ROWS * rg + ROWS - 1 : N - 1;
-  const int64_t last_base = last_row * rb;  // the wave's highest row: its pieces reach furthest
+  int32_t st_plain;
+  {
+    const int64_t room = total - 16 * CPR + 16 - last_row * rb;  // plain iff seg_off(st) < room
+    const int64_t units = room <= 0 ? 0 : (room + B - 1) / B;   // segments (blocks or super-blocks) below room
+    st_plain = (int32_t)((SUP ? 8 * units : units) - 1 < INT32_MAX ? (SUP ? 8 * units : units) - 1 : INT32_MAX);
+  }
   uint4 v[NPL];
   int vsh[NPL];
   bool fixed = false;  // whether the fetch in v took the clamped form (wave-uniform)
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const v4u gv4u;
   auto fetch = [&](int st, int32_t ge) {  // ge: the end of st's chunk
-    const bool plain = ((last_base + seg_off(st)) & ~(int64_t)15) + 16 * CPR <= total;
+    const bool plain = st <= st_plain;
     fixed = !plain;
+    const uintptr_t soff = (uintptr_t)seg_off(st);
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       const int t = lane + 64 * k;
       const bool wpiece = t < NCH || t >= NT;
-      const int pc = pcs[k];
-      const int64_t so = rbase[k] + seg_off(st);
       int sh = 0;
-      int64_t at;
+      const gv4u* src;
       if (plain) {
-        at = (so & ~(int64_t)15) + 16 * pc;
+        src = (const gv4u*)((pbase[k] + soff) & ~(uintptr_t)15);
       } else {
+        const int pc = pcs[k];
+        const int64_t so = (int64_t)(pbase[k] - (uintptr_t)w) - 16 * pc + (int64_t)soff;  // row start + step offset
         const bool need = t < NCH && 16 * pc < (int)(so & 15) + seg_len(st, ge);
-        at = piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh);
+        src = (const gv4u*)(w + piece_addr((so & ~(int64_t)15) + (need ? 16 * pc : 0), total, sh));
       }
-      const uint8_t* src = w + at;
       if (!wpiece) {
         const int i = t - NCH;
         const int sb = st + (i >> 3);
-        src = (const uint8_t*)(x + (int64_t)(sb < ge ? sb : st) * QK) + 16 * (i & 7);
+        src = (const gv4u*)((const uint8_t*)(x + (int64_t)(sb < ge ? sb : st) * QK) + 16 * (i & 7));
         sh = 0;
       }
       vsh[k] = sh;
-      typedef unsigned v4u __attribute__((ext_vector_type(4)));
       v4u tt;
       if (64 * k + 63 < NCH) {  // a constant once the loop is unrolled
-        tt = __builtin_nontemporal_load((const v4u*)src);  // weights only: streamed once
+        tt = __builtin_nontemporal_load(src);  // weights only: streamed once
       } else {
-        tt = *(const v4u*)src;
+        tt = *src;
       }
       v[k] = make_uint4(tt[0], tt[1], tt[2], tt[3]);
     }
@@ -643,19 +655,24 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   for (int st = g0;;) {
     if (fixed) {
 #pragma unroll
-      for (int k = 0; k < NPL; ++k)
-        if (lane + 64 * k < NT) lw[lane + 64 * k] = piece_fix(v[k], vsh[k]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NPL; ++k)
-        if (lane + 64 * k < NT) lw[lane + 64 * k] = v[k];
+      for (int k = 0; k < NPL; ++k) v[k] = piece_fix(v[k], vsh[k]);
     }
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (lane + 64 * k < NT) lw[lane + 64 * k] = v[k];
     // the next step's bytes (the first of the wave's next chunk after a chunk's
-    // last step), in flight while this one is summed
+    // last step; past the wave's last step this one's again, so that every step
+    // issues the same loads), in flight while this one is summed
     int32_t ns = st + LPR, ne = g1;
-    const bool more = ns < g1 || c + W < ceff;
-    if (ns >= g1 && more) range(c + W, ns, ne);
-    if (more) fetch(ns, ne);
+    bool more = true;
+    if (ns >= g1) {
+      more = c + W < ceff;
+      if (more)
+        range(c + W, ns, ne);
+      else
+        ns = st;
+    }
+    fetch(ns, ne);
     if (st + LPR <= g1)
       terms(st, std::integral_constant<bool, true>());
     else
