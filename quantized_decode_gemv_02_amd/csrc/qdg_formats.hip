@@ -88,6 +88,25 @@ __device__ __forceinline__ void ld_words(const uint8_t* p, unsigned* w) {
   }
 }
 
+// A funnel window on the n dwords at p (in the wave's LDS slot): n + 1 aligned
+// dwords d and a shift sh such that alignbit(d[i+1], d[i], sh) is dword i at p
+// shifted right by `off` bits (-8 < off < 8: a field's place within each byte,
+// negative to move it up) -- the realignment and the field's shift in one
+// v_alignbit.  The total shift 8*mis + off is negative only for an aligned p and
+// off < 0; then the window starts one dword early (p - 4: the slots sit 16
+// bytes above the start of LDS, so that dword is always in the allocation) and
+// shifts by 32 + off.  The last dword is read only when it holds wanted bytes.
+template <int NW>
+__device__ __forceinline__ unsigned ld_funnel(const uint8_t* p, int off, unsigned (&d)[NW + 1]) {
+  const unsigned mis = (unsigned)(uintptr_t)p & 3u;
+  const int s = 8 * (int)mis + off;
+  const unsigned* a = (const unsigned*)(p - mis - (s < 0 ? 4 : 0));  // pointer arithmetic keeps the LDS address space
+#pragma unroll
+  for (int i = 0; i < NW; ++i) d[i] = a[i];
+  d[NW] = a[(mis != 0 || s < 0) ? NW : NW - 1];
+  return (unsigned)s & 31u;
+}
+
 // The low nibbles of a word's four bytes and the high ones, as bytes.
 __device__ __forceinline__ unsigned lo_nib(unsigned q) { return q & 0x0f0f0f0fu; }
 __device__ __forceinline__ unsigned hi_nib(unsigned q) { return (q >> 4) & 0x0f0f0f0fu; }
@@ -223,19 +242,19 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
     }
   } else if constexpr (F == F_Q6_K) {
     const int half = j >> 2, k = j & 3;
-    unsigned ql[8], qh[8];
-    ld_words<8, true>(b + 64 * half + 32 * (k & 1), ql);
-    ld_words<8, true>(b + 128 + 32 * half, qh);
+    unsigned qd[9], hd[9];
+    // the nibble (low for k < 2, high otherwise) of each level byte to bits 0-3,
+    // and bits 2k, 2k+1 of each high byte to bits 4, 5
+    const unsigned nsh = ld_funnel<8>(b + 64 * half + 32 * (k & 1), 4 * (k >> 1), qd);
+    const unsigned hsh = ld_funnel<8>(b + 128 + 32 * half, 2 * k - 4, hd);
     const unsigned scw = ld_u16(b + 192 + 8 * half + 2 * k);
     const float dd = h16(ld_u16(b + 208));
     s.d[0] = __fmul_rn(dd, (float)(int)(signed char)(scw & 255));
     s.d[1] = __fmul_rn(dd, (float)(int)(signed char)(scw >> 8));
-    // the nibble (low for k < 2, high otherwise) and bits 2k, 2k+1 of each qh byte
-    // rotated to bits 4, 5 of the same byte
-    const unsigned nsh = 4u * (unsigned)(k >> 1), rot = (unsigned)(2 * k - 4) & 31u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      s.w[i] = ((ql[i] >> nsh) & 0x0f0f0f0fu) | (__builtin_amdgcn_alignbit(qh[i], qh[i], rot) & 0x30303030u);
+      s.w[i] = (__builtin_amdgcn_alignbit(qd[i + 1], qd[i], nsh) & 0x0f0f0f0fu) |
+               (__builtin_amdgcn_alignbit(hd[i + 1], hd[i], hsh) & 0x30303030u);
     s.off = 32;
   } else if constexpr (F == F_Q2_K) {
     const int half = j >> 2, k = j & 3;  // b 4-byte aligned: 84 is a multiple of 4
@@ -255,27 +274,27 @@ __device__ __forceinline__ void decode(const uint8_t* __restrict__ b, int j, Sub
     for (int i = 0; i < 8; ++i) s.w[i] = (q[i] >> (2 * k)) & 0x03030303u;
   } else if constexpr (F == F_Q3_K) {
     const int half = j >> 2, k = j & 3;
-    unsigned hm[8], q[8], sp[3];
-    ld_words<8, true>(b, hm);
-    ld_words<8, true>(b + 32 + 32 * half, q);
-    ld_words<3, true>(b + 96, sp);
+    unsigned hd[9], qd[9];
+    // bit 4*half + k (the sub-block's) of each high-mask byte to bit 2, and bits
+    // 2k, 2k+1 of each level byte to bits 0, 1
+    const unsigned hsh = ld_funnel<8>(b, 4 * half + k - 2, hd);
+    const unsigned qsh = ld_funnel<8>(b + 32 + 32 * half, 2 * k, qd);
+    // the 16 six-bit scales: scale i = low nibble of byte i & 7 (shifted by
+    // 4*(i >> 3)) | bits 2*(i >> 2) of byte 8 + (i & 3) as its top two bits;
+    // the lane's two, i = 8*half + 2*k + h, sit in the byte pairs 2k, 2k+1 and
+    // 8 + 2(k & 1), +1 (the fields are 2-byte aligned)
+    const unsigned lo16 = ld_u16(b + 96 + 2 * k), hi16 = ld_u16(b + 104 + 2 * (k & 1));
     const float dd = h16(ld_u16(b + 108));
-    auto spb = [&](int i) {  // byte i of the 12 scale bytes (word picked by selects, not an indexed array)
-      const unsigned wd = (i >> 2) == 0 ? sp[0] : (i >> 2) == 1 ? sp[1] : sp[2];
-      return (wd >> (8 * (i & 3))) & 255u;
-    };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int i = 8 * half + 2 * k + h;
-      const unsigned lo4 = (spb(i & 7) >> (4 * (i >> 3))) & 15u;
-      const unsigned hi2 = (spb(8 + (i & 3)) >> (2 * (i >> 2))) & 3u;
+      const unsigned lo4 = (lo16 >> (8 * h + 4 * half)) & 15u;
+      const unsigned hi2 = (hi16 >> (8 * h + 2 * (2 * half + (k >> 1)))) & 3u;
       s.d[h] = __fmul_rn(dd, (float)((int)(lo4 | (hi2 << 4)) - 32));
     }
-    // bit mbit of each high-mask byte rotated to bit 2 of the same byte
-    const unsigned rot = (unsigned)(4 * half + k - 2) & 31u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      s.w[i] = ((q[i] >> (2 * k)) & 0x03030303u) | (__builtin_amdgcn_alignbit(hm[i], hm[i], rot) & 0x04040404u);
+      s.w[i] = (__builtin_amdgcn_alignbit(qd[i + 1], qd[i], qsh) & 0x03030303u) |
+               (__builtin_amdgcn_alignbit(hd[i + 1], hd[i], hsh) & 0x04040404u);
     s.off = 4;  // level = low2 - 4 + 4*high bit
   } else if constexpr (F == F_IQ4_XS) {
     const int ib = j;  // b 8-byte aligned
@@ -437,6 +456,10 @@ struct Seg {
   static constexpr int NCH = ROWS * CPR;  // weight pieces a wave stages a step
 };
 
+// The wave slots start 16 bytes into the workgroup's LDS, so that a funnel
+// window that starts a dword before a field (ld_funnel) stays in the allocation.
+constexpr int SLOT_BASE = 16;
+
 // A wave's LDS slot for one step: the rows' weight pieces, then under Dequant
 // the step's activation (LPR sub-blocks of 32 binary32 values, 8 pieces each).
 // The quantized modes read their activation words and scales from global
@@ -454,7 +477,7 @@ struct Stage {
   static constexpr int SLOT = NT * 16;
   // 16 chunk waves' slots and the partials of QDG_MAX_SPLITS chunks stay within
   // the 64 KiB a launch gets without raising the kernel's LDS limit
-  static_assert(16 * SLOT + QDG_MAX_SPLITS * ROWS * 8 <= 65536, "LDS of a 16-wave workgroup");
+  static_assert(SLOT_BASE + 16 * SLOT + QDG_MAX_SPLITS * ROWS * 8 <= 65536, "LDS of a 16-wave workgroup");
 };
 
 // The 16 bytes at w + a with those at or past `total` read as 0 (a < total),
@@ -509,9 +532,9 @@ __global__ __launch_bounds__(1024) void k_gemv_fmt(const uint8_t* __restrict__ w
   constexpr int B = Geo<F>::B, LPR = G::LPR, CPR = G::CPR, NCH = G::NCH, NT = T::NT, NPL = T::NPL;
   extern __shared__ uint4 lds_dyn[];  // [waves] slots, then the chunk partials [R][ceff][ROWS]
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwaves = blockDim.x >> 6;
-  uint8_t* slot = (uint8_t*)lds_dyn + wave * T::SLOT;
+  uint8_t* slot = (uint8_t*)lds_dyn + SLOT_BASE + wave * T::SLOT;
   uint4* lw = (uint4*)slot;
-  Acc* lpart = (Acc*)((uint8_t*)lds_dyn + nwaves * T::SLOT);
+  Acc* lpart = (Acc*)((uint8_t*)lds_dyn + SLOT_BASE + nwaves * T::SLOT);
   const int W = nwaves / R;  // chunk waves a row group
   const int rg = wave / W, cw = wave % W;
   const int r = lane / LPR, j = lane % LPR;
@@ -724,7 +747,7 @@ void f_chunks(int64_t K, int S, int& m, int& ceff) {
 template <int F, int MODE, int ROWS, int R>
 size_t fr_lds(int W, int ceff) {
   using Acc = typename std::conditional<MODE == 0, double, float>::type;
-  return (size_t)R * W * Stage<F, MODE, ROWS>::SLOT + (size_t)R * ceff * ROWS * sizeof(Acc);
+  return SLOT_BASE + (size_t)R * W * Stage<F, MODE, ROWS>::SLOT + (size_t)R * ceff * ROWS * sizeof(Acc);
 }
 
 template <int F, int MODE, int ROWS, int R>
