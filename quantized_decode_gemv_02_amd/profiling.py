@@ -13,6 +13,7 @@ kernels write only their outputs.
 Usage (from the repository root, after the rocprofv3 runs):
     python -m quantized_decode_gemv_02_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT.md OUT.json \
         KERNEL GRID "COMMAND" [OCC_DIR]
+    python -m quantized_decode_gemv_02_amd.profiling counters OUT.md "COMMAND" PASS_DIR [PASS_DIR ...]
 """
 from __future__ import annotations
 
@@ -213,7 +214,55 @@ def summarize(trace_dir, fetch_dir, write_dir, out_md, out_json, command: str, d
     return dom
 
 
+# Per-wave instruction counts and wave-cycle fractions from SQ counter passes
+# (each pass its own rocprofv3 --pmc run of the same command).
+COUNTER_COLUMNS = (
+    ("VALU/wave", lambda c: c["SQ_INSTS_VALU"] / c["SQ_WAVES"]),
+    ("SALU/wave", lambda c: c["SQ_INSTS_SALU"] / c["SQ_WAVES"]),
+    ("VMEM rd/wave", lambda c: c["SQ_INSTS_VMEM_RD"] / c["SQ_WAVES"]),
+    ("LDS/wave", lambda c: c["SQ_INSTS_LDS"] / c["SQ_WAVES"]),
+    ("f64 FMA/wave", lambda c: c["SQ_INSTS_VALU_FMA_F64"] / c["SQ_WAVES"]),
+    ("CVT/wave", lambda c: c["SQ_INSTS_VALU_CVT"] / c["SQ_WAVES"]),
+    ("wait any", lambda c: c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("wait issue", lambda c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("active", lambda c: c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("LDS bank confl./wave", lambda c: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_WAVES"]),
+    ("LDS unaligned stall/wave", lambda c: c["SQ_LDS_UNALIGNED_STALL"] / c["SQ_WAVES"]),
+)
+
+
+def summarize_counters(out_md: str, command: str, pass_dirs: list[str], prefix: str = "k_gemv") -> None:
+    merged = defaultdict(dict)
+    for d in pass_dirs:
+        for key, vals in per_kernel_counters(d).items():
+            merged[key].update(vals)
+    lines = [f"# rocprofv3 counters: {os.path.basename(out_md)[:-3]}", "",
+             "Commands (from the repository root; one --pmc pass each):", "", "```", command, "```", "",
+             "Per dispatch, mean over the dispatches of each kernel and grid. The wave-cycle fractions are "
+             "SQ_WAIT_ANY (waiting on a load, LDS or other counter), SQ_WAIT_INST_ANY (ready, waiting for "
+             "its instruction to issue) and SQ_ACTIVE_INST_ANY (issuing), each over SQ_WAVE_CYCLES; they "
+             "overlap and need not add to 1.", ""]
+    cols = [name for name, _ in COUNTER_COLUMNS]
+    lines += ["| kernel | grid | waves | " + " | ".join(cols) + " |", "|---|---|---|" + "---|" * len(cols)]
+    for key in sorted(merged):
+        if not key[0].startswith(prefix):
+            continue
+        c = merged[key]
+        cells = []
+        for _, fn in COUNTER_COLUMNS:
+            try:
+                v = fn(c)
+                cells.append(f"{v:.2f}" if v < 10 else f"{v:.0f}")
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        lines.append(f"| {key[0]} | {key[1]} | {c.get('SQ_WAVES', 0):.0f} | " + " | ".join(cells) + " |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
+    if sys.argv[1] == "counters":
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4:])
+        sys.exit(0)
     t, f, w, md, js, kern, grid = sys.argv[1:8]
     cmd = sys.argv[8] if len(sys.argv) > 8 else ""
     occ = sys.argv[9] if len(sys.argv) > 9 else None
