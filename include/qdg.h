@@ -428,6 +428,19 @@ int qdg_gemv_fmt(int fmt, int mode, const uint8_t *w, int64_t N, int64_t K, cons
                  const int8_t *xq, const int8_t *xl, const float *xs, int splits, float *y,
                  qdg_stream stream);
 
+/* Host only; asks the current device (its compute-unit count, the kernel's
+ * occupancy): the chunk waves a workgroup's rows get in qdg_gemv_fmt for this
+ * shape, W >= 1 -- each wave sums the non-empty chunks w, w + W, ... of the
+ * split rule in turn; W equal to the chunk count is a wave a chunk.  The result
+ * never changes the output bits.  Negative status on bad arguments (those
+ * qdg_gemv_fmt rejects without touching memory). */
+int qdg_gemv_fmt_chunk_waves(int fmt, int mode, int64_t N, int64_t K, int splits);
+
+/* Host only, the same for the Dequant chunk-wave kernel of qdg_gemv_q8_fused and
+ * qdg_gemv_q8_parts on one matrix of N rows: QDG_EMODE where that kernel does
+ * not serve (K, splits). */
+int qdg_gemv_dq_chunk_waves(int64_t N, int64_t K, int splits);
+
 /*
  * Test hook: the exact int32 per-block dots the GEMV forms (lane kernel library
  * page, lk_q8_block_dot), dh[t][o][g] = sum_{k in block g} wq[o][k]*xq[t][k] and,
@@ -505,7 +518,8 @@ enum {
                            /*    then return QDG_EHIP (the error path's test hook)           */
   QDG_TUNE_FMT_WAVES = 14, /* 1..16 chunk waves a row group of the block-format GEMV; each   */
                            /*    wave sums every W-th non-empty chunk in turn               */
-  QDG_TUNE_COUNT = 15
+  QDG_TUNE_DQ_WAVES = 15,  /* 1..16 chunk waves a row group of the Dequant chunk-wave kernel */
+  QDG_TUNE_COUNT = 16
 };
 
 /* Sets knob to value (-1 restores the default).  QDG_EINVAL for an unknown knob. */

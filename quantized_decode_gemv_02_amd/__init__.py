@@ -85,6 +85,8 @@ _SIGS = {
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
+    "qdg_gemv_fmt_chunk_waves": ([_I, _I, _I64, _I64, _I], _I),
+    "qdg_gemv_dq_chunk_waves": ([_I64, _I64, _I], _I),
     "qdg_gemv_q8_argmax_noalloc": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_set_tuning": ([_I, _I], _I),
     "qdg_get_tuning": ([_I], _I),
@@ -116,7 +118,7 @@ def _check(fn: str, status: int) -> None:
 # launch shapes that give the same bits; -1 is the library's own choice.
 TUNE = {"sk_wsplit": 0, "ws_dma": 1, "ws_local": 2, "ws_rows": 3, "dq_seg": 4, "dq_rows": 5, "dq_x64": 6,
         "mfma_general": 7, "mfma_shape": 8, "mfma_wide": 9, "gemv_order": 10, "gemv_rpw": 11,
-        "gemv_unroll": 12, "reject_launch": 13, "fmt_waves": 14}
+        "gemv_unroll": 12, "reject_launch": 13, "fmt_waves": 14, "dq_waves": 15}
 
 
 def set_tuning(knob: str, value: int) -> None:
@@ -376,6 +378,20 @@ def sk_workgroup_shape(mode: int, K: int, splits: int):
     if r < 0:
         _check("qdg_gemv_sk_combines_in_workgroup", r)
     return (int(arr[0]), int(arr[1])) if r == 1 else None
+
+
+def fmt_chunk_waves(fmt: int, mode: int, N: int, K: int, splits: int) -> int:
+    """Chunk waves a workgroup's rows get in ``gemv_fmt`` for this shape on the current device."""
+    r = int(_lib.qdg_gemv_fmt_chunk_waves(fmt, mode, N, K, splits))
+    _check("qdg_gemv_fmt_chunk_waves", r if r < 0 else 0)
+    return r
+
+
+def dq_chunk_waves(N: int, K: int, splits: int) -> int:
+    """Chunk waves a workgroup's rows get in the Dequant chunk-wave kernel on the current device."""
+    r = int(_lib.qdg_gemv_dq_chunk_waves(N, K, splits))
+    _check("qdg_gemv_dq_chunk_waves", r if r < 0 else 0)
+    return r
 
 
 def sk_workspace(N: int, splits: int):

@@ -16,8 +16,8 @@ thread_local int g_last_hip_error = 0;
 thread_local qdg::LaunchTiming g_timing = {nullptr, nullptr};
 
 // qdg_set_tuning's knobs (-1: the library's own choice)
-std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-static_assert(QDG_TUNE_COUNT == 15, "one initializer a knob");
+std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QDG_TUNE_COUNT == 16, "one initializer a knob");
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -346,6 +346,23 @@ int64_t qdg_fmt_row_bytes(int fmt, int64_t K) {
   qdg::fmt_geometry(fmt, values, bytes);
   if (!values || K < values || K % values) return 0;
   return K / values * bytes;
+}
+
+int qdg_gemv_fmt_chunk_waves(int fmt, int mode, int64_t N, int64_t K, int splits) {
+  if (mode < QDG_DEQUANT || mode > QDG_TWOPASS) return QDG_EINVAL;
+  int values, bytes;
+  qdg::fmt_geometry(fmt, values, bytes);
+  if (!values) return QDG_EINVAL;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_EINVAL;
+  if (!shape_ok(N, K) || K % values || N / 8 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  return qdg::fmt_chunk_waves(fmt, mode, N, K, splits);
+}
+
+int qdg_gemv_dq_chunk_waves(int64_t N, int64_t K, int splits) {
+  if (!shape_ok(N, K)) return QDG_ESHAPE;
+  if (splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  const int w = qdg::dq_chunk_waves(N, K, splits);
+  return w > 0 ? w : QDG_EMODE;
 }
 
 int qdg_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq,

@@ -28,6 +28,8 @@
 // took two DPP moves, two additions and a multiplication: 8% faster on the
 // 5120x25600 projection at S = 8 (35.7 -> 32.7 us).
 
+#include <atomic>
+
 #include "qdg_device.h"
 
 namespace qdg {
@@ -101,10 +103,10 @@ template <int R, int NB>
 __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, const float* __restrict__ x, int64_t K,
                                                         int S, int m, int ceff) {
   constexpr int ROWS = 4 * R;
-  __shared__ double lpart[DS_NT / 64][4];
+  __shared__ double lpart[DS_NT / 64][4];  // [row group * ceff + chunk][row]
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave / ceff, c = wave % ceff;
-  const int chunk = c < m ? c : S - 1;
+  const int W = (int)(blockDim.x >> 6) / R;  // chunk waves a row group
+  const int rg = wave / W, cw = wave % W;
   const int64_t nb = K / QK;
   int64_t o_wg;
   const int part = find_part(tab, (int)blockIdx.x, ROWS, o_wg);
@@ -112,12 +114,6 @@ __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, cons
   const uint16_t* __restrict__ ws = tab.ws[part];
   float* __restrict__ y = tab.y[part];
   const int64_t N = tab.N[part];
-  int32_t g0, g1;
-  split_range(K, S, chunk, g0, g1);
-  // 8-value pieces of the row (32-bit offsets: K < 2^31)
-  const int p0 = 4 * g0, p1 = 4 * g1;
-  const int nsteps = (p1 - p0 + 63) / 64;
-
   const int8_t* wrow[4];
   const uint16_t* srow[4];
 #pragma unroll
@@ -127,6 +123,14 @@ __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, cons
     wrow[r] = wq + o * K;
     srow[r] = ws + o * nb;
   }
+  // the wave's chunks in turn: cw, cw + W, ... (chunks 0..m-1, then S-1)
+  const int nq = (int)(K >> 9), nbk = (int)(K / QK), per = (nq + S - 1) / S;  // K < 2^29
+  for (int c = cw; c < ceff; c += W) {
+  int32_t g0, g1;
+  split_range32(nq, nbk, per, S, c < m ? c : S - 1, g0, g1);
+  // 8-value pieces of the row (32-bit offsets: K < 2^31)
+  const int p0 = 4 * g0, p1 = 4 * g1;
+  const int nsteps = (p1 - p0 + 63) / 64;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   if (nsteps > 0) {
     const int plast = p1 - 1;
@@ -164,7 +168,8 @@ __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, cons
   }
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lpart[wave][r] = acc[r];
+    for (int r = 0; r < 4; ++r) lpart[rg * ceff + c][r] = acc[r];
+  }
   }
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
@@ -188,9 +193,39 @@ void ds_chunks(int64_t K, int S, int& m, int& ceff) {
 #endif
 constexpr int DS_NB = QDG_DS_NB;  // step buffers: DS_NB - 1 steps in flight beyond the one being folded
 
+// Workgroups of R row groups of W chunk waves that a compute unit holds at once
+// (the HIP occupancy calculator: the kernel keeps 75 VGPRs, six waves a SIMD),
+// asked once a row-group count and W.
+template <int R>
+int ds_resident(int W) {
+  static std::atomic<int> cache[17];
+  int n = cache[W].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)k_gemv_dq_seg<R, DS_NB>, 64 * R * W, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      b = 1;
+    }
+    n = b > 0 ? b : 1;
+    cache[W].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// W chunk waves a row group (pick_chunk_waves): at 5120 rows and S = 8 eight
+// waves a workgroup would take 1.67 rounds of three workgroups a CU; four waves
+// of two chunks fit one round.  QDG_TUNE_DQ_WAVES overrides.
+template <int R>
+int ds_waves(int64_t wgs, int64_t K, int S, int m, int ceff) {
+  return pick_chunk_waves(wgs, 16 / R, K, S, m, ceff, tune(QDG_TUNE_DQ_WAVES), [](int w) { return ds_resident<R>(w); });
+}
+
 template <int R>
 hipError_t launch_ds(const PartTable& tab, int64_t K, const float* x, int S, int m, int ceff, hipStream_t st) {
-  const dim3 grid((unsigned)tab.tile_end[tab.n - 1]), block((unsigned)(64 * R * ceff));
+  const int64_t wgs = tab.tile_end[tab.n - 1];
+  const int W = ds_waves<R>(wgs, K, S, m, ceff);
+  const dim3 grid((unsigned)wgs), block((unsigned)(64 * R * W));
   return launch((k_gemv_dq_seg<R, DS_NB>), grid, block, 0, st, tab, x, K, S, m, ceff);
 }
 
@@ -207,18 +242,38 @@ int dq_seg_chunks(int64_t K, int splits) {
   return ceff <= 16 ? S : 0;
 }
 
-hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
-                                    float* const* y, int64_t K, const float* x, int splits, hipStream_t st) {
-  const int S = dq_seg_chunks(K, splits);
-  int m, ceff;
-  ds_chunks(K, S, m, ceff);
-  // one row group a workgroup (measured on the 5120-row projections: R = 1 is
-  // 10-25% faster than 2-4 at S = 4, 5 and 8); QDG_TUNE_DQ_ROWS overrides
+// Row groups a workgroup: one (measured on the 5120-row projections: R = 1 is
+// 10-25% faster than 2-4 at S = 4, 5 and 8); QDG_TUNE_DQ_ROWS overrides.
+int ds_rows(int ceff) {
   int R = 1;
   if (tune(QDG_TUNE_DQ_ROWS) > 0) R = tune(QDG_TUNE_DQ_ROWS);
   if (R < 1) R = 1;
   if (R > 4) R = 4;
   while (R > 1 && R * ceff > 16) --R;
+  return R;
+}
+
+int dq_chunk_waves(int64_t N, int64_t K, int splits) {
+  const int S = dq_seg_chunks(K, splits);
+  if (S == 0) return 0;
+  int m, ceff;
+  ds_chunks(K, S, m, ceff);
+  const int R = ds_rows(ceff);
+  const int64_t wgs = (N + 4 * R - 1) / (4 * R);
+  switch (R) {
+    case 1: return ds_waves<1>(wgs, K, S, m, ceff);
+    case 2: return ds_waves<2>(wgs, K, S, m, ceff);
+    case 3: return ds_waves<3>(wgs, K, S, m, ceff);
+    default: return ds_waves<4>(wgs, K, S, m, ceff);
+  }
+}
+
+hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
+                                    float* const* y, int64_t K, const float* x, int splits, hipStream_t st) {
+  const int S = dq_seg_chunks(K, splits);
+  int m, ceff;
+  ds_chunks(K, S, m, ceff);
+  const int R = ds_rows(ceff);
   PartTable tab;
   if (!make_parts(tab, nparts, wq, ws, y, N, 4 * R)) return hipErrorInvalidValue;
   switch (R) {

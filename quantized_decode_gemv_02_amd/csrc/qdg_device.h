@@ -70,6 +70,40 @@ __host__ __device__ inline void split_range(int64_t K, int S, int s, int32_t& g0
   g1 = (s == S - 1) ? (int32_t)nb : (int32_t)(q1 * SUPER);
 }
 
+// Chunk waves a row group for the kernels whose workgroups hold the S chunks of
+// their rows as waves, W of them each summing chunks w, w + W, ... in turn (so W
+// changes no bit).  A compute unit holds a bounded number of a kernel's
+// workgroups at once (resident(W), from the HIP occupancy calculator); with a
+// wave a chunk the 5120-row projections at S = 8 ask for more than fit and run
+// their last workgroups as a second, thinly occupied round.  The choice: the
+// smallest W for which every workgroup (wgs of them) is resident at once and
+// whose busiest wave holds the fewest blocks; where no W fits one round,
+// min(ceff, cap).  `forced` (> 0) overrides.
+int device_cus();
+template <typename Resident>
+int pick_chunk_waves(int64_t wgs, int cap, int64_t K, int S, int m, int ceff, int forced, Resident resident) {
+  cap = ceff < cap ? ceff : cap;
+  if (forced > 0) return forced < cap ? forced : cap;
+  const int64_t cus = device_cus();
+  int best = cap;
+  int64_t best_load = INT64_MAX;
+  for (int W = 1; W <= cap; ++W) {
+    if ((int64_t)resident(W) * cus < wgs) break;
+    int64_t load = 0;
+    for (int w = 0; w < W; ++w) {
+      int64_t l = 0;
+      for (int c = w; c < ceff; c += W) {
+        int32_t g0, g1;
+        split_range(K, S, c < m ? c : S - 1, g0, g1);
+        l += g1 - g0;
+      }
+      load = l > load ? l : load;
+    }
+    if (load < best_load) best_load = load, best = W;
+  }
+  return best;
+}
+
 // DPP lane moves (GFX9 encodings).  A lane whose source lies outside its
 // 16-lane row reads 0; callers only consume lanes whose source is inside.
 enum : int {
@@ -543,6 +577,8 @@ hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float*
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
 bool glu_fits(int mode, int64_t K);
 void fmt_geometry(int fmt, int& values, int& bytes);
+int fmt_chunk_waves(int fmt, int mode, int64_t N, int64_t K, int S);
+int dq_chunk_waves(int64_t N, int64_t K, int splits);
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
                            const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
                            hipStream_t st);

@@ -759,25 +759,6 @@ hipError_t launch_fr(const uint8_t* w, int64_t N, int64_t K, const float* x, con
                 N * rb, x, xq, xl, xs, K, S, m, ceff, y);
 }
 
-// Compute units of the current device (256 on the MI355X), asked once a device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return 256;
-  }
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-      (void)hipGetLastError();
-      n = 256;
-    }
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // Workgroups of W chunk waves that a compute unit holds at once: the HIP
 // occupancy calculator over the kernel's VGPRs, LDS and wave slots (8 waves a
 // SIMD at most 64 VGPRs, 7 at 72, 6 at 80, 5 at 96), asked once a kernel and W
@@ -799,51 +780,33 @@ int fr_resident(int W) {
   return n;
 }
 
-// Chunk waves a row group, W (at most 16).  With a wave a chunk, the 5120-row
-// projections at S = 8 -- 1280 workgroups, five a CU, eight waves each -- ask a
-// CU for 40 waves where it holds 32 at best, and run a fifth of their
-// workgroups as a second, thinly occupied round: measured 5-18% slower than
-// S = 4 on the same matrix.  W is the smallest count whose workgroups are all
-// resident at once and whose busiest wave (chunks w, w + W, ...) holds the
-// fewest sub-blocks: four waves of two chunks there.  Where no count lets every
-// workgroup be resident, min(ceff, 16).  QDG_TUNE_FMT_WAVES (1..16) overrides.
-template <int F, int MODE, int ROWS, int R>
-int fr_waves(int64_t N, int64_t K, int S, int m, int ceff) {
-  const int cap = ceff < 16 ? ceff : 16;
-  const int forced = tune(QDG_TUNE_FMT_WAVES);
-  if (forced > 0) return forced < cap ? forced : cap;
-  const int64_t wgs = (N + ROWS * R - 1) / (ROWS * R), cus = device_cus();
-  int best = cap;
-  int64_t best_load = INT64_MAX;
-  for (int W = 1; W <= cap; ++W) {
-    if ((int64_t)fr_resident<F, MODE, ROWS, R>(W) * cus < wgs) break;
-    int64_t load = 0;
-    for (int w = 0; w < W; ++w) {
-      int64_t l = 0;
-      for (int c = w; c < ceff; c += W) {
-        int32_t g0, g1;
-        split_range(K, S, c < m ? c : S - 1, g0, g1);
-        l += g1 - g0;
-      }
-      load = l > load ? l : load;
-    }
-    if (load < best_load) best_load = load, best = W;
-  }
-  return best;
-}
-
 // Four rows a wave (16 lanes a row) and one row group a workgroup.  Measured on
 // the 5120 x 25600 projection: 8 rows a wave was slower in 70 of 72 format,
 // mode and S (4, 5, 8) cases, by up to 43%; two row groups a workgroup and
 // fetching two or three steps ahead were slower too.
 template <int F, int MODE>
+int f_waves(int64_t N, int64_t K, int S, int& m, int& ceff) {
+  f_chunks(K, S, m, ceff);
+  if (S == 1) m = 1, ceff = 1;
+  // at 5120 rows and S = 8: four waves of two chunks; at S = 16, five or six
+  return pick_chunk_waves((N + 3) / 4, 16, K, S, m, ceff, tune(QDG_TUNE_FMT_WAVES),
+                          [](int w) { return fr_resident<F, MODE, 4, 1>(w); });
+}
+
+template <int F, int MODE>
 hipError_t launch_f(const uint8_t* w, int64_t N, int64_t K, const float* x, const int8_t* xq, const int8_t* xl,
                     const float* xs, int S, float* y, hipStream_t st) {
   int m, ceff;
-  f_chunks(K, S, m, ceff);
-  if (S == 1) m = 1, ceff = 1;
-  const int W = fr_waves<F, MODE, 4, 1>(N, K, S, m, ceff);
+  const int W = f_waves<F, MODE>(N, K, S, m, ceff);
   return launch_fr<F, MODE, 4, 1>(w, N, K, x, xq, xl, xs, S, m, ceff, W, y, st);
+}
+
+template <int F>
+int fm_waves(int mode, int64_t N, int64_t K, int S) {
+  int m, ceff;
+  if (mode == 0) return f_waves<F, 0>(N, K, S, m, ceff);
+  if (mode == 1) return f_waves<F, 1>(N, K, S, m, ceff);
+  return f_waves<F, 2>(N, K, S, m, ceff);
 }
 
 template <int F>
@@ -855,6 +818,25 @@ hipError_t launch_fm(int mode, const uint8_t* w, int64_t N, int64_t K, const flo
 }
 
 }  // namespace
+
+// Compute units of the current device (256 on the MI355X), asked once a device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Values per block and bytes per block of a format (0, 0 if unknown).
 void fmt_geometry(int fmt, int& values, int& bytes) {
@@ -873,6 +855,23 @@ void fmt_geometry(int fmt, int& values, int& bytes) {
     case F_Q6_K: values = 256; bytes = 210; break;
     case F_IQ4_XS: values = 256; bytes = 136; break;
     default: values = 0; bytes = 0;
+  }
+}
+
+int fmt_chunk_waves(int fmt, int mode, int64_t N, int64_t K, int S) {
+  switch (fmt) {
+    case F_Q4_0: return fm_waves<F_Q4_0>(mode, N, K, S);
+    case F_Q4_1: return fm_waves<F_Q4_1>(mode, N, K, S);
+    case F_Q5_0: return fm_waves<F_Q5_0>(mode, N, K, S);
+    case F_Q5_1: return fm_waves<F_Q5_1>(mode, N, K, S);
+    case F_IQ4_NL: return fm_waves<F_IQ4_NL>(mode, N, K, S);
+    case F_MXFP4: return fm_waves<F_MXFP4>(mode, N, K, S);
+    case F_Q2_K: return fm_waves<F_Q2_K>(mode, N, K, S);
+    case F_Q3_K: return fm_waves<F_Q3_K>(mode, N, K, S);
+    case F_Q4_K: return fm_waves<F_Q4_K>(mode, N, K, S);
+    case F_Q5_K: return fm_waves<F_Q5_K>(mode, N, K, S);
+    case F_Q6_K: return fm_waves<F_Q6_K>(mode, N, K, S);
+    default: return fm_waves<F_IQ4_XS>(mode, N, K, S);
   }
 }
 

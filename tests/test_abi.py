@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 33
+    assert len(names) == 35
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -367,6 +367,19 @@ def test_fmt_validation():
     assert call(splits=65) == EINVAL
 
 
+def test_chunk_wave_queries_validate():
+    """The wave-count queries reject what the launches reject, before asking the device."""
+    fw, dw = lib.qdg_gemv_fmt_chunk_waves, lib.qdg_gemv_dq_chunk_waves
+    assert fw(8, 1, 64, 512, 8) == EINVAL        # unknown format
+    assert fw(2, 3, 64, 512, 8) == EINVAL        # unknown mode
+    assert fw(2, 1, 64, 512, 0) == EINVAL
+    assert fw(12, 1, 64, 480, 8) == ESHAPE       # Q4_K needs whole 256-value super-blocks
+    assert fw(2, 1, 0, 512, 8) == ESHAPE
+    assert dw(0, 512, 8) == ESHAPE
+    assert dw(64, 500, 8) == ESHAPE
+    assert dw(64, 512, 65) == ESHAPE
+
+
 def test_stream_read_validation():
     f = lib.qdg_stream_read
     assert f(None, 1024, P(A), None) == EINVAL
@@ -439,11 +452,11 @@ def test_tuning_knobs():
     """The tuning hooks start at the library's own choice (-1), never read the
     environment, reject unknown knobs, and the binding's context manager puts
     every knob back."""
-    for k in range(15):
+    for k in range(16):
         assert lib.qdg_get_tuning(k) == -1, k
-    assert lib.qdg_get_tuning(15) == EINVAL
+    assert lib.qdg_get_tuning(16) == EINVAL
     assert lib.qdg_get_tuning(-1) == EINVAL
-    assert lib.qdg_set_tuning(15, 0) == EINVAL
+    assert lib.qdg_set_tuning(16, 0) == EINVAL
     assert lib.qdg_set_tuning(2, 1) == OK and lib.qdg_get_tuning(2) == 1
     assert lib.qdg_set_tuning(2, -7) == OK and lib.qdg_get_tuning(2) == -1
     with q.tuning(ws_dma=0, ws_local=1):
@@ -452,7 +465,7 @@ def test_tuning_knobs():
             assert q.get_tuning("ws_local") == 0
         assert q.get_tuning("ws_local") == 1
     assert q.get_tuning("ws_dma") == -1 and q.get_tuning("ws_local") == -1
-    assert sorted(q.TUNE.values()) == list(range(15))
+    assert sorted(q.TUNE.values()) == list(range(16))
     assert lib.qdg_time_next_launch(None, None) == OK
 
 
@@ -466,7 +479,7 @@ def test_knobs_ignore_the_environment():
     env = dict(os.environ, QDG_WS_ROWS="1", QDG_SK_WSPLIT="0", QDG_WS_DMA="0", QDG_MFMA_GENERAL="1")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300, env=env)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.strip() == str([-1] * 15) + " (12, 15)", r.stdout
+    assert r.stdout.strip() == str([-1] * 16) + " (12, 15)", r.stdout
 
 
 def test_binding_checks_sizes_before_the_call():

@@ -121,6 +121,29 @@ def test_fmt_split(fmt, N, K, S, mode):
     assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
 
 
+def test_chunk_wave_queries(tune):
+    """The wave counts the launches use: within 1..min(chunks, 16), the knobs
+    reflected (clamped to the chunk count), QDG_EMODE where the Dequant
+    chunk-wave kernel does not serve the shape."""
+    announce("chunk-wave queries")
+    for fmt, mode, N, K, S, ceff in ((11, 1, 5120, 25600, 8, 8), (2, 2, 5120, 25600, 16, 13), (14, 0, 300, 4096, 5, 4),
+                                     (10, 1, 70, 512 * 40 + 256, 40, 40), (23, 2, 8, 256, 1, 1)):
+        w = q.fmt_chunk_waves(fmt, mode, N, K, S)
+        assert 1 <= w <= min(ceff, 16), (fmt, mode, N, K, S, w)
+        tune(fmt_waves=3)
+        assert q.fmt_chunk_waves(fmt, mode, N, K, S) == min(3, ceff)
+        tune(fmt_waves=-1)
+    for N, K, S, ceff in ((5120, 25600, 8, 8), (5120, 8192, 5, 4), (300, 25632, 5, 5)):
+        w = q.dq_chunk_waves(N, K, S)
+        assert 1 <= w <= ceff, (N, K, S, w)
+        tune(dq_waves=2)
+        assert q.dq_chunk_waves(N, K, S) == 2
+        tune(dq_waves=-1)
+    with pytest.raises(q.QdgError) as e:
+        q.dq_chunk_waves(64, 512 * 17, 17)   # 17 chunk waves: not this kernel
+    assert e.value.status == -4
+
+
 def wave_cases(fmt):
     """(N, K, S, W): W chunk waves forced below the chunk count, and more chunks
     than a workgroup has waves (S = 40, the last chunk with the K mod 512 tail)."""

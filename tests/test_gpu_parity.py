@@ -534,6 +534,26 @@ def test_fused_dequant_split_k(N, K, S, kernel, tune):
     assert not host(wsp).any()  # tickets and partial slots all back at zero
 
 
+@pytest.mark.parametrize("N,K,S", [(300, 25600, 8), (300, 25632, 5), (37, 8192, 16)])
+def test_dequant_chunk_waves_several_chunks_a_wave(N, K, S, tune):
+    """Waves that sum several chunks of the Dequant chunk-wave kernel one after
+    another (the wave count forced below the chunk count): the same bits as a
+    wave a chunk, and within the Dequant tolerance of the binary64 reference."""
+    wq, ws, x = _quant_case(N, K, 1, 31 * N + K + S, outliers=True)
+    Y, tn = oracle.reference_f64(0, wq, ws, x=x, nthreads=8)
+    wsp = q.sk_workspace(N, S)
+    outs = {}
+    for W in (16, 1, 2, 3):
+        announce(f"dequant chunk waves N={N} K={K} S={S} W={W}")
+        tune(dq_waves=W)
+        y = torch.full((1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_fused(0, dev(wq), dev(ws), y, dev(x.reshape(1, K)), S, wsp)
+        outs[W] = host(y)
+    assert oracle.within_tolerance(outs[16], Y, tn).all()
+    for W in (1, 2, 3):
+        assert outs[W].tobytes() == outs[16].tobytes(), W
+
+
 @pytest.mark.parametrize("N,K,S", [(37, 1600, 2), (100, 25600, 16), (5120, 8192, 4), (9, 256, 2), (65, 25632, 7),
                                    (5120, 25600, 5), (300, 25600, 1), (1, 32, 1), (130, 12288, 8), (21, 4608, 3)])
 @pytest.mark.parametrize("variant", ["R1", "R2", "R3", "R4"])
