@@ -399,7 +399,7 @@ def main() -> int:
         per_mode["dequant"] = {}
         for si, sh in enumerate(shapes):
             y0 = torch.empty((1, sh.N), dtype=torch.float32, device=dev)
-            S = (5, 8)[min(si, 1)]  # Dequant's measured best: five chunks (o-proj), eight (down-proj)
+            S = (5, 4)[min(si, 1)]  # Dequant's measured best: five chunks (o-proj), four (down-proj)
             dws = q.sk_workspace(sh.N, S)
             calls = [q.bind_gemv_q8_fused(0, copies[c][si][0], copies[c][si][1], y0, acts[si], S, dws)
                      for c in range(R)]

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, cons
     srow[r] = ws + o * nb;
   }
   // the wave's chunks in turn: cw, cw + W, ... (chunks 0..m-1, then S-1)
-  const int nq = (int)(K >> 9), nbk = (int)(K / QK), per = (nq + S - 1) / S;  // K < 2^29
+  const int nq = (int)(K >> 9), nbk = (int)(K / QK), per = (nq + S - 1) / S;  // K <= 2^31
   for (int c = cw; c < ceff; c += W) {
   int32_t g0, g1;
   split_range32(nq, nbk, per, S, c < m ? c : S - 1, g0, g1);
