@@ -17,6 +17,7 @@ Functions (each mirrors one step of the method; citations in ``qdg_oracle.c``):
 * ``reference_f64(mode, ...)`` -> ``(Y, tnorm)`` binary64 anchor of the tolerance
 * ``rmsnorm(x, r=None, w=None, eps)`` -> ``(s, y)``: residual sum and RMSNorm
 * ``swiglu(g, u)`` -> ``h = silu(g) * u``
+* ``glu(act, g, u)`` -> ``h = act(g) * u`` (silu, sigmoid or the tanh-form GELU)
 * ``fmt_geometry(fmt)``, ``fmt_row_bytes(fmt, K)``, ``fmt_decode(fmt, w, N, K)`` ->
   ``(levels [N][K], d [N][K/16], c [N][K/16])``, ``gemv_fmt(fmt, mode, w, N, K, ...)``:
   the other GGUF block formats
@@ -55,6 +56,7 @@ def _load():
         lib.orc_reference_f64.argtypes = [I, P, P, I64, I64, P, P, P, P, I64, P, P, I]
         lib.orc_rmsnorm.argtypes = [P, P, P, ctypes.c_float, I64, I64, P, P]
         lib.orc_swiglu.argtypes = [P, P, I64, P]
+        lib.orc_glu.argtypes = [I, P, P, I64, P]
         lib.orc_fmt_geometry.argtypes = [I, P, P]
         lib.orc_fmt_row_bytes.argtypes = [I, I64]
         lib.orc_fmt_row_bytes.restype = I64
@@ -64,7 +66,7 @@ def _load():
         lib.orc_half_to_float.restype = ctypes.c_float
         for name in ("orc_quantize", "orc_block_dots", "orc_gemv", "orc_split_bounds",
                      "orc_gemv_split", "orc_combine", "orc_argmax", "orc_reference_f64",
-                     "orc_rmsnorm", "orc_swiglu", "orc_fmt_geometry", "orc_fmt_decode", "orc_gemv_fmt"):
+                     "orc_rmsnorm", "orc_swiglu", "orc_glu", "orc_fmt_geometry", "orc_fmt_decode", "orc_gemv_fmt"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -223,6 +225,23 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
         raise ValueError("swiglu: g and u differ in shape")
     h = np.empty_like(g)
     _check(_load().orc_swiglu(_p(g), _p(u), g.size, _p(h)), "swiglu")
+    return h
+
+
+# Activation numbers of the gated product (the lane kernel library page's lk_act)
+SILU, SIGMOID, GELU_TANH = 0, 1, 2
+
+
+def glu(act: int, g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """``h = fl32(act(g) * u)`` evaluated in binary64, elementwise: act 0 silu
+    ``g / (1 + exp(-g))``, 1 sigmoid ``1 / (1 + exp(-g))``, 2 the tanh-form GELU
+    ``g / (1 + exp(-2z))``, ``z = sqrt(2/pi) * (g + 0.044715 g^3)``."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    if g.shape != u.shape:
+        raise ValueError("glu: g and u differ in shape")
+    h = np.empty_like(g)
+    _check(_load().orc_glu(int(act), _p(g), _p(u), g.size, _p(h)), "glu")
     return h
 
 

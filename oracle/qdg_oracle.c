@@ -416,6 +416,41 @@ int orc_swiglu(const float *g, const float *u, int64_t n, float *h)
 }
 
 /*
+ * glu -- [P1] lk_act (the activation numbers: 0 silu g / (1 + e^-g), 1 sigmoid
+ * 1 / (1 + e^-g), 2 the GELU in ggml's tanh form g / (1 + e^-2z) with
+ * z = sqrt(2/pi) * (g + 0.044715 g^3)) and GLU / lk_gemv_glu (the gated value
+ * u * act(g) that feeds the next quantized GEMV); [P3] the gelu-gated MLP of the
+ * megakernel page (gelu_tanh(gate) times up).
+ *
+ * Reading: h = act(g) * u, each step below evaluated in binary64 from the
+ * binary32 g and u in the order written and rounded once to binary32, as for
+ * silu above (act 0 is the same computation as orc_swiglu).  The two constants
+ * of the GELU are the binary64 values of sqrt(2/pi) and 0.044715 (the page
+ * writes them as binary32 literals of those numbers); g^3 is (g * g) * g.
+ * exp overflows to +inf for large negative arguments, where the quotients are
+ * signed zeros, their limits.  act outside 0..2: -1.
+ */
+int orc_glu(int act, const float *g, const float *u, int64_t n, float *h)
+{
+    static const double c1 = 0.79788456080286535588, c2 = 0.044715;
+    if (n < 0 || act < 0 || act > 2) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double gv = (double)g[i];
+        double a;
+        if (act == 0) {
+            a = gv / (1.0 + exp(-gv));
+        } else if (act == 1) {
+            a = 1.0 / (1.0 + exp(-gv));
+        } else {
+            const double z = c1 * (gv + c2 * ((gv * gv) * gv));
+            a = gv / (1.0 + exp(-2.0 * z));
+        }
+        h[i] = (float)(a * (double)u[i]);
+    }
+    return 0;
+}
+
+/*
  * Block formats other than the split Q8_0 -- [P1] module doc (a matrix in any
  * other GGUF format keeps its blocks as stored; a 32-weight sub-block decodes to
  * int8 levels with a scale d and an offset c per half of 16, weight = d*level +

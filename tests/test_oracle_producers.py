@@ -176,3 +176,96 @@ def test_swiglu_scipy_logistic():
     ref = (g.astype(np.float64) * special.expit(g.astype(np.float64)) * u).astype(np.float32)
     diff = np.abs(h.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
     assert diff.max() <= 1 and np.mean(diff == 0) > 0.999
+
+
+# The gated product with the other activations of the lane kernel library
+# page's lk_act: sigmoid and the GELU in its tanh form.
+PI50 = Decimal("3.1415926535897932384626433832795028841971693993751")
+
+
+def glu_decimal(act, g, u):
+    gd = dec(g)
+    if act == 0:
+        a = gd / (1 + (-gd).exp())
+    elif act == 1:
+        a = 1 / (1 + (-gd).exp())
+    else:
+        z = (2 / PI50).sqrt() * (gd + Decimal("0.044715") * gd * gd * gd)
+        a = gd / (1 + (-2 * z).exp())
+    return a * dec(u)
+
+
+def test_glu_silu_is_the_swiglu():
+    rng = np.random.default_rng(6)
+    g = rng.uniform(-30, 30, 2000).astype(np.float32)
+    u = rng.standard_normal(2000).astype(np.float32)
+    assert np.array_equal(oracle.glu(oracle.SILU, g, u).view(np.uint32), oracle.swiglu(g, u).view(np.uint32))
+
+
+@pytest.mark.parametrize("act", [1, 2])
+def test_glu_against_fifty_digits(act):
+    rng = np.random.default_rng(7 + act)
+    g = np.concatenate([rng.uniform(-12, 12, 400), rng.standard_normal(400) * 1e-3,
+                        [0.5, -0.5, 3.0, -3.0, 1e-30, -1e-30]]).astype(np.float32)
+    u = rng.standard_normal(g.size).astype(np.float32)
+    h = oracle.glu(act, g, u)
+    near = sum(check_rounded(h[i], glu_decimal(act, g[i], u[i]), (act, i, g[i], u[i])) for i in range(g.size))
+    assert near <= 3
+
+
+def test_glu_sigmoid_closed_forms_symmetry_and_limits():
+    u = np.array([3.0, -7.25, 1e-30, 6e37], np.float32)
+    h = oracle.glu(oracle.SIGMOID, np.zeros(4, np.float32), u)
+    assert np.array_equal(h, u / 2)                            # the logistic at 0 is exactly 1/2
+    one = np.ones(4, np.float32)
+    lim = oracle.glu(oracle.SIGMOID, np.array([100.0, -800.0, -1e38, 1e38], np.float32), one)
+    assert lim[0] == 1.0 and lim[3] == 1.0                     # e^-100 vanishes next to 1 in binary64
+    assert lim[1] == 0 and not np.signbit(lim[1]) and lim[2] == 0
+    # sigma(g) + sigma(-g) = 1
+    g = np.random.default_rng(8).uniform(-15, 15, 1000).astype(np.float32)
+    s = oracle.glu(oracle.SIGMOID, g, np.ones_like(g)).astype(np.float64) + \
+        oracle.glu(oracle.SIGMOID, -g, np.ones_like(g))
+    assert np.all(np.abs(s - 1.0) <= 2 * np.spacing(np.float32(1.0)))
+
+
+def test_glu_gelu_identities_and_limits():
+    one = np.ones(6, np.float32)
+    h = oracle.glu(oracle.GELU_TANH, np.array([0.0, -0.0, 20.0, -20.0, 1e38, -1e38], np.float32), one)
+    assert h[0] == 0 and h[1] == 0
+    assert h[2] == 20.0                                        # e^-2z is some e^-1e3 there
+    assert h[3] == 0 and np.signbit(h[3])                     # -20 / e^600: below every binary32
+    assert h[4] == np.float32(1e38) and h[5] == 0 and np.signbit(h[5])
+    # gelu(g) - gelu(-g) = g, since 1 / (1 + e^-2z) + 1 / (1 + e^2z) = 1
+    g = np.random.default_rng(9).uniform(-8, 8, 1000).astype(np.float32)
+    d = oracle.glu(oracle.GELU_TANH, g, np.ones_like(g)).astype(np.float64) - \
+        oracle.glu(oracle.GELU_TANH, -g, np.ones_like(g))
+    assert np.all(np.abs(d - g) <= 4 * np.spacing(np.abs(g)).astype(np.float64))
+    # the same function as 0.5 g (1 + tanh z), evaluated through tanh instead of
+    # exp, where that form is well conditioned (z > -1/2: no cancellation in
+    # 1 + tanh z; below, the fifty-digit pin above covers it)
+    rng = np.random.default_rng(10)
+    g = rng.uniform(-0.6, 6, 20000).astype(np.float32)
+    gd = g.astype(np.float64)
+    z = np.sqrt(2 / np.pi) * (gd + 0.044715 * gd ** 3)
+    g, gd, z = g[z > -0.5], gd[z > -0.5], z[z > -0.5]
+    u = rng.standard_normal(g.size).astype(np.float32)
+    ref = (0.5 * gd * (1 + np.tanh(z)) * u).astype(np.float32)
+    hh = oracle.glu(oracle.GELU_TANH, g, u)
+    diff = np.abs(hh.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert diff.max() <= 1 and np.mean(diff == 0) > 0.999
+
+
+def test_glu_sigmoid_scipy_logistic():
+    special = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(11)
+    g = rng.uniform(-40, 40, 20000).astype(np.float32)
+    u = rng.standard_normal(20000).astype(np.float32)
+    h = oracle.glu(oracle.SIGMOID, g, u)
+    ref = (special.expit(g.astype(np.float64)) * u).astype(np.float32)
+    diff = np.abs(h.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert diff.max() <= 1 and np.mean(diff == 0) > 0.999
+
+
+def test_glu_rejects_an_unknown_activation():
+    with pytest.raises(Exception):
+        oracle.glu(3, np.zeros(4, np.float32), np.zeros(4, np.float32))
