@@ -348,6 +348,27 @@ int qdg_gemv_q8_rmsnorm(int mode, const int8_t *wq, const uint16_t *ws, int64_t 
 int qdg_swiglu_quantize(int mode, const float *g, const float *u, int64_t B, int64_t K,
                         float *h, int8_t *xq, int8_t *xl, float *xs, qdg_stream stream);
 
+/* The activations of the gated product (lane kernel library page, lk_act's ACT numbers). */
+enum {
+  QDG_ACT_SILU = 0,      /* g / (1 + e^-g): SwiGLU                                       */
+  QDG_ACT_SIGMOID = 1,   /* 1 / (1 + e^-g)                                               */
+  QDG_ACT_GELU_TANH = 2  /* g / (1 + e^-2z), z = sqrt(2/pi) * (g + 0.044715 g^3): GeGLU  */
+};
+
+/*
+ * The same with any of lk_act's activations (lane kernel library page, lk_act
+ * and GLU / lk_gemv_glu: u * act(g); the megakernel page's gelu-gated MLP):
+ * h = act(g) * u per value, each step in binary64 from the binary32 g and u in
+ * the order written -- g^3 as (g*g)*g, the GELU's constants the binary64 values
+ * of sqrt(2/pi) and 0.044715 -- and rounded once to binary32 (within one unit in
+ * the last place of the exactly rounded value); then quantized as
+ * qdg_quantize_act quantizes it.  act QDG_ACT_SILU is qdg_swiglu_quantize, bit
+ * for bit.  An act outside the three: QDG_EINVAL.  Arguments otherwise as
+ * qdg_swiglu_quantize.
+ */
+int qdg_glu_quantize(int act, int mode, const float *g, const float *u, int64_t B, int64_t K,
+                     float *h, int8_t *xq, int8_t *xl, float *xs, qdg_stream stream);
+
 /*
  * Up to QDG_MAX_PARTS weight matrices over one activation row in one launch:
  * q, k and v, or gate and up, side by side (lane kernel library page,
@@ -384,6 +405,14 @@ int qdg_gemv_q8_parts(int mode, const qdg_part *parts, int nparts, int64_t K, co
 int qdg_gemv_glu_q8(int mode, const int8_t *wg, const uint16_t *sg, const int8_t *wu,
                     const uint16_t *su, int64_t F, int64_t K, const int8_t *xq, const int8_t *xl,
                     const float *xs, float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
+
+/* The same with any of lk_act's activations (h = act(g) * u as qdg_glu_quantize
+ * computes it; lane kernel library page, lk_gemv_glu's ACT): bit-identical to two
+ * qdg_gemv_q8 calls and qdg_glu_quantize.  act QDG_ACT_SILU is qdg_gemv_glu_q8;
+ * an act outside the three: QDG_EINVAL.  Arguments otherwise as qdg_gemv_glu_q8. */
+int qdg_gemv_glu_act_q8(int act, int mode, const int8_t *wg, const uint16_t *sg, const int8_t *wu,
+                        const uint16_t *su, int64_t F, int64_t K, const int8_t *xq, const int8_t *xl,
+                        const float *xs, float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
 
 /* GGUF type numbers of the other block formats (qdg_gemv_fmt). */
 enum {

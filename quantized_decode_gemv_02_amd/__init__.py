@@ -81,8 +81,10 @@ _SIGS = {
     "qdg_gemv_q8_rmsnorm": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _P, ctypes.c_float, _I, _P, _P, _P,
                              _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_swiglu_quantize": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
+    "qdg_glu_quantize": ([_I, _I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "qdg_gemv_glu_act_q8": ([_I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
     "qdg_gemv_fmt_chunk_waves": ([_I, _I, _I64, _I64, _I], _I),
@@ -270,6 +272,20 @@ def bind_swiglu_quantize(mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> 
     return Bound("qdg_swiglu_quantize", *_swiglu_args(mode, g, u, h, xq, xl, xs))
 
 
+# The activations of the gated product (include/qdg.h: QDG_ACT_*, the lane kernel library page's lk_act numbers)
+ACT_SILU, ACT_SIGMOID, ACT_GELU_TANH = 0, 1, 2
+
+
+def glu_quantize(act: int, mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> None:
+    """``h = act(g) * u`` (silu, sigmoid or the tanh-form GELU; optional output under the
+    quantized modes) and its quantized words."""
+    _check("qdg_glu_quantize", _lib.qdg_glu_quantize(act, *_swiglu_args(mode, g, u, h, xq, xl, xs)))
+
+
+def bind_glu_quantize(act: int, mode: int, g, u, h=None, xq=None, xl=None, xs=None) -> Bound:
+    return Bound("qdg_glu_quantize", act, *_swiglu_args(mode, g, u, h, xq, xl, xs))
+
+
 def _glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs):
     F, K = wg.shape
     if tuple(wu.shape) != (F, K):
@@ -287,6 +303,16 @@ def gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> No
 
 def bind_gemv_glu_q8(mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> Bound:
     return Bound("qdg_gemv_glu_q8", *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs))
+
+
+def gemv_glu_act_q8(act: int, mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> None:
+    """``gemv_glu_q8`` with any of the gated product's activations (``ACT_*``)."""
+    _check("qdg_gemv_glu_act_q8",
+           _lib.qdg_gemv_glu_act_q8(act, *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs)))
+
+
+def bind_gemv_glu_act_q8(act: int, mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> Bound:
+    return Bound("qdg_gemv_glu_act_q8", act, *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs))
 
 
 # GGUF type numbers of the other block formats

@@ -329,6 +329,13 @@ int qdg_gemv_q8_parts(int mode, const qdg_part* parts, int nparts, int64_t K, co
 int qdg_gemv_glu_q8(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
                     int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq, int8_t* hl,
                     float* hs, qdg_stream stream) {
+  return qdg_gemv_glu_act_q8(QDG_ACT_SILU, mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, stream);
+}
+
+int qdg_gemv_glu_act_q8(int act, int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu,
+                        const uint16_t* su, int64_t F, int64_t K, const int8_t* xq, const int8_t* xl,
+                        const float* xs, float* h, int8_t* hq, int8_t* hl, float* hs, qdg_stream stream) {
+  if (act < QDG_ACT_SILU || act > QDG_ACT_GELU_TANH) return QDG_EINVAL;
   if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
   if (!wg || !sg || !wu || !su || !xq || !xs || !hq || !hs) return QDG_EINVAL;
   if ((mode == QDG_TWOPASS) != (xl != nullptr) || (mode == QDG_TWOPASS) != (hl != nullptr)) return QDG_EINVAL;
@@ -338,7 +345,8 @@ int qdg_gemv_glu_q8(int mode, const int8_t* wg, const uint16_t* sg, const int8_t
       (hl && !aligned(hl, 4)) || !aligned(hs, 4))
     return QDG_EALIGN;
   if (!qdg::glu_fits(mode, K)) return QDG_EMODE;
-  return hip_status(qdg::launch_gemv_glu(mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, as_stream(stream)));
+  return hip_status(
+      qdg::launch_gemv_glu(act, mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, as_stream(stream)));
 }
 
 int64_t qdg_fmt_row_bytes(int fmt, int64_t K) {
@@ -460,13 +468,19 @@ int qdg_gemv_q8_rmsnorm(int mode, const int8_t* wq, const uint16_t* ws, int64_t 
 
 int qdg_swiglu_quantize(int mode, const float* g, const float* u, int64_t B, int64_t K, float* h, int8_t* xq,
                         int8_t* xl, float* xs, qdg_stream stream) {
+  return qdg_glu_quantize(QDG_ACT_SILU, mode, g, u, B, K, h, xq, xl, xs, stream);
+}
+
+int qdg_glu_quantize(int act, int mode, const float* g, const float* u, int64_t B, int64_t K, float* h, int8_t* xq,
+                     int8_t* xl, float* xs, qdg_stream stream) {
+  if (act < QDG_ACT_SILU || act > QDG_ACT_GELU_TANH) return QDG_EINVAL;
   if (!g || !u) return QDG_EINVAL;
   const int st = producer_outputs(mode, h, xq, xl, xs);
   if (st != QDG_OK) return st;
   if (!shape_ok(B, K)) return QDG_ESHAPE;
   if ((B * K / qdg::QK) * 8 / 256 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
   if (!aligned(g, 16) || !aligned(u, 16) || !words_aligned(h, xq, xl, xs)) return QDG_EALIGN;
-  return hip_status(qdg::launch_swiglu_quant(mode, g, u, B * K / qdg::QK, h, xq, xl, xs, as_stream(stream)));
+  return hip_status(qdg::launch_glu_quant(act, mode, g, u, B * K / qdg::QK, h, xq, xl, xs, as_stream(stream)));
 }
 
 int qdg_block_dots(int mode, const int8_t* wq, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,

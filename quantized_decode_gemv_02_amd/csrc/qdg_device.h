@@ -327,13 +327,25 @@ __device__ __forceinline__ float4 norm4(float4 t, double den, bool has_w, float4
   return make_float4((float)ox, (float)oy, (float)oz, (float)ow);
 }
 
-// SwiGLU of one value (lane kernel library page, lk_act: silu(g) = g / (1 + e^-g),
-// times u): evaluated in binary64 from the binary32 operands and rounded once.
-// Shared by the SwiGLU producer and the gate/up GEMV epilogue, so the two give
-// the same bits.
-__device__ __forceinline__ float silu_mul(float g, float u) {
+// The gated product of one value, act(g) * u (lane kernel library page, lk_act
+// and GLU): act 0 silu g / (1 + e^-g), 1 sigmoid 1 / (1 + e^-g), 2 the GELU in its
+// tanh form g / (1 + e^-2z) with z = sqrt(2/pi) * (g + 0.044715 g^3), g^3 as
+// (g*g)*g; every step in binary64 from the binary32 operands, in the order
+// written, and rounded once to binary32.  Shared by the producer and the gate/up
+// GEMV epilogue, so the two give the same bits.
+template <int ACT>
+__device__ __forceinline__ float glu_mul(float g, float u) {
   const double gd = (double)g;
-  return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+  double a;
+  if constexpr (ACT == 0) {
+    a = gd / (1.0 + exp(-gd));
+  } else if constexpr (ACT == 1) {
+    a = 1.0 / (1.0 + exp(-gd));
+  } else {
+    const double z = 0.79788456080286535588 * (gd + 0.044715 * ((gd * gd) * gd));
+    a = gd / (1.0 + exp(-2.0 * z));
+  }
+  return (float)(a * (double)u);
 }
 
 // The s_waitcnt operand that waits until at most n vector-memory loads of the
@@ -582,11 +594,11 @@ int dq_chunk_waves(int64_t N, int64_t K, int splits);
 hipError_t launch_gemv_fmt(int fmt, int mode, const uint8_t* w, int64_t N, int64_t K, const float* x,
                            const int8_t* xq, const int8_t* xl, const float* xs, int splits, float* y,
                            hipStream_t st);
-hipError_t launch_gemv_glu(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
-                           int64_t F, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h,
-                           int8_t* hq, int8_t* hl, float* hs, hipStream_t st);
-hipError_t launch_swiglu_quant(int mode, const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq,
-                               int8_t* xl, float* xs, hipStream_t st);
+hipError_t launch_gemv_glu(int act, int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu,
+                           const uint16_t* su, int64_t F, int64_t K, const int8_t* xq, const int8_t* xl,
+                           const float* xs, float* h, int8_t* hq, int8_t* hl, float* hs, hipStream_t st);
+hipError_t launch_glu_quant(int act, int mode, const float* g, const float* u, int64_t nblocks, float* h,
+                            int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st);
 int64_t gemv_tiles(int64_t N);
 hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,

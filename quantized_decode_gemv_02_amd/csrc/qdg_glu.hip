@@ -1,16 +1,17 @@
 // qdg_glu.hip -- the gate and up projections of one activation in one launch,
-// with the SwiGLU and the quantizer as the epilogue (lane kernel library page,
-// GLU / lk_gemv_glu: a block of warps takes 32 outputs, gates them, and writes
-// one quantized block of the next projection's activation; lk_act for silu).
+// with the gated product and the quantizer as the epilogue (lane kernel library
+// page, GLU / lk_gemv_glu: a block of warps takes 32 outputs, gates them, and
+// writes one quantized block of the next projection's activation; lk_act for
+// the activation: silu, sigmoid or the tanh-form GELU).
 //
 // A workgroup of 16 waves owns outputs [32b, 32b + 32): waves 0-7 the 32 gate
 // rows, waves 8-15 the 32 up rows, four rows a wave over all of K, each row
 // summed exactly as the batch-1 GEMV sums it (chunk_dot4 over the whole row).
-// The 64 results meet in LDS; then eight lanes form h = silu(g) * u for the 32
-// outputs (silu_mul, the SwiGLU producer's own arithmetic) and quantize them as
-// one block (quant_lane4).  So g, u, h and the words are bit-identical to two
-// qdg_gemv_q8 calls followed by qdg_swiglu_quantize, without the g/u round trip
-// or the extra launch.
+// The 64 results meet in LDS; then eight lanes form h = act(g) * u for the 32
+// outputs (glu_mul, the producer's own arithmetic) and quantize them as one
+// block (quant_lane4).  So g, u, h and the words are bit-identical to two
+// qdg_gemv_q8 calls followed by qdg_glu_quantize, without the g/u round trip or
+// the extra launch.
 //
 // Staging (DMA): as in the split-K GEMV, the activation and the 64 rows' weight
 // scales go straight from global memory into LDS (global_load_lds_dwordx4)
@@ -31,7 +32,7 @@ constexpr int GL_LDS_MAX = 79 * 1024;      // two workgroups a CU
 template <int MODE>
 constexpr int gl_bytes_per_block() { return (MODE == 2 ? 2 : 1) * QK + 4 + 2 * GL_ROWS; }
 
-template <int MODE, bool DMA>
+template <int MODE, bool DMA, int ACT>
 __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void k_gemv_glu(
     const int8_t* __restrict__ wg, const uint16_t* __restrict__ sg, const int8_t* __restrict__ wu,
     const uint16_t* __restrict__ su, int64_t K, const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < 8) {
       const int i = 4 * lane;
-      v = make_float4(silu_mul(lout[i], lout[32 + i]), silu_mul(lout[i + 1], lout[33 + i]),
-                      silu_mul(lout[i + 2], lout[34 + i]), silu_mul(lout[i + 3], lout[35 + i]));
+      v = make_float4(glu_mul<ACT>(lout[i], lout[32 + i]), glu_mul<ACT>(lout[i + 1], lout[33 + i]),
+                      glu_mul<ACT>(lout[i + 2], lout[34 + i]), glu_mul<ACT>(lout[i + 3], lout[35 + i]));
       if (h) *(float4*)(h + o0 + i) = v;
     }
     int hw, lw;
@@ -116,29 +117,29 @@ __global__ __launch_bounds__(GL_NT) __attribute__((amdgpu_waves_per_eu(8))) void
   }
 }
 
-template <int MODE, bool DMA>
+template <int MODE, bool DMA, int ACT>
 hipError_t launch_glu_s(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
                         int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq,
                         int8_t* hl, float* hs, hipStream_t st) {
-  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_glu<MODE, DMA>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)&k_gemv_glu<MODE, DMA, ACT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, GL_LDS_MAX);
   if (attr != hipSuccess) return attr;
   const size_t lds = (size_t)(K / QK) * gl_bytes_per_block<MODE>();
   const dim3 grid((unsigned)(F / 32)), block(GL_NT);
-  return launch((k_gemv_glu<MODE, DMA>), grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
+  return launch((k_gemv_glu<MODE, DMA, ACT>), grid, block, lds, st, wg, sg, wu, su, K, xq, xl, xs, h, hq, hl, hs);
 }
 
 // LDS DMA staging when K is a multiple of 256 and every staged array starts
-// 16-byte aligned; QDG_WS_DMA=0 turns it off (read on every call).
-template <int MODE>
+// 16-byte aligned; the knob QDG_TUNE_WS_DMA = 0 turns it off.
+template <int MODE, int ACT>
 hipError_t launch_glu_m(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F,
                         int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h, int8_t* hq,
                         int8_t* hl, float* hs, hipStream_t st) {
   bool dma = K % 256 == 0 && (((uintptr_t)xq | (uintptr_t)xs | (uintptr_t)sg | (uintptr_t)su) & 15) == 0 &&
              (MODE == 1 || ((uintptr_t)xl & 15) == 0);
   if (tune(QDG_TUNE_WS_DMA) == 0) dma = false;
-  if (dma) return launch_glu_s<MODE, true>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
-  return launch_glu_s<MODE, false>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  if (dma) return launch_glu_s<MODE, true, ACT>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  return launch_glu_s<MODE, false, ACT>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
 }
 
 }  // namespace
@@ -148,11 +149,22 @@ bool glu_fits(int mode, int64_t K) {
   return (K / QK) * bpb <= GL_LDS_MAX;
 }
 
-hipError_t launch_gemv_glu(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
-                           int64_t F, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h,
-                           int8_t* hq, int8_t* hl, float* hs, hipStream_t st) {
-  if (mode == 1) return launch_glu_m<1>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
-  return launch_glu_m<2>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+namespace {
+template <int ACT>
+hipError_t launch_gemv_glu_a(int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                        int64_t F, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs, float* h,
+                        int8_t* hq, int8_t* hl, float* hs, hipStream_t st) {
+  if (mode == 1) return launch_glu_m<1, ACT>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  return launch_glu_m<2, ACT>(wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+}
+}  // namespace
+
+hipError_t launch_gemv_glu(int act, int mode, const int8_t* wg, const uint16_t* sg, const int8_t* wu,
+                           const uint16_t* su, int64_t F, int64_t K, const int8_t* xq, const int8_t* xl,
+                           const float* xs, float* h, int8_t* hq, int8_t* hl, float* hs, hipStream_t st) {
+  if (act == 0) return launch_gemv_glu_a<0>(mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  if (act == 1) return launch_gemv_glu_a<1>(mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
+  return launch_gemv_glu_a<2>(mode, wg, sg, wu, su, F, K, xq, xl, xs, h, hq, hl, hs, st);
 }
 
 }  // namespace qdg

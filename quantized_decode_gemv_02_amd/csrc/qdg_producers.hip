@@ -6,10 +6,12 @@
 //    RMSNORM: v = x + r, y = v / sqrt(mean(v^2) + eps) * w; QWEN38 page,
 //    gk_add_rmsnorm_q8f: the add writes the residual stream back), then the
 //    32-value block quantizer on y.
-//  * k_swiglu_quant: h = silu(g) * u (lane kernel library page, lk_act and GLU;
-//    QWEN38 page, gk_silu_had_q8), then the same quantizer on h.
+//  * k_glu_quant: h = act(g) * u -- silu (SwiGLU), sigmoid or the tanh-form
+//    GELU (lane kernel library page, lk_act and GLU; QWEN38 page,
+//    gk_silu_had_q8; the megakernel page's gelu-gated MLP) -- then the same
+//    quantizer on h.
 //
-// Arithmetic: the residual sum is one binary32 addition.  The norm and silu are
+// Arithmetic: the residual sum is one binary32 addition.  The norm and act are
 // evaluated in binary64 from binary32 operands and rounded once to binary32.
 // The squares are exact in binary64, and the row's sum of squares runs in a
 // fixed order: per thread, then a butterfly inside each wave, then the waves in
@@ -97,8 +99,8 @@ __global__ __launch_bounds__(NT) void k_rmsnorm_quant(const float* x, const floa
 }
 
 // Eight lanes a 32-value block, four values a lane, as k_quantize.  h may be g or u.
-template <int MODE>
-__global__ __launch_bounds__(256) void k_swiglu_quant(const float* g, const float* u, float* h,
+template <int MODE, int ACT>
+__global__ __launch_bounds__(256) void k_glu_quant(const float* g, const float* u, float* h,
                                                       int8_t* __restrict__ xq, int8_t* __restrict__ xl,
                                                       float* __restrict__ xs, int64_t nblocks) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const float* g, const floa
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   if (on) {
     const float4 a = *(const float4*)(g + e), b = *(const float4*)(u + e);
-    o = make_float4(silu_mul(a.x, b.x), silu_mul(a.y, b.y), silu_mul(a.z, b.z), silu_mul(a.w, b.w));
+    o = make_float4(glu_mul<ACT>(a.x, b.x), glu_mul<ACT>(a.y, b.y), glu_mul<ACT>(a.z, b.z), glu_mul<ACT>(a.w, b.w));
     if (h) *(float4*)(h + e) = o;
   }
   if constexpr (MODE != 0) {
@@ -135,12 +137,20 @@ hipError_t launch_rms(const float* x, const float* r, float* s, const float* w, 
 #undef QDG_RMS
 }
 
-template <int MODE>
-hipError_t launch_swiglu_m(const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq, int8_t* xl,
-                           float* xs, hipStream_t st) {
+template <int MODE, int ACT>
+hipError_t launch_glu_ma(const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq, int8_t* xl,
+                         float* xs, hipStream_t st) {
   const int64_t threads = nblocks * 8;
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  return launch(k_swiglu_quant<MODE>, grid, block, 0, st, g, u, h, xq, xl, xs, nblocks);
+  return launch(k_glu_quant<MODE, ACT>, grid, block, 0, st, g, u, h, xq, xl, xs, nblocks);
+}
+
+template <int ACT>
+hipError_t launch_glu_a(int mode, const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq,
+                        int8_t* xl, float* xs, hipStream_t st) {
+  if (mode == 0) return launch_glu_ma<0, ACT>(g, u, nblocks, h, xq, xl, xs, st);
+  if (mode == 1) return launch_glu_ma<1, ACT>(g, u, nblocks, h, xq, xl, xs, st);
+  return launch_glu_ma<2, ACT>(g, u, nblocks, h, xq, xl, xs, st);
 }
 
 }  // namespace
@@ -154,11 +164,11 @@ hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float*
   return launch_rms<2>(x, r, s, w, eps, B, K, y, xq, xl, xs, st);
 }
 
-hipError_t launch_swiglu_quant(int mode, const float* g, const float* u, int64_t nblocks, float* h, int8_t* xq,
-                               int8_t* xl, float* xs, hipStream_t st) {
-  if (mode == 0) return launch_swiglu_m<0>(g, u, nblocks, h, xq, xl, xs, st);
-  if (mode == 1) return launch_swiglu_m<1>(g, u, nblocks, h, xq, xl, xs, st);
-  return launch_swiglu_m<2>(g, u, nblocks, h, xq, xl, xs, st);
+hipError_t launch_glu_quant(int act, int mode, const float* g, const float* u, int64_t nblocks, float* h,
+                            int8_t* xq, int8_t* xl, float* xs, hipStream_t st) {
+  if (act == 0) return launch_glu_a<0>(mode, g, u, nblocks, h, xq, xl, xs, st);
+  if (act == 1) return launch_glu_a<1>(mode, g, u, nblocks, h, xq, xl, xs, st);
+  return launch_glu_a<2>(mode, g, u, nblocks, h, xq, xl, xs, st);
 }
 
 }  // namespace qdg

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 35
+    assert len(names) == 37
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -284,6 +284,36 @@ def test_swiglu_quantize_validation():
     assert call(u=A + 8) == EALIGN
     assert call(h=A + 4) == EALIGN
     assert call(mode=2, xl=A + 4) == EALIGN
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_glu_quantize_validation(act):
+    """qdg_glu_quantize checks as qdg_swiglu_quantize does, and rejects an unknown activation first."""
+    f = lib.qdg_glu_quantize
+
+    def call(act=act, mode=1, g=A, u=A, B=1, K=512, h=None, xq=A, xl=None, xs=A):
+        return f(act, mode, P(g), P(u), B, K, P(h), P(xq), P(xl), P(xs), None)
+
+    assert call(act=3) == EINVAL and call(act=-1) == EINVAL
+    assert call(g=None) == EINVAL
+    assert call(mode=0) == EINVAL
+    assert call(K=48) == ESHAPE
+    assert call(u=A + 8) == EALIGN
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_glu_act_validation(act):
+    f = lib.qdg_gemv_glu_act_q8
+
+    def call(act=act, mode=1, wg=A, sg=A, wu=A, su=A, F=128, K=4096, xq=A, xl=None, xs=A, h=None, hq=A, hl=None,
+             hs=A):
+        return f(act, mode, P(wg), P(sg), P(wu), P(su), F, K, P(xq), P(xl), P(xs), P(h), P(hq), P(hl), P(hs), None)
+
+    assert call(act=3) == EINVAL and call(act=-2) == EINVAL
+    assert call(mode=0) == EINVAL
+    assert call(F=100) == ESHAPE
+    assert call(h=A + 4) == EALIGN
+    assert call(mode=1, K=15808) == EMODE
 
 
 def test_parts_validation():

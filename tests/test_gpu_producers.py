@@ -316,3 +316,93 @@ def test_glu_unaligned_scales(mode):
     for a, b in zip(*outs):
         if a is not None:
             assert a.tobytes() == b.tobytes()
+
+
+# ---- the gated product with the other activations of lk_act: sigmoid and the tanh-form GELU
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("B,K", [(1, 32), (3, 544), (1, 25600), (16, 5120)])
+def test_glu_quantize(act, mode, B, K):
+    """qdg_glu_quantize against the oracle's gated product (h within one ulp, almost
+    always equal) and its words against the oracle's quantizer on the kernel's h;
+    act 0 bit for bit the SwiGLU call."""
+    announce(f"glu_quantize act={act} mode={mode} B={B} K={K}")
+    g, u = workloads.glu_inputs(B, K, 140 + K + act)
+    if act == 2:
+        g = g * np.float32(2.5)   # reach the GELU's saturated tails too
+    oh = oracle.glu(act, g, u)
+    dg, du = dev(g), dev(u)
+    h = torch.empty_like(dg)
+    xq, xl, xs = words(mode, B, K) if mode else (None, None, None)
+    q.glu_quantize(act, mode, dg, du, h, xq, xl, xs)
+    gh = host(h)
+    check_f32(gh, oh, f"act {act} h")
+    if mode:
+        check_words(mode, gh, xq, xl, xs, f"glu act {act}")
+    if act == 0:
+        h2 = torch.empty_like(dg)
+        q.swiglu_quantize(mode, dg, du, h2, *(words(mode, B, K) if mode else (None, None, None)))
+        assert torch.equal(h2.view(torch.int32), h.view(torch.int32))
+
+
+@pytest.mark.parametrize("act", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_glu_special_values_and_in_place(act, mode):
+    """Zeros, the saturated tails (overflowing exponentials, subnormal and zero
+    results) and h written over g."""
+    announce(f"glu special values act={act} mode={mode}")
+    K = 64
+    g = np.zeros((1, K), np.float32)
+    u = np.ones((1, K), np.float32)
+    g[0, :12] = [0.0, -0.0, 20.0, -20.0, 100.0, -100.0, -800.0, 1e-30, -1e-30, 3e38, -3e38, 5.0]
+    u[0, 5] = 3.0
+    u[0, 12:] = np.linspace(-4, 4, K - 12, dtype=np.float32)
+    g[0, 12:] = np.linspace(-12, 12, K - 12, dtype=np.float32)
+    oh = oracle.glu(act, g, u)
+    dg = dev(g)
+    xq, xl, xs = words(mode, 1, K)
+    q.glu_quantize(act, mode, dg, dev(u), dg, xq, xl, xs)      # h over g
+    gh = host(dg)
+    check_f32(gh, oh, "special h")
+    assert np.array_equal(gh[0, :11].view(np.uint32), oh[0, :11].view(np.uint32))
+    check_words(mode, gh, xq, xl, xs, f"glu act {act} special")
+
+
+@pytest.mark.parametrize("act", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("F,K", [(32, 32), (64, 544), (12288, 4096), (96, 12800)])
+def test_glu_act_matches_the_three_calls(act, mode, F, K):
+    """qdg_gemv_glu_act_q8 against two qdg_gemv_q8 calls and qdg_glu_quantize, bit
+    for bit, and the oracle: g and u bit-exact, h within one ulp, words bit-exact on
+    the kernel's h."""
+    announce(f"gemv_glu act={act} mode={mode} F={F} K={K}")
+    wg, sg = workloads.weights(F, K, 171 + K, 172 + K)
+    wu, su = workloads.weights(F, K, 173 + K, 174 + K)
+    x = workloads.batch_activation(1, K, 175 + K, True, 176 + K)
+    dwg, dsg = dev(wg), dev(sg.view(np.int16))
+    dwu, dsu = dev(wu), dev(su.view(np.int16))
+    xq, xl, xs = words(mode, 1, K)
+    q.quantize_act(mode, dev(x), xq, xl, xs)
+    h = torch.empty((F,), dtype=torch.float32, device=DEV)
+    hq, hl, hs = words(mode, 1, F)
+    q.gemv_glu_act_q8(act, mode, dwg, dsg, dwu, dsu, xq, xl, xs, hq, hl, hs, h=h)
+    g = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    u = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    q.gemv_q8(mode, dwg, dsg, g, xq=xq, xl=xl, xs=xs)
+    q.gemv_q8(mode, dwu, dsu, u, xq=xq, xl=xl, xs=xs)
+    h2 = torch.empty((1, F), dtype=torch.float32, device=DEV)
+    hq2, hl2, hs2 = words(mode, 1, F)
+    q.glu_quantize(act, mode, g, u, h2, hq2, hl2, hs2)
+    assert torch.equal(h.view(torch.int32), h2.view(-1).view(torch.int32))
+    assert torch.equal(hq.view(-1), hq2.view(-1)) and torch.equal(hs.view(torch.int32).view(-1),
+                                                                  hs2.view(torch.int32).view(-1))
+    if mode == 2:
+        assert torch.equal(hl.view(-1), hl2.view(-1))
+    oq, ol, os_ = oracle.quantize(mode, x)
+    og = oracle.gemv(mode, wg, sg, xq=oq, xl=ol, xs=os_, nthreads=8)
+    ou = oracle.gemv(mode, wu, su, xq=oq, xl=ol, xs=os_, nthreads=8)
+    assert np.array_equal(host(g), og) and np.array_equal(host(u), ou)
+    gh = host(h).reshape(1, F)
+    check_f32(gh, oracle.glu(act, og, ou), f"glu act {act} h")
+    check_words(mode, gh, hq.view(1, F), None if hl is None else hl.view(1, F), hs.view(1, F // 32), "glu act")
