@@ -544,8 +544,31 @@ def main() -> int:
             calls = [q.bind_gemv_q8(mode, w, s, y, xq=xq, xl=xl, xs=xs) for w, s in wsets]
             rec[NAMES[mode]] = {"B": sh.B, "alg_bytes": alg_bytes(mode, sh.N, sh.K, sh.B),
                                 **rate(alg_bytes(mode, sh.N, sh.K, sh.B), timer.median_us(calls, args.launches))}
-        configs[f"batched_B{sh.B}_{sh.N}x{sh.K}"] = rec
+        # the same batch over MFMA-ordered operands: the weights repacked once
+        # (qdg_q8_tile_mma), the activations quantized into the MFMA order
+        # (qdg_quantize_act_mma, timed beside), the GEMV qdg_gemv_q8_mma_tiled
+        tiles = []
+        for w, s in wsets:
+            wt = torch.empty(q.q8_tile_mma_bytes(sh.N, sh.K), dtype=torch.uint8, device=dev)
+            q.q8_tile_mma(w, s, wt)
+            tiles.append(wt)
         del wsets
+        torch.cuda.empty_cache()
+        tiled = {}
+        for mode in (1, 2):
+            tq = torch.empty(16 * sh.K, dtype=torch.int8, device=dev)
+            tl = torch.empty(16 * sh.K, dtype=torch.int8, device=dev) if mode == 2 else None
+            ts = torch.empty(16 * (sh.K // 32), dtype=torch.float32, device=dev)
+            qcall = q.bind_quantize_act_mma(mode, x, tq, tl, ts)
+            qcall()
+            y = torch.empty((sh.B, sh.N), dtype=torch.float32, device=dev)
+            calls = [q.bind_gemv_q8_mma_tiled(mode, wt, sh.N, sh.K, y, tq, tl, ts, sh.B) for wt in tiles]
+            b = alg_bytes(mode, sh.N, sh.K, sh.B)
+            tiled[NAMES[mode]] = {"B": sh.B, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches)),
+                                  "quantize_us": round(timer.median_us([qcall], args.launches), 3)}
+        rec["mma_tiled"] = tiled
+        configs[f"batched_B{sh.B}_{sh.N}x{sh.K}"] = rec
+        del tiles
         torch.cuda.empty_cache()
         progress("batched done")
 

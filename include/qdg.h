@@ -518,6 +518,60 @@ int qdg_gemv_q8_sk_tiled(int mode, const int8_t *wt, const uint16_t *ws, int64_t
                          qdg_stream stream);
 
 /*
+ * MFMA-tiled weights for the batched GEMV (megakernel page, the GEMV's
+ * tiled-weights option: only the addresses of the weights change).  One record
+ * per (64-row group q, 8-block step s, residue r in 0..3), in that row-major
+ * order, holds what one wave of qdg_gemv_q8_mma_tiled consumes in one step:
+ *   - bytes 0..4095: byte 1024*m + 16*l + 8*h + j (tile m in 0..3, lane l in
+ *     0..63, c = l mod 16, u = l / 16, h in 0..1) is byte 8*u + j of block
+ *     8*s + r + 4*h of row 64*q + 16*m + c -- a lane's 16 bytes are the int8
+ *     MFMA's B operands of the step's two blocks;
+ *   - bytes 4096..4351: 16-bit word 8*c + 2*m + h is the binary16 scale (bits)
+ *     of that row and block.
+ * Rows past N are zero.  qdg_q8_tile_mma_bytes gives the size,
+ * ceil(N/64) * (K/256) * 4 * 4352, or 0 when the shape is not served: K a
+ * positive multiple of 256 below 2^30, N >= 1 (and the record count below
+ * 2^31).  wq [N][K] (16-byte aligned), ws [N][K/32] (2-byte aligned) and wt
+ * (16-byte aligned) are device arrays; wt must not overlap wq or ws
+ * (QDG_EINVAL).  The caller owns all three.
+ */
+int64_t qdg_q8_tile_mma_bytes(int64_t N, int64_t K);
+int qdg_q8_tile_mma(const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K, uint8_t *wt,
+                    qdg_stream stream);
+
+/*
+ * qdg_quantize_act for 1 <= B <= 16 rows, with the words and scales written in
+ * the MFMA order that qdg_gemv_q8_mma_tiled reads: for step s (8 blocks) and
+ * residue r in 0..3, record (s, r) holds 1024 word bytes, byte 16*l + 8*h + j
+ * (lane l, t = l mod 16, u = l / 16) being word 8*u + j of block 8*s + r + 4*h of
+ * row t, and 32 scales, scale 16*h + t of the record being that block's scale
+ * of row t.  Records run (s, r) in row-major order: xq (and xl under
+ * QDG_TWOPASS) hold 16*K bytes, xs 16*K/32 floats.  The words and scales of rows
+ * t < B are qdg_quantize_act's on the same x, bit for bit; rows B..15 are those
+ * of a zero row.  x [B][K] (16-byte aligned); xq, xl 16-byte aligned; xs
+ * 4-byte.  K as qdg_q8_tile_mma (else QDG_ESHAPE).
+ */
+int qdg_quantize_act_mma(int mode, const float *x, int64_t B, int64_t K, int8_t *xq, int8_t *xl,
+                         float *xs, qdg_stream stream);
+
+/*
+ * qdg_gemv_q8 for 1 <= B <= 16 activation rows over MFMA-tiled weights wt (from
+ * qdg_q8_tile_mma) and MFMA-ordered activations xq, xl, xs (from
+ * qdg_quantize_act_mma): the same terms in the same order (the int8 MFMA's exact
+ * block dots, partial g mod 4, (P0 + P2) + (P1 + P3)), so out is bit-identical
+ * to qdg_gemv_q8 over the plain weights and the plain activations of the same x
+ * with the same B and splits, and every row to its batch-1 result.
+ * QDG_INT8ACT or QDG_TWOPASS (xl NULL for QDG_INT8ACT; QDG_DEQUANT gives
+ * QDG_EMODE); B > 16 gives QDG_EMODE.  splits == 1: out is y [B][N];
+ * splits > 1: partials [splits][B][N] for qdg_sk_combine.  Shapes as
+ * qdg_q8_tile_mma (else QDG_ESHAPE).  wt, xq, xl 16-byte aligned, xs and out
+ * 4-byte.  Needs no workspace.
+ */
+int qdg_gemv_q8_mma_tiled(int mode, const uint8_t *wt, int64_t N, int64_t K, const int8_t *xq,
+                          const int8_t *xl, const float *xs, int64_t B, int splits, float *out,
+                          qdg_stream stream);
+
+/*
  * Tuning and test hooks.  Process-wide settings that choose among the library's
  * kernels, staging forms and launch shapes for the same call -- never the
  * arithmetic or its order, so every setting gives the same output bits -- for
@@ -548,7 +602,8 @@ enum {
   QDG_TUNE_FMT_WAVES = 14, /* 1..16 chunk waves a row group of the block-format GEMV; each   */
                            /*    wave sums every W-th non-empty chunk in turn               */
   QDG_TUNE_DQ_WAVES = 15,  /* 1..16 chunk waves a row group of the Dequant chunk-wave kernel */
-  QDG_TUNE_COUNT = 16
+  QDG_TUNE_MT_GROUPS = 16, /* 1 or 2 64-row record groups a workgroup of qdg_gemv_q8_mma_tiled */
+  QDG_TUNE_COUNT = 17
 };
 
 /* Sets knob to value (-1 restores the default).  QDG_EINVAL for an unknown knob. */

@@ -67,6 +67,10 @@ _SIGS = {
     "qdg_gemv_q8_fused": ([_I, _P, _P, _I64, _I64, _P, _I, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_q8_tile_rows": ([_P, _I64, _I64, _P, _P], _I),
     "qdg_gemv_q8_sk_tiled": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _I, _P, _P], _I),
+    "qdg_q8_tile_mma_bytes": ([_I64, _I64], _I64),
+    "qdg_q8_tile_mma": ([_P, _P, _I64, _I64, _P, _P], _I),
+    "qdg_gemv_q8_mma_tiled": ([_I, _P, _I64, _I64, _P, _P, _P, _I64, _I, _P, _P], _I),
+    "qdg_quantize_act_mma": ([_I, _P, _I64, _I64, _P, _P, _P, _P], _I),
     "qdg_gemv_argmax_workspace_bytes": ([_I64], ctypes.c_size_t),
     "qdg_gemv_q8_argmax": ([_I, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "qdg_argmax_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
@@ -120,7 +124,7 @@ def _check(fn: str, status: int) -> None:
 # launch shapes that give the same bits; -1 is the library's own choice.
 TUNE = {"sk_wsplit": 0, "ws_dma": 1, "ws_local": 2, "ws_rows": 3, "dq_seg": 4, "dq_rows": 5, "dq_x64": 6,
         "mfma_general": 7, "mfma_shape": 8, "mfma_wide": 9, "gemv_order": 10, "gemv_rpw": 11,
-        "gemv_unroll": 12, "reject_launch": 13, "fmt_waves": 14, "dq_waves": 15}
+        "gemv_unroll": 12, "reject_launch": 13, "fmt_waves": 14, "dq_waves": 15, "mt_groups": 16}
 
 
 def set_tuning(knob: str, value: int) -> None:
@@ -456,6 +460,46 @@ def gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> None:
         _ptr(xs, _f32(), "xs"), int(splits), _ptr(y, _f32(), "y"), _stream()))
 
 
+def _u8():
+    torch = _torch()
+    return (torch.uint8, torch.int8)
+
+
+def q8_tile_mma_bytes(N: int, K: int) -> int:
+    """Bytes of the MFMA-tiled form of an ``[N][K]`` Q8_0 matrix (0: shape not served)."""
+    return int(_lib.qdg_q8_tile_mma_bytes(N, K))
+
+
+def q8_tile_mma(wq, ws, wt) -> None:
+    """The weights ``wq [N][K]`` and scales ``ws [N][K/32]`` as MFMA-tiled records, into the byte array ``wt``."""
+    N, K = wq.shape
+    _gemv_sizes(1, wq.shape, ws, 1)
+    _need(wt=(wt, q8_tile_mma_bytes(N, K) // wt.element_size()))
+    _check("qdg_q8_tile_mma", _lib.qdg_q8_tile_mma(
+        _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(wt, _u8(), "wt"), _stream()))
+
+
+def quantize_act_mma(mode: int, x, xq, xl, xs) -> None:
+    """``x [B][K]`` (B <= 16) quantized as ``quantize_act`` does, written in the MFMA order
+    ``gemv_q8_mma_tiled`` reads: ``xq``, ``xl`` hold 16*K int8, ``xs`` 16*K/32 float32."""
+    B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)))
+    _check("qdg_quantize_act_mma", _lib.qdg_quantize_act_mma(
+        mode, _ptr(x, _f32(), "x"), B, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
+        _stream()))
+
+
+def gemv_q8_mma_tiled(mode: int, wt, N: int, K: int, out, xq, xl, xs, B: int, splits: int = 1) -> None:
+    """``gemv_q8`` for B <= 16 activation rows over MFMA-tiled weights ``wt`` (from ``q8_tile_mma``) and
+    MFMA-ordered activations (from ``quantize_act_mma``): ``out = Y [B][N]`` (``splits == 1``) or the
+    partials ``[splits][B][N]``."""
+    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)), out=(out, int(splits) * B * N))
+    _need(wt=(wt, q8_tile_mma_bytes(N, K) // wt.element_size()))
+    _check("qdg_gemv_q8_mma_tiled", _lib.qdg_gemv_q8_mma_tiled(
+        mode, _ptr(wt, _u8(), "wt"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
+        B, int(splits), _ptr(out, _f32(), "out"), _stream()))
+
+
 def gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> None:
     """One launch for a batch-1 projection: quantize ``x [1][K]`` (f32), split-K GEMV and ascending
     combine into ``y [1][N]`` (``workspace`` from ``sk_workspace(N, splits)``; may be None when S == 1)."""
@@ -637,6 +681,14 @@ def bind_gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> Boun
     return Bound("qdg_gemv_q8_sk_tiled", mode, wt, ws, N, K, xq, xl, xs, int(splits), y, _stream())
 
 
+def bind_gemv_q8_mma_tiled(mode: int, wt, N: int, K: int, out, xq, xl, xs, B: int, splits: int = 1) -> Bound:
+    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)), out=(out, int(splits) * B * N))
+    _need(wt=(wt, q8_tile_mma_bytes(N, K) // wt.element_size()))
+    for t, n in ((wt, "wt"), (out, "out"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    return Bound("qdg_gemv_q8_mma_tiled", mode, wt, N, K, xq, xl, xs, B, int(splits), out, _stream())
+
+
 def bind_gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> Bound:
     N, K = wq.shape
     _gemv_sizes(mode, wq.shape, ws, 1, x, y=(y, N))
@@ -651,6 +703,14 @@ def bind_stream_read(buf, nbytes: int, sink) -> Bound:
     _ptr(buf, None, "buf")
     _ptr(sink, None, "sink")
     return Bound("qdg_stream_read", buf, int(nbytes), sink, _stream())
+
+
+def bind_quantize_act_mma(mode: int, x, xq, xl, xs) -> Bound:
+    B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
+    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)))
+    for t, n in ((x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
+        _ptr(t, None, n)
+    return Bound("qdg_quantize_act_mma", mode, x, B, K, xq, xl, xs, _stream())
 
 
 def bind_quantize_act(mode: int, x, xq, xl, xs) -> Bound:

@@ -16,8 +16,8 @@ thread_local int g_last_hip_error = 0;
 thread_local qdg::LaunchTiming g_timing = {nullptr, nullptr};
 
 // qdg_set_tuning's knobs (-1: the library's own choice)
-std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-static_assert(QDG_TUNE_COUNT == 16, "one initializer a knob");
+std::atomic<int> g_tune[QDG_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+static_assert(QDG_TUNE_COUNT == 17, "one initializer a knob");
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -176,6 +176,52 @@ int qdg_gemv_q8_sk_tiled(int mode, const int8_t* wt, const uint16_t* ws, int64_t
       !aligned(y, 4))
     return QDG_EALIGN;
   return hip_status(qdg::launch_gemv_wsplit(mode, wt, ws, N, K, xq, xl, xs, splits, y, as_stream(stream), true));
+}
+
+// MFMA-tiled weights: K a multiple of 256, the record grid within a 1-D launch
+static bool mma_tiled_shape(int64_t N, int64_t K) {
+  if (!shape_ok(N, K) || K < 256 || K % 256 || K >= ((int64_t)1 << 30)) return false;
+  return (N + 63) / 64 * (K / 256) * 4 < ((int64_t)1 << 31);
+}
+
+int64_t qdg_q8_tile_mma_bytes(int64_t N, int64_t K) {
+  return mma_tiled_shape(N, K) ? qdg::tile_mma_bytes(N, K) : 0;
+}
+
+int qdg_q8_tile_mma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, uint8_t* wt, qdg_stream stream) {
+  if (!wq || !ws || !wt) return QDG_EINVAL;
+  if (!mma_tiled_shape(N, K)) return QDG_ESHAPE;
+  if (!aligned(wq, 16) || !aligned(ws, 2) || !aligned(wt, 16)) return QDG_EALIGN;
+  const uintptr_t t0 = (uintptr_t)wt, t1 = t0 + (uintptr_t)qdg::tile_mma_bytes(N, K);
+  const uintptr_t q0 = (uintptr_t)wq, q1 = q0 + (uintptr_t)(N * K);
+  const uintptr_t s0 = (uintptr_t)ws, s1 = s0 + (uintptr_t)(N * (K / qdg::QK)) * 2;
+  if ((q0 < t1 && t0 < q1) || (s0 < t1 && t0 < s1)) return QDG_EINVAL;
+  return hip_status(qdg::launch_tile_mma(wq, ws, N, K, wt, as_stream(stream)));
+}
+
+int qdg_quantize_act_mma(int mode, const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs,
+                         qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!x || !xq || !xs) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!mma_tiled_shape(1, K) || B < 1 || B > 16) return QDG_ESHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4)) return QDG_EALIGN;
+  return hip_status(qdg::launch_quantize_mma(mode, x, B, K, xq, xl, xs, as_stream(stream)));
+}
+
+int qdg_gemv_q8_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl,
+                          const float* xs, int64_t B, int splits, float* out, qdg_stream stream) {
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return mode == QDG_DEQUANT ? QDG_EMODE : QDG_EINVAL;
+  if (!wt || !xq || !xs || !out) return QDG_EINVAL;
+  if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
+  if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
+  if (!mma_tiled_shape(N, K)) return QDG_ESHAPE;
+  if (B < 1 || B > QDG_MAX_B || splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
+  if (B > 16) return QDG_EMODE;
+  if (!aligned(wt, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) || !aligned(out, 4))
+    return QDG_EALIGN;
+  return hip_status(qdg::launch_gemv_mma_tiled(mode, wt, N, K, xq, xl, xs, B, splits, out, as_stream(stream)));
 }
 
 int qdg_gemv_sk_combines_in_workgroup(int mode, int64_t K, int splits, int32_t* shape) {

@@ -584,6 +584,13 @@ hipError_t launch_gemv_wsplit_norm(int mode, const int8_t* wq, const uint16_t* w
                                    const float* r, float* s, const float* w, float eps, int qmode, float* yn,
                                    int8_t* hq, int8_t* hl, float* hs, void* workspace, hipStream_t st);
 hipError_t launch_tile_rows(const int8_t* wq, int64_t N, int64_t K, int8_t* wt, hipStream_t st);
+int64_t tile_mma_bytes(int64_t N, int64_t K);
+hipError_t launch_tile_mma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, uint8_t* wt, hipStream_t st);
+hipError_t launch_quantize_mma(int mode, const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs,
+                               hipStream_t st);
+hipError_t launch_gemv_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq,
+                                 const int8_t* xl, const float* xs, int64_t B, int splits, float* out,
+                                 hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);

@@ -1,0 +1,310 @@
+// qdg_mma_tiled.hip -- the batched (B <= 16) Q8_0 GEMV on int8 MFMA over weights
+// stored in the MFMA's own operand order (megakernel page: the GEMV's
+// tiled-weights option, where only the addresses of the weights change; lane
+// kernel library page: lk_gemv_mma, whose rows sum exactly as a single row).
+//
+// The sums are k_gemv_mfma_dma's, term for term: block g's exact int32 dots D
+// (and E) from v_mfma_i32_16x16x32_i8, the step p <- fma(a, b, p) of
+// lk_q8_term into partial g mod 4 in ascending block order, then
+// (P0 + P2) + (P1 + P3).  So every row equals qdg_gemv_q8's, bit for bit, for the
+// same splits, whatever the batch.
+//
+// Layout.  A record holds what one wave consumes in one step: for a group of 64
+// weight rows q (four 16-row tiles m), an 8-block step s and a residue r (the
+// blocks 8s + r and 8s + r + 4, which feed partial r), 4096 weight bytes and 256
+// scale bytes:
+//  * weight byte 1024*m + 16*l + 8*h + j (lane l, column c = l % 16, group
+//    u = l / 16) is byte 8*u + j of block 8s + r + 4h of row 64q + 16m + c -- so
+//    a lane's 16 bytes are exactly its B operands of the step's two MFMAs;
+//  * scale halfword 4096/2 + 8*c + 2*m + h is the binary16 scale of that row and
+//    block.
+// Records run (q, s, r) in row-major order; rows past N are zero.  A wave's
+// weight load is one contiguous KiB, its scale load 256 bytes.
+//
+// The activations come in the same order (qdg_quantize_act_mma): for step s and
+// residue r, lane l's 16 bytes are the A operands of the two blocks (activation
+// row t = l % 16, 8 bytes from 8 * (l / 16) of blocks 8s + r and 8s + r + 4), and
+// 32 scales follow the same (s, r) order, [h][t].  Sixteen rows always; the
+// quantizer writes rows past the batch as the words of a zero row.
+//
+// Kernel.  A workgroup of 4 * (4 / TPW) waves owns one 64-row group and one chunk
+// of K; wave (g, r) takes tiles TPW*g .. TPW*g + TPW - 1 of the group for
+// residue r and walks the chunk's steps reading records (q, s, r) and the
+// activation records (s, r) straight into registers -- no LDS tile, no
+// workgroup barrier until the end -- with P - 1 steps in flight (named step
+// buffers; every step issues the same loads, so the compiler's wait counts stay
+// exact).  Each load is a contiguous run: 1 KiB a tile, 1 KiB of activation
+// words, 128 bytes of activation scales.  A lane loads one activation scale and
+// the scales of its four batch rows reach it by ds_bpermute.  The partial waves
+// meet in LDS at the end.
+
+#include "qdg_device.h"
+
+namespace qdg {
+namespace {
+
+constexpr int MT_ROWS = 64;               // weight rows of a record group
+constexpr int MT_WBYTES = 4096;           // weight bytes of a record
+constexpr int MT_REC = MT_WBYTES + 256;   // record bytes (weights, then scales)
+constexpr int MT_STEP = 8;                // blocks a step
+
+__global__ __launch_bounds__(256) void k_tile_mma(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
+                                                  int64_t N, int64_t K, uint8_t* __restrict__ wt) {
+  const int64_t rec = blockIdx.x, nst = K / 256, nb = K / QK;
+  const int r = (int)(rec & 3);
+  const int64_t qs = rec >> 2, s = qs % nst, q = qs / nst;
+  const int tid = threadIdx.x, m = tid >> 6, l = tid & 63, c = l & 15, u = l >> 4;
+  const int64_t row = q * MT_ROWS + 16 * m + c, b0 = s * MT_STEP + r;
+  int2 lo = make_int2(0, 0), hi = make_int2(0, 0);
+  if (row < N) {
+    lo = *(const int2*)(wq + row * K + b0 * QK + 8 * u);
+    hi = *(const int2*)(wq + row * K + (b0 + 4) * QK + 8 * u);
+  }
+  uint8_t* dst = wt + rec * MT_REC;
+  *(int4*)(dst + 16 * tid) = make_int4(lo.x, lo.y, hi.x, hi.y);
+  if (tid < 16) {
+    unsigned w[4];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int64_t rw = q * MT_ROWS + 16 * mm + tid;
+      const unsigned a = rw < N ? ws[rw * nb + b0] : 0u, b = rw < N ? ws[rw * nb + b0 + 4] : 0u;
+      w[mm] = a | (b << 16);
+    }
+    *(int4*)(dst + MT_WBYTES + 16 * tid) = make_int4((int)w[0], (int)w[1], (int)w[2], (int)w[3]);
+  }
+}
+
+// The activation quantizer of qdg_quantize_act (quant_lane4: eight lanes a
+// 32-value block, four values a lane), writing the words and scales in the
+// MFMA order above.  Rows B..15 quantize a zero row.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_quantize_mma(const float* __restrict__ x, int B, int64_t K,
+                                                      int8_t* __restrict__ xq, int8_t* __restrict__ xl,
+                                                      float* __restrict__ xs) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nb = K / QK, blk = gid >> 3;  // blk over [16][nb]
+  const int sub = (int)(gid & 7);
+  const bool on = blk < 16 * nb;
+  const int t = (int)(blk / nb);
+  const int64_t b = blk - (int64_t)t * nb;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (on && t < B) v = *(const float4*)(x + (int64_t)t * K + b * QK + 4 * sub);
+  int h, l;
+  const float sc = quant_lane4<MODE>(v, &h, &l);
+  if (!on) return;
+  const int64_t rs = (b >> 3) * 4 + (b & 3);  // record (s, r)
+  const int hh = (int)((b >> 2) & 1);
+  const int64_t off = (rs * 64 + 16 * (sub >> 1) + t) * 16 + 8 * hh + 4 * (sub & 1);
+  *(int*)(xq + off) = h;
+  if constexpr (MODE == 2) *(int*)(xl + off) = l;
+  if (sub == 0) xs[rs * 32 + 16 * hh + t] = sc;
+}
+
+__device__ __forceinline__ v4i mma16x16x32(long a, long b) {
+  const v4i z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, z, 0, 0, 0);
+}
+
+// One step's operands of a lane.
+template <int MODE, int TPW>
+struct MtStep {
+  v4i w[TPW];  // the B operands of blocks 8s + r (.x, .y) and 8s + r + 4 (.z, .w), a tile each
+  v4i sc;      // the scales of column c's four rows: word m = block 8s + r (low), 8s + r + 4 (high)
+  v4i a;       // A operands (activation row t = c) of the two blocks
+  v4i al;      // TwoPass low words
+  float sx;    // the scale of activation row t = l % 16, block 8s + r + 4 * ((l / 16) & 1)
+};
+
+template <int MODE, int TPW>
+__device__ __forceinline__ void mt_load(MtStep<MODE, TPW>& b, const uint8_t* rec, int m0, const int8_t* xa,
+                                        const int8_t* xla, const float* xsa) {
+  __builtin_amdgcn_sched_barrier(0);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+    b.w[m] = __builtin_nontemporal_load((const v4i*)(rec + 1024 * (m0 + m) + 16 * lane));
+  b.sc = *(const v4i*)(rec + MT_WBYTES + 16 * (lane & 15));
+  b.a = *(const v4i*)(xa + 16 * lane);
+  if constexpr (MODE == 2) b.al = *(const v4i*)(xla + 16 * lane);
+  b.sx = xsa[lane & 31];
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE, int TPW>
+__device__ __forceinline__ void mt_terms(const MtStep<MODE, TPW>& b, int m0, float (&p)[TPW][4]) {
+  const int lane = threadIdx.x & 63, u = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float sig[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sig[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * h + 4 * u + i), __float_as_int(b.sx)));
+    const long ak = h == 0 ? (long)(((unsigned long)(unsigned)b.a[1] << 32) | (unsigned)b.a[0])
+                           : (long)(((unsigned long)(unsigned)b.a[3] << 32) | (unsigned)b.a[2]);
+    long lk = 0;
+    if constexpr (MODE == 2)
+      lk = h == 0 ? (long)(((unsigned long)(unsigned)b.al[1] << 32) | (unsigned)b.al[0])
+                  : (long)(((unsigned long)(unsigned)b.al[3] << 32) | (unsigned)b.al[2]);
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const long wk = h == 0 ? (long)(((unsigned long)(unsigned)b.w[m][1] << 32) | (unsigned)b.w[m][0])
+                             : (long)(((unsigned long)(unsigned)b.w[m][3] << 32) | (unsigned)b.w[m][2]);
+      const v4i D = mma16x16x32(ak, wk);
+      v4i E = {0, 0, 0, 0};
+      if constexpr (MODE == 2) E = mma16x16x32(lk, wk);
+      const unsigned sw = (unsigned)b.sc[m0 + m];
+      const float sgm = half_bits_to_float((unsigned short)(h == 0 ? (sw & 0xffffu) : (sw >> 16)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float ta, tb;
+        q8_term<MODE>(sgm, sig[i], D[i], E[i], ta, tb);
+        p[m][i] = __fmaf_rn(ta, tb, p[m][i]);
+      }
+    }
+  }
+}
+
+// Grid (workgroup row blocks of 64*GW rows, splits), 4 * (4*GW / TPW) waves a
+// workgroup.  out [splits][B][N].
+template <int MODE, int TPW, int P, int GW>
+__global__ __launch_bounds__(256 * (4 * GW / TPW)) void k_gemv_mma_tiled(const uint8_t* __restrict__ wt,
+                                                                    const int8_t* __restrict__ xq,
+                                                                    const int8_t* __restrict__ xl,
+                                                                    const float* __restrict__ xs, int64_t N, int64_t K,
+                                                                    int B, int S, float* __restrict__ out) {
+  constexpr int G = 4 * GW / TPW;      // tile groups a workgroup
+  __shared__ float red[4 * G][TPW][4][64];  // [wave][tile][i][lane]
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = wave & 3, g = wave >> 2, m0 = (TPW * g) & 3;  // tile m0.. of record group q
+  const int c = lane & 15, u = lane >> 4;
+  const int s_idx = blockIdx.y;
+  int32_t g0, g1;
+  split_range(K, S, s_idx, g0, g1);
+  const int64_t nst = K / 256;
+  const int64_t q = (int64_t)blockIdx.x * GW + (TPW * g) / 4;  // this wave's record group
+  // K is a multiple of 256: chunks are whole steps; a record group past the
+  // matrix (the last workgroup's, when GW > 1) loads nothing
+  const int nsteps = q < (N + MT_ROWS - 1) / MT_ROWS ? (g1 - g0) / MT_STEP : 0;
+  const int gs0 = g0 / MT_STEP;
+  // record (q, gs0 + st, r) and activation record (gs0 + st, r)
+  const uint8_t* rec0 = wt + ((q * nst + gs0) * 4 + r) * (int64_t)MT_REC;
+  const int8_t* xa0 = xq + ((int64_t)gs0 * 4 + r) * 1024;
+  const int8_t* xla0 = MODE == 2 ? xl + ((int64_t)gs0 * 4 + r) * 1024 : nullptr;
+  const float* xsa0 = xs + ((int64_t)gs0 * 4 + r) * 32;
+
+  float p[TPW][4];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+
+  if (nsteps > 0) {
+    auto load = [&](MtStep<MODE, TPW>& b, int st) {
+      const int64_t k = st < nsteps ? st : nsteps - 1;  // past the chunk: its last step again
+      mt_load<MODE, TPW>(b, rec0 + k * 4 * MT_REC, m0, xa0 + k * 4096, MODE == 2 ? xla0 + k * 4096 : nullptr,
+                         xsa0 + k * 128);
+    };
+    MtStep<MODE, TPW> b[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) load(b[k], k);
+    int st = 0;
+    // while every refill is due
+    for (; st + 2 * P - 1 < nsteps; st += P) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        mt_terms<MODE, TPW>(b[k], m0, p);
+        load(b[k], st + k + P);
+      }
+    }
+    // the last 1 .. 2P - 1 steps, in order
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if (st + k < nsteps) mt_terms<MODE, TPW>(b[k], m0, p);
+      if (st + k + P < nsteps) load(b[k], st + k + P);
+    }
+#pragma unroll
+    for (int k = 0; k + 1 < P; ++k)
+      if (st + P + k < nsteps) mt_terms<MODE, TPW>(b[k], m0, p);
+  }
+
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = p[m][i];
+  __syncthreads();
+  // wave (g, 0) writes its tiles: lane (c, u) holds row 64q + 16(m0 + m) + c, batch rows 4u + i
+  if (r == 0) {
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int64_t o = q * MT_ROWS + 16 * (m0 + m) + c;  // rows past the last record group: o >= N
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * u + i;
+        const float y = __fadd_rn(__fadd_rn(red[4 * g][m][i][lane], red[4 * g + 2][m][i][lane]),
+                                  __fadd_rn(red[4 * g + 1][m][i][lane], red[4 * g + 3][m][i][lane]));
+        if (t < B && o < N) out[((int64_t)s_idx * B + t) * N + o] = y;
+      }
+    }
+  }
+}
+
+// Steps in flight: P - 1 ahead of the one being summed (P = 4 measured best
+// against 3 and 5 on 25600x5120, B = 16).
+constexpr int MT_P = 4;
+
+// Record groups a workgroup.  Two (eight waves, 128 rows) when the launch still
+// spreads over most of the machine: the two waves of a residue read the same
+// activation record, which the second finds in L1, so a compute unit moves half
+// the activation bytes per weight byte -- 23.0 against 25.2 us (Int8Act) and
+// 26.7 against 28.4 us (TwoPass) on 25600x5120, B = 16, though 56 compute units
+// then stay idle.  QDG_TUNE_MT_GROUPS overrides.
+int mt_groups(int64_t N, int splits) {
+  const int f = tune(QDG_TUNE_MT_GROUPS);
+  if (f == 1 || f == 2) return f;
+  return (N + 127) / 128 * splits >= 192 ? 2 : 1;
+}
+
+template <int MODE, int GW>
+hipError_t launch_mt(const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
+                     int64_t B, int splits, float* out, hipStream_t st) {
+  const dim3 grid((unsigned)((N + GW * MT_ROWS - 1) / (GW * MT_ROWS)), (unsigned)splits), block(256 * GW);
+  return launch((k_gemv_mma_tiled<MODE, 4, MT_P, GW>), grid, block, 0, st, wt, xq, xl, xs, N, K, (int)B, splits,
+                out);
+}
+
+template <int MODE>
+hipError_t launch_qm(const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs, hipStream_t st) {
+  const int64_t threads = 16 * (K / QK) * 8;
+  return launch(k_quantize_mma<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, (int)B, K, xq,
+                xl, xs);
+}
+
+}  // namespace
+
+int64_t tile_mma_bytes(int64_t N, int64_t K) {
+  return (N + MT_ROWS - 1) / MT_ROWS * (K / 256) * 4 * (int64_t)MT_REC;
+}
+
+hipError_t launch_tile_mma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, uint8_t* wt, hipStream_t st) {
+  const int64_t recs = (N + MT_ROWS - 1) / MT_ROWS * (K / 256) * 4;
+  return launch(k_tile_mma, dim3((unsigned)recs), dim3(256), 0, st, wq, ws, N, K, wt);
+}
+
+hipError_t launch_quantize_mma(int mode, const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs,
+                               hipStream_t st) {
+  if (mode == 1) return launch_qm<1>(x, B, K, xq, xl, xs, st);
+  return launch_qm<2>(x, B, K, xq, xl, xs, st);
+}
+
+hipError_t launch_gemv_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq,
+                                 const int8_t* xl, const float* xs, int64_t B, int splits, float* out,
+                                 hipStream_t st) {
+  const int gw = mt_groups(N, splits);
+  if (mode == 1)
+    return gw == 2 ? launch_mt<1, 2>(wt, N, K, xq, xl, xs, B, splits, out, st)
+                   : launch_mt<1, 1>(wt, N, K, xq, xl, xs, B, splits, out, st);
+  return gw == 2 ? launch_mt<2, 2>(wt, N, K, xq, xl, xs, B, splits, out, st)
+                 : launch_mt<2, 1>(wt, N, K, xq, xl, xs, B, splits, out, st);
+}
+
+}  // namespace qdg

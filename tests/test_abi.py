@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 37
+    assert len(names) == 41
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -482,11 +482,11 @@ def test_tuning_knobs():
     """The tuning hooks start at the library's own choice (-1), never read the
     environment, reject unknown knobs, and the binding's context manager puts
     every knob back."""
-    for k in range(16):
+    for k in range(17):
         assert lib.qdg_get_tuning(k) == -1, k
-    assert lib.qdg_get_tuning(16) == EINVAL
+    assert lib.qdg_get_tuning(17) == EINVAL
     assert lib.qdg_get_tuning(-1) == EINVAL
-    assert lib.qdg_set_tuning(16, 0) == EINVAL
+    assert lib.qdg_set_tuning(17, 0) == EINVAL
     assert lib.qdg_set_tuning(2, 1) == OK and lib.qdg_get_tuning(2) == 1
     assert lib.qdg_set_tuning(2, -7) == OK and lib.qdg_get_tuning(2) == -1
     with q.tuning(ws_dma=0, ws_local=1):
@@ -495,7 +495,7 @@ def test_tuning_knobs():
             assert q.get_tuning("ws_local") == 0
         assert q.get_tuning("ws_local") == 1
     assert q.get_tuning("ws_dma") == -1 and q.get_tuning("ws_local") == -1
-    assert sorted(q.TUNE.values()) == list(range(16))
+    assert sorted(q.TUNE.values()) == list(range(17))
     assert lib.qdg_time_next_launch(None, None) == OK
 
 
@@ -509,7 +509,7 @@ def test_knobs_ignore_the_environment():
     env = dict(os.environ, QDG_WS_ROWS="1", QDG_SK_WSPLIT="0", QDG_WS_DMA="0", QDG_MFMA_GENERAL="1")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300, env=env)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.strip() == str([-1] * 16) + " (12, 15)", r.stdout
+    assert r.stdout.strip() == str([-1] * 17) + " (12, 15)", r.stdout
 
 
 def test_binding_checks_sizes_before_the_call():
@@ -539,3 +539,47 @@ def test_binding_checks_sizes_before_the_call():
     for i, c in enumerate(cases):
         with pytest.raises(ValueError, match="holds|ws must"):
             c()
+
+
+def test_mma_tiled_validation():
+    """The MFMA-tiled batched path: sizes, modes, shapes, alignment and overlap are
+    rejected on the host with the documented status."""
+    nbytes = lib.qdg_q8_tile_mma_bytes
+    nbytes.restype = ctypes.c_int64
+    nbytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert nbytes(64, 256) == 4 * 4352
+    assert nbytes(65, 512) == 2 * 2 * 4 * 4352
+    assert nbytes(25600, 5120) == 400 * 20 * 4 * 4352
+    for N, K in ((64, 32), (64, 288), (0, 256), (64, 0), (1, 1 << 30)):
+        assert nbytes(N, K) == 0, (N, K)
+
+    def tile(wq=A, ws=A, N=64, K=512, wt=A + (1 << 30)):
+        return lib.qdg_q8_tile_mma(P(wq), P(ws), N, K, P(wt), None)
+
+    assert tile(wq=None) == EINVAL and tile(ws=None) == EINVAL and tile(wt=None) == EINVAL
+    assert tile(K=288) == ESHAPE and tile(N=0) == ESHAPE and tile(K=32) == ESHAPE
+    assert tile(wq=A + 8) == EALIGN and tile(ws=A + 1) == EALIGN and tile(wt=A + (1 << 30) + 8) == EALIGN
+    assert tile(wt=A) == EINVAL                      # overlaps wq
+    assert tile(ws=A + (1 << 30) + 4096) == EINVAL   # ws inside wt
+
+    def quant(mode=1, x=A, B=4, K=512, xq=A, xl=None, xs=A):
+        return lib.qdg_quantize_act_mma(mode, P(x), B, K, P(xq), P(xl), P(xs), None)
+
+    assert quant(mode=0) == EINVAL and quant(mode=3) == EINVAL
+    assert quant(x=None) == EINVAL and quant(xq=None) == EINVAL and quant(xs=None) == EINVAL
+    assert quant(mode=2) == EINVAL                   # TwoPass needs xl
+    assert quant(xl=A) == EINVAL                     # Int8Act takes no xl
+    assert quant(B=0) == ESHAPE and quant(B=17) == ESHAPE and quant(K=288) == ESHAPE
+    assert quant(x=A + 4) == EALIGN and quant(xq=A + 8) == EALIGN and quant(xs=A + 2) == EALIGN
+    assert quant(mode=2, xl=A + 8) == EALIGN
+
+    def mt(mode=1, wt=A, N=64, K=512, xq=A, xl=None, xs=A, B=4, S=1, out=A):
+        return lib.qdg_gemv_q8_mma_tiled(mode, P(wt), N, K, P(xq), P(xl), P(xs), B, S, P(out), None)
+
+    assert mt(mode=0) == EMODE                       # Dequant is not served
+    assert mt(mode=3) == EINVAL and mt(wt=None) == EINVAL and mt(out=None) == EINVAL
+    assert mt(mode=2) == EINVAL and mt(xl=A) == EINVAL
+    assert mt(K=288) == ESHAPE and mt(N=0) == ESHAPE and mt(B=0) == ESHAPE and mt(S=0) == ESHAPE
+    assert mt(S=65) == ESHAPE and mt(B=65) == ESHAPE
+    assert mt(B=17) == EMODE                         # up to 16 activation rows
+    assert mt(wt=A + 8) == EALIGN and mt(xq=A + 4) == EALIGN and mt(xs=A + 2) == EALIGN and mt(out=A + 1) == EALIGN

@@ -1,0 +1,199 @@
+"""GPU parity of the batched GEMV over MFMA-ordered operands: the weight records
+of qdg_q8_tile_mma and the activation records of qdg_quantize_act_mma, both
+checked byte for byte against the layout the header defines (restated here in
+numpy from that definition, not from the kernels), and qdg_gemv_q8_mma_tiled
+against the oracle bit for bit, equal to qdg_gemv_q8 over the plain operands,
+batch-invariant, in both workgroup shapes (one or two 64-row record groups)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_gemv_02_amd as q
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def dev(a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def records_weights(wq, ws):
+    """The weight records by the header's definition: record (q, s, r) holds, at
+    byte 1024*m + 16*l + 8*h + j, byte 8*(l//16) + j of block 8s + r + 4h of row
+    64q + 16m + l%16, then the 16-bit scales at word 2048 + 8*c + 2*m + h."""
+    N, K = wq.shape
+    G, S = -(-N // 64), K // 256
+    w = np.zeros((G * 64, K), np.int8)
+    w[:N] = wq
+    s = np.zeros((G * 64, K // 32), np.uint16)
+    s[:N] = ws
+    out = np.zeros((G, S, 4, 4352), np.uint8)
+    for qg in range(G):
+        for st in range(S):
+            for r in range(4):
+                rec = out[qg, st, r]
+                for m in range(4):
+                    for l in range(64):
+                        row, u = 64 * qg + 16 * m + l % 16, l // 16
+                        for h in range(2):
+                            b = 8 * st + r + 4 * h
+                            o = 1024 * m + 16 * l + 8 * h
+                            rec[o:o + 8] = w[row, 32 * b + 8 * u:32 * b + 8 * u + 8].view(np.uint8)
+                words = rec[4096:].view(np.uint16)
+                for c in range(16):
+                    for m in range(4):
+                        for h in range(2):
+                            words[8 * c + 2 * m + h] = s[64 * qg + 16 * m + c, 8 * st + r + 4 * h]
+    return out.reshape(-1)
+
+
+def records_acts(xq, xs, B, zero_scale):
+    """The activation records by the header's definition: record (s, r) holds, at
+    byte 16*l + 8*h + j, word 8*(l//16) + j of block 8s + r + 4h of row l%16, and
+    scale 16*h + t of that block and row t; rows past B are a zero row's."""
+    K = xq.shape[1]
+    full = np.zeros((16, K), np.int8)
+    full[:B] = xq
+    sc = np.full((16, K // 32), zero_scale, np.float32)
+    sc[:B] = xs
+    S = K // 256
+    words = np.zeros((S, 4, 1024), np.int8)
+    scales = np.zeros((S, 4, 32), np.float32)
+    for st in range(S):
+        for r in range(4):
+            for l in range(64):
+                t, u = l % 16, l // 16
+                for h in range(2):
+                    b = 8 * st + r + 4 * h
+                    words[st, r, 16 * l + 8 * h:16 * l + 8 * h + 8] = full[t, 32 * b + 8 * u:32 * b + 8 * u + 8]
+            for h in range(2):
+                for t in range(16):
+                    scales[st, r, 16 * h + t] = sc[t, 8 * st + r + 4 * h]
+    return words.reshape(-1), scales.reshape(-1)
+
+
+def zero_row_scale(mode):
+    # the quantizer's scale of an all-zero block: 1 (Int8Act), 1e-30/127 (TwoPass)
+    return np.float32(1.0) if mode == 1 else np.float32(np.float32(1e-30) / np.float32(127.0))
+
+
+def tile(wq, ws):
+    N, K = wq.shape
+    wt = torch.full((q.q8_tile_mma_bytes(N, K),), 0xA5, dtype=torch.uint8, device=DEV)
+    q.q8_tile_mma(dev(wq), dev(ws), wt)
+    return wt
+
+
+def acts(mode, x):
+    B, K = x.shape
+    xd = dev(x)
+    tq = torch.full((16 * K,), 77, dtype=torch.int8, device=DEV)
+    tl = torch.full((16 * K,), 77, dtype=torch.int8, device=DEV) if mode == 2 else None
+    ts = torch.full((16 * (K // 32),), float("nan"), dtype=torch.float32, device=DEV)
+    q.quantize_act_mma(mode, xd, tq, tl, ts)
+    return tq, tl, ts
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (100, 512), (5, 768), (130, 1536)])
+def test_tile_mma_layout(N, K):
+    announce(f"tile_mma N={N} K={K}")
+    wq, ws = workloads.weights(N, K, N + K, N + K + 1)
+    got = host(tile(wq, ws))
+    np.testing.assert_array_equal(got, records_weights(wq, ws))
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,K", [(16, 512), (1, 256), (5, 1280), (16, 2048)])
+def test_quantize_act_mma_layout(mode, B, K):
+    """The words and scales are the oracle quantizer's, in the MFMA order, with a
+    zero row's words and scale past the batch."""
+    announce(f"quantize_act_mma mode={mode} B={B} K={K}")
+    x = workloads.batch_activation(B, K, 40 + B + K, True, 41 + B + K)
+    x[0, :32] = 0.0  # a zero block inside the batch
+    oq, ol, os_ = oracle.quantize(mode, x)
+    tq, tl, ts = acts(mode, x)
+    wq_, ws_ = records_acts(oq, os_, B, zero_row_scale(mode))
+    np.testing.assert_array_equal(host(tq), wq_)
+    np.testing.assert_array_equal(host(ts).view(np.int32), ws_.view(np.int32))
+    if mode == 2:
+        wl_, _ = records_acts(ol, os_, B, zero_row_scale(mode))
+        np.testing.assert_array_equal(host(tl), wl_)
+
+
+CASES = [(16, 256, 5120, 1), (2, 33, 512, 1), (5, 100, 1536, 2), (16, 130, 768, 3), (11, 64, 25600, 4),
+         (1, 77, 256, 1), (16, 200, 5120, 3), (7, 192, 1024, 1),
+         (3, 40, 256, 2), (16, 64, 256, 4)]  # the last two: empty chunks
+
+
+@pytest.mark.parametrize("groups", [1, 2])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,N,K,S", CASES)
+def test_mma_tiled_bit_exact(B, N, K, S, mode, groups, tune):
+    """Against the oracle bit for bit (y, or the chunk partials for S > 1), equal
+    to qdg_gemv_q8 over the plain operands, and row t alone gives row t's bits."""
+    announce(f"gemv_q8_mma_tiled mode={mode} B={B} N={N} K={K} S={S} groups={groups}")
+    tune(mt_groups=groups)
+    wq, ws, x = (*workloads.weights(N, K, 3 * N + K, 3 * N + K + 1),
+                 workloads.batch_activation(B, K, 5 * B + K, True, 6 * B + K))
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = (oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=THREADS) if S == 1
+            else oracle.gemv_split(mode, wq, ws, oq, ol, os_, S, nthreads=THREADS))
+    wt = tile(wq, ws)
+    tq, tl, ts = acts(mode, x)
+    out = torch.full((S, B, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wt, N, K, out, tq, tl, ts, B, splits=S)
+    got = host(out)
+    np.testing.assert_array_equal(got[0] if S == 1 else got, want)
+    # the plain batched path on the plain operands gives the same bits
+    xd = dev(x)
+    pq = torch.empty((B, K), dtype=torch.int8, device=DEV)
+    pl = torch.empty((B, K), dtype=torch.int8, device=DEV) if mode == 2 else None
+    ps = torch.empty((B, K // 32), dtype=torch.float32, device=DEV)
+    q.quantize_act(mode, xd, pq, pl, ps)
+    plain = torch.full((S, B, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8(mode, dev(wq), dev(ws), plain, xq=pq, xl=pl, xs=ps, splits=S)
+    assert host(plain).tobytes() == got.tobytes()
+    for t in sorted({0, B - 1}):
+        tq1, tl1, ts1 = acts(mode, x[t:t + 1])
+        one = torch.full((S, 1, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_mma_tiled(mode, wt, N, K, one, tq1, tl1, ts1, 1, splits=S)
+        assert host(one)[:, 0].tobytes() == got[:, t].tobytes(), t
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_mma_tiled_decode_b16_full(mode):
+    """The 16-row batch against 25600x5120 in the benchmark's launch: every output
+    against the oracle, and a repeat gives the same bytes."""
+    announce(f"gemv_q8_mma_tiled B=16 25600x5120 mode {mode}")
+    d = workloads.make(4, 0)
+    wq, ws, x = d["wq"], d["ws"], d["x"]
+    B, K = x.shape
+    N = wq.shape[0]
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=THREADS)
+    wt = tile(wq, ws)
+    tq, tl, ts = acts(mode, x)
+    outs = []
+    for _ in range(2):
+        y = torch.full((B, N), float("nan"), dtype=torch.float32, device=DEV)
+        q.gemv_q8_mma_tiled(mode, wt, N, K, y, tq, tl, ts, B)
+        outs.append(host(y))
+    np.testing.assert_array_equal(outs[0], want)
+    assert outs[0].tobytes() == outs[1].tobytes()
