@@ -48,29 +48,34 @@ constexpr int MT_WBYTES = 4096;           // weight bytes of a record
 constexpr int MT_REC = MT_WBYTES + 256;   // record bytes (weights, then scales)
 constexpr int MT_STEP = 8;                // blocks a step
 
+// One workgroup a (row group, step): its four records, one residue after the
+// other, so the step's 256-byte row segments are fetched once and re-read from
+// the cache for the later residues.
 __global__ __launch_bounds__(256) void k_tile_mma(const int8_t* __restrict__ wq, const uint16_t* __restrict__ ws,
                                                   int64_t N, int64_t K, uint8_t* __restrict__ wt) {
-  const int64_t rec = blockIdx.x, nst = K / 256, nb = K / QK;
-  const int r = (int)(rec & 3);
-  const int64_t qs = rec >> 2, s = qs % nst, q = qs / nst;
+  const int64_t qs = blockIdx.x, nst = K / 256, nb = K / QK;  // qs = q * nst + s
+  const int64_t s = qs % nst, q = qs / nst;
   const int tid = threadIdx.x, m = tid >> 6, l = tid & 63, c = l & 15, u = l >> 4;
-  const int64_t row = q * MT_ROWS + 16 * m + c, b0 = s * MT_STEP + r;
-  int2 lo = make_int2(0, 0), hi = make_int2(0, 0);
-  if (row < N) {
-    lo = *(const int2*)(wq + row * K + b0 * QK + 8 * u);
-    hi = *(const int2*)(wq + row * K + (b0 + 4) * QK + 8 * u);
-  }
-  uint8_t* dst = wt + rec * MT_REC;
-  *(int4*)(dst + 16 * tid) = make_int4(lo.x, lo.y, hi.x, hi.y);
-  if (tid < 16) {
-    unsigned w[4];
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const int64_t rw = q * MT_ROWS + 16 * mm + tid;
-      const unsigned a = rw < N ? ws[rw * nb + b0] : 0u, b = rw < N ? ws[rw * nb + b0 + 4] : 0u;
-      w[mm] = a | (b << 16);
+  const int64_t row = q * MT_ROWS + 16 * m + c;
+  for (int r = 0; r < 4; ++r) {
+    const int64_t b0 = s * MT_STEP + r;
+    int2 lo = make_int2(0, 0), hi = make_int2(0, 0);
+    if (row < N) {
+      lo = *(const int2*)(wq + row * K + b0 * QK + 8 * u);
+      hi = *(const int2*)(wq + row * K + (b0 + 4) * QK + 8 * u);
     }
-    *(int4*)(dst + MT_WBYTES + 16 * tid) = make_int4((int)w[0], (int)w[1], (int)w[2], (int)w[3]);
+    uint8_t* dst = wt + (qs * 4 + r) * MT_REC;
+    *(int4*)(dst + 16 * tid) = make_int4(lo.x, lo.y, hi.x, hi.y);
+    if (tid < 16) {
+      unsigned w[4];
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const int64_t rw = q * MT_ROWS + 16 * mm + tid;
+        const unsigned a = rw < N ? ws[rw * nb + b0] : 0u, b = rw < N ? ws[rw * nb + b0 + 4] : 0u;
+        w[mm] = a | (b << 16);
+      }
+      *(int4*)(dst + MT_WBYTES + 16 * tid) = make_int4((int)w[0], (int)w[1], (int)w[2], (int)w[3]);
+    }
   }
 }
 
@@ -286,8 +291,8 @@ int64_t tile_mma_bytes(int64_t N, int64_t K) {
 }
 
 hipError_t launch_tile_mma(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, uint8_t* wt, hipStream_t st) {
-  const int64_t recs = (N + MT_ROWS - 1) / MT_ROWS * (K / 256) * 4;
-  return launch(k_tile_mma, dim3((unsigned)recs), dim3(256), 0, st, wq, ws, N, K, wt);
+  const int64_t steps = (N + MT_ROWS - 1) / MT_ROWS * (K / 256);  // a workgroup a (row group, step)
+  return launch(k_tile_mma, dim3((unsigned)steps), dim3(256), 0, st, wq, ws, N, K, wt);
 }
 
 hipError_t launch_quantize_mma(int mode, const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs,
