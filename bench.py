@@ -136,8 +136,9 @@ class DeviceTimer:
 
     def median_us(self, calls, launches: int, warm: int = 5) -> float:
         """Median device duration (µs) of the first kernel of ``calls[i % len(calls)]()`` over
-        ``launches`` launches after ``warm`` untimed ones."""
-        for i in range(warm):
+        ``launches`` launches after ``warm`` untimed ones -- and at least one untimed launch on
+        every rotated copy, so that no timed launch is a copy's first touch."""
+        for i in range(max(warm, len(calls))):
             calls[i % len(calls)]()
         self.torch.cuda.synchronize()
         n = min(launches, len(self.pairs))
@@ -149,8 +150,9 @@ class DeviceTimer:
 
     def wall_us(self, calls, launches: int, warm: int = 5) -> float:
         """Mean time a call takes in a back-to-back sequence: one event pair around ``launches``
-        calls (every kernel of the call, and the gaps between launches, counted)."""
-        for i in range(warm):
+        calls (every kernel of the call, and the gaps between launches, counted), after one untimed
+        launch on every rotated copy."""
+        for i in range(max(warm, len(calls))):
             calls[i % len(calls)]()
         e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
         self.torch.cuda.synchronize()
