@@ -540,32 +540,34 @@ int qdg_q8_tile_mma(const int8_t *wq, const uint16_t *ws, int64_t N, int64_t K, 
                     qdg_stream stream);
 
 /*
- * qdg_quantize_act for 1 <= B <= 16 rows, with the words and scales written in
- * the MFMA order that qdg_gemv_q8_mma_tiled reads: for step s (8 blocks) and
- * residue r in 0..3, record (s, r) holds 1024 word bytes, byte 16*l + 8*h + j
- * (lane l, t = l mod 16, u = l / 16) being word 8*u + j of block 8*s + r + 4*h of
- * row t, and 32 scales, scale 16*h + t of the record being that block's scale
- * of row t.  Records run (s, r) in row-major order: xq (and xl under
- * QDG_TWOPASS) hold 16*K bytes, xs 16*K/32 floats.  The words and scales of rows
- * t < B are qdg_quantize_act's on the same x, bit for bit; rows B..15 are those
- * of a zero row.  x [B][K] (16-byte aligned); xq, xl 16-byte aligned; xs
- * 4-byte.  K as qdg_q8_tile_mma (else QDG_ESHAPE).
+ * qdg_quantize_act for 1 <= B <= QDG_MAX_B rows, with the words and scales
+ * written in the MFMA order that qdg_gemv_q8_mma_tiled reads, in T activation
+ * tiles of 16 rows (T = 1, 2 or 4 for B <= 16, <= 32, <= 64; rows 16*a .. 16*a + 15
+ * form tile a).  Tile a holds, for step s (8 blocks) and residue r in 0..3, a
+ * record (s, r) of 1024 word bytes -- byte 16*l + 8*h + j (lane l, t = l mod 16,
+ * u = l / 16) being word 8*u + j of block 8*s + r + 4*h of row 16*a + t -- and 32
+ * scales, scale 16*h + t of the record being that block's scale of row 16*a + t.
+ * Records run (s, r) in row-major order within a tile, tiles one after the
+ * other: xq (and xl under QDG_TWOPASS) hold 16*T*K bytes, xs 16*T*K/32 floats.
+ * The words and scales of rows t < B are qdg_quantize_act's on the same x, bit
+ * for bit; rows B..16*T-1 are those of a zero row.  x [B][K] (16-byte aligned);
+ * xq, xl 16-byte aligned; xs 4-byte.  K as qdg_q8_tile_mma (else QDG_ESHAPE).
  */
 int qdg_quantize_act_mma(int mode, const float *x, int64_t B, int64_t K, int8_t *xq, int8_t *xl,
                          float *xs, qdg_stream stream);
 
 /*
- * qdg_gemv_q8 for 1 <= B <= 16 activation rows over MFMA-tiled weights wt (from
- * qdg_q8_tile_mma) and MFMA-ordered activations xq, xl, xs (from
- * qdg_quantize_act_mma): the same terms in the same order (the int8 MFMA's exact
- * block dots, partial g mod 4, (P0 + P2) + (P1 + P3)), so out is bit-identical
- * to qdg_gemv_q8 over the plain weights and the plain activations of the same x
- * with the same B and splits, and every row to its batch-1 result.
- * QDG_INT8ACT or QDG_TWOPASS (xl NULL for QDG_INT8ACT; QDG_DEQUANT gives
- * QDG_EMODE); B > 16 gives QDG_EMODE.  splits == 1: out is y [B][N];
- * splits > 1: partials [splits][B][N] for qdg_sk_combine.  Shapes as
- * qdg_q8_tile_mma (else QDG_ESHAPE).  wt, xq, xl 16-byte aligned, xs and out
- * 4-byte.  Needs no workspace.
+ * qdg_gemv_q8 for 1 <= B <= QDG_MAX_B activation rows over MFMA-tiled weights
+ * wt (from qdg_q8_tile_mma) and MFMA-ordered activations xq, xl, xs (from
+ * qdg_quantize_act_mma with the same B): the same terms in the same order (the
+ * int8 MFMA's exact block dots, partial g mod 4, (P0 + P2) + (P1 + P3)), so out
+ * is bit-identical to qdg_gemv_q8 over the plain weights and the plain
+ * activations of the same x with the same B and splits, and every row to its
+ * batch-1 result.  QDG_INT8ACT or QDG_TWOPASS (xl NULL for QDG_INT8ACT;
+ * QDG_DEQUANT gives QDG_EMODE).  splits == 1: out is y [B][N]; splits > 1:
+ * partials [splits][B][N] for qdg_sk_combine.  Shapes as qdg_q8_tile_mma (else
+ * QDG_ESHAPE).  wt, xq, xl 16-byte aligned, xs and out 4-byte.  Needs no
+ * workspace.
  */
 int qdg_gemv_q8_mma_tiled(int mode, const uint8_t *wt, int64_t N, int64_t K, const int8_t *xq,
                           const int8_t *xl, const float *xs, int64_t B, int splits, float *out,

@@ -479,11 +479,17 @@ def q8_tile_mma(wq, ws, wt) -> None:
         _ptr(wq, _i8(), "wq"), _ptr(ws, _scales(), "ws"), N, K, _ptr(wt, _u8(), "wt"), _stream()))
 
 
+def mma_act_rows(B: int) -> int:
+    """Rows of the MFMA-ordered activations for a batch of B: 16 activation-tile rows times 1, 2 or 4."""
+    return 16 if B <= 16 else 32 if B <= 32 else 64
+
+
 def quantize_act_mma(mode: int, x, xq, xl, xs) -> None:
-    """``x [B][K]`` (B <= 16) quantized as ``quantize_act`` does, written in the MFMA order
-    ``gemv_q8_mma_tiled`` reads: ``xq``, ``xl`` hold 16*K int8, ``xs`` 16*K/32 float32."""
+    """``x [B][K]`` quantized as ``quantize_act`` does, written in the MFMA order ``gemv_q8_mma_tiled``
+    reads: ``xq``, ``xl`` hold ``mma_act_rows(B)*K`` int8, ``xs`` ``mma_act_rows(B)*K/32`` float32."""
     B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
-    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)))
+    R = mma_act_rows(B)
+    _need(xq=(xq, R * K), xl=(xl, R * K), xs=(xs, R * (K // QK)))
     _check("qdg_quantize_act_mma", _lib.qdg_quantize_act_mma(
         mode, _ptr(x, _f32(), "x"), B, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
         _stream()))
@@ -493,7 +499,8 @@ def gemv_q8_mma_tiled(mode: int, wt, N: int, K: int, out, xq, xl, xs, B: int, sp
     """``gemv_q8`` for B <= 16 activation rows over MFMA-tiled weights ``wt`` (from ``q8_tile_mma``) and
     MFMA-ordered activations (from ``quantize_act_mma``): ``out = Y [B][N]`` (``splits == 1``) or the
     partials ``[splits][B][N]``."""
-    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)), out=(out, int(splits) * B * N))
+    R = mma_act_rows(B)
+    _need(xq=(xq, R * K), xl=(xl, R * K), xs=(xs, R * (K // QK)), out=(out, int(splits) * B * N))
     _need(wt=(wt, q8_tile_mma_bytes(N, K) // wt.element_size()))
     _check("qdg_gemv_q8_mma_tiled", _lib.qdg_gemv_q8_mma_tiled(
         mode, _ptr(wt, _u8(), "wt"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
@@ -682,7 +689,8 @@ def bind_gemv_q8_sk_tiled(mode: int, wt, ws, y, xq, xl, xs, splits: int) -> Boun
 
 
 def bind_gemv_q8_mma_tiled(mode: int, wt, N: int, K: int, out, xq, xl, xs, B: int, splits: int = 1) -> Bound:
-    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)), out=(out, int(splits) * B * N))
+    R = mma_act_rows(B)
+    _need(xq=(xq, R * K), xl=(xl, R * K), xs=(xs, R * (K // QK)), out=(out, int(splits) * B * N))
     _need(wt=(wt, q8_tile_mma_bytes(N, K) // wt.element_size()))
     for t, n in ((wt, "wt"), (out, "out"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
@@ -707,7 +715,8 @@ def bind_stream_read(buf, nbytes: int, sink) -> Bound:
 
 def bind_quantize_act_mma(mode: int, x, xq, xl, xs) -> Bound:
     B, K = x.shape if x.dim() == 2 else (1, x.shape[0])
-    _need(xq=(xq, 16 * K), xl=(xl, 16 * K), xs=(xs, 16 * (K // QK)))
+    R = mma_act_rows(B)
+    _need(xq=(xq, R * K), xl=(xl, R * K), xs=(xs, R * (K // QK)))
     for t, n in ((x, "x"), (xq, "xq"), (xl, "xl"), (xs, "xs")):
         _ptr(t, None, n)
     return Bound("qdg_quantize_act_mma", mode, x, B, K, xq, xl, xs, _stream())

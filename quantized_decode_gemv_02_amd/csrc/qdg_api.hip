@@ -205,7 +205,7 @@ int qdg_quantize_act_mma(int mode, const float* x, int64_t B, int64_t K, int8_t*
   if (!x || !xq || !xs) return QDG_EINVAL;
   if (mode == QDG_TWOPASS && !xl) return QDG_EINVAL;
   if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
-  if (!mma_tiled_shape(1, K) || B < 1 || B > 16) return QDG_ESHAPE;
+  if (!mma_tiled_shape(1, K) || B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
   if (!aligned(x, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4)) return QDG_EALIGN;
   return hip_status(qdg::launch_quantize_mma(mode, x, B, K, xq, xl, xs, as_stream(stream)));
 }
@@ -218,7 +218,6 @@ int qdg_gemv_q8_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, con
   if (mode == QDG_INT8ACT && xl) return QDG_EINVAL;
   if (!mma_tiled_shape(N, K)) return QDG_ESHAPE;
   if (B < 1 || B > QDG_MAX_B || splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;
-  if (B > 16) return QDG_EMODE;
   if (!aligned(wt, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) || !aligned(out, 4))
     return QDG_EALIGN;
   return hip_status(qdg::launch_gemv_mma_tiled(mode, wt, N, K, xq, xl, xs, B, splits, out, as_stream(stream)));

@@ -81,15 +81,16 @@ __global__ __launch_bounds__(256) void k_tile_mma(const int8_t* __restrict__ wq,
 
 // The activation quantizer of qdg_quantize_act (quant_lane4: eight lanes a
 // 32-value block, four values a lane), writing the words and scales in the
-// MFMA order above.  Rows B..15 quantize a zero row.
+// MFMA order above, AT tiles of 16 rows one after the other.  Rows B..16*AT-1
+// quantize a zero row.
 template <int MODE>
-__global__ __launch_bounds__(256) void k_quantize_mma(const float* __restrict__ x, int B, int64_t K,
+__global__ __launch_bounds__(256) void k_quantize_mma(const float* __restrict__ x, int B, int64_t K, int AT,
                                                       int8_t* __restrict__ xq, int8_t* __restrict__ xl,
                                                       float* __restrict__ xs) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nb = K / QK, blk = gid >> 3;  // blk over [16][nb]
+  const int64_t nb = K / QK, blk = gid >> 3;  // blk over [16*AT][nb]
   const int sub = (int)(gid & 7);
-  const bool on = blk < 16 * nb;
+  const bool on = blk < 16 * AT * nb;
   const int t = (int)(blk / nb);
   const int64_t b = blk - (int64_t)t * nb;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -97,12 +98,13 @@ __global__ __launch_bounds__(256) void k_quantize_mma(const float* __restrict__ 
   int h, l;
   const float sc = quant_lane4<MODE>(v, &h, &l);
   if (!on) return;
+  const int at = t >> 4, tt = t & 15;
   const int64_t rs = (b >> 3) * 4 + (b & 3);  // record (s, r)
   const int hh = (int)((b >> 2) & 1);
-  const int64_t off = (rs * 64 + 16 * (sub >> 1) + t) * 16 + 8 * hh + 4 * (sub & 1);
+  const int64_t off = at * 16 * K + (rs * 64 + 16 * (sub >> 1) + tt) * 16 + 8 * hh + 4 * (sub & 1);
   *(int*)(xq + off) = h;
   if constexpr (MODE == 2) *(int*)(xl + off) = l;
-  if (sub == 0) xs[rs * 32 + 16 * hh + t] = sc;
+  if (sub == 0) xs[at * (K / 2) + rs * 32 + 16 * hh + tt] = sc;
 }
 
 __device__ __forceinline__ v4i mma16x16x32(long a, long b) {
@@ -111,74 +113,85 @@ __device__ __forceinline__ v4i mma16x16x32(long a, long b) {
 }
 
 // One step's operands of a lane.
-template <int MODE, int TPW>
+template <int MODE, int TPW, int AT>
 struct MtStep {
-  v4i w[TPW];  // the B operands of blocks 8s + r (.x, .y) and 8s + r + 4 (.z, .w), a tile each
-  v4i sc;      // the scales of column c's four rows: word m = block 8s + r (low), 8s + r + 4 (high)
-  v4i a;       // A operands (activation row t = c) of the two blocks
-  v4i al;      // TwoPass low words
-  float sx;    // the scale of activation row t = l % 16, block 8s + r + 4 * ((l / 16) & 1)
+  v4i w[TPW];   // the B operands of blocks 8s + r (.x, .y) and 8s + r + 4 (.z, .w), a tile each
+  v4i sc;       // the scales of column c's four rows: word m = block 8s + r (low), 8s + r + 4 (high)
+  v4i a[AT];    // A operands (activation row t = c of each activation tile) of the two blocks
+  v4i al[AT];   // TwoPass low words
+  float sx[AT]; // the scale of activation row t = l % 16, block 8s + r + 4 * ((l / 16) & 1)
 };
 
-template <int MODE, int TPW>
-__device__ __forceinline__ void mt_load(MtStep<MODE, TPW>& b, const uint8_t* rec, int m0, const int8_t* xa,
-                                        const int8_t* xla, const float* xsa) {
+__device__ __forceinline__ long lo64(v4i v) { return (long)(((unsigned long)(unsigned)v[1] << 32) | (unsigned)v[0]); }
+__device__ __forceinline__ long hi64(v4i v) { return (long)(((unsigned long)(unsigned)v[3] << 32) | (unsigned)v[2]); }
+
+// xa, xla, xsa point at this step's record of activation tile 0; tile `at`
+// lies at + at * 16K bytes (words) and + at * K/2 scales.
+template <int MODE, int TPW, int AT>
+__device__ __forceinline__ void mt_load(MtStep<MODE, TPW, AT>& b, const uint8_t* rec, int m0, const int8_t* xa,
+                                        const int8_t* xla, const float* xsa, int64_t K) {
   __builtin_amdgcn_sched_barrier(0);
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int m = 0; m < TPW; ++m)
     b.w[m] = __builtin_nontemporal_load((const v4i*)(rec + 1024 * (m0 + m) + 16 * lane));
   b.sc = *(const v4i*)(rec + MT_WBYTES + 16 * (lane & 15));
-  b.a = *(const v4i*)(xa + 16 * lane);
-  if constexpr (MODE == 2) b.al = *(const v4i*)(xla + 16 * lane);
-  b.sx = xsa[lane & 31];
+#pragma unroll
+  for (int at = 0; at < AT; ++at) {
+    b.a[at] = *(const v4i*)(xa + at * 16 * K + 16 * lane);
+    if constexpr (MODE == 2) b.al[at] = *(const v4i*)(xla + at * 16 * K + 16 * lane);
+    b.sx[at] = xsa[at * (K / 2) + (lane & 31)];
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE, int TPW>
-__device__ __forceinline__ void mt_terms(const MtStep<MODE, TPW>& b, int m0, float (&p)[TPW][4]) {
+template <int MODE, int TPW, int AT>
+__device__ __forceinline__ void mt_terms(const MtStep<MODE, TPW, AT>& b, int m0, float (&p)[TPW][AT][4]) {
   const int lane = threadIdx.x & 63, u = lane >> 4;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float sig[4];
+    float sig[AT][4];
+    long ak[AT], lk[AT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sig[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * h + 4 * u + i), __float_as_int(b.sx)));
-    const long ak = h == 0 ? (long)(((unsigned long)(unsigned)b.a[1] << 32) | (unsigned)b.a[0])
-                           : (long)(((unsigned long)(unsigned)b.a[3] << 32) | (unsigned)b.a[2]);
-    long lk = 0;
-    if constexpr (MODE == 2)
-      lk = h == 0 ? (long)(((unsigned long)(unsigned)b.al[1] << 32) | (unsigned)b.al[0])
-                  : (long)(((unsigned long)(unsigned)b.al[3] << 32) | (unsigned)b.al[2]);
+    for (int at = 0; at < AT; ++at) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sig[at][i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * h + 4 * u + i), __float_as_int(b.sx[at])));
+      ak[at] = h == 0 ? lo64(b.a[at]) : hi64(b.a[at]);
+      lk[at] = 0;
+      if constexpr (MODE == 2) lk[at] = h == 0 ? lo64(b.al[at]) : hi64(b.al[at]);
+    }
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
-      const long wk = h == 0 ? (long)(((unsigned long)(unsigned)b.w[m][1] << 32) | (unsigned)b.w[m][0])
-                             : (long)(((unsigned long)(unsigned)b.w[m][3] << 32) | (unsigned)b.w[m][2]);
-      const v4i D = mma16x16x32(ak, wk);
-      v4i E = {0, 0, 0, 0};
-      if constexpr (MODE == 2) E = mma16x16x32(lk, wk);
+      const long wk = h == 0 ? lo64(b.w[m]) : hi64(b.w[m]);
       const unsigned sw = (unsigned)b.sc[m0 + m];
       const float sgm = half_bits_to_float((unsigned short)(h == 0 ? (sw & 0xffffu) : (sw >> 16)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float ta, tb;
-        q8_term<MODE>(sgm, sig[i], D[i], E[i], ta, tb);
-        p[m][i] = __fmaf_rn(ta, tb, p[m][i]);
+      for (int at = 0; at < AT; ++at) {
+        const v4i D = mma16x16x32(ak[at], wk);
+        v4i E = {0, 0, 0, 0};
+        if constexpr (MODE == 2) E = mma16x16x32(lk[at], wk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float ta, tb;
+          q8_term<MODE>(sgm, sig[at][i], D[i], E[i], ta, tb);
+          p[m][at][i] = __fmaf_rn(ta, tb, p[m][at][i]);
+        }
       }
     }
   }
 }
 
 // Grid (workgroup row blocks of 64*GW rows, splits), 4 * (4*GW / TPW) waves a
-// workgroup.  out [splits][B][N].
-template <int MODE, int TPW, int P, int GW>
+// workgroup, AT activation tiles of 16 rows (B <= 16 * AT).  out [splits][B][N].
+template <int MODE, int TPW, int P, int GW, int AT>
 __global__ __launch_bounds__(256 * (4 * GW / TPW)) void k_gemv_mma_tiled(const uint8_t* __restrict__ wt,
                                                                     const int8_t* __restrict__ xq,
                                                                     const int8_t* __restrict__ xl,
                                                                     const float* __restrict__ xs, int64_t N, int64_t K,
                                                                     int B, int S, float* __restrict__ out) {
   constexpr int G = 4 * GW / TPW;      // tile groups a workgroup
-  __shared__ float red[4 * G][TPW][4][64];  // [wave][tile][i][lane]
+  __shared__ float red[4 * G][TPW][4][64];  // [wave][tile][i][lane], one activation tile at a time
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = wave & 3, g = wave >> 2, m0 = (TPW * g) & 3;  // tile m0.. of record group q
   const int c = lane & 15, u = lane >> 4;
@@ -197,19 +210,21 @@ __global__ __launch_bounds__(256 * (4 * GW / TPW)) void k_gemv_mma_tiled(const u
   const int8_t* xla0 = MODE == 2 ? xl + ((int64_t)gs0 * 4 + r) * 1024 : nullptr;
   const float* xsa0 = xs + ((int64_t)gs0 * 4 + r) * 32;
 
-  float p[TPW][4];
+  float p[TPW][AT][4];
 #pragma unroll
   for (int m = 0; m < TPW; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[m][i] = 0.0f;
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][at][i] = 0.0f;
 
   if (nsteps > 0) {
-    auto load = [&](MtStep<MODE, TPW>& b, int st) {
+    auto load = [&](MtStep<MODE, TPW, AT>& b, int st) {
       const int64_t k = st < nsteps ? st : nsteps - 1;  // past the chunk: its last step again
-      mt_load<MODE, TPW>(b, rec0 + k * 4 * MT_REC, m0, xa0 + k * 4096, MODE == 2 ? xla0 + k * 4096 : nullptr,
-                         xsa0 + k * 128);
+      mt_load<MODE, TPW, AT>(b, rec0 + k * 4 * MT_REC, m0, xa0 + k * 4096, MODE == 2 ? xla0 + k * 4096 : nullptr,
+                             xsa0 + k * 128, K);
     };
-    MtStep<MODE, TPW> b[P];
+    MtStep<MODE, TPW, AT> b[P];
 #pragma unroll
     for (int k = 0; k < P; ++k) load(b[k], k);
     int st = 0;
@@ -217,37 +232,42 @@ __global__ __launch_bounds__(256 * (4 * GW / TPW)) void k_gemv_mma_tiled(const u
     for (; st + 2 * P - 1 < nsteps; st += P) {
 #pragma unroll
       for (int k = 0; k < P; ++k) {
-        mt_terms<MODE, TPW>(b[k], m0, p);
+        mt_terms<MODE, TPW, AT>(b[k], m0, p);
         load(b[k], st + k + P);
       }
     }
     // the last 1 .. 2P - 1 steps, in order
 #pragma unroll
     for (int k = 0; k < P; ++k) {
-      if (st + k < nsteps) mt_terms<MODE, TPW>(b[k], m0, p);
+      if (st + k < nsteps) mt_terms<MODE, TPW, AT>(b[k], m0, p);
       if (st + k + P < nsteps) load(b[k], st + k + P);
     }
 #pragma unroll
     for (int k = 0; k + 1 < P; ++k)
-      if (st + P + k < nsteps) mt_terms<MODE, TPW>(b[k], m0, p);
+      if (st + P + k < nsteps) mt_terms<MODE, TPW, AT>(b[k], m0, p);
   }
 
+  // one activation tile at a time through LDS: wave (g, 0) writes its tiles,
+  // lane (c, u) holding row 64q + 16(m0 + m) + c and batch rows 16 at + 4u + i
 #pragma unroll
-  for (int m = 0; m < TPW; ++m)
+  for (int at = 0; at < AT; ++at) {
+    if (at > 0) __syncthreads();  // the previous tile's reads are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = p[m][i];
-  __syncthreads();
-  // wave (g, 0) writes its tiles: lane (c, u) holds row 64q + 16(m0 + m) + c, batch rows 4u + i
-  if (r == 0) {
+    for (int m = 0; m < TPW; ++m)
 #pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const int64_t o = q * MT_ROWS + 16 * (m0 + m) + c;  // rows past the last record group: o >= N
+      for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = p[m][at][i];
+    __syncthreads();
+    if (r == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * u + i;
-        const float y = __fadd_rn(__fadd_rn(red[4 * g][m][i][lane], red[4 * g + 2][m][i][lane]),
-                                  __fadd_rn(red[4 * g + 1][m][i][lane], red[4 * g + 3][m][i][lane]));
-        if (t < B && o < N) out[((int64_t)s_idx * B + t) * N + o] = y;
+      for (int m = 0; m < TPW; ++m) {
+        const int64_t o = q * MT_ROWS + 16 * (m0 + m) + c;  // rows past the last record group: o >= N
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * at + 4 * u + i;
+          const float y = __fadd_rn(__fadd_rn(red[4 * g][m][i][lane], red[4 * g + 2][m][i][lane]),
+                                    __fadd_rn(red[4 * g + 1][m][i][lane], red[4 * g + 3][m][i][lane]));
+          if (t < B && o < N) out[((int64_t)s_idx * B + t) * N + o] = y;
+        }
       }
     }
   }
@@ -269,18 +289,34 @@ int mt_groups(int64_t N, int splits) {
   return (N + 127) / 128 * splits >= 192 ? 2 : 1;
 }
 
+// Activation tiles of 16 rows for B rows: 1, 2 or 4.
+int mt_tiles(int64_t B) { return B <= 16 ? 1 : B <= 32 ? 2 : 4; }
+
+// Steps in flight fall with the activation tiles a step holds in registers.
+template <int MODE, int GW, int AT>
+hipError_t launch_mta(const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
+                      int64_t B, int splits, float* out, hipStream_t st) {
+  constexpr int P = AT == 1 ? MT_P : AT == 2 ? 3 : 2;
+  const dim3 grid((unsigned)((N + GW * MT_ROWS - 1) / (GW * MT_ROWS)), (unsigned)splits), block(256 * GW);
+  return launch((k_gemv_mma_tiled<MODE, 4, P, GW, AT>), grid, block, 0, st, wt, xq, xl, xs, N, K, (int)B, splits,
+                out);
+}
+
 template <int MODE, int GW>
 hipError_t launch_mt(const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq, const int8_t* xl, const float* xs,
                      int64_t B, int splits, float* out, hipStream_t st) {
-  const dim3 grid((unsigned)((N + GW * MT_ROWS - 1) / (GW * MT_ROWS)), (unsigned)splits), block(256 * GW);
-  return launch((k_gemv_mma_tiled<MODE, 4, MT_P, GW>), grid, block, 0, st, wt, xq, xl, xs, N, K, (int)B, splits,
-                out);
+  switch (mt_tiles(B)) {
+    case 1: return launch_mta<MODE, GW, 1>(wt, N, K, xq, xl, xs, B, splits, out, st);
+    case 2: return launch_mta<MODE, GW, 2>(wt, N, K, xq, xl, xs, B, splits, out, st);
+    default: return launch_mta<MODE, GW, 4>(wt, N, K, xq, xl, xs, B, splits, out, st);
+  }
 }
 
 template <int MODE>
 hipError_t launch_qm(const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs, hipStream_t st) {
-  const int64_t threads = 16 * (K / QK) * 8;
-  return launch(k_quantize_mma<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, (int)B, K, xq,
+  const int AT = mt_tiles(B);
+  const int64_t threads = 16 * AT * (K / QK) * 8;
+  return launch(k_quantize_mma<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, (int)B, K, AT, xq,
                 xl, xs);
 }
 

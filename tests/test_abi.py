@@ -569,7 +569,7 @@ def test_mma_tiled_validation():
     assert quant(x=None) == EINVAL and quant(xq=None) == EINVAL and quant(xs=None) == EINVAL
     assert quant(mode=2) == EINVAL                   # TwoPass needs xl
     assert quant(xl=A) == EINVAL                     # Int8Act takes no xl
-    assert quant(B=0) == ESHAPE and quant(B=17) == ESHAPE and quant(K=288) == ESHAPE
+    assert quant(B=0) == ESHAPE and quant(B=65) == ESHAPE and quant(K=288) == ESHAPE
     assert quant(x=A + 4) == EALIGN and quant(xq=A + 8) == EALIGN and quant(xs=A + 2) == EALIGN
     assert quant(mode=2, xl=A + 8) == EALIGN
 
@@ -581,5 +581,4 @@ def test_mma_tiled_validation():
     assert mt(mode=2) == EINVAL and mt(xl=A) == EINVAL
     assert mt(K=288) == ESHAPE and mt(N=0) == ESHAPE and mt(B=0) == ESHAPE and mt(S=0) == ESHAPE
     assert mt(S=65) == ESHAPE and mt(B=65) == ESHAPE
-    assert mt(B=17) == EMODE                         # up to 16 activation rows
     assert mt(wt=A + 8) == EALIGN and mt(xq=A + 4) == EALIGN and mt(xs=A + 2) == EALIGN and mt(out=A + 1) == EALIGN

@@ -65,27 +65,30 @@ def records_weights(wq, ws):
 
 
 def records_acts(xq, xs, B, zero_scale):
-    """The activation records by the header's definition: record (s, r) holds, at
-    byte 16*l + 8*h + j, word 8*(l//16) + j of block 8s + r + 4h of row l%16, and
-    scale 16*h + t of that block and row t; rows past B are a zero row's."""
+    """The activation records by the header's definition: tiles of 16 rows (1, 2
+    or 4 of them), each a run of records (s, r) holding, at byte 16*l + 8*h + j,
+    word 8*(l//16) + j of block 8s + r + 4h of row l%16 of the tile, then scale
+    16*h + t of that block and tile row t; rows past B are a zero row's."""
     K = xq.shape[1]
-    full = np.zeros((16, K), np.int8)
+    R = 16 if B <= 16 else 32 if B <= 32 else 64
+    full = np.zeros((R, K), np.int8)
     full[:B] = xq
-    sc = np.full((16, K // 32), zero_scale, np.float32)
+    sc = np.full((R, K // 32), zero_scale, np.float32)
     sc[:B] = xs
     S = K // 256
-    words = np.zeros((S, 4, 1024), np.int8)
-    scales = np.zeros((S, 4, 32), np.float32)
-    for st in range(S):
-        for r in range(4):
-            for l in range(64):
-                t, u = l % 16, l // 16
+    words = np.zeros((R // 16, S, 4, 1024), np.int8)
+    scales = np.zeros((R // 16, S, 4, 32), np.float32)
+    for a in range(R // 16):
+        for st in range(S):
+            for r in range(4):
+                for l in range(64):
+                    t, u = 16 * a + l % 16, l // 16
+                    for h in range(2):
+                        b = 8 * st + r + 4 * h
+                        words[a, st, r, 16 * l + 8 * h:16 * l + 8 * h + 8] = full[t, 32 * b + 8 * u:32 * b + 8 * u + 8]
                 for h in range(2):
-                    b = 8 * st + r + 4 * h
-                    words[st, r, 16 * l + 8 * h:16 * l + 8 * h + 8] = full[t, 32 * b + 8 * u:32 * b + 8 * u + 8]
-            for h in range(2):
-                for t in range(16):
-                    scales[st, r, 16 * h + t] = sc[t, 8 * st + r + 4 * h]
+                    for t in range(16):
+                        scales[a, st, r, 16 * h + t] = sc[16 * a + t, 8 * st + r + 4 * h]
     return words.reshape(-1), scales.reshape(-1)
 
 
@@ -103,10 +106,11 @@ def tile(wq, ws):
 
 def acts(mode, x):
     B, K = x.shape
+    R = q.mma_act_rows(B)
     xd = dev(x)
-    tq = torch.full((16 * K,), 77, dtype=torch.int8, device=DEV)
-    tl = torch.full((16 * K,), 77, dtype=torch.int8, device=DEV) if mode == 2 else None
-    ts = torch.full((16 * (K // 32),), float("nan"), dtype=torch.float32, device=DEV)
+    tq = torch.full((R * K,), 77, dtype=torch.int8, device=DEV)
+    tl = torch.full((R * K,), 77, dtype=torch.int8, device=DEV) if mode == 2 else None
+    ts = torch.full((R * (K // 32),), float("nan"), dtype=torch.float32, device=DEV)
     q.quantize_act_mma(mode, xd, tq, tl, ts)
     return tq, tl, ts
 
@@ -120,7 +124,8 @@ def test_tile_mma_layout(N, K):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-@pytest.mark.parametrize("B,K", [(16, 512), (1, 256), (5, 1280), (16, 2048)])
+@pytest.mark.parametrize("B,K", [(16, 512), (1, 256), (5, 1280), (16, 2048), (17, 512), (32, 256), (33, 768),
+                                 (64, 512)])
 def test_quantize_act_mma_layout(mode, B, K):
     """The words and scales are the oracle quantizer's, in the MFMA order, with a
     zero row's words and scale past the batch."""
@@ -139,7 +144,8 @@ def test_quantize_act_mma_layout(mode, B, K):
 
 CASES = [(16, 256, 5120, 1), (2, 33, 512, 1), (5, 100, 1536, 2), (16, 130, 768, 3), (11, 64, 25600, 4),
          (1, 77, 256, 1), (16, 200, 5120, 3), (7, 192, 1024, 1),
-         (3, 40, 256, 2), (16, 64, 256, 4)]  # the last two: empty chunks
+         (3, 40, 256, 2), (16, 64, 256, 4),  # these two: empty chunks
+         (17, 100, 512, 1), (32, 64, 2048, 2), (40, 130, 768, 1), (64, 200, 1024, 3), (64, 16, 256, 2)]  # prefill
 
 
 @pytest.mark.parametrize("groups", [1, 2])
@@ -170,7 +176,7 @@ def test_mma_tiled_bit_exact(B, N, K, S, mode, groups, tune):
     plain = torch.full((S, B, N), float("nan"), dtype=torch.float32, device=DEV)
     q.gemv_q8(mode, dev(wq), dev(ws), plain, xq=pq, xl=pl, xs=ps, splits=S)
     assert host(plain).tobytes() == got.tobytes()
-    for t in sorted({0, B - 1}):
+    for t in sorted({0, B - 1, min(16, B - 1)}):
         tq1, tl1, ts1 = acts(mode, x[t:t + 1])
         one = torch.full((S, 1, N), float("nan"), dtype=torch.float32, device=DEV)
         q.gemv_q8_mma_tiled(mode, wt, N, K, one, tq1, tl1, ts1, 1, splits=S)
@@ -197,3 +203,26 @@ def test_mma_tiled_decode_b16_full(mode):
         outs.append(host(y))
     np.testing.assert_array_equal(outs[0], want)
     assert outs[0].tobytes() == outs[1].tobytes()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B", [40, 64])
+def test_mma_tiled_prefill_full(mode, B):
+    """A prefill chunk of B rows against 25600x5120: every output against the
+    oracle, and the first 16 rows equal a 16-row call."""
+    announce(f"gemv_q8_mma_tiled B={B} 25600x5120 mode {mode}")
+    N, K = 25600, 5120
+    wq, ws = workloads.weights(N, K, 71, 72)
+    x = workloads.batch_activation(B, K, 73 + B, True, 74 + B)
+    oq, ol, os_ = oracle.quantize(mode, x)
+    want = oracle.gemv(mode, wq, ws, xq=oq, xl=ol, xs=os_, nthreads=THREADS)
+    wt = tile(wq, ws)
+    tq, tl, ts = acts(mode, x)
+    y = torch.full((B, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wt, N, K, y, tq, tl, ts, B)
+    got = host(y)
+    np.testing.assert_array_equal(got, want)
+    tq16, tl16, ts16 = acts(mode, x[:16])
+    y16 = torch.full((16, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wt, N, K, y16, tq16, tl16, ts16, 16)
+    assert host(y16).tobytes() == got[:16].tobytes()
