@@ -1,7 +1,7 @@
-// qdg_mma_tiled.hip -- the batched (B <= 16) Q8_0 GEMV on int8 MFMA over weights
-// stored in the MFMA's own operand order (megakernel page: the GEMV's
-// tiled-weights option, where only the addresses of the weights change; lane
-// kernel library page: lk_gemv_mma, whose rows sum exactly as a single row).
+// qdg_mma_tiled.hip -- the batched (B <= 64) Q8_0 GEMV on int8 MFMA over weights
+// and activations stored in the MFMA's own operand order (megakernel page: the
+// GEMV's tiled-weights option, where only the addresses of the weights change;
+// lane kernel library page: lk_gemv_mma, whose rows sum exactly as a single row).
 //
 // The sums are k_gemv_mfma_dma's, term for term: block g's exact int32 dots D
 // (and E) from v_mfma_i32_16x16x32_i8, the step p <- fma(a, b, p) of
@@ -21,22 +21,23 @@
 // Records run (q, s, r) in row-major order; rows past N are zero.  A wave's
 // weight load is one contiguous KiB, its scale load 256 bytes.
 //
-// The activations come in the same order (qdg_quantize_act_mma): for step s and
-// residue r, lane l's 16 bytes are the A operands of the two blocks (activation
-// row t = l % 16, 8 bytes from 8 * (l / 16) of blocks 8s + r and 8s + r + 4), and
-// 32 scales follow the same (s, r) order, [h][t].  Sixteen rows always; the
-// quantizer writes rows past the batch as the words of a zero row.
+// The activations come in the same order (qdg_quantize_act_mma), in AT tiles of
+// 16 rows (1, 2 or 4 of them, one after the other): for step s and residue r,
+// lane l's 16 bytes of a tile are the A operands of the two blocks (tile row
+// t = l % 16, 8 bytes from 8 * (l / 16) of blocks 8s + r and 8s + r + 4), and 32
+// scales follow the same (s, r) order, [h][t].  The quantizer writes the rows
+// past the batch as the words of a zero row.
 //
-// Kernel.  A workgroup of 4 * (4 / TPW) waves owns one 64-row group and one chunk
-// of K; wave (g, r) takes tiles TPW*g .. TPW*g + TPW - 1 of the group for
-// residue r and walks the chunk's steps reading records (q, s, r) and the
-// activation records (s, r) straight into registers -- no LDS tile, no
-// workgroup barrier until the end -- with P - 1 steps in flight (named step
-// buffers; every step issues the same loads, so the compiler's wait counts stay
-// exact).  Each load is a contiguous run: 1 KiB a tile, 1 KiB of activation
-// words, 128 bytes of activation scales.  A lane loads one activation scale and
-// the scales of its four batch rows reach it by ds_bpermute.  The partial waves
-// meet in LDS at the end.
+// Kernel.  A workgroup of 4 * (4 * GW / TPW) waves owns GW 64-row groups and one
+// chunk of K; wave (g, r) takes TPW tiles for residue r and walks the chunk's
+// steps reading records (q, s, r) and the activation records (s, r) of every
+// activation tile straight into registers -- no LDS tile, no workgroup barrier
+// until the end -- with P - 1 steps in flight (named step buffers; every step
+// issues the same loads, so the compiler's wait counts stay exact).  Each load
+// is a contiguous run: 1 KiB a weight tile, 1 KiB of activation words and 128
+// bytes of activation scales an activation tile.  A lane loads one activation
+// scale a tile and the scales of its four batch rows reach it by ds_bpermute.
+// The partial waves meet in LDS at the end, one activation tile at a time.
 
 #include "qdg_device.h"
 
