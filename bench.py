@@ -470,7 +470,7 @@ def main() -> int:
     if want("8b"):
         # S per projection (measured best, in-workgroup combine / Dequant chunk waves)
         s_q8 = {"qkv": 2, "gate_up": 2, "down": 6}
-        s_dq = {"qkv": 5, "gate_up": 2, "down": 4}
+        s_dq = {"qkv": 3, "gate_up": 2, "down": 2}
         for si, sh in enumerate(workloads.CONFIGS[1]):
             d, wsets = upload_set(1, si)
             x = torch.from_numpy(d["x"]).to(dev)
