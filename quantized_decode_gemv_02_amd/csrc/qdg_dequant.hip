@@ -273,13 +273,36 @@ bool dq_x64() { return tune(QDG_TUNE_DQ_X64) != 0; }
 
 }  // namespace
 
-hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
-                               float* out, hipStream_t st) {
-  return launch_gemv_dequant_sk(wq, ws, N, K, x, 1, out, nullptr, st);
+// The unsplit call (qdg_gemv_q8, and its arg-max form, which must give the same
+// logits) runs the chunk-wave kernel with its own chunk count: two from 8192 rows
+// up, four below.  Measured on the 151936x5120 LM head, two chunks take 153 us
+// against 224-230 us at five; on the 5120-row projections four is the best of
+// 2..8.  0 when that kernel does not serve the shape or QDG_TUNE_DQ_SEG = 0
+// asks for this file's kernel.
+int dq_unsplit_chunks(int64_t N, int64_t K) {
+  if (tune(QDG_TUNE_DQ_SEG) == 0) return 0;
+  const int S = N >= 8192 ? 2 : 4;
+  return dq_seg_chunks(K, S) > 0 ? S : 0;
 }
 
+hipError_t launch_gemv_dequant(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
+                               float* out, hipStream_t st) {
+  const int S = dq_unsplit_chunks(N, K);
+  if (S > 0) return launch_gemv_dq_seg(wq, ws, N, K, x, S, out, st);
+  if (dq_x64()) return launch_dq<true>(wq, ws, N, K, x, 1, out, nullptr, st);
+  return launch_dq<false>(wq, ws, N, K, x, 1, out, nullptr, st);
+}
+
+// The same kernel as launch_gemv_dequant, so the logits are its bits; the
+// chunk-wave kernel has no arg-max epilogue, so a pass over y writes the tile keys.
 hipError_t launch_gemv_dequant_argmax(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                                       float* y, unsigned long long* keys, hipStream_t st) {
+  const int S = dq_unsplit_chunks(N, K);
+  if (S > 0) {
+    const hipError_t e = launch_gemv_dq_seg(wq, ws, N, K, x, S, y, st);
+    if (e != hipSuccess) return e;
+    return launch_tile_keys(y, N, keys, st);
+  }
   if (dq_x64()) return launch_dq<true, true>(wq, ws, N, K, x, 1, y, nullptr, st, keys);
   return launch_dq<false, true>(wq, ws, N, K, x, 1, y, nullptr, st, keys);
 }

@@ -607,6 +607,7 @@ hipError_t launch_gemv_glu(int act, int mode, const int8_t* wg, const uint16_t* 
 hipError_t launch_glu_quant(int act, int mode, const float* g, const float* u, int64_t nblocks, float* h,
                             int8_t* xq, int8_t* xl, float* xs, hipStream_t st);
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st);
+hipError_t launch_tile_keys(const float* y, int64_t N, unsigned long long* keys, hipStream_t st);
 int64_t gemv_tiles(int64_t N);
 hipError_t launch_gemv_argmax(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x,
                               const int8_t* xq, const int8_t* xl, const float* xs, float* y, int32_t* idx,

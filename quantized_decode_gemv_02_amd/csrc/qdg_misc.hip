@@ -165,6 +165,27 @@ hipError_t launch_argmax(const float* y, int64_t B, int64_t N, int32_t* idx, uns
   return launch(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, ws, G, idx);
 }
 
+// The arg-max key of each 16-row tile of y [N] (the keys a GEMV's arg-max
+// epilogue writes), for a GEMV without that epilogue: sixteen lanes a tile, a
+// lane a row, the tile's maximum by a butterfly over the sixteen.
+__global__ __launch_bounds__(256) void k_tile_keys(const float* __restrict__ y, int64_t N,
+                                                   unsigned long long* __restrict__ keys) {
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4), tiles = (N + 15) / 16;
+  const int64_t row = 16 * tile + (threadIdx.x & 15);
+  unsigned long long k = row < N ? amax_key(y[row], (unsigned)row) : 0ull;
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+    const unsigned long long o = __shfl_xor(k, m, 64);
+    k = o > k ? o : k;
+  }
+  if ((threadIdx.x & 15) == 0 && tile < tiles) keys[tile] = k;
+}
+
+hipError_t launch_tile_keys(const float* y, int64_t N, unsigned long long* keys, hipStream_t st) {
+  const int64_t tiles = (N + 15) / 16;
+  return launch(k_tile_keys, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, st, y, N, keys);
+}
+
 hipError_t launch_argmax_final(const unsigned long long* keys, int64_t B, int G, int32_t* idx, hipStream_t st) {
   return launch(k_argmax_final, dim3((unsigned)B), dim3(AF_THREADS), 0, st, keys, G, idx);
 }
