@@ -176,6 +176,42 @@ def test_within_f64_tolerance(mode, config, shape_index):
         assert rel.max() < (1e-1 if mode == 1 else 2e-3)
 
 
+def test_reference_tnorm_closed_forms():
+    """The tolerance scale tnorm is the root-sum-square of a row's block terms
+    (sigma * the block's exact dot), pinned on rows whose terms are known: equal
+    terms give Y = nb*T and tnorm = sqrt(nb)*|T|; alternating signs give Y = 0
+    with the same tnorm (so tnorm is not |Y|); one nonzero block gives
+    tnorm = |Y|; a TwoPass row whose low words carry the whole term weighs them
+    by 1/128."""
+    nb = 16
+    K = 32 * nb
+    ones = np.ones((3, K), np.int8)
+    ones[1].reshape(nb, 32)[1::2] = -1          # alternating block signs
+    ones[2].reshape(nb, 32)[1:] = 0             # one nonzero block
+    ws = np.full((3, nb), 0x3C00, np.uint16)     # sigma = 1
+    # Dequant: x = 0.5 everywhere, T = 32 * 0.5 = 16 per block
+    x = np.full((1, K), 0.5, np.float32)
+    Y, tn = oracle.reference_f64(0, ones, ws, x=x)
+    assert Y[0, 0] == 16.0 * nb and tn[0, 0] == 16.0 * np.sqrt(nb)
+    assert Y[0, 1] == 0.0 and tn[0, 1] == 16.0 * np.sqrt(nb)
+    assert Y[0, 2] == 16.0 and tn[0, 2] == 16.0
+    # Int8Act: the words of x = 0.5 are 127 with s = fl32(0.5/127), T = 32*127*s
+    xq, xl, xs = oracle.quantize(1, x)
+    assert (xq == 127).all() and (xs == np.float32(0.5) / np.float32(127.0)).all()
+    T = 32 * 127 * float(xs[0, 0])
+    Y, tn = oracle.reference_f64(1, ones, ws, xq=xq, xl=xl, xs=xs)
+    assert Y[0, 0] == pytest.approx(T * nb, rel=1e-15) and tn[0, 0] == pytest.approx(T * np.sqrt(nb), rel=1e-15)
+    assert Y[0, 1] == 0.0 and tn[0, 1] == pytest.approx(T * np.sqrt(nb), rel=1e-15)
+    assert tn[0, 2] == pytest.approx(abs(Y[0, 2]), rel=1e-15)
+    # TwoPass with high words zero and low words 64: T = s * (0 + 32*64/128) = 16 s
+    hq = np.zeros((1, K), np.int8)
+    lq = np.full((1, K), 64, np.int8)
+    s = np.full((1, nb), 0.25, np.float32)
+    Y, tn = oracle.reference_f64(2, ones, ws, xq=hq, xl=lq, xs=s)
+    assert Y[0, 0] == 4.0 * nb and tn[0, 0] == 4.0 * np.sqrt(nb)
+    assert Y[0, 1] == 0.0 and tn[0, 1] == 4.0 * np.sqrt(nb)
+
+
 def test_tolerance_catches_low_word_1_over_127():
     # the f64 criterion with the low word weighted 1/127 instead of 1/128 fails on a
     # low-word-dominated row: a mistake of that kind in the oracle would show
