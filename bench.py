@@ -546,6 +546,17 @@ def main() -> int:
             calls = [q.bind_gemv_q8(mode, w, s, y, xq=xq, xl=xl, xs=xs) for w, s in wsets]
             rec[NAMES[mode]] = {"B": sh.B, "alg_bytes": alg_bytes(mode, sh.N, sh.K, sh.B),
                                 **rate(alg_bytes(mode, sh.N, sh.K, sh.B), timer.median_us(calls, args.launches))}
+        # a 64-row prefill chunk on the same weights (seeded rows of the same
+        # distribution), plain and MFMA-ordered, beside the 16-row batch
+        PB = 64
+        xp = torch.from_numpy(workloads.batch_activation(PB, sh.K, 4000, True, 4001)).to(dev)
+        prefill = {"plain": {}, "mma_tiled": {}}
+        for mode in (1, 2):
+            xq, xl, xs = quantized(mode, xp)
+            y = torch.empty((PB, sh.N), dtype=torch.float32, device=dev)
+            calls = [q.bind_gemv_q8(mode, w, s, y, xq=xq, xl=xl, xs=xs) for w, s in wsets]
+            b = alg_bytes(mode, sh.N, sh.K, PB)
+            prefill["plain"][NAMES[mode]] = {"B": PB, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches))}
         # the same batch over MFMA-ordered operands: the weights repacked once
         # (qdg_q8_tile_mma), the activations quantized into the MFMA order
         # (qdg_quantize_act_mma, timed beside), the GEMV qdg_gemv_q8_mma_tiled
@@ -569,7 +580,18 @@ def main() -> int:
             tiled[NAMES[mode]] = {"B": sh.B, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches)),
                                   "quantize_us": round(timer.median_us([qcall], args.launches), 3)}
         rec["mma_tiled"] = tiled
+        for mode in (1, 2):
+            R = q.mma_act_rows(PB)
+            tq = torch.empty(R * sh.K, dtype=torch.int8, device=dev)
+            tl = torch.empty(R * sh.K, dtype=torch.int8, device=dev) if mode == 2 else None
+            ts = torch.empty(R * (sh.K // 32), dtype=torch.float32, device=dev)
+            q.quantize_act_mma(mode, xp, tq, tl, ts)
+            y = torch.empty((PB, sh.N), dtype=torch.float32, device=dev)
+            calls = [q.bind_gemv_q8_mma_tiled(mode, wt, sh.N, sh.K, y, tq, tl, ts, PB) for wt in tiles]
+            b = alg_bytes(mode, sh.N, sh.K, PB)
+            prefill["mma_tiled"][NAMES[mode]] = {"B": PB, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches))}
         configs[f"batched_B{sh.B}_{sh.N}x{sh.K}"] = rec
+        configs[f"prefill_B{PB}_{sh.N}x{sh.K}"] = prefill
         del tiles
         torch.cuda.empty_cache()
         progress("batched done")
