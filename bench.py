@@ -451,6 +451,43 @@ def main() -> int:
         rec.update(rate(rec["alg_bytes"], timer.median_us(calls, args.launches)))
         return rec
 
+    def glu_record(mode, sh, wsets, x):
+        """The stacked gate+up matrix (gate rows first, then up) as the gate and up GEMVs
+        with the SwiGLU epilogue in one launch -- Dequant qdg_gemv_glu_dequant (h in f32),
+        the quantized modes qdg_gemv_glu_q8 (h's words) -- against the three calls it
+        equals: two unsplit qdg_gemv_q8 calls and the producer."""
+        F = sh.N // 2
+        g = torch.empty((1, F), dtype=torch.float32, device=dev)
+        u = torch.empty_like(g)
+        halves = [(w[:F], s[:F], w[F:], s[F:]) for w, s in wsets]
+        if mode == 0:
+            h = torch.empty((F,), dtype=torch.float32, device=dev)
+            fused = [q.bind_gemv_glu_dequant(0, *hv, x.view(-1), h) for hv in halves]
+            gemv = [q.bind_gemv_q8(0, hv[0], hv[1], g, x=x) for hv in halves]
+            prod = q.bind_glu_quantize(0, 0, g, u, h.view(1, F))
+            ups = [q.bind_gemv_q8(0, hv[2], hv[3], u, x=x) for hv in halves]
+        else:
+            xq, xl, xs = quantized(mode, x)
+            hq = torch.empty((F,), dtype=torch.int8, device=dev)
+            hl = torch.empty_like(hq) if mode == 2 else None
+            hs = torch.empty((F // 32,), dtype=torch.float32, device=dev)
+            fused = [q.bind_gemv_glu_q8(mode, *hv, xq, xl, xs, hq, hl, hs) for hv in halves]
+            gemv = [q.bind_gemv_q8(mode, hv[0], hv[1], g, xq=xq, xl=xl, xs=xs) for hv in halves]
+            ups = [q.bind_gemv_q8(mode, hv[2], hv[3], u, xq=xq, xl=xl, xs=xs) for hv in halves]
+            prod = q.bind_swiglu_quantize(mode, g, u, None, hq.view(1, F), None if hl is None else hl.view(1, F),
+                                          hs.view(1, F // 32))
+        f_us = timer.median_us(fused, args.launches)
+        g_us = timer.median_us(gemv, args.launches)
+        p_us = timer.median_us([prod], args.launches)
+        three = [lambda a=a, b=b: (a(), b(), prod()) for a, b in zip(gemv, ups)]
+        return {"F": F, "fused_us": round(f_us, 2), "gemv_us": round(g_us, 2), "producer_us": round(p_us, 2),
+                "three_calls_us": round(2 * g_us + p_us, 2),
+                "fused_wall_us": round(timer.wall_us(fused, args.launches), 2),
+                "three_calls_wall_us": round(timer.wall_us(three, args.launches), 2),
+                # both matrices, the activation once, and h (f32, or its words and scales)
+                **rate(2 * (F * sh.K + F * sh.K // 16) + alg_bytes(mode, 0, sh.K)
+                       + {0: 4 * F, 1: F + F // 8, 2: 2 * F + F // 8}[mode], f_us)}
+
     if want("tiny"):
         sh = workloads.CONFIGS[0][0]
         d, wsets = upload_set(0, 0, 0)
@@ -477,6 +514,8 @@ def main() -> int:
             rec = {}
             for mode in (0, 1, 2):
                 rec[NAMES[mode]] = projection_record(mode, sh, wsets, x, s_dq[sh.name] if mode == 0 else s_q8[sh.name])
+            if sh.name == "gate_up":
+                rec["glu"] = {NAMES[mode]: glu_record(mode, sh, wsets, x) for mode in (0, 1, 2)}
             configs[f"8b_{sh.name}_{sh.N}x{sh.K}"] = rec
             del wsets
         torch.cuda.empty_cache()

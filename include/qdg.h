@@ -414,6 +414,26 @@ int qdg_gemv_glu_act_q8(int act, int mode, const int8_t *wg, const uint16_t *sg,
                         const uint16_t *su, int64_t F, int64_t K, const int8_t *xq, const int8_t *xl,
                         const float *xs, float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
 
+/*
+ * The gate and up projections under the Dequant numerics with the gated product
+ * as the epilogue, in one launch (lane kernel library page, GLU: lk_gemv_glu
+ * with the Dequant accumulator and a binary32 output; lk_act): g = Wg x and
+ * u = Wu x as qdg_gemv_q8 computes them under QDG_DEQUANT (splits 1: the same
+ * chunk count for F rows and the same order), h = act(g) * u as
+ * qdg_glu_quantize computes it.  Bit-identical to those three calls (the
+ * producer under QDG_DEQUANT, h only) while QDG_TUNE_DQ_SEG keeps its default;
+ * g and u never reach memory.  h is the input of the down projection under
+ * QDG_DEQUANT.
+ * Device pointers: wg, wu int8 [F][K] (16-byte aligned); sg, su binary16 bits
+ * [F][K/32] (2-byte aligned); x f32 [K] (16-byte aligned); h f32 [F] (4-byte
+ * aligned), which must not overlap x, the weights or the scales (QDG_EINVAL).
+ * act one of QDG_ACT_*, else QDG_EINVAL.  F >= 1 (any F: h is not quantized)
+ * with F/4 < 2^31, K >= 32 a multiple of 32 up to 2^31, else QDG_ESHAPE.
+ */
+int qdg_gemv_glu_dequant(int act, const int8_t *wg, const uint16_t *sg, const int8_t *wu,
+                         const uint16_t *su, int64_t F, int64_t K, const float *x, float *h,
+                         qdg_stream stream);
+
 /* GGUF type numbers of the other block formats (qdg_gemv_fmt). */
 enum {
   QDG_FMT_Q4_0 = 2, QDG_FMT_Q4_1 = 3, QDG_FMT_Q5_0 = 6, QDG_FMT_Q5_1 = 7,

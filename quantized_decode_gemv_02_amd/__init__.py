@@ -89,6 +89,7 @@ _SIGS = {
     "qdg_gemv_q8_parts": ([_I, _P, _I, _I64, _P, _P, _P, _P, _I, _P], _I),
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_glu_act_q8": ([_I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "qdg_gemv_glu_dequant": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
     "qdg_gemv_fmt_chunk_waves": ([_I, _I, _I64, _I64, _I], _I),
@@ -317,6 +318,26 @@ def gemv_glu_act_q8(act: int, mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs,
 
 def bind_gemv_glu_act_q8(act: int, mode: int, wg, sg, wu, su, xq, xl, xs, hq, hl, hs, h=None) -> Bound:
     return Bound("qdg_gemv_glu_act_q8", act, *_glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs))
+
+
+def _glu_dequant_args(act, wg, sg, wu, su, x, h):
+    F, K = wg.shape
+    if tuple(wu.shape) != (F, K):
+        raise ValueError("gemv_glu_dequant: gate and up must have the same shape")
+    if x.numel() != K or h.numel() != F:
+        raise ValueError("gemv_glu_dequant: x must hold K values and h F values")
+    return (act, _ptr(wg, _i8(), "wg"), _ptr(sg, _scales(), "sg"), _ptr(wu, _i8(), "wu"), _ptr(su, _scales(), "su"),
+            F, K, _ptr(x, _f32(), "x"), _ptr(h, _f32(), "h"), _stream())
+
+
+def gemv_glu_dequant(act: int, wg, sg, wu, su, x, h) -> None:
+    """Gate and up GEMVs under the Dequant numerics with the gated product as the
+    epilogue: ``h = act(Wg x) * (Wu x)`` in f32, the down projection's input."""
+    _check("qdg_gemv_glu_dequant", _lib.qdg_gemv_glu_dequant(*_glu_dequant_args(act, wg, sg, wu, su, x, h)))
+
+
+def bind_gemv_glu_dequant(act: int, wg, sg, wu, su, x, h) -> Bound:
+    return Bound("qdg_gemv_glu_dequant", *_glu_dequant_args(act, wg, sg, wu, su, x, h))
 
 
 # GGUF type numbers of the other block formats

@@ -511,6 +511,27 @@ int qdg_gemv_q8_rmsnorm(int mode, const int8_t* wq, const uint16_t* ws, int64_t 
                                                  hq, hl, hs, workspace, as_stream(stream)));
 }
 
+int qdg_gemv_glu_dequant(int act, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                         int64_t F, int64_t K, const float* x, float* h, qdg_stream stream) {
+  if (act < QDG_ACT_SILU || act > QDG_ACT_GELU_TANH) return QDG_EINVAL;
+  if (!wg || !sg || !wu || !su || !x || !h) return QDG_EINVAL;
+  if (!shape_ok(F, K) || (F + 3) / 4 >= ((int64_t)1 << 31)) return QDG_ESHAPE;
+  if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(sg, 2) || !aligned(su, 2) || !aligned(x, 16) ||
+      !aligned(h, 4))
+    return QDG_EALIGN;
+  // h is written while other workgroups still read the operands
+  const uintptr_t h0 = (uintptr_t)h, h1 = h0 + (uintptr_t)F * 4;
+  const uintptr_t spans[5][2] = {{(uintptr_t)x, (uintptr_t)x + (uintptr_t)K * 4},
+                                 {(uintptr_t)wg, (uintptr_t)wg + (uintptr_t)(F * K)},
+                                 {(uintptr_t)wu, (uintptr_t)wu + (uintptr_t)(F * K)},
+                                 {(uintptr_t)sg, (uintptr_t)sg + (uintptr_t)(F * (K / qdg::QK)) * 2},
+                                 {(uintptr_t)su, (uintptr_t)su + (uintptr_t)(F * (K / qdg::QK)) * 2}};
+  for (const auto& sp : spans)
+    if (sp[0] < h1 && h0 < sp[1]) return QDG_EINVAL;
+  return hip_status(
+      qdg::launch_gemv_dq_glu(act, wg, sg, wu, su, F, K, x, qdg::dq_unsplit_order(F), h, as_stream(stream)));
+}
+
 int qdg_swiglu_quantize(int mode, const float* g, const float* u, int64_t B, int64_t K, float* h, int8_t* xq,
                         int8_t* xl, float* xs, qdg_stream stream) {
   return qdg_glu_quantize(QDG_ACT_SILU, mode, g, u, B, K, h, xq, xl, xs, stream);

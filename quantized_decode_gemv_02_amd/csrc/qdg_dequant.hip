@@ -279,9 +279,11 @@ bool dq_x64() { return tune(QDG_TUNE_DQ_X64) != 0; }
 // against 224-230 us at five; on the 5120-row projections four is the best of
 // 2..8.  0 when that kernel does not serve the shape or QDG_TUNE_DQ_SEG = 0
 // asks for this file's kernel.
+int dq_unsplit_order(int64_t N) { return N >= 8192 ? 2 : 4; }
+
 int dq_unsplit_chunks(int64_t N, int64_t K) {
   if (tune(QDG_TUNE_DQ_SEG) == 0) return 0;
-  const int S = N >= 8192 ? 2 : 4;
+  const int S = dq_unsplit_order(N);
   return dq_seg_chunks(K, S) > 0 ? S : 0;
 }
 

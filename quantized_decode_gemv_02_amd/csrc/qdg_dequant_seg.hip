@@ -92,38 +92,18 @@ __device__ __forceinline__ void dq_fold(const DqStep& b, bool act, double (&acc)
   }
 }
 
-// The wave index is a scalar (readfirstlane), so the chunk bounds and the four
-// rows' pointers sit in SGPRs.  The operands stream through NB named step
-// buffers: buffer k's terms are taken, then it is refilled NB steps ahead, so
-// NB - 1 later steps stay in flight while a step is folded and no register copy
-// waits for a load.  The earlier loop loaded a step and waited for all of it
-// before its terms (one step in flight a wave), with a predicate that made every
-// load and term a branch.
-template <int R, int NB>
-__global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, const float* __restrict__ x, int64_t K,
-                                                        int S, int m, int ceff) {
-  constexpr int ROWS = 4 * R;
-  __shared__ double lpart[DS_NT / 64][4];  // [row group * ceff + chunk][row]
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = (int)(blockDim.x >> 6) / R;  // chunk waves a row group
-  const int rg = wave / W, cw = wave % W;
-  const int64_t nb = K / QK;
-  int64_t o_wg;
-  const int part = find_part(tab, (int)blockIdx.x, ROWS, o_wg);
-  const int8_t* __restrict__ wq = tab.wq[part];
-  const uint16_t* __restrict__ ws = tab.ws[part];
-  float* __restrict__ y = tab.y[part];
-  const int64_t N = tab.N[part];
-  const int8_t* wrow[4];
-  const uint16_t* srow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int64_t o = o_wg + rg * 4 + r;
-    if (o >= N) o = N - 1;
-    wrow[r] = wq + o * K;
-    srow[r] = ws + o * nb;
-  }
-  // the wave's chunks in turn: cw, cw + W, ... (chunks 0..m-1, then S-1)
+// The partials of one row group's chunks: the wave takes chunks cw, cw + W, ...
+// (chunks 0..m-1, then S-1) of the four rows at wrow/srow and leaves chunk c's
+// four partials in lp[c].  The operands stream through NB named step buffers:
+// buffer k's terms are taken, then it is refilled NB steps ahead, so NB - 1
+// later steps stay in flight while a step is folded and no register copy waits
+// for a load.  The earlier loop loaded a step and waited for all of it before
+// its terms (one step in flight a wave), with a predicate that made every load
+// and term a branch.
+template <int NB>
+__device__ __forceinline__ void dq_chunk_partials(const int8_t* const (&wrow)[4], const uint16_t* const (&srow)[4],
+                                                  const float* __restrict__ x, int64_t K, int S, int m, int ceff,
+                                                  int cw, int W, int lane, double (*lp)[4]) {
   const int nq = (int)(K >> 9), nbk = (int)(K / QK), per = (nq + S - 1) / S;  // K <= 2^31
   for (int c = cw; c < ceff; c += W) {
   int32_t g0, g1;
@@ -168,15 +148,79 @@ __global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, cons
   }
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lpart[rg * ceff + c][r] = acc[r];
+    for (int r = 0; r < 4; ++r) lp[c][r] = acc[r];
   }
   }
+}
+
+// The four rows from o of one matrix, clamped into its N rows (a clamped row's
+// partials are computed and never written).
+__device__ __forceinline__ void dq_rows(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, int64_t o,
+                                        const int8_t* (&wrow)[4], const uint16_t* (&srow)[4]) {
+  const int64_t nb = K / QK;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t q = o + r < N ? o + r : N - 1;
+    wrow[r] = wq + q * K;
+    srow[r] = ws + q * nb;
+  }
+}
+
+// The wave index is a scalar (readfirstlane), so the chunk bounds and the four
+// rows' pointers sit in SGPRs.
+template <int R, int NB>
+__global__ __launch_bounds__(DS_NT) void k_gemv_dq_seg(const PartTable tab, const float* __restrict__ x, int64_t K,
+                                                        int S, int m, int ceff) {
+  constexpr int ROWS = 4 * R;
+  __shared__ double lpart[DS_NT / 64][4];  // [row group * ceff + chunk][row]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = (int)(blockDim.x >> 6) / R;  // chunk waves a row group
+  const int rg = wave / W, cw = wave % W;
+  int64_t o_wg;
+  const int part = find_part(tab, (int)blockIdx.x, ROWS, o_wg);
+  float* __restrict__ y = tab.y[part];
+  const int64_t N = tab.N[part];
+  const int8_t* wrow[4];
+  const uint16_t* srow[4];
+  dq_rows(tab.wq[part], tab.ws[part], N, K, o_wg + rg * 4, wrow, srow);
+  dq_chunk_partials<NB>(wrow, srow, x, K, S, m, ceff, cw, W, lane, lpart + rg * ceff);
   __syncthreads();
   if (tid < ROWS && o_wg + tid < N) {
     const int g = tid >> 2, q = tid & 3;
     double a = 0.0;
     for (int cc = 0; cc < ceff; ++cc) a = __dadd_rn(a, lpart[g * ceff + cc][q]);
     y[o_wg + tid] = (float)a;
+  }
+}
+
+// The gate and up projections of four rows side by side (lane kernel library
+// page, GLU / lk_gemv_glu under the Dequant accumulator with a binary32
+// output): the first W waves take the gate's four rows, the next W the up's, each
+// row group in the chunk order of k_gemv_dq_seg, so g and u are the bits that
+// kernel writes at the same chunk count; four lanes then round both rows once
+// and write h = act(g) * u with the producer's glu_mul.
+template <int NB, int ACT>
+__global__ __launch_bounds__(DS_NT) void k_gemv_dq_glu(const int8_t* __restrict__ wg, const uint16_t* __restrict__ sg,
+                                                        const int8_t* __restrict__ wu, const uint16_t* __restrict__ su,
+                                                        int64_t F, int64_t K, const float* __restrict__ x, int S,
+                                                        int m, int ceff, float* __restrict__ h) {
+  __shared__ double lpart[DS_NT / 64][4];  // [matrix * ceff + chunk][row]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = (int)(blockDim.x >> 6) / 2;
+  const int rg = wave / W, cw = wave % W;
+  const int64_t o = (int64_t)blockIdx.x * 4;
+  const int8_t* wrow[4];
+  const uint16_t* srow[4];
+  dq_rows(rg ? wu : wg, rg ? su : sg, F, K, o, wrow, srow);
+  dq_chunk_partials<NB>(wrow, srow, x, K, S, m, ceff, cw, W, lane, lpart + rg * ceff);
+  __syncthreads();
+  if (tid < 4 && o + tid < F) {
+    double a = 0.0, b = 0.0;
+    for (int cc = 0; cc < ceff; ++cc) {
+      a = __dadd_rn(a, lpart[cc][tid]);
+      b = __dadd_rn(b, lpart[ceff + cc][tid]);
+    }
+    h[o + tid] = glu_mul<ACT>((float)a, (float)b);
   }
 }
 
@@ -227,6 +271,35 @@ hipError_t launch_ds(const PartTable& tab, int64_t K, const float* x, int S, int
   const int W = ds_waves<R>(wgs, K, S, m, ceff);
   const dim3 grid((unsigned)wgs), block((unsigned)(64 * R * W));
   return launch((k_gemv_dq_seg<R, DS_NB>), grid, block, 0, st, tab, x, K, S, m, ceff);
+}
+
+// The gate/up kernel's workgroups (two row groups of W chunk waves) a compute
+// unit holds at once, asked once an activation and W.
+template <int ACT>
+int dg_resident(int W) {
+  static std::atomic<int> cache[9];
+  int n = cache[W].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)k_gemv_dq_glu<DS_NB, ACT>, 128 * W, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      b = 1;
+    }
+    n = b > 0 ? b : 1;
+    cache[W].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int ACT>
+hipError_t launch_dg(const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su, int64_t F, int64_t K,
+                     const float* x, int S, int m, int ceff, float* h, hipStream_t st) {
+  const int64_t wgs = (F + 3) / 4;
+  const int W = pick_chunk_waves(wgs, 8, K, S, m, ceff, tune(QDG_TUNE_DQ_WAVES),
+                                 [](int w) { return dg_resident<ACT>(w); });
+  const dim3 grid((unsigned)wgs), block((unsigned)(128 * W));
+  return launch((k_gemv_dq_glu<DS_NB, ACT>), grid, block, 0, st, wg, sg, wu, su, F, K, x, S, m, ceff, h);
 }
 
 }  // namespace
@@ -287,6 +360,18 @@ hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const u
 hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K, const float* x, int splits,
                               float* y, hipStream_t st) {
   return launch_gemv_dq_seg_parts(1, &wq, &ws, &N, &y, K, x, splits, st);
+}
+
+// The gate and up projections of F rows with the gated product, S chunks a row
+// (at most 8 chunk partials a matrix: both sit in the workgroup's 16 slots).
+hipError_t launch_gemv_dq_glu(int act, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                              int64_t F, int64_t K, const float* x, int S, float* h, hipStream_t st) {
+  int m, ceff;
+  ds_chunks(K, S, m, ceff);
+  if (ceff < 1 || ceff > 8 || (F + 3) / 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (act == 0) return launch_dg<0>(wg, sg, wu, su, F, K, x, S, m, ceff, h, st);
+  if (act == 1) return launch_dg<1>(wg, sg, wu, su, F, K, x, S, m, ceff, h, st);
+  return launch_dg<2>(wg, sg, wu, su, F, K, x, S, m, ceff, h, st);
 }
 
 }  // namespace qdg

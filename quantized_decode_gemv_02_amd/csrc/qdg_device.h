@@ -565,6 +565,11 @@ hipError_t launch_gemv_dq_seg(const int8_t* wq, const uint16_t* ws, int64_t N, i
                               float* y, hipStream_t st);
 hipError_t launch_gemv_dq_seg_parts(int nparts, const int8_t* const* wq, const uint16_t* const* ws, const int64_t* N,
                                     float* const* y, int64_t K, const float* x, int splits, hipStream_t st);
+// the unsplit Dequant call's chunk count for N rows (qdg_dequant.hip), and the
+// gate/up kernel with the gated product in that order (qdg_dequant_seg.hip)
+int dq_unsplit_order(int64_t N);
+hipError_t launch_gemv_dq_glu(int act, const int8_t* wg, const uint16_t* sg, const int8_t* wu, const uint16_t* su,
+                              int64_t F, int64_t K, const float* x, int S, float* h, hipStream_t st);
 void wsplit_shape(int64_t K, int splits, int& rows, int& waves);
 // tiled: the weights in row tiles of four rows by 256 values (launch_tile_rows)
 hipError_t launch_gemv_wsplit(int mode, const int8_t* wq, const uint16_t* ws, int64_t N, int64_t K,

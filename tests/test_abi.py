@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 41
+    assert len(names) == 42
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -369,6 +369,37 @@ def test_glu_validation():
     assert call(hs=A + 2) == EALIGN
     assert call(mode=2, xl=A, hl=A, K=13216) == EMODE   # the activation and 64 rows of scales exceed LDS
     assert call(mode=1, K=15808) == EMODE
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_glu_dequant_validation(act):
+    """qdg_gemv_glu_dequant: each operand at an address of its own, then one bad argument
+    at a time; h may not overlap x, a weight matrix or a scale array."""
+    f = lib.qdg_gemv_glu_dequant
+    X, WG, WU, SG, SU, H = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    F, K = 128, 4096  # spans: x 16 KiB, weights 512 KiB, scales 32 KiB
+
+    def call(act=act, wg=WG, sg=SG, wu=WU, su=SU, F=F, K=K, x=X, h=H):
+        return f(act, P(wg), P(sg), P(wu), P(su), F, K, P(x), P(h), None)
+
+    assert call(act=3) == EINVAL and call(act=-1) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(h=None) == EINVAL
+    assert call(wu=None) == EINVAL and call(su=None) == EINVAL
+    assert call(F=0) == ESHAPE
+    assert call(K=48) == ESHAPE and call(K=0) == ESHAPE
+    assert call(F=1 << 33, K=32) == ESHAPE              # more than 2^31 four-row workgroups
+    assert call(wg=WG + 8) == EALIGN
+    assert call(wu=WU + 8) == EALIGN
+    assert call(sg=SG + 1) == EALIGN
+    assert call(x=X + 4) == EALIGN
+    assert call(h=H + 2) == EALIGN
+    assert call(h=X + 16) == EINVAL                     # h over x
+    assert call(h=X - 4 * F + 4) == EINVAL              # h's last value on x's first
+    assert call(h=WU + 0x80000 - 4) == EINVAL           # h's first value on the up matrix's last word
+    assert call(h=SG + 0x8000 - 4) == EINVAL
+    assert call(h=SU) == EINVAL
+    assert call(h=WG, act=act, F=F) == EINVAL
 
 
 def test_fmt_validation():

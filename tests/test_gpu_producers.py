@@ -406,3 +406,72 @@ def test_glu_act_matches_the_three_calls(act, mode, F, K):
     gh = host(h).reshape(1, F)
     check_f32(gh, oracle.glu(act, og, ou), f"glu act {act} h")
     check_words(mode, gh, hq.view(1, F), None if hl is None else hl.view(1, F), hs.view(1, F // 32), "glu act")
+
+
+def glu_dequant_three_calls(act, dwg, dsg, dwu, dsu, dx, F):
+    """g and u by two qdg_gemv_q8 Dequant calls, h by qdg_glu_quantize under
+    Dequant over g and u padded with zeros to whole 32-value blocks."""
+    K = dx.numel()
+    g = torch.full((1, F), float("nan"), dtype=torch.float32, device=DEV)
+    u = torch.full((1, F), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8(0, dwg, dsg, g, x=dx.view(1, K))
+    q.gemv_q8(0, dwu, dsu, u, x=dx.view(1, K))
+    Fp = -(-F // 32) * 32
+    gp = torch.zeros((1, Fp), dtype=torch.float32, device=DEV)
+    up = torch.zeros((1, Fp), dtype=torch.float32, device=DEV)
+    gp[:, :F], up[:, :F] = g, u
+    h = torch.empty((1, Fp), dtype=torch.float32, device=DEV)
+    q.glu_quantize(act, 0, gp, up, h)
+    return host(g)[0], host(u)[0], host(h)[0, :F]
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+@pytest.mark.parametrize("F,K", [(32, 32), (3, 544), (7, 1536), (101, 4096), (5120, 5120), (8191, 1056),
+                                 (8192, 1056), (12289, 800), (25600, 5120)])
+def test_glu_dequant_matches_the_three_calls(act, F, K):
+    """qdg_gemv_glu_dequant against two qdg_gemv_q8 Dequant calls and qdg_glu_quantize,
+    bit for bit (both sides of the 8192-row change of chunk count, ragged F, K with
+    a tail past the last 512-value superblock); the calls' g and u within the Dequant
+    tolerance of the binary64 reference, h within one ulp of the oracle's gated
+    product of them."""
+    announce(f"gemv_glu_dequant act={act} F={F} K={K}")
+    wg, sg = workloads.weights(F, K, 181 + K + F, 182 + K)
+    wu, su = workloads.weights(F, K, 183 + K + F, 184 + K)
+    x = workloads.activation(K, 185 + K, True, 186 + K)
+    dwg, dsg = dev(wg), dev(sg.view(np.int16))
+    dwu, dsu = dev(wu), dev(su.view(np.int16))
+    dx = dev(x)
+    h = torch.full((F,), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_glu_dequant(act, dwg, dsg, dwu, dsu, dx, h)
+    gh, uh, want = glu_dequant_three_calls(act, dwg, dsg, dwu, dsu, dx, F)
+    got = host(h)
+    assert got.view(np.int32).tobytes() == want.view(np.int32).tobytes()
+    for w, s, y in ((wg, sg, gh), (wu, su, uh)):
+        Y, tn = oracle.reference_f64(0, w, s, x=x[None, :], nthreads=16)
+        assert oracle.within_tolerance(y[None, :], Y, tn).all()
+    check_f32(got[None, :], oracle.glu(act, gh[None, :], uh[None, :]), f"glu dequant act {act}")
+    # a repeat gives the same bytes
+    h2 = torch.full((F,), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_glu_dequant(act, dwg, dsg, dwu, dsu, dx, h2)
+    assert host(h2).tobytes() == got.tobytes()
+
+
+def test_glu_dequant_h_beside_x():
+    """h may sit right after x in one buffer; one value over x is refused before any launch."""
+    announce("gemv_glu_dequant h beside x")
+    F, K = 96, 1024
+    wg, sg = workloads.weights(F, K, 191, 192)
+    wu, su = workloads.weights(F, K, 193, 194)
+    x = workloads.activation(K, 195, True, 196)
+    dwg, dsg = dev(wg), dev(sg.view(np.int16))
+    dwu, dsu = dev(wu), dev(su.view(np.int16))
+    buf = torch.full((K + F,), float("nan"), dtype=torch.float32, device=DEV)
+    buf[:K] = dev(x)
+    q.gemv_glu_dequant(0, dwg, dsg, dwu, dsu, buf[:K], buf[K:])
+    alone = torch.empty((F,), dtype=torch.float32, device=DEV)
+    q.gemv_glu_dequant(0, dwg, dsg, dwu, dsu, dev(x), alone)
+    assert host(buf[K:]).tobytes() == host(alone).tobytes()
+    assert host(buf[:K]).tobytes() == x.tobytes()
+    with pytest.raises(q.QdgError) as e:
+        q.gemv_glu_dequant(0, dwg, dsg, dwu, dsu, buf[:K], buf[K - 1:K - 1 + F])
+    assert e.value.status == -1
