@@ -599,11 +599,18 @@ def main() -> int:
         # the same batch over MFMA-ordered operands: the weights repacked once
         # (qdg_q8_tile_mma), the activations quantized into the MFMA order
         # (qdg_quantize_act_mma, timed beside), the GEMV qdg_gemv_q8_mma_tiled
-        tiles = []
+        tiles, halves = [], []
+        F = sh.N // 2
         for w, s in wsets:
             wt = torch.empty(q.q8_tile_mma_bytes(sh.N, sh.K), dtype=torch.uint8, device=dev)
             q.q8_tile_mma(w, s, wt)
             tiles.append(wt)
+            pair = []
+            for lo in (0, F):  # the gate rows, then the up rows, each repacked on its own
+                ht = torch.empty(q.q8_tile_mma_bytes(F, sh.K), dtype=torch.uint8, device=dev)
+                q.q8_tile_mma(w[lo:lo + F], s[lo:lo + F], ht)
+                pair.append(ht)
+            halves.append(pair)
         del wsets
         torch.cuda.empty_cache()
         tiled = {}
@@ -629,9 +636,46 @@ def main() -> int:
             calls = [q.bind_gemv_q8_mma_tiled(mode, wt, sh.N, sh.K, y, tq, tl, ts, PB) for wt in tiles]
             b = alg_bytes(mode, sh.N, sh.K, PB)
             prefill["mma_tiled"][NAMES[mode]] = {"B": PB, "alg_bytes": b, **rate(b, timer.median_us(calls, args.launches))}
+        # the two halves as gate and up with the SwiGLU and the quantizer into the down
+        # projection's MFMA-ordered words (qdg_gemv_glu_mma_tiled), against the four calls it
+        # equals: two tiled GEMVs, the producer (f32 h) and the MFMA-order quantizer
+        glu = {}
+        for mode in (1, 2):
+            for Bg in (sh.B, PB):
+                xg = x if Bg == sh.B else xp
+                Rg = q.mma_act_rows(Bg)
+                tq = torch.empty(Rg * sh.K, dtype=torch.int8, device=dev)
+                tl = torch.empty(Rg * sh.K, dtype=torch.int8, device=dev) if mode == 2 else None
+                ts = torch.empty(Rg * (sh.K // 32), dtype=torch.float32, device=dev)
+                q.quantize_act_mma(mode, xg, tq, tl, ts)
+                hq = torch.empty(Rg * F, dtype=torch.int8, device=dev)
+                hl = torch.empty(Rg * F, dtype=torch.int8, device=dev) if mode == 2 else None
+                hs = torch.empty(Rg * (F // 32), dtype=torch.float32, device=dev)
+                fused = [q.bind_gemv_glu_mma_tiled(0, mode, a, b, F, sh.K, tq, tl, ts, Bg, hq, hl, hs)
+                         for a, b in halves]
+                g = torch.empty((Bg, F), dtype=torch.float32, device=dev)
+                u = torch.empty_like(g)
+                hf = torch.empty_like(g)
+                gcalls = [q.bind_gemv_q8_mma_tiled(mode, a, F, sh.K, g, tq, tl, ts, Bg) for a, _ in halves]
+                ucalls = [q.bind_gemv_q8_mma_tiled(mode, b, F, sh.K, u, tq, tl, ts, Bg) for _, b in halves]
+                prod = q.bind_glu_quantize(0, 0, g, u, hf)
+                qcall = q.bind_quantize_act_mma(mode, hf, hq, hl, hs)
+                f_us = timer.median_us(fused, args.launches)
+                g_us = timer.median_us(gcalls, args.launches)
+                p_us = timer.median_us([prod], args.launches)
+                q_us = timer.median_us([qcall], args.launches)
+                four = [lambda a=a, b=b: (a(), b(), prod(), qcall()) for a, b in zip(gcalls, ucalls)]
+                nb = 2 * (F * sh.K + F * sh.K // 16) + Bg * {1: sh.K + sh.K // 8, 2: 2 * sh.K + sh.K // 8}[mode] \
+                    + Bg * {1: F + F // 8, 2: 2 * F + F // 8}[mode]
+                glu[f"{NAMES[mode]}_B{Bg}"] = {
+                    "F": F, "fused_us": round(f_us, 2), "gemv_us": round(g_us, 2), "producer_us": round(p_us, 2),
+                    "quantize_us": round(q_us, 2), "four_calls_us": round(2 * g_us + p_us + q_us, 2),
+                    "fused_wall_us": round(timer.wall_us(fused, args.launches), 2),
+                    "four_calls_wall_us": round(timer.wall_us(four, args.launches), 2), **rate(nb, f_us)}
+        rec["glu_mma_tiled"] = glu
         configs[f"batched_B{sh.B}_{sh.N}x{sh.K}"] = rec
         configs[f"prefill_B{PB}_{sh.N}x{sh.K}"] = prefill
-        del tiles
+        del tiles, halves
         torch.cuda.empty_cache()
         progress("batched done")
 

@@ -594,6 +594,30 @@ int qdg_gemv_q8_mma_tiled(int mode, const uint8_t *wt, int64_t N, int64_t K, con
                           qdg_stream stream);
 
 /*
+ * The gate and up projections of 1 <= B <= QDG_MAX_B activation rows with the
+ * gated product and the quantizer as the epilogue, in one launch (lane kernel
+ * library page, GLU: lk_gemv_glu with a quantized output and its ACT; lk_act),
+ * over MFMA-tiled gate and up weights wgt, wut (qdg_q8_tile_mma of Wg, Wu, each
+ * [F][K]) and MFMA-ordered activations xq, xl, xs (qdg_quantize_act_mma with the
+ * same B).  g = Wg x and u = Wu x as qdg_gemv_q8_mma_tiled computes them with
+ * splits 1, h = act(g) * u as qdg_glu_quantize computes it, and h quantized in
+ * the same mode and written in the MFMA order of qdg_quantize_act_mma for a
+ * projection with K = F: hq (and hl under QDG_TWOPASS) 16*T*F bytes, hs
+ * 16*T*F/32 floats, T as qdg_quantize_act_mma for B, rows B..16*T-1 those of a
+ * zero row.  So (hq, hl, hs) are the bytes of qdg_gemv_q8_mma_tiled twice,
+ * qdg_glu_quantize (h) and qdg_quantize_act_mma on h -- the down projection's
+ * operands -- and h [B][F] (optional, NULL to skip) the producer's h, bit for
+ * bit; g and u never reach memory.  act one of QDG_ACT_*, mode QDG_INT8ACT or
+ * QDG_TWOPASS (xl, hl NULL under QDG_INT8ACT), else QDG_EINVAL.  K as
+ * qdg_q8_tile_mma and F a positive multiple of 256 (the down projection's K),
+ * else QDG_ESHAPE.  wgt, wut, xq, xl, h 16-byte aligned; xs, hq, hl, hs 4-byte.
+ * No output may overlap an input (QDG_EINVAL).  Needs no workspace.
+ */
+int qdg_gemv_glu_mma_tiled(int act, int mode, const uint8_t *wgt, const uint8_t *wut, int64_t F,
+                           int64_t K, const int8_t *xq, const int8_t *xl, const float *xs, int64_t B,
+                           float *h, int8_t *hq, int8_t *hl, float *hs, qdg_stream stream);
+
+/*
  * Tuning and test hooks.  Process-wide settings that choose among the library's
  * kernels, staging forms and launch shapes for the same call -- never the
  * arithmetic or its order, so every setting gives the same output bits -- for

@@ -90,6 +90,7 @@ _SIGS = {
     "qdg_gemv_glu_q8": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_glu_act_q8": ([_I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "qdg_gemv_glu_dequant": ([_I, _P, _P, _P, _P, _I64, _I64, _P, _P, _P], _I),
+    "qdg_gemv_glu_mma_tiled": ([_I, _I, _P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P], _I),
     "qdg_fmt_row_bytes": ([_I, _I64], _I64),
     "qdg_gemv_fmt": ([_I, _I, _P, _I64, _I64, _P, _P, _P, _P, _I, _P, _P], _I),
     "qdg_gemv_fmt_chunk_waves": ([_I, _I, _I64, _I64, _I], _I),
@@ -526,6 +527,33 @@ def gemv_q8_mma_tiled(mode: int, wt, N: int, K: int, out, xq, xl, xs, B: int, sp
     _check("qdg_gemv_q8_mma_tiled", _lib.qdg_gemv_q8_mma_tiled(
         mode, _ptr(wt, _u8(), "wt"), N, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"),
         B, int(splits), _ptr(out, _f32(), "out"), _stream()))
+
+
+def _glu_mma_args(act, mode, wgt, wut, F, K, xq, xl, xs, B, hq, hl, hs, h):
+    R = mma_act_rows(B)
+    _need(xq=(xq, R * K), xl=(xl, R * K), xs=(xs, R * (K // QK)), hq=(hq, R * F), hl=(hl, R * F),
+          hs=(hs, R * (F // QK)))
+    if h is not None:
+        _need(h=(h, B * F))
+    _need(wgt=(wgt, q8_tile_mma_bytes(F, K) // wgt.element_size()), wut=(wut, q8_tile_mma_bytes(F, K) // wut.element_size()))
+    return (act, mode, _ptr(wgt, _u8(), "wgt"), _ptr(wut, _u8(), "wut"), F, K, _ptr(xq, _i8(), "xq"),
+            _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), B, _ptr(h, _f32(), "h"), _ptr(hq, _i8(), "hq"),
+            _ptr(hl, _i8(), "hl"), _ptr(hs, _f32(), "hs"), _stream())
+
+
+def gemv_glu_mma_tiled(act: int, mode: int, wgt, wut, F: int, K: int, xq, xl, xs, B: int, hq, hl, hs,
+                       h=None) -> None:
+    """Gate and up GEMVs of B <= 64 rows over MFMA-tiled weights (``q8_tile_mma`` of each ``[F][K]``
+    matrix) and MFMA-ordered activations, with the gated product and the quantizer as the epilogue:
+    ``(hq, hl, hs)`` hold ``act(g) * u`` quantized in the MFMA order ``quantize_act_mma`` writes for
+    K = F (``mma_act_rows(B)*F`` words, ``mma_act_rows(B)*F/32`` scales); ``h`` (optional) is ``[B][F]``."""
+    _check("qdg_gemv_glu_mma_tiled", _lib.qdg_gemv_glu_mma_tiled(
+        *_glu_mma_args(act, mode, wgt, wut, F, K, xq, xl, xs, B, hq, hl, hs, h)))
+
+
+def bind_gemv_glu_mma_tiled(act: int, mode: int, wgt, wut, F: int, K: int, xq, xl, xs, B: int, hq, hl, hs,
+                            h=None) -> Bound:
+    return Bound("qdg_gemv_glu_mma_tiled", *_glu_mma_args(act, mode, wgt, wut, F, K, xq, xl, xs, B, hq, hl, hs, h))
 
 
 def gemv_q8_fused(mode: int, wq, ws, y, x, splits: int = 1, workspace=None) -> None:

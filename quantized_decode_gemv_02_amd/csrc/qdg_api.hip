@@ -223,6 +223,36 @@ int qdg_gemv_q8_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, con
   return hip_status(qdg::launch_gemv_mma_tiled(mode, wt, N, K, xq, xl, xs, B, splits, out, as_stream(stream)));
 }
 
+int qdg_gemv_glu_mma_tiled(int act, int mode, const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K,
+                           const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, float* h, int8_t* hq,
+                           int8_t* hl, float* hs, qdg_stream stream) {
+  if (act < QDG_ACT_SILU || act > QDG_ACT_GELU_TANH) return QDG_EINVAL;
+  if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
+  if (!wgt || !wut || !xq || !xs || !hq || !hs) return QDG_EINVAL;
+  if ((mode == QDG_TWOPASS) != (xl != nullptr) || (mode == QDG_TWOPASS) != (hl != nullptr)) return QDG_EINVAL;
+  if (!mma_tiled_shape(F, K) || F % 256 != 0 || F >= ((int64_t)1 << 30)) return QDG_ESHAPE;
+  if (B < 1 || B > QDG_MAX_B) return QDG_ESHAPE;
+  if (!aligned(wgt, 16) || !aligned(wut, 16) || !aligned(xq, 16) || (xl && !aligned(xl, 16)) || !aligned(xs, 4) ||
+      (h && !aligned(h, 16)) || !aligned(hq, 4) || (hl && !aligned(hl, 4)) || !aligned(hs, 4))
+    return QDG_EALIGN;
+  // the outputs are written while other workgroups still read the inputs
+  const int64_t T = qdg::mma_act_tiles(B), wb = qdg::tile_mma_bytes(F, K);
+  const uintptr_t in[5][2] = {{(uintptr_t)wgt, (uintptr_t)wgt + (uintptr_t)wb},
+                              {(uintptr_t)wut, (uintptr_t)wut + (uintptr_t)wb},
+                              {(uintptr_t)xq, (uintptr_t)xq + (uintptr_t)(16 * T * K)},
+                              {(uintptr_t)xl, xl ? (uintptr_t)xl + (uintptr_t)(16 * T * K) : (uintptr_t)xl},
+                              {(uintptr_t)xs, (uintptr_t)xs + (uintptr_t)(16 * T * (K / qdg::QK)) * 4}};
+  const uintptr_t out[4][2] = {{(uintptr_t)h, h ? (uintptr_t)h + (uintptr_t)(B * F) * 4 : (uintptr_t)h},
+                               {(uintptr_t)hq, (uintptr_t)hq + (uintptr_t)(16 * T * F)},
+                               {(uintptr_t)hl, hl ? (uintptr_t)hl + (uintptr_t)(16 * T * F) : (uintptr_t)hl},
+                               {(uintptr_t)hs, (uintptr_t)hs + (uintptr_t)(16 * T * (F / qdg::QK)) * 4}};
+  for (const auto& a : in)
+    for (const auto& b : out)
+      if (a[0] < b[1] && b[0] < a[1]) return QDG_EINVAL;  // an empty span (NULL) meets nothing
+  return hip_status(
+      qdg::launch_gemv_glu_mma(act, mode, wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, as_stream(stream)));
+}
+
 int qdg_gemv_sk_combines_in_workgroup(int mode, int64_t K, int splits, int32_t* shape) {
   if (mode != QDG_INT8ACT && mode != QDG_TWOPASS) return QDG_EINVAL;
   if (K < qdg::QK || K % qdg::QK || splits < 1 || splits > QDG_MAX_SPLITS) return QDG_ESHAPE;

@@ -596,6 +596,10 @@ hipError_t launch_quantize_mma(int mode, const float* x, int64_t B, int64_t K, i
 hipError_t launch_gemv_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq,
                                  const int8_t* xl, const float* xs, int64_t B, int splits, float* out,
                                  hipStream_t st);
+int mma_act_tiles(int64_t B);
+hipError_t launch_gemv_glu_mma(int act, int mode, const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K,
+                               const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, float* h, int8_t* hq,
+                               int8_t* hl, float* hs, hipStream_t st);
 int64_t rmsnorm_max_k();
 hipError_t launch_rmsnorm_quant(int mode, const float* x, const float* r, float* s, const float* w, float eps,
                                 int64_t B, int64_t K, float* y, int8_t* xq, int8_t* xl, float* xs, hipStream_t st);

@@ -183,6 +183,51 @@ __device__ __forceinline__ void mt_terms(const MtStep<MODE, TPW, AT>& b, int m0,
   }
 }
 
+// A wave's partials over its chunk: nsteps steps from record rec0 and
+// activation records xa0 / xla0 / xsa0, tiles m0.. of the record group, P - 1
+// steps in flight (named step buffers; past the chunk a load repeats its last
+// step, so every step issues the same loads and the wait counts stay exact).
+template <int MODE, int TPW, int P, int AT>
+__device__ __forceinline__ void mt_partials(const uint8_t* rec0, const int8_t* xa0, const int8_t* xla0,
+                                            const float* xsa0, int nsteps, int m0, int64_t K,
+                                            float (&p)[TPW][AT][4]) {
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+#pragma unroll
+    for (int at = 0; at < AT; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[m][at][i] = 0.0f;
+
+  if (nsteps > 0) {
+    auto load = [&](MtStep<MODE, TPW, AT>& b, int st) {
+      const int64_t k = st < nsteps ? st : nsteps - 1;  // past the chunk: its last step again
+      mt_load<MODE, TPW, AT>(b, rec0 + k * 4 * MT_REC, m0, xa0 + k * 4096, MODE == 2 ? xla0 + k * 4096 : nullptr,
+                             xsa0 + k * 128, K);
+    };
+    MtStep<MODE, TPW, AT> b[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) load(b[k], k);
+    int st = 0;
+    // while every refill is due
+    for (; st + 2 * P - 1 < nsteps; st += P) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        mt_terms<MODE, TPW, AT>(b[k], m0, p);
+        load(b[k], st + k + P);
+      }
+    }
+    // the last 1 .. 2P - 1 steps, in order
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      if (st + k < nsteps) mt_terms<MODE, TPW, AT>(b[k], m0, p);
+      if (st + k + P < nsteps) load(b[k], st + k + P);
+    }
+#pragma unroll
+    for (int k = 0; k + 1 < P; ++k)
+      if (st + P + k < nsteps) mt_terms<MODE, TPW, AT>(b[k], m0, p);
+  }
+}
+
 // Grid (workgroup row blocks of 64*GW rows, splits), 4 * (4*GW / TPW) waves a
 // workgroup, AT activation tiles of 16 rows (B <= 16 * AT).  out [splits][B][N].
 template <int MODE, int TPW, int P, int GW, int AT>
@@ -274,6 +319,73 @@ __global__ __launch_bounds__(256 * (4 * GW / TPW)) void k_gemv_mma_tiled(const u
   }
 }
 
+// The gate and up projections of a batch with the gated product and the
+// quantizer as the epilogue (lane kernel library page, GLU / lk_gemv_glu with a
+// quantized output, here for up to 64 activation rows): workgroup q's first
+// four waves sum record group q of the gate records, the next four the same
+// group of the up records, exactly as k_gemv_mma_tiled sums them unsplit.  Per
+// activation tile the eight waves' partials meet in LDS; four waves then form,
+// for each of the tile's 16 rows and the group's two 32-row blocks of outputs,
+// g and u in that kernel's order, h = act(g) * u with the producer's glu_mul
+// (+0 for a row past the batch), and quantize each 32-value block with eight
+// lanes as the quantizer does -- writing the words in the activation record
+// order of qdg_quantize_act_mma for a projection with K = F.  h [B][F] is
+// written too when asked for.  Grid F / 64, 512 threads.
+template <int MODE, int P, int AT, int ACT>
+__global__ __launch_bounds__(512) void k_gemv_mma_glu(const uint8_t* __restrict__ wgt, const uint8_t* __restrict__ wut,
+                                                      const int8_t* __restrict__ xq, const int8_t* __restrict__ xl,
+                                                      const float* __restrict__ xs, int64_t F, int64_t K, int B,
+                                                      float* __restrict__ h, int8_t* __restrict__ hq,
+                                                      int8_t* __restrict__ hl, float* __restrict__ hs) {
+  __shared__ float red[8][4][4][64];  // [wave][tile][i][lane], one activation tile at a time
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = wave & 3, g = wave >> 2;  // g = 0 gate, 1 up
+  const int64_t nst = K / 256, q = blockIdx.x;
+  const uint8_t* rec0 = (g ? wut : wgt) + (q * nst * 4 + r) * (int64_t)MT_REC;
+  const int8_t* xa0 = xq + (int64_t)r * 1024;
+  const int8_t* xla0 = MODE == 2 ? xl + (int64_t)r * 1024 : nullptr;
+  const float* xsa0 = xs + (int64_t)r * 32;
+  float p[4][AT][4];
+  mt_partials<MODE, 4, P, AT>(rec0, xa0, xla0, xsa0, (int)nst, 0, K, p);
+
+  // block bk of the group's 32 (16 tile rows x 2 output blocks), lane sub of its eight
+  const int bk = 8 * (wave & 3) + (lane >> 3), tt = bk >> 1, half = bk & 1, sub = lane & 7;
+  const int64_t b = 2 * q + half;                // output block along F
+  const int64_t rs = (b >> 3) * 4 + (b & 3);     // its activation record (s, r) for K = F
+  const int hh = (int)((b >> 2) & 1);
+#pragma unroll
+  for (int at = 0; at < AT; ++at) {
+    if (at > 0) __syncthreads();  // the previous tile's reads are done
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][m][i][lane] = p[m][at][i];
+    __syncthreads();
+    if (wave < 4) {
+      const int t = 16 * at + tt;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = 32 * half + 4 * sub + j;  // row of the group
+        const int m = o >> 4, i = tt & 3, ln = (o & 15) + 16 * (tt >> 2);
+        const float gv = __fadd_rn(__fadd_rn(red[0][m][i][ln], red[2][m][i][ln]),
+                                   __fadd_rn(red[1][m][i][ln], red[3][m][i][ln]));
+        const float uv = __fadd_rn(__fadd_rn(red[4][m][i][ln], red[6][m][i][ln]),
+                                   __fadd_rn(red[5][m][i][ln], red[7][m][i][ln]));
+        v[j] = t < B ? glu_mul<ACT>(gv, uv) : 0.0f;
+      }
+      const float4 v4 = make_float4(v[0], v[1], v[2], v[3]);
+      if (h && t < B) *(float4*)(h + (int64_t)t * F + 64 * q + 32 * half + 4 * sub) = v4;
+      int wh, wl;
+      const float sc = quant_lane4<MODE>(v4, &wh, &wl);
+      const int64_t off = at * 16 * F + (rs * 64 + 16 * (sub >> 1) + tt) * 16 + 8 * hh + 4 * (sub & 1);
+      *(int*)(hq + off) = wh;
+      if constexpr (MODE == 2) *(int*)(hl + off) = wl;
+      if (sub == 0) hs[at * (F / 2) + rs * 32 + 16 * hh + tt] = sc;
+    }
+  }
+}
+
 // Steps in flight: P - 1 ahead of the one being summed (P = 4 measured best
 // against 3 and 5 on 25600x5120, B = 16).
 constexpr int MT_P = 4;
@@ -313,6 +425,33 @@ hipError_t launch_mt(const uint8_t* wt, int64_t N, int64_t K, const int8_t* xq, 
   }
 }
 
+template <int MODE, int AT, int ACT>
+hipError_t launch_mga(const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K, const int8_t* xq,
+                      const int8_t* xl, const float* xs, int64_t B, float* h, int8_t* hq, int8_t* hl, float* hs,
+                      hipStream_t st) {
+  constexpr int P = AT == 1 ? MT_P : AT == 2 ? 3 : 2;
+  return launch((k_gemv_mma_glu<MODE, P, AT, ACT>), dim3((unsigned)(F / MT_ROWS)), dim3(512), 0, st, wgt, wut, xq,
+                xl, xs, F, K, (int)B, h, hq, hl, hs);
+}
+
+template <int MODE, int ACT>
+hipError_t launch_mg(const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K, const int8_t* xq, const int8_t* xl,
+                     const float* xs, int64_t B, float* h, int8_t* hq, int8_t* hl, float* hs, hipStream_t st) {
+  switch (mt_tiles(B)) {
+    case 1: return launch_mga<MODE, 1, ACT>(wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+    case 2: return launch_mga<MODE, 2, ACT>(wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+    default: return launch_mga<MODE, 4, ACT>(wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+  }
+}
+
+template <int ACT>
+hipError_t launch_mg_a(int mode, const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K, const int8_t* xq,
+                       const int8_t* xl, const float* xs, int64_t B, float* h, int8_t* hq, int8_t* hl, float* hs,
+                       hipStream_t st) {
+  if (mode == 1) return launch_mg<1, ACT>(wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+  return launch_mg<2, ACT>(wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+}
+
 template <int MODE>
 hipError_t launch_qm(const float* x, int64_t B, int64_t K, int8_t* xq, int8_t* xl, float* xs, hipStream_t st) {
   const int AT = mt_tiles(B);
@@ -347,6 +486,16 @@ hipError_t launch_gemv_mma_tiled(int mode, const uint8_t* wt, int64_t N, int64_t
                    : launch_mt<1, 1>(wt, N, K, xq, xl, xs, B, splits, out, st);
   return gw == 2 ? launch_mt<2, 2>(wt, N, K, xq, xl, xs, B, splits, out, st)
                  : launch_mt<2, 1>(wt, N, K, xq, xl, xs, B, splits, out, st);
+}
+
+int mma_act_tiles(int64_t B) { return mt_tiles(B); }
+
+hipError_t launch_gemv_glu_mma(int act, int mode, const uint8_t* wgt, const uint8_t* wut, int64_t F, int64_t K,
+                               const int8_t* xq, const int8_t* xl, const float* xs, int64_t B, float* h, int8_t* hq,
+                               int8_t* hl, float* hs, hipStream_t st) {
+  if (act == 0) return launch_mg_a<0>(mode, wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+  if (act == 1) return launch_mg_a<1>(mode, wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
+  return launch_mg_a<2>(mode, wgt, wut, F, K, xq, xl, xs, B, h, hq, hl, hs, st);
 }
 
 }  // namespace qdg

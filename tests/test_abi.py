@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 42
+    assert len(names) == 43
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(q.EXPORTS)
@@ -400,6 +400,37 @@ def test_glu_dequant_validation(act):
     assert call(h=SG + 0x8000 - 4) == EINVAL
     assert call(h=SU) == EINVAL
     assert call(h=WG, act=act, F=F) == EINVAL
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_glu_mma_tiled_validation(act):
+    """qdg_gemv_glu_mma_tiled: operands at addresses of their own, one bad argument at a time;
+    no output may overlap an input."""
+    f = lib.qdg_gemv_glu_mma_tiled
+    WG, WU, XQ, XL, XS, H, HQ, HL, HS = (0x1000000 * (i + 1) for i in range(9))
+    F, K, B = 512, 1024, 16  # records (512/64)*(1024/256)*4*4352 = 557056 bytes; words 16*K bytes
+
+    def call(act=act, mode=1, wgt=WG, wut=WU, F=F, K=K, xq=XQ, xl=None, xs=XS, B=B, h=H, hq=HQ, hl=None, hs=HS):
+        return f(act, mode, P(wgt), P(wut), F, K, P(xq), P(xl), P(xs), B, P(h), P(hq), P(hl), P(hs), None)
+
+    assert call(act=3) == EINVAL and call(act=-1) == EINVAL
+    assert call(mode=0) == EINVAL and call(mode=3) == EINVAL
+    assert call(wut=None) == EINVAL and call(hq=None) == EINVAL and call(hs=None) == EINVAL
+    assert call(mode=2, xl=XL) == EINVAL                # TwoPass needs hl too
+    assert call(mode=1, hl=HL) == EINVAL
+    assert call(F=320) == ESHAPE                        # F a multiple of 256
+    assert call(K=288) == ESHAPE and call(K=0) == ESHAPE
+    assert call(B=0) == ESHAPE and call(B=65) == ESHAPE
+    assert call(wgt=WG + 8) == EALIGN
+    assert call(xq=XQ + 4) == EALIGN
+    assert call(h=H + 4) == EALIGN
+    assert call(hq=HQ + 2) == EALIGN
+    assert call(mode=2, xl=XL, hl=HL + 1) == EALIGN
+    assert call(hq=XQ + 16 * K - 4) == EINVAL          # hq's first word on xq's last
+    assert call(hs=XS) == EINVAL
+    assert call(h=WU + 557056 - 16) == EINVAL          # h on the up records' last bytes
+    assert call(mode=2, xl=XL, hl=XL + 64) == EINVAL
+    assert call(hq=WG - 16 * F + 4) == EINVAL          # hq's last word on the gate records' first
 
 
 def test_fmt_validation():

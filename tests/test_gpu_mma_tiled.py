@@ -226,3 +226,137 @@ def test_mma_tiled_prefill_full(mode, B):
     y16 = torch.full((16, N), float("nan"), dtype=torch.float32, device=DEV)
     q.gemv_q8_mma_tiled(mode, wt, N, K, y16, tq16, tl16, ts16, 16)
     assert host(y16).tobytes() == got[:16].tobytes()
+
+
+def ulp_diff(a, b):
+    """Distance in binary32 units in the last place (sign-magnitude bit patterns)."""
+    def key(v):
+        i = np.asarray(v, np.float32).view(np.int32).astype(np.int64)
+        return np.where(i < 0, -(i & 0x7fffffff), i)
+    return np.abs(key(a) - key(b))
+
+
+def glu_outputs(mode, B, F, fill=True):
+    R = q.mma_act_rows(B)
+    hq = torch.full((R * F,), 77, dtype=torch.int8, device=DEV)
+    hl = torch.full((R * F,), 77, dtype=torch.int8, device=DEV) if mode == 2 else None
+    hs = torch.full((R * (F // 32),), float("nan"), dtype=torch.float32, device=DEV)
+    return hq, hl, hs
+
+
+def glu_three_calls(act, mode, wgt, wut, F, K, tq, tl, ts, B):
+    """g and u by qdg_gemv_q8_mma_tiled, h by qdg_glu_quantize (f32 only), h's words
+    by qdg_quantize_act_mma."""
+    g = torch.full((B, F), float("nan"), dtype=torch.float32, device=DEV)
+    u = torch.full((B, F), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wgt, F, K, g, tq, tl, ts, B)
+    q.gemv_q8_mma_tiled(mode, wut, F, K, u, tq, tl, ts, B)
+    h = torch.empty((B, F), dtype=torch.float32, device=DEV)
+    q.glu_quantize(act, 0, g, u, h)
+    rq, rl, rs = glu_outputs(mode, B, F)
+    q.quantize_act_mma(mode, h, rq, rl, rs)
+    return g, u, h, rq, rl, rs
+
+
+GLU_CASES = [(1, 256, 256), (5, 512, 768), (16, 768, 1024), (17, 256, 512), (33, 512, 256), (64, 256, 1280),
+             (16, 1280, 5120)]
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B,F,K", GLU_CASES)
+def test_glu_mma_tiled(B, F, K, mode, act):
+    """qdg_gemv_glu_mma_tiled: h and its MFMA-ordered words equal two tiled GEMVs, the
+    producer and the MFMA-order quantizer bit for bit; g and u of those calls equal the
+    oracle's, h is within one ulp of the oracle's gated product of them, and the words
+    are the oracle quantizer's on the kernel's h in the header's order (zero rows past
+    the batch).  Without h the words are the same."""
+    announce(f"gemv_glu_mma_tiled act={act} mode={mode} B={B} F={F} K={K}")
+    wg, sg = workloads.weights(F, K, 7 * F + K, 7 * F + K + 1)
+    wu, su = workloads.weights(F, K, 9 * F + K, 9 * F + K + 1)
+    x = workloads.batch_activation(B, K, 11 * B + K, True, 12 * B + K)
+    wgt, wut = tile(wg, sg), tile(wu, su)
+    tq, tl, ts = acts(mode, x)
+    hq, hl, hs = glu_outputs(mode, B, F)
+    h = torch.full((B, F), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_glu_mma_tiled(act, mode, wgt, wut, F, K, tq, tl, ts, B, hq, hl, hs, h=h)
+    g, u, h2, rq, rl, rs = glu_three_calls(act, mode, wgt, wut, F, K, tq, tl, ts, B)
+    got = host(h)
+    assert got.tobytes() == host(h2).tobytes()
+    assert host(hq).tobytes() == host(rq).tobytes()
+    assert host(hs).tobytes() == host(rs).tobytes()
+    if mode == 2:
+        assert host(hl).tobytes() == host(rl).tobytes()
+    # against the oracle
+    oq, ol, os_ = oracle.quantize(mode, x)
+    og = oracle.gemv(mode, wg, sg, xq=oq, xl=ol, xs=os_, nthreads=THREADS)
+    ou = oracle.gemv(mode, wu, su, xq=oq, xl=ol, xs=os_, nthreads=THREADS)
+    np.testing.assert_array_equal(host(g), og)
+    np.testing.assert_array_equal(host(u), ou)
+    d = ulp_diff(got, oracle.glu(act, og, ou))
+    assert d.max() <= 1 and np.count_nonzero(d) <= max(2, d.size // 1000)
+    hq_o, hl_o, hs_o = oracle.quantize(mode, got)
+    w_, s_ = records_acts(hq_o, hs_o, B, zero_row_scale(mode))
+    np.testing.assert_array_equal(host(hq), w_)
+    np.testing.assert_array_equal(host(hs).view(np.int32), s_.view(np.int32))
+    if mode == 2:
+        wl_, _ = records_acts(hl_o, hs_o, B, zero_row_scale(mode))
+        np.testing.assert_array_equal(host(hl), wl_)
+    # no h: the same words
+    hq2, hl2, hs2 = glu_outputs(mode, B, F)
+    q.gemv_glu_mma_tiled(act, mode, wgt, wut, F, K, tq, tl, ts, B, hq2, hl2, hs2)
+    assert host(hq2).tobytes() == host(hq).tobytes() and host(hs2).tobytes() == host(hs).tobytes()
+    if mode == 2:
+        assert host(hl2).tobytes() == host(hl).tobytes()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("B", [16, 64])
+def test_glu_mma_tiled_full(mode, B):
+    """The gate and up halves of the 25600x5120 batched gate+up matrix (F = 12800): the
+    words and h equal the three calls and the quantizer bit for bit, and the down
+    projection over them (5120 rows, K = 12800) gives the same bytes either way."""
+    announce(f"gemv_glu_mma_tiled full B={B} mode={mode}")
+    F, K = 12800, 5120
+    wq, ws = workloads.weights(2 * F, K, 81, 82)
+    x = workloads.batch_activation(B, K, 83 + B, True, 84 + B)
+    wgt, wut = tile(wq[:F], ws[:F]), tile(wq[F:], ws[F:])
+    tq, tl, ts = acts(mode, x)
+    hq, hl, hs = glu_outputs(mode, B, F)
+    h = torch.full((B, F), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_glu_mma_tiled(0, mode, wgt, wut, F, K, tq, tl, ts, B, hq, hl, hs, h=h)
+    _, _, h2, rq, rl, rs = glu_three_calls(0, mode, wgt, wut, F, K, tq, tl, ts, B)
+    assert host(h).tobytes() == host(h2).tobytes()
+    assert host(hq).tobytes() == host(rq).tobytes() and host(hs).tobytes() == host(rs).tobytes()
+    if mode == 2:
+        assert host(hl).tobytes() == host(rl).tobytes()
+    wd, sd = workloads.weights(K, F, 85, 86)
+    wdt = tile(wd, sd)
+    y = torch.full((B, K), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wdt, K, F, y, hq, hl, hs, B)
+    y2 = torch.full((B, K), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_q8_mma_tiled(mode, wdt, K, F, y2, rq, rl, rs, B)
+    assert host(y).tobytes() == host(y2).tobytes()
+    assert not np.isnan(host(y)).any()
+
+
+def test_glu_mma_tiled_overlap_refused():
+    """An output over an input is refused before any launch; outputs right after the inputs are not."""
+    announce("gemv_glu_mma_tiled overlap")
+    B, F, K, mode = 16, 256, 512, 1
+    wg, sg = workloads.weights(F, K, 91, 92)
+    wu, su = workloads.weights(F, K, 93, 94)
+    x = workloads.batch_activation(B, K, 95)
+    wgt, wut = tile(wg, sg), tile(wu, su)
+    R = q.mma_act_rows(B)
+    buf = torch.zeros(R * K + R * F, dtype=torch.int8, device=DEV)
+    tq, hq = buf[:R * K], buf[R * K:]
+    ts = torch.empty(R * (K // 32), dtype=torch.float32, device=DEV)
+    q.quantize_act_mma(mode, dev(x), tq, None, ts)
+    hs = torch.empty(R * (F // 32), dtype=torch.float32, device=DEV)
+    q.gemv_glu_mma_tiled(0, mode, wgt, wut, F, K, tq, None, ts, B, hq, None, hs)
+    _, _, _, rq, _, rs = glu_three_calls(0, mode, wgt, wut, F, K, tq, None, ts, B)
+    assert host(hq).tobytes() == host(rq).tobytes() and host(hs).tobytes() == host(rs).tobytes()
+    with pytest.raises(q.QdgError) as e:
+        q.gemv_glu_mma_tiled(0, mode, wgt, wut, F, K, tq, None, ts, B, buf[R * K - 4:R * K - 4 + R * F], None, hs)
+    assert e.value.status == -1
