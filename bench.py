@@ -627,10 +627,10 @@ def main() -> int:
                                   "quantize_us": round(timer.median_us([qcall], args.launches), 3)}
         rec["mma_tiled"] = tiled
         for mode in (1, 2):
-            R = q.mma_act_rows(PB)
-            tq = torch.empty(R * sh.K, dtype=torch.int8, device=dev)
-            tl = torch.empty(R * sh.K, dtype=torch.int8, device=dev) if mode == 2 else None
-            ts = torch.empty(R * (sh.K // 32), dtype=torch.float32, device=dev)
+            Rp = q.mma_act_rows(PB)
+            tq = torch.empty(Rp * sh.K, dtype=torch.int8, device=dev)
+            tl = torch.empty(Rp * sh.K, dtype=torch.int8, device=dev) if mode == 2 else None
+            ts = torch.empty(Rp * (sh.K // 32), dtype=torch.float32, device=dev)
             q.quantize_act_mma(mode, xp, tq, tl, ts)
             y = torch.empty((PB, sh.N), dtype=torch.float32, device=dev)
             calls = [q.bind_gemv_q8_mma_tiled(mode, wt, sh.N, sh.K, y, tq, tl, ts, PB) for wt in tiles]
