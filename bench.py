@@ -84,7 +84,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps before the timed ones (about 75 ms by default: the clocks settle)")
     ap.add_argument("--splits", default=None,
                     help="split-K chunks: one S for both projections, or 'S_o,S_down'; default per path: 5,5 "
                          "for the in-workgroup combine (fused), 4,16 otherwise")
@@ -134,10 +135,12 @@ class DeviceTimer:
         a, b = self.pairs[i]
         return a.elapsed_time(b)
 
-    def median_us(self, calls, launches: int, warm: int = 5) -> float:
+    def median_us(self, calls, launches: int, warm: int = 300) -> float:
         """Median device duration (µs) of the first kernel of ``calls[i % len(calls)]()`` over
         ``launches`` launches after ``warm`` untimed ones -- and at least one untimed launch on
-        every rotated copy, so that no timed launch is a copy's first touch."""
+        every rotated copy, so that no timed launch is a copy's first touch.  A few untimed
+        launches are not enough: the same kernel, timed again later in one process, ran up to 6%
+        faster (TwoPass, 16 rows) until several milliseconds of launches had passed."""
         for i in range(max(warm, len(calls))):
             calls[i % len(calls)]()
         self.torch.cuda.synchronize()
@@ -148,7 +151,7 @@ class DeviceTimer:
         self.torch.cuda.synchronize()
         return statistics.median(self.ms(i) for i in range(n)) * 1e3
 
-    def wall_us(self, calls, launches: int, warm: int = 5) -> float:
+    def wall_us(self, calls, launches: int, warm: int = 300) -> float:
         """Mean time a call takes in a back-to-back sequence: one event pair around ``launches``
         calls (every kernel of the call, and the gaps between launches, counted), after one untimed
         launch on every rotated copy."""
