@@ -189,7 +189,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     modes = [int(m) for m in args.modes.split(",")]
-    shapes = workloads.CONFIGS[2]
+    shapes = workloads.CONFIGS[workloads.NARROW]
     timer = DeviceTimer(torch, q, max(args.steps * len(modes) * len(shapes), args.launches, 64))
 
     def progress(msg):
@@ -200,7 +200,7 @@ def main() -> int:
     host = []
     base = []
     for si, sh in enumerate(shapes):
-        d = workloads.make(2, si)
+        d = workloads.make(workloads.NARROW, si)
         host.append(d)
         base.append((torch.from_numpy(d["wq"]).to(dev), torch.from_numpy(d["ws"].view(np.int16)).to(dev)))
     set_bytes = sum(w.numel() + 2 * s.numel() for w, s in base)
@@ -492,8 +492,8 @@ def main() -> int:
                        + {0: 4 * F, 1: F + F // 8, 2: 2 * F + F // 8}[mode], f_us)}
 
     if want("tiny"):
-        sh = workloads.CONFIGS[0][0]
-        d, wsets = upload_set(0, 0, 0)
+        sh = workloads.CONFIGS[workloads.TINY][0]
+        d, wsets = upload_set(workloads.TINY, 0, 0)
         x = torch.from_numpy(d["x"]).to(dev)
         rec = {}
         for mode in (0, 1, 2):
@@ -511,8 +511,8 @@ def main() -> int:
         # S per projection (measured best, in-workgroup combine / Dequant chunk waves)
         s_q8 = {"qkv": 2, "gate_up": 2, "down": 6}
         s_dq = {"qkv": 3, "gate_up": 2, "down": 2}
-        for si, sh in enumerate(workloads.CONFIGS[1]):
-            d, wsets = upload_set(1, si)
+        for si, sh in enumerate(workloads.CONFIGS[workloads.DECODE_8B]):
+            d, wsets = upload_set(workloads.DECODE_8B, si)
             x = torch.from_numpy(d["x"]).to(dev)
             rec = {}
             for mode in (0, 1, 2):
@@ -543,9 +543,9 @@ def main() -> int:
         progress("narrow S sweep done")
 
     if want("lm_head"):
-        sh = workloads.CONFIGS[3][0]
-        d = workloads.make(3, 0)
-        a, b = workloads.tie_rows(sh.N, workloads.seed_of(3, 0, 4))
+        sh = workloads.CONFIGS[workloads.LM_HEAD][0]
+        d = workloads.make(workloads.LM_HEAD, 0)
+        a, b = workloads.tie_rows(sh.N, workloads.seed_of(workloads.LM_HEAD, 0, 4))
         workloads.plant_tie(d["wq"], d["ws"], d["x"][0], a, b)
         w = torch.from_numpy(d["wq"]).to(dev)
         s = torch.from_numpy(d["ws"].view(np.int16)).to(dev)
@@ -578,8 +578,8 @@ def main() -> int:
         progress("LM head done")
 
     if want("batched"):
-        sh = workloads.CONFIGS[4][0]
-        d, wsets = upload_set(4, 0)
+        sh = workloads.CONFIGS[workloads.BATCHED][0]
+        d, wsets = upload_set(workloads.BATCHED, 0)
         x = torch.from_numpy(d["x"]).to(dev)
         rec = {}
         for mode in (1, 2):

@@ -81,8 +81,8 @@ def measure(reps: int, step: bool = False, pair: bool = False) -> dict:
     for e in ev:
         e.record()
     out = {}
-    for si, sh in enumerate(workloads.CONFIGS[2]):
-        d = workloads.make(2, si)
+    for si, sh in enumerate(workloads.CONFIGS[workloads.NARROW]):
+        d = workloads.make(workloads.NARROW, si)
         w0 = torch.from_numpy(d["wq"]).to(dev)
         s0 = torch.from_numpy(d["ws"].view(np.int16)).to(dev)
         R = max(2, int(1.2e9 // (w0.numel() * 1.0625)))

@@ -54,7 +54,8 @@ def run_path(mode, w, x, splits=1, with_argmax=False):
     return buf, y.cpu().numpy()
 
 
-@pytest.mark.parametrize("config,shape_index", [(0, 0), (1, 0), (1, 1), (1, 2)])
+@pytest.mark.parametrize("config,shape_index", [(workloads.TINY, 0), (workloads.DECODE_8B, 0), (workloads.DECODE_8B, 1),
+                                                 (workloads.DECODE_8B, 2)])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_decode_projections(config, shape_index, mode):
     announce(f"config {config}.{shape_index} mode {mode}")
@@ -67,7 +68,7 @@ def test_decode_projections(config, shape_index, mode):
 @pytest.mark.parametrize("shape_index", [0, 1])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_narrow_projections_split_k(shape_index, mode):
-    d = workloads.make(2, shape_index)
+    d = workloads.make(workloads.NARROW, shape_index)
     w = Q8Matrix.from_numpy(d["wq"], d["ws"])
     for S in (1, 2, 4, 8):
         announce(f"config 2.{shape_index} mode {mode} S={S}")
@@ -82,7 +83,7 @@ def test_narrow_projections_split_k(shape_index, mode):
 @pytest.fixture(scope="module")
 def lm_head():
     announce("generating the 151936x5120 LM head")
-    d = workloads.make(3, 0)
+    d = workloads.make(workloads.LM_HEAD, 0)
     return d
 
 
@@ -91,7 +92,7 @@ def test_lm_head_argmax_planted_ties(lm_head):
     wq, ws, x = d["wq"], d["ws"], d["x"]
     N = wq.shape[0]
     w = Q8Matrix.from_numpy(wq, ws)
-    a0, b0 = workloads.tie_rows(N, workloads.seed_of(3, 0, 4))
+    a0, b0 = workloads.tie_rows(N, workloads.seed_of(workloads.LM_HEAD, 0, 4))
     placements = [(a0, b0), (0, N - 1), (15, 16), (2025, 2026), (N - 2, N - 1), (1, N - 1)]
     for a, b in placements:
         saved = (wq[[a, b]].copy(), ws[[a, b]].copy())
@@ -132,7 +133,7 @@ def test_lm_head_argmax_planted_ties(lm_head):
 @pytest.mark.parametrize("mode", [1, 2])
 def test_batched_decode_b16(mode):
     announce(f"batched B=16 25600x5120 mode {mode}")
-    d = workloads.make(4, 0)
+    d = workloads.make(workloads.BATCHED, 0)
     w = Q8Matrix.from_numpy(d["wq"], d["ws"])
     _, y = run_path(mode, w, d["x"])
     check(mode, y, d["wq"], d["ws"], d["x"])

@@ -188,7 +188,7 @@ def test_mma_tiled_decode_b16_full(mode):
     """The 16-row batch against 25600x5120 in the benchmark's launch: every output
     against the oracle, and a repeat gives the same bytes."""
     announce(f"gemv_q8_mma_tiled B=16 25600x5120 mode {mode}")
-    d = workloads.make(4, 0)
+    d = workloads.make(workloads.BATCHED, 0)
     wq, ws, x = d["wq"], d["ws"], d["x"]
     B, K = x.shape
     N = wq.shape[0]

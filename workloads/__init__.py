@@ -43,20 +43,27 @@ class Shape:
     outliers: bool = False
 
 
-# config index -> list of shapes (index in the list is the shape_index of the seed)
+# The workload sets, each a seed base (it enters every seed, so the inputs stay
+# fixed) and its shapes (the position in the list is the shape_index of the seed).
+TINY = 0        # 256x512, one tile's worth: the case the oracle finishes in a blink
+DECODE_8B = 1   # the projections of an 8B-class decoder layer
+NARROW = 2      # o-proj 5120x8192 and down-proj 5120x25600, batch 1
+LM_HEAD = 3     # 151936x5120 with an arg-max
+BATCHED = 4     # the 25600x5120 gate+up matrix with 16 activation rows
+
 CONFIGS: dict[int, list[Shape]] = {
-    0: [Shape("tiny", K=512, N=256)],
-    1: [
+    TINY: [Shape("tiny", K=512, N=256)],
+    DECODE_8B: [
         Shape("qkv", K=4096, N=6144, outliers=True),
         Shape("gate_up", K=4096, N=24576, outliers=True),
         Shape("down", K=12288, N=4096, outliers=True),
     ],
-    2: [
+    NARROW: [
         Shape("o_proj", K=8192, N=5120, outliers=True),
         Shape("down_proj", K=25600, N=5120, outliers=True),
     ],
-    3: [Shape("lm_head", K=5120, N=151936)],
-    4: [Shape("batched_gate_up", K=5120, N=25600, B=16)],
+    LM_HEAD: [Shape("lm_head", K=5120, N=151936)],
+    BATCHED: [Shape("batched_gate_up", K=5120, N=25600, B=16)],
 }
 
 
