@@ -39,6 +39,7 @@ DOMINANT_SOURCES = (os.path.join(CSRC, "qdg_wsplit.hip"), os.path.join(CSRC, "qd
 def sources_for(kernel: str) -> tuple:
     """The translation unit of a traced kernel, for the hash stored beside its byte count."""
     unit = {"k_gemv_fmt": "qdg_formats.hip", "k_gemv_dq_seg": "qdg_dequant_seg.hip",
+            "k_gemv_dq_glu": "qdg_dequant_seg.hip", "k_gemv_glu": "qdg_glu.hip", "k_gemv_mma": "qdg_mma_tiled.hip",
             "k_gemv_mfma": "qdg_mfma.hip", "k_gemv_dot4": "qdg_gemv.hip"}
     for prefix, f in unit.items():
         if kernel.startswith(prefix):
