@@ -296,6 +296,8 @@ def _glu_args(mode, wg, sg, wu, su, xq, xl, xs, h, hq, hl, hs):
     F, K = wg.shape
     if tuple(wu.shape) != (F, K):
         raise ValueError("gemv_glu_q8: gate and up must have the same shape")
+    _need(sg=(sg, F * (K // QK)), su=(su, F * (K // QK)), xq=(xq, K), xl=(xl, K), xs=(xs, K // QK), h=(h, F),
+          hq=(hq, F), hl=(hl, F), hs=(hs, F // QK))
     return (mode, _ptr(wg, _i8(), "wg"), _ptr(sg, _scales(), "sg"), _ptr(wu, _i8(), "wu"), _ptr(su, _scales(), "su"),
             F, K, _ptr(xq, _i8(), "xq"), _ptr(xl, _i8(), "xl"), _ptr(xs, _f32(), "xs"), _ptr(h, _f32(), "h"),
             _ptr(hq, _i8(), "hq"), _ptr(hl, _i8(), "hl"), _ptr(hs, _f32(), "hs"), _stream())
@@ -327,6 +329,7 @@ def _glu_dequant_args(act, wg, sg, wu, su, x, h):
         raise ValueError("gemv_glu_dequant: gate and up must have the same shape")
     if x.numel() != K or h.numel() != F:
         raise ValueError("gemv_glu_dequant: x must hold K values and h F values")
+    _need(sg=(sg, F * (K // QK)), su=(su, F * (K // QK)))
     return (act, _ptr(wg, _i8(), "wg"), _ptr(sg, _scales(), "sg"), _ptr(wu, _i8(), "wu"), _ptr(su, _scales(), "su"),
             F, K, _ptr(x, _f32(), "x"), _ptr(h, _f32(), "h"), _stream())
 

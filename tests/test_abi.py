@@ -598,6 +598,25 @@ def test_binding_checks_sizes_before_the_call():
         lambda: q.gemv_q8_argmax(q.INT8ACT, w, ws, torch.zeros(N - 2), torch.zeros(1, dtype=torch.int32), wsp,
                                  xq=xq, xs=xs),
     ]
+    # the gate/up epilogues: F = 64 outputs
+    F = 64
+    wg = torch.zeros((F, K), dtype=torch.int8)
+    sg = torch.zeros((F, K // 32), dtype=torch.int16)
+    hq, hs = torch.zeros(F, dtype=torch.int8), torch.zeros(F // 32)
+    R = q.mma_act_rows(16)
+    wt = torch.zeros(q.q8_tile_mma_bytes(F, K), dtype=torch.uint8)
+    tq, ts = torch.zeros(R * K, dtype=torch.int8), torch.zeros(R * (K // 32))
+    cases += [
+        lambda: q.gemv_glu_q8(q.INT8ACT, wg, sg[:F // 2].contiguous(), wg, sg, xq, None, xs, hq, None, hs),
+        lambda: q.gemv_glu_q8(q.INT8ACT, wg, sg, wg, sg, xq, None, xs, hq[:F - 4].contiguous(), None, hs),
+        lambda: q.gemv_glu_act_q8(q.ACT_SIGMOID, q.INT8ACT, wg, sg, wg, sg, xq, None, xs[:, :2].contiguous(), hq,
+                                  None, hs),
+        lambda: q.gemv_glu_dequant(0, wg, sg, wg, sg[:3].contiguous(), torch.zeros(K), torch.zeros(F)),
+        lambda: q.gemv_glu_mma_tiled(0, q.INT8ACT, wt, wt, F, K, tq, None, ts, 16, torch.zeros(R * F - 4,
+                                     dtype=torch.int8), None, torch.zeros(R * (F // 32))),
+        lambda: q.gemv_glu_mma_tiled(0, q.INT8ACT, wt[:100].contiguous(), wt, F, K, tq, None, ts, 16,
+                                     torch.zeros(R * F, dtype=torch.int8), None, torch.zeros(R * (F // 32))),
+    ]
     for i, c in enumerate(cases):
         with pytest.raises(ValueError, match="holds|ws must"):
             c()
