@@ -427,7 +427,7 @@ def glu_dequant_three_calls(act, dwg, dsg, dwu, dsu, dx, F):
 
 @pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("F,K", [(32, 32), (3, 544), (7, 1536), (101, 4096), (5120, 5120), (8191, 1056),
-                                 (8192, 1056), (12289, 800), (25600, 5120)])
+                                 (8192, 1056), (12289, 800), (12288, 4096), (25600, 5120)])
 def test_glu_dequant_matches_the_three_calls(act, F, K):
     """qdg_gemv_glu_dequant against two qdg_gemv_q8 Dequant calls and qdg_glu_quantize,
     bit for bit (both sides of the 8192-row change of chunk count, ragged F, K with
